@@ -24,7 +24,8 @@
  *     channels: s = fp16((max - min) / 3), z = fp16(min), both rounded to
  *     nearest even; codes use the fp16-rounded s and z:
  *     code = clamp(rint((y - z) / s), 0, 3), rint rounding half to even;
- *     s == 0 gives code 0 everywhere;
+ *     s == 0 gives code 0 everywhere; a zero range or minimum is stored as
+ *     +0 whatever the sign of the zeros it came from;
  *   - four codes of consecutive channels share a byte, first channel in the
  *     least significant bits.
  * All fp32 operations are IEEE binary32 with correctly rounded results
@@ -128,9 +129,11 @@ void oracle_quantize(const float *y, int d, int G, uint8_t *codes,
             mn = fminf(mn, v[k]);
             mx = fmaxf(mx, v[k]);
         }
-        float range = mx - mn;
+        /* "+ 0.0f" maps a zero of either sign to +0, so an exactly zero
+         * range or minimum is always stored as the +0 pattern */
+        float range = (mx - mn) + 0.0f;
         uint16_t s16 = oracle_f32_to_f16(range / 3.0f);
-        uint16_t z16 = oracle_f32_to_f16(mn);
+        uint16_t z16 = oracle_f32_to_f16(mn + 0.0f);
         float s = oracle_f16_to_f32(s16);
         float z = oracle_f16_to_f32(z16);
         for (int k = 0; k < G; ++k) {

@@ -156,3 +156,10 @@ def test_encode_matches_steps():
     assert np.array_equal(pk, oracle.pack(codes))
     assert np.array_equal(s16, s2) and np.array_equal(z16, z2)
     assert np.abs(y).max() <= 1.5
+
+
+def test_signed_zero_groups_store_plus_zero():
+    # a group of zeros of both signs: range and minimum are stored as +0
+    y = np.array([[0.0, -0.0, 0.0, -0.0], [-0.0, -0.0, -0.0, -0.0]], dtype=np.float32)
+    codes, s16, z16 = oracle.quantize(y, 4)
+    assert np.all(s16 == 0) and np.all(z16 == 0) and np.all(codes == 0)
