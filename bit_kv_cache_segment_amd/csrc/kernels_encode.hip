@@ -1,0 +1,288 @@
+// Eviction / prefill encoder for gfx950: rotate by R, clip, quantize to four
+// levels with a group-wise fp16 scale and zero point, pack 2-bit codes into
+// the paged history, and maintain the BF16 sink and recent windows.
+//
+// Method: news article on OSCAR (sanyangsrq.com), section "From offline
+// calibration to online inference" — the oldest recent-window token is
+// rotated, clipped, quantized and packed (four 2-bit values per byte) by one
+// fused kernel and moved into the INT2 history; section "OSCAR aims the
+// rotation at attention" — R = U . Hadamard . bit-reversal and the clip
+// thresholds are fixed offline.
+//
+// Arithmetic (kept identical to the definition so codes are reproducible):
+//   y_j = fma chain over i = 0..d-1 of x_i * R[i][j] in fp32 from +0,
+//   y_j = min(max(y_j, -c_j), c_j),
+//   per group of G channels: s = fp16_rne((max - min) / 3), z = fp16_rne(min),
+//   code = s == 0 ? 0 : clamp(rint((y - z) / s), 0, 3), with the fp16 s, z.
+// One thread owns one output channel j and keeps column j of R in registers,
+// so every token costs d fused multiply-adds per thread in a fixed order.
+// The rotation is d x d per token (~33 MFLOP per step for 64 sequences x 8
+// heads x K,V): it is far too small to pay for MFMA tiles, and MFMA would not
+// reproduce the fixed accumulation order the codes are defined with.
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f16_bits(float f) {
+  _Float16 h = (_Float16)f; // v_cvt_f16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// OR of a value over the 16 lanes of an aligned lane group.
+__device__ __forceinline__ uint32_t or16(uint32_t v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Quantize this thread's clipped value y (channel j) of one token.  `red`
+// is LDS scratch of 2 * (D/64) floats.  Returns the code and sets the
+// group's fp16 scale/zero bits (uniform over the group).
+template <int D, int G>
+__device__ __forceinline__ uint32_t quantize_channel(float y, float *red, uint16_t &s16, uint16_t &z16) {
+  const int j = threadIdx.x, w = j / 64;
+  float mn = wave_min(y), mx = wave_max(y);
+  if (G > 64) {
+    // a group spans G/64 waves: combine through LDS
+    if ((j & 63) == 0) {
+      red[2 * w] = mn;
+      red[2 * w + 1] = mx;
+    }
+    __syncthreads();
+    const int w0 = (j / G) * (G / 64);
+    mn = red[2 * w0];
+    mx = red[2 * w0 + 1];
+#pragma unroll
+    for (int k = 1; k < G / 64; ++k) {
+      mn = fminf(mn, red[2 * (w0 + k)]);
+      mx = fmaxf(mx, red[2 * (w0 + k) + 1]);
+    }
+    __syncthreads();
+  }
+  // "+ 0.0f" stores an exactly zero range or minimum as +0 whatever the
+  // sign of the zeros min/max returned
+  s16 = f16_bits(((mx - mn) + 0.0f) / 3.0f);
+  z16 = f16_bits(mn + 0.0f);
+  const float s = f16_val(s16), z = f16_val(z16);
+  float q = 0.0f;
+  if (s != 0.0f) q = fminf(fmaxf(rintf((y - z) / s), 0.0f), 3.0f);
+  return (uint32_t)q;
+}
+
+// Write token slot t's K code of channel j: 16 lanes assemble one dword.
+template <int D>
+__device__ __forceinline__ void store_k_code(uint8_t *blk, int t, uint32_t code) {
+  const int j = threadIdx.x;
+  uint32_t dw = or16(code << (2 * (j & 15)));
+  if ((j & 15) == 0) {
+    const int r = (j & 63) / 16, m = j / 64;
+    *(uint32_t *)(blk + kcode_dword_off(D, t, r, m)) = dw;
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void store_params(uint8_t *blk, int off, uint16_t s16, uint16_t z16) {
+  if ((threadIdx.x % G) == 0) *(uint32_t *)(blk + off) = (uint32_t)s16 | ((uint32_t)z16 << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one block per (history page of the prompt, kv head, K|V).
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(D) void prefill_encode_kernel(PoolDev p, int seq, const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ v, int n_hist) {
+  const int pg_idx = blockIdx.x, kv = blockIdx.y, kind = blockIdx.z, j = threadIdx.x;
+  const int Hkv = p.Hkv;
+  const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
+  const float c = (kind ? p.clipV : p.clipK)[kv * D + j];
+  const uint16_t *src = kind ? v : k;
+  __shared__ float xs[kPage][D];
+  __shared__ float red[2 * (D / 64)];
+
+  float rc[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) rc[i] = R[i * D + j];
+
+  const int t0 = pg_idx * kPage;
+  const int nt = min(kPage, n_hist - t0);
+  for (int t = 0; t < nt; ++t)
+    xs[t][j] = bf16f(src[((size_t)(kSink + t0 + t) * Hkv + kv) * D + j]);
+  __syncthreads();
+
+  const int page = p.page_table[(size_t)seq * p.maxp + pg_idx];
+  uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
+  uint32_t vdw[kPage / 16] = {0, 0, 0, 0};
+  for (int t = 0; t < nt; ++t) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc = fmaf(xs[t][i], rc[i], acc);
+    const float y = fminf(fmaxf(acc, -c), c);
+    uint16_t s16, z16;
+    const uint32_t code = quantize_channel<D, G>(y, red, s16, z16);
+    if (kind == 0) {
+      store_k_code<D>(blk, t, code);
+      store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
+    } else {
+      vdw[t / 16] |= code << (2 * (t % 16));
+      store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
+    }
+  }
+  if (kind == 1) {
+#pragma unroll
+    for (int tb = 0; tb < kPage / 16; ++tb)
+      if (tb * 16 < nt) *(uint32_t *)(blk + vcode_dword_off(D, tb, j)) = vdw[tb];
+  }
+}
+
+// Prefill: copy sink and recent positions into the BF16 windows.
+// grid (window positions, Hkv), block D: position index u < n_sink is sink
+// position u; otherwise recent position n_hist + 64 + (u - n_sink).
+template <int D>
+__global__ void prefill_window_kernel(PoolDev p, int seq, const uint16_t *__restrict__ k,
+                                      const uint16_t *__restrict__ v, int n_sink, int n_hist) {
+  const int u = blockIdx.x, kv = blockIdx.y, j = threadIdx.x, Hkv = p.Hkv;
+  int pos;
+  size_t dst;
+  if (u < n_sink) {
+    pos = u;
+    dst = (((size_t)seq * Hkv + kv) * kSink + pos) * D + j;
+    p.sinkK[dst] = k[((size_t)pos * Hkv + kv) * D + j];
+    p.sinkV[dst] = v[((size_t)pos * Hkv + kv) * D + j];
+  } else {
+    pos = kSink + n_hist + (u - n_sink);
+    dst = (((size_t)seq * Hkv + kv) * kRecent + (pos - kSink) % kRecent) * D + j;
+    p.recentK[dst] = k[((size_t)pos * Hkv + kv) * D + j];
+    p.recentV[dst] = v[((size_t)pos * Hkv + kv) * D + j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append: grid (ceil(n / E), Hkv, K|V), block D.  Each block serves up to E
+// sequences of the batch; R's column stays in registers across them.
+// ---------------------------------------------------------------------------
+template <int D, int G, int E>
+__global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, const uint16_t *__restrict__ k_new,
+                                                   const uint16_t *__restrict__ v_new) {
+  const int kv = blockIdx.y, kind = blockIdx.z, j = threadIdx.x, Hkv = p.Hkv;
+  const int e0 = blockIdx.x * E, e1 = min(b.n, e0 + E);
+  const uint16_t *src_new = kind ? v_new : k_new;
+  uint16_t *sink = kind ? p.sinkV : p.sinkK;
+  uint16_t *recent = kind ? p.recentV : p.recentK;
+  __shared__ float xs[D];
+  __shared__ float red[2 * (D / 64)];
+
+  bool any_evict = false;
+  for (int e = e0; e < e1; ++e) any_evict |= b.len[e] >= kWindow;
+  float rc[D];
+  float c = 0.0f;
+  if (any_evict) {
+    const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) rc[i] = R[i * D + j];
+    c = (kind ? p.clipV : p.clipK)[kv * D + j];
+  }
+  for (int e = e0; e < e1; ++e) {
+    const int seq = b.seq[e], L = b.len[e];
+    const uint16_t xnew = src_new[((size_t)e * Hkv + kv) * D + j];
+    if (L < kSink) {
+      sink[(((size_t)seq * Hkv + kv) * kSink + L) * D + j] = xnew;
+      continue;
+    }
+    const int slot = (L - kSink) % kRecent;
+    uint16_t *rs = recent + (((size_t)seq * Hkv + kv) * kRecent + slot) * D;
+    if (L < kWindow) {
+      rs[j] = xnew;
+      continue;
+    }
+    // evict the oldest recent token (held in this slot) into history n_hist
+    const int n_hist = L - kWindow;
+    xs[j] = bf16f(rs[j]);
+    rs[j] = xnew; // this thread read element j above; no other thread touches it
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc = fmaf(xs[i], rc[i], acc);
+    const float y = fminf(fmaxf(acc, -c), c);
+    uint16_t s16, z16;
+    const uint32_t code = quantize_channel<D, G>(y, red, s16, z16);
+    const int pg_idx = n_hist / kPage, t = n_hist % kPage;
+    int page;
+    if (t == 0) {
+      page = b.new_page[e];
+      if (kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
+    } else {
+      page = p.page_table[(size_t)seq * p.maxp + pg_idx];
+    }
+    uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
+    if (kind == 0) {
+      store_k_code<D>(blk, t, code);
+      store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
+    } else {
+      // one byte holds four consecutive tokens of channel j: read-modify-write
+      uint8_t *byte = blk + vcode_dword_off(D, t / 16, j) + (t % 16) / 4;
+      const int sh = 2 * (t % 4);
+      const uint32_t old = (t % 4 == 0) ? 0u : *byte;
+      *byte = (uint8_t)((old & ~(3u << sh)) | (code << sh));
+      store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
+    }
+    __syncthreads(); // xs is reused by the next sequence
+  }
+}
+
+template <int D, int G>
+hipError_t prefill_impl(const PoolDev &p, int seq, const uint16_t *k, const uint16_t *v, int L, hipStream_t s) {
+  const int n_hist = max(0, L - kWindow);
+  const int n_sink = min(L, kSink);
+  const int n_rec = L - n_sink - n_hist;
+  if (n_sink + n_rec > 0)
+    hipLaunchKernelGGL(prefill_window_kernel<D>, dim3(n_sink + n_rec, p.Hkv), dim3(D), 0, s, p, seq, k, v,
+                       n_sink, n_hist);
+  if (n_hist > 0) {
+    const int np = (n_hist + kPage - 1) / kPage;
+    hipLaunchKernelGGL((prefill_encode_kernel<D, G>), dim3(np, p.Hkv, 2), dim3(D), 0, s, p, seq, k, v, n_hist);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t append_impl(const PoolDev &p, const AppendBatch &b, const uint16_t *kn, const uint16_t *vn,
+                       hipStream_t s, const KernelTimer &t) {
+  constexpr int E = 8;
+  if (t.on) (void)hipEventRecord(t.ev[0], s);
+  hipLaunchKernelGGL((append_kernel<D, G, E>), dim3((b.n + E - 1) / E, p.Hkv, 2), dim3(D), 0, s, p, b, kn, vn);
+  if (t.on) (void)hipEventRecord(t.ev[1], s);
+  return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const uint16_t *v, int L, hipStream_t s) {
+  if (p.d == 128 && p.G == 128) return prefill_impl<128, 128>(p, seq, k, v, L, s);
+  if (p.d == 128 && p.G == 64) return prefill_impl<128, 64>(p, seq, k, v, L, s);
+  if (p.d == 64 && p.G == 64) return prefill_impl<64, 64>(p, seq, k, v, L, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *kn, const uint16_t *vn,
+                         hipStream_t s, const KernelTimer &t) {
+  if (p.d == 128 && p.G == 128) return append_impl<128, 128>(p, b, kn, vn, s, t);
+  if (p.d == 128 && p.G == 64) return append_impl<128, 64>(p, b, kn, vn, s, t);
+  if (p.d == 64 && p.G == 64) return append_impl<64, 64>(p, b, kn, vn, s, t);
+  return hipErrorInvalidValue;
+}
+
+} // namespace oscar

@@ -1,0 +1,674 @@
+// Host side of the OSCAR pool library: configuration and layout, argument
+// validation, the host mirror of lengths / page tables / free list, the
+// offline helpers (rotation construction, clip calibration) and the C ABI.
+//
+// Method source: news article on OSCAR (sanyangsrq.com), sections
+// "OSCAR aims the rotation at attention" (R = U . Hadamard . bit-reversal,
+// thresholds fixed offline) and "From offline calibration to online
+// inference" (three-segment pool, eviction of the oldest recent token,
+// paged layout).
+#include "../../include/oscar.h"
+#include "oscar_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace oscar;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return OSCAR_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(OSCAR_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t RK, RV, RVt, clipK, clipV, page_table, sinkK, sinkV, recentK, recentV, pages, total;
+};
+
+int validate_config(const oscar_pool_config *c) {
+  if (!c) return fail(OSCAR_EINVAL, "config is NULL");
+  if (c->max_seqs < 1 || c->max_seqs > 65536)
+    return fail(OSCAR_EINVAL, "max_seqs %d outside [1, 65536]", c->max_seqs);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > 64)
+    return fail(OSCAR_EINVAL, "num_kv_heads %d outside [1, 64]", c->num_kv_heads);
+  if (c->num_q_heads < 1 || c->num_q_heads % c->num_kv_heads != 0)
+    return fail(OSCAR_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                c->num_q_heads, c->num_kv_heads);
+  int g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+    return fail(OSCAR_EINVAL, "query heads per kv head (%d) must be 1, 2, 4, 8 or 16", g);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(OSCAR_EINVAL, "head_dim %d must be 64 or 128", c->head_dim);
+  if ((c->group_size != 64 && c->group_size != 128) || c->group_size > c->head_dim)
+    return fail(OSCAR_EINVAL, "group_size %d must be 64 or 128 and <= head_dim", c->group_size);
+  if (c->num_pages < 0 || c->num_pages > (1 << 28))
+    return fail(OSCAR_EINVAL, "num_pages %d outside [0, 2^28]", c->num_pages);
+  if (c->max_pages_per_seq < 0 || c->max_pages_per_seq > (1 << 20))
+    return fail(OSCAR_EINVAL, "max_pages_per_seq %d outside [0, 2^20]", c->max_pages_per_seq);
+  if ((int64_t)c->max_seqs * c->max_pages_per_seq > (int64_t)1 << 31)
+    return fail(OSCAR_EINVAL, "page table of %d x %d entries is too large", c->max_seqs,
+                c->max_pages_per_seq);
+  if (c->flags & ~OSCAR_POOL_HOST_ONLY) return fail(OSCAR_EINVAL, "unknown flags 0x%x", c->flags);
+  return OSCAR_OK;
+}
+
+Layout layout_of(const oscar_pool_config &c) {
+  Layout L;
+  size_t d = c.head_dim, H = c.num_kv_heads, S = c.max_seqs;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.RK = take(H * d * d * 4);
+  L.RV = take(H * d * d * 4);
+  L.RVt = take(H * d * d * 4);
+  L.clipK = take(H * d * 4);
+  L.clipV = take(H * d * 4);
+  L.page_table = take(S * (size_t)c.max_pages_per_seq * 4);
+  L.sinkK = take(S * H * kSink * d * 2);
+  L.sinkV = take(S * H * kSink * d * 2);
+  L.recentK = take(S * H * kRecent * d * 2);
+  L.recentV = take(S * H * kRecent * d * 2);
+  L.pages = take((size_t)c.num_pages * H * block_bytes_for(c.head_dim, c.group_size));
+  L.total = off;
+  return L;
+}
+
+int pages_for(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPage); }
+
+// Split policy of one decode launch: pages per split is a multiple of 4 (one
+// page per wave per step), at least 8, large enough for ~2048 split blocks
+// in total and for at most kMaxSplits splits per (sequence, kv head).
+constexpr int kMaxSplits = 32;
+constexpr int kTargetBlocks = 2048;
+
+int choose_pages_per_split(int64_t total_pages, int max_np, int Hkv) {
+  int64_t ps = (total_pages * Hkv + kTargetBlocks - 1) / kTargetBlocks;
+  ps = std::max<int64_t>(ps, (max_np + kMaxSplits - 1) / kMaxSplits);
+  ps = std::max<int64_t>(ps, 8);
+  ps = (ps + 3) / 4 * 4;
+  return (int)ps;
+}
+
+} // namespace
+
+// Event pairs for per-kernel timing (oscar_profile_begin / _end).
+struct Profiler {
+  bool on = false;
+  int cap = 0;
+  std::vector<hipEvent_t> ev[3]; // decode main, decode merge, append: 2 per launch
+  int used[3] = {0, 0, 0};
+  KernelTimer next(int kind) {
+    KernelTimer t;
+    if (on && used[kind] < cap) {
+      t.on = true;
+      t.ev[0] = ev[kind][2 * used[kind]];
+      t.ev[1] = ev[kind][2 * used[kind] + 1];
+      ++used[kind];
+    }
+    return t;
+  }
+  void release() {
+    for (auto &v : ev) {
+      for (hipEvent_t e : v) hipEventDestroy(e);
+      v.clear();
+    }
+    on = false;
+    cap = 0;
+    used[0] = used[1] = used[2] = 0;
+  }
+};
+
+struct oscar_pool {
+  Profiler prof;
+  ~oscar_pool() { prof.release(); }
+  oscar_pool_config cfg;
+  Layout lay;
+  PoolDev dev;
+  bool host_only;
+  std::vector<int32_t> len;
+  std::vector<std::vector<int32_t>> table;
+  std::vector<int32_t> free_list; // pages [free_head, end) are free, front first
+  size_t free_head = 0;
+
+  int64_t n_free() const { return (int64_t)free_list.size() - (int64_t)free_head; }
+  int32_t pop() { return free_list[free_head++]; }
+  void compact() {
+    if (free_head > 4096 && free_head * 2 > free_list.size()) {
+      free_list.erase(free_list.begin(), free_list.begin() + free_head);
+      free_head = 0;
+    }
+  }
+};
+
+extern "C" {
+
+const char *oscar_last_error(void) { return g_err.c_str(); }
+
+int oscar_pool_bytes(const oscar_pool_config *cfg, size_t *device_bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!device_bytes) return fail(OSCAR_EINVAL, "device_bytes is NULL");
+  *device_bytes = layout_of(*cfg).total;
+  return ok();
+}
+
+int oscar_decode_workspace_bytes(const oscar_pool_config *cfg, int32_t max_batch, size_t *bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!bytes || max_batch < 0) return fail(OSCAR_EINVAL, "bad arguments");
+  int n = std::min(max_batch, kMaxBatch);
+  int g = cfg->num_q_heads / cfg->num_kv_heads;
+  long hist_blocks = (long)n * cfg->num_kv_heads * kMaxSplits;
+  *bytes = decode_ws_floats(cfg->num_q_heads, cfg->head_dim, n, hist_blocks, g) * sizeof(float);
+  return ok();
+}
+
+int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t bytes, const float *R_K,
+                      const float *R_V, const float *clip_K, const float *clip_V, void *stream,
+                      oscar_pool **out) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(OSCAR_EINVAL, "out is NULL");
+  bool host_only = cfg->flags & OSCAR_POOL_HOST_ONLY;
+  Layout lay = layout_of(*cfg);
+  const int H = cfg->num_kv_heads, d = cfg->head_dim;
+  if (!host_only) {
+    if (!device_buf || !R_K || !R_V || !clip_K || !clip_V)
+      return fail(OSCAR_EINVAL, "NULL buffer or table");
+    if ((uintptr_t)device_buf % 256) return fail(OSCAR_EINVAL, "device_buf is not 256-byte aligned");
+    if (bytes < lay.total)
+      return fail(OSCAR_EINVAL, "device buffer of %zu bytes < %zu required", bytes, lay.total);
+    for (size_t i = 0; i < (size_t)H * d * d; ++i)
+      if (!std::isfinite(R_K[i]) || !std::isfinite(R_V[i]))
+        return fail(OSCAR_EINVAL, "rotation entry %zu is not finite", i);
+    for (size_t i = 0; i < (size_t)H * d; ++i) {
+      float ck = clip_K[i], cv = clip_V[i];
+      // clipped values lie in [-c, c]: the zero point fp16(min) and the scale
+      // fp16((max - min) / 3) <= fp16(2c/3) stay finite for c <= 65504.
+      if (!(ck > 0.f && ck <= 65504.f) || !(cv > 0.f && cv <= 65504.f))
+        return fail(OSCAR_EINVAL, "clip threshold %zu (%g, %g) outside (0, 65504]", i, ck, cv);
+    }
+  }
+  oscar_pool *p = new oscar_pool();
+  p->cfg = *cfg;
+  p->lay = lay;
+  p->host_only = host_only;
+  p->len.assign(cfg->max_seqs, 0);
+  p->table.assign(cfg->max_seqs, {});
+  // Free list: Fisher-Yates shuffle of [0, num_pages) driven by SplitMix64.
+  p->free_list.resize(cfg->num_pages);
+  for (int i = 0; i < cfg->num_pages; ++i) p->free_list[i] = i;
+  uint64_t state = cfg->page_shuffle_seed;
+  auto next = [&state]() {
+    uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  };
+  for (int i = cfg->num_pages - 1; i > 0; --i) {
+    uint64_t j = next() % (uint64_t)(i + 1);
+    std::swap(p->free_list[i], p->free_list[j]);
+  }
+  PoolDev &D = p->dev;
+  std::memset(&D, 0, sizeof D);
+  D.Hq = cfg->num_q_heads;
+  D.Hkv = H;
+  D.d = d;
+  D.G = cfg->group_size;
+  D.maxp = cfg->max_pages_per_seq;
+  D.block_bytes = block_bytes_for(d, cfg->group_size);
+  if (!host_only) {
+    char *b = (char *)device_buf;
+    D.RK = (const float *)(b + lay.RK);
+    D.RV = (const float *)(b + lay.RV);
+    D.RVt = (const float *)(b + lay.RVt);
+    D.clipK = (const float *)(b + lay.clipK);
+    D.clipV = (const float *)(b + lay.clipV);
+    D.page_table = (int32_t *)(b + lay.page_table);
+    D.sinkK = (uint16_t *)(b + lay.sinkK);
+    D.sinkV = (uint16_t *)(b + lay.sinkV);
+    D.recentK = (uint16_t *)(b + lay.recentK);
+    D.recentV = (uint16_t *)(b + lay.recentV);
+    D.pages = (uint8_t *)(b + lay.pages);
+    std::vector<float> rvt((size_t)H * d * d);
+    for (int h = 0; h < H; ++h)
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j)
+          rvt[((size_t)h * d + j) * d + i] = R_V[((size_t)h * d + i) * d + j];
+    hipStream_t s = (hipStream_t)stream;
+    size_t rb = (size_t)H * d * d * 4, cb = (size_t)H * d * 4;
+    hipError_t e = hipMemcpyAsync((void *)D.RK, R_K, rb, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync((void *)D.RV, R_V, rb, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync((void *)D.RVt, rvt.data(), rb, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync((void *)D.clipK, clip_K, cb, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync((void *)D.clipV, clip_V, cb, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "copying rotation/clip tables");
+    }
+  }
+  *out = p;
+  return ok();
+}
+
+int oscar_pool_destroy(oscar_pool *pool) {
+  if (!pool) return fail(OSCAR_EINVAL, "pool is NULL");
+  delete pool;
+  return ok();
+}
+
+static int check_seq(const oscar_pool *p, int32_t seq) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (seq < 0 || seq >= p->cfg.max_seqs)
+    return fail(OSCAR_EINVAL, "sequence id %d outside [0, %d)", seq, p->cfg.max_seqs);
+  return OSCAR_OK;
+}
+
+int oscar_prefill(oscar_pool *p, int32_t seq, const uint16_t *k, const uint16_t *v, int32_t L,
+                  void *stream) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (p->len[seq] != 0 || !p->table[seq].empty())
+    return fail(OSCAR_EINVAL, "sequence %d is not empty", seq);
+  if (L < 0 || L > (1 << 30)) return fail(OSCAR_EINVAL, "prompt length %d is invalid", L);
+  if (L == 0) return ok();
+  if (!p->host_only && (!k || !v)) return fail(OSCAR_EINVAL, "NULL k or v");
+  int64_t n_hist = std::max(0, L - kWindow);
+  int np = pages_for(n_hist);
+  if (np > p->cfg.max_pages_per_seq)
+    return fail(OSCAR_ERANGE, "sequence %d needs %d pages > max_pages_per_seq %d", seq, np,
+                p->cfg.max_pages_per_seq);
+  if (np > p->n_free())
+    return fail(OSCAR_ENOMEM, "sequence %d needs %d pages, %lld free", seq, np,
+                (long long)p->n_free());
+  std::vector<int32_t> row(np);
+  size_t head0 = p->free_head;
+  for (int i = 0; i < np; ++i) row[i] = p->pop();
+  if (!p->host_only) {
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (np)
+      e = hipMemcpyAsync(p->dev.page_table + (size_t)seq * p->cfg.max_pages_per_seq, row.data(),
+                         np * sizeof(int32_t), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = launch_prefill(p->dev, seq, k, v, L, s);
+    if (e == hipSuccess && np) e = hipStreamSynchronize(s); // `row` is released on return
+    if (e != hipSuccess) {
+      p->free_head = head0;
+      return hip_fail(e, "prefill");
+    }
+  }
+  p->table[seq] = std::move(row);
+  p->len[seq] = L;
+  return ok();
+}
+
+int oscar_append_evict(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
+                       const uint16_t *v_new, void *stream) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (n < 0) return fail(OSCAR_EINVAL, "n = %d < 0", n);
+  if (n == 0) return ok();
+  if (!seq_ids) return fail(OSCAR_EINVAL, "seq_ids is NULL");
+  if (!p->host_only && (!k_new || !v_new)) return fail(OSCAR_EINVAL, "NULL k_new or v_new");
+  std::vector<int32_t> sorted(seq_ids, seq_ids + n);
+  std::sort(sorted.begin(), sorted.end());
+  for (int i = 0; i < n; ++i) {
+    int rc = check_seq(p, sorted[i]);
+    if (rc) return rc;
+    if (i && sorted[i] == sorted[i - 1])
+      return fail(OSCAR_EINVAL, "sequence id %d repeated in one append", sorted[i]);
+  }
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    int32_t s = seq_ids[i], L = p->len[s];
+    if (L >= (1 << 30)) return fail(OSCAR_ERANGE, "sequence %d is at the length limit", s);
+    if (L >= kWindow && (L - kWindow) % kPage == 0) {
+      int np = (L - kWindow) / kPage + 1;
+      if (np > p->cfg.max_pages_per_seq)
+        return fail(OSCAR_ERANGE, "sequence %d would need %d pages > max_pages_per_seq %d", s, np,
+                    p->cfg.max_pages_per_seq);
+      ++need;
+    }
+  }
+  if (need > p->n_free())
+    return fail(OSCAR_ENOMEM, "append needs %lld new pages, %lld free", (long long)need,
+                (long long)p->n_free());
+  // Build the launches, taking pages in seq_ids order.
+  size_t head0 = p->free_head;
+  std::vector<AppendBatch> batches;
+  for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
+    AppendBatch b;
+    b.n = std::min(kMaxBatch, n - i0);
+    for (int e = 0; e < b.n; ++e) {
+      int32_t s = seq_ids[i0 + e], L = p->len[s];
+      b.seq[e] = s;
+      b.len[e] = L;
+      b.new_page[e] = (L >= kWindow && (L - kWindow) % kPage == 0) ? p->pop() : -1;
+    }
+    batches.push_back(b);
+  }
+  if (!p->host_only) {
+    for (size_t i = 0; i < batches.size(); ++i) {
+      const AppendBatch &b = batches[i];
+      hipError_t e = launch_append(p->dev, b, k_new + (size_t)i * kMaxBatch * p->cfg.num_kv_heads *
+                                                          p->cfg.head_dim,
+                                   v_new + (size_t)i * kMaxBatch * p->cfg.num_kv_heads *
+                                               p->cfg.head_dim,
+                                   (hipStream_t)stream, p->prof.next(2));
+      if (e != hipSuccess) {
+        if (i == 0) p->free_head = head0;  // nothing was enqueued
+        else {
+          // earlier launches are in flight: keep their effect in the mirror
+          for (size_t j = 0; j < i; ++j)
+            for (int q = 0; q < batches[j].n; ++q) {
+              int s = batches[j].seq[q];
+              if (batches[j].new_page[q] >= 0) p->table[s].push_back(batches[j].new_page[q]);
+              p->len[s] += 1;
+            }
+        }
+        return hip_fail(e, "append launch");
+      }
+    }
+  }
+  for (const AppendBatch &b : batches)
+    for (int e = 0; e < b.n; ++e) {
+      if (b.new_page[e] >= 0) p->table[b.seq[e]].push_back(b.new_page[e]);
+      p->len[b.seq[e]] += 1;
+    }
+  p->compact();
+  return ok();
+}
+
+int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *q, float *out,
+                      float softmax_scale, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (p->host_only) return fail(OSCAR_EINVAL, "decode on a host-only pool");
+  if (n < 0) return fail(OSCAR_EINVAL, "n = %d < 0", n);
+  if (n == 0) return ok();
+  if (!seq_ids || !q || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
+  if (!std::isfinite(softmax_scale)) return fail(OSCAR_EINVAL, "softmax_scale is not finite");
+  for (int i = 0; i < n; ++i) {
+    int rc = check_seq(p, seq_ids[i]);
+    if (rc) return rc;
+    if (p->len[seq_ids[i]] < 1) return fail(OSCAR_EINVAL, "sequence %d is empty", seq_ids[i]);
+  }
+  const int Hq = p->cfg.num_q_heads, Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim;
+  const int g = Hq / Hkv;
+  std::vector<DecodeBatch> batches;
+  size_t need = 0;
+  for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
+    DecodeBatch b;
+    b.n = std::min(kMaxBatch, n - i0);
+    int64_t total = 0;
+    int max_np = 0;
+    for (int e = 0; e < b.n; ++e) {
+      int32_t s = seq_ids[i0 + e];
+      b.seq[e] = s;
+      b.len[e] = p->len[s];
+      int np = pages_for(std::max(0, b.len[e] - kWindow));
+      total += np;
+      max_np = std::max(max_np, np);
+    }
+    b.pages_per_split = choose_pages_per_split(total, max_np, Hkv);
+    b.split_prefix[0] = 0;
+    for (int e = 0; e < b.n; ++e) {
+      int np = pages_for(std::max(0, b.len[e] - kWindow));
+      b.split_prefix[e + 1] = b.split_prefix[e] + (np + b.pages_per_split - 1) / b.pages_per_split;
+    }
+    b.hist_blocks = b.split_prefix[b.n] * Hkv;
+    need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
+    batches.push_back(b);
+  }
+  if (workspace_bytes < need)
+    return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  for (size_t i = 0; i < batches.size(); ++i) {
+    KernelTimer tm = p->prof.next(0), tg = p->prof.next(1);
+    hipError_t e = launch_decode(p->dev, batches[i], q + i * (size_t)kMaxBatch * Hq * d,
+                                 out + i * (size_t)kMaxBatch * Hq * d, softmax_scale,
+                                 (float *)workspace, (hipStream_t)stream, tm, tg);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  return ok();
+}
+
+int oscar_release_seq(oscar_pool *p, int32_t seq) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  for (int32_t pg : p->table[seq]) p->free_list.push_back(pg);
+  p->table[seq].clear();
+  p->len[seq] = 0;
+  return ok();
+}
+
+int oscar_seq_length(const oscar_pool *p, int32_t seq, int32_t *L) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (!L) return fail(OSCAR_EINVAL, "L is NULL");
+  *L = p->len[seq];
+  return ok();
+}
+
+int oscar_page_table(const oscar_pool *p, int32_t seq, int32_t *pages, int32_t capacity,
+                     int32_t *n_pages) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (!n_pages) return fail(OSCAR_EINVAL, "n_pages is NULL");
+  const auto &row = p->table[seq];
+  if ((size_t)capacity < row.size() || (row.size() && !pages))
+    return fail(OSCAR_EINVAL, "capacity %d < %zu pages", capacity, row.size());
+  std::copy(row.begin(), row.end(), pages);
+  *n_pages = (int32_t)row.size();
+  return ok();
+}
+
+int oscar_free_pages(const oscar_pool *p, int32_t *n_free) {
+  if (!p || !n_free) return fail(OSCAR_EINVAL, "NULL argument");
+  *n_free = (int32_t)p->n_free();
+  return ok();
+}
+
+int oscar_export_history(oscar_pool *p, int32_t seq, int32_t first, int32_t count, uint8_t *codes,
+                         uint16_t *params, void *stream) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (p->host_only) return fail(OSCAR_EINVAL, "export from a host-only pool");
+  int64_t n_hist = std::max(0, p->len[seq] - kWindow);
+  if (first < 0 || count < 0 || first + (int64_t)count > n_hist)
+    return fail(OSCAR_EINVAL, "history range [%d, %d) outside [0, %lld)", first, first + count,
+                (long long)n_hist);
+  if (count == 0) return ok();
+  if (!codes || !params) return fail(OSCAR_EINVAL, "NULL output");
+  const int H = p->cfg.num_kv_heads, d = p->cfg.head_dim, G = p->cfg.group_size;
+  const int bb = p->dev.block_bytes;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "export sync");
+  std::vector<uint8_t> page((size_t)H * bb);
+  int cur = -1;
+  for (int64_t i = first; i < first + count; ++i) {
+    int pg_idx = (int)(i / kPage), t = (int)(i % kPage);
+    if (pg_idx != cur) {
+      int pg = p->table[seq][pg_idx];
+      e = hipMemcpy(page.data(), p->dev.pages + (size_t)pg * H * bb, page.size(), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "export copy");
+      cur = pg_idx;
+    }
+    for (int h = 0; h < H; ++h) {
+      const uint8_t *blk = page.data() + (size_t)h * bb;
+      size_t o = (size_t)(i - first) * H + h;
+      uint8_t *ck = codes + (o * 2 + 0) * (d / 4), *cv = codes + (o * 2 + 1) * (d / 4);
+      std::memset(ck, 0, d / 4);
+      std::memset(cv, 0, d / 4);
+      for (int c = 0; c < d; ++c) {
+        uint32_t kw, vw;
+        std::memcpy(&kw, blk + kcode_dword_off(d, t, (c % 64) / 16, c / 64), 4);
+        std::memcpy(&vw, blk + vcode_dword_off(d, t / 16, c), 4);
+        uint32_t kc = (kw >> (2 * (c % 16))) & 3, vc = (vw >> (2 * (t % 16))) & 3;
+        ck[c / 4] |= kc << (2 * (c % 4));
+        cv[c / 4] |= vc << (2 * (c % 4));
+      }
+      for (int gi = 0; gi < d / G; ++gi) {
+        std::memcpy(params + ((o * 2 + 0) * (d / G) + gi) * 2, blk + kparam_off(d, G, t, gi), 4);
+        std::memcpy(params + ((o * 2 + 1) * (d / G) + gi) * 2, blk + vparam_off(d, G, t, gi), 4);
+      }
+    }
+  }
+  return ok();
+}
+
+int oscar_export_window(oscar_pool *p, int32_t seq, uint16_t *sink_k, uint16_t *sink_v,
+                        uint16_t *recent_k, uint16_t *recent_v, void *stream) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (p->host_only) return fail(OSCAR_EINVAL, "export from a host-only pool");
+  if (!sink_k || !sink_v || !recent_k || !recent_v) return fail(OSCAR_EINVAL, "NULL output");
+  const int H = p->cfg.num_kv_heads, d = p->cfg.head_dim;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "export sync");
+  struct Part {
+    const uint16_t *src;
+    uint16_t *dst;
+    int slots;
+  } parts[4] = {{p->dev.sinkK, sink_k, kSink},
+                {p->dev.sinkV, sink_v, kSink},
+                {p->dev.recentK, recent_k, kRecent},
+                {p->dev.recentV, recent_v, kRecent}};
+  for (const Part &pt : parts) {
+    std::vector<uint16_t> tmp((size_t)H * pt.slots * d);
+    e = hipMemcpy(tmp.data(), pt.src + (size_t)seq * H * pt.slots * d, tmp.size() * 2,
+                  hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "export copy");
+    for (int h = 0; h < H; ++h)
+      for (int s = 0; s < pt.slots; ++s)
+        std::memcpy(pt.dst + ((size_t)s * H + h) * d, tmp.data() + ((size_t)h * pt.slots + s) * d, d * 2);
+  }
+  return ok();
+}
+
+int oscar_profile_begin(oscar_pool *p, int32_t max_calls) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (p->host_only) return fail(OSCAR_EINVAL, "profiling a host-only pool");
+  if (max_calls < 1 || max_calls > (1 << 16)) return fail(OSCAR_EINVAL, "max_calls %d outside [1, 65536]", max_calls);
+  p->prof.release();
+  for (auto &v : p->prof.ev) {
+    v.resize(2 * (size_t)max_calls);
+    for (hipEvent_t &e : v) {
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) {
+        e = nullptr;
+        p->prof.release();
+        return hip_fail(r, "hipEventCreate");
+      }
+    }
+  }
+  p->prof.cap = max_calls;
+  p->prof.on = true;
+  return ok();
+}
+
+int oscar_profile_end(oscar_pool *p, oscar_profile *out) {
+  if (!p || !out) return fail(OSCAR_EINVAL, "NULL argument");
+  if (!p->prof.on) return fail(OSCAR_EINVAL, "profiling was not started");
+  float ms[3] = {0.f, 0.f, 0.f};
+  for (int k = 0; k < 3; ++k)
+    for (int i = 0; i < p->prof.used[k]; ++i) {
+      hipError_t r = hipEventSynchronize(p->prof.ev[k][2 * i + 1]);
+      float t = 0.f;
+      if (r == hipSuccess) r = hipEventElapsedTime(&t, p->prof.ev[k][2 * i], p->prof.ev[k][2 * i + 1]);
+      if (r != hipSuccess) {
+        p->prof.release();
+        return hip_fail(r, "reading profile events");
+      }
+      ms[k] += t;
+    }
+  out->n_decode_main = p->prof.used[0];
+  out->ms_decode_main = ms[0];
+  out->n_decode_merge = p->prof.used[1];
+  out->ms_decode_merge = ms[1];
+  out->n_append = p->prof.used[2];
+  out->ms_append = ms[2];
+  p->prof.release();
+  return ok();
+}
+
+int oscar_build_rotation(int32_t d, const float *U, float *R) {
+  if (d < 1 || d > 1024 || (d & (d - 1))) return fail(OSCAR_EINVAL, "d = %d is not a power of two <= 1024", d);
+  if (!U || !R) return fail(OSCAR_EINVAL, "NULL argument");
+  int bits = 0;
+  while ((1 << bits) < d) ++bits;
+  std::vector<double> row(d);
+  const double sq = std::sqrt((double)d);
+  for (int i = 0; i < d; ++i) {
+    for (int k = 0; k < d; ++k) row[k] = U[(size_t)i * d + k];
+    // row . H (Sylvester order) by the fast Walsh-Hadamard butterflies
+    for (int len = 1; len < d; len <<= 1)
+      for (int b = 0; b < d; b += 2 * len)
+        for (int j = b; j < b + len; ++j) {
+          double a = row[j], c = row[j + len];
+          row[j] = a + c;
+          row[j + len] = a - c;
+        }
+    // (U H Pi)[i][j] = (U H)[i][bitrev(j)]
+    for (int j = 0; j < d; ++j) {
+      int r = 0;
+      for (int t = 0; t < bits; ++t) r |= ((j >> t) & 1) << (bits - 1 - t);
+      R[(size_t)i * d + j] = (float)(row[r] / sq);
+    }
+  }
+  return ok();
+}
+
+int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R, double pct, float *clip) {
+  if (d < 1 || d > 1024) return fail(OSCAR_EINVAL, "bad d = %d", d);
+  if (n < 1 || !x || !R || !clip) return fail(OSCAR_EINVAL, "bad arguments");
+  if (!(pct >= 0.0 && pct <= 100.0)) return fail(OSCAR_EINVAL, "percentile %g outside [0, 100]", pct);
+  std::vector<float> y((size_t)n * d);
+  for (int64_t t = 0; t < n; ++t)
+    for (int j = 0; j < d; ++j) {
+      float acc = 0.0f;
+      for (int i = 0; i < d; ++i) {
+        uint32_t u = (uint32_t)x[(size_t)t * d + i] << 16;
+        float xf;
+        std::memcpy(&xf, &u, 4);
+        acc = std::fmaf(xf, R[(size_t)i * d + j], acc);
+      }
+      y[(size_t)j * n + t] = std::fabs(acc);
+    }
+  const double h = (double)(n - 1) * (pct / 100.0);
+  const int64_t k = (int64_t)std::floor(h);
+  for (int j = 0; j < d; ++j) {
+    float *col = y.data() + (size_t)j * n;
+    std::sort(col, col + n);
+    double lo = col[k], hi = col[std::min<int64_t>(k + 1, n - 1)];
+    clip[j] = (float)(lo + (h - (double)k) * (hi - lo));
+  }
+  return ok();
+}
+
+} // extern "C"

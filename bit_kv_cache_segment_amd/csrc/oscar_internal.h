@@ -1,0 +1,110 @@
+// Internal definitions shared by the host library and the HIP kernels:
+// the device view of a pool, the byte layout of a history page, and the
+// small by-value argument blocks kernels receive.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kSink = 64;      // BF16 attention sink tokens
+constexpr int kRecent = 256;   // BF16 recent window tokens (a ring of slots)
+constexpr int kWindow = kSink + kRecent;
+constexpr int kPage = 64;      // history tokens per page
+constexpr int kMaxBatch = 256; // sequences per kernel launch (by-value metadata)
+
+// Device-side view of a pool.  All arrays live in the caller's pool buffer.
+struct PoolDev {
+  const float *RK;     // [Hkv][d][d]  x_rot = x . R_K
+  const float *RV;     // [Hkv][d][d]
+  const float *RVt;    // [Hkv][d][d]  transpose of R_V (de-rotation, coalesced)
+  const float *clipK;  // [Hkv][d]
+  const float *clipV;  // [Hkv][d]
+  int32_t *page_table; // [max_seqs][maxp]
+  uint16_t *sinkK;     // [max_seqs][Hkv][64][d] bf16
+  uint16_t *sinkV;
+  uint16_t *recentK;   // [max_seqs][Hkv][256][d] bf16, slot = (pos - 64) % 256
+  uint16_t *recentV;
+  uint8_t *pages;      // [num_pages][Hkv][block_bytes]
+  int32_t Hq, Hkv, d, G, maxp;
+  int32_t block_bytes; // bytes of one (page, kv head) block
+};
+
+// ---------------------------------------------------------------------------
+// History page layout.  One page holds 64 consecutive history tokens of one
+// sequence for every kv head; the (page, head) block is contiguous:
+//
+//   [K codes 16d B][V codes 16d B][K params 256 d/G B][V params 256 d/G B]
+//
+// K codes, token-major in four channel quarters ("quads").  The 16
+// channels {64m + 16r + k : k < 16} of token t form one little-endian
+// dword (channel 64m+16r+k in bits 2k..2k+1) at byte
+//      r * 4d + t * (d/16) + 4m            (r = 0..3, m = 0..d/64-1).
+// A lane that owns (quad r, tokens t..t+3) reads d/4 contiguous bytes.
+//
+// V codes, channel-major in 16-token blocks.  The 16 tokens
+// {16 tb + k : k < 16} of channel c form one dword (token 16tb+k in bits
+// 2k..2k+1) at byte   16d + tb * 4d + 4 * sigma(c),
+// sigma(c) = (d/16) * (c % 16) + c / 16, so that the d/16 dwords a lane
+// needs for channels {c : c % 16 == n} are contiguous.
+//
+// Params: fp16 (scale, zero) of token t, group g at byte
+//      32d + 4 (t * d/G + g)               (K)
+//      32d + 256 d/G + 4 (t * d/G + g)     (V)
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int block_bytes_for(int d, int G) { return 32 * d + 512 * d / G; }
+__host__ __device__ inline int kcode_dword_off(int d, int t, int r, int m) {
+  return r * 4 * d + t * (d / 16) + 4 * m;
+}
+__host__ __device__ inline int vsigma(int d, int c) { return (d / 16) * (c % 16) + c / 16; }
+__host__ __device__ inline int vcode_dword_off(int d, int tb, int c) {
+  return 16 * d + tb * 4 * d + 4 * vsigma(d, c);
+}
+__host__ __device__ inline int kparam_off(int d, int G, int t, int g) {
+  return 32 * d + 4 * (t * (d / G) + g);
+}
+__host__ __device__ inline int vparam_off(int d, int G, int t, int g) {
+  return 32 * d + 256 * d / G + 4 * (t * (d / G) + g);
+}
+
+// By-value metadata of one append launch (<= kMaxBatch sequences).
+struct AppendBatch {
+  int32_t n;
+  int32_t seq[kMaxBatch];
+  int32_t len[kMaxBatch];      // length before the append
+  int32_t new_page[kMaxBatch]; // page taken by this append, or -1
+};
+
+// By-value metadata of one decode launch (<= kMaxBatch sequences).
+struct DecodeBatch {
+  int32_t n;
+  int32_t pages_per_split;     // history pages per split (multiple of 4)
+  int32_t hist_blocks;         // split blocks: split_prefix[n] * Hkv
+  int32_t seq[kMaxBatch];
+  int32_t len[kMaxBatch];
+  int32_t split_prefix[kMaxBatch + 1]; // exclusive prefix of splits per sequence
+};
+
+// Optional per-kernel timing: when `on`, a launch wrapper records ev[0]
+// before and ev[1] after the kernel on its stream.
+struct KernelTimer {
+  bool on = false;
+  hipEvent_t ev[2];
+};
+
+hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const uint16_t *v,
+                          int L, hipStream_t s);
+hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *k_new,
+                         const uint16_t *v_new, hipStream_t s, const KernelTimer &t);
+hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out,
+                         float scale, float *ws, hipStream_t s, const KernelTimer &t_main,
+                         const KernelTimer &t_merge);
+
+// Workspace (floats) for one decode launch: window partials for kMaxBatch
+// sequences plus split partials.
+inline size_t decode_ws_floats(int Hq, int d, int n, long hist_blocks, int g) {
+  return (size_t)n * Hq * (d + 2) + (size_t)hist_blocks * g * (d + 2);
+}
+
+} // namespace oscar

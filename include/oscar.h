@@ -1,0 +1,222 @@
+/*
+ * oscar.h — C ABI of the MI355X (gfx950) implementation of OSCAR's
+ * three-segment 2-bit KV cache: the eviction path (rotate, clip, quantize,
+ * pack) and decode attention over the segmented pool.
+ *
+ * Source of the method: the news article on OSCAR "Beyond TurboQuant:
+ * Together AI brings 2-bit KV Cache to real serving" (sanyangsrq.com),
+ *   [A] section "OSCAR aims the rotation at attention": the rotation is
+ *       R = U . Hadamard . bit-reversal, with R and the clip thresholds fixed
+ *       offline per layer and head and reused unchanged at inference;
+ *   [B] section "From offline calibration to online inference": the token
+ *       pool is BF16 sink (64 tokens) | INT2 history | BF16 recent
+ *       (256 tokens); new tokens enter the recent window; the oldest recent
+ *       token is rotated, clipped, quantized and packed into the history,
+ *       four 2-bit values per byte; decode runs an INT2 kernel (unpack,
+ *       scale/zero-point dequantization, float accumulation) and a BF16
+ *       kernel over sink and recent, and merges the two with an online
+ *       softmax; the layout works with a paged KV cache;
+ *   [C] section "Not better vector compression but protecting attention":
+ *       2-bit integers have only four levels.
+ * Readings where the article is silent (group-wise fp16 scale and zero,
+ * per-channel symmetric clipping, row-vector rotation x . R, page size,
+ * allocation order) are fixed below and in the design notes.
+ *
+ * Conventions for every function:
+ *   - return 0 on success or a negative OSCAR_E* code; oscar_last_error()
+ *     then describes the failure (thread-local, valid until the next call
+ *     on the same thread);
+ *   - every argument is validated on the host before anything is enqueued;
+ *     a failing call changes no host or device state;
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory owned by the caller; the library
+ *     never allocates device memory and never frees caller memory;
+ *   - `stream` is a hipStream_t (NULL = the default stream); device work is
+ *     enqueued asynchronously on it unless stated otherwise;
+ *   - bf16 and fp16 values are passed as their uint16_t bit patterns;
+ *   - a pool is not thread-safe: use it from one thread and one stream at a
+ *     time.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_SINK_TOKENS   64   /* [B] BF16 attention sink                       */
+#define OSCAR_RECENT_TOKENS 256  /* [B] BF16 recent window                         */
+#define OSCAR_PAGE_TOKENS   64   /* history tokens per page of the paged pool     */
+#define OSCAR_MAX_BATCH_PER_LAUNCH 256
+
+#define OSCAR_OK       0
+#define OSCAR_EHIP    (-5)   /* a HIP runtime call failed                          */
+#define OSCAR_ENOMEM  (-12)  /* the pool has too few free pages                    */
+#define OSCAR_EINVAL  (-22)  /* invalid argument or shape                          */
+#define OSCAR_ERANGE  (-34)  /* a sequence would exceed max_pages_per_seq pages    */
+
+/* Pool flag: keep only the host bookkeeping (lengths, page tables, free
+ * list); never touch device memory.  For capacity planning and for testing
+ * the host logic without a GPU.  Decode and export then fail with EINVAL. */
+#define OSCAR_POOL_HOST_ONLY 1u
+
+typedef struct oscar_pool oscar_pool;  /* opaque, host side */
+
+typedef struct oscar_pool_config {
+    int32_t  max_seqs;          /* sequence ids are 0 .. max_seqs-1                  */
+    int32_t  num_q_heads;       /* Hq                                                */
+    int32_t  num_kv_heads;      /* Hkv, Hq % Hkv == 0, Hq / Hkv <= 16                */
+    int32_t  head_dim;          /* d: 64 or 128                                      */
+    int32_t  group_size;        /* G: 64 or 128 channels per scale/zero, G <= d      */
+    int32_t  num_pages;         /* history pages in the pool (>= 0)                  */
+    int32_t  max_pages_per_seq; /* page-table width                                  */
+    uint32_t flags;             /* 0 or OSCAR_POOL_HOST_ONLY                         */
+    uint64_t page_shuffle_seed; /* seeds the free-list order                         */
+} oscar_pool_config;
+
+/* Bytes of device memory a pool with this configuration needs (its layout:
+ * rotation and clip tables, page table, sink and recent windows for every
+ * sequence slot, and num_pages history pages).  Host only. */
+int oscar_pool_bytes(const oscar_pool_config *cfg, size_t *device_bytes);
+
+/* Bytes of device workspace oscar_decode_attn needs for batches of up to
+ * max_batch sequences.  Host only. */
+int oscar_decode_workspace_bytes(const oscar_pool_config *cfg, int32_t max_batch,
+                                 size_t *bytes);
+
+/* Create a pool in caller-owned device memory `device_buf` (at least
+ * oscar_pool_bytes bytes, 256-byte aligned).
+ *   R_K, R_V:      host fp32 [Hkv][d][d], row-major; a token x (row vector)
+ *                  is stored rotated as x . R ([A]);
+ *   clip_K, clip_V host fp32 [Hkv][d]; rotated channel j of head h is clipped
+ *                  to [-clip[h][j], clip[h][j]] before quantization ([A], [B]).
+ *                  Every threshold must be finite, > 0 and small enough that
+ *                  fp16(2 c / 3) is finite (the largest possible scale).
+ * The tables are copied into the pool (the call waits for the copy); the
+ * host arrays may be freed on return.  The free list is a Fisher-Yates
+ * shuffle of the page ids driven by SplitMix64(page_shuffle_seed); pages are
+ * handed out from its front.  With OSCAR_POOL_HOST_ONLY, device_buf, the
+ * tables and the stream are ignored (they may be NULL).
+ * Errors: EINVAL (shapes, null pointers, bad thresholds, buffer too small),
+ * EHIP. */
+int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t bytes,
+                      const float *R_K, const float *R_V,
+                      const float *clip_K, const float *clip_V,
+                      void *stream, oscar_pool **out);
+
+/* Destroy the host side of a pool (the device buffer stays the caller's). */
+int oscar_pool_destroy(oscar_pool *pool);
+
+/* Fill an empty sequence with a prompt of L tokens ([B]): positions
+ * 0..min(L,64)-1 go to the sink, the last min(L-64, 256) positions to the
+ * recent window, and the n_hist = max(0, L-320) positions in between are
+ * encoded into ceil(n_hist/64) history pages taken from the free list in
+ * history order.  k, v: device bf16 [L][Hkv][d].  Inputs may be released
+ * once the stream has passed this call.
+ * Errors: EINVAL (bad seq, sequence not empty, L < 0, null), ENOMEM, ERANGE. */
+int oscar_prefill(oscar_pool *pool, int32_t seq, const uint16_t *k,
+                  const uint16_t *v, int32_t L, void *stream);
+
+/* Append one token to each listed sequence ([B]).  For a sequence of length
+ * L before the call the token at position L goes to the sink (L < 64) or to
+ * recent slot (L-64) mod 256 (L >= 64).  When the recent window is full
+ * (L >= 320), the oldest recent token (position 64 + n_hist, n_hist = L-320,
+ * held in that same slot) is first rotated, clipped, quantized and packed
+ * into history index n_hist (page n_hist/64, slot n_hist%64); a new page is
+ * taken from the free list when n_hist % 64 == 0, sequences being served in
+ * the order of seq_ids.
+ *   seq_ids: host int32 [n], distinct;  k_new, v_new: device bf16 [n][Hkv][d].
+ * Errors: EINVAL (n < 0, bad or repeated id, null), ENOMEM, ERANGE. */
+int oscar_append_evict(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
+                       const uint16_t *k_new, const uint16_t *v_new, void *stream);
+
+/* Decode attention for one new query per listed sequence ([B]).  For query
+ * head h (kv head h / (Hq/Hkv)) the result is softmax attention with scale
+ * `softmax_scale` over every token of the sequence: sink and recent tokens
+ * as stored (bf16), history tokens as decoded, i.e. dequantized with their
+ * group scale and zero point and mapped back by R_V^T / R_K^T.  Internally
+ * the history is attended in the rotated basis (q . R_K, then acc . R_V^T),
+ * split over pages, and merged with the window by an online softmax.
+ *   seq_ids: host int32 [n] (every sequence non-empty);
+ *   q:       device bf16 [n][Hq][d];   out: device fp32 [n][Hq][d];
+ *   workspace: device, >= oscar_decode_workspace_bytes(cfg, n) bytes.
+ * Errors: EINVAL (bad id, empty sequence, workspace too small, null,
+ * host-only pool), EHIP. */
+int oscar_decode_attn(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
+                      const uint16_t *q, float *out, float softmax_scale,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Return a sequence's pages to the back of the free list (in page-table
+ * order) and set its length to 0.  Host only.  Errors: EINVAL. */
+int oscar_release_seq(oscar_pool *pool, int32_t seq);
+
+/* Current length of a sequence (host mirror).  Errors: EINVAL. */
+int oscar_seq_length(const oscar_pool *pool, int32_t seq, int32_t *L);
+
+/* Copy a sequence's page-table row (host mirror) into pages[capacity];
+ * *n_pages receives its length.  Errors: EINVAL (capacity too small). */
+int oscar_page_table(const oscar_pool *pool, int32_t seq, int32_t *pages,
+                     int32_t capacity, int32_t *n_pages);
+
+/* Number of pages currently on the free list.  Errors: EINVAL. */
+int oscar_free_pages(const oscar_pool *pool, int32_t *n_free);
+
+/* Copy history entries [first, first+count) of a sequence to host memory in
+ * a canonical layout independent of the physical pages:
+ *   codes:  uint8 [count][Hkv][2 (K,V)][d/4], four consecutive channels per
+ *           byte, first channel in the low bits;
+ *   params: uint16 [count][Hkv][2 (K,V)][d/G][2 (scale, zero)] fp16 bits.
+ * Synchronous: waits for `stream`.  Errors: EINVAL (range, host-only), EHIP. */
+int oscar_export_history(oscar_pool *pool, int32_t seq, int32_t first, int32_t count,
+                         uint8_t *codes, uint16_t *params, void *stream);
+
+/* Copy a sequence's BF16 windows to host memory: sink_k/sink_v
+ * [64][Hkv][d] (slot = position) and recent_k/recent_v [256][Hkv][d]
+ * (slot = (position - 64) mod 256); slots not holding a token are copied as
+ * they are.  Synchronous.  Errors: EINVAL, EHIP. */
+int oscar_export_window(oscar_pool *pool, int32_t seq, uint16_t *sink_k,
+                        uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v,
+                        void *stream);
+
+/* Offline: R = U . H . Pi ([A]) for one head, host fp32 U[d][d] -> R[d][d].
+ * H is the Sylvester-ordered Hadamard matrix scaled by 1/sqrt(d), Pi the
+ * bit-reversal permutation (Pi[i][j] = 1 iff j = bitrev(i)).  U . H_unscaled
+ * is formed with a fast Walsh-Hadamard transform in fp64 (exact when U lies
+ * on a fixed-point grid), divided by sqrt(d) in fp64 and rounded to fp32.
+ * d must be a power of two <= 1024.  Errors: EINVAL. */
+int oscar_build_rotation(int32_t d, const float *U, float *R);
+
+/* Offline: per-channel clip thresholds for one head:
+ * clip[j] = percentile(|(x R)[j]|, pct) over n host bf16 tokens x[n][d],
+ * with (x R) evaluated exactly as the eviction does (fp32 FMA chain) and
+ * the percentile interpolated linearly between order statistics in fp64:
+ * h = (n-1) pct/100, k = floor(h), a[k] + (h-k)(a[k+1]-a[k]).
+ * Errors: EINVAL. */
+int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R,
+                         double pct, float *clip);
+
+/* Kernel timing with HIP events recorded on the launch stream around each
+ * kernel of the pool's decode and append calls.  oscar_profile_begin
+ * creates event pairs for up to max_calls launches of each kernel (later
+ * launches go untimed); oscar_profile_end waits for the events, writes the
+ * number of timed launches and their summed durations (milliseconds), and
+ * releases the events.  Timing adds one event record before and after each
+ * launch.  Errors: EINVAL, EHIP. */
+typedef struct oscar_profile {
+    int32_t n_decode_main;   float ms_decode_main;   /* INT2 splits + BF16 window */
+    int32_t n_decode_merge;  float ms_decode_merge;  /* merge + de-rotation      */
+    int32_t n_append;        float ms_append;        /* append / eviction        */
+} oscar_profile;
+
+int oscar_profile_begin(oscar_pool *pool, int32_t max_calls);
+int oscar_profile_end(oscar_pool *pool, oscar_profile *out);
+
+const char *oscar_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OSCAR_H */

@@ -172,17 +172,19 @@ def _outlier_mask(outliers: np.ndarray, d: int, device) -> torch.Tensor:
 
 
 def kv_tokens(w: Workload, kind: int, seq: int, pos0: int, count: int,
-              device="cpu") -> torch.Tensor:
-    """bf16 [count][Hkv][d] tokens at positions pos0 .. pos0+count-1 of ``seq``."""
+              device="cpu", heads=None) -> torch.Tensor:
+    """bf16 [count][H][d] tokens at positions pos0 .. pos0+count-1 of ``seq``
+    for kv heads ``heads`` (default: all Hkv heads)."""
     assert 0 <= seq < MAX_SEQ_ID and 0 <= pos0 and pos0 + count <= (1 << POS_BITS)
     Hkv, d = w.num_kv_heads, w.head_dim
+    heads = list(range(Hkv)) if heads is None else list(heads)
     key = stream_key(w.seed(STREAM_K if kind == 0 else STREAM_V), 0)
     pos = torch.arange(pos0, pos0 + count, dtype=torch.int64, device=device)
-    head = torch.arange(Hkv, dtype=torch.int64, device=device)
+    head = torch.tensor(heads, dtype=torch.int64, device=device)
     ch = torch.arange(d, dtype=torch.int64, device=device)
     idx = (((seq << POS_BITS) + pos)[:, None, None] * Hkv + head[None, :, None]) * d + ch[None, None, :]
     vals = normals_f32(key, idx)
-    vals = vals * _outlier_mask(outlier_channels(w, kind), d, device)[None]
+    vals = vals * _outlier_mask(outlier_channels(w, kind), d, device)[heads][None]
     return vals.to(torch.bfloat16)
 
 
@@ -237,3 +239,17 @@ def random_orthogonal_u(w: Workload, kind: int) -> np.ndarray:
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """uint16 view (numpy) of a bf16 tensor's bit patterns (CPU copy)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def kv_tokens_at(w: Workload, kind: int, seqs, positions, device="cpu") -> torch.Tensor:
+    """bf16 [n][Hkv][d]: the token at positions[i] of sequence seqs[i], for each i."""
+    Hkv, d = w.num_kv_heads, w.head_dim
+    key = stream_key(w.seed(STREAM_K if kind == 0 else STREAM_V), 0)
+    s = torch.as_tensor(np.asarray(seqs, dtype=np.int64), device=device)
+    p = torch.as_tensor(np.asarray(positions, dtype=np.int64), device=device)
+    head = torch.arange(Hkv, dtype=torch.int64, device=device)
+    ch = torch.arange(d, dtype=torch.int64, device=device)
+    idx = (((s << POS_BITS) + p)[:, None, None] * Hkv + head[None, :, None]) * d + ch[None, None, :]
+    vals = normals_f32(key, idx)
+    vals = vals * _outlier_mask(outlier_channels(w, kind), d, device)[None]
+    return vals.to(torch.bfloat16)

@@ -1,0 +1,150 @@
+"""GPU parity of the HIP path against the CPU oracle on small pools that
+span several pages, ragged last pages and every segment boundary.  Codes,
+scale/zero, page tables and windows must be bit-exact; attention within
+2e-3 row-relative error."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_segment_amd as ok
+import harness
+import oracle
+import synth
+from gpu_common import check_history_codes, check_rows, check_windows, oracle_sequence
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = [1, 63, 64, 65, 300, 319, 320, 321, 383, 384, 385, 1000]
+SHAPES = {  # (Hq, Hkv, d, G)
+    "g8_d128_G64": (16, 2, 128, 64),
+    "g4_d128_G128": (8, 2, 128, 128),
+    "g1_d64_G64": (4, 4, 64, 64),
+    "g2_d64_G64": (4, 2, 64, 64),
+    "g16_d128_G128": (32, 2, 128, 128),
+}
+
+
+def _workload(name):
+    Hq, Hkv, d, G = SHAPES[name]
+    return synth.Workload("edge_" + name, 20 + list(SHAPES).index(name), len(EDGE_LENS), Hq, Hkv, d, G, 0, 0)
+
+
+def _pool(w, lengths, extra=0, seed=None, slack=0):
+    RK, RV, cK, cV = harness.tables(w)
+    cfg = harness.config_for(w, lengths, extra_tokens=extra, seed=seed, slack_pages=slack)
+    return ok.Pool(cfg, RK, RV, cK, cV, max_batch=len(lengths)), cfg
+
+
+def _model(cfg):
+    return oracle.PoolModel(cfg.num_pages, cfg.page_shuffle_seed, cfg.max_pages_per_seq)
+
+
+def _check_all_rows(w, out, lengths, step, seqs=None):
+    q = synth.bf16_bits(synth.queries(w, step, batch=len(lengths)))
+    worst = 0.0
+    for b, L in enumerate(lengths):
+        st, _, _ = oracle_sequence(w, b, L)
+        worst = max(worst, check_rows(out[b], st, q[b], w, list(range(w.num_q_heads))))
+    return worst
+
+
+def test_tiny_workload_prefill_and_decode():
+    w = synth.WORKLOADS["tiny"]
+    L = w.len_lo
+    pool, cfg = _pool(w, [L], slack=2)
+    harness.prefill_all(pool, w, [L])
+    m = _model(cfg)
+    m.prefill(0, L)
+    assert list(pool.page_table(0)) == m.table[0]
+    st, k, v = oracle_sequence(w, 0, L)
+    check_history_codes(pool, w, 0, st, range(w.num_kv_heads))
+    check_windows(pool, w, 0, L, k, v, range(w.num_kv_heads))
+    q = synth.queries(w, 0, device="cuda")
+    out = pool.decode([0], q.view(torch.uint16))
+    torch.cuda.synchronize()
+    check_rows(out[0], st, synth.bf16_bits(q.cpu())[0], w, list(range(w.num_q_heads)))
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_edge_lengths_prefill_then_fused_steps(shape):
+    w = _workload(shape)
+    lengths = list(EDGE_LENS)
+    steps = 70
+    pool, cfg = _pool(w, lengths, extra=steps, slack=3)
+    m = _model(cfg)
+    harness.prefill_all(pool, w, lengths)
+    for b, L in enumerate(lengths):
+        m.prefill(b, L)
+    q = synth.queries(w, 0, device="cuda", batch=len(lengths))
+    out = pool.decode(list(range(len(lengths))), q.view(torch.uint16))
+    torch.cuda.synchronize()
+    _check_all_rows(w, out, lengths, 0)
+    rng = np.random.default_rng(5)
+    for step in range(1, steps + 1):
+        order = [int(x) for x in rng.permutation(len(lengths))]
+        k_new, v_new = harness.step_tokens(w, lengths, order)
+        pool.append(order, k_new, v_new)
+        m.append(order)
+        for b in order:
+            lengths[b] += 1
+        if step % 10 == 0 or step == 1:
+            q = synth.queries(w, step, device="cuda", batch=len(lengths))
+            # decode in a permuted order too: outputs follow seq_ids
+            out = pool.decode(order, q.view(torch.uint16)[order].contiguous())
+            torch.cuda.synchronize()
+            inv = np.argsort(order)
+            _check_all_rows(w, out[torch.as_tensor(inv, device="cuda")], lengths, step)
+    for b, L in enumerate(lengths):
+        assert pool.length(b) == L
+        assert list(pool.page_table(b)) == m.table[b]
+        st, k, v = oracle_sequence(w, b, L)
+        check_history_codes(pool, w, b, st, range(w.num_kv_heads))
+        check_windows(pool, w, b, L, k, v, range(w.num_kv_heads))
+
+
+def test_shuffle_invariance_and_determinism():
+    w = _workload("g8_d128_G64")
+    lengths = [1000, 700, 385, 64]
+    outs = []
+    for seed in (1, 2):
+        pool, cfg = _pool(w, lengths, seed=seed, slack=5)
+        harness.prefill_all(pool, w, lengths)
+        assert seed == 1 or list(pool.page_table(0)) != first_table
+        first_table = list(pool.page_table(0))
+        q = synth.queries(w, 3, device="cuda", batch=len(lengths)).view(torch.uint16)
+        a = pool.decode(list(range(4)), q)
+        b = pool.decode(list(range(4)), q)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        outs.append(a)
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_identical_queries_in_a_group_give_identical_rows():
+    w = _workload("g4_d128_G128")
+    pool, cfg = _pool(w, [900])
+    harness.prefill_all(pool, w, [900])
+    q = synth.queries(w, 1, device="cuda", batch=1)
+    q[0, 1:4] = q[0, 0]
+    out = pool.decode([0], q.view(torch.uint16).contiguous())
+    torch.cuda.synchronize()
+    for h in range(1, 4):
+        assert torch.equal(out[0, 0], out[0, h])
+
+
+def test_decode_rejects_small_workspace_and_empty_sequence():
+    w = _workload("g4_d128_G128")
+    pool, cfg = _pool(w, [500, 10])
+    harness.prefill_all(pool, w, [500, 10])
+    q = synth.queries(w, 0, device="cuda", batch=2).view(torch.uint16)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    small = torch.empty(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(ok.OscarError) as ei:
+        ok.oscar_decode_attn(pool.handle, [0, 1], q, out, 0.1, small)
+    assert ei.value.code == ok.EINVAL
+    pool.release(1)
+    with pytest.raises(ok.OscarError) as ei:
+        pool.decode([0, 1], q)
+    assert ei.value.code == ok.EINVAL
