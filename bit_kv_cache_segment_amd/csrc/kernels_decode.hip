@@ -7,16 +7,32 @@
 // sink and recent tokens; an online softmax merges the two results.
 //
 // Launches (one stream):
-//   decode_main_kernel: two block roles in one grid.
-//     * split blocks, one per (sequence, kv head, run of pages): rotate the
-//       g = Hq/Hkv queries by R_K, attend to the INT2 history in the rotated
-//       basis, write a partial (m, l, acc) per query head;
-//     * window blocks, one per (sequence, kv head): attend to the BF16 sink
-//       and recent tokens with the raw queries, write one partial.
-//   decode_merge_kernel: one block per (sequence, kv head): merge the split
+//   decode_main_kernel, two block roles in one grid:
+//     * window blocks (first in the grid), one per (sequence, kv head):
+//       attend to the BF16 sink and recent tokens with the raw queries;
+//     * split blocks, one per (sequence, kv head, run of history pages):
+//       rotate the g = Hq/Hkv queries by R_K and attend to the INT2 history
+//       in the rotated basis.
+//     Each block writes one partial (m, l, acc) per query head.
+//   decode_merge_kernel, one block per (sequence, kv head): merge the split
 //     partials, de-rotate the history accumulator by R_V^T, merge with the
 //     window partial, normalise, write fp32.
 // Softmax runs in base 2: logits are pre-multiplied by scale * log2(e).
+//
+// History split blocks (4 waves; each wave streams its own pages):
+//   QK^T on v_mfma_i32_16x16x64_i8.  The rotated query of each head is put
+//   on a fixed-point grid q_int = rint(q 2^E) with |q_int| <= 2^18 and split
+//   into three signed byte limbs; an MFMA row is one (head, limb).  2-bit
+//   codes become int8 operands with AND masks (5 VALU ops per 16 codes).
+//   The integer products are exact; recombining the limbs in fp32 leaves a
+//   relative error near 2^-18 of the query's largest element.
+//     logit = s_t * (q_int . code_t) 2^-E + z_t * sum(q)   per group.
+//   PV on v_mfma_f32_16x16x32_f16.  V codes are stored so that one AND with
+//   0x00030003 << 2i yields tokens (2i, 2i+1) of a 16-token block as two fp16
+//   sub-normals code * 4^e * 2^-24; the factor 4^-e, the token's V scale and
+//   a pool constant 2^pv_shift go into the fp16 softmax weight P' of the A
+//   operand, the 2^24 / 2^pv_shift is undone once at the end.  The zero-point
+//   term sum_t p_t z_t is accumulated on the VALU.
 #include "oscar_internal.h"
 
 namespace oscar {
@@ -26,10 +42,16 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-__device__ __forceinline__ float f16_val(uint32_t b) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-}
+__device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu)); }
+__device__ __forceinline__ float f16hi(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16)); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -40,59 +62,72 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// reductions over the 16 lanes of an aligned lane row
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Order LDS traffic of the lanes of one wave (no cross-wave barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ? 0.f : exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// shared memory
+// ---------------------------------------------------------------------------
 template <int D, int G, int GQ>
-struct Smem {
-  float qs[GQ][D];             // scaled (and, for history, rotated) queries
-  float qsum[GQ][D / G];       // per-group sums of the rotated queries
-  float P[kWaves][GQ][64];     // softmax numerators of the current tile
-  float vsz[kWaves][64][2 * (D / G)]; // V scale/zero of the current page
+struct HistSmem {
+  static constexpr int NG = D / G;
+  float qs[GQ][D];          // rotated queries times scale*log2(e)
+  float qsum[GQ][NG];       // per-group sums of qs
+  int qexp[GQ];             // fixed-point exponent E of each head
+  float alpha[kWaves][16];  // per-wave rescale factors of the PV rows
+  float zsum[kWaves][16][NG];
   float M[kWaves][GQ], L[kWaves][GQ];
-  float A[kWaves][GQ][D];      // per-wave accumulators for the block merge
+  union {
+    float qraw[GQ][D];                       // prologue
+    _Float16 P[kWaves][NG][16][64];          // page loop: P' rows per wave
+    float A[kWaves][GQ][D];                  // epilogue: per-wave accumulators
+  } u;
 };
 
-// Online-softmax update of one 64-token tile for one wave.  lg: this lane's
-// logits (-inf for an empty lane).  Writes the tile's numerators to P and
-// returns the rescale factor of each head through alpha.
-template <int GQ>
-__device__ __forceinline__ void softmax_tile(const float (&lg)[GQ], float (&m_run)[GQ], float (&l_run)[GQ],
-                                             float (&alpha)[GQ], float (*P)[64], int lane) {
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    const float mt = wave_max(lg[h]);
-    const float mnew = fmaxf(m_run[h], mt);
-    alpha[h] = exp2f(m_run[h] - mnew); // m_run = -inf at the start gives 0
-    const float pr = exp2f(lg[h] - mnew);
-    l_run[h] = l_run[h] * alpha[h] + wave_sum(pr);
-    m_run[h] = mnew;
-    P[h][lane] = pr;
-  }
-}
+template <int D, int GQ>
+struct WinSmem {
+  float qs[GQ][D];
+  float P[kWaves][GQ][64];
+  float M[kWaves][GQ], L[kWaves][GQ];
+  float A[kWaves][GQ][D];
+};
 
-// Merge the per-wave (m, l, acc) of a block and store one partial per head.
 template <int D, int G, int GQ>
-__device__ void block_merge_store(Smem<D, G, GQ> &sm, const float (&m_run)[GQ], const float (&l_run)[GQ],
-                                  const float (&acc)[GQ][D / 64], float *dst /*[GQ][D+2]*/) {
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    if (lane == 0) {
-      sm.M[w][h] = m_run[h];
-      sm.L[w][h] = l_run[h];
-    }
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) sm.A[w][h][lane + 64 * k] = acc[h][k];
-  }
-  __syncthreads();
+union MainSmem {
+  HistSmem<D, G, GQ> h;
+  WinSmem<D, GQ> w;
+};
+
+// Merge per-wave (M, L, A) in shared memory and store one partial per head.
+template <int D, int GQ>
+__device__ void block_merge_store(const float (*M)[GQ], const float (*L)[GQ], const float (*A)[GQ][D],
+                                  float *dst /*[GQ][D+2]*/) {
+  const int tid = threadIdx.x;
   for (int idx = tid; idx < GQ * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
     float m = -INFINITY;
-    for (int ww = 0; ww < kWaves; ++ww) m = fmaxf(m, sm.M[ww][h]);
+    for (int ww = 0; ww < kWaves; ++ww) m = fmaxf(m, M[ww][h]);
     float a = 0.f, l = 0.f;
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = sm.M[ww][h] == -INFINITY ? 0.f : exp2f(sm.M[ww][h] - m);
-      a += f * sm.A[ww][h][c];
-      l += f * sm.L[ww][h];
+      const float f = M[ww][h] == -INFINITY ? 0.f : exp2f(M[ww][h] - m);
+      a += f * A[ww][h][c];
+      l += f * L[ww][h];
     }
     float *o = dst + (size_t)h * (D + 2);
     o[c] = a;
@@ -103,16 +138,27 @@ __device__ void block_merge_store(Smem<D, G, GQ> &sm, const float (&m_run)[GQ], 
   }
 }
 
-template <int D, int G, int GQ>
-__global__ __launch_bounds__(kThreads) void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
-                                                               float qscale, float *__restrict__ ws) {
-  __shared__ Smem<D, G, GQ> sm;
+// ---------------------------------------------------------------------------
+// BF16 sink + recent window: one block per (sequence, kv head).  Lanes own
+// tokens for QK^T and channels for PV (fp32 VALU).
+// ---------------------------------------------------------------------------
+template <int D, int GQ>
+__device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
+                             float qscale, float *ws_win, int idx0) {
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
   const int Hkv = p.Hkv, Hq = p.Hq;
-  float *ws_win = ws;
-  float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
+  const int e = idx0 / Hkv, kv = idx0 % Hkv;
+  const int seq = b.seq[e], L = b.len[e];
+  const int n_sink = min(L, kSink), n_rec = min(max(L - kSink, 0), kRecent), n_win = n_sink + n_rec;
+  for (int idx = tid; idx < GQ * D; idx += kThreads)
+    sm.qs[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]) * qscale;
+  __syncthreads();
+  const uint16_t *sinkK = p.sinkK + ((size_t)seq * Hkv + kv) * kSink * D;
+  const uint16_t *sinkV = p.sinkV + ((size_t)seq * Hkv + kv) * kSink * D;
+  const uint16_t *recK = p.recentK + ((size_t)seq * Hkv + kv) * kRecent * D;
+  const uint16_t *recV = p.recentV + ((size_t)seq * Hkv + kv) * kRecent * D;
 
-  float m_run[GQ], l_run[GQ], alpha[GQ], acc[GQ][D / 64];
+  float m_run[GQ], l_run[GQ], acc[GQ][D / 64];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
     m_run[h] = -INFINITY;
@@ -120,175 +166,365 @@ __global__ __launch_bounds__(kThreads) void decode_main_kernel(PoolDev p, Decode
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) acc[h][k] = 0.f;
   }
-
-  if ((int)blockIdx.x < b.hist_blocks) {
-    // ---------------- INT2 history split ----------------
-    const int blk = blockIdx.x, kv = blk % Hkv, sidx = blk / Hkv;
-    int lo = 0, hi = b.n;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) / 2;
-      if (b.split_prefix[mid] <= sidx) lo = mid;
-      else hi = mid;
-    }
-    const int e = lo, s = sidx - b.split_prefix[e];
-    const int seq = b.seq[e], n_hist = b.len[e] - kWindow;
-    const int np = (n_hist + kPage - 1) / kPage;
-    const int p0 = s * b.pages_per_split, p1 = min(np, p0 + b.pages_per_split);
-
-    // q_rot = q . R_K, scaled by softmax_scale * log2(e)
-    float(*qraw)[D] = (float(*)[D]) & sm.A[0][0][0];
-    for (int idx = tid; idx < GQ * D; idx += kThreads)
-      qraw[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]);
-    __syncthreads();
-    const float *RK = p.RK + (size_t)kv * D * D;
-    for (int idx = tid; idx < GQ * D; idx += kThreads) {
-      const int h = idx / D, j = idx % D;
-      float a = 0.f;
-      for (int i = 0; i < D; ++i) a = fmaf(qraw[h][i], RK[i * D + j], a);
-      sm.qs[h][j] = a * qscale;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < GQ * (D / G); idx += kThreads) {
-      const int h = idx / (D / G), gi = idx % (D / G);
-      float a = 0.f;
-      for (int c = gi * G; c < (gi + 1) * G; ++c) a += sm.qs[h][c];
-      sm.qsum[h][gi] = a;
-    }
-    __syncthreads();
-
-    const int iters = (p1 - p0 + kWaves - 1) / kWaves;
-    for (int it = 0; it < iters; ++it) {
-      const int pi = p0 + it * kWaves + w;
-      const bool active = pi < p1;
-      const uint8_t *blkp = nullptr;
-      int ntok = 0;
-      if (active) {
-        const int page = p.page_table[(size_t)seq * p.maxp + pi];
-        blkp = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
-        ntok = min(kPage, n_hist - pi * kPage);
-      }
-      const int t = lane;
-      const bool valid = active && t < ntok;
-      if (active) {
-        float lg[GQ];
+  const int nch = (n_win + 63) / 64;
+  for (int ch = w; ch < nch; ch += kWaves) {
+    const int ntok = min(64, n_win - ch * 64);
+    const int u = ch * 64 + lane;
+    float lg[GQ];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) lg[h] = -INFINITY;
-        if (valid) {
-          float dot[GQ][D / G];
+    for (int h = 0; h < GQ; ++h) lg[h] = -INFINITY;
+    if (lane < ntok) {
+      const uint16_t *row = u < n_sink ? sinkK + (size_t)u * D : recK + (size_t)(u - n_sink) * D;
 #pragma unroll
-          for (int h = 0; h < GQ; ++h)
+      for (int h = 0; h < GQ; ++h) lg[h] = 0.f;
+#pragma unroll 4
+      for (int c8 = 0; c8 < D; c8 += 8) {
+        const u32x4 kw = *(const u32x4 *)(row + c8);
 #pragma unroll
-            for (int gi = 0; gi < D / G; ++gi) dot[h][gi] = 0.f;
+        for (int k = 0; k < 8; ++k) {
+          const float kc = __uint_as_float(k & 1 ? (kw[k / 2] & 0xffff0000u) : (kw[k / 2] << 16));
 #pragma unroll
-          for (int m = 0; m < D / 64; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t dw = *(const uint32_t *)(blkp + kcode_dword_off(D, t, r, m));
-#pragma unroll
-              for (int k = 0; k < 16; ++k) {
-                const int c = 64 * m + 16 * r + k;
-                const float fc = (float)((dw >> (2 * k)) & 3u);
-#pragma unroll
-                for (int h = 0; h < GQ; ++h) dot[h][c / G] = fmaf(sm.qs[h][c], fc, dot[h][c / G]);
-              }
-            }
-#pragma unroll
-          for (int h = 0; h < GQ; ++h) lg[h] = 0.f;
-#pragma unroll
-          for (int gi = 0; gi < D / G; ++gi) {
-            const uint32_t sz = *(const uint32_t *)(blkp + kparam_off(D, G, t, gi));
-            const float sc = f16_val(sz & 0xffffu), zp = f16_val(sz >> 16);
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) lg[h] += sc * dot[h][gi] + zp * sm.qsum[h][gi];
-          }
-#pragma unroll
-          for (int gi = 0; gi < D / G; ++gi) {
-            const uint32_t sz = *(const uint32_t *)(blkp + vparam_off(D, G, t, gi));
-            sm.vsz[w][t][2 * gi] = f16_val(sz & 0xffffu);
-            sm.vsz[w][t][2 * gi + 1] = f16_val(sz >> 16);
-          }
-        }
-        softmax_tile<GQ>(lg, m_run, l_run, alpha, sm.P[w], lane);
-#pragma unroll
-        for (int h = 0; h < GQ; ++h)
-#pragma unroll
-          for (int k = 0; k < D / 64; ++k) acc[h][k] *= alpha[h];
-      }
-      __syncthreads();
-      if (active) {
-#pragma unroll
-        for (int k = 0; k < D / 64; ++k) {
-          const int c = lane + 64 * k;
-          uint32_t vdw[4];
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) vdw[tb] = *(const uint32_t *)(blkp + vcode_dword_off(D, tb, c));
-          for (int tt = 0; tt < ntok; ++tt) {
-            const float code = (float)((vdw[tt / 16] >> (2 * (tt % 16))) & 3u);
-            const float v = fmaf(code, sm.vsz[w][tt][2 * (c / G)], sm.vsz[w][tt][2 * (c / G) + 1]);
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) acc[h][k] = fmaf(sm.P[w][h][tt], v, acc[h][k]);
-          }
+          for (int h = 0; h < GQ; ++h) lg[h] = fmaf(sm.qs[h][c8 + k], kc, lg[h]);
         }
       }
-      __syncthreads();
     }
-    block_merge_store<D, G, GQ>(sm, m_run, l_run, acc, ws_hist + (size_t)blk * GQ * (D + 2));
-  } else {
-    // ---------------- BF16 sink + recent window ----------------
-    const int idx0 = blockIdx.x - b.hist_blocks, e = idx0 / Hkv, kv = idx0 % Hkv;
-    const int seq = b.seq[e], L = b.len[e];
-    const int n_sink = min(L, kSink), n_rec = min(max(L - kSink, 0), kRecent), n_win = n_sink + n_rec;
-    for (int idx = tid; idx < GQ * D; idx += kThreads)
-      sm.qs[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]) * qscale;
-    __syncthreads();
-    const uint16_t *sinkK = p.sinkK + ((size_t)seq * Hkv + kv) * kSink * D;
-    const uint16_t *sinkV = p.sinkV + ((size_t)seq * Hkv + kv) * kSink * D;
-    const uint16_t *recK = p.recentK + ((size_t)seq * Hkv + kv) * kRecent * D;
-    const uint16_t *recV = p.recentV + ((size_t)seq * Hkv + kv) * kRecent * D;
-    const int nch = (n_win + 63) / 64;
-    const int iters = (nch + kWaves - 1) / kWaves;
-    for (int it = 0; it < iters; ++it) {
-      const int ch = it * kWaves + w;
-      const bool active = ch < nch;
-      const int ntok = active ? min(64, n_win - ch * 64) : 0;
-      if (active) {
-        const int u = ch * 64 + lane;
-        float lg[GQ];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) lg[h] = -INFINITY;
-        if (lane < ntok) {
-          const uint16_t *row = u < n_sink ? sinkK + (size_t)u * D : recK + (size_t)(u - n_sink) * D;
+    for (int h = 0; h < GQ; ++h) {
+      const float mt = wave_max(lg[h]);
+      const float mnew = fmaxf(m_run[h], mt);
+      const float alpha = exp2_or_zero(m_run[h] - mnew);
+      const float pr = exp2_or_zero(lg[h] - mnew);
+      l_run[h] = l_run[h] * alpha + wave_sum(pr);
+      m_run[h] = mnew;
+      sm.P[w][h][lane] = pr;
 #pragma unroll
-          for (int h = 0; h < GQ; ++h) lg[h] = 0.f;
-          for (int c = 0; c < D; ++c) {
-            const float kc = bf16f(row[c]);
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) lg[h] = fmaf(sm.qs[h][c], kc, lg[h]);
-          }
-        }
-        softmax_tile<GQ>(lg, m_run, l_run, alpha, sm.P[w], lane);
-#pragma unroll
-        for (int h = 0; h < GQ; ++h)
-#pragma unroll
-          for (int k = 0; k < D / 64; ++k) acc[h][k] *= alpha[h];
-      }
-      __syncthreads();
-      if (active) {
-        for (int tt = 0; tt < ntok; ++tt) {
-          const int u = ch * 64 + tt;
-          const uint16_t *row = u < n_sink ? sinkV + (size_t)u * D : recV + (size_t)(u - n_sink) * D;
-#pragma unroll
-          for (int k = 0; k < D / 64; ++k) {
-            const float v = bf16f(row[lane + 64 * k]);
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) acc[h][k] = fmaf(sm.P[w][h][tt], v, acc[h][k]);
-          }
-        }
-      }
-      __syncthreads();
+      for (int k = 0; k < D / 64; ++k) acc[h][k] *= alpha;
     }
-    block_merge_store<D, G, GQ>(sm, m_run, l_run, acc, ws_win + ((size_t)e * Hq + kv * GQ) * (D + 2));
+    wave_sync();
+    for (int tt = 0; tt < ntok; ++tt) {
+      const int uu = ch * 64 + tt;
+      const uint16_t *row = uu < n_sink ? sinkV + (size_t)uu * D : recV + (size_t)(uu - n_sink) * D;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        const float v = bf16f(row[lane + 64 * k]);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) acc[h][k] = fmaf(sm.P[w][h][tt], v, acc[h][k]);
+      }
+    }
+    wave_sync();
   }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    if (lane == 0) {
+      sm.M[w][h] = m_run[h];
+      sm.L[w][h] = l_run[h];
+    }
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) sm.A[w][h][lane + 64 * k] = acc[h][k];
+  }
+  __syncthreads();
+  block_merge_store<D, GQ>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * Hq + kv * GQ) * (D + 2));
+}
+
+// ---------------------------------------------------------------------------
+// INT2 history split block.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+struct PageRegs {
+  u32x4 kc[D / 64]; // K codes of tokens 4n..4n+3, quad r (D/4 bytes)
+  u32x4 vc[D / 64]; // V codes of channels {16j+n}, token block r (D/4 bytes)
+  u32x4 kp[D / G];  // K (scale, zero) of tokens 4n..4n+3
+  u32x4 vp[D / G];  // V (scale, zero)
+};
+
+template <int D, int G>
+__device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk, int n, int r) {
+  constexpr int NG = D / G;
+  const u32x4 *kc = (const u32x4 *)(blk + r * 4 * D + 4 * n * (D / 16));
+  const u32x4 *vc = (const u32x4 *)(blk + 16 * D + r * 4 * D + 4 * (D / 16) * n);
+  const u32x4 *kp = (const u32x4 *)(blk + 32 * D + 16 * NG * n);
+  const u32x4 *vp = (const u32x4 *)(blk + 32 * D + 256 * NG + 16 * NG * n);
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    pr.kc[i] = kc[i];
+    pr.vc[i] = vc[i];
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    pr.kp[g] = kp[g];
+    pr.vp[g] = vp[g];
+  }
+}
+
+template <int D, int G, int GQ>
+__device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
+                              float qscale, float *ws_hist, int blk) {
+  constexpr int NG = D / G;                // scale/zero groups per token
+  constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
+  constexpr int RT = GQ >= 4 ? GQ / 4 : 1; // MFMA row tiles of 4 heads x 4 limb rows
+  constexpr int NJ = D / 16;               // PV column tiles of 16 channels
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, r = lane >> 4;
+  const int Hkv = p.Hkv, Hq = p.Hq;
+  const int kv = blk % Hkv, sidx = blk / Hkv;
+  int lo = 0, hi = b.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (b.split_prefix[mid] <= sidx) lo = mid;
+    else hi = mid;
+  }
+  const int e = lo, s = sidx - b.split_prefix[e];
+  const int seq = b.seq[e], n_hist = b.len[e] - kWindow;
+  const int np = (n_hist + kPage - 1) / kPage;
+  const int p0 = s * b.pages_per_split, p1 = min(np, p0 + b.pages_per_split);
+
+  // ---- prologue: q_rot = (q . R_K) * scale * log2(e), its group sums and
+  // fixed-point exponent; rows of P' that no head owns stay zero.
+  for (int idx = tid; idx < GQ * D; idx += kThreads)
+    sm.u.qraw[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]);
+  for (int idx = tid; idx < kWaves * 16; idx += kThreads) sm.alpha[idx / 16][idx % 16] = 1.f;
+  __syncthreads();
+  const float *RK = p.RK + (size_t)kv * D * D;
+  for (int idx = tid; idx < GQ * D; idx += kThreads) {
+    const int h = idx / D, j = idx % D;
+    float a = 0.f;
+    for (int i = 0; i < D; ++i) a = fmaf(sm.u.qraw[h][i], RK[i * D + j], a);
+    sm.qs[h][j] = a * qscale;
+  }
+  __syncthreads();
+  if (tid < GQ * NG) {
+    const int h = tid / NG, g = tid % NG;
+    float a = 0.f;
+    for (int c = g * G; c < (g + 1) * G; ++c) a += sm.qs[h][c];
+    sm.qsum[h][g] = a;
+  } else if (tid >= 128 && tid < 128 + GQ) {
+    const int h = tid - 128;
+    float mx = 0.f;
+    for (int c = 0; c < D; ++c) mx = fmaxf(mx, fabsf(sm.qs[h][c]));
+    int ex = 0;
+    frexpf(mx, &ex);                      // mx = f 2^ex, f in [0.5, 1)
+    sm.qexp[h] = mx > 0.f ? 18 - ex : 0;  // |q 2^E| < 2^18
+  }
+  {
+    _Float16 *P = &sm.u.P[0][0][0][0];
+    for (int idx = tid; idx < kWaves * NG * 16 * 64; idx += kThreads) P[idx] = (_Float16)0.f;
+  }
+  __syncthreads();
+
+  // A operands of QK^T: lane (row m = n, k-quad r).  Row m = 4 hh + limb;
+  // register v of MFMA mi holds channels 64 mi + 16 r + 4 j + v (byte j),
+  // pre-multiplied by {16, 4, 1, 16}[v] to match the code masks below.
+  v4i Aq[RT][MI];
+  float kfac[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int h = rt * 4 + (n >> 2), lam = n & 3;
+    const bool live = h < GQ && lam < 3;
+    const int E = live ? sm.qexp[h] : 0;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int c = 64 * mi + 16 * r + 4 * j4 + v;
+          int X = 0;
+          if (live) {
+            const int qi = (int)rintf(ldexpf(sm.qs[h][c], E));
+            X = qi * (v == 1 ? 4 : (v == 2 ? 1 : 16));
+          }
+          const int a0 = (int)(int8_t)(X & 0xff);
+          const int X1 = (X - a0) >> 8;
+          const int a1 = (int)(int8_t)(X1 & 0xff);
+          const int a2 = (X1 - a1) >> 8;
+          const int limb = lam == 0 ? a0 : (lam == 1 ? a1 : a2);
+          word |= ((uint32_t)limb & 0xffu) << (8 * j4);
+        }
+        Aq[rt][mi][v] = (int)word;
+      }
+    }
+    const int hs = rt * 4 + r; // head of this lane in the logit layout
+    kfac[rt] = hs < GQ ? ldexpf(1.f, -(sm.qexp[hs] + 4)) : 0.f;
+  }
+  // per-token factor of P': 2^pv_shift * 4^-e(k), k = token within its
+  // 16-token block, e = pair index (k >> 1), or (k >> 1) - 5 past the shift
+  float pfac[4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const int k = (4 * n + T) & 15, i = k >> 1;
+    const int ee = i <= 4 ? i : i - 5;
+    pfac[T] = ldexpf(1.f, p.pv_shift - 2 * ee);
+  }
+
+  float m_run[RT], l_run[RT], zs[RT][NG];
+  v4f acc[NJ];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) zs[rt][g] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t *ptab = p.page_table + (size_t)seq * p.maxp;
+  const size_t hstride = (size_t)Hkv * p.block_bytes;
+  const size_t hoff = (size_t)kv * p.block_bytes;
+  PageRegs<D, G> cur, nxt;
+  int pi = p0 + w;
+  if (pi < p1) load_page<D, G>(cur, p.pages + (size_t)ptab[pi] * hstride + hoff, n, r);
+  for (; pi < p1; pi += kWaves) {
+    if (pi + kWaves < p1) load_page<D, G>(nxt, p.pages + (size_t)ptab[pi + kWaves] * hstride + hoff, n, r);
+    const int ntok = min(kPage, n_hist - pi * kPage);
+
+    // ---- QK^T: logits of heads (rt*4 + r) for tokens 4n + T
+    float lg[RT][4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      v4i cacc[RT][NG];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) cacc[rt][g] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const uint32_t wv = cur.kc[(T * MI + mi) / 4][(T * MI + mi) % 4];
+        const v4i B = v4i{(int)(wv & 0x03030303u), (int)(wv & 0x0C0C0C0Cu), (int)(wv & 0x30303030u),
+                          (int)((wv >> 6) & 0x03030303u)};
+        const int g = NG == 1 ? 0 : mi;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          cacc[rt][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[rt][mi], B, cacc[rt][g], 0, 0, 0);
+      }
+      const bool tvalid = 4 * n + T < ntok;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int hs = min(rt * 4 + r, GQ - 1);
+        float l = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const float dv = (float)cacc[rt][g][0] + 256.f * (float)cacc[rt][g][1] + 65536.f * (float)cacc[rt][g][2];
+          const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
+          l = fmaf(f16lo(sz) * kfac[rt], dv, fmaf(f16hi(sz), sm.qsum[hs][g], l));
+        }
+        lg[rt][T] = (tvalid && rt * 4 + r < GQ) ? l : -INFINITY;
+      }
+    }
+
+    // ---- online softmax over the page (per head: 16 lanes x 4 tokens)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int hrow = rt * 4 + r;
+      float mt = fmaxf(fmaxf(lg[rt][0], lg[rt][1]), fmaxf(lg[rt][2], lg[rt][3]));
+      mt = row16_max(mt);
+      const float mnew = fmaxf(m_run[rt], mt);
+      const float alpha = m_run[rt] == mnew ? 1.f : exp2_or_zero(m_run[rt] - mnew);
+      m_run[rt] = mnew;
+      float psum = 0.f;
+      float zadd[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) zadd[g] = 0.f;
+      float pv[NG][4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const bool ok = lg[rt][T] != -INFINITY;
+        const float pt = ok ? exp2f(lg[rt][T] - mnew) : 0.f;
+        psum += pt;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const uint32_t sz = cur.vp[(T * NG + g) / 4][(T * NG + g) % 4];
+          zadd[g] = ok ? fmaf(pt, f16hi(sz), zadd[g]) : zadd[g];
+          pv[g][T] = ok ? pt * f16lo(sz) * pfac[T] : 0.f;
+        }
+      }
+      l_run[rt] = fmaf(l_run[rt], alpha, psum);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        zs[rt][g] = fmaf(zs[rt][g], alpha, zadd[g]);
+        if (hrow < GQ) {
+          union {
+            _Float16 h[4];
+            u32x2 u;
+          } pk;
+#pragma unroll
+          for (int T = 0; T < 4; ++T) pk.h[T] = (_Float16)pv[g][T];
+          *(u32x2 *)&sm.u.P[w][g][hrow][4 * n] = pk.u;
+        }
+      }
+      if (n == 0 && hrow < GQ) sm.alpha[w][hrow] = alpha;
+    }
+    wave_sync();
+
+    // ---- rescale the PV accumulators when some row's max moved
+    const v4f a4 = *(const v4f *)&sm.alpha[w][4 * r];
+    const bool moved = a4[0] != 1.f || a4[1] != 1.f || a4[2] != 1.f || a4[3] != 1.f;
+    if (__any(moved)) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] *= a4;
+    }
+
+    // ---- PV: rows = heads, columns = channels 16 j + n
+    v8h Ap[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) Ap[g][kb] = *(const v8h *)&sm.u.P[w][g][n][16 * r + 8 * kb];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t wv = cur.vc[j / 4][j % 4];
+      const uint32_t w2 = wv >> 10;
+      const u32x4 b0 = u32x4{wv & 0x00030003u, wv & 0x000C000Cu, wv & 0x00300030u, wv & 0x00C000C0u};
+      const u32x4 b1 = u32x4{wv & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
+      const int g = (16 * j) / G;
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][0], __builtin_bit_cast(v8h, b0), acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][1], __builtin_bit_cast(v8h, b1), acc[j], 0, 0, 0);
+    }
+    // the next page rewrites P' and alpha only after every lane read them
+    wave_sync();
+    cur = nxt;
+  }
+
+  // ---- epilogue: per-wave (m, l, acc) then the block merge
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int hrow = rt * 4 + r;
+    const float l = row16_sum(l_run[rt]);
+    float z[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) z[g] = row16_sum(zs[rt][g]);
+    if (n == 0 && hrow < GQ) {
+      sm.M[w][hrow] = m_run[rt];
+      sm.L[w][hrow] = l;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) sm.zsum[w][hrow][g] = z[g];
+    }
+  }
+  __syncthreads(); // every wave has left the loop: P' may be overwritten
+  const float unscale = ldexpf(1.f, 24 - p.pv_shift);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r + i, c = 16 * j + n;
+      if (h < GQ) sm.u.A[w][h][c] = fmaf(acc[j][i], unscale, sm.zsum[w][h][c / G]);
+    }
+  __syncthreads();
+  block_merge_store<D, GQ>(sm.M, sm.L, sm.u.A, ws_hist + (size_t)blk * GQ * (D + 2));
+}
+
+template <int D, int G, int GQ>
+__global__ __launch_bounds__(kThreads) void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
+                                                               float qscale, float *__restrict__ ws) {
+  __shared__ MainSmem<D, G, GQ> sm;
+  float *ws_win = ws;
+  float *ws_hist = ws + (size_t)b.n * p.Hq * (D + 2);
+  const int nwin = b.n * p.Hkv;
+  if ((int)blockIdx.x < nwin)
+    window_block<D, GQ>(sm.w, p, b, q, qscale, ws_win, blockIdx.x);
+  else
+    history_block<D, G, GQ>(sm.h, p, b, q, qscale, ws_hist, blockIdx.x - nwin);
 }
 
 template <int D, int GQ>
@@ -333,7 +569,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(PoolDev p, DecodeBatch 
 template <int D, int G, int GQ>
 hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                        float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
-  const int blocks = b.hist_blocks + b.n * p.Hkv;
+  const int blocks = b.n * p.Hkv + b.hist_blocks;
   if (tm.on) (void)hipEventRecord(tm.ev[0], s);
   hipLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(kThreads), 0, s, p, b, q, scale * kLog2e, ws);
   if (tm.on) (void)hipEventRecord(tm.ev[1], s);

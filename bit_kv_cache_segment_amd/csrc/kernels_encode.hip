@@ -137,7 +137,7 @@ __global__ __launch_bounds__(D) void prefill_encode_kernel(PoolDev p, int seq, c
       store_k_code<D>(blk, t, code);
       store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
     } else {
-      vdw[t / 16] |= code << (2 * (t % 16));
+      vdw[t / 16] |= code << vbit(t % 16);
       store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
     }
   }
@@ -232,10 +232,12 @@ __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, con
       store_k_code<D>(blk, t, code);
       store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
     } else {
-      // one byte holds four consecutive tokens of channel j: read-modify-write
-      uint8_t *byte = blk + vcode_dword_off(D, t / 16, j) + (t % 16) / 4;
-      const int sh = 2 * (t % 4);
-      const uint32_t old = (t % 4 == 0) ? 0u : *byte;
+      // a byte holds four tokens of channel j (those with equal k & 1 and
+      // k >> 3, k = t % 16); the first of them, k & 6 == 0, starts the byte
+      const int k = t % 16;
+      uint8_t *byte = blk + vcode_dword_off(D, t / 16, j) + vbit(k) / 8;
+      const int sh = vbit(k) % 8;
+      const uint32_t old = (k & 6) == 0 ? 0u : *byte;
       *byte = (uint8_t)((old & ~(3u << sh)) | (code << sh));
       store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
     }

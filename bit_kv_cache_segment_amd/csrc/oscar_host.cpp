@@ -244,6 +244,16 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
   D.G = cfg->group_size;
   D.maxp = cfg->max_pages_per_seq;
   D.block_bytes = block_bytes_for(d, cfg->group_size);
+  D.pv_shift = 0;
+  if (!host_only) {
+    // V scales never exceed fp16(2 c / 3) for the largest V threshold c; keep
+    // weight * scale * 2^pv_shift below 65504 with a margin for fp16 rounding.
+    float cmax = 0.f;
+    for (size_t i = 0; i < (size_t)H * d; ++i) cmax = std::max(cmax, clip_V[i]);
+    double smax = 2.0 * cmax / 3.0 * 1.002;
+    int sh = (int)std::floor(std::log2(65504.0 / smax));
+    D.pv_shift = std::max(0, std::min(sh, 60));
+  }
   if (!host_only) {
     char *b = (char *)device_buf;
     D.RK = (const float *)(b + lay.RK);
@@ -529,7 +539,7 @@ int oscar_export_history(oscar_pool *p, int32_t seq, int32_t first, int32_t coun
         uint32_t kw, vw;
         std::memcpy(&kw, blk + kcode_dword_off(d, t, (c % 64) / 16, c / 64), 4);
         std::memcpy(&vw, blk + vcode_dword_off(d, t / 16, c), 4);
-        uint32_t kc = (kw >> (2 * (c % 16))) & 3, vc = (vw >> (2 * (t % 16))) & 3;
+        uint32_t kc = (kw >> (2 * (c % 16))) & 3, vc = (vw >> vbit(t % 16)) & 3;
         ck[c / 4] |= kc << (2 * (c % 4));
         cv[c / 4] |= vc << (2 * (c % 4));
       }

@@ -29,6 +29,9 @@ struct PoolDev {
   uint8_t *pages;      // [num_pages][Hkv][block_bytes]
   int32_t Hq, Hkv, d, G, maxp;
   int32_t block_bytes; // bytes of one (page, kv head) block
+  // 2^pv_shift * fp16(2 max(clip_V) / 3) <= 65504: the largest power of two
+  // by which a softmax weight times a V scale may be multiplied in fp16.
+  int32_t pv_shift;
 };
 
 // ---------------------------------------------------------------------------
@@ -44,10 +47,13 @@ struct PoolDev {
 // A lane that owns (quad r, tokens t..t+3) reads d/4 contiguous bytes.
 //
 // V codes, channel-major in 16-token blocks.  The 16 tokens
-// {16 tb + k : k < 16} of channel c form one dword (token 16tb+k in bits
-// 2k..2k+1) at byte   16d + tb * 4d + 4 * sigma(c),
-// sigma(c) = (d/16) * (c % 16) + c / 16, so that the d/16 dwords a lane
-// needs for channels {c : c % 16 == n} are contiguous.
+// {16 tb + k : k < 16} of channel c form one dword at byte
+//      16d + tb * 4d + 4 * sigma(c),   sigma(c) = (d/16) * (c % 16) + c / 16,
+// so that the d/16 dwords a lane needs for channels {c : c % 16 == n} are
+// contiguous.  Inside the dword, token k sits at bit vbit(k) =
+// 16 (k & 1) + 2 (k >> 1): even tokens fill the low half, odd tokens the
+// high half, so one AND with 0x00030003 << 2i yields tokens (2i, 2i+1) as a
+// pair of fp16 sub-normals.
 //
 // Params: fp16 (scale, zero) of token t, group g at byte
 //      32d + 4 (t * d/G + g)               (K)
@@ -61,6 +67,7 @@ __host__ __device__ inline int vsigma(int d, int c) { return (d / 16) * (c % 16)
 __host__ __device__ inline int vcode_dword_off(int d, int tb, int c) {
   return 16 * d + tb * 4 * d + 4 * vsigma(d, c);
 }
+__host__ __device__ inline int vbit(int k) { return 16 * (k & 1) + 2 * (k >> 1); }
 __host__ __device__ inline int kparam_off(int d, int G, int t, int g) {
   return 32 * d + 4 * (t * (d / G) + g);
 }

@@ -92,7 +92,8 @@ def test_edge_lengths_prefill_then_fused_steps(shape):
         if step % 10 == 0 or step == 1:
             q = synth.queries(w, step, device="cuda", batch=len(lengths))
             # decode in a permuted order too: outputs follow seq_ids
-            out = pool.decode(order, q.view(torch.uint16)[order].contiguous())
+            qo = q[torch.as_tensor(order, device="cuda")].contiguous().view(torch.uint16)
+            out = pool.decode(order, qo)
             torch.cuda.synchronize()
             inv = np.argsort(order)
             _check_all_rows(w, out[torch.as_tensor(inv, device="cuda")], lengths, step)
