@@ -145,10 +145,13 @@ def main():
     qs = [synth.queries(w, s, device="cuda").view(torch.uint16).contiguous() for s in range(total_steps)]
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     if args.copy_probe_mib:
+        # a plain device copy of known size: reads and writes copy_probe_mib MiB
+        # (its FETCH_SIZE / WRITE_SIZE calibrate the counter units)
         n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
     torch.cuda.synchronize()

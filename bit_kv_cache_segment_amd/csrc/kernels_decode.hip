@@ -7,12 +7,14 @@
 // sink and recent tokens; an online softmax merges the two results.
 //
 // Launches (one stream):
+//   q_prep_kernel, one block per (sequence with history, kv head): rotate
+//     the g = Hq/Hkv queries by R_K, scale them, and lay them out as the
+//     int8-limb MFMA operands every split block of that pair loads;
 //   decode_main_kernel, two block roles in one grid:
 //     * window blocks (first in the grid), one per (sequence, kv head):
 //       attend to the BF16 sink and recent tokens with the raw queries;
 //     * split blocks, one per (sequence, kv head, run of history pages):
-//       rotate the g = Hq/Hkv queries by R_K and attend to the INT2 history
-//       in the rotated basis.
+//       attend to the INT2 history in the rotated basis.
 //     Each block writes one partial (m, l, acc) per query head.
 //   decode_merge_kernel, one block per (sequence, kv head): merge the split
 //     partials, de-rotate the history accumulator by R_V^T, merge with the
@@ -41,6 +43,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f; // log2 headroom of the lazy softmax reference (host keeps 2^kLazy in pv_shift)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -87,17 +90,21 @@ __device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ?
 template <int D, int G, int GQ>
 struct HistSmem {
   static constexpr int NG = D / G;
-  float qs[GQ][D];          // rotated queries times scale*log2(e)
-  float qsum[GQ][NG];       // per-group sums of qs
-  int qexp[GQ];             // fixed-point exponent E of each head
   float alpha[kWaves][16];  // per-wave rescale factors of the PV rows
   float zsum[kWaves][16][NG];
   float M[kWaves][GQ], L[kWaves][GQ];
   union {
-    float qraw[GQ][D];                       // prologue
     _Float16 P[kWaves][NG][16][64];          // page loop: P' rows per wave
     float A[kWaves][GQ][D];                  // epilogue: per-wave accumulators
   } u;
+};
+
+template <int D, int G, int GQ>
+struct QPrepSmem {
+  float R[D][D];     // R_K of this kv head, staged with one coalesced pass
+  float qraw[GQ][D];
+  float qs[GQ][D];
+  int qexp[GQ];
 };
 
 template <int D, int GQ>
@@ -177,7 +184,7 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
       const uint16_t *row = u < n_sink ? sinkK + (size_t)u * D : recK + (size_t)(u - n_sink) * D;
 #pragma unroll
       for (int h = 0; h < GQ; ++h) lg[h] = 0.f;
-#pragma unroll 4
+#pragma unroll 1
       for (int c8 = 0; c8 < D; c8 += 8) {
         const u32x4 kw = *(const u32x4 *)(row + c8);
 #pragma unroll
@@ -227,6 +234,81 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
 }
 
 // ---------------------------------------------------------------------------
+// Query preparation for the split blocks of one (sequence, kv head).
+//   qs = (q . R_K) * scale * log2(e)          (fp32, fixed-order FMA chain)
+//   E  = 18 - e  with max|qs| = f 2^e, f in [0.5, 1)   ->  |qs 2^E| < 2^18
+//   A operand word [rt][mi][lane][v]: lane = (row m, k-quad r); row
+//     m = 4 hh + limb of head 4 rt + hh; byte j of register v holds limb
+//     `limb` of rint(qs[h][c] 2^E) * {16, 4, 1, 16}[v], c = 64 mi + 16 r + 4 j + v.
+//   Limbs are balanced signed bytes: X = a0 + 2^8 a1 + 2^16 a2.
+// Record tail: qsum[h][g] (group sums of qs) at 0, kfac[h] = 2^-(E+4) at 32.
+// ---------------------------------------------------------------------------
+template <int D, int G, int GQ>
+__global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
+                                                          float qscale, uint32_t *__restrict__ qrec) {
+  constexpr int NG = D / G, MI = D / 64, RT = GQ >= 4 ? GQ / 4 : 1;
+  __shared__ QPrepSmem<D, G, GQ> sm;
+  const int tid = threadIdx.x, Hkv = p.Hkv, Hq = p.Hq;
+  const int e = blockIdx.x / Hkv, kv = blockIdx.x % Hkv;
+  if (b.len[e] <= kWindow) return; // no history: no split block reads this record
+  uint32_t *rec = qrec + (size_t)blockIdx.x * qprep_words(D, GQ);
+  {
+    const u32x4 *src = (const u32x4 *)(p.RK + (size_t)kv * D * D);
+    u32x4 *dst = (u32x4 *)&sm.R[0][0];
+#pragma unroll
+    for (int i = 0; i < D * D / 4 / kThreads; ++i) dst[tid + i * kThreads] = src[tid + i * kThreads];
+  }
+  for (int idx = tid; idx < GQ * D; idx += kThreads)
+    sm.qraw[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]);
+  __syncthreads();
+  for (int idx = tid; idx < GQ * D; idx += kThreads) {
+    const int h = idx / D, j = idx % D;
+    float a = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < D; ++i) a = fmaf(sm.qraw[h][i], sm.R[i][j], a);
+    sm.qs[h][j] = a * qscale;
+  }
+  __syncthreads();
+  float *tail = (float *)(rec + RT * MI * 256);
+  if (tid < GQ * NG) {
+    const int h = tid / NG, g = tid % NG;
+    float a = 0.f;
+    for (int c = g * G; c < (g + 1) * G; ++c) a += sm.qs[h][c];
+    tail[h * NG + g] = a;
+  } else if (tid >= 128 && tid < 128 + GQ) {
+    const int h = tid - 128;
+    float mx = 0.f;
+    for (int c = 0; c < D; ++c) mx = fmaxf(mx, fabsf(sm.qs[h][c]));
+    int ex = 0;
+    frexpf(mx, &ex);
+    const int E = mx > 0.f ? 18 - ex : 0;
+    sm.qexp[h] = E;
+    tail[32 + h] = ldexpf(1.f, -(E + 4));
+  }
+  __syncthreads();
+  for (int idx = tid; idx < RT * MI * 256; idx += kThreads) {
+    const int v = idx & 3, lane = (idx >> 2) & 63, mi = (idx >> 8) % MI, rt = (idx >> 8) / MI;
+    const int m = lane & 15, r = lane >> 4;
+    const int h = rt * 4 + (m >> 2), lam = m & 3;
+    const bool live = h < GQ && lam < 3;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int c = 64 * mi + 16 * r + 4 * j4 + v;
+      int X = 0;
+      if (live) X = (int)rintf(ldexpf(sm.qs[h][c], sm.qexp[h])) * (v == 1 ? 4 : (v == 2 ? 1 : 16));
+      const int a0 = (int)(int8_t)(X & 0xff);
+      const int X1 = (X - a0) >> 8;
+      const int a1 = (int)(int8_t)(X1 & 0xff);
+      const int a2 = (X1 - a1) >> 8;
+      const int limb = lam == 0 ? a0 : (lam == 1 ? a1 : a2);
+      word |= ((uint32_t)limb & 0xffu) << (8 * j4);
+    }
+    rec[idx] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // INT2 history split block.
 // ---------------------------------------------------------------------------
 template <int D, int G>
@@ -257,15 +339,15 @@ __device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk
 }
 
 template <int D, int G, int GQ>
-__device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
-                              float qscale, float *ws_hist, int blk) {
+__device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const DecodeBatch &b,
+                              const uint32_t *qrec, float *ws_hist, int blk) {
   constexpr int NG = D / G;                // scale/zero groups per token
   constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
   constexpr int RT = GQ >= 4 ? GQ / 4 : 1; // MFMA row tiles of 4 heads x 4 limb rows
   constexpr int NJ = D / 16;               // PV column tiles of 16 channels
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n = lane & 15, r = lane >> 4;
-  const int Hkv = p.Hkv, Hq = p.Hq;
+  const int Hkv = p.Hkv;
   const int kv = blk % Hkv, sidx = blk / Hkv;
   int lo = 0, hi = b.n;
   while (hi - lo > 1) {
@@ -278,75 +360,28 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   const int np = (n_hist + kPage - 1) / kPage;
   const int p0 = s * b.pages_per_split, p1 = min(np, p0 + b.pages_per_split);
 
-  // ---- prologue: q_rot = (q . R_K) * scale * log2(e), its group sums and
-  // fixed-point exponent; rows of P' that no head owns stay zero.
-  for (int idx = tid; idx < GQ * D; idx += kThreads)
-    sm.u.qraw[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]);
+  // ---- prologue: load this pair's query record; rows of P' that no head
+  // owns stay zero for the whole loop.
+  const uint32_t *rec = qrec + ((size_t)e * Hkv + kv) * qprep_words(D, GQ);
+  const float *tail = (const float *)(rec + RT * MI * 256);
+  v4i Aq[RT][MI];
+  float kfac[RT], qsum[RT][NG];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) Aq[rt][mi] = *(const v4i *)(rec + ((rt * MI + mi) * 64 + lane) * 4);
+    const int hs = min(rt * 4 + r, GQ - 1); // head of this lane in the logit layout
+    kfac[rt] = tail[32 + hs];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) qsum[rt][g] = tail[hs * NG + g];
+  }
   for (int idx = tid; idx < kWaves * 16; idx += kThreads) sm.alpha[idx / 16][idx % 16] = 1.f;
-  __syncthreads();
-  const float *RK = p.RK + (size_t)kv * D * D;
-  for (int idx = tid; idx < GQ * D; idx += kThreads) {
-    const int h = idx / D, j = idx % D;
-    float a = 0.f;
-    for (int i = 0; i < D; ++i) a = fmaf(sm.u.qraw[h][i], RK[i * D + j], a);
-    sm.qs[h][j] = a * qscale;
-  }
-  __syncthreads();
-  if (tid < GQ * NG) {
-    const int h = tid / NG, g = tid % NG;
-    float a = 0.f;
-    for (int c = g * G; c < (g + 1) * G; ++c) a += sm.qs[h][c];
-    sm.qsum[h][g] = a;
-  } else if (tid >= 128 && tid < 128 + GQ) {
-    const int h = tid - 128;
-    float mx = 0.f;
-    for (int c = 0; c < D; ++c) mx = fmaxf(mx, fabsf(sm.qs[h][c]));
-    int ex = 0;
-    frexpf(mx, &ex);                      // mx = f 2^ex, f in [0.5, 1)
-    sm.qexp[h] = mx > 0.f ? 18 - ex : 0;  // |q 2^E| < 2^18
-  }
   {
     _Float16 *P = &sm.u.P[0][0][0][0];
     for (int idx = tid; idx < kWaves * NG * 16 * 64; idx += kThreads) P[idx] = (_Float16)0.f;
   }
   __syncthreads();
 
-  // A operands of QK^T: lane (row m = n, k-quad r).  Row m = 4 hh + limb;
-  // register v of MFMA mi holds channels 64 mi + 16 r + 4 j + v (byte j),
-  // pre-multiplied by {16, 4, 1, 16}[v] to match the code masks below.
-  v4i Aq[RT][MI];
-  float kfac[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int h = rt * 4 + (n >> 2), lam = n & 3;
-    const bool live = h < GQ && lam < 3;
-    const int E = live ? sm.qexp[h] : 0;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const int c = 64 * mi + 16 * r + 4 * j4 + v;
-          int X = 0;
-          if (live) {
-            const int qi = (int)rintf(ldexpf(sm.qs[h][c], E));
-            X = qi * (v == 1 ? 4 : (v == 2 ? 1 : 16));
-          }
-          const int a0 = (int)(int8_t)(X & 0xff);
-          const int X1 = (X - a0) >> 8;
-          const int a1 = (int)(int8_t)(X1 & 0xff);
-          const int a2 = (X1 - a1) >> 8;
-          const int limb = lam == 0 ? a0 : (lam == 1 ? a1 : a2);
-          word |= ((uint32_t)limb & 0xffu) << (8 * j4);
-        }
-        Aq[rt][mi][v] = (int)word;
-      }
-    }
-    const int hs = rt * 4 + r; // head of this lane in the logit layout
-    kfac[rt] = hs < GQ ? ldexpf(1.f, -(sm.qexp[hs] + 4)) : 0.f;
-  }
   // per-token factor of P': 2^pv_shift * 4^-e(k), k = token within its
   // 16-token block, e = pair index (k >> 1), or (k >> 1) - 5 past the shift
   float pfac[4];
@@ -372,118 +407,141 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   const int32_t *ptab = p.page_table + (size_t)seq * p.maxp;
   const size_t hstride = (size_t)Hkv * p.block_bytes;
   const size_t hoff = (size_t)kv * p.block_bytes;
-  PageRegs<D, G> cur, nxt;
-  int pi = p0 + w;
-  if (pi < p1) load_page<D, G>(cur, p.pages + (size_t)ptab[pi] * hstride + hoff, n, r);
-  for (; pi < p1; pi += kWaves) {
-    if (pi + kWaves < p1) load_page<D, G>(nxt, p.pages + (size_t)ptab[pi + kWaves] * hstride + hoff, n, r);
-    const int ntok = min(kPage, n_hist - pi * kPage);
 
-    // ---- QK^T: logits of heads (rt*4 + r) for tokens 4n + T
-    float lg[RT][4];
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      v4i cacc[RT][NG];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int g = 0; g < NG; ++g) cacc[rt][g] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const uint32_t wv = cur.kc[(T * MI + mi) / 4][(T * MI + mi) % 4];
-        const v4i B = v4i{(int)(wv & 0x03030303u), (int)(wv & 0x0C0C0C0Cu), (int)(wv & 0x30303030u),
-                          (int)((wv >> 6) & 0x03030303u)};
-        const int g = NG == 1 ? 0 : mi;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          cacc[rt][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[rt][mi], B, cacc[rt][g], 0, 0, 0);
-      }
-      const bool tvalid = 4 * n + T < ntok;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int hs = min(rt * 4 + r, GQ - 1);
-        float l = 0.f;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const float dv = (float)cacc[rt][g][0] + 256.f * (float)cacc[rt][g][1] + 65536.f * (float)cacc[rt][g][2];
-          const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
-          l = fmaf(f16lo(sz) * kfac[rt], dv, fmaf(f16hi(sz), sm.qsum[hs][g], l));
-        }
-        lg[rt][T] = (tvalid && rt * 4 + r < GQ) ? l : -INFINITY;
-      }
-    }
+  // One page of this wave: logits, online softmax, P' and PV.
+  // `full`: every token of the page is valid (all pages but a sequence's last)
+  auto page_step = [&](const PageRegs<D, G> &cur, const int pi, const bool full) __attribute__((always_inline)) {
+      const int ntok = full ? kPage : min(kPage, n_hist - pi * kPage);
 
-    // ---- online softmax over the page (per head: 16 lanes x 4 tokens)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int hrow = rt * 4 + r;
-      float mt = fmaxf(fmaxf(lg[rt][0], lg[rt][1]), fmaxf(lg[rt][2], lg[rt][3]));
-      mt = row16_max(mt);
-      const float mnew = fmaxf(m_run[rt], mt);
-      const float alpha = m_run[rt] == mnew ? 1.f : exp2_or_zero(m_run[rt] - mnew);
-      m_run[rt] = mnew;
-      float psum = 0.f;
-      float zadd[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) zadd[g] = 0.f;
-      float pv[NG][4];
-#pragma unroll
+      // ---- QK^T: logits of heads (rt*4 + r) for tokens 4n + T
+      float lg[RT][4];
+  #pragma unroll
       for (int T = 0; T < 4; ++T) {
-        const bool ok = lg[rt][T] != -INFINITY;
-        const float pt = ok ? exp2f(lg[rt][T] - mnew) : 0.f;
-        psum += pt;
-#pragma unroll
+        v4i cacc[RT][NG];
+  #pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+  #pragma unroll
+          for (int g = 0; g < NG; ++g) cacc[rt][g] = v4i{0, 0, 0, 0};
+  #pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const uint32_t wv = cur.kc[(T * MI + mi) / 4][(T * MI + mi) % 4];
+          const v4i B = v4i{(int)(wv & 0x03030303u), (int)(wv & 0x0C0C0C0Cu), (int)(wv & 0x30303030u),
+                            (int)((wv >> 6) & 0x03030303u)};
+          const int g = NG == 1 ? 0 : mi;
+  #pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            cacc[rt][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[rt][mi], B, cacc[rt][g], 0, 0, 0);
+        }
+        const bool tvalid = full || 4 * n + T < ntok;
+  #pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float l = 0.f;
+  #pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const float dv = (float)cacc[rt][g][0] + 256.f * (float)cacc[rt][g][1] + 65536.f * (float)cacc[rt][g][2];
+            const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
+            l = fmaf(f16lo(sz) * kfac[rt], dv, fmaf(f16hi(sz), qsum[rt][g], l));
+          }
+          lg[rt][T] = (tvalid && (GQ >= 4 || rt * 4 + r < GQ)) ? l : -INFINITY;
+        }
+      }
+
+      // ---- online softmax over the page (per head: 16 lanes x 4 tokens)
+  #pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int hrow = rt * 4 + r;
+        float mt = fmaxf(fmaxf(lg[rt][0], lg[rt][1]), fmaxf(lg[rt][2], lg[rt][3]));
+        mt = row16_max(mt);
+        // The running reference moves only when a page's maximum exceeds it
+        // by more than kLazy: weights stay <= 2^kLazy and the PV accumulators
+        // are rescaled rarely.
+        const bool jump = mt > m_run[rt] + kLazy;
+        const float mnew = jump ? mt : m_run[rt];
+        const float alpha = jump ? exp2_or_zero(m_run[rt] - mnew) : 1.f;
+        m_run[rt] = mnew;
+        float psum = 0.f;
+        float zadd[NG];
+  #pragma unroll
+        for (int g = 0; g < NG; ++g) zadd[g] = 0.f;
+        float pv[NG][4];
+  #pragma unroll
+        for (int T = 0; T < 4; ++T) {
+          const bool ok = (full && GQ >= 4) || lg[rt][T] != -INFINITY;
+          const float pt = ok ? exp2f(lg[rt][T] - mnew) : 0.f;
+          psum += pt;
+  #pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const uint32_t sz = cur.vp[(T * NG + g) / 4][(T * NG + g) % 4];
+            zadd[g] = ok ? fmaf(pt, f16hi(sz), zadd[g]) : zadd[g];
+            pv[g][T] = ok ? pt * f16lo(sz) * pfac[T] : 0.f;
+          }
+        }
+        l_run[rt] = fmaf(l_run[rt], alpha, psum);
+  #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          const uint32_t sz = cur.vp[(T * NG + g) / 4][(T * NG + g) % 4];
-          zadd[g] = ok ? fmaf(pt, f16hi(sz), zadd[g]) : zadd[g];
-          pv[g][T] = ok ? pt * f16lo(sz) * pfac[T] : 0.f;
+          zs[rt][g] = fmaf(zs[rt][g], alpha, zadd[g]);
+          if (hrow < GQ) {
+            union {
+              _Float16 h[4];
+              u32x2 u;
+            } pk;
+  #pragma unroll
+            for (int T = 0; T < 4; ++T) pk.h[T] = (_Float16)pv[g][T];
+            *(u32x2 *)&sm.u.P[w][g][hrow][4 * n] = pk.u;
+          }
         }
+        if (n == 0 && hrow < GQ) sm.alpha[w][hrow] = alpha;
       }
-      l_run[rt] = fmaf(l_run[rt], alpha, psum);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        zs[rt][g] = fmaf(zs[rt][g], alpha, zadd[g]);
-        if (hrow < GQ) {
-          union {
-            _Float16 h[4];
-            u32x2 u;
-          } pk;
-#pragma unroll
-          for (int T = 0; T < 4; ++T) pk.h[T] = (_Float16)pv[g][T];
-          *(u32x2 *)&sm.u.P[w][g][hrow][4 * n] = pk.u;
-        }
+      wave_sync();
+
+      // ---- rescale the PV accumulators when some row's max moved
+      const v4f a4 = *(const v4f *)&sm.alpha[w][4 * r];
+      const bool moved = a4[0] != 1.f || a4[1] != 1.f || a4[2] != 1.f || a4[3] != 1.f;
+      if (__any(moved)) {
+  #pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] *= a4;
       }
-      if (n == 0 && hrow < GQ) sm.alpha[w][hrow] = alpha;
-    }
-    wave_sync();
 
-    // ---- rescale the PV accumulators when some row's max moved
-    const v4f a4 = *(const v4f *)&sm.alpha[w][4 * r];
-    const bool moved = a4[0] != 1.f || a4[1] != 1.f || a4[2] != 1.f || a4[3] != 1.f;
-    if (__any(moved)) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[j] *= a4;
-    }
+      // ---- PV: rows = heads, columns = channels 16 j + n
+      v8h Ap[NG][2];
+  #pragma unroll
+      for (int g = 0; g < NG; ++g)
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Ap[g][kb] = *(const v8h *)&sm.u.P[w][g][n][16 * r + 8 * kb];
+  #pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t wv = cur.vc[j / 4][j % 4];
+        const uint32_t w2 = wv >> 10;
+        const u32x4 b0 = u32x4{wv & 0x00030003u, wv & 0x000C000Cu, wv & 0x00300030u, wv & 0x00C000C0u};
+        const u32x4 b1 = u32x4{wv & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
+        const int g = (16 * j) / G;
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][0], __builtin_bit_cast(v8h, b0), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][1], __builtin_bit_cast(v8h, b1), acc[j], 0, 0, 0);
+      }
+      // the next page rewrites P' and alpha only after every lane read them
+      wave_sync();
+  };
 
-    // ---- PV: rows = heads, columns = channels 16 j + n
-    v8h Ap[NG][2];
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) Ap[g][kb] = *(const v8h *)&sm.u.P[w][g][n][16 * r + 8 * kb];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint32_t wv = cur.vc[j / 4][j % 4];
-      const uint32_t w2 = wv >> 10;
-      const u32x4 b0 = u32x4{wv & 0x00030003u, wv & 0x000C000Cu, wv & 0x00300030u, wv & 0x00C000C0u};
-      const u32x4 b1 = u32x4{wv & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
-      const int g = (16 * j) / G;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][0], __builtin_bit_cast(v8h, b0), acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][1], __builtin_bit_cast(v8h, b1), acc[j], 0, 0, 0);
-    }
-    // the next page rewrites P' and alpha only after every lane read them
-    wave_sync();
-    cur = nxt;
+  // Two register buffers in ping-pong: the loads of the wave's next page are
+  // in flight while the current one is computed (no register copy between
+  // iterations, so no wait on the prefetch before the next compute).
+  // Only a sequence's last page can be partial; it is handled after the loop.
+  const int pf = (n_hist % kPage == 0) ? p1 : min(p1, np - 1); // end of full pages
+  PageRegs<D, G> bufA, bufB;
+  int pi = p0 + w;
+  if (pi < pf) load_page<D, G>(bufA, p.pages + (size_t)ptab[pi] * hstride + hoff, n, r);
+  while (pi < pf) {
+    if (pi + kWaves < pf) load_page<D, G>(bufB, p.pages + (size_t)ptab[pi + kWaves] * hstride + hoff, n, r);
+    page_step(bufA, pi, true);
+    pi += kWaves;
+    if (pi >= pf) break;
+    if (pi + kWaves < pf) load_page<D, G>(bufA, p.pages + (size_t)ptab[pi + kWaves] * hstride + hoff, n, r);
+    page_step(bufB, pi, true);
+    pi += kWaves;
+  }
+  if (pf < p1 && (pf - p0) % kWaves == w) {
+    load_page<D, G>(bufA, p.pages + (size_t)ptab[pf] * hstride + hoff, n, r);
+    page_step(bufA, pf, false);
   }
 
   // ---- epilogue: per-wave (m, l, acc) then the block merge
@@ -514,9 +572,15 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   block_merge_store<D, GQ>(sm.M, sm.L, sm.u.A, ws_hist + (size_t)blk * GQ * (D + 2));
 }
 
+// Waves per SIMD the register budget is sized for (3 where it fits without
+// spilling: more waves in flight hide more HBM latency).
+constexpr int main_occupancy(int D, int G, int GQ) { return (GQ <= 4 || (GQ == 8 && D == G)) ? 3 : (GQ <= 8 ? 2 : 1); }
+
 template <int D, int G, int GQ>
-__global__ __launch_bounds__(kThreads) void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
-                                                               float qscale, float *__restrict__ ws) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
+void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
+                                                               float qscale, float *__restrict__ ws,
+                                                               const uint32_t *__restrict__ qrec) {
   __shared__ MainSmem<D, G, GQ> sm;
   float *ws_win = ws;
   float *ws_hist = ws + (size_t)b.n * p.Hq * (D + 2);
@@ -524,41 +588,104 @@ __global__ __launch_bounds__(kThreads) void decode_main_kernel(PoolDev p, Decode
   if ((int)blockIdx.x < nwin)
     window_block<D, GQ>(sm.w, p, b, q, qscale, ws_win, blockIdx.x);
   else
-    history_block<D, G, GQ>(sm.h, p, b, q, qscale, ws_hist, blockIdx.x - nwin);
+    history_block<D, G, GQ>(sm.h, p, b, qrec, ws_hist, blockIdx.x - nwin);
 }
 
+// Merge of one (sequence, kv head): split partials -> history (m, l, acc),
+// acc . R_V^T, then the window partial, then out = acc / l.  Every load that
+// does not depend on another is issued up front: R_V^T goes to shared memory
+// in one coalesced pass, split partials are read in batches of 8.
+constexpr int kMergeThreads = 512;
+constexpr int kMaxSplitsDev = 32;
+
 template <int D, int GQ>
-__global__ __launch_bounds__(D) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
-                                                         const float *__restrict__ ws) {
-  const int e = blockIdx.x, kv = blockIdx.y, c = threadIdx.x;
+struct MergeSmem {
+  float R[D][D];                   // R_V^T of this kv head
+  float AH[GQ][D];                 // merged history accumulators (rotated basis)
+  float w[kMaxSplitsDev][GQ];      // split weights exp2(m_s - m_H)
+  float MH[GQ], LH[GQ];
+};
+
+template <int D, int GQ>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
+                                                                     const float *__restrict__ ws) {
+  constexpr int HG = kMergeThreads / D;       // head groups in the de-rotation
+  constexpr int HPT = (GQ + HG - 1) / HG;     // heads per thread there
+  __shared__ MergeSmem<D, GQ> sm;
+  const int e = blockIdx.x / p.Hkv, kv = blockIdx.x % p.Hkv, tid = threadIdx.x;
   const int Hkv = p.Hkv, Hq = p.Hq;
   const float *ws_win = ws;
   const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
   const int s0 = b.split_prefix[e], S = b.split_prefix[e + 1] - s0;
-  const float *RVt = p.RVt + (size_t)kv * D * D;
-  __shared__ float AH[D];
-  for (int h = 0; h < GQ; ++h) {
+  const size_t stride = (size_t)Hkv * GQ * (D + 2); // between splits of one pair
+  const float *part0 = ws_hist + ((size_t)s0 * Hkv + kv) * GQ * (D + 2);
+  if (S > 0) {
+    const u32x4 *src = (const u32x4 *)(p.RVt + (size_t)kv * D * D);
+    u32x4 *dst = (u32x4 *)&sm.R[0][0];
+#pragma unroll
+    for (int i = 0; i < D * D / 4 / kMergeThreads; ++i) dst[tid + i * kMergeThreads] = src[tid + i * kMergeThreads];
+    if (tid < GQ) {
+      const int h = tid;
+      float ms[kMaxSplitsDev], ls[kMaxSplitsDev];
+#pragma unroll
+      for (int s = 0; s < kMaxSplitsDev; ++s) {
+        ms[s] = s < S ? part0[s * stride + h * (D + 2) + D] : -INFINITY;
+        ls[s] = s < S ? part0[s * stride + h * (D + 2) + D + 1] : 0.f;
+      }
+      float mH = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < kMaxSplitsDev; ++s) mH = fmaxf(mH, ms[s]);
+      float lH = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxSplitsDev; ++s) {
+        const float f = s < S ? exp2f(ms[s] - mH) : 0.f;
+        sm.w[s][h] = f;
+        lH = fmaf(f, ls[s], lH);
+      }
+      sm.MH[h] = mH;
+      sm.LH[h] = lH;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < GQ * D; idx += kMergeThreads) {
+      const int h = idx / D, c = idx % D;
+      const float *pc = part0 + h * (D + 2) + c;
+      float aH = 0.f;
+      for (int s8 = 0; s8 < S; s8 += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = s8 + k < S ? pc[(s8 + k) * stride] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) aH = fmaf(s8 + k < S ? sm.w[s8 + k][h] : 0.f, v[k], aH);
+      }
+      sm.AH[h][c] = aH;
+    }
+    __syncthreads();
+  }
+  const int c = tid % D, hg = tid / D;
+  float der[HPT];
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) der[k] = 0.f;
+  if (S > 0) {
+#pragma unroll 8
+    for (int j = 0; j < D; ++j) {
+      const float rv = sm.R[j][c];
+#pragma unroll
+      for (int k = 0; k < HPT; ++k) {
+        const int h = hg + k * HG;
+        if (h < GQ) der[k] = fmaf(sm.AH[h][j], rv, der[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    const int h = hg + k * HG;
+    if (h >= GQ) continue;
     const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
     const float mw = win[D], lw = win[D + 1], aw = win[c];
     float o;
     if (S > 0) {
-      float mH = -INFINITY;
-      for (int s = 0; s < S; ++s)
-        mH = fmaxf(mH, ws_hist[(((size_t)(s0 + s) * Hkv + kv) * GQ + h) * (D + 2) + D]);
-      float lH = 0.f, aH = 0.f;
-      for (int s = 0; s < S; ++s) {
-        const float *part = ws_hist + (((size_t)(s0 + s) * Hkv + kv) * GQ + h) * (D + 2);
-        const float f = exp2f(part[D] - mH);
-        lH = fmaf(f, part[D + 1], lH);
-        aH = fmaf(f, part[c], aH);
-      }
-      AH[c] = aH;
-      __syncthreads();
-      float der = 0.f;
-      for (int j = 0; j < D; ++j) der = fmaf(AH[j], RVt[(size_t)j * D + c], der);
-      __syncthreads();
-      const float m = fmaxf(mw, mH), fw = exp2f(mw - m), fh = exp2f(mH - m);
-      o = (fw * aw + fh * der) / (fw * lw + fh * lH);
+      const float m = fmaxf(mw, sm.MH[h]), fw = exp2f(mw - m), fh = exp2f(sm.MH[h] - m);
+      o = (fw * aw + fh * der[k]) / (fw * lw + fh * sm.LH[h]);
     } else {
       o = aw / lw;
     }
@@ -570,11 +697,17 @@ template <int D, int G, int GQ>
 hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                        float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
   const int blocks = b.n * p.Hkv + b.hist_blocks;
+  uint32_t *qrec = (uint32_t *)(ws + (size_t)b.n * p.Hq * (D + 2) + (size_t)b.hist_blocks * GQ * (D + 2));
+  if (b.hist_blocks > 0)
+    hipLaunchKernelGGL((q_prep_kernel<D, G, GQ>), dim3(b.n * p.Hkv), dim3(kThreads), 0, s, p, b, q, scale * kLog2e,
+                       qrec);
   if (tm.on) (void)hipEventRecord(tm.ev[0], s);
-  hipLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(kThreads), 0, s, p, b, q, scale * kLog2e, ws);
+  hipLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(kThreads), 0, s, p, b, q, scale * kLog2e, ws,
+                     (const uint32_t *)qrec);
   if (tm.on) (void)hipEventRecord(tm.ev[1], s);
   if (tg.on) (void)hipEventRecord(tg.ev[0], s);
-  hipLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n, p.Hkv), dim3(D), 0, s, p, b, out, (const float *)ws);
+  hipLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(kMergeThreads), 0, s, p, b, out,
+                     (const float *)ws);
   if (tg.on) (void)hipEventRecord(tg.ev[1], s);
   return hipGetLastError();
 }

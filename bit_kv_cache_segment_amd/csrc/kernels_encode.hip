@@ -263,7 +263,7 @@ hipError_t prefill_impl(const PoolDev &p, int seq, const uint16_t *k, const uint
 template <int D, int G>
 hipError_t append_impl(const PoolDev &p, const AppendBatch &b, const uint16_t *kn, const uint16_t *vn,
                        hipStream_t s, const KernelTimer &t) {
-  constexpr int E = 8;
+  constexpr int E = 1; // one sequence per block: many short blocks beat long serial ones
   if (t.on) (void)hipEventRecord(t.ev[0], s);
   hipLaunchKernelGGL((append_kernel<D, G, E>), dim3((b.n + E - 1) / E, p.Hkv, 2), dim3(D), 0, s, p, b, kn, vn);
   if (t.on) (void)hipEventRecord(t.ev[1], s);

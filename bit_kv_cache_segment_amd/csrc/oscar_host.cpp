@@ -246,13 +246,14 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
   D.block_bytes = block_bytes_for(d, cfg->group_size);
   D.pv_shift = 0;
   if (!host_only) {
-    // V scales never exceed fp16(2 c / 3) for the largest V threshold c; keep
+    // V scales never exceed fp16(2 c / 3) for the largest V threshold c and
+    // the decode's softmax weights never exceed 2^8 (its lazy max); keep
     // weight * scale * 2^pv_shift below 65504 with a margin for fp16 rounding.
     float cmax = 0.f;
     for (size_t i = 0; i < (size_t)H * d; ++i) cmax = std::max(cmax, clip_V[i]);
     double smax = 2.0 * cmax / 3.0 * 1.002;
-    int sh = (int)std::floor(std::log2(65504.0 / smax));
-    D.pv_shift = std::max(0, std::min(sh, 60));
+    int sh = (int)std::floor(std::log2(65504.0 / smax)) - 8;
+    D.pv_shift = std::max(-30, std::min(sh, 60));
   }
   if (!host_only) {
     char *b = (char *)device_buf;

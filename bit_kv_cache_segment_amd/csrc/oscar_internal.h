@@ -29,8 +29,9 @@ struct PoolDev {
   uint8_t *pages;      // [num_pages][Hkv][block_bytes]
   int32_t Hq, Hkv, d, G, maxp;
   int32_t block_bytes; // bytes of one (page, kv head) block
-  // 2^pv_shift * fp16(2 max(clip_V) / 3) <= 65504: the largest power of two
-  // by which a softmax weight times a V scale may be multiplied in fp16.
+  // 2^(pv_shift + 8) * fp16(2 max(clip_V) / 3) <= 65504: the largest power of
+  // two by which a softmax weight (<= 2^8) times a V scale may be multiplied
+  // and stay finite in fp16.
   int32_t pv_shift;
 };
 
@@ -108,10 +109,17 @@ hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t 
                          float scale, float *ws, hipStream_t s, const KernelTimer &t_main,
                          const KernelTimer &t_merge);
 
-// Workspace (floats) for one decode launch: window partials for kMaxBatch
-// sequences plus split partials.
+// Per (sequence, kv head) query record written by the q-prep kernel and read
+// by every split block of that pair: the int8-limb MFMA A operands
+// [row tiles][d/64][64 lanes][4 words], then per-head group sums of the
+// rotated query and the fixed-point factors 2^-(E+4) (64 words).
+__host__ __device__ inline int qprep_words(int d, int g) { return (g >= 4 ? g / 4 : 1) * (d / 64) * 256 + 64; }
+
+// Workspace (4-byte words) of one decode launch: window partials, split
+// partials, query records.
 inline size_t decode_ws_floats(int Hq, int d, int n, long hist_blocks, int g) {
-  return (size_t)n * Hq * (d + 2) + (size_t)hist_blocks * g * (d + 2);
+  const int Hkv = Hq / g;
+  return (size_t)n * Hq * (d + 2) + (size_t)hist_blocks * g * (d + 2) + (size_t)n * Hkv * qprep_words(d, g);
 }
 
 } // namespace oscar
