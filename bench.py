@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_32k")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="0 skips the CPU baseline")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="time the steps without per-kernel events (roofline fields become null)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -165,8 +167,9 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    for p in pools:
-        p.profile_begin(args.steps)
+    if not args.no_kernel_timing:
+        for p in pools:
+            p.profile_begin(args.steps)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -177,11 +180,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    profs = [p.profile_end() for p in pools]
-    n_main = sum(p.n_decode_main for p in profs)
-    ms_main = sum(p.ms_decode_main for p in profs) / max(n_main, 1)
-    ms_merge = sum(p.ms_decode_merge for p in profs) / max(sum(p.n_decode_merge for p in profs), 1)
-    ms_append = sum(p.ms_append for p in profs) / max(sum(p.n_append for p in profs), 1)
+    if args.no_kernel_timing:
+        ms_main = float("nan")
+    else:
+        profs = [p.profile_end() for p in pools]
+        n_main = sum(p.n_decode_main for p in profs)
+        ms_main = sum(p.ms_decode_main for p in profs) / max(n_main, 1)
+
     # algorithmic bytes of each timed decode launch (lengths after its append)
     bytes_main = []
     for s in range(args.warmup, total_steps):
@@ -215,7 +220,7 @@ def main():
                      "kernel": "decode_main_kernel", "bytes_per_launch": bytes_launch,
                      "ms_per_launch": ms_main},
         "cpu_baseline": cpu,
-        "detail": {"ms_decode_main": ms_main, "ms_decode_merge": ms_merge, "ms_append": ms_append,
+        "detail": {"ms_decode_main": ms_main,
                    "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
                    "bits_per_element": (sum(max(0, L - 320) * (2 + 32 / w.group_size) + min(L, 320) * 16
                                             for L in lengths0) / sum(lengths0)),

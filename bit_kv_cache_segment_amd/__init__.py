@@ -59,7 +59,7 @@ class PoolConfig(ctypes.Structure):
 class Profile(ctypes.Structure):
     _fields_ = [
         ("n_decode_main", ctypes.c_int32), ("ms_decode_main", ctypes.c_float),
-        ("n_decode_merge", ctypes.c_int32), ("ms_decode_merge", ctypes.c_float),
+        ("n_decode_prep", ctypes.c_int32), ("ms_decode_prep", ctypes.c_float),
         ("n_append", ctypes.c_int32), ("ms_append", ctypes.c_float),
     ]
 
@@ -93,7 +93,7 @@ def lib() -> ctypes.CDLL:
             "oscar_export_window": [_P, _I32, _P, _P, _P, _P, _P],
             "oscar_build_rotation": [_I32, _P, _P],
             "oscar_calibrate_clip": [_I32, ctypes.c_int64, _P, _P, ctypes.c_double, _P],
-            "oscar_profile_begin": [_P, _I32],
+            "oscar_profile_begin": [_P, _I32, ctypes.c_uint32],
             "oscar_profile_end": [_P, _P],
         }
         for name, args in sig.items():
@@ -241,8 +241,11 @@ def oscar_calibrate_clip(x_bf16: np.ndarray, R: np.ndarray, pct: float = 99.0) -
     return out
 
 
-def oscar_profile_begin(h, max_calls: int):
-    _check(lib().oscar_profile_begin(h, max_calls))
+PROFILE_DECODE_MAIN, PROFILE_DECODE_PREP, PROFILE_APPEND = 1, 2, 4
+
+
+def oscar_profile_begin(h, max_calls: int, kernels: int = PROFILE_DECODE_MAIN):
+    _check(lib().oscar_profile_begin(h, max_calls, kernels))
 
 
 def oscar_profile_end(h) -> Profile:
@@ -328,8 +331,8 @@ class Pool:
         return oscar_export_history(self.handle, seq, first, count, c.num_kv_heads, c.head_dim,
                                     c.group_size, stream)
 
-    def profile_begin(self, max_calls):
-        oscar_profile_begin(self.handle, max_calls)
+    def profile_begin(self, max_calls, kernels=PROFILE_DECODE_MAIN):
+        oscar_profile_begin(self.handle, max_calls, kernels)
 
     def profile_end(self) -> Profile:
         return oscar_profile_end(self.handle)

@@ -37,6 +37,8 @@
 //   term sum_t p_t z_t is accumulated on the VALU.
 #include "oscar_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace oscar {
 namespace {
 
@@ -174,6 +176,7 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
     for (int k = 0; k < D / 64; ++k) acc[h][k] = 0.f;
   }
   const int nch = (n_win + 63) / 64;
+  constexpr int CPL = D / 64; // channels per lane in PV (adjacent)
   for (int ch = w; ch < nch; ch += kWaves) {
     const int ntok = min(64, n_win - ch * 64);
     const int u = ch * 64 + lane;
@@ -181,17 +184,20 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
 #pragma unroll
     for (int h = 0; h < GQ; ++h) lg[h] = -INFINITY;
     if (lane < ntok) {
-      const uint16_t *row = u < n_sink ? sinkK + (size_t)u * D : recK + (size_t)(u - n_sink) * D;
+      // QK^T: this lane's token row, all loads in flight at once
+      const u32x4 *row = (const u32x4 *)(u < n_sink ? sinkK + (size_t)u * D : recK + (size_t)(u - n_sink) * D);
+      u32x4 kw[D / 8];
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) kw[i] = row[i];
 #pragma unroll
       for (int h = 0; h < GQ; ++h) lg[h] = 0.f;
-#pragma unroll 1
-      for (int c8 = 0; c8 < D; c8 += 8) {
-        const u32x4 kw = *(const u32x4 *)(row + c8);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float kc = __uint_as_float(k & 1 ? (kw[k / 2] & 0xffff0000u) : (kw[k / 2] << 16));
+          const float kc = __uint_as_float(k & 1 ? (kw[i][k / 2] & 0xffff0000u) : (kw[i][k / 2] << 16));
 #pragma unroll
-          for (int h = 0; h < GQ; ++h) lg[h] = fmaf(sm.qs[h][c8 + k], kc, lg[h]);
+          for (int h = 0; h < GQ; ++h) lg[h] = fmaf(sm.qs[h][8 * i + k], kc, lg[h]);
         }
       }
     }
@@ -205,17 +211,28 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
       m_run[h] = mnew;
       sm.P[w][h][lane] = pr;
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) acc[h][k] *= alpha;
+      for (int k = 0; k < CPL; ++k) acc[h][k] *= alpha;
     }
     wave_sync();
-    for (int tt = 0; tt < ntok; ++tt) {
-      const int uu = ch * 64 + tt;
-      const uint16_t *row = uu < n_sink ? sinkV + (size_t)uu * D : recV + (size_t)(uu - n_sink) * D;
+    // PV: lanes own CPL adjacent channels; V values of 8 tokens in flight
+    for (int t8 = 0; t8 < ntok; t8 += 8) {
+      uint32_t vv[8];
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) {
-        const float v = bf16f(row[lane + 64 * k]);
+      for (int k = 0; k < 8; ++k) {
+        const int uu = ch * 64 + min(t8 + k, ntok - 1);
+        const uint16_t *row = uu < n_sink ? sinkV + (size_t)uu * D : recV + (size_t)(uu - n_sink) * D;
+        vv[k] = CPL == 2 ? *(const uint32_t *)(row + 2 * lane) : (uint32_t)row[lane];
+      }
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) acc[h][k] = fmaf(sm.P[w][h][tt], v, acc[h][k]);
+      for (int k = 0; k < 8; ++k) {
+        if (t8 + k < ntok) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float v = __uint_as_float(c ? (vv[k] & 0xffff0000u) : (vv[k] << 16));
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) acc[h][c] = fmaf(sm.P[w][h][t8 + k], v, acc[h][c]);
+          }
+        }
       }
     }
     wave_sync();
@@ -227,7 +244,7 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
       sm.L[w][h] = l_run[h];
     }
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) sm.A[w][h][lane + 64 * k] = acc[h][k];
+    for (int k = 0; k < CPL; ++k) sm.A[w][h][CPL * lane + k] = acc[h][k];
   }
   __syncthreads();
   block_merge_store<D, GQ>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * Hq + kv * GQ) * (D + 2));
@@ -253,10 +270,15 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch
   if (b.len[e] <= kWindow) return; // no history: no split block reads this record
   uint32_t *rec = qrec + (size_t)blockIdx.x * qprep_words(D, GQ);
   {
+    // all loads first, then all LDS stores: one memory round trip
     const u32x4 *src = (const u32x4 *)(p.RK + (size_t)kv * D * D);
     u32x4 *dst = (u32x4 *)&sm.R[0][0];
+    constexpr int NL = D * D / 4 / kThreads;
+    u32x4 t[NL];
 #pragma unroll
-    for (int i = 0; i < D * D / 4 / kThreads; ++i) dst[tid + i * kThreads] = src[tid + i * kThreads];
+    for (int i = 0; i < NL; ++i) t[i] = __builtin_nontemporal_load(&src[tid + i * kThreads]);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) dst[tid + i * kThreads] = t[i];
   }
   for (int idx = tid; idx < GQ * D; idx += kThreads)
     sm.qraw[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]);
@@ -270,20 +292,38 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch
   }
   __syncthreads();
   float *tail = (float *)(rec + RT * MI * 256);
-  if (tid < GQ * NG) {
-    const int h = tid / NG, g = tid % NG;
-    float a = 0.f;
-    for (int c = g * G; c < (g + 1) * G; ++c) a += sm.qs[h][c];
-    tail[h * NG + g] = a;
-  } else if (tid >= 128 && tid < 128 + GQ) {
-    const int h = tid - 128;
-    float mx = 0.f;
-    for (int c = 0; c < D; ++c) mx = fmaxf(mx, fabsf(sm.qs[h][c]));
-    int ex = 0;
-    frexpf(mx, &ex);
-    const int E = mx > 0.f ? 18 - ex : 0;
-    sm.qexp[h] = E;
-    tail[32 + h] = ldexpf(1.f, -(E + 4));
+  {
+    // one wave per head: lane k holds channels k, k + 64 (if D = 128)
+    const int w = tid >> 6, lane = tid & 63;
+    for (int h = w; h < GQ; h += kWaves) {
+      float v[D / 64], mx = 0.f;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        v[k] = sm.qs[h][lane + 64 * k];
+        mx = fmaxf(mx, fabsf(v[k]));
+      }
+      mx = wave_max(mx);
+      if (G == 64) {
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) {
+          const float sum = wave_sum(v[k]);
+          if (lane == 0) tail[h * NG + k] = sum;
+        }
+      } else {
+        float a = 0.f;
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) a += v[k];
+        a = wave_sum(a);
+        if (lane == 0) tail[h * NG] = a;
+      }
+      int ex = 0;
+      frexpf(mx, &ex);
+      const int E = mx > 0.f ? 18 - ex : 0;
+      if (lane == 0) {
+        sm.qexp[h] = E;
+        tail[32 + h] = ldexpf(1.f, -(E + 4));
+      }
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < RT * MI * 256; idx += kThreads) {
@@ -337,6 +377,10 @@ __device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk
     pr.vp[g] = vp[g];
   }
 }
+
+// Pages a wave keeps in flight beyond the one it computes (register budget).
+template <int D, int G, int GQ>
+constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
 template <int D, int G, int GQ>
 __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const DecodeBatch &b,
@@ -527,20 +571,56 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   // iterations, so no wait on the prefetch before the next compute).
   // Only a sequence's last page can be partial; it is handled after the loop.
   const int pf = (n_hist % kPage == 0) ? p1 : min(p1, np - 1); // end of full pages
+  // Page ids of this wave's pages (p0 + w + 4k) sit one per lane, 64 at a
+  // time, so a prefetch does not wait on a page-table load first.
+  int pt_vec = 0, pt_chunk = -1;
+  auto page_id = [&](int page_idx) __attribute__((always_inline)) {
+    const int k = (page_idx - p0 - w) / kWaves, chunk = k >> 6;
+    if (chunk != pt_chunk) {
+      const int idx = p0 + w + kWaves * (chunk * 64 + lane);
+      pt_vec = idx < p1 ? ptab[idx] : 0;
+      pt_chunk = chunk;
+    }
+    return __builtin_amdgcn_readlane(pt_vec, k & 63);
+  };
+  auto load = [&](PageRegs<D, G> &buf, int page_idx) __attribute__((always_inline)) {
+    load_page<D, G>(buf, p.pages + (size_t)page_id(page_idx) * hstride + hoff, n, r);
+  };
+  constexpr int W = kWaves;
   PageRegs<D, G> bufA, bufB;
   int pi = p0 + w;
-  if (pi < pf) load_page<D, G>(bufA, p.pages + (size_t)ptab[pi] * hstride + hoff, n, r);
-  while (pi < pf) {
-    if (pi + kWaves < pf) load_page<D, G>(bufB, p.pages + (size_t)ptab[pi + kWaves] * hstride + hoff, n, r);
-    page_step(bufA, pi, true);
-    pi += kWaves;
-    if (pi >= pf) break;
-    if (pi + kWaves < pf) load_page<D, G>(bufA, p.pages + (size_t)ptab[pi + kWaves] * hstride + hoff, n, r);
-    page_step(bufB, pi, true);
-    pi += kWaves;
+  if (pi < pf) load(bufA, pi);
+  if constexpr (kPrefetch<D, G, GQ> >= 2) {
+    // three register buffers in rotation: two pages in flight per wave
+    PageRegs<D, G> bufC;
+    if (pi + W < pf) load(bufB, pi + W);
+    while (pi < pf) {
+      if (pi + 2 * W < pf) load(bufC, pi + 2 * W);
+      page_step(bufA, pi, true);
+      pi += W;
+      if (pi >= pf) break;
+      if (pi + 2 * W < pf) load(bufA, pi + 2 * W);
+      page_step(bufB, pi, true);
+      pi += W;
+      if (pi >= pf) break;
+      if (pi + 2 * W < pf) load(bufB, pi + 2 * W);
+      page_step(bufC, pi, true);
+      pi += W;
+    }
+  } else {
+    // two register buffers in ping-pong: one page in flight per wave
+    while (pi < pf) {
+      if (pi + W < pf) load(bufB, pi + W);
+      page_step(bufA, pi, true);
+      pi += W;
+      if (pi >= pf) break;
+      if (pi + W < pf) load(bufA, pi + W);
+      page_step(bufB, pi, true);
+      pi += W;
+    }
   }
-  if (pf < p1 && (pf - p0) % kWaves == w) {
-    load_page<D, G>(bufA, p.pages + (size_t)ptab[pf] * hstride + hoff, n, r);
+  if (pf < p1 && (pf - p0) % W == w) {
+    load(bufA, pf);
     page_step(bufA, pf, false);
   }
 
@@ -600,20 +680,19 @@ constexpr int kMaxSplitsDev = 32;
 
 template <int D, int GQ>
 struct MergeSmem {
-  float R[D][D];                   // R_V^T of this kv head
-  float AH[GQ][D];                 // merged history accumulators (rotated basis)
-  float w[kMaxSplitsDev][GQ];      // split weights exp2(m_s - m_H)
-  float MH[GQ], LH[GQ];
+  float R[D][D];   // R_V^T of this kv head
+  float AH[GQ][D]; // merged history accumulators (rotated basis), normalised weights
 };
 
 template <int D, int GQ>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
                                                                      const float *__restrict__ ws) {
-  constexpr int HG = kMergeThreads / D;       // head groups in the de-rotation
-  constexpr int HPT = (GQ + HG - 1) / HG;     // heads per thread there
+  constexpr int HG = kMergeThreads / D;       // head groups
+  constexpr int HPT = (GQ + HG - 1) / HG;     // heads per thread
   __shared__ MergeSmem<D, GQ> sm;
   const int e = blockIdx.x / p.Hkv, kv = blockIdx.x % p.Hkv, tid = threadIdx.x;
   const int Hkv = p.Hkv, Hq = p.Hq;
+  const int c = tid % D, hg = tid / D;
   const float *ws_win = ws;
   const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
   const int s0 = b.split_prefix[e], S = b.split_prefix[e + 1] - s0;
@@ -622,73 +701,62 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
   if (S > 0) {
     const u32x4 *src = (const u32x4 *)(p.RVt + (size_t)kv * D * D);
     u32x4 *dst = (u32x4 *)&sm.R[0][0];
+    constexpr int NL = D * D / 4 / kMergeThreads;
+    u32x4 t[NL];
 #pragma unroll
-    for (int i = 0; i < D * D / 4 / kMergeThreads; ++i) dst[tid + i * kMergeThreads] = src[tid + i * kMergeThreads];
-    if (tid < GQ) {
-      const int h = tid;
-      float ms[kMaxSplitsDev], ls[kMaxSplitsDev];
+    for (int i = 0; i < NL; ++i) t[i] = src[tid + i * kMergeThreads];
 #pragma unroll
-      for (int s = 0; s < kMaxSplitsDev; ++s) {
-        ms[s] = s < S ? part0[s * stride + h * (D + 2) + D] : -INFINITY;
-        ls[s] = s < S ? part0[s * stride + h * (D + 2) + D + 1] : 0.f;
-      }
-      float mH = -INFINITY;
-#pragma unroll
-      for (int s = 0; s < kMaxSplitsDev; ++s) mH = fmaxf(mH, ms[s]);
-      float lH = 0.f;
-#pragma unroll
-      for (int s = 0; s < kMaxSplitsDev; ++s) {
-        const float f = s < S ? exp2f(ms[s] - mH) : 0.f;
-        sm.w[s][h] = f;
-        lH = fmaf(f, ls[s], lH);
-      }
-      sm.MH[h] = mH;
-      sm.LH[h] = lH;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < GQ * D; idx += kMergeThreads) {
-      const int h = idx / D, c = idx % D;
-      const float *pc = part0 + h * (D + 2) + c;
-      float aH = 0.f;
-      for (int s8 = 0; s8 < S; s8 += 8) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = s8 + k < S ? pc[(s8 + k) * stride] : 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) aH = fmaf(s8 + k < S ? sm.w[s8 + k][h] : 0.f, v[k], aH);
-      }
-      sm.AH[h][c] = aH;
-    }
-    __syncthreads();
+    for (int i = 0; i < NL; ++i) dst[tid + i * kMergeThreads] = t[i];
   }
-  const int c = tid % D, hg = tid / D;
-  float der[HPT];
+  // every thread issues all of its loads (splits' m, l, acc and the window
+  // partial) before using any
+  float mwin[HPT], lwin[HPT], awin[HPT], mH[HPT], lH[HPT], aH[HPT];
 #pragma unroll
-  for (int k = 0; k < HPT; ++k) der[k] = 0.f;
-  if (S > 0) {
-#pragma unroll 8
-    for (int j = 0; j < D; ++j) {
-      const float rv = sm.R[j][c];
+  for (int k = 0; k < HPT; ++k) {
+    const int h = min(hg + k * HG, GQ - 1);
+    const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
+    mwin[k] = win[D];
+    lwin[k] = win[D + 1];
+    awin[k] = win[c];
+    float ms[kMaxSplitsDev], ls[kMaxSplitsDev], as[kMaxSplitsDev];
+    const float *ph = part0 + (size_t)h * (D + 2);
 #pragma unroll
-      for (int k = 0; k < HPT; ++k) {
-        const int h = hg + k * HG;
-        if (h < GQ) der[k] = fmaf(sm.AH[h][j], rv, der[k]);
-      }
+    for (int s = 0; s < kMaxSplitsDev; ++s) {
+      ms[s] = s < S ? ph[s * stride + D] : -INFINITY;
+      ls[s] = s < S ? ph[s * stride + D + 1] : 0.f;
+      as[s] = s < S ? ph[s * stride + c] : 0.f;
     }
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplitsDev; ++s) m = fmaxf(m, ms[s]);
+    float l = 0.f, a = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplitsDev; ++s) {
+      const float f = s < S ? exp2f(ms[s] - m) : 0.f;
+      l = fmaf(f, ls[s], l);
+      a = fmaf(f, as[s], a);
+    }
+    mH[k] = m;
+    lH[k] = l;
+    aH[k] = a;
+    if (S > 0 && hg + k * HG < GQ) sm.AH[h][c] = a;
   }
+  __syncthreads();
 #pragma unroll
   for (int k = 0; k < HPT; ++k) {
     const int h = hg + k * HG;
     if (h >= GQ) continue;
-    const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
-    const float mw = win[D], lw = win[D + 1], aw = win[c];
     float o;
     if (S > 0) {
-      const float m = fmaxf(mw, sm.MH[h]), fw = exp2f(mw - m), fh = exp2f(sm.MH[h] - m);
-      o = (fw * aw + fh * der[k]) / (fw * lw + fh * sm.LH[h]);
+      float der = 0.f;
+#pragma unroll 16
+      for (int j = 0; j < D; ++j) der = fmaf(sm.AH[h][j], sm.R[j][c], der);
+      const float m = fmaxf(mwin[k], mH[k]), fw = exp2f(mwin[k] - m), fh = exp2f(mH[k] - m);
+      o = (fw * awin[k] + fh * der) / (fw * lwin[k] + fh * lH[k]);
     } else {
-      o = aw / lw;
+      o = awin[k] / lwin[k];
     }
+    (void)aH[k];
     out[((size_t)e * Hq + kv * GQ + h) * D + c] = o;
   }
 }
@@ -698,17 +766,15 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
                        float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
   const int blocks = b.n * p.Hkv + b.hist_blocks;
   uint32_t *qrec = (uint32_t *)(ws + (size_t)b.n * p.Hq * (D + 2) + (size_t)b.hist_blocks * GQ * (D + 2));
+  // Timed launches take their start/stop timestamps from the dispatch itself
+  // (no extra packets between kernels).
   if (b.hist_blocks > 0)
-    hipLaunchKernelGGL((q_prep_kernel<D, G, GQ>), dim3(b.n * p.Hkv), dim3(kThreads), 0, s, p, b, q, scale * kLog2e,
-                       qrec);
-  if (tm.on) (void)hipEventRecord(tm.ev[0], s);
-  hipLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(kThreads), 0, s, p, b, q, scale * kLog2e, ws,
-                     (const uint32_t *)qrec);
-  if (tm.on) (void)hipEventRecord(tm.ev[1], s);
-  if (tg.on) (void)hipEventRecord(tg.ev[0], s);
+    hipExtLaunchKernelGGL((q_prep_kernel<D, G, GQ>), dim3(b.n * p.Hkv), dim3(kThreads), 0, s,
+                          tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, qrec);
+  hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(kThreads), 0, s, tm.on ? tm.ev[0] : nullptr,
+                        tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, (const uint32_t *)qrec);
   hipLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(kMergeThreads), 0, s, p, b, out,
                      (const float *)ws);
-  if (tg.on) (void)hipEventRecord(tg.ev[1], s);
   return hipGetLastError();
 }
 

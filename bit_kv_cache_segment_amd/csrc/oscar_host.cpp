@@ -122,11 +122,12 @@ int choose_pages_per_split(int64_t total_pages, int max_np, int Hkv) {
 struct Profiler {
   bool on = false;
   int cap = 0;
-  std::vector<hipEvent_t> ev[3]; // decode main, decode merge, append: 2 per launch
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> ev[3]; // decode main, query prep, append: 2 per launch
   int used[3] = {0, 0, 0};
   KernelTimer next(int kind) {
     KernelTimer t;
-    if (on && used[kind] < cap) {
+    if (on && (mask >> kind & 1u) && used[kind] < cap) {
       t.on = true;
       t.ev[0] = ev[kind][2 * used[kind]];
       t.ev[1] = ev[kind][2 * used[kind] + 1];
@@ -582,8 +583,9 @@ int oscar_export_window(oscar_pool *p, int32_t seq, uint16_t *sink_k, uint16_t *
   return ok();
 }
 
-int oscar_profile_begin(oscar_pool *p, int32_t max_calls) {
+int oscar_profile_begin(oscar_pool *p, int32_t max_calls, uint32_t kernels) {
   if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (kernels == 0 || (kernels & ~7u)) return fail(OSCAR_EINVAL, "bad kernel mask 0x%x", kernels);
   if (p->host_only) return fail(OSCAR_EINVAL, "profiling a host-only pool");
   if (max_calls < 1 || max_calls > (1 << 16)) return fail(OSCAR_EINVAL, "max_calls %d outside [1, 65536]", max_calls);
   p->prof.release();
@@ -599,6 +601,7 @@ int oscar_profile_begin(oscar_pool *p, int32_t max_calls) {
     }
   }
   p->prof.cap = max_calls;
+  p->prof.mask = kernels;
   p->prof.on = true;
   return ok();
 }
@@ -620,8 +623,8 @@ int oscar_profile_end(oscar_pool *p, oscar_profile *out) {
     }
   out->n_decode_main = p->prof.used[0];
   out->ms_decode_main = ms[0];
-  out->n_decode_merge = p->prof.used[1];
-  out->ms_decode_merge = ms[1];
+  out->n_decode_prep = p->prof.used[1];
+  out->ms_decode_prep = ms[1];
   out->n_append = p->prof.used[2];
   out->ms_append = ms[2];
   p->prof.release();

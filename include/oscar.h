@@ -198,20 +198,25 @@ int oscar_build_rotation(int32_t d, const float *U, float *R);
 int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R,
                          double pct, float *clip);
 
-/* Kernel timing with HIP events recorded on the launch stream around each
- * kernel of the pool's decode and append calls.  oscar_profile_begin
- * creates event pairs for up to max_calls launches of each kernel (later
- * launches go untimed); oscar_profile_end waits for the events, writes the
- * number of timed launches and their summed durations (milliseconds), and
- * releases the events.  Timing adds one event record before and after each
- * launch.  Errors: EINVAL, EHIP. */
+/* Kernel timing with HIP events recorded on the launch stream around the
+ * kernels selected by `kernels` (OSCAR_PROFILE_* bits) in the pool's decode
+ * and append calls.  oscar_profile_begin creates event pairs for up to
+ * max_calls launches of each selected kernel (later launches go untimed);
+ * oscar_profile_end waits for the events, writes the number of timed
+ * launches and their summed durations (milliseconds), and releases the
+ * events.  Each event record adds a few microseconds between launches, so
+ * time only the kernels of interest.  Errors: EINVAL, EHIP. */
 typedef struct oscar_profile {
-    int32_t n_decode_main;   float ms_decode_main;   /* INT2 splits + BF16 window */
-    int32_t n_decode_merge;  float ms_decode_merge;  /* merge + de-rotation      */
-    int32_t n_append;        float ms_append;        /* append / eviction        */
+    int32_t n_decode_main;   float ms_decode_main;   /* INT2 splits + BF16 window + merge */
+    int32_t n_decode_prep;   float ms_decode_prep;   /* query rotation and layout         */
+    int32_t n_append;        float ms_append;        /* append / eviction                 */
 } oscar_profile;
 
-int oscar_profile_begin(oscar_pool *pool, int32_t max_calls);
+#define OSCAR_PROFILE_DECODE_MAIN 1u  /* INT2 splits + BF16 window kernel  */
+#define OSCAR_PROFILE_DECODE_PREP 2u  /* query rotation and layout kernel  */
+#define OSCAR_PROFILE_APPEND      4u  /* append / eviction kernel          */
+
+int oscar_profile_begin(oscar_pool *pool, int32_t max_calls, uint32_t kernels);
 int oscar_profile_end(oscar_pool *pool, oscar_profile *out);
 
 const char *oscar_last_error(void);
