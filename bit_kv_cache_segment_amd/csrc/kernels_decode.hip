@@ -45,6 +45,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kIdCache = 1024; // page ids staged in shared memory per segment of a split
 constexpr float kLazy = 8.f; // log2 headroom of the lazy softmax reference (host keeps 2^kLazy in pv_shift)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -52,6 +53,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Waves per SIMD the register budget is sized for (3 where it fits without
+// spilling: more waves in flight hide more HBM latency).
+constexpr int main_occupancy(int D, int G, int GQ) { return (GQ <= 4 || (GQ == 8 && D == G)) ? 3 : (GQ <= 8 ? 2 : 1); }
+
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu)); }
@@ -68,23 +75,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 // reductions over the 16 lanes of an aligned lane row
-__device__ __forceinline__ float row16_max(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
 __device__ __forceinline__ float row16_sum(float v) {
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Sum over aligned groups of N lanes (N = 8 or 16) by DPP butterflies; every
+// lane of a group ends with the same bits (each step adds a commuted pair).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  v += dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v); // row_half_mirror: quad 0 <-> quad 1 of each 8 lanes
+  if constexpr (N == 16) v += dpp_f<0x140>(v); // row_mirror: halves of each 16 lanes
+  return v;
+}
+
+// Maximum over aligned groups of 16 lanes (one DPP row), in every lane.
+__device__ __forceinline__ float row16_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return fmaxf(v, dpp_f<0x140>(v));
+}
+// 2^x by the hardware instruction (x = -inf gives 0; results below the
+// normal range flush to 0, which a softmax weight can afford).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Order LDS traffic of the lanes of one wave (no cross-wave barrier).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-__device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ? 0.f : exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // shared memory
@@ -95,6 +122,7 @@ struct HistSmem {
   float alpha[kWaves][16];  // per-wave rescale factors of the PV rows
   float zsum[kWaves][16][NG];
   float M[kWaves][GQ], L[kWaves][GQ];
+  int32_t ids[kIdCache];                     // page ids of a segment of the split
   union {
     _Float16 P[kWaves][NG][16][64];          // page loop: P' rows per wave
     float A[kWaves][GQ][D];                  // epilogue: per-wave accumulators
@@ -111,8 +139,7 @@ struct QPrepSmem {
 
 template <int D, int GQ>
 struct WinSmem {
-  float qs[GQ][D];
-  float P[kWaves][GQ][64];
+  uint32_t q2[GQ][D / 2]; // query rows as bf16 pairs
   float M[kWaves][GQ], L[kWaves][GQ];
   float A[kWaves][GQ][D];
 };
@@ -148,103 +175,133 @@ __device__ void block_merge_store(const float (*M)[GQ], const float (*L)[GQ], co
 }
 
 // ---------------------------------------------------------------------------
-// BF16 sink + recent window: one block per (sequence, kv head).  Lanes own
-// tokens for QK^T and channels for PV (fp32 VALU).
+// BF16 sink + recent window of one (sequence, kv head), up to 320 tokens.
+// A wave load covers TPI consecutive token rows (1 KB): lane (ts, cc) holds
+// channels 8 cc .. 8 cc + 7 of token TPI gi + ts.  Token groups gi go round
+// robin over the waves; each wave issues the K and V loads of WG groups at
+// once, then computes them: QK^T by bf16 dot2 and a DPP sum over the D/8
+// lanes of a token, a lazy online softmax per lane (reference moved only
+// when a logit exceeds it by kLazy), PV into fp32 accumulators of the lane's
+// 8 channels.  Token slots and waves are merged at the end.
 // ---------------------------------------------------------------------------
-template <int D, int GQ>
+template <int D, int G, int GQ>
+constexpr int win_groups() {
+  constexpr int TPI = 512 / D, nk = kWindow / TPI / kWaves; // groups per wave
+  // unified VGPR file share of a wave, at most 256 addressable VGPRs
+  constexpr int budget = 512 / main_occupancy(D, G, GQ) / 8 * 8 < 256 ? 512 / main_occupancy(D, G, GQ) / 8 * 8 : 256;
+  constexpr int fit = (budget - 10 * GQ - 48) / 8;           // 8 registers per group in flight
+  constexpr int hk = fit < 1 ? 1 : (fit < nk ? fit : nk);
+  constexpr int passes = (nk + hk - 1) / hk;
+  return (nk + passes - 1) / passes;
+}
+
+template <int D, int G, int GQ>
 __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
                              float qscale, float *ws_win, int idx0) {
+  constexpr int LPT = D / 8, TPI = 64 / LPT, WG = win_groups<D, G, GQ>();
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+  const int ts = lane / LPT, cc = lane % LPT;
   const int Hkv = p.Hkv, Hq = p.Hq;
   const int e = idx0 / Hkv, kv = idx0 % Hkv;
   const int seq = b.seq[e], L = b.len[e];
   const int n_sink = min(L, kSink), n_rec = min(max(L - kSink, 0), kRecent), n_win = n_sink + n_rec;
-  for (int idx = tid; idx < GQ * D; idx += kThreads)
-    sm.qs[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]) * qscale;
+  {
+    const uint32_t *src = (const uint32_t *)(q + ((size_t)e * Hq + kv * GQ) * D);
+    for (int idx = tid; idx < GQ * D / 2; idx += kThreads) sm.q2[idx / (D / 2)][idx % (D / 2)] = src[idx];
+  }
   __syncthreads();
   const uint16_t *sinkK = p.sinkK + ((size_t)seq * Hkv + kv) * kSink * D;
   const uint16_t *sinkV = p.sinkV + ((size_t)seq * Hkv + kv) * kSink * D;
   const uint16_t *recK = p.recentK + ((size_t)seq * Hkv + kv) * kRecent * D;
   const uint16_t *recV = p.recentV + ((size_t)seq * Hkv + kv) * kRecent * D;
 
-  float m_run[GQ], l_run[GQ], acc[GQ][D / 64];
+  float m_ref[GQ], l_run[GQ], acc[GQ][8];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    m_run[h] = -INFINITY;
+    m_ref[h] = -INFINITY;
     l_run[h] = 0.f;
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) acc[h][k] = 0.f;
+    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
   }
-  const int nch = (n_win + 63) / 64;
-  constexpr int CPL = D / 64; // channels per lane in PV (adjacent)
-  for (int ch = w; ch < nch; ch += kWaves) {
-    const int ntok = min(64, n_win - ch * 64);
-    const int u = ch * 64 + lane;
-    float lg[GQ];
+  const int ngroups = (n_win + TPI - 1) / TPI;
+  const int nk = (ngroups - w + kWaves - 1) / kWaves; // groups of this wave
+  for (int k0 = 0; k0 < nk; k0 += WG) {
+    u32x4 kr[WG], vr[WG];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) lg[h] = -INFINITY;
-    if (lane < ntok) {
-      // QK^T: this lane's token row, all loads in flight at once
-      const u32x4 *row = (const u32x4 *)(u < n_sink ? sinkK + (size_t)u * D : recK + (size_t)(u - n_sink) * D);
-      u32x4 kw[D / 8];
+    for (int i = 0; i < WG; ++i) {
+      const int u = (w + kWaves * (k0 + i)) * TPI + ts;
+      kr[i] = vr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (k0 + i < nk && u < n_win) {
+        const size_t off = (size_t)(u < n_sink ? u : u - n_sink) * D + 8 * cc;
+        kr[i] = __builtin_nontemporal_load((const u32x4 *)((u < n_sink ? sinkK : recK) + off));
+        vr[i] = __builtin_nontemporal_load((const u32x4 *)((u < n_sink ? sinkV : recV) + off));
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) kw[i] = row[i];
+    for (int i = 0; i < WG; ++i) {
+      if (k0 + i >= nk) break;
+      const int u = (w + kWaves * (k0 + i)) * TPI + ts;
+      const bool ok = u < n_win;
+      float vf[8];
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) lg[h] = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        vf[2 * j] = __uint_as_float(vr[i][j] << 16);
+        vf[2 * j + 1] = __uint_as_float(vr[i][j] & 0xffff0000u);
+      }
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
+      for (int h = 0; h < GQ; ++h) {
+        const u32x4 qv = *(const u32x4 *)&sm.q2[h][4 * cc];
+        float d = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float kc = __uint_as_float(k & 1 ? (kw[i][k / 2] & 0xffff0000u) : (kw[i][k / 2] << 16));
-#pragma unroll
-          for (int h = 0; h < GQ; ++h) lg[h] = fmaf(sm.qs[h][8 * i + k], kc, lg[h]);
+        for (int j = 0; j < 4; ++j) {
+          // element copies first: a bit cast of a vector element itself
+          // would read element 0
+          const uint32_t kw = kr[i][j], qw = qv[j];
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qw), d, false);
         }
-      }
-    }
+        d = lanes_sum<LPT>(d);
+        const float sc = ok ? d * qscale : -INFINITY;
+        const bool jump = sc > m_ref[h] + kLazy;
+        if (__any(jump)) {
+          const float mn = jump ? sc : m_ref[h];
+          const float al = jump ? fast_exp2(m_ref[h] - mn) : 1.f;
+          l_run[h] *= al;
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      const float mt = wave_max(lg[h]);
-      const float mnew = fmaxf(m_run[h], mt);
-      const float alpha = exp2_or_zero(m_run[h] - mnew);
-      const float pr = exp2_or_zero(lg[h] - mnew);
-      l_run[h] = l_run[h] * alpha + wave_sum(pr);
-      m_run[h] = mnew;
-      sm.P[w][h][lane] = pr;
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[h][k] *= alpha;
-    }
-    wave_sync();
-    // PV: lanes own CPL adjacent channels; V values of 8 tokens in flight
-    for (int t8 = 0; t8 < ntok; t8 += 8) {
-      uint32_t vv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int uu = ch * 64 + min(t8 + k, ntok - 1);
-        const uint16_t *row = uu < n_sink ? sinkV + (size_t)uu * D : recV + (size_t)(uu - n_sink) * D;
-        vv[k] = CPL == 2 ? *(const uint32_t *)(row + 2 * lane) : (uint32_t)row[lane];
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (t8 + k < ntok) {
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const float v = __uint_as_float(c ? (vv[k] & 0xffff0000u) : (vv[k] << 16));
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) acc[h][c] = fmaf(sm.P[w][h][t8 + k], v, acc[h][c]);
-          }
+          for (int j = 0; j < 8; ++j) acc[h][j] *= al;
+          m_ref[h] = mn;
         }
+        const float pr = ok ? fast_exp2(sc - m_ref[h]) : 0.f;
+        l_run[h] += pr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pr, vf[j], acc[h][j]);
       }
     }
-    wave_sync();
   }
+  // merge the TPI token slots of the wave (lanes cc, cc + LPT, ...)
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    if (lane == 0) {
-      sm.M[w][h] = m_run[h];
-      sm.L[w][h] = l_run[h];
-    }
+    float m = m_ref[h];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) sm.A[w][h][CPL * lane + k] = acc[h][k];
+    for (int o = LPT; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float f = m_ref[h] == -INFINITY ? 0.f : exp2f(m_ref[h] - m);
+    float l = l_run[h] * f;
+#pragma unroll
+    for (int o = LPT; o < 64; o <<= 1) l += __shfl_xor(l, o, 64);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float a = acc[h][j] * f;
+#pragma unroll
+      for (int o = LPT; o < 64; o <<= 1) a += __shfl_xor(a, o, 64);
+      acc[h][j] = a;
+    }
+    if (lane == 0) {
+      sm.M[w][h] = m;
+      sm.L[w][h] = l;
+    }
+    if (ts == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm.A[w][h][8 * cc + j] = acc[h][j];
+    }
   }
   __syncthreads();
   block_merge_store<D, GQ>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * Hq + kv * GQ) * (D + 2));
@@ -362,19 +419,22 @@ struct PageRegs {
 template <int D, int G>
 __device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk, int n, int r) {
   constexpr int NG = D / G;
-  const u32x4 *kc = (const u32x4 *)(blk + r * 4 * D + 4 * n * (D / 16));
-  const u32x4 *vc = (const u32x4 *)(blk + 16 * D + r * 4 * D + 4 * (D / 16) * n);
+  // codes: 1 KB contiguous per instruction; params: 16 lanes share 256 B.
+  // Every byte is read once per call: non-temporal loads.
+  const int lane = 16 * r + n;
+  const u32x4 *kc = (const u32x4 *)(blk + 16 * lane);
+  const u32x4 *vc = (const u32x4 *)(blk + 16 * D + 16 * lane);
   const u32x4 *kp = (const u32x4 *)(blk + 32 * D + 16 * NG * n);
   const u32x4 *vp = (const u32x4 *)(blk + 32 * D + 256 * NG + 16 * NG * n);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
-    pr.kc[i] = kc[i];
-    pr.vc[i] = vc[i];
+    pr.kc[i] = __builtin_nontemporal_load(kc + 64 * i);
+    pr.vc[i] = __builtin_nontemporal_load(vc + 64 * i);
   }
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    pr.kp[g] = kp[g];
-    pr.vp[g] = vp[g];
+    pr.kp[g] = __builtin_nontemporal_load(kp + g);
+    pr.vp[g] = __builtin_nontemporal_load(vp + g);
   }
 }
 
@@ -384,7 +444,7 @@ constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
 template <int D, int G, int GQ>
 __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const DecodeBatch &b,
-                              const uint32_t *qrec, float *ws_hist, int blk) {
+                              const uint32_t *qrec, float *ws_hist, int blk, int e, int p0, int p1) {
   constexpr int NG = D / G;                // scale/zero groups per token
   constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
   constexpr int RT = GQ >= 4 ? GQ / 4 : 1; // MFMA row tiles of 4 heads x 4 limb rows
@@ -392,17 +452,9 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n = lane & 15, r = lane >> 4;
   const int Hkv = p.Hkv;
-  const int kv = blk % Hkv, sidx = blk / Hkv;
-  int lo = 0, hi = b.n;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) / 2;
-    if (b.split_prefix[mid] <= sidx) lo = mid;
-    else hi = mid;
-  }
-  const int e = lo, s = sidx - b.split_prefix[e];
+  const int kv = blk % Hkv;
   const int seq = b.seq[e], n_hist = b.len[e] - kWindow;
   const int np = (n_hist + kPage - 1) / kPage;
-  const int p0 = s * b.pages_per_split, p1 = min(np, p0 + b.pages_per_split);
 
   // ---- prologue: load this pair's query record; rows of P' that no head
   // owns stay zero for the whole loop.
@@ -482,7 +534,9 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
           float l = 0.f;
   #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            const float dv = (float)cacc[rt][g][0] + 256.f * (float)cacc[rt][g][1] + 65536.f * (float)cacc[rt][g][2];
+            // |dv| < 2^31: the limb sum is exact in wrapping int32 arithmetic
+            const float dv = (float)(int)((uint32_t)cacc[rt][g][0] + ((uint32_t)cacc[rt][g][1] << 8) +
+                                          ((uint32_t)cacc[rt][g][2] << 16));
             const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
             l = fmaf(f16lo(sz) * kfac[rt], dv, fmaf(f16hi(sz), qsum[rt][g], l));
           }
@@ -495,13 +549,13 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
       for (int rt = 0; rt < RT; ++rt) {
         const int hrow = rt * 4 + r;
         float mt = fmaxf(fmaxf(lg[rt][0], lg[rt][1]), fmaxf(lg[rt][2], lg[rt][3]));
-        mt = row16_max(mt);
+        mt = row16_max_dpp(mt);
         // The running reference moves only when a page's maximum exceeds it
         // by more than kLazy: weights stay <= 2^kLazy and the PV accumulators
         // are rescaled rarely.
         const bool jump = mt > m_run[rt] + kLazy;
         const float mnew = jump ? mt : m_run[rt];
-        const float alpha = jump ? exp2_or_zero(m_run[rt] - mnew) : 1.f;
+        const float alpha = jump ? fast_exp2(m_run[rt] - mnew) : 1.f;
         m_run[rt] = mnew;
         float psum = 0.f;
         float zadd[NG];
@@ -511,7 +565,7 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   #pragma unroll
         for (int T = 0; T < 4; ++T) {
           const bool ok = (full && GQ >= 4) || lg[rt][T] != -INFINITY;
-          const float pt = ok ? exp2f(lg[rt][T] - mnew) : 0.f;
+          const float pt = ok ? fast_exp2(lg[rt][T] - mnew) : 0.f;
           psum += pt;
   #pragma unroll
           for (int g = 0; g < NG; ++g) {
@@ -566,62 +620,58 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
       wave_sync();
   };
 
-  // Two register buffers in ping-pong: the loads of the wave's next page are
-  // in flight while the current one is computed (no register copy between
-  // iterations, so no wait on the prefetch before the next compute).
-  // Only a sequence's last page can be partial; it is handled after the loop.
+  // Register buffers in rotation: the loads of the wave's next page(s) are in
+  // flight while the current one is computed (no register copy between
+  // iterations).  Page ids come from shared memory, staged per segment of up
+  // to kIdCache pages, so a prefetch never waits on a page-table load.
+  // Only a sequence's last page can be partial; it is handled last.
   const int pf = (n_hist % kPage == 0) ? p1 : min(p1, np - 1); // end of full pages
-  // Page ids of this wave's pages (p0 + w + 4k) sit one per lane, 64 at a
-  // time, so a prefetch does not wait on a page-table load first.
-  int pt_vec = 0, pt_chunk = -1;
-  auto page_id = [&](int page_idx) __attribute__((always_inline)) {
-    const int k = (page_idx - p0 - w) / kWaves, chunk = k >> 6;
-    if (chunk != pt_chunk) {
-      const int idx = p0 + w + kWaves * (chunk * 64 + lane);
-      pt_vec = idx < p1 ? ptab[idx] : 0;
-      pt_chunk = chunk;
-    }
-    return __builtin_amdgcn_readlane(pt_vec, k & 63);
-  };
-  auto load = [&](PageRegs<D, G> &buf, int page_idx) __attribute__((always_inline)) {
-    load_page<D, G>(buf, p.pages + (size_t)page_id(page_idx) * hstride + hoff, n, r);
-  };
   constexpr int W = kWaves;
-  PageRegs<D, G> bufA, bufB;
-  int pi = p0 + w;
-  if (pi < pf) load(bufA, pi);
-  if constexpr (kPrefetch<D, G, GQ> >= 2) {
-    // three register buffers in rotation: two pages in flight per wave
-    PageRegs<D, G> bufC;
-    if (pi + W < pf) load(bufB, pi + W);
-    while (pi < pf) {
-      if (pi + 2 * W < pf) load(bufC, pi + 2 * W);
-      page_step(bufA, pi, true);
-      pi += W;
-      if (pi >= pf) break;
-      if (pi + 2 * W < pf) load(bufA, pi + 2 * W);
-      page_step(bufB, pi, true);
-      pi += W;
-      if (pi >= pf) break;
-      if (pi + 2 * W < pf) load(bufB, pi + 2 * W);
-      page_step(bufC, pi, true);
-      pi += W;
+  for (int s0 = p0; s0 < p1; s0 += kIdCache) {
+    const int s1 = min(p1, s0 + kIdCache), sf = min(s1, pf);
+    if (s0 != p0) __syncthreads(); // every wave is done with the previous ids
+    for (int i = s0 + tid; i < s1; i += kThreads) sm.ids[i - s0] = ptab[i];
+    __syncthreads();
+    auto load = [&](PageRegs<D, G> &buf, int page_idx) __attribute__((always_inline)) {
+      const int id = __builtin_amdgcn_readfirstlane(sm.ids[page_idx - s0]);
+      load_page<D, G>(buf, p.pages + (size_t)id * hstride + hoff, n, r);
+    };
+    PageRegs<D, G> bufA, bufB;
+    int pi = s0 + w;
+    if (pi < sf) load(bufA, pi);
+    if constexpr (kPrefetch<D, G, GQ> >= 2) {
+      // three register buffers in rotation: two pages in flight per wave
+      PageRegs<D, G> bufC;
+      if (pi + W < sf) load(bufB, pi + W);
+      while (pi < sf) {
+        if (pi + 2 * W < sf) load(bufC, pi + 2 * W);
+        page_step(bufA, pi, true);
+        pi += W;
+        if (pi >= sf) break;
+        if (pi + 2 * W < sf) load(bufA, pi + 2 * W);
+        page_step(bufB, pi, true);
+        pi += W;
+        if (pi >= sf) break;
+        if (pi + 2 * W < sf) load(bufB, pi + 2 * W);
+        page_step(bufC, pi, true);
+        pi += W;
+      }
+    } else {
+      // two register buffers in ping-pong: one page in flight per wave
+      while (pi < sf) {
+        if (pi + W < sf) load(bufB, pi + W);
+        page_step(bufA, pi, true);
+        pi += W;
+        if (pi >= sf) break;
+        if (pi + W < sf) load(bufA, pi + W);
+        page_step(bufB, pi, true);
+        pi += W;
+      }
     }
-  } else {
-    // two register buffers in ping-pong: one page in flight per wave
-    while (pi < pf) {
-      if (pi + W < pf) load(bufB, pi + W);
-      page_step(bufA, pi, true);
-      pi += W;
-      if (pi >= pf) break;
-      if (pi + W < pf) load(bufA, pi + W);
-      page_step(bufB, pi, true);
-      pi += W;
+    if (pf < s1 && pf >= s0 && (pf - s0) % W == w) {
+      load(bufA, pf);
+      page_step(bufA, pf, false);
     }
-  }
-  if (pf < p1 && (pf - p0) % W == w) {
-    load(bufA, pf);
-    page_step(bufA, pf, false);
   }
 
   // ---- epilogue: per-wave (m, l, acc) then the block merge
@@ -652,9 +702,6 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   block_merge_store<D, GQ>(sm.M, sm.L, sm.u.A, ws_hist + (size_t)blk * GQ * (D + 2));
 }
 
-// Waves per SIMD the register budget is sized for (3 where it fits without
-// spilling: more waves in flight hide more HBM latency).
-constexpr int main_occupancy(int D, int G, int GQ) { return (GQ <= 4 || (GQ == 8 && D == G)) ? 3 : (GQ <= 8 ? 2 : 1); }
 
 template <int D, int G, int GQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
@@ -664,11 +711,23 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   __shared__ MainSmem<D, G, GQ> sm;
   float *ws_win = ws;
   float *ws_hist = ws + (size_t)b.n * p.Hq * (D + 2);
-  const int nwin = b.n * p.Hkv;
-  if ((int)blockIdx.x < nwin)
-    window_block<D, GQ>(sm.w, p, b, q, qscale, ws_win, blockIdx.x);
-  else
-    history_block<D, G, GQ>(sm.h, p, b, qrec, ws_hist, blockIdx.x - nwin);
+  const int blk = blockIdx.x, Hkv = p.Hkv;
+  const int kv = blk % Hkv, sidx = blk / Hkv;
+  int lo = 0, hi = b.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (b.split_prefix[mid] <= sidx) lo = mid;
+    else hi = mid;
+  }
+  const int e = lo, s = sidx - b.split_prefix[e], S = b.split_prefix[e + 1] - b.split_prefix[e];
+  const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
+  int p0, p1;
+  split_range(np, S, s, b.win_units, p0, p1);
+  if (p0 < p1) history_block<D, G, GQ>(sm.h, p, b, qrec, ws_hist, blk, e, p0, p1);
+  if (s == S - 1) {
+    if (p0 < p1) __syncthreads(); // the window reuses the history's shared memory
+    window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, e * Hkv + kv);
+  }
 }
 
 // Merge of one (sequence, kv head): split partials -> history (m, l, acc),
@@ -696,9 +755,17 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
   const float *ws_win = ws;
   const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
   const int s0 = b.split_prefix[e], S = b.split_prefix[e + 1] - s0;
+  // splits that hold history pages (a split may hold the window alone)
+  const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
+  uint32_t has = 0;
+  for (int s = 0; s < S; ++s) {
+    int p0, p1;
+    split_range(np, S, s, b.win_units, p0, p1);
+    if (p0 < p1) has |= 1u << s;
+  }
   const size_t stride = (size_t)Hkv * GQ * (D + 2); // between splits of one pair
   const float *part0 = ws_hist + ((size_t)s0 * Hkv + kv) * GQ * (D + 2);
-  if (S > 0) {
+  if (has) {
     const u32x4 *src = (const u32x4 *)(p.RVt + (size_t)kv * D * D);
     u32x4 *dst = (u32x4 *)&sm.R[0][0];
     constexpr int NL = D * D / 4 / kMergeThreads;
@@ -722,9 +789,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
     const float *ph = part0 + (size_t)h * (D + 2);
 #pragma unroll
     for (int s = 0; s < kMaxSplitsDev; ++s) {
-      ms[s] = s < S ? ph[s * stride + D] : -INFINITY;
-      ls[s] = s < S ? ph[s * stride + D + 1] : 0.f;
-      as[s] = s < S ? ph[s * stride + c] : 0.f;
+      const bool v = has >> s & 1u;
+      ms[s] = v ? ph[s * stride + D] : -INFINITY;
+      ls[s] = v ? ph[s * stride + D + 1] : 0.f;
+      as[s] = v ? ph[s * stride + c] : 0.f;
     }
     float m = -INFINITY;
 #pragma unroll
@@ -732,14 +800,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
     float l = 0.f, a = 0.f;
 #pragma unroll
     for (int s = 0; s < kMaxSplitsDev; ++s) {
-      const float f = s < S ? exp2f(ms[s] - m) : 0.f;
+      const float f = has >> s & 1u ? exp2f(ms[s] - m) : 0.f;
       l = fmaf(f, ls[s], l);
       a = fmaf(f, as[s], a);
     }
     mH[k] = m;
     lH[k] = l;
     aH[k] = a;
-    if (S > 0 && hg + k * HG < GQ) sm.AH[h][c] = a;
+    if (has && hg + k * HG < GQ) sm.AH[h][c] = a;
   }
   __syncthreads();
 #pragma unroll
@@ -747,7 +815,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
     const int h = hg + k * HG;
     if (h >= GQ) continue;
     float o;
-    if (S > 0) {
+    if (has) {
       float der = 0.f;
 #pragma unroll 16
       for (int j = 0; j < D; ++j) der = fmaf(sm.AH[h][j], sm.R[j][c], der);
@@ -764,11 +832,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
 template <int D, int G, int GQ>
 hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                        float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
-  const int blocks = b.n * p.Hkv + b.hist_blocks;
+  const int blocks = b.hist_blocks;
   uint32_t *qrec = (uint32_t *)(ws + (size_t)b.n * p.Hq * (D + 2) + (size_t)b.hist_blocks * GQ * (D + 2));
   // Timed launches take their start/stop timestamps from the dispatch itself
   // (no extra packets between kernels).
-  if (b.hist_blocks > 0)
+  if (b.total_pages > 0)
     hipExtLaunchKernelGGL((q_prep_kernel<D, G, GQ>), dim3(b.n * p.Hkv), dim3(kThreads), 0, s,
                           tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, qrec);
   hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(kThreads), 0, s, tm.on ? tm.ev[0] : nullptr,
@@ -791,7 +859,28 @@ hipError_t decode_g(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, f
   return hipErrorInvalidValue;
 }
 
+template <int D, int G>
+int blocks_per_cu_g(const PoolDev &p) {
+  int nb = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (p.Hq / p.Hkv) {
+  case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 1>, kThreads, 0); break;
+  case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 2>, kThreads, 0); break;
+  case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 4>, kThreads, 0); break;
+  case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 8>, kThreads, 0); break;
+  case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 16>, kThreads, 0); break;
+  }
+  return e == hipSuccess ? nb : 0;
+}
+
 } // namespace
+
+int decode_main_blocks_per_cu(const PoolDev &p) {
+  if (p.d == 128 && p.G == 128) return blocks_per_cu_g<128, 128>(p);
+  if (p.d == 128 && p.G == 64) return blocks_per_cu_g<128, 64>(p);
+  if (p.d == 64 && p.G == 64) return blocks_per_cu_g<64, 64>(p);
+  return 0;
+}
 
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                          float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {

@@ -102,18 +102,52 @@ Layout layout_of(const oscar_pool_config &c) {
 
 int pages_for(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPage); }
 
-// Split policy of one decode launch: pages per split is a multiple of 4 (one
-// page per wave per step), at least 8, large enough for ~2048 split blocks
-// in total and for at most kMaxSplits splits per (sequence, kv head).
+// Split policy of one decode launch.  A pair's work is its history pages
+// plus its window, worth win_units pages (the window's bytes over a page
+// block's bytes, times kWindowCost).  Pieces of at most P units: a pair gets
+// S = ceil(U / P) splits (at most kMaxSplits), and P is the smallest piece
+// size for which all blocks fit in kSplitRounds rounds of the device's
+// resident block slots (compute units x decode blocks per unit), so that no
+// block waits for a slot and every slot streams until the end.
 constexpr int kMaxSplits = 32;
-constexpr int kTargetBlocks = 2048;
+constexpr int kSplitRounds = 1;
+constexpr double kWindowCost = 1.0;
 
-int choose_pages_per_split(int64_t total_pages, int max_np, int Hkv) {
-  int64_t ps = (total_pages * Hkv + kTargetBlocks - 1) / kTargetBlocks;
-  ps = std::max<int64_t>(ps, (max_np + kMaxSplits - 1) / kMaxSplits);
-  ps = std::max<int64_t>(ps, 8);
-  ps = (ps + 3) / 4 * 4;
-  return (int)ps;
+int window_units(int d, int G) {
+  return (int)std::lround(kWindowCost * (double)kWindow * 4 * d / block_bytes_for(d, G));
+}
+
+void plan_splits(DecodeBatch &b, const std::vector<int> &np, int Hkv, int slots, int wu) {
+  b.win_units = wu;
+  int64_t total = 0, umax = 1;
+  for (int e = 0; e < b.n; ++e) {
+    total += np[e];
+    umax = std::max<int64_t>(umax, np[e] + wu);
+  }
+  b.total_pages = (int32_t)total;
+  // at most U / wu splits: pieces of at least a window keep every split but
+  // the last one on history pages
+  auto splits = [&](int e, int64_t P) {
+    const int64_t U = np[e] + wu;
+    int64_t S = std::min<int64_t>(kMaxSplits, (U + P - 1) / P);
+    if (wu > 0) S = std::min<int64_t>(S, U / wu);
+    return (int)std::max<int64_t>(1, S);
+  };
+  auto blocks = [&](int64_t P) {
+    int64_t nb = 0;
+    for (int e = 0; e < b.n; ++e) nb += splits(e, P);
+    return nb * Hkv;
+  };
+  const int64_t budget = (int64_t)kSplitRounds * slots;
+  int64_t lo = 1, hi = umax; // blocks(umax) = n * Hkv: the fewest possible
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (blocks(mid) <= budget) hi = mid;
+    else lo = mid + 1;
+  }
+  b.split_prefix[0] = 0;
+  for (int e = 0; e < b.n; ++e) b.split_prefix[e + 1] = b.split_prefix[e] + splits(e, lo);
+  b.hist_blocks = b.split_prefix[b.n] * Hkv;
 }
 
 } // namespace
@@ -137,7 +171,7 @@ struct Profiler {
   }
   void release() {
     for (auto &v : ev) {
-      for (hipEvent_t e : v) hipEventDestroy(e);
+      for (hipEvent_t e : v) (void)hipEventDestroy(e);
       v.clear();
     }
     on = false;
@@ -153,6 +187,7 @@ struct oscar_pool {
   Layout lay;
   PoolDev dev;
   bool host_only;
+  int decode_slots = 768; // resident decode blocks on the device
   std::vector<int32_t> len;
   std::vector<std::vector<int32_t>> table;
   std::vector<int32_t> free_list; // pages [free_head, end) are free, front first
@@ -286,6 +321,15 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
       delete p;
       return hip_fail(e, "copying rotation/clip tables");
     }
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int per_cu = decode_main_blocks_per_cu(D);
+    if (e != hipSuccess || cus <= 0 || per_cu <= 0) {
+      delete p;
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "querying the decode occupancy");
+    }
+    p->decode_slots = cus * per_cu;
   }
   *out = p;
   return ok();
@@ -438,23 +482,14 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
     DecodeBatch b;
     b.n = std::min(kMaxBatch, n - i0);
-    int64_t total = 0;
-    int max_np = 0;
+    std::vector<int> np(b.n);
     for (int e = 0; e < b.n; ++e) {
       int32_t s = seq_ids[i0 + e];
       b.seq[e] = s;
       b.len[e] = p->len[s];
-      int np = pages_for(std::max(0, b.len[e] - kWindow));
-      total += np;
-      max_np = std::max(max_np, np);
+      np[e] = pages_for(std::max(0, b.len[e] - kWindow));
     }
-    b.pages_per_split = choose_pages_per_split(total, max_np, Hkv);
-    b.split_prefix[0] = 0;
-    for (int e = 0; e < b.n; ++e) {
-      int np = pages_for(std::max(0, b.len[e] - kWindow));
-      b.split_prefix[e + 1] = b.split_prefix[e] + (np + b.pages_per_split - 1) / b.pages_per_split;
-    }
-    b.hist_blocks = b.split_prefix[b.n] * Hkv;
+    plan_splits(b, np, Hkv, p->decode_slots, window_units(d, p->cfg.group_size));
     need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
     batches.push_back(b);
   }

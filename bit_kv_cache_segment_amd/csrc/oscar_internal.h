@@ -41,32 +41,35 @@ struct PoolDev {
 //
 //   [K codes 16d B][V codes 16d B][K params 256 d/G B][V params 256 d/G B]
 //
-// K codes, token-major in four channel quarters ("quads").  The 16
-// channels {64m + 16r + k : k < 16} of token t form one little-endian
-// dword (channel 64m+16r+k in bits 2k..2k+1) at byte
-//      r * 4d + t * (d/16) + 4m            (r = 0..3, m = 0..d/64-1).
-// A lane that owns (quad r, tokens t..t+3) reads d/4 contiguous bytes.
+// Code bytes are ordered so that the lanes of a wave read them with
+// contiguous 16-byte loads: the code region is a sequence of 1 KB chunks,
+// chunk i holding bytes 16 i .. 16 i + 15 of every lane's share, lane l at
+// byte 16 l of the chunk (lane l = 16 r + n).
 //
-// V codes, channel-major in 16-token blocks.  The 16 tokens
-// {16 tb + k : k < 16} of channel c form one dword at byte
-//      16d + tb * 4d + 4 * sigma(c),   sigma(c) = (d/16) * (c % 16) + c / 16,
-// so that the d/16 dwords a lane needs for channels {c : c % 16 == n} are
-// contiguous.  Inside the dword, token k sits at bit vbit(k) =
-// 16 (k & 1) + 2 (k >> 1): even tokens fill the low half, odd tokens the
-// high half, so one AND with 0x00030003 << 2i yields tokens (2i, 2i+1) as a
-// pair of fp16 sub-normals.
+// K codes (16d bytes from 0): lane (n, r) owns tokens 4n .. 4n+3 of channel
+// quarter r; its share is token-major, d/16 bytes per token.  The 16
+// channels {64m + 16r + k : k < 16} of token t form one little-endian dword
+// (channel 64m+16r+k in bits 2k..2k+1) at lane-share byte
+// b = (t % 4) * (d/16) + 4m of lane (t / 4, r).
+//
+// V codes (16d bytes from 16d): lane (n, r) owns the 16 tokens
+// {16 r + k : k < 16} (a "token block") of the channels {16 j + n}; the
+// dword of channel c = 16 j + n sits at lane-share byte b = 4j.  Inside the
+// dword, token k sits at bit vbit(k) = 16 (k & 1) + 2 (k >> 1): even tokens
+// fill the low half, odd tokens the high half, so one AND with
+// 0x00030003 << 2i yields tokens (2i, 2i+1) as a pair of fp16 sub-normals.
 //
 // Params: fp16 (scale, zero) of token t, group g at byte
 //      32d + 4 (t * d/G + g)               (K)
 //      32d + 256 d/G + 4 (t * d/G + g)     (V)
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int block_bytes_for(int d, int G) { return 32 * d + 512 * d / G; }
+__host__ __device__ inline int lane_share_off(int lane, int b) { return (b / 16) * 1024 + lane * 16 + b % 16; }
 __host__ __device__ inline int kcode_dword_off(int d, int t, int r, int m) {
-  return r * 4 * d + t * (d / 16) + 4 * m;
+  return lane_share_off(16 * r + t / 4, (t % 4) * (d / 16) + 4 * m);
 }
-__host__ __device__ inline int vsigma(int d, int c) { return (d / 16) * (c % 16) + c / 16; }
 __host__ __device__ inline int vcode_dword_off(int d, int tb, int c) {
-  return 16 * d + tb * 4 * d + 4 * vsigma(d, c);
+  return 16 * d + lane_share_off(16 * tb + c % 16, 4 * (c / 16));
 }
 __host__ __device__ inline int vbit(int k) { return 16 * (k & 1) + 2 * (k >> 1); }
 __host__ __device__ inline int kparam_off(int d, int G, int t, int g) {
@@ -84,15 +87,30 @@ struct AppendBatch {
   int32_t new_page[kMaxBatch]; // page taken by this append, or -1
 };
 
-// By-value metadata of one decode launch (<= kMaxBatch sequences).
+// By-value metadata of one decode launch (<= kMaxBatch sequences).  The work of a (sequence, kv head) pair is its np
+// history pages plus its BF16 window, counted as win_units pages; it is cut
+// into S splits of about equal work (split_range), the window going to the
+// last split.  One block per (split, kv head): block = split * Hkv + kv.
 struct DecodeBatch {
   int32_t n;
-  int32_t pages_per_split;     // history pages per split (multiple of 4)
-  int32_t hist_blocks;         // split blocks: split_prefix[n] * Hkv
+  int32_t hist_blocks;         // blocks: split_prefix[n] * Hkv
+  int32_t win_units;           // window work in page units (>= 0)
+  int32_t total_pages;         // sum of np over the batch
   int32_t seq[kMaxBatch];
   int32_t len[kMaxBatch];
-  int32_t split_prefix[kMaxBatch + 1]; // exclusive prefix of splits per sequence
+  int32_t split_prefix[kMaxBatch + 1]; // exclusive prefix of splits per sequence (each >= 1)
 };
+
+// History pages [p0, p1) of split s of S of a pair with np pages: the pair's
+// units [0, np + wu) are cut evenly, pages are units below np.  Only the last
+// split can be left without pages.
+__host__ __device__ inline void split_range(int np, int S, int s, int wu, int &p0, int &p1) {
+  const long U = (long)np + wu;
+  p0 = (int)(s * U / S);
+  p1 = (int)((s + 1) * U / S);
+  p0 = p0 < np ? p0 : np;
+  p1 = p1 < np ? p1 : np;
+}
 
 // Optional per-kernel timing: when `on`, a launch wrapper records ev[0]
 // before and ev[1] after the kernel on its stream.
@@ -105,9 +123,12 @@ hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const ui
                           int L, hipStream_t s);
 hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t s, const KernelTimer &t);
+// Resident decode_main blocks per compute unit for this pool's shape.
+int decode_main_blocks_per_cu(const PoolDev &p);
+
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out,
                          float scale, float *ws, hipStream_t s, const KernelTimer &t_main,
-                         const KernelTimer &t_merge);
+                         const KernelTimer &t_prep);
 
 // Per (sequence, kv head) query record written by the q-prep kernel and read
 // by every split block of that pair: the int8-limb MFMA A operands
