@@ -45,6 +45,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
+// P' rows hold 64 fp16 weights plus 8 of padding: the PV operand reads of 8
+// lanes (rows n .. n+7 at one column) then fall on distinct LDS banks.
+constexpr int kPRow = 72;
 constexpr int kIdCache = 1024; // page ids staged in shared memory per segment of a split
 constexpr float kLazy = 8.f; // log2 headroom of the lazy softmax reference (host keeps 2^kLazy in pv_shift)
 
@@ -124,7 +127,7 @@ struct HistSmem {
   float M[kWaves][GQ], L[kWaves][GQ];
   int32_t ids[kIdCache];                     // page ids of a segment of the split
   union {
-    _Float16 P[kWaves][NG][16][64];          // page loop: P' rows per wave
+    _Float16 P[kWaves][NG][16][kPRow];       // page loop: P' rows per wave (padded)
     float A[kWaves][GQ][D];                  // epilogue: per-wave accumulators
   } u;
 };
@@ -139,7 +142,7 @@ struct QPrepSmem {
 
 template <int D, int GQ>
 struct WinSmem {
-  uint32_t q2[GQ][D / 2]; // query rows as bf16 pairs
+  alignas(16) uint32_t q2[GQ][D / 2]; // query rows as bf16 pairs
   float M[kWaves][GQ], L[kWaves][GQ];
   float A[kWaves][GQ][D];
 };
@@ -474,7 +477,7 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   for (int idx = tid; idx < kWaves * 16; idx += kThreads) sm.alpha[idx / 16][idx % 16] = 1.f;
   {
     _Float16 *P = &sm.u.P[0][0][0][0];
-    for (int idx = tid; idx < kWaves * NG * 16 * 64; idx += kThreads) P[idx] = (_Float16)0.f;
+    for (int idx = tid; idx < kWaves * NG * 16 * kPRow; idx += kThreads) P[idx] = (_Float16)0.f;
   }
   __syncthreads();
 
@@ -538,7 +541,7 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
             const float dv = (float)(int)((uint32_t)cacc[rt][g][0] + ((uint32_t)cacc[rt][g][1] << 8) +
                                           ((uint32_t)cacc[rt][g][2] << 16));
             const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
-            l = fmaf(f16lo(sz) * kfac[rt], dv, fmaf(f16hi(sz), qsum[rt][g], l));
+            l = fmaf(f16lo(sz), kfac[rt] * dv, fmaf(f16hi(sz), qsum[rt][g], l));
           }
           lg[rt][T] = (tvalid && (GQ >= 4 || rt * 4 + r < GQ)) ? l : -INFINITY;
         }
@@ -571,7 +574,7 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
           for (int g = 0; g < NG; ++g) {
             const uint32_t sz = cur.vp[(T * NG + g) / 4][(T * NG + g) % 4];
             zadd[g] = ok ? fmaf(pt, f16hi(sz), zadd[g]) : zadd[g];
-            pv[g][T] = ok ? pt * f16lo(sz) * pfac[T] : 0.f;
+            pv[g][T] = ok ? f16lo(sz) * (pt * pfac[T]) : 0.f;
           }
         }
         l_run[rt] = fmaf(l_run[rt], alpha, psum);
