@@ -22,6 +22,7 @@ RECENT_TOKENS = 256
 PAGE_TOKENS = 64
 MAX_BATCH_PER_LAUNCH = 256
 POOL_HOST_ONLY = 1
+POOL_DETERMINISTIC = 2
 
 OK, EHIP, ENOMEM, EINVAL, ERANGE = 0, -5, -12, -22, -34
 _NAMES = {EHIP: "EHIP", ENOMEM: "ENOMEM", EINVAL: "EINVAL", ERANGE: "ERANGE"}

@@ -48,7 +48,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // P' rows hold 64 fp16 weights plus 8 of padding: the PV operand reads of 8
 // lanes (rows n .. n+7 at one column) then fall on distinct LDS banks.
 constexpr int kPRow = 72;
-constexpr int kIdCache = 1024; // page ids staged in shared memory per segment of a split
 constexpr float kLazy = 8.f; // log2 headroom of the lazy softmax reference (host keeps 2^kLazy in pv_shift)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -61,6 +60,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Waves per SIMD the register budget is sized for (3 where it fits without
 // spilling: more waves in flight hide more HBM latency).
 constexpr int main_occupancy(int D, int G, int GQ) { return (GQ <= 4 || (GQ == 8 && D == G)) ? 3 : (GQ <= 8 ? 2 : 1); }
+// Waves of a decode_main block: one block fills a compute unit, so no unit
+// holds blocks of different ages (the issue arbiter favours older waves);
+// inside a block the waves share pages dynamically.
+constexpr int main_waves(int D, int G, int GQ) { return 4 * main_occupancy(D, G, GQ); }
 
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -119,16 +122,29 @@ __device__ __forceinline__ void wave_sync() {
 // ---------------------------------------------------------------------------
 // shared memory
 // ---------------------------------------------------------------------------
-template <int D, int G, int GQ>
+template <int D, int GQ, int NW>
+struct WinSmem {
+  alignas(16) uint32_t q2[NW][GQ][D / 2]; // query rows as bf16 pairs, one copy per wave
+  float M[NW][GQ], L[NW][GQ];
+  float A[NW][GQ][D];
+};
+
+// Waves of a history block that process the pair's window while the others
+// start on the pages; they join the page stream afterwards.
+constexpr int win_waves(int W) { return W < 4 ? W : 4; }
+
+template <int D, int G, int GQ, int W>
 struct HistSmem {
   static constexpr int NG = D / G;
-  float alpha[kWaves][16];  // per-wave rescale factors of the PV rows
-  float zsum[kWaves][16][NG];
-  float M[kWaves][GQ], L[kWaves][GQ];
-  int32_t ids[kIdCache];                     // page ids of a segment of the split
+  float alpha[W][16];  // per-wave rescale factors of the PV rows
+  float zsum[W][16][NG];
+  float M[W][GQ], L[W][GQ];
+  int32_t ids[kIdCache];                // page ids of a segment of the split
+  uint32_t claim;                       // next page of the segment to hand out
+  WinSmem<D, GQ, win_waves(W)> win;     // window results of the window waves
   union {
-    _Float16 P[kWaves][NG][16][kPRow];       // page loop: P' rows per wave (padded)
-    float A[kWaves][GQ][D];                  // epilogue: per-wave accumulators
+    _Float16 P[W][NG][16][kPRow];       // page loop: P' rows per wave (padded)
+    float A[W][GQ][D];                  // epilogue: per-wave accumulators
   } u;
 };
 
@@ -140,30 +156,25 @@ struct QPrepSmem {
   int qexp[GQ];
 };
 
-template <int D, int GQ>
-struct WinSmem {
-  alignas(16) uint32_t q2[GQ][D / 2]; // query rows as bf16 pairs
-  float M[kWaves][GQ], L[kWaves][GQ];
-  float A[kWaves][GQ][D];
-};
 
-template <int D, int G, int GQ>
+template <int D, int G, int GQ, int W>
 union MainSmem {
-  HistSmem<D, G, GQ> h;
-  WinSmem<D, GQ> w;
+  HistSmem<D, G, GQ, W> h;
+  WinSmem<D, GQ, W> w;
 };
 
-// Merge per-wave (M, L, A) in shared memory and store one partial per head.
-template <int D, int GQ>
+// Merge per-wave (M, L, A) of the W waves in shared memory and store one
+// partial per head.
+template <int D, int GQ, int W>
 __device__ void block_merge_store(const float (*M)[GQ], const float (*L)[GQ], const float (*A)[GQ][D],
                                   float *dst /*[GQ][D+2]*/) {
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < GQ * D; idx += kThreads) {
+  for (int idx = tid; idx < GQ * D; idx += W * 64) {
     const int h = idx / D, c = idx % D;
     float m = -INFINITY;
-    for (int ww = 0; ww < kWaves; ++ww) m = fmaxf(m, M[ww][h]);
+    for (int ww = 0; ww < W; ++ww) m = fmaxf(m, M[ww][h]);
     float a = 0.f, l = 0.f;
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < W; ++ww) {
       const float f = M[ww][h] == -INFINITY ? 0.f : exp2f(M[ww][h] - m);
       a += f * A[ww][h][c];
       l += f * L[ww][h];
@@ -187,9 +198,9 @@ __device__ void block_merge_store(const float (*M)[GQ], const float (*L)[GQ], co
 // when a logit exceeds it by kLazy), PV into fp32 accumulators of the lane's
 // 8 channels.  Token slots and waves are merged at the end.
 // ---------------------------------------------------------------------------
-template <int D, int G, int GQ>
+template <int D, int G, int GQ, int NW>
 constexpr int win_groups() {
-  constexpr int TPI = 512 / D, nk = kWindow / TPI / kWaves; // groups per wave
+  constexpr int TPI = 512 / D, nk = (kWindow / TPI + NW - 1) / NW; // groups per wave
   // unified VGPR file share of a wave, at most 256 addressable VGPRs
   constexpr int budget = 512 / main_occupancy(D, G, GQ) / 8 * 8 < 256 ? 512 / main_occupancy(D, G, GQ) / 8 * 8 : 256;
   constexpr int fit = (budget - 10 * GQ - 48) / 8;           // 8 registers per group in flight
@@ -198,21 +209,24 @@ constexpr int win_groups() {
   return (nk + passes - 1) / passes;
 }
 
-template <int D, int G, int GQ>
-__device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
-                             float qscale, float *ws_win, int idx0) {
-  constexpr int LPT = D / 8, TPI = 64 / LPT, WG = win_groups<D, G, GQ>();
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+// Window tokens of one (sequence, kv head) processed by NW waves: wave wi
+// takes the token groups wi, wi + NW, ... and leaves its (m, l, acc) in
+// sm.M[wi], sm.L[wi], sm.A[wi] (a block merge combines the NW waves).
+template <int D, int G, int GQ, int NW>
+__device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
+                             float qscale, int e, int kv, int wi) {
+  constexpr int LPT = D / 8, TPI = 64 / LPT, WG = win_groups<D, G, GQ, NW>();
+  const int lane = threadIdx.x % 64;
   const int ts = lane / LPT, cc = lane % LPT;
   const int Hkv = p.Hkv, Hq = p.Hq;
-  const int e = idx0 / Hkv, kv = idx0 % Hkv;
   const int seq = b.seq[e], L = b.len[e];
   const int n_sink = min(L, kSink), n_rec = min(max(L - kSink, 0), kRecent), n_win = n_sink + n_rec;
   {
-    const uint32_t *src = (const uint32_t *)(q + ((size_t)e * Hq + kv * GQ) * D);
-    for (int idx = tid; idx < GQ * D / 2; idx += kThreads) sm.q2[idx / (D / 2)][idx % (D / 2)] = src[idx];
+    // this wave's copy of the query rows: no block barrier needed
+    const uint32_t *src = (const uint32_t *)(q + ((size_t)b.row[e] * Hq + kv * GQ) * D);
+    for (int idx = lane; idx < GQ * D / 2; idx += 64) sm.q2[wi][idx / (D / 2)][idx % (D / 2)] = src[idx];
   }
-  __syncthreads();
+  wave_sync();
   const uint16_t *sinkK = p.sinkK + ((size_t)seq * Hkv + kv) * kSink * D;
   const uint16_t *sinkV = p.sinkV + ((size_t)seq * Hkv + kv) * kSink * D;
   const uint16_t *recK = p.recentK + ((size_t)seq * Hkv + kv) * kRecent * D;
@@ -227,12 +241,12 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
   }
   const int ngroups = (n_win + TPI - 1) / TPI;
-  const int nk = (ngroups - w + kWaves - 1) / kWaves; // groups of this wave
+  const int nk = (ngroups - wi + NW - 1) / NW; // groups of this wave
   for (int k0 = 0; k0 < nk; k0 += WG) {
     u32x4 kr[WG], vr[WG];
 #pragma unroll
     for (int i = 0; i < WG; ++i) {
-      const int u = (w + kWaves * (k0 + i)) * TPI + ts;
+      const int u = (wi + NW * (k0 + i)) * TPI + ts;
       kr[i] = vr[i] = u32x4{0u, 0u, 0u, 0u};
       if (k0 + i < nk && u < n_win) {
         const size_t off = (size_t)(u < n_sink ? u : u - n_sink) * D + 8 * cc;
@@ -243,7 +257,7 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
 #pragma unroll
     for (int i = 0; i < WG; ++i) {
       if (k0 + i >= nk) break;
-      const int u = (w + kWaves * (k0 + i)) * TPI + ts;
+      const int u = (wi + NW * (k0 + i)) * TPI + ts;
       const bool ok = u < n_win;
       float vf[8];
 #pragma unroll
@@ -253,7 +267,7 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
       }
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const u32x4 qv = *(const u32x4 *)&sm.q2[h][4 * cc];
+        const u32x4 qv = *(const u32x4 *)&sm.q2[wi][h][4 * cc];
         float d = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -298,16 +312,25 @@ __device__ void window_block(WinSmem<D, GQ> &sm, const PoolDev &p, const DecodeB
       acc[h][j] = a;
     }
     if (lane == 0) {
-      sm.M[w][h] = m;
-      sm.L[w][h] = l;
+      sm.M[wi][h] = m;
+      sm.L[wi][h] = l;
     }
     if (ts == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sm.A[w][h][8 * cc + j] = acc[h][j];
+      for (int j = 0; j < 8; ++j) sm.A[wi][h][8 * cc + j] = acc[h][j];
     }
   }
+}
+
+// A block that holds only a pair's window: all its waves take part.
+template <int D, int G, int GQ>
+__device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
+                             const uint16_t *q, float qscale, float *ws_win, int e, int kv) {
+  constexpr int W = main_waves(D, G, GQ);
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  window_waves<D, G, GQ, W>(sm, p, b, q, qscale, e, kv, w);
   __syncthreads();
-  block_merge_store<D, GQ>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * Hq + kv * GQ) * (D + 2));
+  block_merge_store<D, GQ, W>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2));
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch
     for (int i = 0; i < NL; ++i) dst[tid + i * kThreads] = t[i];
   }
   for (int idx = tid; idx < GQ * D; idx += kThreads)
-    sm.qraw[idx / D][idx % D] = bf16f(q[((size_t)e * Hq + kv * GQ + idx / D) * D + idx % D]);
+    sm.qraw[idx / D][idx % D] = bf16f(q[((size_t)b.row[e] * Hq + kv * GQ + idx / D) * D + idx % D]);
   __syncthreads();
   for (int idx = tid; idx < GQ * D; idx += kThreads) {
     const int h = idx / D, j = idx % D;
@@ -446,21 +469,45 @@ template <int D, int G, int GQ>
 constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
 template <int D, int G, int GQ>
-__device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const DecodeBatch &b,
-                              const uint32_t *qrec, float *ws_hist, int blk, int e, int p0, int p1) {
+__device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
+                              const uint32_t *qrec, float *ws_hist, float *ws_win, const uint16_t *q, float qscale,
+                              int blk, int e, int kv, int p0, int p1, bool with_window) {
+  constexpr int W = main_waves(D, G, GQ), NT = 64 * W, WW = win_waves(W);
   constexpr int NG = D / G;                // scale/zero groups per token
   constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
   constexpr int RT = GQ >= 4 ? GQ / 4 : 1; // MFMA row tiles of 4 heads x 4 limb rows
   constexpr int NJ = D / 16;               // PV column tiles of 16 channels
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 15, r = lane >> 4;
   const int Hkv = p.Hkv;
-  const int kv = blk % Hkv;
   const int seq = b.seq[e], n_hist = b.len[e] - kWindow;
   const int np = (n_hist + kPage - 1) / kPage;
 
-  // ---- prologue: load this pair's query record; rows of P' that no head
-  // owns stay zero for the whole loop.
+  const int32_t *ptab = p.page_table + (size_t)seq * p.maxp;
+  const size_t hstride = (size_t)Hkv * p.block_bytes;
+  const size_t hoff = (size_t)kv * p.block_bytes;
+  const int pf = (n_hist % kPage == 0) ? p1 : min(p1, np - 1); // end of full pages
+
+  // ---- prologue: rows of P' that no head owns stay zero for the whole
+  // loop; the first segment's page ids are staged (one barrier).
+  for (int idx = tid; idx < W * 16; idx += NT) sm.alpha[idx / 16][idx % 16] = 1.f;
+  {
+    _Float16 *P = &sm.u.P[0][0][0][0];
+    for (int idx = tid; idx < W * NG * 16 * kPRow; idx += NT) P[idx] = (_Float16)0.f;
+  }
+  auto stage = [&](int s0, int sf) __attribute__((always_inline)) {
+    for (int i = s0 + tid; i < sf; i += NT) sm.ids[i - s0] = ptab[i];
+    if (tid == 0) sm.claim = (uint32_t)s0;
+    __syncthreads();
+  };
+  stage(p0, min(pf, p0 + kIdCache));
+  // The first WW waves take the pair's window (if this block holds it)
+  // before joining the page stream; the other waves start on the pages.
+  // The history state below is set up afterwards, so it is not live
+  // during the window.
+  if (with_window && w < WW) window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
+
+  // this pair's query record
   const uint32_t *rec = qrec + ((size_t)e * Hkv + kv) * qprep_words(D, GQ);
   const float *tail = (const float *)(rec + RT * MI * 256);
   v4i Aq[RT][MI];
@@ -474,12 +521,6 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
 #pragma unroll
     for (int g = 0; g < NG; ++g) qsum[rt][g] = tail[hs * NG + g];
   }
-  for (int idx = tid; idx < kWaves * 16; idx += kThreads) sm.alpha[idx / 16][idx % 16] = 1.f;
-  {
-    _Float16 *P = &sm.u.P[0][0][0][0];
-    for (int idx = tid; idx < kWaves * NG * 16 * kPRow; idx += kThreads) P[idx] = (_Float16)0.f;
-  }
-  __syncthreads();
 
   // per-token factor of P': 2^pv_shift * 4^-e(k), k = token within its
   // 16-token block, e = pair index (k >> 1), or (k >> 1) - 5 past the shift
@@ -502,10 +543,6 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int32_t *ptab = p.page_table + (size_t)seq * p.maxp;
-  const size_t hstride = (size_t)Hkv * p.block_bytes;
-  const size_t hoff = (size_t)kv * p.block_bytes;
 
   // One page of this wave: logits, online softmax, P' and PV.
   // `full`: every token of the page is valid (all pages but a sequence's last)
@@ -623,58 +660,58 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
       wave_sync();
   };
 
-  // Register buffers in rotation: the loads of the wave's next page(s) are in
-  // flight while the current one is computed (no register copy between
-  // iterations).  Page ids come from shared memory, staged per segment of up
-  // to kIdCache pages, so a prefetch never waits on a page-table load.
-  // Only a sequence's last page can be partial; it is handled last.
-  const int pf = (n_hist % kPage == 0) ? p1 : min(p1, np - 1); // end of full pages
-  constexpr int W = kWaves;
-  for (int s0 = p0; s0 < p1; s0 += kIdCache) {
-    const int s1 = min(p1, s0 + kIdCache), sf = min(s1, pf);
-    if (s0 != p0) __syncthreads(); // every wave is done with the previous ids
-    for (int i = s0 + tid; i < s1; i += kThreads) sm.ids[i - s0] = ptab[i];
-    __syncthreads();
-    auto load = [&](PageRegs<D, G> &buf, int page_idx) __attribute__((always_inline)) {
-      const int id = __builtin_amdgcn_readfirstlane(sm.ids[page_idx - s0]);
-      load_page<D, G>(buf, p.pages + (size_t)id * hstride + hoff, n, r);
+  // Page stream of a wave.  The split's pages [p0, p1) are cut in segments
+  // of up to kIdCache pages whose ids are staged in shared memory.  Inside a
+  // segment a wave takes one page at a time from a shared-memory counter
+  // (or, deterministic pools, pages w, w + W, ... of the segment), so waves
+  // that run ahead take more pages.  NB register buffers rotate: the loads
+  // of the page PF steps ahead are in flight while a page is computed; the
+  // page for those loads was taken one step earlier.  Every step issues its
+  // loads (a page past the segment end reads a small cached table instead),
+  // so each wait is an exact count of younger loads.  Only a sequence's
+  // last page can be partial; it goes to the last wave after the loop.
+  constexpr int PF = kPrefetch<D, G, GQ>, NB = PF + 1;
+  const uint8_t *dummy = (const uint8_t *)p.RK; // >= one page block, read-only
+  const bool det = p.deterministic != 0;
+  for (int s0 = p0; s0 < pf; s0 += kIdCache) {
+    const int sf = min(pf, s0 + kIdCache);
+    if (s0 != p0) {
+      __syncthreads(); // every wave is done with the previous ids
+      stage(s0, sf);
+    }
+    // deterministic pools: wave w takes pages w, w + W, ... of the segment
+    int next_static = s0 + w;
+    auto take = [&]() __attribute__((always_inline)) {
+      uint32_t c = 0;
+      if (!det && lane == 0) c = atomicAdd(&sm.claim, 1u);
+      const int pg = det ? next_static : (int)__builtin_amdgcn_readlane(c, 0);
+      next_static += W;
+      return pg;
     };
-    PageRegs<D, G> bufA, bufB;
-    int pi = s0 + w;
-    if (pi < sf) load(bufA, pi);
-    if constexpr (kPrefetch<D, G, GQ> >= 2) {
-      // three register buffers in rotation: two pages in flight per wave
-      PageRegs<D, G> bufC;
-      if (pi + W < sf) load(bufB, pi + W);
-      while (pi < sf) {
-        if (pi + 2 * W < sf) load(bufC, pi + 2 * W);
-        page_step(bufA, pi, true);
-        pi += W;
-        if (pi >= sf) break;
-        if (pi + 2 * W < sf) load(bufA, pi + 2 * W);
-        page_step(bufB, pi, true);
-        pi += W;
-        if (pi >= sf) break;
-        if (pi + 2 * W < sf) load(bufB, pi + 2 * W);
-        page_step(bufC, pi, true);
-        pi += W;
-      }
-    } else {
-      // two register buffers in ping-pong: one page in flight per wave
-      while (pi < sf) {
-        if (pi + W < sf) load(bufB, pi + W);
-        page_step(bufA, pi, true);
-        pi += W;
-        if (pi >= sf) break;
-        if (pi + W < sf) load(bufA, pi + W);
-        page_step(bufB, pi, true);
-        pi += W;
+    auto load = [&](PageRegs<D, G> &buf, int page) __attribute__((always_inline)) {
+      const int id = __builtin_amdgcn_readfirstlane(sm.ids[min(page, sf - 1) - s0]);
+      load_page<D, G>(buf, page < sf ? p.pages + (size_t)id * hstride + hoff : dummy, n, r);
+    };
+    PageRegs<D, G> buf[NB];
+    int pg[NB];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      pg[i] = take();
+      load(buf[i], pg[i]);
+    }
+    while (pg[0] < sf) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        pg[(j + PF) % NB] = take();
+        load(buf[(j + PF) % NB], pg[(j + PF) % NB]);
+        if (pg[j] < sf) page_step(buf[j], pg[j], true);
       }
     }
-    if (pf < s1 && pf >= s0 && (pf - s0) % W == w) {
-      load(bufA, pf);
-      page_step(bufA, pf, false);
-    }
+  }
+  if (pf < p1 && w == W - 1) {
+    PageRegs<D, G> last;
+    load_page<D, G>(last, p.pages + (size_t)ptab[pf] * hstride + hoff, n, r);
+    page_step(last, pf, false);
   }
 
   // ---- epilogue: per-wave (m, l, acc) then the block merge
@@ -702,43 +739,41 @@ __device__ void history_block(HistSmem<D, G, GQ> &sm, const PoolDev &p, const De
       if (h < GQ) sm.u.A[w][h][c] = fmaf(acc[j][i], unscale, sm.zsum[w][h][c / G]);
     }
   __syncthreads();
-  block_merge_store<D, GQ>(sm.M, sm.L, sm.u.A, ws_hist + (size_t)blk * GQ * (D + 2));
+  block_merge_store<D, GQ, W>(sm.M, sm.L, sm.u.A, ws_hist + (size_t)blk * GQ * (D + 2));
+  // the window waves' results were written before the barriers above
+  if (with_window) block_merge_store<D, GQ, WW>(sm.win.M, sm.win.L, sm.win.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2));
 }
 
 
 template <int D, int G, int GQ>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
-void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
-                                                               float qscale, float *__restrict__ ws,
-                                                               const uint32_t *__restrict__ qrec) {
-  __shared__ MainSmem<D, G, GQ> sm;
+__global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
+void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
+                        float *__restrict__ ws, const uint32_t *__restrict__ qrec) {
+  constexpr int W = main_waves(D, G, GQ);
+  __shared__ MainSmem<D, G, GQ, W> sm;
   float *ws_win = ws;
   float *ws_hist = ws + (size_t)b.n * p.Hq * (D + 2);
   const int blk = blockIdx.x, Hkv = p.Hkv;
-  const int kv = blk % Hkv, sidx = blk / Hkv;
-  int lo = 0, hi = b.n;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) / 2;
-    if (b.split_prefix[mid] <= sidx) lo = mid;
-    else hi = mid;
-  }
-  const int e = lo, s = sidx - b.split_prefix[e], S = b.split_prefix[e + 1] - b.split_prefix[e];
+  int s = 0; // split layer: the largest s with layer_prefix[s] <= blk
+#pragma unroll
+  for (int step = kMaxSplits / 2; step >= 1; step >>= 1)
+    if (b.layer_prefix[s + step] <= blk) s += step;
+  const int pos = blk - b.layer_prefix[s], e = pos / Hkv, kv = pos % Hkv;
+  const int S = b.nsplit[e];
   const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
   int p0, p1;
   split_range(np, S, s, b.win_units, p0, p1);
-  if (p0 < p1) history_block<D, G, GQ>(sm.h, p, b, qrec, ws_hist, blk, e, p0, p1);
-  if (s == S - 1) {
-    if (p0 < p1) __syncthreads(); // the window reuses the history's shared memory
-    window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, e * Hkv + kv);
-  }
+  if (p0 < p1)
+    history_block<D, G, GQ>(sm.h, p, b, qrec, ws_hist, ws_win, q, qscale, blk, e, kv, p0, p1, s == S - 1);
+  else if (s == S - 1)
+    window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, e, kv);
 }
 
 // Merge of one (sequence, kv head): split partials -> history (m, l, acc),
 // acc . R_V^T, then the window partial, then out = acc / l.  Every load that
 // does not depend on another is issued up front: R_V^T goes to shared memory
-// in one coalesced pass, split partials are read in batches of 8.
+// in one coalesced pass, split partials are all read before any is used.
 constexpr int kMergeThreads = 512;
-constexpr int kMaxSplitsDev = 32;
 
 template <int D, int GQ>
 struct MergeSmem {
@@ -757,17 +792,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
   const int c = tid % D, hg = tid / D;
   const float *ws_win = ws;
   const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
-  const int s0 = b.split_prefix[e], S = b.split_prefix[e + 1] - s0;
-  // splits that hold history pages (a split may hold the window alone)
+  const int S = b.nsplit[e];
+  // splits that hold history pages (only the last one can hold the window alone)
   const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
-  uint32_t has = 0;
+  uint32_t has_mask = 0;
   for (int s = 0; s < S; ++s) {
     int p0, p1;
     split_range(np, S, s, b.win_units, p0, p1);
-    if (p0 < p1) has |= 1u << s;
+    if (p0 < p1) has_mask |= 1u << s;
   }
-  const size_t stride = (size_t)Hkv * GQ * (D + 2); // between splits of one pair
-  const float *part0 = ws_hist + ((size_t)s0 * Hkv + kv) * GQ * (D + 2);
+  const bool has = has_mask != 0;
   if (has) {
     const u32x4 *src = (const u32x4 *)(p.RVt + (size_t)kv * D * D);
     u32x4 *dst = (u32x4 *)&sm.R[0][0];
@@ -788,22 +822,23 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
     mwin[k] = win[D];
     lwin[k] = win[D + 1];
     awin[k] = win[c];
-    float ms[kMaxSplitsDev], ls[kMaxSplitsDev], as[kMaxSplitsDev];
-    const float *ph = part0 + (size_t)h * (D + 2);
+    // split s of this pair wrote its partial at block layer_prefix[s] + e Hkv + kv
+    float ms[kMaxSplits], ls[kMaxSplits], as[kMaxSplits];
 #pragma unroll
-    for (int s = 0; s < kMaxSplitsDev; ++s) {
-      const bool v = has >> s & 1u;
-      ms[s] = v ? ph[s * stride + D] : -INFINITY;
-      ls[s] = v ? ph[s * stride + D + 1] : 0.f;
-      as[s] = v ? ph[s * stride + c] : 0.f;
+    for (int s = 0; s < kMaxSplits; ++s) {
+      const bool v = (has_mask >> s) & 1u;
+      const float *ph = ws_hist + ((size_t)(b.layer_prefix[s] + e * Hkv + kv) * GQ + h) * (D + 2);
+      ms[s] = v ? ph[D] : -INFINITY;
+      ls[s] = v ? ph[D + 1] : 0.f;
+      as[s] = v ? ph[c] : 0.f;
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxSplitsDev; ++s) m = fmaxf(m, ms[s]);
+    for (int s = 0; s < kMaxSplits; ++s) m = fmaxf(m, ms[s]);
     float l = 0.f, a = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxSplitsDev; ++s) {
-      const float f = has >> s & 1u ? exp2f(ms[s] - m) : 0.f;
+    for (int s = 0; s < kMaxSplits; ++s) {
+      const float f = ms[s] == -INFINITY ? 0.f : exp2f(ms[s] - m);
       l = fmaf(f, ls[s], l);
       a = fmaf(f, as[s], a);
     }
@@ -818,7 +853,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
     const int h = hg + k * HG;
     if (h >= GQ) continue;
     float o;
-    if (has) {
+    if (has && mH[k] != -INFINITY) {
       float der = 0.f;
 #pragma unroll 16
       for (int j = 0; j < D; ++j) der = fmaf(sm.AH[h][j], sm.R[j][c], der);
@@ -828,7 +863,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, 
       o = awin[k] / lwin[k];
     }
     (void)aH[k];
-    out[((size_t)e * Hq + kv * GQ + h) * D + c] = o;
+    out[((size_t)b.row[e] * Hq + kv * GQ + h) * D + c] = o;
   }
 }
 
@@ -842,8 +877,9 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
   if (b.total_pages > 0)
     hipExtLaunchKernelGGL((q_prep_kernel<D, G, GQ>), dim3(b.n * p.Hkv), dim3(kThreads), 0, s,
                           tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, qrec);
-  hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(kThreads), 0, s, tm.on ? tm.ev[0] : nullptr,
-                        tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, (const uint32_t *)qrec);
+  hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
+                        tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws,
+                        (const uint32_t *)qrec);
   hipLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(kMergeThreads), 0, s, p, b, out,
                      (const float *)ws);
   return hipGetLastError();
@@ -867,11 +903,11 @@ int blocks_per_cu_g(const PoolDev &p) {
   int nb = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (p.Hq / p.Hkv) {
-  case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 1>, kThreads, 0); break;
-  case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 2>, kThreads, 0); break;
-  case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 4>, kThreads, 0); break;
-  case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 8>, kThreads, 0); break;
-  case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 16>, kThreads, 0); break;
+  case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 1>, 64 * main_waves(D, G, 1), 0); break;
+  case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 2>, 64 * main_waves(D, G, 2), 0); break;
+  case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 4>, 64 * main_waves(D, G, 4), 0); break;
+  case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 8>, 64 * main_waves(D, G, 8), 0); break;
+  case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 16>, 64 * main_waves(D, G, 16), 0); break;
   }
   return e == hipSuccess ? nb : 0;
 }

@@ -72,7 +72,8 @@ int validate_config(const oscar_pool_config *c) {
   if ((int64_t)c->max_seqs * c->max_pages_per_seq > (int64_t)1 << 31)
     return fail(OSCAR_EINVAL, "page table of %d x %d entries is too large", c->max_seqs,
                 c->max_pages_per_seq);
-  if (c->flags & ~OSCAR_POOL_HOST_ONLY) return fail(OSCAR_EINVAL, "unknown flags 0x%x", c->flags);
+  if (c->flags & ~(OSCAR_POOL_HOST_ONLY | OSCAR_POOL_DETERMINISTIC))
+    return fail(OSCAR_EINVAL, "unknown flags 0x%x", c->flags);
   return OSCAR_OK;
 }
 
@@ -103,31 +104,26 @@ Layout layout_of(const oscar_pool_config &c) {
 int pages_for(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPage); }
 
 // Split policy of one decode launch.  A pair's work is its history pages
-// plus its window, worth win_units pages (the window's bytes over a page
-// block's bytes, times kWindowCost).  Pieces of at most P units: a pair gets
-// S = ceil(U / P) splits (at most kMaxSplits), and P is the smallest piece
-// size for which all blocks fit in kSplitRounds rounds of the device's
-// resident block slots (compute units x decode blocks per unit), so that no
-// block waits for a slot and every slot streams until the end.
-constexpr int kMaxSplits = 32;
-constexpr int kSplitRounds = 1;
-constexpr double kWindowCost = 1.0;
+// plus its window, worth window_units pages (the window's bytes over a page
+// block's bytes).  Pieces of at most P units: a pair gets
+// S = ceil(U / P) blocks (at most kMaxSplits, and at most U / wu so that
+// only the last split can be window-only), and P is the smallest piece size
+// for which all blocks fit in one round of the device's resident block
+// slots (one decode block fills a compute unit).
+int window_units(int d, int G) { return (int)std::lround((double)kWindow * 4 * d / block_bytes_for(d, G)); }
 
-int window_units(int d, int G) {
-  return (int)std::lround(kWindowCost * (double)kWindow * 4 * d / block_bytes_for(d, G));
-}
-
-void plan_splits(DecodeBatch &b, const std::vector<int> &np, int Hkv, int slots, int wu) {
-  b.win_units = wu;
+void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vector<int> &len, int Hkv, int slots, int wu) {
+  std::vector<int> np(b.n);
   int64_t total = 0, umax = 1;
   for (int e = 0; e < b.n; ++e) {
+    np[e] = pages_for(std::max(0, len[e] - kWindow));
     total += np[e];
     umax = std::max<int64_t>(umax, np[e] + wu);
   }
   b.total_pages = (int32_t)total;
-  // at most U / wu splits: pieces of at least a window keep every split but
-  // the last one on history pages
+  b.win_units = wu;
   auto splits = [&](int e, int64_t P) {
+    if (np[e] == 0) return 1; // window only
     const int64_t U = np[e] + wu;
     int64_t S = std::min<int64_t>(kMaxSplits, (U + P - 1) / P);
     if (wu > 0) S = std::min<int64_t>(S, U / wu);
@@ -138,16 +134,34 @@ void plan_splits(DecodeBatch &b, const std::vector<int> &np, int Hkv, int slots,
     for (int e = 0; e < b.n; ++e) nb += splits(e, P);
     return nb * Hkv;
   };
-  const int64_t budget = (int64_t)kSplitRounds * slots;
   int64_t lo = 1, hi = umax; // blocks(umax) = n * Hkv: the fewest possible
   while (lo < hi) {
     const int64_t mid = (lo + hi) / 2;
-    if (blocks(mid) <= budget) hi = mid;
+    if (blocks(mid) <= slots) hi = mid;
     else lo = mid + 1;
   }
-  b.split_prefix[0] = 0;
-  for (int e = 0; e < b.n; ++e) b.split_prefix[e + 1] = b.split_prefix[e] + splits(e, lo);
-  b.hist_blocks = b.split_prefix[b.n] * Hkv;
+  std::vector<int> S(b.n), order(b.n);
+  for (int e = 0; e < b.n; ++e) {
+    S[e] = splits(e, lo);
+    order[e] = e;
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return S[x] > S[y]; });
+  for (int i = 0; i < b.n; ++i) {
+    const int e = order[i];
+    b.seq[i] = seq_ids[e];
+    b.len[i] = len[e];
+    b.row[i] = (uint16_t)e;
+    b.nsplit[i] = (uint8_t)S[e];
+  }
+  // layer l holds the pairs of the sequences with more than l splits: the
+  // first count(S > l) sequences of the launch order
+  b.layer_prefix[0] = 0;
+  for (int l = 0; l < kMaxSplits; ++l) {
+    int cnt = 0;
+    while (cnt < b.n && b.nsplit[cnt] > l) ++cnt;
+    b.layer_prefix[l + 1] = b.layer_prefix[l] + cnt * Hkv;
+  }
+  b.hist_blocks = b.layer_prefix[kMaxSplits];
 }
 
 } // namespace
@@ -281,6 +295,7 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
   D.maxp = cfg->max_pages_per_seq;
   D.block_bytes = block_bytes_for(d, cfg->group_size);
   D.pv_shift = 0;
+  D.deterministic = (cfg->flags & OSCAR_POOL_DETERMINISTIC) ? 1 : 0;
   if (!host_only) {
     // V scales never exceed fp16(2 c / 3) for the largest V threshold c and
     // the decode's softmax weights never exceed 2^8 (its lazy max); keep
@@ -482,14 +497,9 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
     DecodeBatch b;
     b.n = std::min(kMaxBatch, n - i0);
-    std::vector<int> np(b.n);
-    for (int e = 0; e < b.n; ++e) {
-      int32_t s = seq_ids[i0 + e];
-      b.seq[e] = s;
-      b.len[e] = p->len[s];
-      np[e] = pages_for(std::max(0, b.len[e] - kWindow));
-    }
-    plan_splits(b, np, Hkv, p->decode_slots, window_units(d, p->cfg.group_size));
+    std::vector<int> len(b.n);
+    for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]];
+    plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size));
     need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
     batches.push_back(b);
   }

@@ -33,6 +33,9 @@ struct PoolDev {
   // two by which a softmax weight (<= 2^8) times a V scale may be multiplied
   // and stay finite in fp16.
   int32_t pv_shift;
+  // 1: the waves of a decode block take their pages in a fixed order, so
+  // results are bitwise reproducible; 0: pages are handed out dynamically.
+  int32_t deterministic;
 };
 
 // ---------------------------------------------------------------------------
@@ -87,23 +90,30 @@ struct AppendBatch {
   int32_t new_page[kMaxBatch]; // page taken by this append, or -1
 };
 
-// By-value metadata of one decode launch (<= kMaxBatch sequences).  The work of a (sequence, kv head) pair is its np
-// history pages plus its BF16 window, counted as win_units pages; it is cut
-// into S splits of about equal work (split_range), the window going to the
-// last split.  One block per (split, kv head): block = split * Hkv + kv.
+// By-value metadata of one decode launch (<= kMaxBatch sequences).  The
+// work of a (sequence, kv head) pair is its np history pages plus its BF16
+// window, counted as win_units pages; it is cut into nsplit splits of about
+// equal work (split_range), the window going to the last split, one block
+// per split.  Sequences are ordered by nsplit, descending, and blocks are
+// numbered split-major: block = layer_prefix[s] + e * Hkv + kv for split
+// s < nsplit[e].
+constexpr int kMaxSplits = 32;
+constexpr int kIdCache = 1024; // page ids staged in shared memory per segment
 struct DecodeBatch {
   int32_t n;
-  int32_t hist_blocks;         // blocks: split_prefix[n] * Hkv
-  int32_t win_units;           // window work in page units (>= 0)
-  int32_t total_pages;         // sum of np over the batch
-  int32_t seq[kMaxBatch];
-  int32_t len[kMaxBatch];
-  int32_t split_prefix[kMaxBatch + 1]; // exclusive prefix of splits per sequence (each >= 1)
+  int32_t hist_blocks;               // blocks of the launch: layer_prefix[kMaxSplits]
+  int32_t total_pages;               // history pages of the batch
+  int32_t win_units;                 // window work in page units (>= 0)
+  int32_t seq[kMaxBatch];            // pool sequence id, launch order
+  int32_t len[kMaxBatch];            // its length
+  uint16_t row[kMaxBatch];           // its row in q and out
+  uint8_t nsplit[kMaxBatch];         // blocks per pair, 1 .. kMaxSplits
+  int32_t layer_prefix[kMaxSplits + 1];
 };
 
 // History pages [p0, p1) of split s of S of a pair with np pages: the pair's
 // units [0, np + wu) are cut evenly, pages are units below np.  Only the last
-// split can be left without pages.
+// split can be left without pages when S <= (np + wu) / max(wu, 1).
 __host__ __device__ inline void split_range(int np, int S, int s, int wu, int &p0, int &p1) {
   const long U = (long)np + wu;
   p0 = (int)(s * U / S);

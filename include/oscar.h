@@ -63,6 +63,15 @@ extern "C" {
  * the host logic without a GPU.  Decode and export then fail with EINVAL. */
 #define OSCAR_POOL_HOST_ONLY 1u
 
+/* Pool flag: decode results are bitwise reproducible from call to call and
+ * independent of where pages sit in the pool.  By default the waves of a
+ * decode block hand history pages out among themselves as they finish them,
+ * which balances their progress but lets the summation order and the fp16
+ * rounding of the softmax weights vary between calls; with this flag each
+ * wave takes a fixed set of pages.  Either mode computes the same attention
+ * within the kernel's rounding (relative differences of order 1e-4). */
+#define OSCAR_POOL_DETERMINISTIC 2u
+
 typedef struct oscar_pool oscar_pool;  /* opaque, host side */
 
 typedef struct oscar_pool_config {
@@ -73,7 +82,7 @@ typedef struct oscar_pool_config {
     int32_t  group_size;        /* G: 64 or 128 channels per scale/zero, G <= d      */
     int32_t  num_pages;         /* history pages in the pool (>= 0)                  */
     int32_t  max_pages_per_seq; /* page-table width                                  */
-    uint32_t flags;             /* 0 or OSCAR_POOL_HOST_ONLY                         */
+    uint32_t flags;             /* OR of OSCAR_POOL_HOST_ONLY, OSCAR_POOL_DETERMINISTIC */
     uint64_t page_shuffle_seed; /* seeds the free-list order                         */
 } oscar_pool_config;
 

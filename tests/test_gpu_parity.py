@@ -12,7 +12,7 @@ import bit_kv_cache_segment_amd as ok
 import harness
 import oracle
 import synth
-from gpu_common import check_history_codes, check_rows, check_windows, oracle_sequence
+from gpu_common import TOL, check_history_codes, check_rows, check_windows, oracle_sequence
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +31,9 @@ def _workload(name):
     return synth.Workload("edge_" + name, 20 + list(SHAPES).index(name), len(EDGE_LENS), Hq, Hkv, d, G, 0, 0)
 
 
-def _pool(w, lengths, extra=0, seed=None, slack=0):
+def _pool(w, lengths, extra=0, seed=None, slack=0, flags=0):
     RK, RV, cK, cV = harness.tables(w)
-    cfg = harness.config_for(w, lengths, extra_tokens=extra, seed=seed, slack_pages=slack)
+    cfg = harness.config_for(w, lengths, extra_tokens=extra, seed=seed, slack_pages=slack, flags=flags)
     return ok.Pool(cfg, RK, RV, cK, cV, max_batch=len(lengths)), cfg
 
 
@@ -106,11 +106,13 @@ def test_edge_lengths_prefill_then_fused_steps(shape):
 
 
 def test_shuffle_invariance_and_determinism():
+    # Deterministic pools: bitwise equal results from call to call and for
+    # any placement of the pages in the pool.
     w = _workload("g8_d128_G64")
     lengths = [1000, 700, 385, 64]
     outs = []
     for seed in (1, 2):
-        pool, cfg = _pool(w, lengths, seed=seed, slack=5)
+        pool, cfg = _pool(w, lengths, seed=seed, slack=5, flags=ok.POOL_DETERMINISTIC)
         harness.prefill_all(pool, w, lengths)
         assert seed == 1 or list(pool.page_table(0)) != first_table
         first_table = list(pool.page_table(0))
@@ -121,6 +123,19 @@ def test_shuffle_invariance_and_determinism():
         assert torch.equal(a, b)
         outs.append(a)
     assert torch.equal(outs[0], outs[1])
+    # The default pool hands pages out dynamically inside a block: which wave
+    # sees which page moves the lazy softmax reference and with it the fp16
+    # rounding of the weights, so results agree within the attention
+    # tolerance (each mode is itself checked against the oracle), not bitwise.
+    pool, cfg = _pool(w, lengths, seed=1, slack=5)
+    harness.prefill_all(pool, w, lengths)
+    q = synth.queries(w, 3, device="cuda", batch=len(lengths)).view(torch.uint16)
+    c = pool.decode(list(range(4)), q)
+    torch.cuda.synchronize()
+    ref = outs[0].double().cpu().numpy()
+    got = c.double().cpu().numpy()
+    for b_ in range(len(lengths)):
+        assert oracle.row_rel_err(got[b_], ref[b_]) <= TOL
 
 
 def test_identical_queries_in_a_group_give_identical_rows():

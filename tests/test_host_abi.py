@@ -103,7 +103,7 @@ def test_errors_leave_state_unchanged():
 
 @pytest.mark.parametrize("kw", [dict(head_dim=96), dict(group_size=32), dict(num_q_heads=6),
                                 dict(num_q_heads=12, num_kv_heads=4), dict(max_seqs=0),
-                                dict(group_size=128, head_dim=64), dict(num_pages=-1)])
+                                dict(group_size=128, head_dim=64), dict(num_pages=-1), dict(flags=4)])
 def test_bad_configs_rejected(kw):
     base = dict(max_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=64, group_size=64, num_pages=4,
                 max_pages_per_seq=2)
@@ -112,6 +112,12 @@ def test_bad_configs_rejected(kw):
     with pytest.raises(ok.OscarError) as ei:
         ok.oscar_pool_bytes(cfg)
     assert ei.value.code == ok.EINVAL
+
+
+def test_known_flags_accepted():
+    for flags in (ok.POOL_HOST_ONLY, ok.POOL_DETERMINISTIC, ok.POOL_HOST_ONLY | ok.POOL_DETERMINISTIC):
+        cfg = ok.make_config(2, 8, 2, 64, 64, 4, 2, flags=flags)
+        assert ok.oscar_pool_bytes(cfg) > 0
 
 
 def test_bad_clip_thresholds_rejected_before_device_access():
