@@ -486,7 +486,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   const int32_t *ptab = p.page_table + (size_t)seq * p.maxp;
   const size_t hstride = (size_t)Hkv * p.block_bytes;
   const size_t hoff = (size_t)kv * p.block_bytes;
-  const int pf = (n_hist % kPage == 0) ? p1 : min(p1, np - 1); // end of full pages
+  const int pf = full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
 
   // ---- prologue: rows of P' that no head owns stay zero for the whole
   // loop; the first segment's page ids are staged (one barrier).
@@ -754,11 +754,8 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   float *ws_win = ws;
   float *ws_hist = ws + (size_t)b.n * p.Hq * (D + 2);
   const int blk = blockIdx.x, Hkv = p.Hkv;
-  int s = 0; // split layer: the largest s with layer_prefix[s] <= blk
-#pragma unroll
-  for (int step = kMaxSplits / 2; step >= 1; step >>= 1)
-    if (b.layer_prefix[s + step] <= blk) s += step;
-  const int pos = blk - b.layer_prefix[s], e = pos / Hkv, kv = pos % Hkv;
+  int s, e, kv;
+  block_split(b, Hkv, blk, s, e, kv);
   const int S = b.nsplit[e];
   const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
   int p0, p1;

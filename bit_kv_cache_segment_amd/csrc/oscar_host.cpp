@@ -9,6 +9,7 @@
 // paged layout).
 #include "../../include/oscar.h"
 #include "oscar_internal.h"
+#include "decode_plan.h"
 
 #include <algorithm>
 #include <cmath>
@@ -102,67 +103,6 @@ Layout layout_of(const oscar_pool_config &c) {
 }
 
 int pages_for(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPage); }
-
-// Split policy of one decode launch.  A pair's work is its history pages
-// plus its window, worth window_units pages (the window's bytes over a page
-// block's bytes).  Pieces of at most P units: a pair gets
-// S = ceil(U / P) blocks (at most kMaxSplits, and at most U / wu so that
-// only the last split can be window-only), and P is the smallest piece size
-// for which all blocks fit in one round of the device's resident block
-// slots (one decode block fills a compute unit).
-int window_units(int d, int G) { return (int)std::lround((double)kWindow * 4 * d / block_bytes_for(d, G)); }
-
-void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vector<int> &len, int Hkv, int slots, int wu) {
-  std::vector<int> np(b.n);
-  int64_t total = 0, umax = 1;
-  for (int e = 0; e < b.n; ++e) {
-    np[e] = pages_for(std::max(0, len[e] - kWindow));
-    total += np[e];
-    umax = std::max<int64_t>(umax, np[e] + wu);
-  }
-  b.total_pages = (int32_t)total;
-  b.win_units = wu;
-  auto splits = [&](int e, int64_t P) {
-    if (np[e] == 0) return 1; // window only
-    const int64_t U = np[e] + wu;
-    int64_t S = std::min<int64_t>(kMaxSplits, (U + P - 1) / P);
-    if (wu > 0) S = std::min<int64_t>(S, U / wu);
-    return (int)std::max<int64_t>(1, S);
-  };
-  auto blocks = [&](int64_t P) {
-    int64_t nb = 0;
-    for (int e = 0; e < b.n; ++e) nb += splits(e, P);
-    return nb * Hkv;
-  };
-  int64_t lo = 1, hi = umax; // blocks(umax) = n * Hkv: the fewest possible
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) / 2;
-    if (blocks(mid) <= slots) hi = mid;
-    else lo = mid + 1;
-  }
-  std::vector<int> S(b.n), order(b.n);
-  for (int e = 0; e < b.n; ++e) {
-    S[e] = splits(e, lo);
-    order[e] = e;
-  }
-  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return S[x] > S[y]; });
-  for (int i = 0; i < b.n; ++i) {
-    const int e = order[i];
-    b.seq[i] = seq_ids[e];
-    b.len[i] = len[e];
-    b.row[i] = (uint16_t)e;
-    b.nsplit[i] = (uint8_t)S[e];
-  }
-  // layer l holds the pairs of the sequences with more than l splits: the
-  // first count(S > l) sequences of the launch order
-  b.layer_prefix[0] = 0;
-  for (int l = 0; l < kMaxSplits; ++l) {
-    int cnt = 0;
-    while (cnt < b.n && b.nsplit[cnt] > l) ++cnt;
-    b.layer_prefix[l + 1] = b.layer_prefix[l] + cnt * Hkv;
-  }
-  b.hist_blocks = b.layer_prefix[kMaxSplits];
-}
 
 } // namespace
 

@@ -122,6 +122,29 @@ __host__ __device__ inline void split_range(int np, int S, int s, int wu, int &p
   p1 = p1 < np ? p1 : np;
 }
 
+// Split layer s, sequence e (launch order) and kv head of decode block blk:
+// s is the largest layer with layer_prefix[s] <= blk.
+__host__ __device__ inline void block_split(const DecodeBatch &b, int Hkv, int blk, int &s, int &e, int &kv) {
+  s = 0;
+#pragma unroll
+  for (int step = kMaxSplits / 2; step >= 1; step >>= 1)
+    if (b.layer_prefix[s + step] <= blk) s += step;
+  const int pos = blk - b.layer_prefix[s];
+  e = pos / Hkv;
+  kv = pos % Hkv;
+}
+
+// End of the full pages of a split's page range [p0, p1) of a pair with
+// n_hist history tokens: only the sequence's last page can be partial.  The
+// partial page, if the split holds it, is page pf (pf < p1, pf = np - 1).
+// An empty range gives p0.
+__host__ __device__ inline int full_pages_end(int n_hist, int p0, int p1) {
+  if (p0 >= p1) return p0;
+  const int np = (n_hist + kPage - 1) / kPage; // n_hist > 0: the range is not empty
+  const int last = np - 1;
+  return (n_hist % kPage == 0 || p1 < np) ? p1 : (last > p0 ? last : p0);
+}
+
 // Optional per-kernel timing: when `on`, a launch wrapper records ev[0]
 // before and ev[1] after the kernel on its stream.
 struct KernelTimer {
