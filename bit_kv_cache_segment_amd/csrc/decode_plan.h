@@ -15,12 +15,20 @@ inline int plan_pages(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPag
 
 // Split policy of one decode launch.  A pair's work is its history pages
 // plus its window, worth window_units pages (the window's bytes over a page
-// block's bytes).  Pieces of at most P units: a pair gets
+// block's bytes, times kWindowCost).  Pieces of at most P units: a pair gets
 // S = ceil(U / P) blocks (at most kMaxSplits, and at most U / wu so that
 // only the last split can be window-only), and P is the smallest piece size
-// for which all blocks fit in one round of the device's resident block
-// slots (one decode block fills a compute unit).
-inline int window_units(int d, int G) { return (int)std::lround((double)kWindow * 4 * d / block_bytes_for(d, G)); }
+// for which all blocks fit in R rounds of the device's resident block slots
+// (one decode block fills a compute unit): one round when the batch has no
+// more pairs than slots, else kExtraRounds more than the pairs need, so that
+// long pairs are cut and rounds even out.  Blocks are dispatched largest
+// first (more splits, then more pages).
+constexpr double kWindowCost = 1.0;
+constexpr int kExtraRounds = 0;
+
+inline int window_units(int d, int G) {
+  return (int)std::lround(kWindowCost * kWindow * 4 * d / block_bytes_for(d, G));
+}
 
 inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vector<int> &len, int Hkv, int slots, int wu) {
   std::vector<int> np(b.n);
@@ -44,10 +52,13 @@ inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vecto
     for (int e = 0; e < b.n; ++e) nb += splits(e, P);
     return nb * Hkv;
   };
+  const int64_t pairs = (int64_t)b.n * Hkv;
+  const int64_t rounds = pairs <= slots ? 1 : (pairs + slots - 1) / slots + kExtraRounds;
+  const int64_t budget = rounds * slots;
   int64_t lo = 1, hi = umax; // blocks(umax) = n * Hkv: the fewest possible
   while (lo < hi) {
     const int64_t mid = (lo + hi) / 2;
-    if (blocks(mid) <= slots) hi = mid;
+    if (blocks(mid) <= budget) hi = mid;
     else lo = mid + 1;
   }
   std::vector<int> S(b.n), order(b.n);
@@ -55,7 +66,8 @@ inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vecto
     S[e] = splits(e, lo);
     order[e] = e;
   }
-  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return S[x] > S[y]; });
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return S[x] != S[y] ? S[x] > S[y] : np[x] > np[y]; });
   for (int i = 0; i < b.n; ++i) {
     const int e = order[i];
     b.seq[i] = seq_ids[e];
