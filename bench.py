@@ -72,9 +72,9 @@ def cpu_baseline(w, lengths, budget_s):
     q = synth.bf16_bits(synth.queries(w, 0))
     g, d, G = w.gqa, w.head_dim, w.group_size
     timed, pairs = 0.0, 0
+    order = [(b, kv) for kv in range(w.num_kv_heads) for b in range(w.batch)]
     with threadpool_limits(limits=1):
-        for b in range(w.batch):
-            kv = b % w.num_kv_heads
+        for b, kv in order:
             L = int(lengths[b])
             k = synth.bf16_bits(synth.kv_tokens(w, 0, b, 0, L + 1, heads=[kv]))[:, 0]
             v = synth.bf16_bits(synth.kv_tokens(w, 1, b, 0, L + 1, heads=[kv]))[:, 0]
@@ -98,6 +98,8 @@ def cpu_baseline(w, lengths, budget_s):
             pairs += 1
             if timed >= budget_s:
                 break
+    if pairs == 0:
+        return None
     t_step = timed / pairs * w.batch * w.num_kv_heads
     return {"value": w.batch / t_step, "unit": "tokens/s per layer", "cores": 1, "kind": "oracle",
             "sample": f"{pairs} of {w.batch * w.num_kv_heads} (sequence, kv head) pairs of one step "
