@@ -60,7 +60,7 @@ class PoolConfig(ctypes.Structure):
 class Profile(ctypes.Structure):
     _fields_ = [
         ("n_decode_main", ctypes.c_int32), ("ms_decode_main", ctypes.c_float),
-        ("n_decode_prep", ctypes.c_int32), ("ms_decode_prep", ctypes.c_float),
+        ("n_decode_merge", ctypes.c_int32), ("ms_decode_merge", ctypes.c_float),
         ("n_append", ctypes.c_int32), ("ms_append", ctypes.c_float),
     ]
 
@@ -242,7 +242,7 @@ def oscar_calibrate_clip(x_bf16: np.ndarray, R: np.ndarray, pct: float = 99.0) -
     return out
 
 
-PROFILE_DECODE_MAIN, PROFILE_DECODE_PREP, PROFILE_APPEND = 1, 2, 4
+PROFILE_DECODE_MAIN, PROFILE_DECODE_MERGE, PROFILE_APPEND = 1, 2, 4
 
 
 def oscar_profile_begin(h, max_calls: int, kernels: int = PROFILE_DECODE_MAIN):

@@ -7,21 +7,23 @@
 // sink and recent tokens; an online softmax merges the two results.
 //
 // Launches (one stream):
-//   q_prep_kernel, one block per (sequence with history, kv head): rotate
-//     the g = Hq/Hkv queries by R_K, scale them, and lay them out as the
-//     int8-limb MFMA operands every split block of that pair loads;
-//   decode_main_kernel, two block roles in one grid:
-//     * window blocks (first in the grid), one per (sequence, kv head):
-//       attend to the BF16 sink and recent tokens with the raw queries;
-//     * split blocks, one per (sequence, kv head, run of history pages):
-//       attend to the INT2 history in the rotated basis.
-//     Each block writes one partial (m, l, acc) per query head.
-//   decode_merge_kernel, one block per (sequence, kv head): merge the split
-//     partials, de-rotate the history accumulator by R_V^T, merge with the
-//     window partial, normalise, write fp32.
+//   decode_main_kernel, one block per (sequence, kv head, split of its
+//     history pages), one block per compute unit (4 x occupancy waves):
+//     * the block rotates the g = Hq/Hkv queries by R_K, scales them and
+//       lays them out as int8-limb MFMA operands (in shared memory);
+//     * its waves stream the split's INT2 pages in the rotated basis,
+//       taking pages from a shared counter;
+//     * the block that holds the pair's last split also attends to the
+//       BF16 sink and recent tokens with the raw queries (four waves, while
+//       the others stream pages);
+//     * the block merges its waves and de-rotates the history accumulator
+//       by R_V^T; it writes one partial (m, l, acc) per query head for the
+//       history and, if it holds it, one for the window.
+//   decode_merge_kernel, one block per (sequence, kv head): merge the
+//     partials, normalise, write fp32.
 // Softmax runs in base 2: logits are pre-multiplied by scale * log2(e).
 //
-// History split blocks (4 waves; each wave streams its own pages):
+// History pages (per wave):
 //   QK^T on v_mfma_i32_16x16x64_i8.  The rotated query of each head is put
 //   on a fixed-point grid q_int = rint(q 2^E) with |q_int| <= 2^18 and split
 //   into three signed byte limbs; an MFMA row is one (head, limb).  2-bit
@@ -112,6 +114,18 @@ __device__ __forceinline__ float row16_max_dpp(float v) {
 // normal range flush to 0, which a softmax weight can afford).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Copy a D x D fp32 table into shared memory with direct global-to-LDS
+// loads: each wave instruction moves 1 KB (lane i -> bytes 16 i .. 16 i + 15
+// of the chunk) and takes no registers.  Wave w copies chunks w, w + nw, ...
+// The caller waits for the loads (vmcnt) before a barrier and reads.
+template <int D>
+__device__ __forceinline__ void stage_table(float (*dst)[D], const float *src, int w, int nw, int lane) {
+  constexpr int NC = D * D * 4 / 1024; // 1 KB chunks
+  for (int c = w; c < NC; c += nw)
+    __builtin_amdgcn_global_load_lds((const void *)(src + c * 256 + lane * 4),
+                                     (__attribute__((address_space(3))) void *)(&dst[0][0] + c * 256), 16, 0, 0);
+}
+
 // Order LDS traffic of the lanes of one wave (no cross-wave barrier).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -131,29 +145,40 @@ struct WinSmem {
 
 // Waves of a history block that process the pair's window while the others
 // start on the pages; they join the page stream afterwards.
-constexpr int win_waves(int W) { return W < 4 ? W : 4; }
+// (Two for 16 query heads per kv head, whose per-wave window state would not
+// fit in shared memory next to the rotation table.)
+constexpr int win_waves(int W, int GQ) { return GQ >= 16 ? 2 : (W < 4 ? W : 4); }
+
+// Query record built by a history block: the int8-limb MFMA A operands
+// [row tiles][d/64][64 lanes][4 words], then per-head group sums of the
+// rotated query (at 0) and the fixed-point factors 2^-(E+4) (at 32).
+template <int D, int GQ>
+struct QueryPrep {
+  float qraw[GQ][D];
+  float qs[GQ][D];
+  int qexp[GQ];
+};
+template <int D, int GQ>
+constexpr int query_record_words() { return (GQ >= 4 ? GQ / 4 : 1) * (D / 64) * 256 + 64; }
 
 template <int D, int G, int GQ, int W>
 struct HistSmem {
   static constexpr int NG = D / G;
+  alignas(16) float R[D][D];            // R_K (query prep), then R_V^T (de-rotation)
   float alpha[W][16];  // per-wave rescale factors of the PV rows
   float zsum[W][16][NG];
   float M[W][GQ], L[W][GQ];
+  float merged[GQ][D];                  // block-merged accumulators, rotated basis
+  float mM[GQ], mL[GQ];
+  uint32_t rec[query_record_words<D, GQ>()]; // the pair's query record
   int32_t ids[kIdCache];                // page ids of a segment of the split
   uint32_t claim;                       // next page of the segment to hand out
-  WinSmem<D, GQ, win_waves(W)> win;     // window results of the window waves
+  WinSmem<D, GQ, win_waves(W, GQ)> win;     // window results of the window waves
   union {
+    QueryPrep<D, GQ> pre;               // prologue: query preparation
     _Float16 P[W][NG][16][kPRow];       // page loop: P' rows per wave (padded)
     float A[W][GQ][D];                  // epilogue: per-wave accumulators
   } u;
-};
-
-template <int D, int G, int GQ>
-struct QPrepSmem {
-  float R[D][D];     // R_K of this kv head, staged with one coalesced pass
-  float qraw[GQ][D];
-  float qs[GQ][D];
-  int qexp[GQ];
 };
 
 
@@ -334,7 +359,7 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
 }
 
 // ---------------------------------------------------------------------------
-// Query preparation for the split blocks of one (sequence, kv head).
+// Query preparation, by the whole history block, in shared memory:
 //   qs = (q . R_K) * scale * log2(e)          (fp32, fixed-order FMA chain)
 //   E  = 18 - e  with max|qs| = f 2^e, f in [0.5, 1)   ->  |qs 2^E| < 2^18
 //   A operand word [rt][mi][lane][v]: lane = (row m, k-quad r); row
@@ -342,47 +367,29 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
 //     `limb` of rint(qs[h][c] 2^E) * {16, 4, 1, 16}[v], c = 64 mi + 16 r + 4 j + v.
 //   Limbs are balanced signed bytes: X = a0 + 2^8 a1 + 2^16 a2.
 // Record tail: qsum[h][g] (group sums of qs) at 0, kfac[h] = 2^-(E+4) at 32.
+// On entry R holds R_K and qraw the query rows (after a barrier); on exit
+// (after a barrier) rec holds the record.
 // ---------------------------------------------------------------------------
-template <int D, int G, int GQ>
-__global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
-                                                          float qscale, uint32_t *__restrict__ qrec) {
-  constexpr int NG = D / G, MI = D / 64, RT = GQ >= 4 ? GQ / 4 : 1;
-  __shared__ QPrepSmem<D, G, GQ> sm;
-  const int tid = threadIdx.x, Hkv = p.Hkv, Hq = p.Hq;
-  const int e = blockIdx.x / Hkv, kv = blockIdx.x % Hkv;
-  if (b.len[e] <= kWindow) return; // no history: no split block reads this record
-  uint32_t *rec = qrec + (size_t)blockIdx.x * qprep_words(D, GQ);
-  {
-    // all loads first, then all LDS stores: one memory round trip
-    const u32x4 *src = (const u32x4 *)(p.RK + (size_t)kv * D * D);
-    u32x4 *dst = (u32x4 *)&sm.R[0][0];
-    constexpr int NL = D * D / 4 / kThreads;
-    u32x4 t[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) t[i] = __builtin_nontemporal_load(&src[tid + i * kThreads]);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) dst[tid + i * kThreads] = t[i];
-  }
-  for (int idx = tid; idx < GQ * D; idx += kThreads)
-    sm.qraw[idx / D][idx % D] = bf16f(q[((size_t)b.row[e] * Hq + kv * GQ + idx / D) * D + idx % D]);
-  __syncthreads();
-  for (int idx = tid; idx < GQ * D; idx += kThreads) {
+template <int D, int G, int GQ, int W>
+__device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const float (*R)[D], float qscale, int tid) {
+  constexpr int NT = 64 * W, NG = D / G, MI = D / 64, RT = GQ >= 4 ? GQ / 4 : 1;
+  for (int idx = tid; idx < GQ * D; idx += NT) {
     const int h = idx / D, j = idx % D;
     float a = 0.f;
 #pragma unroll 8
-    for (int i = 0; i < D; ++i) a = fmaf(sm.qraw[h][i], sm.R[i][j], a);
-    sm.qs[h][j] = a * qscale;
+    for (int i = 0; i < D; ++i) a = fmaf(pr.qraw[h][i], R[i][j], a);
+    pr.qs[h][j] = a * qscale;
   }
   __syncthreads();
   float *tail = (float *)(rec + RT * MI * 256);
   {
     // one wave per head: lane k holds channels k, k + 64 (if D = 128)
     const int w = tid >> 6, lane = tid & 63;
-    for (int h = w; h < GQ; h += kWaves) {
+    for (int h = w; h < GQ; h += W) {
       float v[D / 64], mx = 0.f;
 #pragma unroll
       for (int k = 0; k < D / 64; ++k) {
-        v[k] = sm.qs[h][lane + 64 * k];
+        v[k] = pr.qs[h][lane + 64 * k];
         mx = fmaxf(mx, fabsf(v[k]));
       }
       mx = wave_max(mx);
@@ -403,13 +410,13 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch
       frexpf(mx, &ex);
       const int E = mx > 0.f ? 18 - ex : 0;
       if (lane == 0) {
-        sm.qexp[h] = E;
+        pr.qexp[h] = E;
         tail[32 + h] = ldexpf(1.f, -(E + 4));
       }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < RT * MI * 256; idx += kThreads) {
+  for (int idx = tid; idx < RT * MI * 256; idx += NT) {
     const int v = idx & 3, lane = (idx >> 2) & 63, mi = (idx >> 8) % MI, rt = (idx >> 8) / MI;
     const int m = lane & 15, r = lane >> 4;
     const int h = rt * 4 + (m >> 2), lam = m & 3;
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch
     for (int j4 = 0; j4 < 4; ++j4) {
       const int c = 64 * mi + 16 * r + 4 * j4 + v;
       int X = 0;
-      if (live) X = (int)rintf(ldexpf(sm.qs[h][c], sm.qexp[h])) * (v == 1 ? 4 : (v == 2 ? 1 : 16));
+      if (live) X = (int)rintf(ldexpf(pr.qs[h][c], pr.qexp[h])) * (v == 1 ? 4 : (v == 2 ? 1 : 16));
       const int a0 = (int)(int8_t)(X & 0xff);
       const int X1 = (X - a0) >> 8;
       const int a1 = (int)(int8_t)(X1 & 0xff);
@@ -429,6 +436,7 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(PoolDev p, DecodeBatch
     }
     rec[idx] = word;
   }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -470,9 +478,9 @@ constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
 template <int D, int G, int GQ>
 __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
-                              const uint32_t *qrec, float *ws_hist, float *ws_win, const uint16_t *q, float qscale,
+                              float *ws_hist, float *ws_win, const uint16_t *q, float qscale,
                               int blk, int e, int kv, int p0, int p1, bool with_window) {
-  constexpr int W = main_waves(D, G, GQ), NT = 64 * W, WW = win_waves(W);
+  constexpr int W = main_waves(D, G, GQ), NT = 64 * W, WW = win_waves(W, GQ);
   constexpr int NG = D / G;                // scale/zero groups per token
   constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
   constexpr int RT = GQ >= 4 ? GQ / 4 : 1; // MFMA row tiles of 4 heads x 4 limb rows
@@ -488,27 +496,77 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   const size_t hoff = (size_t)kv * p.block_bytes;
   const int pf = full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
 
-  // ---- prologue: rows of P' that no head owns stay zero for the whole
-  // loop; the first segment's page ids are staged (one barrier).
-  for (int idx = tid; idx < W * 16; idx += NT) sm.alpha[idx / 16][idx % 16] = 1.f;
+  // ---- prologue: R_K (direct to shared memory), the query rows and the
+  // first segment's page ids are staged; the block builds the query record;
+  // R_V^T (for the de-rotation at the end) replaces R_K while the pages
+  // stream; rows of P' that no head owns stay zero for the whole loop.
+  stage_table<D>(sm.R, p.RK + (size_t)kv * D * D, w, W, lane);
   {
+    const uint16_t *qrow = q + ((size_t)b.row[e] * p.Hq + kv * GQ) * D;
+    for (int idx = tid; idx < GQ * D; idx += NT) sm.u.pre.qraw[idx / D][idx % D] = bf16f(qrow[idx]);
+  }
+  for (int i = p0 + tid; i < min(pf, p0 + kIdCache); i += NT) sm.ids[i - p0] = ptab[i];
+  if (tid == 0) sm.claim = (uint32_t)p0;
+  for (int idx = tid; idx < W * 16; idx += NT) sm.alpha[idx / 16][idx % 16] = 1.f;
+  __builtin_amdgcn_s_waitcnt(0); // the direct loads of R_K have landed
+  __syncthreads();
+
+  // Page stream state.  Segment [seg0, segf) of the split's full pages has
+  // its ids in shared memory; deterministic pools take pages w, w + W, ...
+  // of the segment, others take them from the shared counter.
+  constexpr int PF = kPrefetch<D, G, GQ>, NB = PF + 1;
+  const uint8_t *dummy = (const uint8_t *)p.RK; // >= one page block, read-only
+  const bool det = p.deterministic != 0;
+  int seg0 = p0, segf = min(pf, p0 + kIdCache), next_static = p0 + w;
+  auto take = [&]() __attribute__((always_inline)) {
+    uint32_t c = 0;
+    if (!det && lane == 0) c = atomicAdd(&sm.claim, 1u);
+    const int pg = det ? next_static : (int)__builtin_amdgcn_readlane(c, 0);
+    next_static += W;
+    return pg;
+  };
+  auto load = [&](PageRegs<D, G> &buf, int page) __attribute__((always_inline)) {
+    const int id = __builtin_amdgcn_readfirstlane(sm.ids[min(page, segf - 1) - seg0]);
+    load_page<D, G>(buf, page < segf ? p.pages + (size_t)id * hstride + hoff : dummy, n, r);
+  };
+  PageRegs<D, G> buf[NB];
+  int pg[NB];
+  // The first WW waves take the pair's window (if this block holds it)
+  // before joining the page stream; the other waves issue the loads of
+  // their first pages before the query preparation, which then overlaps
+  // them.  The two kinds of wave run the same barriers (query_prep's and
+  // one more) on separate code paths, so the registers of the primed pages
+  // are not held across the window.
+  auto finish_prologue = [&]() __attribute__((always_inline)) {
+    query_prep<D, G, GQ, W>(sm.u.pre, sm.rec, sm.R, qscale, tid);
+    stage_table<D>(sm.R, p.RVt + (size_t)kv * D * D, w, W, lane);
     _Float16 *P = &sm.u.P[0][0][0][0];
     for (int idx = tid; idx < W * NG * 16 * kPRow; idx += NT) P[idx] = (_Float16)0.f;
+    __syncthreads();
+  };
+  bool primed = false;
+  if (!(with_window && w < WW)) {
+    if (p0 < pf) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        pg[i] = take();
+        load(buf[i], pg[i]);
+      }
+      primed = true;
+    }
+    finish_prologue();
+  } else {
+    finish_prologue();
+    window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
   }
   auto stage = [&](int s0, int sf) __attribute__((always_inline)) {
     for (int i = s0 + tid; i < sf; i += NT) sm.ids[i - s0] = ptab[i];
     if (tid == 0) sm.claim = (uint32_t)s0;
     __syncthreads();
   };
-  stage(p0, min(pf, p0 + kIdCache));
-  // The first WW waves take the pair's window (if this block holds it)
-  // before joining the page stream; the other waves start on the pages.
-  // The history state below is set up afterwards, so it is not live
-  // during the window.
-  if (with_window && w < WW) window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
 
   // this pair's query record
-  const uint32_t *rec = qrec + ((size_t)e * Hkv + kv) * qprep_words(D, GQ);
+  const uint32_t *rec = sm.rec;
   const float *tail = (const float *)(rec + RT * MI * 256);
   v4i Aq[RT][MI];
   float kfac[RT], qsum[RT][NG];
@@ -670,35 +728,23 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // loads (a page past the segment end reads a small cached table instead),
   // so each wait is an exact count of younger loads.  Only a sequence's
   // last page can be partial; it goes to the last wave after the loop.
-  constexpr int PF = kPrefetch<D, G, GQ>, NB = PF + 1;
-  const uint8_t *dummy = (const uint8_t *)p.RK; // >= one page block, read-only
-  const bool det = p.deterministic != 0;
   for (int s0 = p0; s0 < pf; s0 += kIdCache) {
     const int sf = min(pf, s0 + kIdCache);
     if (s0 != p0) {
       __syncthreads(); // every wave is done with the previous ids
       stage(s0, sf);
+      seg0 = s0;
+      segf = sf;
+      next_static = s0 + w;
     }
-    // deterministic pools: wave w takes pages w, w + W, ... of the segment
-    int next_static = s0 + w;
-    auto take = [&]() __attribute__((always_inline)) {
-      uint32_t c = 0;
-      if (!det && lane == 0) c = atomicAdd(&sm.claim, 1u);
-      const int pg = det ? next_static : (int)__builtin_amdgcn_readlane(c, 0);
-      next_static += W;
-      return pg;
-    };
-    auto load = [&](PageRegs<D, G> &buf, int page) __attribute__((always_inline)) {
-      const int id = __builtin_amdgcn_readfirstlane(sm.ids[min(page, sf - 1) - s0]);
-      load_page<D, G>(buf, page < sf ? p.pages + (size_t)id * hstride + hoff : dummy, n, r);
-    };
-    PageRegs<D, G> buf[NB];
-    int pg[NB];
+    if (!primed) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      pg[i] = take();
-      load(buf[i], pg[i]);
+      for (int i = 0; i < PF; ++i) {
+        pg[i] = take();
+        load(buf[i], pg[i]);
+      }
     }
+    primed = false;
     while (pg[0] < sf) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -739,7 +785,41 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       if (h < GQ) sm.u.A[w][h][c] = fmaf(acc[j][i], unscale, sm.zsum[w][h][c / G]);
     }
   __syncthreads();
-  block_merge_store<D, GQ, W>(sm.M, sm.L, sm.u.A, ws_hist + (size_t)blk * GQ * (D + 2));
+  // block merge of the waves (rotated basis), then de-rotation by R_V^T:
+  // the stored partial is in the basis of V itself
+  for (int idx = tid; idx < GQ * D; idx += NT) {
+    const int h = idx / D, c = idx % D;
+    float m = -INFINITY;
+    for (int ww = 0; ww < W; ++ww) m = fmaxf(m, sm.M[ww][h]);
+    float a = 0.f, l = 0.f;
+    for (int ww = 0; ww < W; ++ww) {
+      const float f = sm.M[ww][h] == -INFINITY ? 0.f : exp2f(sm.M[ww][h] - m);
+      a = fmaf(f, sm.u.A[ww][h][c], a);
+      l = fmaf(f, sm.L[ww][h], l);
+    }
+    sm.merged[h][c] = a;
+    if (c == 0) {
+      sm.mM[h] = m;
+      sm.mL[h] = l;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0); // the direct loads of R_V^T have landed
+  __syncthreads();
+  {
+    float *dst = ws_hist + (size_t)blk * GQ * (D + 2);
+    for (int idx = tid; idx < GQ * D; idx += NT) {
+      const int h = idx / D, c = idx % D;
+      float der = 0.f;
+#pragma unroll 16
+      for (int j = 0; j < D; ++j) der = fmaf(sm.merged[h][j], sm.R[j][c], der);
+      float *o = dst + (size_t)h * (D + 2);
+      o[c] = der;
+      if (c == 0) {
+        o[D] = sm.mM[h];
+        o[D + 1] = sm.mL[h];
+      }
+    }
+  }
   // the window waves' results were written before the barriers above
   if (with_window) block_merge_store<D, GQ, WW>(sm.win.M, sm.win.L, sm.win.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2));
 }
@@ -748,7 +828,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
 template <int D, int G, int GQ>
 __global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
 void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
-                        float *__restrict__ ws, const uint32_t *__restrict__ qrec) {
+                        float *__restrict__ ws) {
   constexpr int W = main_waves(D, G, GQ);
   __shared__ MainSmem<D, G, GQ, W> sm;
   float *ws_win = ws;
@@ -761,106 +841,79 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   int p0, p1;
   split_range(np, S, s, b.win_units, p0, p1);
   if (p0 < p1)
-    history_block<D, G, GQ>(sm.h, p, b, qrec, ws_hist, ws_win, q, qscale, blk, e, kv, p0, p1, s == S - 1);
-  else if (s == S - 1)
+    history_block<D, G, GQ>(sm.h, p, b, ws_hist, ws_win, q, qscale, blk, e, kv, p0, p1, s == S - 1);
+  else if (s == S - 1) {
     window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, e, kv);
+    // this split holds no pages: an empty history partial for the merge
+    float *dst = ws_hist + (size_t)blk * GQ * (D + 2);
+    for (int idx = threadIdx.x; idx < GQ * (D + 2); idx += 64 * W) dst[idx] = idx % (D + 2) == D ? -INFINITY : 0.f;
+  }
 }
 
-// Merge of one (sequence, kv head): split partials -> history (m, l, acc),
-// acc . R_V^T, then the window partial, then out = acc / l.  Every load that
-// does not depend on another is issued up front: R_V^T goes to shared memory
-// in one coalesced pass, split partials are all read before any is used.
-constexpr int kMergeThreads = 512;
-
-template <int D, int GQ>
-struct MergeSmem {
-  float R[D][D];   // R_V^T of this kv head
-  float AH[GQ][D]; // merged history accumulators (rotated basis), normalised weights
-};
+// Merge of one (sequence, kv head): the split partials (already in the
+// basis of V; a split without pages holds m = -inf) and the window partial
+// -> out = acc / l.  Splits are read four at a time with every load of a
+// batch issued before any use; one thread per (head, channel).
+constexpr int kMergeThreads = 256;
 
 template <int D, int GQ>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
                                                                      const float *__restrict__ ws) {
   constexpr int HG = kMergeThreads / D;       // head groups
   constexpr int HPT = (GQ + HG - 1) / HG;     // heads per thread
-  __shared__ MergeSmem<D, GQ> sm;
+  constexpr int SB = 4;                       // splits per batch
   const int e = blockIdx.x / p.Hkv, kv = blockIdx.x % p.Hkv, tid = threadIdx.x;
   const int Hkv = p.Hkv, Hq = p.Hq;
   const int c = tid % D, hg = tid / D;
   const float *ws_win = ws;
   const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
   const int S = b.nsplit[e];
-  // splits that hold history pages (only the last one can hold the window alone)
-  const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
-  uint32_t has_mask = 0;
-  for (int s = 0; s < S; ++s) {
-    int p0, p1;
-    split_range(np, S, s, b.win_units, p0, p1);
-    if (p0 < p1) has_mask |= 1u << s;
-  }
-  const bool has = has_mask != 0;
-  if (has) {
-    const u32x4 *src = (const u32x4 *)(p.RVt + (size_t)kv * D * D);
-    u32x4 *dst = (u32x4 *)&sm.R[0][0];
-    constexpr int NL = D * D / 4 / kMergeThreads;
-    u32x4 t[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) t[i] = src[tid + i * kMergeThreads];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) dst[tid + i * kMergeThreads] = t[i];
-  }
-  // every thread issues all of its loads (splits' m, l, acc and the window
-  // partial) before using any
-  float mwin[HPT], lwin[HPT], awin[HPT], mH[HPT], lH[HPT], aH[HPT];
+  float m[HPT], l[HPT], a[HPT];
 #pragma unroll
   for (int k = 0; k < HPT; ++k) {
     const int h = min(hg + k * HG, GQ - 1);
     const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
-    mwin[k] = win[D];
-    lwin[k] = win[D + 1];
-    awin[k] = win[c];
-    // split s of this pair wrote its partial at block layer_prefix[s] + e Hkv + kv
-    float ms[kMaxSplits], ls[kMaxSplits], as[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      const bool v = (has_mask >> s) & 1u;
-      const float *ph = ws_hist + ((size_t)(b.layer_prefix[s] + e * Hkv + kv) * GQ + h) * (D + 2);
-      ms[s] = v ? ph[D] : -INFINITY;
-      ls[s] = v ? ph[D + 1] : 0.f;
-      as[s] = v ? ph[c] : 0.f;
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) m = fmaxf(m, ms[s]);
-    float l = 0.f, a = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      const float f = ms[s] == -INFINITY ? 0.f : exp2f(ms[s] - m);
-      l = fmaf(f, ls[s], l);
-      a = fmaf(f, as[s], a);
-    }
-    mH[k] = m;
-    lH[k] = l;
-    aH[k] = a;
-    if (has && hg + k * HG < GQ) sm.AH[h][c] = a;
+    m[k] = win[D];
+    l[k] = win[D + 1];
+    a[k] = win[c];
   }
-  __syncthreads();
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float hm[SB][HPT], hl[SB][HPT], ha[SB][HPT];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      // split s of this pair wrote its partial at block layer_prefix[s] + e Hkv + kv
+      const int ss = min(s0 + j, S - 1);
+      const float *ps = ws_hist + (size_t)(b.layer_prefix[ss] + e * Hkv + kv) * GQ * (D + 2);
+#pragma unroll
+      for (int k = 0; k < HPT; ++k) {
+        const float *ph = ps + (size_t)min(hg + k * HG, GQ - 1) * (D + 2);
+        hm[j][k] = ph[D];
+        hl[j][k] = ph[D + 1];
+        ha[j][k] = ph[c];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      float mm = m[k];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (s0 + j < S) mm = fmaxf(mm, hm[j][k]);
+      const float f0 = exp2f(m[k] - mm); // the window partial is never empty
+      l[k] *= f0;
+      a[k] *= f0;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const float f = (s0 + j < S && hm[j][k] != -INFINITY) ? exp2f(hm[j][k] - mm) : 0.f;
+        l[k] = fmaf(f, hl[j][k], l[k]);
+        a[k] = fmaf(f, ha[j][k], a[k]);
+      }
+      m[k] = mm;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < HPT; ++k) {
     const int h = hg + k * HG;
-    if (h >= GQ) continue;
-    float o;
-    if (has && mH[k] != -INFINITY) {
-      float der = 0.f;
-#pragma unroll 16
-      for (int j = 0; j < D; ++j) der = fmaf(sm.AH[h][j], sm.R[j][c], der);
-      const float m = fmaxf(mwin[k], mH[k]), fw = exp2f(mwin[k] - m), fh = exp2f(mH[k] - m);
-      o = (fw * awin[k] + fh * der) / (fw * lwin[k] + fh * lH[k]);
-    } else {
-      o = awin[k] / lwin[k];
-    }
-    (void)aH[k];
-    out[((size_t)b.row[e] * Hq + kv * GQ + h) * D + c] = o;
+    if (h < GQ) out[((size_t)b.row[e] * Hq + kv * GQ + h) * D + c] = a[k] / l[k];
   }
 }
 
@@ -868,17 +921,12 @@ template <int D, int G, int GQ>
 hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                        float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
   const int blocks = b.hist_blocks;
-  uint32_t *qrec = (uint32_t *)(ws + (size_t)b.n * p.Hq * (D + 2) + (size_t)b.hist_blocks * GQ * (D + 2));
   // Timed launches take their start/stop timestamps from the dispatch itself
   // (no extra packets between kernels).
-  if (b.total_pages > 0)
-    hipExtLaunchKernelGGL((q_prep_kernel<D, G, GQ>), dim3(b.n * p.Hkv), dim3(kThreads), 0, s,
-                          tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, qrec);
   hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
-                        tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws,
-                        (const uint32_t *)qrec);
-  hipLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(kMergeThreads), 0, s, p, b, out,
-                     (const float *)ws);
+                        tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws);
+  hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(kMergeThreads), 0, s,
+                        tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, out, (const float *)ws);
   return hipGetLastError();
 }
 

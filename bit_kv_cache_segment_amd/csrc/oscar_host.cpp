@@ -111,7 +111,7 @@ struct Profiler {
   bool on = false;
   int cap = 0;
   uint32_t mask = 0;
-  std::vector<hipEvent_t> ev[3]; // decode main, query prep, append: 2 per launch
+  std::vector<hipEvent_t> ev[3]; // decode main, decode merge, append: 2 per launch
   int used[3] = {0, 0, 0};
   KernelTimer next(int kind) {
     KernelTimer t;
@@ -608,8 +608,8 @@ int oscar_profile_end(oscar_pool *p, oscar_profile *out) {
     }
   out->n_decode_main = p->prof.used[0];
   out->ms_decode_main = ms[0];
-  out->n_decode_prep = p->prof.used[1];
-  out->ms_decode_prep = ms[1];
+  out->n_decode_merge = p->prof.used[1];
+  out->ms_decode_merge = ms[1];
   out->n_append = p->prof.used[2];
   out->ms_append = ms[2];
   p->prof.release();

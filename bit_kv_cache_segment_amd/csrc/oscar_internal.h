@@ -161,19 +161,13 @@ int decode_main_blocks_per_cu(const PoolDev &p);
 
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out,
                          float scale, float *ws, hipStream_t s, const KernelTimer &t_main,
-                         const KernelTimer &t_prep);
+                         const KernelTimer &t_merge);
 
-// Per (sequence, kv head) query record written by the q-prep kernel and read
-// by every split block of that pair: the int8-limb MFMA A operands
-// [row tiles][d/64][64 lanes][4 words], then per-head group sums of the
-// rotated query and the fixed-point factors 2^-(E+4) (64 words).
-__host__ __device__ inline int qprep_words(int d, int g) { return (g >= 4 ? g / 4 : 1) * (d / 64) * 256 + 64; }
 
-// Workspace (4-byte words) of one decode launch: window partials, split
-// partials, query records.
+// Workspace (4-byte words) of one decode launch: window partials and split
+// partials.
 inline size_t decode_ws_floats(int Hq, int d, int n, long hist_blocks, int g) {
-  const int Hkv = Hq / g;
-  return (size_t)n * Hq * (d + 2) + (size_t)hist_blocks * g * (d + 2) + (size_t)n * Hkv * qprep_words(d, g);
+  return (size_t)n * Hq * (d + 2) + (size_t)hist_blocks * g * (d + 2);
 }
 
 } // namespace oscar

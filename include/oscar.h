@@ -216,14 +216,14 @@ int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R
  * events.  Each event record adds a few microseconds between launches, so
  * time only the kernels of interest.  Errors: EINVAL, EHIP. */
 typedef struct oscar_profile {
-    int32_t n_decode_main;   float ms_decode_main;   /* INT2 splits + BF16 window + merge */
-    int32_t n_decode_prep;   float ms_decode_prep;   /* query rotation and layout         */
-    int32_t n_append;        float ms_append;        /* append / eviction                 */
+    int32_t n_decode_main;   float ms_decode_main;   /* query prep, INT2 history, BF16 window */
+    int32_t n_decode_merge;  float ms_decode_merge;  /* merge of the partials                 */
+    int32_t n_append;        float ms_append;        /* append / eviction                     */
 } oscar_profile;
 
-#define OSCAR_PROFILE_DECODE_MAIN 1u  /* INT2 splits + BF16 window kernel  */
-#define OSCAR_PROFILE_DECODE_PREP 2u  /* query rotation and layout kernel  */
-#define OSCAR_PROFILE_APPEND      4u  /* append / eviction kernel          */
+#define OSCAR_PROFILE_DECODE_MAIN  1u  /* main decode kernel               */
+#define OSCAR_PROFILE_DECODE_MERGE 2u  /* merge kernel                     */
+#define OSCAR_PROFILE_APPEND       4u  /* append / eviction kernel         */
 
 int oscar_profile_begin(oscar_pool *pool, int32_t max_calls, uint32_t kernels);
 int oscar_profile_end(oscar_pool *pool, oscar_profile *out);
