@@ -825,6 +825,60 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
 }
 
 
+// Merge of one (sequence, kv head): the split partials (already in the
+// basis of V; a split without pages holds m = -inf) and the window partial
+// -> out = acc / l.  Splits are read four at a time with every load of a
+// batch issued before any use; one thread per (head, channel) output.
+template <int D, int GQ, int NT>
+__device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, int e, int kv,
+                           int tid) {
+  constexpr int SB = 4; // splits per batch
+  const int Hkv = p.Hkv, Hq = p.Hq;
+  const float *ws_win = ws;
+  const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
+  const int S = b.nsplit[e];
+  for (int idx = tid; idx < GQ * D; idx += NT) {
+    const int h = idx / D, c = idx % D;
+    const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
+    float m = win[D], l = win[D + 1], a = win[c];
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      float hm[SB], hl[SB], ha[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        // split s of this pair wrote its partial at block layer_prefix[s] + e Hkv + kv
+        const int ss = min(s0 + j, S - 1);
+        const float *ph = ws_hist + ((size_t)(b.layer_prefix[ss] + e * Hkv + kv) * GQ + h) * (D + 2);
+        hm[j] = ph[D];
+        hl[j] = ph[D + 1];
+        ha[j] = ph[c];
+      }
+      float mm = m;
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (s0 + j < S) mm = fmaxf(mm, hm[j]);
+      const float f0 = exp2f(m - mm); // the window partial is never empty
+      l *= f0;
+      a *= f0;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const float f = (s0 + j < S && hm[j] != -INFINITY) ? exp2f(hm[j] - mm) : 0.f;
+        l = fmaf(f, hl[j], l);
+        a = fmaf(f, ha[j], a);
+      }
+      m = mm;
+    }
+    out[((size_t)b.row[e] * Hq + kv * GQ + h) * D + c] = a / l;
+  }
+}
+
+constexpr int kMergeThreads = 256;
+
+template <int D, int GQ>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
+                                                                     const float *__restrict__ ws) {
+  merge_pair<D, GQ, kMergeThreads>(p, b, out, ws, blockIdx.x / p.Hkv, blockIdx.x % p.Hkv, threadIdx.x);
+}
+
 template <int D, int G, int GQ>
 __global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
 void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
@@ -850,73 +904,6 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   }
 }
 
-// Merge of one (sequence, kv head): the split partials (already in the
-// basis of V; a split without pages holds m = -inf) and the window partial
-// -> out = acc / l.  Splits are read four at a time with every load of a
-// batch issued before any use; one thread per (head, channel).
-constexpr int kMergeThreads = 256;
-
-template <int D, int GQ>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
-                                                                     const float *__restrict__ ws) {
-  constexpr int HG = kMergeThreads / D;       // head groups
-  constexpr int HPT = (GQ + HG - 1) / HG;     // heads per thread
-  constexpr int SB = 4;                       // splits per batch
-  const int e = blockIdx.x / p.Hkv, kv = blockIdx.x % p.Hkv, tid = threadIdx.x;
-  const int Hkv = p.Hkv, Hq = p.Hq;
-  const int c = tid % D, hg = tid / D;
-  const float *ws_win = ws;
-  const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
-  const int S = b.nsplit[e];
-  float m[HPT], l[HPT], a[HPT];
-#pragma unroll
-  for (int k = 0; k < HPT; ++k) {
-    const int h = min(hg + k * HG, GQ - 1);
-    const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
-    m[k] = win[D];
-    l[k] = win[D + 1];
-    a[k] = win[c];
-  }
-  for (int s0 = 0; s0 < S; s0 += SB) {
-    float hm[SB][HPT], hl[SB][HPT], ha[SB][HPT];
-#pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      // split s of this pair wrote its partial at block layer_prefix[s] + e Hkv + kv
-      const int ss = min(s0 + j, S - 1);
-      const float *ps = ws_hist + (size_t)(b.layer_prefix[ss] + e * Hkv + kv) * GQ * (D + 2);
-#pragma unroll
-      for (int k = 0; k < HPT; ++k) {
-        const float *ph = ps + (size_t)min(hg + k * HG, GQ - 1) * (D + 2);
-        hm[j][k] = ph[D];
-        hl[j][k] = ph[D + 1];
-        ha[j][k] = ph[c];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < HPT; ++k) {
-      float mm = m[k];
-#pragma unroll
-      for (int j = 0; j < SB; ++j)
-        if (s0 + j < S) mm = fmaxf(mm, hm[j][k]);
-      const float f0 = exp2f(m[k] - mm); // the window partial is never empty
-      l[k] *= f0;
-      a[k] *= f0;
-#pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        const float f = (s0 + j < S && hm[j][k] != -INFINITY) ? exp2f(hm[j][k] - mm) : 0.f;
-        l[k] = fmaf(f, hl[j][k], l[k]);
-        a[k] = fmaf(f, ha[j][k], a[k]);
-      }
-      m[k] = mm;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < HPT; ++k) {
-    const int h = hg + k * HG;
-    if (h < GQ) out[((size_t)b.row[e] * Hq + kv * GQ + h) * D + c] = a[k] / l[k];
-  }
-}
-
 template <int D, int G, int GQ>
 hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                        float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
@@ -925,6 +912,8 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
   // (no extra packets between kernels).
   hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
                         tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws);
+  // A separate launch: merging in the last block of each pair needs
+  // device-scope fences, which cost more than this kernel here.
   hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(kMergeThreads), 0, s,
                         tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, out, (const float *)ws);
   return hipGetLastError();
