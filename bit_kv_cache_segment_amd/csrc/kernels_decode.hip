@@ -72,22 +72,6 @@ __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uin
 __device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu)); }
 __device__ __forceinline__ float f16hi(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16)); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-// reductions over the 16 lanes of an aligned lane row
-__device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 // Sum over aligned groups of N lanes (N = 8 or 16) by DPP butterflies; every
 // lane of a group ends with the same bits (each step adds a commuted pair).
 template <int CTRL>
@@ -110,20 +94,107 @@ __device__ __forceinline__ float row16_max_dpp(float v) {
   v = fmaxf(v, dpp_f<0x141>(v));
   return fmaxf(v, dpp_f<0x140>(v));
 }
+// Value of lane k (wave-uniform result).
+__device__ __forceinline__ float lane_f(float v, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+// Maximum / sum over all 64 lanes: DPP inside each 16-lane row, then the
+// four row results by readlane.  Every lane gets the result.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = row16_max_dpp(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = lanes_sum<16>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
 // 2^x by the hardware instruction (x = -inf gives 0; results below the
 // normal range flush to 0, which a softmax weight can afford).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Copy a D x D fp32 table into shared memory with direct global-to-LDS
-// loads: each wave instruction moves 1 KB (lane i -> bytes 16 i .. 16 i + 15
-// of the chunk) and takes no registers.  Wave w copies chunks w, w + nw, ...
-// The caller waits for the loads (vmcnt) before a barrier and reads.
+// A D x D fp32 rotation table in shared memory: 1 KB chunks of 256 / D
+// rows, each followed by 16 pad floats, so that rows of chunks whose index
+// differs mod 4 start 16 banks apart.
+constexpr int kChunkPad = 16;
 template <int D>
-__device__ __forceinline__ void stage_table(float (*dst)[D], const float *src, int w, int nw, int lane) {
-  constexpr int NC = D * D * 4 / 1024; // 1 KB chunks
+struct RTable {
+  static constexpr int RPC = 256 / D; // rows per chunk
+  alignas(16) float c[D * D / 256][256 + kChunkPad];
+};
+
+// Copy a D x D fp32 table into shared memory with direct global-to-LDS
+// loads: each wave instruction moves one 1 KB chunk (lane i -> bytes
+// 16 i .. 16 i + 15) and takes no registers.  Wave w copies chunks w, w + nw,
+// ...  The caller waits for the loads (vmcnt) before a barrier and reads.
+template <int D>
+__device__ __forceinline__ void stage_table(RTable<D> &dst, const float *src, int w, int nw, int lane) {
+  constexpr int NC = D * D / 256;
   for (int c = w; c < NC; c += nw)
     __builtin_amdgcn_global_load_lds((const void *)(src + c * 256 + lane * 4),
-                                     (__attribute__((address_space(3))) void *)(&dst[0][0] + c * 256), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void *)(&dst.c[c][0]), 16, 0, 0);
+}
+
+// Row stride (floats) of a head-interleaved table xT[D][.]: row j holds
+// channel j of every head; padded so that rows 1 KB-chunk apart fall in
+// distinct banks for 16-byte reads.
+constexpr int qpad(int GQ) { return GQ >= 4 ? GQ + 4 : GQ; }
+
+template <int GQ>
+__device__ __forceinline__ void load_heads(float (&x)[GQ], const float *row) {
+  if constexpr (GQ >= 4) {
+#pragma unroll
+    for (int h = 0; h < GQ; h += 4) {
+      const float4 t = *(const float4 *)(row + h);
+      x[h] = t.x;
+      x[h + 1] = t.y;
+      x[h + 2] = t.z;
+      x[h + 3] = t.w;
+    }
+  } else if constexpr (GQ == 2) {
+    const float2 t = *(const float2 *)row;
+    x[0] = t.x;
+    x[1] = t.y;
+  } else {
+    x[0] = row[0];
+  }
+}
+
+// y[h][c] = sum_j xT[j][h] R[j][c] for the GQ heads: wave w computes the
+// blocks of 16 columns cb = w, w + W, ...; lane (c16, quarter qq) sums the
+// rows of the chunks with index = qq mod 4 (the four quarters read distinct
+// banks of R and each quarter reads one xT row, broadcast), then the
+// quarters are added across the wave.  emit(h, c, y) sees each result once,
+// in a lane of quarter h mod 4.
+template <int D, int GQ, int W, class Emit>
+__device__ __forceinline__ void contract_columns(const float *xT, const RTable<D> &R, int w, int lane, Emit emit) {
+  constexpr int RPC = RTable<D>::RPC, NCB = D / 16, QP = qpad(GQ);
+  const int c16 = lane & 15, qq = lane >> 4;
+  for (int cb = w; cb < NCB; cb += W) {
+    const int c = 16 * cb + c16;
+    float a[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) a[h] = 0.f;
+#pragma unroll 4
+    for (int t = 0; t < D / (4 * RPC); ++t)
+#pragma unroll
+      for (int b = 0; b < RPC; ++b) {
+        const int ch = 4 * t + qq;
+        const float rv = R.c[ch][b * D + c];
+        float x[GQ];
+        load_heads<GQ>(x, xT + (ch * RPC + b) * QP);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) a[h] = fmaf(x[h], rv, a[h]);
+      }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      a[h] += __shfl_xor(a[h], 16, 64);
+      a[h] += __shfl_xor(a[h], 32, 64);
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+      if ((h & 3) == qq) emit(h, c, a[h]);
+  }
 }
 
 // Order LDS traffic of the lanes of one wave (no cross-wave barrier).
@@ -154,9 +225,8 @@ constexpr int win_waves(int W, int GQ) { return GQ >= 16 ? 2 : (W < 4 ? W : 4); 
 // rotated query (at 0) and the fixed-point factors 2^-(E+4) (at 32).
 template <int D, int GQ>
 struct QueryPrep {
-  float qraw[GQ][D];
-  float qs[GQ][D];
-  int qexp[GQ];
+  alignas(16) float qT[D][qpad(GQ)]; // query rows, head-interleaved
+  float qs[GQ][D];                   // rotated, scaled query rows
 };
 template <int D, int GQ>
 constexpr int query_record_words() { return (GQ >= 4 ? GQ / 4 : 1) * (D / 64) * 256 + 64; }
@@ -164,17 +234,17 @@ constexpr int query_record_words() { return (GQ >= 4 ? GQ / 4 : 1) * (D / 64) * 
 template <int D, int G, int GQ, int W>
 struct HistSmem {
   static constexpr int NG = D / G;
-  alignas(16) float R[D][D];            // R_K (query prep), then R_V^T (de-rotation)
+  RTable<D> R;                          // R_K (query prep), then R_V^T (de-rotation)
   float alpha[W][16];  // per-wave rescale factors of the PV rows
   float zsum[W][16][NG];
-  float M[W][GQ], L[W][GQ];
-  float merged[GQ][D];                  // block-merged accumulators, rotated basis
-  float mM[GQ], mL[GQ];
+  alignas(16) float M[W][GQ];
+  float L[W][GQ];
+  alignas(16) float mT[D][qpad(GQ)];    // block-merged accumulators (rotated basis), head-interleaved
   uint32_t rec[query_record_words<D, GQ>()]; // the pair's query record
   int32_t ids[kIdCache];                // page ids of a segment of the split
   uint32_t claim;                       // next page of the segment to hand out
   WinSmem<D, GQ, win_waves(W, GQ)> win;     // window results of the window waves
-  union {
+  union alignas(16) {
     QueryPrep<D, GQ> pre;               // prologue: query preparation
     _Float16 P[W][NG][16][kPRow];       // page loop: P' rows per wave (padded)
     float A[W][GQ][D];                  // epilogue: per-wave accumulators
@@ -360,81 +430,72 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
 
 // ---------------------------------------------------------------------------
 // Query preparation, by the whole history block, in shared memory:
-//   qs = (q . R_K) * scale * log2(e)          (fp32, fixed-order FMA chain)
+//   qs = (q . R_K) * scale * log2(e)          (fp32)
 //   E  = 18 - e  with max|qs| = f 2^e, f in [0.5, 1)   ->  |qs 2^E| < 2^18
 //   A operand word [rt][mi][lane][v]: lane = (row m, k-quad r); row
 //     m = 4 hh + limb of head 4 rt + hh; byte j of register v holds limb
 //     `limb` of rint(qs[h][c] 2^E) * {16, 4, 1, 16}[v], c = 64 mi + 16 r + 4 j + v.
 //   Limbs are balanced signed bytes: X = a0 + 2^8 a1 + 2^16 a2.
 // Record tail: qsum[h][g] (group sums of qs) at 0, kfac[h] = 2^-(E+4) at 32.
-// On entry R holds R_K and qraw the query rows (after a barrier); on exit
-// (after a barrier) rec holds the record.
+// On entry R holds R_K and qT the query rows (after a barrier).  The product
+// is taken by column blocks; then one wave per head finds E and the group
+// sums and writes the head's words.  On exit (after a barrier) rec holds the
+// record.
 // ---------------------------------------------------------------------------
 template <int D, int G, int GQ, int W>
-__device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const float (*R)[D], float qscale, int tid) {
-  constexpr int NT = 64 * W, NG = D / G, MI = D / 64, RT = GQ >= 4 ? GQ / 4 : 1;
-  for (int idx = tid; idx < GQ * D; idx += NT) {
-    const int h = idx / D, j = idx % D;
-    float a = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < D; ++i) a = fmaf(pr.qraw[h][i], R[i][j], a);
-    pr.qs[h][j] = a * qscale;
-  }
+__device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const RTable<D> &R, float qscale, int tid) {
+  constexpr int NG = D / G, MI = D / 64, RT = GQ >= 4 ? GQ / 4 : 1;
+  static_assert(G == 64 || G == D, "channel groups of 64, or one group per token");
+  const int w = tid >> 6, lane = tid & 63;
+  contract_columns<D, GQ, W>(&pr.qT[0][0], R, w, lane, [&](int h, int c, float y) { pr.qs[h][c] = y * qscale; });
   __syncthreads();
   float *tail = (float *)(rec + RT * MI * 256);
-  {
-    // one wave per head: lane k holds channels k, k + 64 (if D = 128)
-    const int w = tid >> 6, lane = tid & 63;
-    for (int h = w; h < GQ; h += W) {
-      float v[D / 64], mx = 0.f;
+  // lane -> (k-quad r, limb row lam, register v) of the head's words
+  const int r = lane >> 4, lam = (lane >> 2) & 3, v = lane & 3;
+  const int mult = v == 1 ? 4 : (v == 2 ? 1 : 16);
+  for (int h = w; h < 4 * RT; h += W) { // heads >= GQ (when GQ < 4) get zero words
+    const bool live = h < GQ;
+    float x[MI], mx = 0.f; // lane holds channels lane + 64 k
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) {
-        v[k] = pr.qs[h][lane + 64 * k];
-        mx = fmaxf(mx, fabsf(v[k]));
+    for (int k = 0; k < MI; ++k) {
+      x[k] = live ? pr.qs[h][lane + 64 * k] : 0.f;
+      mx = fmaxf(mx, fabsf(x[k]));
+    }
+    mx = wave_max_dpp(mx);
+    if (G == 64) {
+#pragma unroll
+      for (int k = 0; k < MI; ++k) {
+        const float sum = wave_sum_dpp(x[k]);
+        if (live && lane == 0) tail[h * NG + k] = sum;
       }
-      mx = wave_max(mx);
-      if (G == 64) {
+    } else {
+      float a = 0.f;
 #pragma unroll
-        for (int k = 0; k < D / 64; ++k) {
-          const float sum = wave_sum(v[k]);
-          if (lane == 0) tail[h * NG + k] = sum;
+      for (int k = 0; k < MI; ++k) a += x[k];
+      a = wave_sum_dpp(a);
+      if (live && lane == 0) tail[h * NG] = a;
+    }
+    int ex = 0;
+    frexpf(mx, &ex);
+    const int E = mx > 0.f ? 18 - ex : 0;
+    if (live && lane == 0) tail[32 + h] = ldexpf(1.f, -(E + 4));
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      uint32_t word = 0;
+      if (live && lam < 3) {
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int X = (int)rintf(ldexpf(pr.qs[h][64 * mi + 16 * r + 4 * j4 + v], E)) * mult;
+          const int a0 = (int)(int8_t)(X & 0xff);
+          const int X1 = (X - a0) >> 8;
+          const int a1 = (int)(int8_t)(X1 & 0xff);
+          const int a2 = (X1 - a1) >> 8;
+          const int limb = lam == 0 ? a0 : (lam == 1 ? a1 : a2);
+          word |= ((uint32_t)limb & 0xffu) << (8 * j4);
         }
-      } else {
-        float a = 0.f;
-#pragma unroll
-        for (int k = 0; k < D / 64; ++k) a += v[k];
-        a = wave_sum(a);
-        if (lane == 0) tail[h * NG] = a;
       }
-      int ex = 0;
-      frexpf(mx, &ex);
-      const int E = mx > 0.f ? 18 - ex : 0;
-      if (lane == 0) {
-        pr.qexp[h] = E;
-        tail[32 + h] = ldexpf(1.f, -(E + 4));
-      }
+      rec[(((h >> 2) * MI + mi) * 64 + 16 * r + 4 * (h & 3) + lam) * 4 + v] = word;
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < RT * MI * 256; idx += NT) {
-    const int v = idx & 3, lane = (idx >> 2) & 63, mi = (idx >> 8) % MI, rt = (idx >> 8) / MI;
-    const int m = lane & 15, r = lane >> 4;
-    const int h = rt * 4 + (m >> 2), lam = m & 3;
-    const bool live = h < GQ && lam < 3;
-    uint32_t word = 0;
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const int c = 64 * mi + 16 * r + 4 * j4 + v;
-      int X = 0;
-      if (live) X = (int)rintf(ldexpf(pr.qs[h][c], pr.qexp[h])) * (v == 1 ? 4 : (v == 2 ? 1 : 16));
-      const int a0 = (int)(int8_t)(X & 0xff);
-      const int X1 = (X - a0) >> 8;
-      const int a1 = (int)(int8_t)(X1 & 0xff);
-      const int a2 = (X1 - a1) >> 8;
-      const int limb = lam == 0 ? a0 : (lam == 1 ? a1 : a2);
-      word |= ((uint32_t)limb & 0xffu) << (8 * j4);
-    }
-    rec[idx] = word;
   }
   __syncthreads();
 }
@@ -496,14 +557,14 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   const size_t hoff = (size_t)kv * p.block_bytes;
   const int pf = full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
 
-  // ---- prologue: R_K (direct to shared memory), the query rows and the
-  // first segment's page ids are staged; the block builds the query record;
-  // R_V^T (for the de-rotation at the end) replaces R_K while the pages
-  // stream; rows of P' that no head owns stay zero for the whole loop.
+  // ---- prologue: R_K (direct to shared memory; no such load may be
+  // outstanding in the page loop, where the compiler would order every
+  // shared-memory access after it), the query rows and the first segment's
+  // page ids are staged; the block builds the query record.
   stage_table<D>(sm.R, p.RK + (size_t)kv * D * D, w, W, lane);
   {
     const uint16_t *qrow = q + ((size_t)b.row[e] * p.Hq + kv * GQ) * D;
-    for (int idx = tid; idx < GQ * D; idx += NT) sm.u.pre.qraw[idx / D][idx % D] = bf16f(qrow[idx]);
+    for (int idx = tid; idx < GQ * D; idx += NT) sm.u.pre.qT[idx % D][idx / D] = bf16f(qrow[idx]);
   }
   for (int i = p0 + tid; i < min(pf, p0 + kIdCache); i += NT) sm.ids[i - p0] = ptab[i];
   if (tid == 0) sm.claim = (uint32_t)p0;
@@ -534,15 +595,14 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // The first WW waves take the pair's window (if this block holds it)
   // before joining the page stream; the other waves issue the loads of
   // their first pages before the query preparation, which then overlaps
-  // them.  The two kinds of wave run the same barriers (query_prep's and
-  // one more) on separate code paths, so the registers of the primed pages
-  // are not held across the window.
+  // them.  The two kinds of wave run the same barriers (query_prep's) on
+  // separate code paths, so the registers of the primed pages are not held
+  // across the window.  Each wave then zeroes its own P' rows (only this
+  // wave touches them; rows no head owns stay zero for the whole loop).
   auto finish_prologue = [&]() __attribute__((always_inline)) {
     query_prep<D, G, GQ, W>(sm.u.pre, sm.rec, sm.R, qscale, tid);
-    stage_table<D>(sm.R, p.RVt + (size_t)kv * D * D, w, W, lane);
-    _Float16 *P = &sm.u.P[0][0][0][0];
-    for (int idx = tid; idx < W * NG * 16 * kPRow; idx += NT) P[idx] = (_Float16)0.f;
-    __syncthreads();
+    u32x4 *P = (u32x4 *)&sm.u.P[w][0][0][0];
+    for (int idx = lane; idx < NG * 16 * kPRow / 8; idx += 64) P[idx] = u32x4{0u, 0u, 0u, 0u};
   };
   bool primed = false;
   if (!(with_window && w < WW)) {
@@ -760,14 +820,26 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     page_step(last, pf, false);
   }
 
-  // ---- epilogue: per-wave (m, l, acc) then the block merge
+  // ---- epilogue: per-wave (m, l, acc); each wave weights its accumulators
+  // by 2^(m_w - m) (m: the block maximum), the waves are summed, and the sum
+  // is de-rotated by R_V^T: the stored partial is in the basis of V itself.
+  // R_V^T replaces R_K in shared memory; its loads are issued here and
+  // written out just before the merge, their latency covered by the steps
+  // between.
+  constexpr int NF4 = D * D / 4, RVL = (NF4 + NT - 1) / NT;
+  u32x4 rvt[RVL];
+  {
+    const u32x4 *src = (const u32x4 *)(p.RVt + (size_t)kv * D * D);
+#pragma unroll
+    for (int i = 0; i < RVL; ++i) rvt[i] = src[min(tid + i * NT, NF4 - 1)];
+  }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int hrow = rt * 4 + r;
-    const float l = row16_sum(l_run[rt]);
+    const float l = lanes_sum<16>(l_run[rt]);
     float z[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) z[g] = row16_sum(zs[rt][g]);
+    for (int g = 0; g < NG; ++g) z[g] = lanes_sum<16>(zs[rt][g]);
     if (n == 0 && hrow < GQ) {
       sm.M[w][hrow] = m_run[rt];
       sm.L[w][hrow] = l;
@@ -776,50 +848,65 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     }
   }
   __syncthreads(); // every wave has left the loop: P' may be overwritten
-  const float unscale = ldexpf(1.f, 24 - p.pv_shift);
+  {
+    // heads 4 r + i of this lane's accumulator rows
+    float mb[4], mw[4];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
+    for (int i = 0; i < 4; ++i) mb[i] = mw[i] = -INFINITY;
+    for (int ww = 0; ww < W; ++ww) {
+      float mm[4];
+      if constexpr (GQ % 4 == 0) {
+        const float4 t = *(const float4 *)&sm.M[ww][4 * r];
+        mm[0] = t.x;
+        mm[1] = t.y;
+        mm[2] = t.z;
+        mm[3] = t.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mm[i] = 4 * r + i < GQ ? sm.M[ww][4 * r + i] : -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mb[i] = fmaxf(mb[i], mm[i]);
+        if (ww == w) mw[i] = mm[i];
+      }
+    }
+    const float unscale = ldexpf(1.f, 24 - p.pv_shift);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = 4 * r + i, c = 16 * j + n;
-      if (h < GQ) sm.u.A[w][h][c] = fmaf(acc[j][i], unscale, sm.zsum[w][h][c / G]);
-    }
-  __syncthreads();
-  // block merge of the waves (rotated basis), then de-rotation by R_V^T:
-  // the stored partial is in the basis of V itself
-  for (int idx = tid; idx < GQ * D; idx += NT) {
-    const int h = idx / D, c = idx % D;
-    float m = -INFINITY;
-    for (int ww = 0; ww < W; ++ww) m = fmaxf(m, sm.M[ww][h]);
-    float a = 0.f, l = 0.f;
-    for (int ww = 0; ww < W; ++ww) {
-      const float f = sm.M[ww][h] == -INFINITY ? 0.f : exp2f(sm.M[ww][h] - m);
-      a = fmaf(f, sm.u.A[ww][h][c], a);
-      l = fmaf(f, sm.L[ww][h], l);
-    }
-    sm.merged[h][c] = a;
-    if (c == 0) {
-      sm.mM[h] = m;
-      sm.mL[h] = l;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0); // the direct loads of R_V^T have landed
-  __syncthreads();
-  {
-    float *dst = ws_hist + (size_t)blk * GQ * (D + 2);
-    for (int idx = tid; idx < GQ * D; idx += NT) {
-      const int h = idx / D, c = idx % D;
-      float der = 0.f;
-#pragma unroll 16
-      for (int j = 0; j < D; ++j) der = fmaf(sm.merged[h][j], sm.R[j][c], der);
-      float *o = dst + (size_t)h * (D + 2);
-      o[c] = der;
-      if (c == 0) {
-        o[D] = sm.mM[h];
-        o[D + 1] = sm.mL[h];
+      const int h = 4 * r + i;
+      const float f = mw[i] == -INFINITY ? 0.f : exp2f(mw[i] - mb[i]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = 16 * j + n;
+        if (h < GQ) sm.u.A[w][h][c] = f * fmaf(acc[j][i], unscale, sm.zsum[w][h][c / G]);
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < RVL; ++i) {
+    const int f = tid + i * NT; // float4 f of the table: chunk f / 64
+    if (f < NF4) *(u32x4 *)&sm.R.c[f / 64][4 * (f % 64)] = rvt[i];
+  }
+  __syncthreads();
+  float *dst = ws_hist + (size_t)blk * GQ * (D + 2);
+  for (int idx = tid; idx < GQ * D; idx += NT) {
+    const int h = idx / D, j = idx % D;
+    float a = 0.f;
+    for (int ww = 0; ww < W; ++ww) a += sm.u.A[ww][h][j];
+    sm.mT[j][h] = a;
+  }
+  if (tid < GQ) {
+    float m = -INFINITY, l = 0.f;
+    for (int ww = 0; ww < W; ++ww) m = fmaxf(m, sm.M[ww][tid]);
+    for (int ww = 0; ww < W; ++ww)
+      if (sm.M[ww][tid] != -INFINITY) l = fmaf(exp2f(sm.M[ww][tid] - m), sm.L[ww][tid], l);
+    dst[(size_t)tid * (D + 2) + D] = m;
+    dst[(size_t)tid * (D + 2) + D + 1] = l;
+  }
+  __syncthreads();
+  contract_columns<D, GQ, W>(&sm.mT[0][0], sm.R, w, lane,
+                             [&](int h, int c, float y) { dst[(size_t)h * (D + 2) + c] = y; });
   // the window waves' results were written before the barriers above
   if (with_window) block_merge_store<D, GQ, WW>(sm.win.M, sm.win.L, sm.win.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2));
 }
