@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="0 skips the CPU baseline")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events (roofline fields become null)")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="events around one decode_main launch in this many, per layer pool "
+                         "(each timed launch adds a few microseconds to its step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -171,7 +174,7 @@ def main():
     torch.cuda.synchronize()
     if not args.no_kernel_timing:
         for p in pools:
-            p.profile_begin(args.steps)
+            p.profile_begin(args.steps, every=args.time_every)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -189,11 +192,14 @@ def main():
         n_main = sum(p.n_decode_main for p in profs)
         ms_main = sum(p.ms_decode_main for p in profs) / max(n_main, 1)
 
-    # algorithmic bytes of each timed decode launch (lengths after its append)
+    # algorithmic bytes of each timed decode launch (lengths after its append):
+    # the k-th decode of each layer pool in the timed region, k = 0, every, ...
     bytes_main = []
     for s in range(args.warmup, total_steps):
         a = s // args.layers
-        bytes_main.append(algorithmic_decode_bytes(w, [L + a + 1 for L in lengths0]))
+        k = sum(1 for t in range(args.warmup, s) if t % args.layers == s % args.layers)
+        if k % args.time_every == 0:
+            bytes_main.append(algorithmic_decode_bytes(w, [L + a + 1 for L in lengths0]))
     bytes_launch = float(np.mean(bytes_main))
     achieved = bytes_launch / (ms_main * 1e-3) / 1e9
     traffic = traffic_record(os.path.join(ROOT, "bit_kv_cache_segment_amd", "csrc", "kernels_decode.hip"),
@@ -223,6 +229,8 @@ def main():
                      "ms_per_launch": ms_main},
         "cpu_baseline": cpu,
         "detail": {"ms_decode_main": ms_main,
+                   "timed_decode_launches": None if args.no_kernel_timing else n_main,
+                   "time_every": args.time_every,
                    "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
                    "bits_per_element": (sum(max(0, L - 320) * (2 + 32 / w.group_size) + min(L, 320) * 16
                                             for L in lengths0) / sum(lengths0)),

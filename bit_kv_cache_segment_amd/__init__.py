@@ -94,7 +94,7 @@ def lib() -> ctypes.CDLL:
             "oscar_export_window": [_P, _I32, _P, _P, _P, _P, _P],
             "oscar_build_rotation": [_I32, _P, _P],
             "oscar_calibrate_clip": [_I32, ctypes.c_int64, _P, _P, ctypes.c_double, _P],
-            "oscar_profile_begin": [_P, _I32, ctypes.c_uint32],
+            "oscar_profile_begin": [_P, _I32, ctypes.c_uint32, _I32],
             "oscar_profile_end": [_P, _P],
         }
         for name, args in sig.items():
@@ -245,8 +245,8 @@ def oscar_calibrate_clip(x_bf16: np.ndarray, R: np.ndarray, pct: float = 99.0) -
 PROFILE_DECODE_MAIN, PROFILE_DECODE_MERGE, PROFILE_APPEND = 1, 2, 4
 
 
-def oscar_profile_begin(h, max_calls: int, kernels: int = PROFILE_DECODE_MAIN):
-    _check(lib().oscar_profile_begin(h, max_calls, kernels))
+def oscar_profile_begin(h, max_calls: int, kernels: int = PROFILE_DECODE_MAIN, every: int = 1):
+    _check(lib().oscar_profile_begin(h, max_calls, kernels, every))
 
 
 def oscar_profile_end(h) -> Profile:
@@ -332,8 +332,8 @@ class Pool:
         return oscar_export_history(self.handle, seq, first, count, c.num_kv_heads, c.head_dim,
                                     c.group_size, stream)
 
-    def profile_begin(self, max_calls, kernels=PROFILE_DECODE_MAIN):
-        oscar_profile_begin(self.handle, max_calls, kernels)
+    def profile_begin(self, max_calls, kernels=PROFILE_DECODE_MAIN, every=1):
+        oscar_profile_begin(self.handle, max_calls, kernels, every)
 
     def profile_end(self) -> Profile:
         return oscar_profile_end(self.handle)

@@ -109,13 +109,14 @@ int pages_for(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPage); }
 // Event pairs for per-kernel timing (oscar_profile_begin / _end).
 struct Profiler {
   bool on = false;
-  int cap = 0;
+  int cap = 0, every = 1;
   uint32_t mask = 0;
   std::vector<hipEvent_t> ev[3]; // decode main, decode merge, append: 2 per launch
   int used[3] = {0, 0, 0};
+  long calls[3] = {0, 0, 0};
   KernelTimer next(int kind) {
     KernelTimer t;
-    if (on && (mask >> kind & 1u) && used[kind] < cap) {
+    if (on && (mask >> kind & 1u) && calls[kind]++ % every == 0 && used[kind] < cap) {
       t.on = true;
       t.ev[0] = ev[kind][2 * used[kind]];
       t.ev[1] = ev[kind][2 * used[kind] + 1];
@@ -130,7 +131,9 @@ struct Profiler {
     }
     on = false;
     cap = 0;
+    every = 1;
     used[0] = used[1] = used[2] = 0;
+    calls[0] = calls[1] = calls[2] = 0;
   }
 };
 
@@ -568,11 +571,12 @@ int oscar_export_window(oscar_pool *p, int32_t seq, uint16_t *sink_k, uint16_t *
   return ok();
 }
 
-int oscar_profile_begin(oscar_pool *p, int32_t max_calls, uint32_t kernels) {
+int oscar_profile_begin(oscar_pool *p, int32_t max_calls, uint32_t kernels, int32_t every) {
   if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
   if (kernels == 0 || (kernels & ~7u)) return fail(OSCAR_EINVAL, "bad kernel mask 0x%x", kernels);
-  if (p->host_only) return fail(OSCAR_EINVAL, "profiling a host-only pool");
+  if (every < 1) return fail(OSCAR_EINVAL, "every = %d < 1", every);
   if (max_calls < 1 || max_calls > (1 << 16)) return fail(OSCAR_EINVAL, "max_calls %d outside [1, 65536]", max_calls);
+  if (p->host_only) return fail(OSCAR_EINVAL, "profiling a host-only pool");
   p->prof.release();
   for (auto &v : p->prof.ev) {
     v.resize(2 * (size_t)max_calls);
@@ -586,6 +590,7 @@ int oscar_profile_begin(oscar_pool *p, int32_t max_calls, uint32_t kernels) {
     }
   }
   p->prof.cap = max_calls;
+  p->prof.every = every;
   p->prof.mask = kernels;
   p->prof.on = true;
   return ok();

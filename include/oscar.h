@@ -210,11 +210,13 @@ int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R
 /* Kernel timing with HIP events recorded on the launch stream around the
  * kernels selected by `kernels` (OSCAR_PROFILE_* bits) in the pool's decode
  * and append calls.  oscar_profile_begin creates event pairs for up to
- * max_calls launches of each selected kernel (later launches go untimed);
- * oscar_profile_end waits for the events, writes the number of timed
- * launches and their summed durations (milliseconds), and releases the
- * events.  Each event record adds a few microseconds between launches, so
- * time only the kernels of interest.  Errors: EINVAL, EHIP. */
+ * max_calls timed launches of each selected kernel: launches 0, every,
+ * 2 every, ... of each kernel are timed (every >= 1), later ones and the
+ * rest go untimed.  oscar_profile_end waits for the events, writes the
+ * number of timed launches and their summed durations (milliseconds), and
+ * releases the events.  Each timed launch adds a few microseconds between
+ * launches, so time only the kernels of interest, or a sample of their
+ * launches.  Errors: EINVAL, EHIP. */
 typedef struct oscar_profile {
     int32_t n_decode_main;   float ms_decode_main;   /* query prep, INT2 history, BF16 window */
     int32_t n_decode_merge;  float ms_decode_merge;  /* merge of the partials                 */
@@ -225,7 +227,7 @@ typedef struct oscar_profile {
 #define OSCAR_PROFILE_DECODE_MERGE 2u  /* merge kernel                     */
 #define OSCAR_PROFILE_APPEND       4u  /* append / eviction kernel         */
 
-int oscar_profile_begin(oscar_pool *pool, int32_t max_calls, uint32_t kernels);
+int oscar_profile_begin(oscar_pool *pool, int32_t max_calls, uint32_t kernels, int32_t every);
 int oscar_profile_end(oscar_pool *pool, oscar_profile *out);
 
 const char *oscar_last_error(void);
