@@ -958,12 +958,15 @@ __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, c
   }
 }
 
-constexpr int kMergeThreads = 256;
+// One thread per (head, channel) output of the pair, so each thread does a
+// single round of loads.
+template <int D, int GQ>
+constexpr int merge_threads() { return GQ * D < 1024 ? GQ * D : 1024; }
 
 template <int D, int GQ>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
+__global__ __launch_bounds__((merge_threads<D, GQ>())) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
                                                                      const float *__restrict__ ws) {
-  merge_pair<D, GQ, kMergeThreads>(p, b, out, ws, blockIdx.x / p.Hkv, blockIdx.x % p.Hkv, threadIdx.x);
+  merge_pair<D, GQ, merge_threads<D, GQ>()>(p, b, out, ws, blockIdx.x / p.Hkv, blockIdx.x % p.Hkv, threadIdx.x);
 }
 
 template <int D, int G, int GQ>
@@ -1001,7 +1004,7 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
                         tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws);
   // A separate launch: merging in the last block of each pair needs
   // device-scope fences, which cost more than this kernel here.
-  hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(kMergeThreads), 0, s,
+  hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(merge_threads<D, GQ>()), 0, s,
                         tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, out, (const float *)ws);
   return hipGetLastError();
 }

@@ -32,21 +32,38 @@ __device__ __forceinline__ uint16_t f16_bits(float f) {
 }
 __device__ __forceinline__ float f16_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// Lane permutations inside each 16-lane row (DPP): swap neighbours, swap
+// pairs, mirror each half row, mirror the row.  Four of them reach every
+// lane of the row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <class Op>
+__device__ __forceinline__ uint32_t row16_reduce(uint32_t v, Op op) {
+  v = op(v, dpp_u<0xB1>(v));  // quad_perm [1,0,3,2]
+  v = op(v, dpp_u<0x4E>(v));  // quad_perm [2,3,0,1]
+  v = op(v, dpp_u<0x141>(v)); // row_half_mirror
+  return op(v, dpp_u<0x140>(v)); // row_mirror
+}
+__device__ __forceinline__ float lane_f(float v, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+__device__ __forceinline__ float fmin_u(uint32_t a, uint32_t b) { return fminf(__uint_as_float(a), __uint_as_float(b)); }
+__device__ __forceinline__ float fmax_u(uint32_t a, uint32_t b) { return fmaxf(__uint_as_float(a), __uint_as_float(b)); }
+// Minimum / maximum over the 64 lanes of the wave: rows by DPP, then the
+// four row results by readlane.  Exact in any order.
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = __uint_as_float(row16_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) { return __float_as_uint(fmin_u(a, b)); }));
+  return fminf(fminf(lane_f(v, 0), lane_f(v, 16)), fminf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = __uint_as_float(row16_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) { return __float_as_uint(fmax_u(a, b)); }));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 // OR of a value over the 16 lanes of an aligned lane group.
 __device__ __forceinline__ uint32_t or16(uint32_t v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
-  return v;
+  return row16_reduce(v, [](uint32_t a, uint32_t b) { return a | b; });
 }
 
 // Quantize this thread's clipped value y (channel j) of one token.  `red`
@@ -171,77 +188,60 @@ __global__ void prefill_window_kernel(PoolDev p, int seq, const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Append: grid (ceil(n / E), Hkv, K|V), block D.  Each block serves up to E
-// sequences of the batch; R's column stays in registers across them.
+// Append: grid (n, Hkv, K|V), block D: one sequence per block.  The loads a
+// token needs (its page id, the evicted element, column j of R) are issued
+// together before any of them is used.
 // ---------------------------------------------------------------------------
-template <int D, int G, int E>
+template <int D, int G>
 __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, const uint16_t *__restrict__ k_new,
                                                    const uint16_t *__restrict__ v_new) {
-  const int kv = blockIdx.y, kind = blockIdx.z, j = threadIdx.x, Hkv = p.Hkv;
-  const int e0 = blockIdx.x * E, e1 = min(b.n, e0 + E);
-  const uint16_t *src_new = kind ? v_new : k_new;
-  uint16_t *sink = kind ? p.sinkV : p.sinkK;
-  uint16_t *recent = kind ? p.recentV : p.recentK;
+  const int e = blockIdx.x, kv = blockIdx.y, kind = blockIdx.z, j = threadIdx.x, Hkv = p.Hkv;
+  const int seq = b.seq[e], L = b.len[e]; // length before the append
+  const uint16_t xnew = (kind ? v_new : k_new)[((size_t)e * Hkv + kv) * D + j];
+  if (L < kSink) {
+    (kind ? p.sinkV : p.sinkK)[(((size_t)seq * Hkv + kv) * kSink + L) * D + j] = xnew;
+    return;
+  }
+  const int slot = (L - kSink) % kRecent;
+  uint16_t *rs = (kind ? p.recentV : p.recentK) + (((size_t)seq * Hkv + kv) * kRecent + slot) * D;
+  if (L < kWindow) {
+    rs[j] = xnew;
+    return;
+  }
+  // evict the oldest recent token (held in this slot) into history n_hist
+  const int n_hist = L - kWindow, pg_idx = n_hist / kPage, t = n_hist % kPage;
+  const int page = t == 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + pg_idx];
+  const float xj = bf16f(rs[j]);
+  const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
+  float rc[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) rc[i] = R[i * D + j];
+  const float c = (kind ? p.clipV : p.clipK)[kv * D + j];
   __shared__ float xs[D];
   __shared__ float red[2 * (D / 64)];
-
-  bool any_evict = false;
-  for (int e = e0; e < e1; ++e) any_evict |= b.len[e] >= kWindow;
-  float rc[D];
-  float c = 0.0f;
-  if (any_evict) {
-    const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
+  xs[j] = xj;
+  rs[j] = xnew; // this thread read element j above; no other thread touches it
+  __syncthreads();
+  float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < D; ++i) rc[i] = R[i * D + j];
-    c = (kind ? p.clipV : p.clipK)[kv * D + j];
-  }
-  for (int e = e0; e < e1; ++e) {
-    const int seq = b.seq[e], L = b.len[e];
-    const uint16_t xnew = src_new[((size_t)e * Hkv + kv) * D + j];
-    if (L < kSink) {
-      sink[(((size_t)seq * Hkv + kv) * kSink + L) * D + j] = xnew;
-      continue;
-    }
-    const int slot = (L - kSink) % kRecent;
-    uint16_t *rs = recent + (((size_t)seq * Hkv + kv) * kRecent + slot) * D;
-    if (L < kWindow) {
-      rs[j] = xnew;
-      continue;
-    }
-    // evict the oldest recent token (held in this slot) into history n_hist
-    const int n_hist = L - kWindow;
-    xs[j] = bf16f(rs[j]);
-    rs[j] = xnew; // this thread read element j above; no other thread touches it
-    __syncthreads();
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < D; ++i) acc = fmaf(xs[i], rc[i], acc);
-    const float y = fminf(fmaxf(acc, -c), c);
-    uint16_t s16, z16;
-    const uint32_t code = quantize_channel<D, G>(y, red, s16, z16);
-    const int pg_idx = n_hist / kPage, t = n_hist % kPage;
-    int page;
-    if (t == 0) {
-      page = b.new_page[e];
-      if (kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
-    } else {
-      page = p.page_table[(size_t)seq * p.maxp + pg_idx];
-    }
-    uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
-    if (kind == 0) {
-      store_k_code<D>(blk, t, code);
-      store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
-    } else {
-      // a byte holds four tokens of channel j (those with equal k & 1 and
-      // k >> 3, k = t % 16); the first of them, k & 6 == 0, starts the byte
-      const int k = t % 16;
-      uint8_t *byte = blk + vcode_dword_off(D, t / 16, j) + vbit(k) / 8;
-      const int sh = vbit(k) % 8;
-      const uint32_t old = (k & 6) == 0 ? 0u : *byte;
-      *byte = (uint8_t)((old & ~(3u << sh)) | (code << sh));
-      store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
-    }
-    __syncthreads(); // xs is reused by the next sequence
+  for (int i = 0; i < D; ++i) acc = fmaf(xs[i], rc[i], acc);
+  const float y = fminf(fmaxf(acc, -c), c);
+  uint16_t s16, z16;
+  const uint32_t code = quantize_channel<D, G>(y, red, s16, z16);
+  if (t == 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
+  uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
+  if (kind == 0) {
+    store_k_code<D>(blk, t, code);
+    store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
+  } else {
+    // a byte holds four tokens of channel j (those with equal k & 1 and
+    // k >> 3, k = t % 16); the first of them, k & 6 == 0, starts the byte
+    const int k = t % 16;
+    uint8_t *byte = blk + vcode_dword_off(D, t / 16, j) + vbit(k) / 8;
+    const int sh = vbit(k) % 8;
+    const uint32_t old = (k & 6) == 0 ? 0u : *byte;
+    *byte = (uint8_t)((old & ~(3u << sh)) | (code << sh));
+    store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
   }
 }
 
@@ -263,9 +263,8 @@ hipError_t prefill_impl(const PoolDev &p, int seq, const uint16_t *k, const uint
 template <int D, int G>
 hipError_t append_impl(const PoolDev &p, const AppendBatch &b, const uint16_t *kn, const uint16_t *vn,
                        hipStream_t s, const KernelTimer &t) {
-  constexpr int E = 1; // one sequence per block: many short blocks beat long serial ones
   if (t.on) (void)hipEventRecord(t.ev[0], s);
-  hipLaunchKernelGGL((append_kernel<D, G, E>), dim3((b.n + E - 1) / E, p.Hkv, 2), dim3(D), 0, s, p, b, kn, vn);
+  hipLaunchKernelGGL((append_kernel<D, G>), dim3(b.n, p.Hkv, 2), dim3(D), 0, s, p, b, kn, vn);
   if (t.on) (void)hipEventRecord(t.ev[1], s);
   return hipGetLastError();
 }
