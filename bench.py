@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="0 skips the CPU baseline")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events (roofline fields become null)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="append and decode as two calls (three launches) instead of one fused step")
     ap.add_argument("--time-every", type=int, default=4,
                     help="events around one decode_main launch in this many, per layer pool "
                          "(each timed launch adds a few microseconds to its step)")
@@ -164,10 +166,15 @@ def main():
     torch.cuda.synchronize()
 
     def step(s):
+        # one serving step of a layer: append the new token, then attend
+        # (one fused call unless --separate-calls)
         layer = s % args.layers
         a = s // args.layers
-        pools[layer].append(ids, toks[a][0], toks[a][1])
-        pools[layer].decode(ids, qs[s], out)
+        if args.separate_calls:
+            pools[layer].append(ids, toks[a][0], toks[a][1])
+            pools[layer].decode(ids, qs[s], out)
+        else:
+            pools[layer].step(ids, toks[a][0], toks[a][1], qs[s], out)
 
     for s in range(args.warmup):
         step(s)
@@ -230,6 +237,8 @@ def main():
         "cpu_baseline": cpu,
         "detail": {"ms_decode_main": ms_main,
                    "timed_decode_launches": None if args.no_kernel_timing else n_main,
+                   "step_call": "oscar_append_evict + oscar_decode_attn" if args.separate_calls
+                   else "oscar_decode_step",
                    "time_every": args.time_every,
                    "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
                    "bits_per_element": (sum(max(0, L - 320) * (2 + 32 / w.group_size) + min(L, 320) * 16

@@ -30,7 +30,11 @@ inline int window_units(int d, int G) {
   return (int)std::lround(kWindowCost * kWindow * 4 * d / block_bytes_for(d, G));
 }
 
-inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vector<int> &len, int Hkv, int slots, int wu) {
+// fused: the launch also appends (len is the length after the append); a
+// pair whose append evicts into the history keeps its last page in its last
+// split, the block that does the append: S <= (np + wu) / (wu + 1).
+inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vector<int> &len, int Hkv, int slots, int wu,
+                        bool fused = false) {
   std::vector<int> np(b.n);
   int64_t total = 0, umax = 1;
   for (int e = 0; e < b.n; ++e) {
@@ -40,11 +44,14 @@ inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vecto
   }
   b.total_pages = (int32_t)total;
   b.win_units = wu;
+  b.fused = fused ? 1 : 0;
+  for (int e = 0; e < kMaxBatch; ++e) b.new_page[e] = -1;
   auto splits = [&](int e, int64_t P) {
     if (np[e] == 0) return 1; // window only
     const int64_t U = np[e] + wu;
     int64_t S = std::min<int64_t>(kMaxSplits, (U + P - 1) / P);
     if (wu > 0) S = std::min<int64_t>(S, U / wu);
+    if (fused && len[e] - 1 >= kWindow) S = std::min<int64_t>(S, U / (wu + 1));
     return (int)std::max<int64_t>(1, S);
   };
   auto blocks = [&](int64_t P) {

@@ -109,6 +109,21 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
+__device__ __forceinline__ float wave_min_dpp(float v) {
+  v = fminf(v, dpp_f<0xB1>(v));
+  v = fminf(v, dpp_f<0x4E>(v));
+  v = fminf(v, dpp_f<0x141>(v));
+  v = fminf(v, dpp_f<0x140>(v));
+  return fminf(fminf(lane_f(v, 0), lane_f(v, 16)), fminf(lane_f(v, 32), lane_f(v, 48)));
+}
+// OR over the 16 lanes of each DPP row.
+__device__ __forceinline__ uint32_t row16_or(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false);
+  return v | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false);
+}
+
 // 2^x by the hardware instruction (x = -inf gives 0; results below the
 // normal range flush to 0, which a softmax weight can afford).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -212,6 +227,10 @@ struct WinSmem {
   alignas(16) uint32_t q2[NW][GQ][D / 2]; // query rows as bf16 pairs, one copy per wave
   float M[NW][GQ], L[NW][GQ];
   float A[NW][GQ][D];
+  // fused step: the evicted K and V rows, and how many of the K / V appends
+  // have published their slot writes and their page writes
+  float app_x[2][D];
+  int app_slot_done, app_page_done;
 };
 
 // Waves of a history block that process the pair's window while the others
@@ -417,12 +436,154 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
   }
 }
 
+// ---------------------------------------------------------------------------
+// Append of a fused step, by waves 0 (K, kind 0) and 1 (V, kind 1) of the
+// block that holds the pair's window: the same eviction as the append
+// kernel.  The new token goes to its sink or recent slot; when the window is
+// full, the slot's old token is rotated (fixed-order fp32 FMA chain over
+// i = 0..d-1 from +0), clipped, quantized per group (fp16 scale and zero)
+// and packed into history index n_hist0 = L0 - 320 (L0: length before the
+// append).  The slot write is published (app_slot_done) before the
+// rotation, the page writes (app_page_done) after it, each with a
+// workgroup-scope release after the wave's stores have completed; readers
+// acquire the counter.  The old token is read, and the V code dwords
+// updated, at device scope (no L1 line of them is ever cached in the
+// block), so every later read of the slot or the page misses in L1.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float f16_val(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Bounded wait for a shared-memory counter (every wave reaches its end).
+__device__ __forceinline__ void wait_count(int *c, int target) {
+  for (int it = 0; it < (1 << 22); ++it) {
+    if (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+__device__ __forceinline__ void publish(int *c, int lane) {
+  __builtin_amdgcn_s_waitcnt(0); // this wave's stores and atomics have completed
+  if (lane == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+struct AppendIn {
+  const uint16_t *k, *v; // [n][Hkv][d] bf16 in batch row order
+};
+
+template <int D, int G, int GQ, int NW>
+__device__ void fused_append(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, const AppendIn &in,
+                             int e, int kv, int kind, int lane) {
+  constexpr int CPL = D / 64; // channels lane + 64 c of this lane
+  const int Hkv = p.Hkv, seq = b.seq[e], L0 = b.len[e] - 1;
+  const uint16_t *xn = (kind ? in.v : in.k) + ((size_t)b.row[e] * Hkv + kv) * D;
+  const bool evict = L0 >= kWindow;
+  {
+    // the slot: dword u of the row (channels 2u, 2u + 1) by lane u
+    uint32_t *row;
+    if (L0 < kSink) row = (uint32_t *)((kind ? p.sinkV : p.sinkK) + (((size_t)seq * Hkv + kv) * kSink + L0) * D);
+    else row = (uint32_t *)((kind ? p.recentV : p.recentK) + (((size_t)seq * Hkv + kv) * kRecent + (L0 - kSink) % kRecent) * D);
+    if (lane < D / 2) {
+      const uint32_t nw = ((const uint32_t *)xn)[lane];
+      if (evict) {
+        const uint32_t old = __hip_atomic_load(row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.app_x[kind][2 * lane] = __uint_as_float(old << 16);
+        sm.app_x[kind][2 * lane + 1] = __uint_as_float(old & 0xffff0000u);
+      }
+      row[lane] = nw;
+    }
+  }
+  publish(&sm.app_slot_done, lane);
+  if (evict) {
+    const int n_hist0 = L0 - kWindow, t = n_hist0 % kPage;
+    const int page = t == 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage];
+    const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
+    const float *clip = (kind ? p.clipV : p.clipK) + (size_t)kv * D;
+    float y[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) y[c] = 0.f;
+#pragma unroll 16
+    for (int i = 0; i < D; ++i) {
+      const float xi = sm.app_x[kind][i];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) y[c] = fmaf(xi, R[i * D + lane + 64 * c], y[c]);
+    }
+    uint32_t code[CPL];
+    uint16_t s16[CPL], z16[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float cl = clip[lane + 64 * c];
+      y[c] = fminf(fmaxf(y[c], -cl), cl);
+    }
+    // group minima / maxima: G = 64 -> group c; G = 128 -> every channel
+    float mn[CPL], mx[CPL];
+    if constexpr (G == 64) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        mn[c] = wave_min_dpp(y[c]);
+        mx[c] = wave_max_dpp(y[c]);
+      }
+    } else {
+      float a = y[0], bmax = y[0];
+#pragma unroll
+      for (int c = 1; c < CPL; ++c) {
+        a = fminf(a, y[c]);
+        bmax = fmaxf(bmax, y[c]);
+      }
+      a = wave_min_dpp(a);
+      bmax = wave_max_dpp(bmax);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        mn[c] = a;
+        mx[c] = bmax;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      // "+ 0.0f" stores an exactly zero range or minimum as +0
+      s16[c] = f16_bits(((mx[c] - mn[c]) + 0.0f) / 3.0f);
+      z16[c] = f16_bits(mn[c] + 0.0f);
+      const float sc = f16_val(s16[c]), ze = f16_val(z16[c]);
+      float qv = 0.0f;
+      if (sc != 0.0f) qv = fminf(fmaxf(rintf((y[c] - ze) / sc), 0.0f), 3.0f);
+      code[c] = (uint32_t)qv;
+    }
+    uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int j = lane + 64 * c, g = j / G;
+      if (kind == 0) {
+        // 16 lanes assemble the dword of channels 64 c + 16 r + k
+        const uint32_t dw = row16_or(code[c] << (2 * (lane & 15)));
+        if ((lane & 15) == 0) *(uint32_t *)(blk + kcode_dword_off(D, t, lane >> 4, c)) = dw;
+        if (j % G == 0) *(uint32_t *)(blk + kparam_off(D, G, t, g)) = (uint32_t)s16[c] | ((uint32_t)z16[c] << 16);
+      } else {
+        // token t's two bits in channel j's dword; the first token of a
+        // byte clears the byte, later ones their own two bits
+        const int k = t % 16, bit = vbit(k);
+        uint32_t *dw = (uint32_t *)(blk + vcode_dword_off(D, t / 16, j));
+        atomicAnd(dw, (k & 6) == 0 ? ~(0xffu << (8 * (bit / 8))) : ~(3u << bit));
+        atomicOr(dw, code[c] << bit);
+        if (j % G == 0) *(uint32_t *)(blk + vparam_off(D, G, t, g)) = (uint32_t)s16[c] | ((uint32_t)z16[c] << 16);
+      }
+    }
+    if (t == 0 && kind == 0 && kv == 0 && lane == 0) p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage] = page;
+  }
+  publish(&sm.app_page_done, lane);
+}
+
 // A block that holds only a pair's window: all its waves take part.
 template <int D, int G, int GQ>
 __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
-                             const uint16_t *q, float qscale, float *ws_win, int e, int kv) {
+                             const uint16_t *q, float qscale, float *ws_win, const AppendIn &in, int e, int kv) {
   constexpr int W = main_waves(D, G, GQ);
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (b.fused) {
+    // (a pair that evicts always holds its last page in this split, so
+    // here the append only writes the new token)
+    if (threadIdx.x == 0) sm.app_slot_done = sm.app_page_done = 0;
+    __syncthreads();
+    if (w < 2) fused_append<D, G, GQ, W>(sm, p, b, in, e, kv, w, threadIdx.x & 63);
+    wait_count(&sm.app_slot_done, 2);
+  }
   window_waves<D, G, GQ, W>(sm, p, b, q, qscale, e, kv, w);
   __syncthreads();
   block_merge_store<D, GQ, W>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2));
@@ -539,7 +700,7 @@ constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
 template <int D, int G, int GQ>
 __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
-                              float *ws_hist, float *ws_win, const uint16_t *q, float qscale,
+                              float *ws_hist, float *ws_win, const uint16_t *q, float qscale, const AppendIn &in,
                               int blk, int e, int kv, int p0, int p1, bool with_window) {
   constexpr int W = main_waves(D, G, GQ), NT = 64 * W, WW = win_waves(W, GQ);
   constexpr int NG = D / G;                // scale/zero groups per token
@@ -555,7 +716,11 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   const int32_t *ptab = p.page_table + (size_t)seq * p.maxp;
   const size_t hstride = (size_t)Hkv * p.block_bytes;
   const size_t hoff = (size_t)kv * p.block_bytes;
-  const int pf = full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
+  // In a fused step the block holding the window appends; when that
+  // evicts, the pair's last page (the plan keeps it in this split) is taken
+  // after the loop, once the append has written it.
+  const bool fused_evict = b.fused && with_window && b.len[e] - 1 >= kWindow;
+  const int pf = fused_evict ? np - 1 : full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
 
   // ---- prologue: R_K (direct to shared memory; no such load may be
   // outstanding in the page loop, where the compiler would order every
@@ -567,7 +732,10 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     for (int idx = tid; idx < GQ * D; idx += NT) sm.u.pre.qT[idx % D][idx / D] = bf16f(qrow[idx]);
   }
   for (int i = p0 + tid; i < min(pf, p0 + kIdCache); i += NT) sm.ids[i - p0] = ptab[i];
-  if (tid == 0) sm.claim = (uint32_t)p0;
+  if (tid == 0) {
+    sm.claim = (uint32_t)p0;
+    sm.win.app_slot_done = sm.win.app_page_done = 0;
+  }
   for (int idx = tid; idx < W * 16; idx += NT) sm.alpha[idx / 16][idx % 16] = 1.f;
   __builtin_amdgcn_s_waitcnt(0); // the direct loads of R_K have landed
   __syncthreads();
@@ -617,6 +785,10 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     finish_prologue();
   } else {
     finish_prologue();
+    if (b.fused) {
+      if (w < 2) fused_append<D, G, GQ, WW>(sm.win, p, b, in, e, kv, w, lane);
+      wait_count(&sm.win.app_slot_done, 2);
+    }
     window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
   }
   auto stage = [&](int s0, int sf) __attribute__((always_inline)) {
@@ -815,8 +987,16 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     }
   }
   if (pf < p1 && w == W - 1) {
+    int id;
+    if (fused_evict) {
+      wait_count(&sm.win.app_page_done, 2);
+      // the evicted token started this page: its id is not in the table yet
+      id = (n_hist - 1) % kPage == 0 ? b.new_page[e] : ptab[pf];
+    } else {
+      id = ptab[pf];
+    }
     PageRegs<D, G> last;
-    load_page<D, G>(last, p.pages + (size_t)ptab[pf] * hstride + hoff, n, r);
+    load_page<D, G>(last, p.pages + (size_t)id * hstride + hoff, n, r);
     page_step(last, pf, false);
   }
 
@@ -972,7 +1152,7 @@ __global__ __launch_bounds__((merge_threads<D, GQ>())) void decode_merge_kernel(
 template <int D, int G, int GQ>
 __global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
 void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
-                        float *__restrict__ ws) {
+                        float *__restrict__ ws, AppendIn in) {
   constexpr int W = main_waves(D, G, GQ);
   __shared__ MainSmem<D, G, GQ, W> sm;
   float *ws_win = ws;
@@ -985,9 +1165,9 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   int p0, p1;
   split_range(np, S, s, b.win_units, p0, p1);
   if (p0 < p1)
-    history_block<D, G, GQ>(sm.h, p, b, ws_hist, ws_win, q, qscale, blk, e, kv, p0, p1, s == S - 1);
+    history_block<D, G, GQ>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, blk, e, kv, p0, p1, s == S - 1);
   else if (s == S - 1) {
-    window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, e, kv);
+    window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, in, e, kv);
     // this split holds no pages: an empty history partial for the merge
     float *dst = ws_hist + (size_t)blk * GQ * (D + 2);
     for (int idx = threadIdx.x; idx < GQ * (D + 2); idx += 64 * W) dst[idx] = idx % (D + 2) == D ? -INFINITY : 0.f;
@@ -996,12 +1176,12 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
 
 template <int D, int G, int GQ>
 hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
-                       float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
+                       float *ws, AppendIn in, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
   const int blocks = b.hist_blocks;
   // Timed launches take their start/stop timestamps from the dispatch itself
   // (no extra packets between kernels).
   hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
-                        tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws);
+                        tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, in);
   // A separate launch: merging in the last block of each pair needs
   // device-scope fences, which cost more than this kernel here.
   hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(merge_threads<D, GQ>()), 0, s,
@@ -1011,13 +1191,13 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
 
 template <int D, int G>
 hipError_t decode_g(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale, float *ws,
-                    hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
+                    AppendIn in, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
   switch (p.Hq / p.Hkv) {
-  case 1: return decode_impl<D, G, 1>(p, b, q, out, scale, ws, s, tm, tg);
-  case 2: return decode_impl<D, G, 2>(p, b, q, out, scale, ws, s, tm, tg);
-  case 4: return decode_impl<D, G, 4>(p, b, q, out, scale, ws, s, tm, tg);
-  case 8: return decode_impl<D, G, 8>(p, b, q, out, scale, ws, s, tm, tg);
-  case 16: return decode_impl<D, G, 16>(p, b, q, out, scale, ws, s, tm, tg);
+  case 1: return decode_impl<D, G, 1>(p, b, q, out, scale, ws, in, s, tm, tg);
+  case 2: return decode_impl<D, G, 2>(p, b, q, out, scale, ws, in, s, tm, tg);
+  case 4: return decode_impl<D, G, 4>(p, b, q, out, scale, ws, in, s, tm, tg);
+  case 8: return decode_impl<D, G, 8>(p, b, q, out, scale, ws, in, s, tm, tg);
+  case 16: return decode_impl<D, G, 16>(p, b, q, out, scale, ws, in, s, tm, tg);
   }
   return hipErrorInvalidValue;
 }
@@ -1046,10 +1226,12 @@ int decode_main_blocks_per_cu(const PoolDev &p) {
 }
 
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
-                         float *ws, hipStream_t s, const KernelTimer &tm, const KernelTimer &tg) {
-  if (p.d == 128 && p.G == 128) return decode_g<128, 128>(p, b, q, out, scale, ws, s, tm, tg);
-  if (p.d == 128 && p.G == 64) return decode_g<128, 64>(p, b, q, out, scale, ws, s, tm, tg);
-  if (p.d == 64 && p.G == 64) return decode_g<64, 64>(p, b, q, out, scale, ws, s, tm, tg);
+                         float *ws, const uint16_t *k_new, const uint16_t *v_new, hipStream_t s, const KernelTimer &tm,
+                         const KernelTimer &tg) {
+  const AppendIn in{k_new, v_new};
+  if (p.d == 128 && p.G == 128) return decode_g<128, 128>(p, b, q, out, scale, ws, in, s, tm, tg);
+  if (p.d == 128 && p.G == 64) return decode_g<128, 64>(p, b, q, out, scale, ws, in, s, tm, tg);
+  if (p.d == 64 && p.G == 64) return decode_g<64, 64>(p, b, q, out, scale, ws, in, s, tm, tg);
   return hipErrorInvalidValue;
 }
 

@@ -344,13 +344,10 @@ int oscar_prefill(oscar_pool *p, int32_t seq, const uint16_t *k, const uint16_t 
   return ok();
 }
 
-int oscar_append_evict(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
-                       const uint16_t *v_new, void *stream) {
-  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
-  if (n < 0) return fail(OSCAR_EINVAL, "n = %d < 0", n);
-  if (n == 0) return ok();
-  if (!seq_ids) return fail(OSCAR_EINVAL, "seq_ids is NULL");
-  if (!p->host_only && (!k_new || !v_new)) return fail(OSCAR_EINVAL, "NULL k_new or v_new");
+// Checks of an append of one token to each of seq_ids[0..n) (n > 0): ids
+// valid and distinct, lengths below the limit, page-table room and free
+// pages for every eviction that starts a page.  Changes nothing.
+static int check_append(oscar_pool *p, const int32_t *seq_ids, int32_t n) {
   std::vector<int32_t> sorted(seq_ids, seq_ids + n);
   std::sort(sorted.begin(), sorted.end());
   for (int i = 0; i < n; ++i) {
@@ -374,6 +371,20 @@ int oscar_append_evict(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
   if (need > p->n_free())
     return fail(OSCAR_ENOMEM, "append needs %lld new pages, %lld free", (long long)need,
                 (long long)p->n_free());
+  return OSCAR_OK;
+}
+
+int oscar_append_evict(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
+                       const uint16_t *v_new, void *stream) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (n < 0) return fail(OSCAR_EINVAL, "n = %d < 0", n);
+  if (n == 0) return ok();
+  if (!seq_ids) return fail(OSCAR_EINVAL, "seq_ids is NULL");
+  if (!p->host_only && (!k_new || !v_new)) return fail(OSCAR_EINVAL, "NULL k_new or v_new");
+  {
+    int rc = check_append(p, seq_ids, n);
+    if (rc) return rc;
+  }
   // Build the launches, taking pages in seq_ids order.
   size_t head0 = p->free_head;
   std::vector<AppendBatch> batches;
@@ -452,9 +463,80 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     KernelTimer tm = p->prof.next(0), tg = p->prof.next(1);
     hipError_t e = launch_decode(p->dev, batches[i], q + i * (size_t)kMaxBatch * Hq * d,
                                  out + i * (size_t)kMaxBatch * Hq * d, softmax_scale,
-                                 (float *)workspace, (hipStream_t)stream, tm, tg);
+                                 (float *)workspace, nullptr, nullptr, (hipStream_t)stream, tm, tg);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
+  return ok();
+}
+
+int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
+                      const uint16_t *v_new, const uint16_t *q, float *out, float softmax_scale,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (p->host_only) return fail(OSCAR_EINVAL, "decode step on a host-only pool");
+  if (n < 0) return fail(OSCAR_EINVAL, "n = %d < 0", n);
+  if (n == 0) return ok();
+  if (!seq_ids || !k_new || !v_new || !q || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
+  if (!std::isfinite(softmax_scale)) return fail(OSCAR_EINVAL, "softmax_scale is not finite");
+  {
+    int rc = check_append(p, seq_ids, n);
+    if (rc) return rc;
+  }
+  const int Hq = p->cfg.num_q_heads, Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim;
+  const int g = Hq / Hkv;
+  // plan on the lengths after the append, then check the workspace: nothing
+  // has changed yet
+  std::vector<DecodeBatch> batches;
+  size_t need = 0;
+  for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
+    DecodeBatch b;
+    b.n = std::min(kMaxBatch, n - i0);
+    std::vector<int> len(b.n);
+    for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
+    plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size), true);
+    need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
+    batches.push_back(b);
+  }
+  if (workspace_bytes < need)
+    return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  // the append's pages, taken in seq_ids order, then placed in launch order
+  const size_t head0 = p->free_head;
+  std::vector<int32_t> taken(n, -1);
+  for (int i = 0; i < n; ++i) {
+    const int32_t L = p->len[seq_ids[i]];
+    if (L >= kWindow && (L - kWindow) % kPage == 0) taken[i] = p->pop();
+  }
+  for (size_t i = 0; i < batches.size(); ++i) {
+    DecodeBatch &b = batches[i];
+    for (int e = 0; e < b.n; ++e) b.new_page[e] = taken[i * kMaxBatch + b.row[e]];
+  }
+  for (size_t i = 0; i < batches.size(); ++i) {
+    const size_t r0 = i * (size_t)kMaxBatch;
+    KernelTimer tm = p->prof.next(0), tg = p->prof.next(1);
+    hipError_t e = launch_decode(p->dev, batches[i], q + r0 * Hq * d, out + r0 * Hq * d, softmax_scale,
+                                 (float *)workspace, k_new + r0 * Hkv * d, v_new + r0 * Hkv * d,
+                                 (hipStream_t)stream, tm, tg);
+    if (e != hipSuccess) {
+      if (i == 0) {
+        p->free_head = head0; // nothing was enqueued
+        return hip_fail(e, "decode step launch");
+      }
+      // earlier launches are in flight: keep their effect in the mirror
+      for (size_t j = 0; j < i * (size_t)kMaxBatch; ++j) {
+        if (taken[j] >= 0) p->table[seq_ids[j]].push_back(taken[j]);
+        p->len[seq_ids[j]] += 1;
+      }
+      p->free_head = head0;
+      for (size_t j = 0; j < i * (size_t)kMaxBatch; ++j)
+        if (taken[j] >= 0) ++p->free_head;
+      return hip_fail(e, "decode step launch");
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    if (taken[i] >= 0) p->table[seq_ids[i]].push_back(taken[i]);
+    p->len[seq_ids[i]] += 1;
+  }
+  p->compact();
   return ok();
 }
 

@@ -109,6 +109,11 @@ struct DecodeBatch {
   uint16_t row[kMaxBatch];           // its row in q and out
   uint8_t nsplit[kMaxBatch];         // blocks per pair, 1 .. kMaxSplits
   int32_t layer_prefix[kMaxSplits + 1];
+  // Fused step (oscar_decode_step): the launch first appends one token per
+  // sequence (len is the length after it).  new_page: the page the append
+  // takes for the evicted token, or -1 (launch order).
+  int32_t fused;
+  int32_t new_page[kMaxBatch];
 };
 
 // History pages [p0, p1) of split s of S of a pair with np pages: the pair's
@@ -159,9 +164,10 @@ hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t 
 // Resident decode_main blocks per compute unit for this pool's shape.
 int decode_main_blocks_per_cu(const PoolDev &p);
 
+// k_new, v_new: the appended tokens of a fused step (b.fused), else null.
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out,
-                         float scale, float *ws, hipStream_t s, const KernelTimer &t_main,
-                         const KernelTimer &t_merge);
+                         float scale, float *ws, const uint16_t *k_new, const uint16_t *v_new, hipStream_t s,
+                         const KernelTimer &t_main, const KernelTimer &t_merge);
 
 
 // Workspace (4-byte words) of one decode launch: window partials and split

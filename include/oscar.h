@@ -158,6 +158,26 @@ int oscar_decode_attn(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
                       const uint16_t *q, float *out, float softmax_scale,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* One decode step in one call: the append of oscar_append_evict(seq_ids,
+ * k_new, v_new) followed by the attention of oscar_decode_attn(seq_ids, q,
+ * out), the serving loop's per-token pair ([N-pipeline]: the newest token
+ * enters the recent window, the oldest recent token moves into the INT2
+ * history, then the query attends over all three segments).  The pool ends
+ * in the same state bit for bit as after the two calls (same pages taken,
+ * in seq_ids order), and out holds the same attention within the kernels'
+ * rounding.  The append runs inside the decode launch: the block of each
+ * (sequence, kv head) that holds its window also writes the new token and
+ * packs the evicted one, ahead of reading them.
+ *   seq_ids: host int32 [n], distinct;  k_new, v_new: device bf16 [n][Hkv][d];
+ *   q: device bf16 [n][Hq][d];  out: device fp32 [n][Hq][d];
+ *   workspace: device, >= oscar_decode_workspace_bytes(cfg, n) bytes.
+ * Errors: every error of the two calls, reported before anything changes
+ * (EINVAL, ENOMEM, ERANGE), and EHIP. */
+int oscar_decode_step(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
+                      const uint16_t *k_new, const uint16_t *v_new,
+                      const uint16_t *q, float *out, float softmax_scale,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Return a sequence's pages to the back of the free list (in page-table
  * order) and set its length to 0.  Host only.  Errors: EINVAL. */
 int oscar_release_seq(oscar_pool *pool, int32_t seq);

@@ -1,9 +1,10 @@
 // Host-side check of the decode plan (decode_plan.h, oscar_internal.h): for
 // random batches, the blocks of a launch cover every pair's history pages
 // exactly once and its window exactly once, every index a decode block
-// derives from its split stays inside the pair, the merge side sees the same
-// splits, and the launch order is a permutation of the batch.  Exits
-// non-zero on the first violation.
+// derives from its split stays inside the pair, a fused step's evicting
+// pair keeps its last page in the split that holds its window (the block
+// that appends), the merge side sees the same splits, and the launch order
+// is a permutation of the batch.  Exits non-zero on the first violation.
 #include "decode_plan.h"
 
 #include <cstdio>
@@ -37,7 +38,8 @@ int main(int argc, char **argv) {
     }
     const int slots = 1 + (int)(rng() % 1024);
     const int d = rng() % 2 ? 128 : 64, G = (d == 128 && rng() % 2) ? 128 : 64;
-    plan_splits(b, ids.data(), len, Hkv, slots, window_units(d, G));
+    const bool fused = rng() % 2;
+    plan_splits(b, ids.data(), len, Hkv, slots, window_units(d, G), fused);
     std::vector<int> seen_row(b.n, 0);
     for (int e = 0; e < b.n; ++e) {
       if (b.row[e] >= b.n || b.seq[e] != ids[b.row[e]] || b.len[e] != len[b.row[e]])
@@ -68,6 +70,10 @@ int main(int argc, char **argv) {
       if (pf < p1 && (pf != np - 1 || n_hist % kPage == 0)) return fail("partial page is not the last", it);
       for (int q = p0; q < p1; ++q) pages[e * Hkv + kv][q]++;
       if (s == S - 1) windows[e * Hkv + kv][0]++;
+      // a fused step's evicting pair keeps its last page in the split that
+      // holds the window (the block that appends)
+      if (fused && s == S - 1 && b.len[e] - 1 >= kWindow && !(p0 <= np - 1 && np - 1 < p1))
+        return fail("fused step: last page outside the window's split", it);
     }
     for (int i = 0; i < b.n * Hkv; ++i) {
       if (windows[i][0] != 1) return fail("window not held by exactly one block", it);

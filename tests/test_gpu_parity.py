@@ -105,6 +105,49 @@ def test_edge_lengths_prefill_then_fused_steps(shape):
         check_windows(pool, w, b, L, k, v, range(w.num_kv_heads))
 
 
+@pytest.mark.parametrize("shape", ["g4_d128_G128", "g8_d128_G64", "g1_d64_G64", "g16_d128_G128"])
+def test_fused_steps_match_oracle_and_separate_calls(shape):
+    # oscar_decode_step (append + decode in one launch) over the edge
+    # lengths: every step checked against the oracle, and the pool state
+    # (lengths, page tables, codes, windows) bit for bit equal to a pool
+    # driven by separate append and decode calls.
+    w = _workload(shape)
+    lengths = list(EDGE_LENS)
+    steps = 70
+    pools = []
+    for _ in range(2):
+        pool, cfg = _pool(w, lengths, extra=steps, slack=3)
+        harness.prefill_all(pool, w, lengths)
+        pools.append(pool)
+    fused, separate = pools
+    m = _model(cfg)
+    for b, L in enumerate(lengths):
+        m.prefill(b, L)
+    rng = np.random.default_rng(11)
+    for step in range(1, steps + 1):
+        order = [int(x) for x in rng.permutation(len(lengths))]
+        k_new, v_new = harness.step_tokens(w, lengths, order)
+        q = synth.queries(w, step, device="cuda", batch=len(lengths))
+        qo = q[torch.as_tensor(order, device="cuda")].contiguous().view(torch.uint16)
+        out = fused.step(order, k_new, v_new, qo)
+        separate.append(order, k_new, v_new)
+        m.append(order)
+        for b in order:
+            lengths[b] += 1
+        if step % 7 == 0 or step <= 3:
+            torch.cuda.synchronize()
+            inv = np.argsort(order)
+            _check_all_rows(w, out[torch.as_tensor(inv, device="cuda")], lengths, step)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lengths):
+        assert fused.length(b) == L == separate.length(b)
+        assert list(fused.page_table(b)) == m.table[b] == list(separate.page_table(b))
+        st, k, v = oracle_sequence(w, b, L)
+        check_history_codes(fused, w, b, st, range(w.num_kv_heads))
+        check_windows(fused, w, b, L, k, v, range(w.num_kv_heads))
+    assert fused.free_pages() == separate.free_pages()
+
+
 def test_shuffle_invariance_and_determinism():
     # Deterministic pools: bitwise equal results from call to call and for
     # any placement of the pages in the pool.

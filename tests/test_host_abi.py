@@ -99,6 +99,9 @@ def test_errors_leave_state_unchanged():
     ids = np.zeros(1, dtype=np.int32)
     rc = ok.lib().oscar_decode_attn(p.handle, ok._np_ptr(ids), 1, None, None, 1.0, None, 0, None)
     assert rc == ok.EINVAL and "host-only" in ok.lib().oscar_last_error().decode()
+    rc = ok.lib().oscar_decode_step(p.handle, ok._np_ptr(ids), 1, None, None, None, None, 1.0, None, 0, None)
+    assert rc == ok.EINVAL and "host-only" in ok.lib().oscar_last_error().decode()
+    assert _state(p, 6) == before
     # profiling: argument checks come before the host-only check
     for args, msg in [((4, 0, 1), "mask"), ((4, 8, 1), "mask"), ((4, 1, 0), "every"), ((0, 1, 1), "max_calls"),
                       ((4, 1, 2), "host-only")]:
