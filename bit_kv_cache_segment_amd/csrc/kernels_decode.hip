@@ -469,10 +469,11 @@ struct AppendIn {
   const uint16_t *k, *v; // [n][Hkv][d] bf16 in batch row order
 };
 
-template <int D, int G, int GQ, int NW>
-__device__ void fused_append(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, const AppendIn &in,
-                             int e, int kv, int kind, int lane) {
-  constexpr int CPL = D / 64; // channels lane + 64 c of this lane
+// First part: the slot (the old token kept in shared memory when it is
+// evicted), published; the window reads the slot after this.
+template <int D, int GQ, int NW>
+__device__ void fused_append_slot(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, const AppendIn &in,
+                                  int e, int kv, int kind, int lane) {
   const int Hkv = p.Hkv, seq = b.seq[e], L0 = b.len[e] - 1;
   const uint16_t *xn = (kind ? in.v : in.k) + ((size_t)b.row[e] * Hkv + kv) * D;
   const bool evict = L0 >= kWindow;
@@ -492,7 +493,18 @@ __device__ void fused_append(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
     }
   }
   publish(&sm.app_slot_done, lane);
-  if (evict) {
+}
+
+// Second part: the evicted token into the history, published; only the
+// pass over the pair's last page, after the page loop, reads it, so this
+// runs after the wave's share of the window.
+template <int D, int G, int GQ, int NW>
+__device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, int e, int kv,
+                                  int kind, int lane) {
+  constexpr int CPL = D / 64; // channels lane + 64 c of this lane
+  const int Hkv = p.Hkv, seq = b.seq[e], L0 = b.len[e] - 1;
+  if (L0 >= kWindow) {
+    wave_sync(); // this wave's writes of the old token to shared memory
     const int n_hist0 = L0 - kWindow, t = n_hist0 % kPage;
     const int page = t == 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage];
     const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
@@ -581,7 +593,7 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
     // here the append only writes the new token)
     if (threadIdx.x == 0) sm.app_slot_done = sm.app_page_done = 0;
     __syncthreads();
-    if (w < 2) fused_append<D, G, GQ, W>(sm, p, b, in, e, kv, w, threadIdx.x & 63);
+    if (w < 2) fused_append_slot<D, GQ, W>(sm, p, b, in, e, kv, w, threadIdx.x & 63);
     wait_count(&sm.app_slot_done, 2);
   }
   window_waves<D, G, GQ, W>(sm, p, b, q, qscale, e, kv, w);
@@ -786,10 +798,11 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   } else {
     finish_prologue();
     if (b.fused) {
-      if (w < 2) fused_append<D, G, GQ, WW>(sm.win, p, b, in, e, kv, w, lane);
+      if (w < 2) fused_append_slot<D, GQ, WW>(sm.win, p, b, in, e, kv, w, lane);
       wait_count(&sm.win.app_slot_done, 2);
     }
     window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
+    if (b.fused && w < 2) fused_append_page<D, G, GQ, WW>(sm.win, p, b, e, kv, w, lane);
   }
   auto stage = [&](int s0, int sf) __attribute__((always_inline)) {
     for (int i = s0 + tid; i < sf; i += NT) sm.ids[i - s0] = ptab[i];

@@ -485,20 +485,35 @@ int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   const int Hq = p->cfg.num_q_heads, Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim;
   const int g = Hq / Hkv;
   // plan on the lengths after the append, then check the workspace: nothing
-  // has changed yet
+  // has changed yet.  The append runs inside the decode launch when every
+  // block of it is resident at once; a launch that needs several rounds of
+  // blocks would wait on the appending blocks round after round, so then
+  // the append is its own launch (same results).
   std::vector<DecodeBatch> batches;
   size_t need = 0;
-  for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
-    DecodeBatch b;
-    b.n = std::min(kMaxBatch, n - i0);
-    std::vector<int> len(b.n);
-    for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
-    plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size), true);
-    need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
-    batches.push_back(b);
+  bool fused = true;
+  for (int pass = 0; pass < 2; ++pass) {
+    batches.clear();
+    need = 0;
+    for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
+      DecodeBatch b;
+      b.n = std::min(kMaxBatch, n - i0);
+      std::vector<int> len(b.n);
+      for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
+      plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size), fused);
+      need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
+      if (b.hist_blocks > p->decode_slots) fused = false;
+      batches.push_back(b);
+    }
+    if (fused || pass == 1) break;
   }
   if (workspace_bytes < need)
     return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  if (!fused) {
+    int rc = oscar_append_evict(p, seq_ids, n, k_new, v_new, stream);
+    if (rc) return rc;
+    return oscar_decode_attn(p, seq_ids, n, q, out, softmax_scale, workspace, workspace_bytes, stream);
+  }
   // the append's pages, taken in seq_ids order, then placed in launch order
   const size_t head0 = p->free_head;
   std::vector<int32_t> taken(n, -1);
