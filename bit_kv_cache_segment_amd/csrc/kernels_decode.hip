@@ -713,7 +713,7 @@ constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 template <int D, int G, int GQ>
 __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
                               float *ws_hist, float *ws_win, const uint16_t *q, float qscale, const AppendIn &in,
-                              int blk, int e, int kv, int p0, int p1, bool with_window) {
+                              int slot, int e, int kv, int p0, int p1, bool with_window) {
   constexpr int W = main_waves(D, G, GQ), NT = 64 * W, WW = win_waves(W, GQ);
   constexpr int NG = D / G;                // scale/zero groups per token
   constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
@@ -822,7 +822,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     const int hs = min(rt * 4 + r, GQ - 1); // head of this lane in the logit layout
     kfac[rt] = tail[32 + hs];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) qsum[rt][g] = tail[hs * NG + g];
+    for (int g = 0; g < NG; ++g) qsum[rt][g] = tail[hs * NG + g] / kfac[rt]; // exact: kfac = 2^-k
   }
 
   // per-token factor of P': 2^pv_shift * 4^-e(k), k = token within its
@@ -881,7 +881,9 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
             const float dv = (float)(int)((uint32_t)cacc[rt][g][0] + ((uint32_t)cacc[rt][g][1] << 8) +
                                           ((uint32_t)cacc[rt][g][2] << 16));
             const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
-            l = fmaf(f16lo(sz), kfac[rt] * dv, fmaf(f16hi(sz), qsum[rt][g], l));
+            // the logit in units of kfac (a power of two; the softmax below
+            // applies it), so the products are those of kfac * logit exactly
+            l = fmaf(f16lo(sz), dv, fmaf(f16hi(sz), qsum[rt][g], l));
           }
           lg[rt][T] = (tvalid && (GQ >= 4 || rt * 4 + r < GQ)) ? l : -INFINITY;
         }
@@ -892,7 +894,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       for (int rt = 0; rt < RT; ++rt) {
         const int hrow = rt * 4 + r;
         float mt = fmaxf(fmaxf(lg[rt][0], lg[rt][1]), fmaxf(lg[rt][2], lg[rt][3]));
-        mt = row16_max_dpp(mt);
+        mt = row16_max_dpp(mt) * kfac[rt];
         // The running reference moves only when a page's maximum exceeds it
         // by more than kLazy: weights stay <= 2^kLazy and the PV accumulators
         // are rescaled rarely.
@@ -908,13 +910,15 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   #pragma unroll
         for (int T = 0; T < 4; ++T) {
           const bool ok = (full && GQ >= 4) || lg[rt][T] != -INFINITY;
-          const float pt = ok ? fast_exp2(lg[rt][T] - mnew) : 0.f;
+          const float pt = ok ? fast_exp2(fmaf(lg[rt][T], kfac[rt], -mnew)) : 0.f;
           psum += pt;
   #pragma unroll
           for (int g = 0; g < NG; ++g) {
             const uint32_t sz = cur.vp[(T * NG + g) / 4][(T * NG + g) % 4];
             zadd[g] = ok ? fmaf(pt, f16hi(sz), zadd[g]) : zadd[g];
-            pv[g][T] = ok ? f16lo(sz) * (pt * pfac[T]) : 0.f;
+            // (an fma with a zero addend: one mixed-precision instruction,
+            // the same single rounding as the product)
+            pv[g][T] = ok ? fmaf(f16lo(sz), pt * pfac[T], 0.f) : 0.f;
           }
         }
         l_run[rt] = fmaf(l_run[rt], alpha, psum);
@@ -1082,7 +1086,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     if (f < NF4) *(u32x4 *)&sm.R.c[f / 64][4 * (f % 64)] = rvt[i];
   }
   __syncthreads();
-  float *dst = ws_hist + (size_t)blk * GQ * (D + 2);
+  float *dst = ws_hist + (size_t)slot * GQ * (D + 2);
   for (int idx = tid; idx < GQ * D; idx += NT) {
     const int h = idx / D, j = idx % D;
     float a = 0.f;
@@ -1107,31 +1111,36 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
 
 // Merge of one (sequence, kv head): the split partials (already in the
 // basis of V; a split without pages holds m = -inf) and the window partial
-// -> out = acc / l.  Splits are read four at a time with every load of a
-// batch issued before any use; one thread per (head, channel) output.
+// -> out = acc / l.  The pair's split partials sit in consecutive slots
+// (stride: the batch's largest split count), so the first SB of them are
+// read together with the window partial, before the pair's own split count
+// is known; slots at or past it are read (in bounds) but never used.  One
+// thread per (head, channel) output.
 template <int D, int GQ, int NT>
 __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, int e, int kv,
                            int tid) {
-  constexpr int SB = 4; // splits per batch
+  constexpr int SB = 4; // splits per batch of loads
   const int Hkv = p.Hkv, Hq = p.Hq;
   const float *ws_win = ws;
-  const float *ws_hist = ws + (size_t)b.n * Hq * (D + 2);
+  const int smax = b.nsplit[0]; // launch order is by split count, descending
+  const float *ws_pair = ws + (size_t)b.n * Hq * (D + 2) + (size_t)(e * Hkv + kv) * smax * GQ * (D + 2);
   const int S = b.nsplit[e];
+  float *out_pair = out + ((size_t)b.row[e] * Hq + kv * GQ) * D;
   for (int idx = tid; idx < GQ * D; idx += NT) {
     const int h = idx / D, c = idx % D;
     const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
     float m = win[D], l = win[D + 1], a = win[c];
-    for (int s0 = 0; s0 < S; s0 += SB) {
-      float hm[SB], hl[SB], ha[SB];
+    float hm[SB], hl[SB], ha[SB];
+    auto fetch = [&](int s0) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < SB; ++j) {
-        // split s of this pair wrote its partial at block layer_prefix[s] + e Hkv + kv
-        const int ss = min(s0 + j, S - 1);
-        const float *ph = ws_hist + ((size_t)(b.layer_prefix[ss] + e * Hkv + kv) * GQ + h) * (D + 2);
+        const float *ph = ws_pair + ((size_t)min(s0 + j, smax - 1) * GQ + h) * (D + 2);
         hm[j] = ph[D];
         hl[j] = ph[D + 1];
         ha[j] = ph[c];
       }
+    };
+    auto fold = [&](int s0) __attribute__((always_inline)) {
       float mm = m;
 #pragma unroll
       for (int j = 0; j < SB; ++j)
@@ -1141,13 +1150,21 @@ __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, c
       a *= f0;
 #pragma unroll
       for (int j = 0; j < SB; ++j) {
-        const float f = (s0 + j < S && hm[j] != -INFINITY) ? exp2f(hm[j] - mm) : 0.f;
-        l = fmaf(f, hl[j], l);
-        a = fmaf(f, ha[j], a);
+        // selects, not branches: slots past S hold stale words
+        const bool use = s0 + j < S && hm[j] != -INFINITY;
+        const float f = exp2f(hm[j] - mm);
+        l = use ? fmaf(f, hl[j], l) : l;
+        a = use ? fmaf(f, ha[j], a) : a;
       }
       m = mm;
+    };
+    fetch(0); // every pair has a split
+    fold(0);
+    for (int s0 = SB; s0 < S; s0 += SB) {
+      fetch(s0);
+      fold(s0);
     }
-    out[((size_t)b.row[e] * Hq + kv * GQ + h) * D + c] = a / l;
+    out_pair[idx] = a / l;
   }
 }
 
@@ -1177,12 +1194,15 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
   int p0, p1;
   split_range(np, S, s, b.win_units, p0, p1);
+  // split partial slot: the pair's splits are consecutive, stride the
+  // batch's largest split count (launch order is by split count, descending)
+  const int slot = (e * Hkv + kv) * b.nsplit[0] + s;
   if (p0 < p1)
-    history_block<D, G, GQ>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, blk, e, kv, p0, p1, s == S - 1);
+    history_block<D, G, GQ>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
   else if (s == S - 1) {
     window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, in, e, kv);
     // this split holds no pages: an empty history partial for the merge
-    float *dst = ws_hist + (size_t)blk * GQ * (D + 2);
+    float *dst = ws_hist + (size_t)slot * GQ * (D + 2);
     for (int idx = threadIdx.x; idx < GQ * (D + 2); idx += 64 * W) dst[idx] = idx % (D + 2) == D ? -INFINITY : 0.f;
   }
 }

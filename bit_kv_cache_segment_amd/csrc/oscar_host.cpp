@@ -178,8 +178,7 @@ int oscar_decode_workspace_bytes(const oscar_pool_config *cfg, int32_t max_batch
   if (!bytes || max_batch < 0) return fail(OSCAR_EINVAL, "bad arguments");
   int n = std::min(max_batch, kMaxBatch);
   int g = cfg->num_q_heads / cfg->num_kv_heads;
-  long hist_blocks = (long)n * cfg->num_kv_heads * kMaxSplits;
-  *bytes = decode_ws_floats(cfg->num_q_heads, cfg->head_dim, n, hist_blocks, g) * sizeof(float);
+  *bytes = decode_ws_floats(cfg->num_q_heads, cfg->head_dim, n, cfg->num_kv_heads, kMaxSplits, g) * sizeof(float);
   return ok();
 }
 
@@ -454,7 +453,7 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     std::vector<int> len(b.n);
     for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]];
     plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size));
-    need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
+    need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
     batches.push_back(b);
   }
   if (workspace_bytes < need)
@@ -501,7 +500,7 @@ int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
       std::vector<int> len(b.n);
       for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
       plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size), fused);
-      need = std::max(need, decode_ws_floats(Hq, d, b.n, b.hist_blocks, g) * sizeof(float));
+      need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
       if (b.hist_blocks > p->decode_slots) fused = false;
       batches.push_back(b);
     }

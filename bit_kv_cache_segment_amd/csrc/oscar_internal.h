@@ -170,10 +170,11 @@ hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t 
                          const KernelTimer &t_main, const KernelTimer &t_merge);
 
 
-// Workspace (4-byte words) of one decode launch: window partials and split
-// partials.
-inline size_t decode_ws_floats(int Hq, int d, int n, long hist_blocks, int g) {
-  return (size_t)n * Hq * (d + 2) + (size_t)hist_blocks * g * (d + 2);
+// Workspace (4-byte words) of one decode launch: window partials
+// [n][Hq][d + 2], then split partials [n][Hkv][smax][g][d + 2], smax the
+// launch's largest split count (slot s of a pair holds its split s).
+inline size_t decode_ws_floats(int Hq, int d, int n, int Hkv, int smax, int g) {
+  return (size_t)n * Hq * (d + 2) + (size_t)n * Hkv * smax * g * (d + 2);
 }
 
 } // namespace oscar
