@@ -15,7 +15,7 @@
  * 2-bit integers give four discrete levels; the decode kernel dequantizes
  * with a scale and a zero point.
  *
- * Readings where the article is silent (each listed in the design doc):
+ * Readings where the article is silent:
  *   - the rotation acts on row vectors, y = x R, evaluated per output
  *     channel j as a fused-multiply-add chain over i = 0..d-1 in fp32,
  *     starting from +0;
