@@ -148,6 +148,50 @@ def test_fused_steps_match_oracle_and_separate_calls(shape):
     assert fused.free_pages() == separate.free_pages()
 
 
+@pytest.mark.parametrize("hkv", [1, 4])
+def test_batches_wider_than_one_launch(hkv):
+    # 300 sequences: a call is cut into launches of at most 256 sequences,
+    # the append's pages still taken in seq_ids order across them.  With one
+    # kv head the first launch fits one round of blocks and the step runs as
+    # one fused launch pair; with four it needs several rounds and runs as
+    # separate append and decode launches.  Sampled rows (both sides of each
+    # launch boundary) against the oracle at every step; every page table
+    # against the oracle's allocator; codes and windows of the sampled
+    # sequences bit-exact at the end.
+    n, steps = 300, 3
+    w = synth.Workload(f"wide_h{hkv}", 30 + hkv, n, 2 * hkv, hkv, 64, 64, 0, 0)
+    rng = np.random.default_rng(17)
+    lengths = [EDGE_LENS[b % len(EDGE_LENS)] if b % 3 == 0 else int(rng.integers(1, 1400)) for b in range(n)]
+    pool, cfg = _pool(w, lengths, extra=steps, slack=4)
+    m = _model(cfg)
+    harness.prefill_all(pool, w, lengths)
+    for b, L in enumerate(lengths):
+        m.prefill(b, L)
+    sample = sorted({0, 1, 127, 254, 255, 256, 257, 298, 299} | set(range(3, n, 37)))
+    for step in range(1, steps + 1):
+        order = [int(x) for x in rng.permutation(n)]
+        k_new, v_new = harness.step_tokens(w, lengths, order)
+        q = synth.queries(w, step, device="cuda", batch=n)
+        qo = q[torch.as_tensor(order, device="cuda")].contiguous().view(torch.uint16)
+        out = pool.step(order, k_new, v_new, qo)
+        m.append(order)
+        for b in order:
+            lengths[b] += 1
+        torch.cuda.synchronize()
+        out = out[torch.as_tensor(np.argsort(order), device="cuda")]
+        qb = synth.bf16_bits(synth.queries(w, step, batch=n))
+        for b in sample:
+            st, _, _ = oracle_sequence(w, b, lengths[b])
+            check_rows(out[b], st, qb[b], w, list(range(w.num_q_heads)))
+    for b in range(n):
+        assert pool.length(b) == lengths[b]
+        assert list(pool.page_table(b)) == m.table[b]
+    for b in sample:
+        st, k, v = oracle_sequence(w, b, lengths[b])
+        check_history_codes(pool, w, b, st, range(w.num_kv_heads))
+        check_windows(pool, w, b, lengths[b], k, v, range(w.num_kv_heads))
+
+
 def test_shuffle_invariance_and_determinism():
     # Deterministic pools: bitwise equal results from call to call and for
     # any placement of the pages in the pool.
