@@ -14,8 +14,11 @@
 //     * its waves stream the split's INT2 pages in the rotated basis,
 //       taking pages from a shared counter;
 //     * the block that holds the pair's last split also attends to the
-//       BF16 sink and recent tokens with the raw queries (four waves, while
-//       the others stream pages);
+//       BF16 sink and recent tokens with the raw queries (four waves, two
+//       for 16 query heads, while the others stream pages); in a decode
+//       step (oscar_decode_step) two of those waves first append the new
+//       token: its slot before the window is read, the evicted token's
+//       rotation, clip, quantization and packing after it;
 //     * the block merges its waves and de-rotates the history accumulator
 //       by R_V^T; it writes one partial (m, l, acc) per query head for the
 //       history and, if it holds it, one for the window.
@@ -44,8 +47,6 @@
 namespace oscar {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 // P' rows hold 64 fp16 weights plus 8 of padding: the PV operand reads of 8
 // lanes (rows n .. n+7 at one column) then fall on distinct LDS banks.
@@ -1176,7 +1177,9 @@ constexpr int merge_threads() { return GQ * D < 1024 ? GQ * D : 1024; }
 template <int D, int GQ>
 __global__ __launch_bounds__((merge_threads<D, GQ>())) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
                                                                      const float *__restrict__ ws) {
-  merge_pair<D, GQ, merge_threads<D, GQ>()>(p, b, out, ws, blockIdx.x / p.Hkv, blockIdx.x % p.Hkv, threadIdx.x);
+  // grid (sequence, kv head): the pair is known before any kernel argument
+  // arrives, so all of them load in one round
+  merge_pair<D, GQ, merge_threads<D, GQ>()>(p, b, out, ws, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 template <int D, int G, int GQ>
@@ -1217,7 +1220,7 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
                         tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, in);
   // A separate launch: merging in the last block of each pair needs
   // device-scope fences, which cost more than this kernel here.
-  hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n * p.Hkv), dim3(merge_threads<D, GQ>()), 0, s,
+  hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s,
                         tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, out, (const float *)ws);
   return hipGetLastError();
 }
