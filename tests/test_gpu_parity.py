@@ -192,6 +192,41 @@ def test_batches_wider_than_one_launch(hkv):
         check_windows(pool, w, b, lengths[b], k, v, range(w.num_kv_heads))
 
 
+def test_steps_on_a_side_stream_match_the_default_stream():
+    # The same deterministic steps enqueued on a second stream (passed through
+    # the C ABI) and on the current stream: bitwise equal outputs and pools.
+    w = _workload("g4_d128_G128")
+    lengths = [1000, 385, 320, 64, 1]
+    steps = 6
+    pools = []
+    for _ in range(2):
+        pool, cfg = _pool(w, lengths, extra=steps, slack=2, flags=ok.POOL_DETERMINISTIC)
+        harness.prefill_all(pool, w, lengths)
+        pools.append(pool)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    ids = list(range(len(lengths)))
+    lens = list(lengths)
+    for step in range(1, steps + 1):
+        k_new, v_new = harness.step_tokens(w, lens, ids)
+        q = synth.queries(w, step, device="cuda", batch=len(lens)).view(torch.uint16).contiguous()
+        a = pools[0].step(ids, k_new, v_new, q)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            b = torch.empty_like(a)
+            pools[1].step(ids, k_new, v_new, q, out=b, stream=side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        lens = [L + 1 for L in lens]
+    for s_ in ids:
+        assert list(pools[0].page_table(s_)) == list(pools[1].page_table(s_))
+        n_hist = max(lens[s_] - 320, 0)
+        h0 = ok.oscar_export_history(pools[0].handle, s_, 0, n_hist, w.num_kv_heads, w.head_dim, w.group_size)
+        h1 = ok.oscar_export_history(pools[1].handle, s_, 0, n_hist, w.num_kv_heads, w.head_dim, w.group_size)
+        assert all(np.array_equal(x, y) for x, y in zip(h0, h1))
+
+
 def test_shuffle_invariance_and_determinism():
     # Deterministic pools: bitwise equal results from call to call and for
     # any placement of the pages in the pool.
