@@ -129,6 +129,16 @@ __device__ __forceinline__ uint32_t row16_or(uint32_t v) {
 // normal range flush to 0, which a softmax weight can afford).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Byte / half-word entries of a kernel-argument array, read through their
+// dword: scalar loads (a sub-dword load would be a vector load).  The
+// arrays start at 4-byte offsets.
+__device__ __forceinline__ int karg_u8(const uint8_t *a, int i) {
+  return (int)((((const uint32_t *)a)[i >> 2] >> (8 * (i & 3))) & 0xffu);
+}
+__device__ __forceinline__ int karg_u16(const uint16_t *a, int i) {
+  return (int)((((const uint32_t *)a)[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+}
+
 // A D x D fp32 rotation table in shared memory: 1 KB chunks of 256 / D
 // rows, each followed by 16 pad floats, so that rows of chunks whose index
 // differs mod 4 start 16 banks apart.
@@ -338,7 +348,7 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
   const int n_sink = min(L, kSink), n_rec = min(max(L - kSink, 0), kRecent), n_win = n_sink + n_rec;
   {
     // this wave's copy of the query rows: no block barrier needed
-    const uint32_t *src = (const uint32_t *)(q + ((size_t)b.row[e] * Hq + kv * GQ) * D);
+    const uint32_t *src = (const uint32_t *)(q + ((size_t)karg_u16(b.row, e) * Hq + kv * GQ) * D);
     for (int idx = lane; idx < GQ * D / 2; idx += 64) sm.q2[wi][idx / (D / 2)][idx % (D / 2)] = src[idx];
   }
   wave_sync();
@@ -476,7 +486,7 @@ template <int D, int GQ, int NW>
 __device__ void fused_append_slot(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, const AppendIn &in,
                                   int e, int kv, int kind, int lane) {
   const int Hkv = p.Hkv, seq = b.seq[e], L0 = b.len[e] - 1;
-  const uint16_t *xn = (kind ? in.v : in.k) + ((size_t)b.row[e] * Hkv + kv) * D;
+  const uint16_t *xn = (kind ? in.v : in.k) + ((size_t)karg_u16(b.row, e) * Hkv + kv) * D;
   const bool evict = L0 >= kWindow;
   {
     // the slot: dword u of the row (channels 2u, 2u + 1) by lane u
@@ -741,7 +751,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // page ids are staged; the block builds the query record.
   stage_table<D>(sm.R, p.RK + (size_t)kv * D * D, w, W, lane);
   {
-    const uint16_t *qrow = q + ((size_t)b.row[e] * p.Hq + kv * GQ) * D;
+    const uint16_t *qrow = q + ((size_t)karg_u16(b.row, e) * p.Hq + kv * GQ) * D;
     for (int idx = tid; idx < GQ * D; idx += NT) sm.u.pre.qT[idx % D][idx / D] = bf16f(qrow[idx]);
   }
   for (int i = p0 + tid; i < min(pf, p0 + kIdCache); i += NT) sm.ids[i - p0] = ptab[i];
@@ -1123,10 +1133,10 @@ __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, c
   constexpr int SB = 4; // splits per batch of loads
   const int Hkv = p.Hkv, Hq = p.Hq;
   const float *ws_win = ws;
-  const int smax = b.nsplit[0]; // launch order is by split count, descending
+  const int smax = karg_u8(b.nsplit, 0); // launch order is by split count, descending
   const float *ws_pair = ws + (size_t)b.n * Hq * (D + 2) + (size_t)(e * Hkv + kv) * smax * GQ * (D + 2);
-  const int S = b.nsplit[e];
-  float *out_pair = out + ((size_t)b.row[e] * Hq + kv * GQ) * D;
+  const int S = karg_u8(b.nsplit, e);
+  float *out_pair = out + ((size_t)karg_u16(b.row, e) * Hq + kv * GQ) * D;
   for (int idx = tid; idx < GQ * D; idx += NT) {
     const int h = idx / D, c = idx % D;
     const float *win = ws_win + ((size_t)e * Hq + kv * GQ + h) * (D + 2);
@@ -1193,13 +1203,13 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   const int blk = blockIdx.x, Hkv = p.Hkv;
   int s, e, kv;
   block_split(b, Hkv, blk, s, e, kv);
-  const int S = b.nsplit[e];
+  const int S = karg_u8(b.nsplit, e);
   const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
   int p0, p1;
   split_range(np, S, s, b.win_units, p0, p1);
   // split partial slot: the pair's splits are consecutive, stride the
   // batch's largest split count (launch order is by split count, descending)
-  const int slot = (e * Hkv + kv) * b.nsplit[0] + s;
+  const int slot = (e * Hkv + kv) * karg_u8(b.nsplit, 0) + s;
   if (p0 < p1)
     history_block<D, G, GQ>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
   else if (s == S - 1) {

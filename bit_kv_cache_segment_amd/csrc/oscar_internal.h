@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace oscar {
@@ -116,6 +117,10 @@ struct DecodeBatch {
   int32_t new_page[kMaxBatch];
 };
 
+// the kernels read row[] and nsplit[] through whole dwords
+static_assert(offsetof(DecodeBatch, row) % 4 == 0 && offsetof(DecodeBatch, nsplit) % 4 == 0,
+              "row and nsplit must start at 4-byte offsets");
+
 // History pages [p0, p1) of split s of S of a pair with np pages: the pair's
 // units [0, np + wu) are cut evenly, pages are units below np.  Only the last
 // split can be left without pages when S <= (np + wu) / max(wu, 1).
@@ -128,13 +133,20 @@ __host__ __device__ inline void split_range(int np, int S, int s, int wu, int &p
 }
 
 // Split layer s, sequence e (launch order) and kv head of decode block blk:
-// s is the largest layer with layer_prefix[s] <= blk.
+// s is the largest layer with layer_prefix[s] <= blk.  layer_prefix does not
+// decrease, so s counts the entries 1..kMaxSplits at or below blk; every
+// entry is read at a fixed offset (on the device: one round of scalar loads
+// rather than a dependent chain).
 __host__ __device__ inline void block_split(const DecodeBatch &b, int Hkv, int blk, int &s, int &e, int &kv) {
   s = 0;
+  int base = 0; // layer_prefix[s]
 #pragma unroll
-  for (int step = kMaxSplits / 2; step >= 1; step >>= 1)
-    if (b.layer_prefix[s + step] <= blk) s += step;
-  const int pos = blk - b.layer_prefix[s];
+  for (int i = 1; i <= kMaxSplits; ++i) {
+    const int v = b.layer_prefix[i];
+    s += v <= blk ? 1 : 0;
+    base = v <= blk ? v : base;
+  }
+  const int pos = blk - base;
   e = pos / Hkv;
   kv = pos % Hkv;
 }
