@@ -56,13 +56,16 @@ _SRC = os.path.join(_HERE, "oscar_oracle.c")
 _LIB = os.path.join(_HERE, "liboscar_oracle.so")
 
 
+# gcc flags of the C codec: no fast-math, no FP contraction; -mfma lets fmaf,
+# which is exact either way, compile to the hardware instruction.
+CFLAGS = ["-O2", "-mfma", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11"]
+
+
 def build(force: bool = False) -> str:
-    """Compile the C codec with gcc (no fast-math, no FP contraction; -mfma lets
-    fmaf, which is exact either way, compile to the hardware instruction)."""
+    """Compile the C codec with gcc (CFLAGS)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-mfma", "-fno-fast-math", "-ffp-contract=off",
-                               "-fPIC", "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -73,21 +76,26 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        L = ctypes.CDLL(build())
-        P = ctypes.c_void_p
-        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
-        L.oracle_f32_to_f16.restype = ctypes.c_uint16
-        L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
-        L.oracle_f16_to_f32.restype = ctypes.c_float
-        L.oracle_rotate.argtypes = [P, P, ctypes.c_int, P]
-        L.oracle_clip.argtypes = [P, P, ctypes.c_int]
-        L.oracle_quantize.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P]
-        L.oracle_pack.argtypes = [P, ctypes.c_int, P]
-        L.oracle_unpack.argtypes = [P, ctypes.c_int, P]
-        L.oracle_encode.argtypes = [P, ctypes.c_long, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
-        L.oracle_rotate_many.argtypes = [P, ctypes.c_long, ctypes.c_int, P, P]
-        _lib = L
+        _lib = configure(ctypes.CDLL(build()))
     return _lib
+
+
+def configure(L):
+    """Declare the C codec's signatures on a loaded library (also used by the
+    tests that load a copy of the codec with a planted mistake)."""
+    P = ctypes.c_void_p
+    L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    L.oracle_f32_to_f16.restype = ctypes.c_uint16
+    L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    L.oracle_f16_to_f32.restype = ctypes.c_float
+    L.oracle_rotate.argtypes = [P, P, ctypes.c_int, P]
+    L.oracle_clip.argtypes = [P, P, ctypes.c_int]
+    L.oracle_quantize.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P]
+    L.oracle_pack.argtypes = [P, ctypes.c_int, P]
+    L.oracle_unpack.argtypes = [P, ctypes.c_int, P]
+    L.oracle_encode.argtypes = [P, ctypes.c_long, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+    L.oracle_rotate_many.argtypes = [P, ctypes.c_long, ctypes.c_int, P, P]
+    return L
 
 
 def _ptr(a: np.ndarray):

@@ -73,6 +73,29 @@ def test_derotation_convention():
     assert np.abs(rot - oracle.attention(q, K, V, 0.125)).max() <= 1e-12
 
 
+def test_history_decodes_back_in_the_original_basis():
+    # A history token x is stored as codes of y = clip(x R); it decodes to
+    # deq . R^T.  R is orthogonal to ~2e-6, so the decoded token lies within
+    # |deq - y| (2-norm) of clip(x R) . R^T, computed here directly.
+    w = synth.WORKLOADS["tiny"]
+    L = w.len_lo
+    k = synth.bf16_bits(synth.kv_tokens(w, 0, 0, 0, L))
+    v = synth.bf16_bits(synth.kv_tokens(w, 1, 0, 0, L))
+    RK, RV = oracle.rotation(synth.random_orthogonal_u(w, 0)), oracle.rotation(synth.random_orthogonal_u(w, 1))
+    cK = np.full((w.num_kv_heads, w.head_dim), 2.5, dtype=np.float32)
+    cV = np.full((w.num_kv_heads, w.head_dim), 2.5, dtype=np.float32)
+    st = oracle.build_sequence(k, v, RK, RV, cK, cV, w.group_size, heads=[0])
+    _, hist, _ = oracle.segments(L)
+    x = oracle.bf16_bits_to_f64(k[hist.start:hist.stop, 0])
+    y = np.clip(x @ RK[0].astype(np.float64), -2.5, 2.5)
+    ref = y @ RK[0].astype(np.float64).T
+    pk, s16, z16 = st.hist[("K", 0)]
+    deq = oracle.dequantize(pk, s16, z16, w.group_size)
+    err = np.linalg.norm(st.K[hist.start:hist.stop, 0] - ref, axis=1)
+    bound = np.linalg.norm(deq - y, axis=1) * (1 + 1e-4) + 1e-4
+    assert np.all(err <= bound)
+
+
 def test_tiny_workload_sequence_end_to_end():
     w = synth.WORKLOADS["tiny"]
     L = w.len_lo

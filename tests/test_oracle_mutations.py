@@ -1,0 +1,221 @@
+"""The oracle's pins catch plausible mistakes.
+
+C codec: each case copies oracle/oscar_oracle.c, plants one mistake by a
+textual edit, builds the copy with the same flags and runs the codec pins
+(tests/test_oracle_codec.py) against it.  Python parts: each case replaces
+one oracle function, for the test's duration only, by a copy with one
+mistake and runs the rotation, attention and pool pins.  Either way at least
+one pin must fail.  The oracle's own files are never modified."""
+import ctypes
+import math
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_attention
+import test_oracle_codec as pins
+import test_oracle_pool
+import test_oracle_rotation
+
+# name: (text in oscar_oracle.c, replacement)
+MISTAKES = {
+    "rotation unfused (mul, then add)": (
+        "acc = fmaf(bf16_to_f32(x[i]), R[(size_t)i * d + j], acc);",
+        "acc = bf16_to_f32(x[i]) * R[(size_t)i * d + j] + acc;"),
+    "rotation summed in reverse order": (
+        "for (int i = 0; i < d; ++i)\n            acc = fmaf(",
+        "for (int i = d - 1; i >= 0; --i)\n            acc = fmaf("),
+    "rotation R x instead of x R": (
+        "R[(size_t)i * d + j], acc)",
+        "R[(size_t)j * d + i], acc)"),
+    "clip on one side only": (
+        "y[j] = fminf(fmaxf(y[j], -c[j]), c[j]);",
+        "y[j] = fminf(y[j], c[j]);"),
+    "codes rounded half away from zero": (
+        "q = rintf((v[k] - z) / s);",
+        "q = roundf((v[k] - z) / s);"),
+    "codes from the unrounded scale": (
+        "float s = oracle_f16_to_f32(s16);",
+        "float s = range / 3.0f;"),
+    "codes from the unrounded zero point": (
+        "float z = oracle_f16_to_f32(z16);",
+        "float z = mn;"),
+    "negative zero kept as the zero point": (
+        "oracle_f32_to_f16(mn + 0.0f)",
+        "oracle_f32_to_f16(mn)"),
+    "codes not clamped to 0..3": (
+        "q = fminf(fmaxf(q, 0.0f), 3.0f);",
+        "(void)0;"),
+    "codes by the reciprocal of the scale": (
+        "q = rintf((v[k] - z) / s);",
+        "q = rintf((v[k] - z) * (1.0f / s));"),
+    "scale from the range times fp32(1/3)": (
+        "oracle_f32_to_f16(range / 3.0f)",
+        "oracle_f32_to_f16(range * (1.0f / 3.0f))"),
+    "group minimum and maximum skip an element": (
+        "for (int k = 1; k < G; ++k) {",
+        "for (int k = 2; k < G; ++k) {"),
+    "pack with the first code in the high bits": (
+        "codes[4 * b] | (codes[4 * b + 1] << 2) |\n                             (codes[4 * b + 2] << 4) | (codes[4 * b + 3] << 6)",
+        "(codes[4 * b] << 6) | (codes[4 * b + 1] << 4) |\n                             (codes[4 * b + 2] << 2) | codes[4 * b + 3]"),
+    "unpack from the high bits": (
+        "codes[i] = (bytes[i / 4] >> (2 * (i % 4))) & 3;",
+        "codes[i] = (bytes[i / 4] >> (2 * (3 - i % 4))) & 3;"),
+}
+
+PINS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
+
+
+def _planted(tmp_path, old, new):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, old
+    c = tmp_path / "planted.c"
+    c.write_text(src.replace(old, new))
+    so = tmp_path / "libplanted.so"
+    subprocess.check_call(["gcc", *oracle.CFLAGS, "-o", str(so), str(c), "-lm"])
+    return oracle.configure(ctypes.CDLL(str(so)))
+
+
+@pytest.mark.parametrize("name", list(MISTAKES))
+def test_planted_mistake_fails_a_pin(name, tmp_path, monkeypatch):
+    monkeypatch.setattr(oracle, "_lib", _planted(tmp_path, *MISTAKES[name]))
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no codec pin catches: {name}"
+
+
+def test_unplanted_copy_passes_every_pin(tmp_path, monkeypatch):
+    # the same machinery with no edit: every pin passes, so a failure above
+    # is the planted mistake's
+    monkeypatch.setattr(oracle, "_lib", _planted(tmp_path, "void oracle_rotate(", "void oracle_rotate("))
+    for pin in PINS:
+        pin()
+
+
+def _calls(module):
+    """The module's pins as zero-argument calls (parametrized ones expanded)."""
+    out = []
+    for name in dir(module):
+        fn = getattr(module, name)
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not marks:
+            out.append((name, fn))
+            continue
+        argname, values = marks[0].args[0], marks[0].args[1]
+        out += [(f"{name}[{v}]", (lambda f, v: lambda: f(v))(fn, v)) for v in values]
+    return out
+
+
+PY_PINS = _calls(test_oracle_rotation) + _calls(test_oracle_attention) + _calls(test_oracle_pool)
+
+
+def _bad_hadamard(d):
+    i, j = np.arange(d)[:, None], np.arange(d)[None, :]
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i | j)
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def _bad_rotation(U):
+    U = np.asarray(U, dtype=np.float32)
+    d = U.shape[-1]
+    S = oracle.hadamard_unnormalized(d) @ oracle.bitrev_permutation(d) @ U.astype(np.float64)
+    return (S / math.sqrt(float(d))).astype(np.float32)
+
+
+def _bad_percentile(a, pct):
+    n = len(a)
+    h = n * (pct / 100.0)
+    k = min(int(math.floor(h)), n - 1)
+    return float(a[k]) + (h - k) * (float(a[min(k + 1, n - 1)]) - float(a[k]))
+
+
+def _bad_free_list(num_pages, seed):
+    a = list(range(num_pages))
+    g = oracle.splitmix64_stream(seed)
+    for i in range(num_pages - 1, 0, -1):
+        j = next(g) % i
+        a[i], a[j] = a[j], a[i]
+    return a
+
+
+def _bad_attention(q, K, V, scale):
+    logits = scale * (K @ q)
+    w = np.exp(logits - logits.max())
+    return w @ V
+
+
+def _bad_merge(parts):
+    m = max(p[0] for p in parts)
+    l, acc = 0.0, 0.0
+    for mi, li, ai in parts:
+        w = 0.0 if mi == -math.inf else math.exp(m - mi)
+        l, acc = l + w * li, acc + w * ai
+    return m, l, acc
+
+
+def _bad_segments(L):
+    n_hist = max(0, L - oracle.WINDOW + 1)
+    return (range(0, min(L, oracle.SINK)), range(oracle.SINK, oracle.SINK + n_hist),
+            range(oracle.SINK + n_hist, max(L, oracle.SINK + n_hist)))
+
+
+def _bad_append(self, seq_ids):
+    for s_ in seq_ids:
+        L = self.length.get(s_, 0)
+        if L >= oracle.WINDOW and (L - oracle.WINDOW) % oracle.PAGE == 1:
+            self.table.setdefault(s_, []).append(self._take())
+        self.length[s_] = L + 1
+
+
+PY_MISTAKES = {
+    "bit reversal left out": ("bitrev", lambda i, bits: i),
+    "Hadamard sign from popcount(i | j)": ("hadamard_unnormalized", _bad_hadamard),
+    "R = Hadamard . bit-reversal . U": ("rotation", _bad_rotation),
+    "percentile position N p instead of (N - 1) p": ("percentile_linear", _bad_percentile),
+    "Fisher-Yates j = next() mod i": ("free_list", _bad_free_list),
+    "history decoded by R instead of R^T": ("decode_history",
+                                             lambda pk, s16, z16, G, R: oracle.dequantize(pk, s16, z16, G) @ np.asarray(R, dtype=np.float64)),
+    "softmax weights not normalised": ("attention", _bad_attention),
+    "merge weights exp(m - m_i)": ("merge_partials", _bad_merge),
+    "history starts one token early": ("segments", _bad_segments),
+    "recent ring of 255 slots": ("ring_slot", lambda pos: (pos - oracle.SINK) % 255),
+    "bits per element with one fp16 parameter": ("bits_per_element",
+                                                 lambda L, G: (max(0, L - oracle.WINDOW) * (2 + 16 / G) + min(L, oracle.WINDOW) * 16) / L),
+}
+
+
+@pytest.mark.parametrize("name", list(PY_MISTAKES))
+def test_planted_python_mistake_fails_a_pin(name, monkeypatch):
+    attr, bad = PY_MISTAKES[name]
+    monkeypatch.setattr(oracle, attr, bad)
+    failed = []
+    for pin_name, pin in PY_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed.append(pin_name)
+    assert failed, f"no pin catches: {name}"
+
+
+def test_planted_page_allocation_mistake_fails_a_pin(monkeypatch):
+    monkeypatch.setattr(oracle.PoolModel, "append", _bad_append)
+    failed = []
+    for pin_name, pin in PY_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed.append(pin_name)
+    assert failed, "no pin catches a page taken one slot late"
+
+
+def test_python_pins_pass_unplanted():
+    for pin_name, pin in PY_PINS:
+        pin()

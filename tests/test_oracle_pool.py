@@ -46,6 +46,17 @@ def test_free_list_is_a_seeded_permutation():
     assert a != list(range(1000))
 
 
+def test_free_list_generator_and_shuffle_match_published_outputs():
+    # SplitMix64 against its published reference outputs, Fisher-Yates
+    # against a case worked by hand (tests/golden/free_list.txt)
+    for row in _rows("free_list.txt"):
+        if row[0] == "S":
+            g = oracle.splitmix64_stream(int(row[1]))
+            assert [next(g) for _ in row[2:]] == [int(v) for v in row[2:]]
+        else:
+            assert oracle.free_list(int(row[1]), int(row[2])) == [int(v) for v in row[3:]]
+
+
 def test_pool_model_pages():
     pm = oracle.PoolModel(num_pages=200, seed=9, max_pages_per_seq=64)
     fl = list(pm.free)

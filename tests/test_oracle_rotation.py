@@ -54,6 +54,23 @@ def test_rotation_orthogonal(name):
     assert np.abs(R64 @ R64.T - np.eye(d)).max() <= 1e-12
 
 
+def test_rotation_matches_its_definition():
+    # R = U . H . Pi / sqrt(d) evaluated without the oracle's own H and Pi:
+    # scipy's Hadamard matrix, and Pi as the column permutation j -> bitrev(j)
+    # by reversing j's binary digits.  U lies on the 2^-40 grid, so U . H is
+    # exact in fp64 and both sides round the same two times.
+    for name in ("tiny", "qwen3_8b_32k"):
+        w = synth.WORKLOADS[name]
+        d = w.head_dim
+        bits = d.bit_length() - 1
+        perm = [int(format(j, f"0{bits}b")[::-1], 2) for j in range(d)]
+        U = synth.random_orthogonal_u(w, 0)
+        R = oracle.rotation(U)
+        for h in range(U.shape[0]):
+            ref = ((U[h].astype(np.float64) @ scipy.linalg.hadamard(d))[:, perm] / math.sqrt(d)).astype(np.float32)
+            assert np.array_equal(R[h], ref), (name, h)
+
+
 def test_rotation_is_exact_on_the_grid():
     # with U on the 2^-40 grid, U.H.Pi has no rounding: a dense fp64 product in
     # a different association order gives the same bits
