@@ -15,7 +15,9 @@ inline int plan_pages(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPag
 
 // Split policy of one decode launch.  A pair's work is its history pages
 // plus its window, worth window_units pages (the window's bytes over a page
-// block's bytes, times kWindowCost).  Pieces of at most P units: a pair gets
+// block's bytes, times kWindowCost; kStepWindowCost when the launch also
+// appends, since the append then runs on the window block's waves after its
+// window).  Pieces of at most P units: a pair gets
 // S = ceil(U / P) blocks (at most kMaxSplits, and at most U / wu so that
 // only the last split can be window-only), and P is the smallest piece size
 // for which all blocks fit in R rounds of the device's resident block slots
@@ -23,11 +25,11 @@ inline int plan_pages(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPag
 // more pairs than slots, else kExtraRounds more than the pairs need, so that
 // long pairs are cut and rounds even out.  Blocks are dispatched largest
 // first (more splits, then more pages).
-constexpr double kWindowCost = 1.0;
+constexpr double kWindowCost = 1.0, kStepWindowCost = 2.4;
 constexpr int kExtraRounds = 0;
 
-inline int window_units(int d, int G) {
-  return (int)std::lround(kWindowCost * kWindow * 4 * d / block_bytes_for(d, G));
+inline int window_units(int d, int G, bool fused = false) {
+  return (int)std::lround((fused ? kStepWindowCost : kWindowCost) * kWindow * 4 * d / block_bytes_for(d, G));
 }
 
 // fused: the launch also appends (len is the length after the append); a

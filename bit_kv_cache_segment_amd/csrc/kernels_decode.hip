@@ -508,10 +508,12 @@ __device__ void fused_append_slot(WinSmem<D, GQ, NW> &sm, const PoolDev &p, cons
 
 // Second part: the evicted token into the history, published; only the
 // pass over the pair's last page, after the page loop, reads it, so this
-// runs after the wave's share of the window.
+// runs after the wave's share of the window.  The K rotation reads R_K from
+// the block's shared-memory table (it holds R_K until the epilogue); the V
+// rotation reads the columns of R_V as rows of R_V^T, 16 bytes per load.
 template <int D, int G, int GQ, int NW>
-__device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, int e, int kv,
-                                  int kind, int lane) {
+__device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_lds, const PoolDev &p,
+                                  const DecodeBatch &b, int e, int kv, int kind, int lane) {
   constexpr int CPL = D / 64; // channels lane + 64 c of this lane
   const int Hkv = p.Hkv, seq = b.seq[e], L0 = b.len[e] - 1;
   if (L0 >= kWindow) {
@@ -523,11 +525,31 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const PoolDev &p, cons
     float y[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) y[c] = 0.f;
+    if (kind == 0) {
+      constexpr int RPC = RTable<D>::RPC;
 #pragma unroll 16
-    for (int i = 0; i < D; ++i) {
-      const float xi = sm.app_x[kind][i];
+      for (int i = 0; i < D; ++i) {
+        const float xi = sm.app_x[0][i];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) y[c] = fmaf(xi, R[i * D + lane + 64 * c], y[c]);
+        for (int c = 0; c < CPL; ++c) y[c] = fmaf(xi, RK_lds.c[i / RPC][(i % RPC) * D + lane + 64 * c], y[c]);
+      }
+    } else {
+      // column j of R_V is row j of R_V^T: 16-byte loads, four rows of the
+      // chain each
+      const float4 *col[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) col[c] = (const float4 *)(p.RVt + ((size_t)kv * D + lane + 64 * c) * D);
+#pragma unroll 8
+      for (int i4 = 0; i4 < D / 4; ++i4) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float4 r4 = col[c][i4];
+          y[c] = fmaf(sm.app_x[1][4 * i4 + 0], r4.x, y[c]);
+          y[c] = fmaf(sm.app_x[1][4 * i4 + 1], r4.y, y[c]);
+          y[c] = fmaf(sm.app_x[1][4 * i4 + 2], r4.z, y[c]);
+          y[c] = fmaf(sm.app_x[1][4 * i4 + 3], r4.w, y[c]);
+        }
+      }
     }
     uint32_t code[CPL];
     uint16_t s16[CPL], z16[CPL];
@@ -813,7 +835,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       wait_count(&sm.win.app_slot_done, 2);
     }
     window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
-    if (b.fused && w < 2) fused_append_page<D, G, GQ, WW>(sm.win, p, b, e, kv, w, lane);
+    if (b.fused && w < 2) fused_append_page<D, G, GQ, WW>(sm.win, sm.R, p, b, e, kv, w, lane);
   }
   auto stage = [&](int s0, int sf) __attribute__((always_inline)) {
     for (int i = s0 + tid; i < sf; i += NT) sm.ids[i - s0] = ptab[i];

@@ -499,7 +499,7 @@ int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
       b.n = std::min(kMaxBatch, n - i0);
       std::vector<int> len(b.n);
       for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
-      plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size), fused);
+      plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size, fused), fused);
       need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
       if (b.hist_blocks > p->decode_slots) fused = false;
       batches.push_back(b);

@@ -39,7 +39,7 @@ int main(int argc, char **argv) {
     const int slots = 1 + (int)(rng() % 1024);
     const int d = rng() % 2 ? 128 : 64, G = (d == 128 && rng() % 2) ? 128 : 64;
     const bool fused = rng() % 2;
-    plan_splits(b, ids.data(), len, Hkv, slots, window_units(d, G), fused);
+    plan_splits(b, ids.data(), len, Hkv, slots, window_units(d, G, fused), fused);
     std::vector<int> seen_row(b.n, 0);
     for (int e = 0; e < b.n; ++e) {
       if (b.row[e] >= b.n || b.seq[e] != ids[b.row[e]] || b.len[e] != len[b.row[e]])
