@@ -677,7 +677,9 @@ int oscar_profile_begin(oscar_pool *p, int32_t max_calls, uint32_t kernels, int3
   for (auto &v : p->prof.ev) {
     v.resize(2 * (size_t)max_calls);
     for (hipEvent_t &e : v) {
-      hipError_t r = hipEventCreate(&e);
+      // timing only: without the system-scope fence a timed launch is not
+      // preceded by a cache write-back that the interval would count
+      hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
       if (r != hipSuccess) {
         e = nullptr;
         p->prof.release();

@@ -234,9 +234,11 @@ int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R
  * 2 every, ... of each kernel are timed (every >= 1), later ones and the
  * rest go untimed.  oscar_profile_end waits for the events, writes the
  * number of timed launches and their summed durations (milliseconds), and
- * releases the events.  Each timed launch adds a few microseconds between
- * launches, so time only the kernels of interest, or a sample of their
- * launches.  Errors: EINVAL, EHIP. */
+ * releases the events.  The events carry no system-scope fence (timing
+ * only).  Each timed launch still starts a few microseconds after the
+ * kernel before it, and the interval counts that gap, so time only the
+ * kernels of interest, or a sample of their launches.  Errors: EINVAL,
+ * EHIP. */
 typedef struct oscar_profile {
     int32_t n_decode_main;   float ms_decode_main;   /* query prep, INT2 history, BF16 window */
     int32_t n_decode_merge;  float ms_decode_merge;  /* merge of the partials                 */
