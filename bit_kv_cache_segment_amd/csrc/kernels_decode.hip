@@ -520,7 +520,6 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_ld
     wave_sync(); // this wave's writes of the old token to shared memory
     const int n_hist0 = L0 - kWindow, t = n_hist0 % kPage;
     const int page = t == 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage];
-    const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
     const float *clip = (kind ? p.clipV : p.clipK) + (size_t)kv * D;
     float y[CPL];
 #pragma unroll
