@@ -273,6 +273,7 @@ struct HistSmem {
   uint32_t rec[query_record_words<D, GQ>()]; // the pair's query record
   int32_t ids[kIdCache];                // page ids of a segment of the split
   uint32_t claim;                       // next page of the segment to hand out
+  uint32_t exited;                      // waves out of the page loop
   WinSmem<D, GQ, win_waves(W, GQ)> win;     // window results of the window waves
   union alignas(16) {
     QueryPrep<D, GQ> pre;               // prologue: query preparation
@@ -778,6 +779,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   for (int i = p0 + tid; i < min(pf, p0 + kIdCache); i += NT) sm.ids[i - p0] = ptab[i];
   if (tid == 0) {
     sm.claim = (uint32_t)p0;
+    sm.exited = 0u;
     sm.win.app_slot_done = sm.win.app_page_done = 0;
   }
   for (int idx = tid; idx < W * 16; idx += NT) sm.alpha[idx / 16][idx % 16] = 1.f;
@@ -1052,15 +1054,18 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // ---- epilogue: per-wave (m, l, acc); each wave weights its accumulators
   // by 2^(m_w - m) (m: the block maximum), the waves are summed, and the sum
   // is de-rotated by R_V^T: the stored partial is in the basis of V itself.
-  // R_V^T replaces R_K in shared memory; its loads are issued here and
-  // written out just before the merge, their latency covered by the steps
-  // between.
-  constexpr int NF4 = D * D / 4, RVL = (NF4 + NT - 1) / NT;
-  u32x4 rvt[RVL];
+  // R_V^T replaces R_K in shared memory: the first wave out of the page loop
+  // copies it (direct to shared memory) while the others finish their last
+  // pages; in a fused step's window block only once the appends are done
+  // reading R_K.  No page load of this wave is outstanding any more.
   {
-    const u32x4 *src = (const u32x4 *)(p.RVt + (size_t)kv * D * D);
-#pragma unroll
-    for (int i = 0; i < RVL; ++i) rvt[i] = src[min(tid + i * NT, NF4 - 1)];
+    uint32_t order = 0;
+    if (lane == 0) order = atomicAdd(&sm.exited, 1u);
+    if (__builtin_amdgcn_readlane(order, 0) == 0) {
+      if (b.fused && with_window) wait_count(&sm.win.app_page_done, 2);
+      stage_table<D>(sm.R, p.RVt + (size_t)kv * D * D, 0, 1, lane);
+      __builtin_amdgcn_s_waitcnt(0); // the copy has landed before the barrier below
+    }
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -1111,11 +1116,6 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
         if (h < GQ) sm.u.A[w][h][c] = f * fmaf(acc[j][i], unscale, sm.zsum[w][h][c / G]);
       }
     }
-  }
-#pragma unroll
-  for (int i = 0; i < RVL; ++i) {
-    const int f = tid + i * NT; // float4 f of the table: chunk f / 64
-    if (f < NF4) *(u32x4 *)&sm.R.c[f / 64][4 * (f % 64)] = rvt[i];
   }
   __syncthreads();
   float *dst = ws_hist + (size_t)slot * GQ * (D + 2);
