@@ -278,7 +278,8 @@ struct HistSmem {
   union alignas(16) {
     QueryPrep<D, GQ> pre;               // prologue: query preparation
     _Float16 P[W][NG][16][kPRow];       // page loop: P' rows per wave (padded)
-    float A[W][GQ][D];                  // epilogue: per-wave accumulators
+    float A[W][GQ][D + 4];              // epilogue: per-wave accumulators (rows padded so
+                                        // that a wave's four head rows write distinct banks)
   } u;
 };
 
