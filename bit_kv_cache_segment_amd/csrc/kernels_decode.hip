@@ -718,25 +718,28 @@ struct PageRegs {
   u32x4 vp[D / G];  // V (scale, zero)
 };
 
+// Loads of one (page, kv head) block through a buffer resource over it.  A
+// page past the end (valid false) gets a resource of zero bytes: its loads
+// return zeros without a memory access, yet count like the others, so the
+// loop's waits stay exact and no load is left in flight behind the loop.
 template <int D, int G>
-__device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk, int n, int r) {
+__device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk, bool valid, int bytes, int n,
+                                          int r) {
   constexpr int NG = D / G;
+  constexpr int kWord3 = 0x00020000; // raw buffer, 32-bit data format
+  constexpr int kNT = 2;             // non-temporal: every byte is read once per call
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, valid ? bytes : 0, kWord3);
   // codes: 1 KB contiguous per instruction; params: 16 lanes share 256 B.
-  // Every byte is read once per call: non-temporal loads.
   const int lane = 16 * r + n;
-  const u32x4 *kc = (const u32x4 *)(blk + 16 * lane);
-  const u32x4 *vc = (const u32x4 *)(blk + 16 * D + 16 * lane);
-  const u32x4 *kp = (const u32x4 *)(blk + 32 * D + 16 * NG * n);
-  const u32x4 *vp = (const u32x4 *)(blk + 32 * D + 256 * NG + 16 * NG * n);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
-    pr.kc[i] = __builtin_nontemporal_load(kc + 64 * i);
-    pr.vc[i] = __builtin_nontemporal_load(vc + 64 * i);
+    pr.kc[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane + 1024 * i, 0, kNT);
+    pr.vc[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * D + 16 * lane + 1024 * i, 0, kNT);
   }
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    pr.kp[g] = __builtin_nontemporal_load(kp + g);
-    pr.vp[g] = __builtin_nontemporal_load(vp + g);
+    pr.kp[g] = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * D + 16 * NG * n + 16 * g, 0, kNT);
+    pr.vp[g] = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * D + 256 * NG + 16 * NG * n + 16 * g, 0, kNT);
   }
 }
 
@@ -791,7 +794,6 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // its ids in shared memory; deterministic pools take pages w, w + W, ...
   // of the segment, others take them from the shared counter.
   constexpr int PF = kPrefetch<D, G, GQ>, NB = PF + 1;
-  const uint8_t *dummy = (const uint8_t *)p.RK; // >= one page block, read-only
   const bool det = p.deterministic != 0;
   int seg0 = p0, segf = min(pf, p0 + kIdCache), next_static = p0 + w;
   auto take = [&]() __attribute__((always_inline)) {
@@ -803,7 +805,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   };
   auto load = [&](PageRegs<D, G> &buf, int page) __attribute__((always_inline)) {
     const int id = __builtin_amdgcn_readfirstlane(sm.ids[min(page, segf - 1) - seg0]);
-    load_page<D, G>(buf, page < segf ? p.pages + (size_t)id * hstride + hoff : dummy, n, r);
+    load_page<D, G>(buf, p.pages + (size_t)id * hstride + hoff, page < segf, p.block_bytes, n, r);
   };
   PageRegs<D, G> buf[NB];
   int pg[NB];
@@ -1009,7 +1011,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // that run ahead take more pages.  NB register buffers rotate: the loads
   // of the page PF steps ahead are in flight while a page is computed; the
   // page for those loads was taken one step earlier.  Every step issues its
-  // loads (a page past the segment end reads a small cached table instead),
+  // loads (a page past the segment end loads through an empty resource),
   // so each wait is an exact count of younger loads.  Only a sequence's
   // last page can be partial; it goes to the last wave after the loop.
   for (int s0 = p0; s0 < pf; s0 += kIdCache) {
@@ -1048,7 +1050,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       id = ptab[pf];
     }
     PageRegs<D, G> last;
-    load_page<D, G>(last, p.pages + (size_t)id * hstride + hoff, n, r);
+    load_page<D, G>(last, p.pages + (size_t)id * hstride + hoff, true, p.block_bytes, n, r);
     page_step(last, pf, false);
   }
 
