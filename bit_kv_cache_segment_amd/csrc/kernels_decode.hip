@@ -269,6 +269,7 @@ struct HistSmem {
   float zsum[W][16][NG];
   alignas(16) float M[W][GQ];
   float L[W][GQ];
+  alignas(16) float Mb[16];             // block maximum per head: max of the waves' M
   alignas(16) float mT[D][qpad(GQ)];    // block-merged accumulators (rotated basis), head-interleaved
   uint32_t rec[query_record_words<D, GQ>()]; // the pair's query record
   int32_t ids[kIdCache];                // page ids of a segment of the split
@@ -787,6 +788,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     sm.win.app_slot_done = sm.win.app_page_done = 0;
   }
   for (int idx = tid; idx < W * 16; idx += NT) sm.alpha[idx / 16][idx % 16] = 1.f;
+  if (tid < 16) sm.Mb[tid] = -INFINITY;
   __builtin_amdgcn_s_waitcnt(0); // the direct loads of R_K have landed
   __syncthreads();
 
@@ -1080,32 +1082,26 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     if (n == 0 && hrow < GQ) {
       sm.M[w][hrow] = m_run[rt];
       sm.L[w][hrow] = l;
+      __hip_atomic_fetch_max(&sm.Mb[hrow], m_run[rt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
       for (int g = 0; g < NG; ++g) sm.zsum[w][hrow][g] = z[g];
     }
   }
   __syncthreads(); // every wave has left the loop: P' may be overwritten
   {
-    // heads 4 r + i of this lane's accumulator rows
+    // heads 4 r + i of this lane's accumulator rows: the block maximum and
+    // this wave's (two shared-memory reads, not one per wave)
     float mb[4], mw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mb[i] = mw[i] = -INFINITY;
-    for (int ww = 0; ww < W; ++ww) {
-      float mm[4];
-      if constexpr (GQ % 4 == 0) {
-        const float4 t = *(const float4 *)&sm.M[ww][4 * r];
-        mm[0] = t.x;
-        mm[1] = t.y;
-        mm[2] = t.z;
-        mm[3] = t.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mm[i] = 4 * r + i < GQ ? sm.M[ww][4 * r + i] : -INFINITY;
-      }
+    if constexpr (GQ % 4 == 0) {
+      const float4 tb = *(const float4 *)&sm.Mb[4 * r];
+      const float4 tw = *(const float4 *)&sm.M[w][4 * r];
+      mb[0] = tb.x, mb[1] = tb.y, mb[2] = tb.z, mb[3] = tb.w;
+      mw[0] = tw.x, mw[1] = tw.y, mw[2] = tw.z, mw[3] = tw.w;
+    } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        mb[i] = fmaxf(mb[i], mm[i]);
-        if (ww == w) mw[i] = mm[i];
+        mb[i] = 4 * r + i < GQ ? sm.Mb[4 * r + i] : -INFINITY;
+        mw[i] = 4 * r + i < GQ ? sm.M[w][4 * r + i] : -INFINITY;
       }
     }
     const float unscale = ldexpf(1.f, 24 - p.pv_shift);
@@ -1129,8 +1125,8 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     sm.mT[j][h] = a;
   }
   if (tid < GQ) {
-    float m = -INFINITY, l = 0.f;
-    for (int ww = 0; ww < W; ++ww) m = fmaxf(m, sm.M[ww][tid]);
+    const float m = sm.Mb[tid];
+    float l = 0.f;
     for (int ww = 0; ww < W; ++ww)
       if (sm.M[ww][tid] != -INFINITY) l = fmaf(exp2f(sm.M[ww][tid] - m), sm.L[ww][tid], l);
     dst[(size_t)tid * (D + 2) + D] = m;
