@@ -69,3 +69,29 @@ def check_rows(out_gpu, st, q_bits, w, rows):
     err = oracle.row_rel_err(got[rows], ref[rows])
     assert err <= TOL, f"row-relative error {err:.3e} > {TOL}"
     return err
+
+
+def check_evicted(pool, w, seqs, lengths, count):
+    """Every kv head of each sequence in `seqs`: the last `count` history
+    entries (the tokens the latest appends evicted) bit-exact against the
+    oracle's encoding of those tokens alone.  lengths[b]: length now.
+    Returns the number of (token, kv head, K|V) encodings compared."""
+    RK, RV, cK, cV = oracle_tables(w)
+    checked = 0
+    for b in seqs:
+        n_hist = max(0, int(lengths[b]) - oracle.WINDOW)
+        c = min(count, n_hist)
+        if c <= 0:
+            continue
+        first = n_hist - c
+        codes, params = pool.export_history(b, first, c)
+        pos0 = oracle.SINK + first
+        toks = [synth.bf16_bits(synth.kv_tokens(w, kind, b, pos0, c)) for kind in (0, 1)]
+        for h in range(w.num_kv_heads):
+            for kvi, (R, clip) in enumerate(((RK, cK), (RV, cV))):
+                pk, s16, z16 = oracle.encode(toks[kvi][:, h], R[h], clip[h], w.group_size)
+                assert np.array_equal(codes[:, h, kvi], pk), (b, h, kvi)
+                assert np.array_equal(params[:, h, kvi, :, 0], s16), (b, h, kvi)
+                assert np.array_equal(params[:, h, kvi, :, 1], z16), (b, h, kvi)
+                checked += c
+    return checked

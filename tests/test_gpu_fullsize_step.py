@@ -1,0 +1,143 @@
+"""GPU parity of the serving step (oscar_decode_step, the call the benchmark
+times) at full workload sizes and on plans no smaller test reaches:
+
+* the 16 x 32K and 32 x 64K layers, several steps through the fused step:
+  every page table, every evicted token of every (sequence, kv head) pair
+  bit-exact, sampled attention rows within 2e-3;
+* a mid-size fused step whose pairs are cut into two splits, so a history
+  block runs beside the window block that appends and the window block
+  reads the evicted token's page after the append has written it;
+* a split holding more than 1024 history pages, so the page ids are staged
+  in several segments, in both pool modes (pages handed out dynamically or
+  in a fixed order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_segment_amd as ok
+import harness
+import oracle
+import synth
+from gpu_common import check_evicted, check_history_codes, check_rows, check_windows, oracle_sequence
+
+pytestmark = pytest.mark.gpu
+
+
+def _pool(w, lengths, extra, flags=0, seed=None):
+    RK, RV, cK, cV = harness.tables(w)
+    cfg = harness.config_for(w, lengths, extra_tokens=extra, flags=flags, seed=seed)
+    pool = ok.Pool(cfg, RK, RV, cK, cV, max_batch=len(lengths))
+    harness.prefill_all(pool, w, lengths)
+    m = oracle.PoolModel(cfg.num_pages, cfg.page_shuffle_seed, cfg.max_pages_per_seq)
+    for b, L in enumerate(lengths):
+        m.prefill(b, int(L))
+    return pool, m
+
+
+def _rows_of(w, kv):
+    return list(range(kv * w.gqa, (kv + 1) * w.gqa))
+
+
+@pytest.mark.parametrize("name,steps", [("qwen3_8b_32k", 3), ("qwen3_32b_64k", 2)])
+def test_fused_step_at_full_size(name, steps):
+    w = synth.WORKLOADS[name]
+    lengths = [int(x) for x in synth.lengths(w)]
+    pool, m = _pool(w, lengths, extra=steps)
+    ids = list(range(w.batch))
+    rng = np.random.default_rng(w.config_id + 700)
+    for step in range(1, steps + 1):
+        k_new, v_new = harness.step_tokens(w, lengths)
+        q = synth.queries(w, step, device="cuda").view(torch.uint16)
+        print(f"{name}: step {step}, lengths {lengths[0]}..{max(lengths)}", flush=True)
+        out = pool.step(ids, k_new, v_new, q)
+        m.append(ids)
+        lengths = [L + 1 for L in lengths]
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        for b in ids:
+            assert list(pool.page_table(b)) == m.table[b]
+        n = check_evicted(pool, w, ids, lengths, 1)
+        assert n == w.batch * w.num_kv_heads * 2
+        qb = synth.bf16_bits(synth.queries(w, step))
+        pair = (int(rng.integers(0, w.batch)), int(rng.integers(0, w.num_kv_heads)))
+        for b, kv in {pair, (w.batch - 1, w.num_kv_heads - 1)}:
+            st, _, _ = oracle_sequence(w, b, lengths[b], heads=[kv])
+            err = check_rows(out[b], st, qb[b], w, _rows_of(w, kv))
+            print(f"  pair {(b, kv)}: row-relative error {err:.2e}", flush=True)
+    # the whole history of the sequences, one kv head each, at the end
+    for b, kv in ((0, 0), (w.batch - 1, w.num_kv_heads - 1)):
+        st, k, v = oracle_sequence(w, b, lengths[b], heads=[kv])
+        check_history_codes(pool, w, b, st, [kv])
+        check_windows(pool, w, b, lengths[b], k, v, [kv])
+
+
+@pytest.mark.parametrize("d,G", [(128, 128), (64, 64)])
+def test_fused_step_with_two_splits_per_pair(d, G):
+    # Three sequences of about 8K tokens, one kv head: every pair is cut into
+    # two splits (the window's split keeps the page the append writes).
+    w = synth.Workload(f"two_split_d{d}", 40 + d // 64, 3, 4, 1, d, G, 0, 0)
+    lengths = [8000, 8255, 8256]
+    steps = 70
+    pool, m = _pool(w, lengths, extra=steps)
+    ids = [2, 0, 1]
+    for step in range(1, steps + 1):
+        k_new, v_new = harness.step_tokens(w, lengths, ids)
+        q = synth.queries(w, step, device="cuda", batch=3)
+        qo = q[torch.as_tensor(ids, device="cuda")].contiguous().view(torch.uint16)
+        out = pool.step(ids, k_new, v_new, qo)
+        m.append(ids)
+        lengths = [L + 1 for L in lengths]
+        torch.cuda.synchronize()
+        check_evicted(pool, w, range(3), lengths, 1)
+        if step % 10 == 0 or step <= 2:
+            qb = synth.bf16_bits(q.cpu())
+            for i, b in enumerate(ids):
+                st, _, _ = oracle_sequence(w, b, lengths[b])
+                check_rows(out[i], st, qb[b], w, list(range(w.num_q_heads)))
+    for b in range(3):
+        assert list(pool.page_table(b)) == m.table[b]
+        st, k, v = oracle_sequence(w, b, lengths[b])
+        check_history_codes(pool, w, b, st, [0])
+        check_windows(pool, w, b, lengths[b], k, v, [0])
+
+
+@pytest.mark.parametrize("flags", [0, ok.POOL_DETERMINISTIC], ids=["dynamic", "deterministic"])
+def test_split_of_more_than_1024_pages(flags):
+    # 300 sequences of 134,000-136,000 tokens (about 2,100 pages each), one
+    # kv head: a launch holds 256 sequences, whose pairs fill the device's
+    # resident block slots, so each split keeps at least half of its pair's
+    # pages (more than 1024) and its page ids are staged in several segments.
+    # Decode, then two fused steps.
+    n = 300
+    w = synth.Workload("long_splits", 45, n, 2, 1, 64, 64, 134000, 136000)
+    lengths = [int(x) for x in synth.lengths(w)]
+    assert min(lengths) >= 134000
+    pool, m = _pool(w, lengths, extra=2, flags=flags)
+    ids = list(range(n))
+    sample = [0, 255, 256, n - 1] if flags == 0 else [1, 299]
+    q = synth.queries(w, 0, device="cuda").view(torch.uint16)
+    print(f"decode, flags {flags}", flush=True)
+    out = pool.decode(ids, q)
+    torch.cuda.synchronize()
+    qb = synth.bf16_bits(synth.queries(w, 0))
+    for b in sample:
+        st, _, _ = oracle_sequence(w, b, lengths[b])
+        check_rows(out[b], st, qb[b], w, [0, 1])
+    for step in (1, 2):
+        k_new, v_new = harness.step_tokens(w, lengths)
+        q = synth.queries(w, step, device="cuda").view(torch.uint16)
+        print(f"step {step}", flush=True)
+        out = pool.step(ids, k_new, v_new, q)
+        m.append(ids)
+        lengths = [L + 1 for L in lengths]
+        torch.cuda.synchronize()
+        check_evicted(pool, w, ids, lengths, 1)
+    for b in ids:
+        assert list(pool.page_table(b)) == m.table[b]
+    qb = synth.bf16_bits(synth.queries(w, 2))
+    for b in sample:
+        st, k, v = oracle_sequence(w, b, lengths[b])
+        check_rows(out[b], st, qb[b], w, [0, 1])
+    st, k, v = oracle_sequence(w, sample[-1], lengths[sample[-1]])
+    check_history_codes(pool, w, sample[-1], st, [0])

@@ -1,7 +1,8 @@
-"""GPU parity at the full workload sizes, in the launch configuration the
-benchmark times: whole page tables, sampled (sequence, kv head) pairs
-compared bit-exactly on their codes and within 2e-3 on attention, and the
-256-step fused serving run."""
+"""GPU parity at the full workload sizes: whole page tables, sampled
+(sequence, kv head) pairs compared bit-exactly on their codes and within
+2e-3 on attention, and the 256-step serving run through oscar_decode_step
+(the call the benchmark times) with every evicted token of every pair
+compared bit-exactly at the end."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import bit_kv_cache_segment_amd as ok
 import harness
 import oracle
 import synth
-from gpu_common import check_history_codes, check_rows, check_windows, oracle_sequence
+from gpu_common import check_evicted, check_history_codes, check_rows, check_windows, oracle_sequence
 
 pytestmark = pytest.mark.gpu
 
@@ -65,16 +66,18 @@ def test_fused_serving_steps():
     checks = {1, 64, 128, 256}
     for step in range(1, w.steps + 1):
         k_new, v_new = harness.step_tokens(w, lengths)
-        pool.append(ids, k_new, v_new)
+        q = synth.queries(w, step, device="cuda").view(torch.uint16)
+        out = pool.step(ids, k_new, v_new, q)
         m.append(ids)
         for b in ids:
             lengths[b] += 1
-        q = synth.queries(w, step, device="cuda").view(torch.uint16)
-        out = pool.decode(ids, q)
         if step in checks:
             torch.cuda.synchronize()
             for b in ids:
                 assert list(pool.page_table(b)) == m.table[b]
             pair = (int(rng.integers(0, w.batch)), int(rng.integers(0, w.num_kv_heads)))
             err = _sampled_check(pool, w, lengths, out, step, [pair])
-            print(f"step {step}: pair {pair} error {err:.2e}")
+            print(f"step {step}: pair {pair} error {err:.2e}", flush=True)
+    # every token the 256 steps evicted, of every (sequence, kv head) pair
+    n = check_evicted(pool, w, ids, lengths, w.steps)
+    assert n == w.batch * w.num_kv_heads * 2 * w.steps

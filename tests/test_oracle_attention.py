@@ -1,6 +1,7 @@
 """Pins of the oracle's attention: brute force on tiny inputs, the textbook
 routine, the online-softmax merge, and the rotation conventions."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -126,3 +127,33 @@ def test_tiny_workload_sequence_end_to_end():
     q2[1] = q2[0]
     out2 = oracle.attend_sequence(st, q2, 1 / math.sqrt(w.head_dim))
     assert np.array_equal(out2[0], out2[1])
+
+
+def _golden_cases(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    cases, cur = [], {}
+    with open(path) as f:
+        for ln in f:
+            ln = ln.strip()
+            if not ln or ln.startswith("#"):
+                continue
+            key, val = ln.split(":", 1)
+            cur[key] = val.strip()
+            if key == "expect":
+                cases.append(cur)
+                cur = {}
+    return cases
+
+
+def _rows(text):
+    return np.array([[float(x) for x in r.split()] for r in text.split("|")])
+
+
+def test_row_relative_error_hand_worked():
+    # the parity metric of every attention check, against hand-worked cases
+    cases = _golden_cases("row_rel_err.txt")
+    assert len(cases) == 4
+    for c in cases:
+        num, den = (int(x) for x in c["expect"].split("/"))
+        got = oracle.row_rel_err(_rows(c["got"]), _rows(c["ref"]))
+        assert got == pytest.approx(num / den, rel=1e-15, abs=0.0), c

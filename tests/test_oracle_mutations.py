@@ -175,6 +175,23 @@ def _bad_append(self, seq_ids):
         self.length[s_] = L + 1
 
 
+def _rel_err_variant(kind):
+    def f(got, ref):
+        got = np.asarray(got, dtype=np.float64).reshape(-1, ref.shape[-1])
+        ref = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
+        diff = np.abs(got - ref)
+        if kind == "global":
+            return float(diff.max() / np.abs(ref).max())
+        if kind == "got":
+            return float((diff.max(axis=1) / np.abs(got).max(axis=1)).max())
+        if kind == "mean":
+            return float((diff.max(axis=1) / np.abs(ref).max(axis=1)).mean())
+        if kind == "l2":
+            return float((np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)).max())
+        return float((diff.max(axis=1) / ref.max(axis=1)).max())  # signed maximum
+    return f
+
+
 PY_MISTAKES = {
     "bit reversal left out": ("bitrev", lambda i, bits: i),
     "Hadamard sign from popcount(i | j)": ("hadamard_unnormalized", _bad_hadamard),
@@ -189,6 +206,11 @@ PY_MISTAKES = {
     "recent ring of 255 slots": ("ring_slot", lambda pos: (pos - oracle.SINK) % 255),
     "bits per element with one fp16 parameter": ("bits_per_element",
                                                  lambda L, G: (max(0, L - oracle.WINDOW) * (2 + 16 / G) + min(L, oracle.WINDOW) * 16) / L),
+    "row error as one ratio over all rows": ("row_rel_err", _rel_err_variant("global")),
+    "row error relative to the result, not the reference": ("row_rel_err", _rel_err_variant("got")),
+    "row errors averaged instead of the largest": ("row_rel_err", _rel_err_variant("mean")),
+    "row error in Euclidean norms": ("row_rel_err", _rel_err_variant("l2")),
+    "row error over the signed maximum of the reference": ("row_rel_err", _rel_err_variant("signed")),
 }
 
 
