@@ -1,11 +1,13 @@
 """Benchmark of the OSCAR INT2-KV decode hot path on one MI355X.
 
-One step = one pass of the whole path over the batch: append one token per
-sequence (evicting the oldest recent token into the INT2 history: rotate,
-clip, quantize, pack) and decode attention for one query per sequence
-(INT2 split-KV + BF16 window + online-softmax merge + de-rotation).
-Steps rotate over several layer pools so the read set exceeds the 256 MB
-Infinity Cache.  Prints one JSON line.
+One step = one pass of the whole path over the batch through
+oscar_decode_step: append one token per sequence (evicting the oldest recent
+token into the INT2 history: rotate, clip, quantize, pack) and decode
+attention for one query per sequence (INT2 split-KV + BF16 window +
+online-softmax merge + de-rotation).  The default workload is the largest
+one that fits a GPU: the serving step of 64 sequences of 4K-64K tokens
+(32 query / 8 kv heads, d 128).  Steps rotate over several layer pools so
+the read set exceeds the 256 MB Infinity Cache.  Prints one JSON line.
 """
 import argparse
 import hashlib
@@ -53,57 +55,113 @@ def traffic_record(kernel_src, workload):
     return float(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, lengths, budget_s):
-    """The CPU oracle on a bounded sample of the same step: for a few
-    (sequence, kv head) pairs, encode the evicted K and V token and attend all
-    g query heads over the decoded pool (dequantize + de-rotate the history,
-    fp64 softmax attention).  Encoding the prompt's history is setup."""
+def _cpu_pair(task):
+    """One (sequence, kv head) pair of the oracle's step, in a worker process
+    (one thread): encode the pair's prompt history (setup, untimed), then the
+    step itself, timed: encode the evicted K and V token and attend all g
+    query heads over the decoded pool (dequantize and de-rotate the history,
+    fp64 softmax attention)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
     import synth
 
-    RK = oracle.rotation(synth.random_orthogonal_u(w, 0))
-    RV = oracle.rotation(synth.random_orthogonal_u(w, 1))
-    cal = [synth.bf16_bits(synth.calibration_tokens(w, k, 4096)) for k in (0, 1)]
-    cK = np.stack([oracle.clip_thresholds(cal[0][h], RK[h]) for h in range(w.num_kv_heads)])
-    cV = np.stack([oracle.clip_thresholds(cal[1][h], RV[h]) for h in range(w.num_kv_heads)])
-    q = synth.bf16_bits(synth.queries(w, 0))
-    g, d, G = w.gqa, w.head_dim, w.group_size
-    timed, pairs = 0.0, 0
-    order = [(b, kv) for kv in range(w.num_kv_heads) for b in range(w.batch)]
+    name, b, kv, L = task
+    w = synth.WORKLOADS[name]
     with threadpool_limits(limits=1):
-        for b, kv in order:
-            L = int(lengths[b])
-            k = synth.bf16_bits(synth.kv_tokens(w, 0, b, 0, L + 1, heads=[kv]))[:, 0]
-            v = synth.bf16_bits(synth.kv_tokens(w, 1, b, 0, L + 1, heads=[kv]))[:, 0]
-            n_hist = max(0, L + 1 - 320)
-            hk = oracle.encode(k[64:64 + n_hist - 1], RK[kv], cK[kv], G) if n_hist > 1 else None
-            hv = oracle.encode(v[64:64 + n_hist - 1], RV[kv], cV[kv], G) if n_hist > 1 else None
-            t0 = time.perf_counter()
-            # the step: evict one token per K/V, then decode-then-attend
-            ek = oracle.encode(k[64 + n_hist - 1:64 + n_hist], RK[kv], cK[kv], G)
-            ev = oracle.encode(v[64 + n_hist - 1:64 + n_hist], RV[kv], cV[kv], G)
-            pk = np.concatenate([hk[0], ek[0]]); sk = np.concatenate([hk[1], ek[1]]); zk = np.concatenate([hk[2], ek[2]])
-            pv = np.concatenate([hv[0], ev[0]]); sv = np.concatenate([hv[1], ev[1]]); zv = np.concatenate([hv[2], ev[2]])
-            K = oracle.bf16_bits_to_f64(k)
-            V = oracle.bf16_bits_to_f64(v)
-            K[64:64 + n_hist] = oracle.decode_history(pk, sk, zk, G, RK[kv])
-            V[64:64 + n_hist] = oracle.decode_history(pv, sv, zv, G, RV[kv])
-            qf = oracle.bf16_bits_to_f64(q[b])
-            for h in range(kv * g, (kv + 1) * g):
-                oracle.attention(qf[h], K, V, 1 / math.sqrt(d))
-            timed += time.perf_counter() - t0
-            pairs += 1
-            if timed >= budget_s:
+        import torch
+        torch.set_num_threads(1)
+        RK, RV, cK, cV = _cpu_tables(name)
+        g, d, G = w.gqa, w.head_dim, w.group_size
+        q = synth.bf16_bits(synth.queries(w, 0))
+        k = synth.bf16_bits(synth.kv_tokens(w, 0, b, 0, L + 1, heads=[kv]))[:, 0]
+        v = synth.bf16_bits(synth.kv_tokens(w, 1, b, 0, L + 1, heads=[kv]))[:, 0]
+        n_hist = max(0, L + 1 - 320)
+        hk = oracle.encode(k[64:64 + n_hist - 1], RK[kv], cK[kv], G) if n_hist > 1 else None
+        hv = oracle.encode(v[64:64 + n_hist - 1], RV[kv], cV[kv], G) if n_hist > 1 else None
+        t0 = time.perf_counter()
+        ek = oracle.encode(k[64 + n_hist - 1:64 + n_hist], RK[kv], cK[kv], G)
+        ev = oracle.encode(v[64 + n_hist - 1:64 + n_hist], RV[kv], cV[kv], G)
+        cat = (lambda a, e: e if a is None else tuple(np.concatenate([x, y]) for x, y in zip(a, e)))
+        pk, sk, zk = cat(hk, ek)
+        pv, sv, zv = cat(hv, ev)
+        K = oracle.bf16_bits_to_f64(k)
+        V = oracle.bf16_bits_to_f64(v)
+        K[64:64 + n_hist] = oracle.decode_history(pk, sk, zk, G, RK[kv])
+        V[64:64 + n_hist] = oracle.decode_history(pv, sv, zv, G, RV[kv])
+        qf = oracle.bf16_bits_to_f64(q[b])
+        for h in range(kv * g, (kv + 1) * g):
+            oracle.attention(qf[h], K, V, 1 / math.sqrt(d))
+        return time.perf_counter() - t0
+
+
+_tables_cache = {}
+
+
+def _cpu_tables(name):
+    """The oracle's own rotation and clip tables (built once per worker)."""
+    if name not in _tables_cache:
+        import numpy as np
+
+        import oracle
+        import synth
+        w = synth.WORKLOADS[name]
+        RK = oracle.rotation(synth.random_orthogonal_u(w, 0))
+        RV = oracle.rotation(synth.random_orthogonal_u(w, 1))
+        cal = [synth.bf16_bits(synth.calibration_tokens(w, k, 4096)) for k in (0, 1)]
+        cK = np.stack([oracle.clip_thresholds(cal[0][h], RK[h]) for h in range(w.num_kv_heads)])
+        cV = np.stack([oracle.clip_thresholds(cal[1][h], RV[h]) for h in range(w.num_kv_heads)])
+        _tables_cache[name] = (RK, RV, cK, cV)
+    return _tables_cache[name]
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, lengths, budget_s, max_workers=16):
+    """The CPU oracle on a bounded sample of one step, on the host's cores:
+    (sequence, kv head) pairs in worker processes (one thread each), spread
+    over the batch, until about budget_s seconds of timed step work are done.
+    Each worker processes pairs independently, so the host's step time is the
+    mean timed seconds per pair x pairs / workers.  Runs before anything
+    touches the GPU; the workers are fresh interpreters that never do."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_workers))
+    rng = np.random.default_rng(7)
+    pairs = [(int(i) // w.num_kv_heads, int(i) % w.num_kv_heads) for i in rng.permutation(w.batch * w.num_kv_heads)]
+    tasks = [(w.name, b, kv, int(lengths[b])) for b, kv in pairs]
+    done, timed = 0, 0.0
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(cores) as pool:
+        for t in pool.imap_unordered(_cpu_pair, tasks):
+            timed += t
+            done += 1
+            if timed >= budget_s and done >= cores:
+                pool.terminate()
                 break
-    if pairs == 0:
+    wall = time.perf_counter() - t0
+    if done == 0:
         return None
-    t_step = timed / pairs * w.batch * w.num_kv_heads
-    return {"value": w.batch / t_step, "unit": "tokens/s per layer", "cores": 1, "kind": "oracle",
-            "sample": f"{pairs} of {w.batch * w.num_kv_heads} (sequence, kv head) pairs of one step "
-                      f"({timed:.1f} s, 1 thread), scaled to the whole batch"}
+    t_step = timed / done * (w.batch * w.num_kv_heads) / cores
+    sample_len = sorted({int(lengths[b]) for b, _ in pairs[:done]})
+    return {"value": w.batch / t_step, "unit": "tokens/s per layer", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.num_kv_heads} (sequence, kv head) pairs of one step "
+                      f"(lengths {sample_len[0]}..{sample_len[-1]}), {timed:.1f} s of timed oracle work on "
+                      f"{cores} worker processes of one thread each ({wall:.1f} s wall with setup); "
+                      f"step time = mean per pair x {w.batch * w.num_kv_heads} pairs / {cores}",
+            "host": {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}}
 
 
 def main():
@@ -111,9 +169,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_8b_32k")
+    ap.add_argument("--workload", default="fused_64x_4k_64k",
+                    help="the largest workload by default: 64 sequences of 4K-64K tokens, 32/8 heads")
     ap.add_argument("--layers", type=int, default=4)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="0 skips the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="seconds of timed oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events (roofline fields become null)")
     ap.add_argument("--separate-calls", action="store_true",
@@ -130,16 +190,21 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    lengths0 = [int(x) for x in synth.lengths(w)]
+    # the CPU baseline first, before this process touches the GPU
+    cpu = cpu_baseline(w, lengths0, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
     import torch
 
     import bit_kv_cache_segment_amd as ok
     import harness
-    import synth
 
-    w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    lengths0 = [int(x) for x in synth.lengths(w)]
     total_steps = args.warmup + args.steps
     appends_per_layer = -(-total_steps // args.layers)
     RK, RV, cK, cV = harness.tables(w)
@@ -212,7 +277,6 @@ def main():
     traffic = traffic_record(os.path.join(ROOT, "bit_kv_cache_segment_amd", "csrc", "kernels_decode.hip"),
                              w.name)
     value = w.batch / (ms_step * 1e-3)
-    cpu = cpu_baseline(w, lengths0, args.cpu_seconds) if args.cpu_seconds > 0 else None
     step_bytes = bytes_launch + w.batch * w.num_q_heads * w.head_dim * 4
     res = {
         "metric": "INT2-KV decode attention tokens/s per layer + achieved HBM GB/s (% peak)",
@@ -228,8 +292,11 @@ def main():
         "dtype": "int2 codes + fp16 scale/zero history, bf16 windows, fp32 accumulate",
         "data": "synthetic (seeded; K/V ~ N(0,1) with 4 outlier channels x20)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
-                   "head_dim": w.head_dim, "group_size": w.group_size, "context": lengths0[0],
-                   "layer_pools": args.layers, "parallelism": "none (1 GPU)"},
+                   "head_dim": w.head_dim, "group_size": w.group_size,
+                   "context_min": min(lengths0), "context_max": max(lengths0),
+                   "context_mean": float(np.mean(lengths0)),
+                   "appended_per_pool": appends_per_layer, "layer_pools": args.layers,
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "decode_main_kernel", "bytes_per_launch": bytes_launch,
