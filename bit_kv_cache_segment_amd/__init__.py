@@ -30,7 +30,8 @@ _NAMES = {EHIP: "EHIP", ENOMEM: "ENOMEM", EINVAL: "EINVAL", ERANGE: "ERANGE"}
 # every symbol include/oscar.h declares
 EXPORTS = (
     "oscar_pool_bytes", "oscar_decode_workspace_bytes", "oscar_pool_create", "oscar_pool_destroy",
-    "oscar_prefill", "oscar_append_evict", "oscar_decode_attn", "oscar_decode_step", "oscar_release_seq",
+    "oscar_prefill", "oscar_append_evict", "oscar_decode_attn", "oscar_decode_step",
+    "oscar_decode_step_static", "oscar_release_seq",
     "oscar_seq_length", "oscar_page_table", "oscar_free_pages", "oscar_export_history",
     "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
     "oscar_profile_end", "oscar_last_error",
@@ -87,6 +88,7 @@ def lib() -> ctypes.CDLL:
             "oscar_append_evict": [_P, _P, _I32, _P, _P, _P],
             "oscar_decode_attn": [_P, _P, _I32, _P, _P, ctypes.c_float, _P, _SZ, _P],
             "oscar_decode_step": [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _SZ, _P],
+            "oscar_decode_step_static": [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P],
             "oscar_release_seq": [_P, _I32],
             "oscar_seq_length": [_P, _I32, _P],
             "oscar_page_table": [_P, _I32, _P, _I32, _P],
@@ -191,6 +193,12 @@ def oscar_decode_step(h, seq_ids, k_new, v_new, q, out, softmax_scale: float, wo
     _check(lib().oscar_decode_step(h, _np_ptr(ids), len(ids), _dev_ptr(k_new), _dev_ptr(v_new), _dev_ptr(q),
                                    _dev_ptr(out), float(softmax_scale), _dev_ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def oscar_decode_step_static(h, seq_ids, k_new, v_new, q, out, softmax_scale: float, stream=None):
+    ids = _ids(seq_ids)
+    _check(lib().oscar_decode_step_static(h, _np_ptr(ids), len(ids), _dev_ptr(k_new), _dev_ptr(v_new),
+                                          _dev_ptr(q), _dev_ptr(out), float(softmax_scale), _stream(stream)))
 
 
 def oscar_release_seq(h, seq: int):
@@ -331,6 +339,16 @@ class Pool:
         if softmax_scale is None:
             softmax_scale = 1.0 / float(np.sqrt(self.cfg.head_dim))
         oscar_decode_step(self.handle, seq_ids, k_new, v_new, q, out, softmax_scale, self.workspace, stream)
+        return out
+
+    def step_static(self, seq_ids, k_new, v_new, q, out=None, softmax_scale=None, stream=None):
+        """step() with the library's static workspace (oscar_decode_step_static)."""
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if softmax_scale is None:
+            softmax_scale = 1.0 / float(np.sqrt(self.cfg.head_dim))
+        oscar_decode_step_static(self.handle, seq_ids, k_new, v_new, q, out, softmax_scale, stream)
         return out
 
     def length(self, seq):

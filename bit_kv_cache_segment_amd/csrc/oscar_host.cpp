@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -105,6 +106,42 @@ Layout layout_of(const oscar_pool_config &c) {
 int pages_for(int64_t n_hist) { return (int)((n_hist + kPage - 1) / kPage); }
 
 } // namespace
+
+// ---------------------------------------------------------------------------
+// Static decode workspace, for callers that cannot allocate device memory
+// (oscar_decode_step_static): the same partials a caller's workspace holds,
+// in a file-scope device array of kStaticScratchBytes on every GPU the
+// library runs on, kept until the process ends.  Host code never uses the
+// array's name as an address: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is
+// kept per device.  Every call on a GPU shares that GPU's array, so calls
+// that overlap on one GPU (on different streams) race; calls on one stream
+// are ordered.  Nothing in it needs clearing: each launch writes every
+// partial it reads.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+hipError_t oscar::static_scratch(void **ptr, size_t *bytes) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
+}
 
 // Event pairs for per-kernel timing (oscar_profile_begin / _end).
 struct Profiler {
@@ -287,6 +324,15 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
       return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "querying the decode occupancy");
     }
     p->decode_slots = cus * per_cu;
+    // set-up of the static decode workspace on this device (its address is
+    // looked up here, once per device, not in the step that uses it)
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    e = static_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "static decode workspace");
+    }
   }
   *out = p;
   return ok();
@@ -468,9 +514,13 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   return ok();
 }
 
-int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
-                      const uint16_t *v_new, const uint16_t *q, float *out, float softmax_scale,
-                      void *workspace, size_t workspace_bytes, void *stream) {
+} // extern "C"
+
+// The decode step with a given workspace: the caller's (oscar_decode_step)
+// or the library's static one (oscar_decode_step_static, `fixed`).
+static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
+                       const uint16_t *v_new, const uint16_t *q, float *out, float softmax_scale,
+                       void *workspace, size_t workspace_bytes, void *stream, bool fixed) {
   if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
   if (p->host_only) return fail(OSCAR_EINVAL, "decode step on a host-only pool");
   if (n < 0) return fail(OSCAR_EINVAL, "n = %d < 0", n);
@@ -506,8 +556,12 @@ int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     }
     if (fused || pass == 1) break;
   }
-  if (workspace_bytes < need)
+  if (workspace_bytes < need) {
+    if (fixed)
+      return fail(OSCAR_EINVAL, "this step needs %zu bytes of decode workspace, more than the %zu bytes of the "
+                  "library's static workspace; use oscar_decode_step with a caller workspace", need, workspace_bytes);
     return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  }
   if (!fused) {
     int rc = oscar_append_evict(p, seq_ids, n, k_new, v_new, stream);
     if (rc) return rc;
@@ -552,6 +606,26 @@ int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   }
   p->compact();
   return ok();
+}
+
+extern "C" {
+
+int oscar_decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
+                      const uint16_t *v_new, const uint16_t *q, float *out, float softmax_scale,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_step(p, seq_ids, n, k_new, v_new, q, out, softmax_scale, workspace, workspace_bytes, stream, false);
+}
+
+int oscar_decode_step_static(oscar_pool *p, const int32_t *seq_ids, int32_t n, const uint16_t *k_new,
+                             const uint16_t *v_new, const uint16_t *q, float *out, float softmax_scale,
+                             void *stream) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (p->host_only) return fail(OSCAR_EINVAL, "decode step on a host-only pool");
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  hipError_t e = static_scratch(&ws, &ws_bytes);
+  if (e != hipSuccess) return hip_fail(e, "static decode workspace");
+  return decode_step(p, seq_ids, n, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, stream, true);
 }
 
 int oscar_release_seq(oscar_pool *p, int32_t seq) {

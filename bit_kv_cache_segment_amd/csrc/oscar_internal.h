@@ -189,4 +189,9 @@ inline size_t decode_ws_floats(int Hq, int d, int n, int Hkv, int smax, int g) {
   return (size_t)n * Hq * (d + 2) + (size_t)n * Hkv * smax * g * (d + 2);
 }
 
+// Device address and size of the library's static decode workspace on the
+// current device (oscar_decode_step_static).  The address is looked up once
+// per device and kept; later calls only read it.
+hipError_t static_scratch(void **ptr, size_t *bytes);
+
 } // namespace oscar

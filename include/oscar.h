@@ -30,7 +30,8 @@
  *     a failing call changes no host or device state;
  *   - "device" pointers are HIP device memory owned by the caller; "host"
  *     pointers are ordinary host memory owned by the caller; the library
- *     never allocates device memory and never frees caller memory;
+ *     never calls hipMalloc and never frees caller memory (its only device
+ *     memory of its own is the static workspace of oscar_decode_step_static);
  *   - `stream` is a hipStream_t (NULL = the default stream); device work is
  *     enqueued asynchronously on it unless stated otherwise;
  *   - bf16 and fp16 values are passed as their uint16_t bit patterns;
@@ -177,6 +178,25 @@ int oscar_decode_step(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
                       const uint16_t *k_new, const uint16_t *v_new,
                       const uint16_t *q, float *out, float softmax_scale,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* oscar_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, with the decode partials in the library's
+ * static workspace instead of a caller workspace.  That workspace is one
+ * 32 MiB device array per GPU the library runs on, held until the process
+ * ends; its address is looked up when a pool is created on the device (or
+ * at the first such call on another device).  The call allocates nothing.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams at once) race and give undefined results; calls on
+ * one stream are ordered.
+ *   Arguments as oscar_decode_step, without workspace.
+ * Errors: those of oscar_decode_step; EINVAL when the step's workspace
+ * (what oscar_decode_workspace_bytes would require for its plan) exceeds
+ * 32 MiB, before anything changes; EHIP. */
+int oscar_decode_step_static(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
+                             const uint16_t *k_new, const uint16_t *v_new,
+                             const uint16_t *q, float *out, float softmax_scale,
+                             void *stream);
 
 /* Return a sequence's pages to the back of the free list (in page-table
  * order) and set its length to 0.  Host only.  Errors: EINVAL. */
