@@ -88,12 +88,26 @@ __device__ __forceinline__ float lanes_sum(float v) {
   return v;
 }
 
-// Maximum over aligned groups of 16 lanes (one DPP row), in every lane.
-__device__ __forceinline__ float row16_max_dpp(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  return fmaxf(v, dpp_f<0x140>(v));
+// Maximum over aligned groups of 16 lanes (one DPP row), in every lane, of
+// values that are not NaN.  It runs on order-preserving integer keys (the
+// bits of a non-negative float; the magnitude bits flipped for a negative
+// one), so each step is one integer max with a DPP operand: a float max
+// would canonicalise the DPP result first (two more instructions per step).
+__device__ __forceinline__ int fkey(float f) {
+  const int i = __float_as_int(f);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float row16_max_dpp(float f) {
+  int v = fkey(f);
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  return __int_as_float(fkey(__int_as_float(v)));  // the key map is its own inverse
 }
 // Value of lane k (wave-uniform result).
 __device__ __forceinline__ float lane_f(float v, int k) {
@@ -874,11 +888,12 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     pfac[T] = ldexpf(1.f, p.pv_shift - 2 * ee);
   }
 
-  float m_run[RT], l_run[RT], zs[RT][NG];
+  float m_run[RT], thr[RT], l_run[RT], zs[RT][NG];
   v4f acc[NJ];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m_run[rt] = -INFINITY;
+    thr[rt] = -INFINITY;
     l_run[rt] = 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) zs[rt][g] = 0.f;
@@ -917,8 +932,9 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   #pragma unroll
           for (int g = 0; g < NG; ++g) {
             // |dv| < 2^31: the limb sum is exact in wrapping int32 arithmetic
-            const float dv = (float)(int)((uint32_t)cacc[rt][g][0] + ((uint32_t)cacc[rt][g][1] << 8) +
-                                          ((uint32_t)cacc[rt][g][2] << 16));
+            // (c0 + 2^8 (c1 + 2^8 c2): two shift-and-add instructions)
+            const uint32_t hi = ((uint32_t)cacc[rt][g][2] << 8) + (uint32_t)cacc[rt][g][1];
+            const float dv = (float)(int)((hi << 8) + (uint32_t)cacc[rt][g][0]);
             const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
             // the logit in units of kfac (a power of two; the softmax below
             // applies it), so the products are those of kfac * logit exactly
@@ -928,19 +944,48 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
         }
       }
 
-      // ---- online softmax over the page (per head: 16 lanes x 4 tokens)
+      // ---- online softmax over the page (per head: 16 lanes x 4 tokens).
+      // The running reference m_run of a head moves only when the page's
+      // maximum exceeds it by more than kLazy: weights stay <= 2^kLazy and
+      // the PV accumulators are rescaled rarely.  Each lane compares its own
+      // maximum with that threshold (kept in logit units, thr = (m_run +
+      // kLazy) / kfac, exact: kfac is a power of two); only on the (rare)
+      // pages where some lane exceeds it are the row maxima, the new
+      // references, their rescale factors and the factors' trip through
+      // shared memory computed.
+      bool any_jump = false;
+      float lmax[RT], alpha[RT];
+  #pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        lmax[rt] = fmaxf(fmaxf(lg[rt][0], lg[rt][1]), fmaxf(lg[rt][2], lg[rt][3]));
+        any_jump = any_jump || lmax[rt] > thr[rt];
+        alpha[rt] = 1.f;
+      }
+      any_jump = __any(any_jump);
+      if (any_jump) {
+  #pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float mt = row16_max_dpp(lmax[rt]) * kfac[rt];
+          const bool jump = mt > m_run[rt] + kLazy;
+          const float mnew = jump ? mt : m_run[rt];
+          alpha[rt] = jump ? fast_exp2(m_run[rt] - mnew) : 1.f;
+          m_run[rt] = mnew;
+          thr[rt] = (mnew + kLazy) / kfac[rt];
+        }
+      }
+      // V scale times the token factor of P' (exact: pfac is a power of
+      // two), once per token for all row tiles
+      float spf[NG][4];
+      if constexpr (RT > 1) {
+  #pragma unroll
+        for (int T = 0; T < 4; ++T)
+  #pragma unroll
+          for (int g = 0; g < NG; ++g) spf[g][T] = fmaf(f16lo(cur.vp[(T * NG + g) / 4][(T * NG + g) % 4]), pfac[T], 0.f);
+      }
   #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int hrow = rt * 4 + r;
-        float mt = fmaxf(fmaxf(lg[rt][0], lg[rt][1]), fmaxf(lg[rt][2], lg[rt][3]));
-        mt = row16_max_dpp(mt) * kfac[rt];
-        // The running reference moves only when a page's maximum exceeds it
-        // by more than kLazy: weights stay <= 2^kLazy and the PV accumulators
-        // are rescaled rarely.
-        const bool jump = mt > m_run[rt] + kLazy;
-        const float mnew = jump ? mt : m_run[rt];
-        const float alpha = jump ? fast_exp2(m_run[rt] - mnew) : 1.f;
-        m_run[rt] = mnew;
+        const float mnew = m_run[rt];
         float psum = 0.f;
         float zadd[NG];
   #pragma unroll
@@ -955,15 +1000,16 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
           for (int g = 0; g < NG; ++g) {
             const uint32_t sz = cur.vp[(T * NG + g) / 4][(T * NG + g) % 4];
             zadd[g] = ok ? fmaf(pt, f16hi(sz), zadd[g]) : zadd[g];
-            // (an fma with a zero addend: one mixed-precision instruction,
-            // the same single rounding as the product)
-            pv[g][T] = ok ? fmaf(f16lo(sz), pt * pfac[T], 0.f) : 0.f;
+            // (an fma with a zero addend: one mixed-precision instruction
+            // that rounds the product once, to fp16)
+            if constexpr (RT > 1) pv[g][T] = ok ? fmaf(pt, spf[g][T], 0.f) : 0.f;
+            else pv[g][T] = ok ? fmaf(f16lo(sz), pt * pfac[T], 0.f) : 0.f;
           }
         }
-        l_run[rt] = fmaf(l_run[rt], alpha, psum);
+        l_run[rt] = fmaf(l_run[rt], alpha[rt], psum);
   #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          zs[rt][g] = fmaf(zs[rt][g], alpha, zadd[g]);
+          zs[rt][g] = fmaf(zs[rt][g], alpha[rt], zadd[g]);
           if (hrow < GQ) {
             union {
               _Float16 h[4];
@@ -974,14 +1020,14 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
             *(u32x2 *)&sm.u.P[w][g][hrow][4 * n] = pk.u;
           }
         }
-        if (n == 0 && hrow < GQ) sm.alpha[w][hrow] = alpha;
+        if (any_jump && n == 0 && hrow < GQ) sm.alpha[w][hrow] = alpha[rt];
       }
       wave_sync();
 
-      // ---- rescale the PV accumulators when some row's max moved
-      const v4f a4 = *(const v4f *)&sm.alpha[w][4 * r];
-      const bool moved = a4[0] != 1.f || a4[1] != 1.f || a4[2] != 1.f || a4[3] != 1.f;
-      if (__any(moved)) {
+      // ---- rescale the PV accumulators when some row's reference moved
+      // (rows whose reference stayed have alpha 1)
+      if (any_jump) {
+        const v4f a4 = *(const v4f *)&sm.alpha[w][4 * r];
   #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[j] *= a4;
       }
