@@ -29,11 +29,11 @@ _NAMES = {EHIP: "EHIP", ENOMEM: "ENOMEM", EINVAL: "EINVAL", ERANGE: "ERANGE"}
 
 # every symbol include/oscar.h declares
 EXPORTS = (
-    "oscar_pool_bytes", "oscar_decode_workspace_bytes", "oscar_pool_create", "oscar_pool_destroy",
+    "oscar_pool_bytes", "oscar_pool_required_bytes", "oscar_decode_workspace_bytes", "oscar_pool_create", "oscar_pool_destroy",
     "oscar_prefill", "oscar_append_evict", "oscar_decode_attn", "oscar_decode_step",
-    "oscar_decode_step_static", "oscar_release_seq",
+    "oscar_decode_step_static", "oscar_pool_check", "oscar_release_seq",
     "oscar_seq_length", "oscar_page_table", "oscar_free_pages", "oscar_export_history",
-    "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
+    "oscar_export_state", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
     "oscar_profile_end", "oscar_last_error",
 )
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "oscar_pool_bytes": [_P, _P],
+            "oscar_pool_required_bytes": [_P, _P, _P],
             "oscar_decode_workspace_bytes": [_P, _I32, _P],
             "oscar_pool_create": [_P, _P, _SZ, _P, _P, _P, _P, _P, _P],
             "oscar_pool_destroy": [_P],
@@ -89,11 +90,13 @@ def lib() -> ctypes.CDLL:
             "oscar_decode_attn": [_P, _P, _I32, _P, _P, ctypes.c_float, _P, _SZ, _P],
             "oscar_decode_step": [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _SZ, _P],
             "oscar_decode_step_static": [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P],
+            "oscar_pool_check": [_P, _P],
             "oscar_release_seq": [_P, _I32],
             "oscar_seq_length": [_P, _I32, _P],
             "oscar_page_table": [_P, _I32, _P, _I32, _P],
             "oscar_free_pages": [_P, _P],
             "oscar_export_history": [_P, _I32, _I32, _I32, _P, _P, _P],
+            "oscar_export_state": [_P, _I32, _P, _P, _P, _P],
             "oscar_export_window": [_P, _I32, _P, _P, _P, _P, _P],
             "oscar_build_rotation": [_I32, _P, _P],
             "oscar_calibrate_clip": [_I32, ctypes.c_int64, _P, _P, ctypes.c_double, _P],
@@ -146,6 +149,13 @@ def oscar_pool_bytes(cfg: PoolConfig) -> int:
     n = ctypes.c_size_t()
     _check(lib().oscar_pool_bytes(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
+
+
+def oscar_pool_required_bytes(cfg: PoolConfig):
+    """(device bytes of the pool, decode workspace bytes for a full launch)."""
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().oscar_pool_required_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def oscar_decode_workspace_bytes(cfg: PoolConfig, max_batch: int) -> int:
@@ -201,6 +211,10 @@ def oscar_decode_step_static(h, seq_ids, k_new, v_new, q, out, softmax_scale: fl
                                           _dev_ptr(q), _dev_ptr(out), float(softmax_scale), _stream(stream)))
 
 
+def oscar_pool_check(h, stream=None, host_only=False):
+    _check(lib().oscar_pool_check(h, None if host_only else _stream(stream)))
+
+
 def oscar_release_seq(h, seq: int):
     _check(lib().oscar_release_seq(h, seq))
 
@@ -230,6 +244,16 @@ def oscar_export_history(h, seq: int, first: int, count: int, Hkv: int, d: int, 
     params = np.zeros((count, Hkv, 2, d // G, 2), dtype=np.uint16)
     _check(lib().oscar_export_history(h, seq, first, count, _np_ptr(codes), _np_ptr(params), _stream(stream)))
     return codes, params
+
+
+def oscar_export_state(h, seq: int, max_pages: int, codes_dev, params_dev, stream=None) -> np.ndarray:
+    """Enqueue the device export of a sequence's history (canonical layout) into
+    codes_dev (uint8) / params_dev (uint16) device tensors; returns the page-table
+    row (int32 [max_pages], -1 past its end)."""
+    table = np.zeros(max(max_pages, 1), dtype=np.int32)
+    _check(lib().oscar_export_state(h, seq, _np_ptr(table), _dev_ptr(codes_dev), _dev_ptr(params_dev),
+                                    _stream(stream)))
+    return table[:max_pages]
 
 
 def oscar_export_window(h, seq: int, Hkv: int, d: int, stream=None):
@@ -350,6 +374,10 @@ class Pool:
             softmax_scale = 1.0 / float(np.sqrt(self.cfg.head_dim))
         oscar_decode_step_static(self.handle, seq_ids, k_new, v_new, q, out, softmax_scale, stream)
         return out
+
+    def check(self, stream=None):
+        """oscar_pool_check: raises OscarError(EHIP) if a decode wait gave up."""
+        oscar_pool_check(self.handle, stream, host_only=self.host_only)
 
     def length(self, seq):
         return oscar_seq_length(self.handle, seq)

@@ -481,12 +481,18 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
 __device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 __device__ __forceinline__ float f16_val(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-// Bounded wait for a shared-memory counter (every wave reaches its end).
-__device__ __forceinline__ void wait_count(int *c, int target) {
-  for (int it = 0; it < (1 << 22); ++it) {
+// Bounded wait for a shared-memory counter (every wave reaches its end):
+// at most p.wait_limit polls.  A wait that gives up is not silent: lane 0
+// of the wave ORs kStatusWaitGaveUp into the pool's status word (a vector
+// atomic), which the host turns into an error at its next synchronising
+// call; the wave then goes on, so the block still ends.
+__device__ __forceinline__ void wait_count(int *c, int target, const PoolDev &p) {
+  for (int it = 0; it < p.wait_limit; ++it) {
     if (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
     __builtin_amdgcn_s_sleep(2);
   }
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(p.status, kStatusWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void publish(int *c, int lane) {
   __builtin_amdgcn_s_waitcnt(0); // this wave's stores and atomics have completed
@@ -643,7 +649,7 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
     if (threadIdx.x == 0) sm.app_slot_done = sm.app_page_done = 0;
     __syncthreads();
     if (w < 2) fused_append_slot<D, GQ, W>(sm, p, b, in, e, kv, w, threadIdx.x & 63);
-    wait_count(&sm.app_slot_done, 2);
+    wait_count(&sm.app_slot_done, 2, p);
   }
   window_waves<D, G, GQ, W>(sm, p, b, q, qscale, e, kv, w);
   __syncthreads();
@@ -852,7 +858,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     finish_prologue();
     if (b.fused) {
       if (w < 2) fused_append_slot<D, GQ, WW>(sm.win, p, b, in, e, kv, w, lane);
-      wait_count(&sm.win.app_slot_done, 2);
+      wait_count(&sm.win.app_slot_done, 2, p);
     }
     window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
     if (b.fused && w < 2) fused_append_page<D, G, GQ, WW>(sm.win, sm.R, p, b, e, kv, w, lane);
@@ -1091,7 +1097,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   if (pf < p1 && w == W - 1) {
     int id;
     if (fused_evict) {
-      wait_count(&sm.win.app_page_done, 2);
+      wait_count(&sm.win.app_page_done, 2, p);
       // the evicted token started this page: its id is not in the table yet
       id = (n_hist - 1) % kPage == 0 ? b.new_page[e] : ptab[pf];
     } else {
@@ -1113,7 +1119,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     uint32_t order = 0;
     if (lane == 0) order = atomicAdd(&sm.exited, 1u);
     if (__builtin_amdgcn_readlane(order, 0) == 0) {
-      if (b.fused && with_window) wait_count(&sm.win.app_page_done, 2);
+      if (b.fused && with_window) wait_count(&sm.win.app_page_done, 2, p);
       stage_table<D>(sm.R, p.RVt + (size_t)kv * D * D, 0, 1, lane);
       __builtin_amdgcn_s_waitcnt(0); // the copy has landed before the barrier below
     }

@@ -245,6 +245,63 @@ __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// Export of a sequence's history in the canonical layout (device to device):
+// one thread per output word.  Threads [0, nc) write code dwords: word
+// (i, h, kind, w) holds canonical bytes 4w .. 4w + 3 of history entry i,
+// i.e. channels 16w .. 16w + 15, four per byte, the first in the low bits.
+// Threads [nc, nc + np) write the fp16 (scale, zero) pair of (i, h, kind,
+// group).  Every read stays inside the entry's (page, head) block.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ void export_state_kernel(PoolDev p, int seq, int n_hist, uint32_t *__restrict__ codes,
+                                    uint32_t *__restrict__ params) {
+  constexpr int CW = D / 16, NG = D / G; // code dwords and groups per (entry, head, kind)
+  const long Hkv = p.Hkv;
+  const long nc = (long)n_hist * Hkv * 2 * CW, np = (long)n_hist * Hkv * 2 * NG;
+  const long x = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= nc + np) return;
+  const bool is_code = x < nc;
+  const long y = is_code ? x : x - nc;
+  const int per = is_code ? CW : NG;
+  const int w = (int)(y % per);
+  const long ihk = y / per;
+  const int kind = (int)(ihk % 2);
+  const int h = (int)((ihk / 2) % Hkv);
+  const int i = (int)(ihk / (2 * Hkv));
+  const int t = i % kPage;
+  const int page = p.page_table[(size_t)seq * p.maxp + i / kPage];
+  const uint8_t *blk = p.pages + ((size_t)page * Hkv + h) * p.block_bytes;
+  if (!is_code) {
+    params[y] = *(const uint32_t *)(blk + (kind ? vparam_off(D, G, t, w) : kparam_off(D, G, t, w)));
+    return;
+  }
+  uint32_t out = 0;
+  if (kind == 0) {
+    // channels 16 w + k, k < 16: one K code dword (quad r, 64-channel block m)
+    const uint32_t kw = *(const uint32_t *)(blk + kcode_dword_off(D, t, w % 4, w / 4));
+    out = kw; // channel 16 w + k at bits 2k, as the canonical bytes hold it
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t vw = *(const uint32_t *)(blk + vcode_dword_off(D, t / 16, 16 * w + k));
+      out |= ((vw >> vbit(t % 16)) & 3u) << (2 * k);
+    }
+  }
+  codes[y] = out;
+}
+
+template <int D, int G>
+hipError_t export_impl(const PoolDev &p, int seq, int n_hist, uint8_t *codes, uint16_t *params, hipStream_t s) {
+  const long total = (long)n_hist * p.Hkv * 2 * (D / 16 + D / G);
+  const int threads = 256;
+  const long blocks = (total + threads - 1) / threads;
+  if (blocks > 0)
+    hipLaunchKernelGGL((export_state_kernel<D, G>), dim3((unsigned)blocks), dim3(threads), 0, s, p, seq, n_hist,
+                       (uint32_t *)codes, (uint32_t *)params);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t prefill_impl(const PoolDev &p, int seq, const uint16_t *k, const uint16_t *v, int L, hipStream_t s) {
   const int n_hist = max(0, L - kWindow);
@@ -275,6 +332,13 @@ hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const ui
   if (p.d == 128 && p.G == 128) return prefill_impl<128, 128>(p, seq, k, v, L, s);
   if (p.d == 128 && p.G == 64) return prefill_impl<128, 64>(p, seq, k, v, L, s);
   if (p.d == 64 && p.G == 64) return prefill_impl<64, 64>(p, seq, k, v, L, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_export(const PoolDev &p, int seq, int n_hist, uint8_t *codes, uint16_t *params, hipStream_t s) {
+  if (p.d == 128 && p.G == 128) return export_impl<128, 128>(p, seq, n_hist, codes, params, s);
+  if (p.d == 128 && p.G == 64) return export_impl<128, 64>(p, seq, n_hist, codes, params, s);
+  if (p.d == 64 && p.G == 64) return export_impl<64, 64>(p, seq, n_hist, codes, params, s);
   return hipErrorInvalidValue;
 }
 

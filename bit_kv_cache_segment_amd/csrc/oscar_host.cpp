@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -48,7 +49,7 @@ int hip_fail(hipError_t e, const char *what) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t RK, RV, RVt, clipK, clipV, page_table, sinkK, sinkV, recentK, recentV, pages, total;
+  size_t RK, RV, RVt, clipK, clipV, status, page_table, sinkK, sinkV, recentK, recentV, pages, total;
 };
 
 int validate_config(const oscar_pool_config *c) {
@@ -93,6 +94,7 @@ Layout layout_of(const oscar_pool_config &c) {
   L.RVt = take(H * d * d * 4);
   L.clipK = take(H * d * 4);
   L.clipV = take(H * d * 4);
+  L.status = take(4);
   L.page_table = take(S * (size_t)c.max_pages_per_seq * 4);
   L.sinkK = take(S * H * kSink * d * 2);
   L.sinkV = take(S * H * kSink * d * 2);
@@ -197,6 +199,21 @@ struct oscar_pool {
   }
 };
 
+// The pool's device status word, read once the work enqueued so far has
+// completed (the caller has synchronised): EHIP if a bounded wait inside a
+// decode block gave up, which leaves that step's results, and possibly the
+// evicted token's codes, undefined.  The word is sticky.
+static int check_device_status(oscar_pool *p) {
+  if (p->host_only) return OSCAR_OK;
+  uint32_t st = 0;
+  hipError_t e = hipMemcpy(&st, p->dev.status, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the pool status");
+  if (st & kStatusWaitGaveUp)
+    return fail(OSCAR_EHIP, "a bounded wait inside a decode step gave up (status 0x%x): the results of the "
+                "steps since the pool was created may be wrong", st);
+  return OSCAR_OK;
+}
+
 extern "C" {
 
 const char *oscar_last_error(void) { return g_err.c_str(); }
@@ -206,6 +223,18 @@ int oscar_pool_bytes(const oscar_pool_config *cfg, size_t *device_bytes) {
   if (rc) return rc;
   if (!device_bytes) return fail(OSCAR_EINVAL, "device_bytes is NULL");
   *device_bytes = layout_of(*cfg).total;
+  return ok();
+}
+
+int oscar_pool_required_bytes(const oscar_pool_config *cfg, size_t *device_bytes, size_t *workspace_bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!device_bytes || !workspace_bytes) return fail(OSCAR_EINVAL, "NULL output");
+  size_t ws = 0;
+  rc = oscar_decode_workspace_bytes(cfg, std::min(cfg->max_seqs, kMaxBatch), &ws);
+  if (rc) return rc;
+  *device_bytes = layout_of(*cfg).total;
+  *workspace_bytes = ws;
   return ok();
 }
 
@@ -275,6 +304,15 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
   D.block_bytes = block_bytes_for(d, cfg->group_size);
   D.pv_shift = 0;
   D.deterministic = (cfg->flags & OSCAR_POOL_DETERMINISTIC) ? 1 : 0;
+  // Polls of a bounded wait inside a decode block before it gives up (and
+  // reports it).  OSCAR_WAIT_SPIN_LIMIT overrides the default, so that a
+  // test can force a give-up: 0 gives up at once.
+  D.wait_limit = kDefaultWaitLimit;
+  if (const char *env = std::getenv("OSCAR_WAIT_SPIN_LIMIT")) {
+    char *end = nullptr;
+    const long v = std::strtol(env, &end, 10);
+    if (end != env && v >= 0 && v <= (1L << 30)) D.wait_limit = (int32_t)v;
+  }
   if (!host_only) {
     // V scales never exceed fp16(2 c / 3) for the largest V threshold c and
     // the decode's softmax weights never exceed 2^8 (its lazy max); keep
@@ -298,6 +336,7 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
     D.recentK = (uint16_t *)(b + lay.recentK);
     D.recentV = (uint16_t *)(b + lay.recentV);
     D.pages = (uint8_t *)(b + lay.pages);
+    D.status = (uint32_t *)(b + lay.status);
     std::vector<float> rvt((size_t)H * d * d);
     for (int h = 0; h < H; ++h)
       for (int i = 0; i < d; ++i)
@@ -310,6 +349,8 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
     if (e == hipSuccess) e = hipMemcpyAsync((void *)D.RVt, rvt.data(), rb, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync((void *)D.clipK, clip_K, cb, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync((void *)D.clipV, clip_V, cb, hipMemcpyHostToDevice, s);
+    static const uint32_t zero = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync((void *)D.status, &zero, 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
       delete p;
@@ -628,6 +669,15 @@ int oscar_decode_step_static(oscar_pool *p, const int32_t *seq_ids, int32_t n, c
   return decode_step(p, seq_ids, n, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, stream, true);
 }
 
+int oscar_pool_check(oscar_pool *p, void *stream) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (p->host_only) return ok();
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pool check sync");
+  const int rc = check_device_status(p);
+  return rc ? rc : ok();
+}
+
 int oscar_release_seq(oscar_pool *p, int32_t seq) {
   int rc = check_seq(p, seq);
   if (rc) return rc;
@@ -679,6 +729,7 @@ int oscar_export_history(oscar_pool *p, int32_t seq, int32_t first, int32_t coun
   const int bb = p->dev.block_bytes;
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "export sync");
+  if ((rc = check_device_status(p))) return rc;
   std::vector<uint8_t> page((size_t)H * bb);
   int cur = -1;
   for (int64_t i = first; i < first + count; ++i) {
@@ -712,6 +763,26 @@ int oscar_export_history(oscar_pool *p, int32_t seq, int32_t first, int32_t coun
   return ok();
 }
 
+int oscar_export_state(oscar_pool *p, int32_t seq, int32_t *page_table_host, void *codes_dev, void *params_dev,
+                       void *stream) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (p->host_only) return fail(OSCAR_EINVAL, "export from a host-only pool");
+  if (!page_table_host) return fail(OSCAR_EINVAL, "page_table_host is NULL");
+  const int64_t n_hist = std::max(0, p->len[seq] - kWindow);
+  if (n_hist > 0 && (!codes_dev || !params_dev)) return fail(OSCAR_EINVAL, "NULL output buffer");
+  if (n_hist > 0 && ((uintptr_t)codes_dev % 4 || (uintptr_t)params_dev % 4))
+    return fail(OSCAR_EINVAL, "output buffers must be 4-byte aligned");
+  if (n_hist > 0) {
+    hipError_t e = launch_export(p->dev, seq, (int)n_hist, (uint8_t *)codes_dev, (uint16_t *)params_dev,
+                                 (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "export launch");
+  }
+  const auto &row = p->table[seq];
+  for (int i = 0; i < p->cfg.max_pages_per_seq; ++i) page_table_host[i] = i < (int)row.size() ? row[i] : -1;
+  return ok();
+}
+
 int oscar_export_window(oscar_pool *p, int32_t seq, uint16_t *sink_k, uint16_t *sink_v,
                         uint16_t *recent_k, uint16_t *recent_v, void *stream) {
   int rc = check_seq(p, seq);
@@ -721,6 +792,7 @@ int oscar_export_window(oscar_pool *p, int32_t seq, uint16_t *sink_k, uint16_t *
   const int H = p->cfg.num_kv_heads, d = p->cfg.head_dim;
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "export sync");
+  if ((rc = check_device_status(p))) return rc;
   struct Part {
     const uint16_t *src;
     uint16_t *dst;
@@ -783,6 +855,19 @@ int oscar_profile_end(oscar_pool *p, oscar_profile *out) {
       }
       ms[k] += t;
     }
+  {
+    // the status of every launch so far
+    hipError_t r = hipDeviceSynchronize();
+    if (r != hipSuccess) {
+      p->prof.release();
+      return hip_fail(r, "synchronising");
+    }
+    const int rc = check_device_status(p);
+    if (rc) {
+      p->prof.release();
+      return rc;
+    }
+  }
   out->n_decode_main = p->prof.used[0];
   out->ms_decode_main = ms[0];
   out->n_decode_merge = p->prof.used[1];

@@ -37,7 +37,16 @@ struct PoolDev {
   // 1: the waves of a decode block take their pages in a fixed order, so
   // results are bitwise reproducible; 0: pages are handed out dynamically.
   int32_t deterministic;
+  // Bounded waits inside a decode block (a wave waiting for another wave of
+  // the block) poll at most wait_limit times; one that gives up ORs
+  // kStatusWaitGaveUp into *status, which the host reports at its next
+  // synchronising call.
+  int32_t wait_limit;
+  uint32_t *status;
 };
+
+constexpr uint32_t kStatusWaitGaveUp = 1u;
+constexpr int32_t kDefaultWaitLimit = 1 << 22;
 
 // ---------------------------------------------------------------------------
 // History page layout.  One page holds 64 consecutive history tokens of one
@@ -173,6 +182,9 @@ hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const ui
                           int L, hipStream_t s);
 hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t s, const KernelTimer &t);
+// History entries [0, n_hist) of a sequence in the canonical layout, device
+// to device (codes 4-byte aligned: d/4 is a multiple of 4).
+hipError_t launch_export(const PoolDev &p, int seq, int n_hist, uint8_t *codes, uint16_t *params, hipStream_t s);
 // Resident decode_main blocks per compute unit for this pool's shape.
 int decode_main_blocks_per_cu(const PoolDev &p);
 

@@ -92,6 +92,14 @@ typedef struct oscar_pool_config {
  * sequence slot, and num_pages history pages).  Host only. */
 int oscar_pool_bytes(const oscar_pool_config *cfg, size_t *device_bytes);
 
+/* Both sizes a pool needs, in one call: *device_bytes as oscar_pool_bytes,
+ * *workspace_bytes as oscar_decode_workspace_bytes for a batch of
+ * min(max_seqs, OSCAR_MAX_BATCH_PER_LAUNCH) sequences (a workspace of that
+ * size serves every decode call, which is cut into launches of at most that
+ * many).  Host only; allocates nothing.  Errors: EINVAL. */
+int oscar_pool_required_bytes(const oscar_pool_config *cfg, size_t *device_bytes,
+                              size_t *workspace_bytes);
+
 /* Bytes of device workspace oscar_decode_attn needs for batches of up to
  * max_batch sequences.  Host only. */
 int oscar_decode_workspace_bytes(const oscar_pool_config *cfg, int32_t max_batch,
@@ -198,6 +206,21 @@ int oscar_decode_step_static(oscar_pool *pool, const int32_t *seq_ids, int32_t n
                              const uint16_t *q, float *out, float softmax_scale,
                              void *stream);
 
+/* Wait for `stream` and report whether every decode step so far ran as
+ * specified.  Inside a decode launch some waves wait, bounded, for other
+ * waves of their block (the window waits for the appended token's slot, the
+ * pair's last page for the evicted token's codes, the de-rotation table for
+ * the append to finish with the rotation table).  A wait that reaches its
+ * bound gives up rather than hang, which leaves that step's attention, and
+ * possibly the evicted token's codes, undefined; it sets a sticky flag in
+ * the pool's device status word.  The bound is 2^22 polls (seconds), or the
+ * value of the environment variable OSCAR_WAIT_SPIN_LIMIT when the pool was
+ * created (0 gives up at once: a test hook).  oscar_export_history,
+ * oscar_export_window and oscar_profile_end check the flag too.
+ * Errors: EINVAL (NULL), EHIP (a wait gave up, or a HIP call failed).
+ * Host-only pools always pass. */
+int oscar_pool_check(oscar_pool *pool, void *stream);
+
 /* Return a sequence's pages to the back of the free list (in page-table
  * order) and set its length to 0.  Host only.  Errors: EINVAL. */
 int oscar_release_seq(oscar_pool *pool, int32_t seq);
@@ -218,14 +241,29 @@ int oscar_free_pages(const oscar_pool *pool, int32_t *n_free);
  *   codes:  uint8 [count][Hkv][2 (K,V)][d/4], four consecutive channels per
  *           byte, first channel in the low bits;
  *   params: uint16 [count][Hkv][2 (K,V)][d/G][2 (scale, zero)] fp16 bits.
- * Synchronous: waits for `stream`.  Errors: EINVAL (range, host-only), EHIP. */
+ * Synchronous: waits for `stream`.  Errors: EINVAL (range, host-only), EHIP
+ * (also when a bounded wait of a decode step gave up, see oscar_pool_check). */
 int oscar_export_history(oscar_pool *pool, int32_t seq, int32_t first, int32_t count,
                          uint8_t *codes, uint16_t *params, void *stream);
+
+/* A sequence's whole state in the canonical layout, without a host copy of
+ * the pages: its page-table row (host mirror) into page_table_host
+ * [max_pages_per_seq] (entries past the row set to -1), and, enqueued on
+ * `stream`, its n_hist = max(0, L - 320) history entries into
+ *   codes_dev:  device uint8 [n_hist][Hkv][2 (K,V)][d/4], four consecutive
+ *               channels per byte, the first in the low bits;
+ *   params_dev: device uint16 [n_hist][Hkv][2 (K,V)][d/G][2 (scale, zero)],
+ *               fp16 bits
+ * ([B]: the paged history, independent of where its pages sit).  Both
+ * buffers caller-owned, 4-byte aligned (may be NULL when n_hist = 0).
+ * Errors: EINVAL (bad seq, host-only pool, NULL or misaligned buffers), EHIP. */
+int oscar_export_state(oscar_pool *pool, int32_t seq, int32_t *page_table_host,
+                       void *codes_dev, void *params_dev, void *stream);
 
 /* Copy a sequence's BF16 windows to host memory: sink_k/sink_v
  * [64][Hkv][d] (slot = position) and recent_k/recent_v [256][Hkv][d]
  * (slot = (position - 64) mod 256); slots not holding a token are copied as
- * they are.  Synchronous.  Errors: EINVAL, EHIP. */
+ * they are.  Synchronous.  Errors: EINVAL, EHIP (as oscar_export_history). */
 int oscar_export_window(oscar_pool *pool, int32_t seq, uint16_t *sink_k,
                         uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v,
                         void *stream);
@@ -257,8 +295,9 @@ int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R
  * releases the events.  The events carry no system-scope fence (timing
  * only).  Each timed launch still starts a few microseconds after the
  * kernel before it, and the interval counts that gap, so time only the
- * kernels of interest, or a sample of their launches.  Errors: EINVAL,
- * EHIP. */
+ * kernels of interest, or a sample of their launches.  oscar_profile_end
+ * waits for the device and checks the pool status (oscar_pool_check).
+ * Errors: EINVAL, EHIP. */
 typedef struct oscar_profile {
     int32_t n_decode_main;   float ms_decode_main;   /* query prep, INT2 history, BF16 window */
     int32_t n_decode_merge;  float ms_decode_merge;  /* merge of the partials                 */

@@ -286,3 +286,41 @@ def test_decode_rejects_small_workspace_and_empty_sequence():
     with pytest.raises(ok.OscarError) as ei:
         pool.decode([0, 1], q)
     assert ei.value.code == ok.EINVAL
+
+
+@pytest.mark.parametrize("shape", ["g4_d128_G128", "g8_d128_G64", "g1_d64_G64"])
+def test_device_export_of_the_state_matches_host_export_and_oracle(shape):
+    # oscar_export_state (device gather into the canonical layout) against
+    # oscar_export_history (host copy of the pages) and the oracle, after
+    # prefill and a few fused steps; page-table rows against the host mirror
+    w = _workload(shape)
+    lengths = list(EDGE_LENS)
+    steps = 5
+    pool, cfg = _pool(w, lengths, extra=steps, slack=3)
+    harness.prefill_all(pool, w, lengths)
+    for step in range(1, steps + 1):
+        k_new, v_new = harness.step_tokens(w, lengths)
+        q = synth.queries(w, step, device="cuda", batch=len(lengths)).view(torch.uint16)
+        pool.step(list(range(len(lengths))), k_new, v_new, q)
+        lengths = [L + 1 for L in lengths]
+    Hkv, d, G = w.num_kv_heads, w.head_dim, w.group_size
+    for b, L in enumerate(lengths):
+        n_hist = max(0, L - 320)
+        codes = torch.full((max(n_hist, 1) * Hkv * 2 * d // 4,), 0xAB, dtype=torch.uint8, device="cuda")
+        params = torch.full((max(n_hist, 1) * Hkv * 2 * (d // G) * 2,), -1, dtype=torch.int16, device="cuda")
+        table = ok.oscar_export_state(pool.handle, b, cfg.max_pages_per_seq, codes, params)
+        torch.cuda.synchronize()
+        row = list(pool.page_table(b))
+        assert list(table[:len(row)]) == row and all(x == -1 for x in table[len(row):])
+        if n_hist == 0:
+            continue
+        c = codes.cpu().numpy()[: n_hist * Hkv * 2 * d // 4].reshape(n_hist, Hkv, 2, d // 4)
+        pr = params.cpu().numpy().view(np.uint16)[: n_hist * Hkv * 2 * (d // G) * 2].reshape(n_hist, Hkv, 2, d // G, 2)
+        hc, hp = pool.export_history(b, 0, n_hist)
+        assert np.array_equal(c, hc) and np.array_equal(pr, hp)
+        st, _, _ = oracle_sequence(w, b, L)
+        for h in range(Hkv):
+            for i, name in enumerate("KV"):
+                pk, s16, z16 = st.hist[(name, h)]
+                assert np.array_equal(c[:, h, i], pk)
+                assert np.array_equal(pr[:, h, i, :, 0], s16) and np.array_equal(pr[:, h, i, :, 1], z16)

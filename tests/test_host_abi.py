@@ -169,3 +169,30 @@ def test_offline_tables_bit_exact_with_oracle(name):
             c_lib = ok.oscar_calibrate_clip(cal[h], R_lib[h], 99.0)
             c_orc = oracle.clip_thresholds(cal[h], R_orc[h], 99.0)
             assert np.array_equal(c_lib.view(np.uint32), c_orc.view(np.uint32))
+
+
+def test_pool_check_on_host_only_pools_and_null():
+    p = _host_pool()
+    ok.oscar_pool_check(p.handle, host_only=True)  # nothing ran on a device
+    rc = ok.lib().oscar_pool_check(None, None)
+    assert rc == ok.EINVAL
+
+
+def test_pool_required_bytes_is_pool_plus_full_launch_workspace():
+    for max_seqs in (1, 6, 300):
+        cfg = ok.make_config(max_seqs, 32, 8, 128, 128, 100, 40, 5)
+        dev, ws = ok.oscar_pool_required_bytes(cfg)
+        assert dev == ok.oscar_pool_bytes(cfg)
+        assert ws == ok.oscar_decode_workspace_bytes(cfg, min(max_seqs, 256))
+    bad = ok.make_config(0, 32, 8, 128, 128, 100, 40, 5)
+    with pytest.raises(ok.OscarError) as ei:
+        ok.oscar_pool_required_bytes(bad)
+    assert ei.value.code == ok.EINVAL
+
+
+def test_export_state_refuses_host_only_pools():
+    p = _host_pool()
+    p.prefill_len(0, 500)
+    table = np.zeros(40, dtype=np.int32)
+    rc = ok.lib().oscar_export_state(p.handle, 0, table.ctypes.data_as(ok._P), None, None, None)
+    assert rc == ok.EINVAL
