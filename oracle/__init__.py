@@ -31,6 +31,9 @@ sanyangsrq.com, cited below as "the article"):
   to dequant(codes) . R^T.  ``partial_attention``/``merge_partials`` write
   out the online-softmax merge itself so that its equality with one softmax
   can be pinned.
+* prefill attention over the pool: each of the last n_q positions attends
+  causally (to itself and every earlier position) over the same decoded
+  pool.  ``prefill_attention``.
 
 Parity pins live in ``tests/test_oracle_*.py``.  Parity unpinned: the
 relation of the synthetic quantization error to the article's accuracy
@@ -455,6 +458,36 @@ def attend_sequence(st: SeqTokens, q_bf16: np.ndarray, scale: float, heads=None)
     for h in (range(Hq) if heads is None else heads):
         kv = h // g
         out[h] = attention(q[h], st.K[:, kv, :], st.V[:, kv, :], scale)
+    return out
+
+
+def prefill_attention(st: SeqTokens, q_bf16: np.ndarray, scale: float, heads=None) -> np.ndarray:
+    """Causal attention of the last n_q positions of a sequence over its pool
+    (prefill, or one chunk of a chunked prefill, over the three-segment pool:
+    article, section "From offline calibration to online inference").
+    Query i sits at position p = L - n_q + i and attends, with softmax, to
+    positions 0..p of the pool as it stands: sink and recent tokens as stored
+    (bf16), history tokens decoded (dequant . R^T).  q_bf16 uint16
+    [n_q][Hq][d]; returns fp64 [n_q][Hq][d]; kv head = h // (Hq/Hkv).
+
+    Written per head as one masked softmax: logits = scale q K^T over all L
+    tokens, positions after a query's own set to -inf, then softmax rows and
+    a product with V."""
+    n_q, Hq, d = q_bf16.shape
+    L = st.L
+    assert 1 <= n_q <= L
+    Hkv = st.K.shape[1]
+    g = Hq // Hkv
+    q = bf16_bits_to_f64(q_bf16)
+    pos = L - n_q + np.arange(n_q)
+    visible = np.arange(L)[None, :] <= pos[:, None]          # [n_q][L]
+    out = np.full((n_q, Hq, d), np.nan)
+    for h in (range(Hq) if heads is None else heads):
+        kv = h // g
+        logits = scale * (q[:, h, :] @ st.K[:, kv, :].T)      # [n_q][L]
+        logits = np.where(visible, logits, -np.inf)
+        w = np.exp(logits - logits.max(axis=1, keepdims=True))
+        out[:, h, :] = (w @ st.V[:, kv, :]) / w.sum(axis=1, keepdims=True)
     return out
 
 

@@ -157,3 +157,72 @@ def test_row_relative_error_hand_worked():
         num, den = (int(x) for x in c["expect"].split("/"))
         got = oracle.row_rel_err(_rows(c["got"]), _rows(c["ref"]))
         assert got == pytest.approx(num / den, rel=1e-15, abs=0.0), c
+
+
+def _random_sequence_tokens(L, Hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((L, Hkv, d))
+    V = rng.standard_normal((L, Hkv, d))
+    return oracle.SeqTokens(L, K, V, {})
+
+
+def _bf16(x):
+    return synth.bf16_bits(torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16))
+
+
+def test_prefill_attention_brute_force_tiny():
+    # every query attends to its own position and all earlier ones only
+    L, Hkv, g, d, n_q = 7, 2, 2, 4, 4
+    st = _random_sequence_tokens(L, Hkv, d, 11)
+    qb = _bf16(np.random.default_rng(12).standard_normal((n_q, Hkv * g, d)))
+    q = oracle.bf16_bits_to_f64(qb)
+    got = oracle.prefill_attention(st, qb, 0.6)
+    for i in range(n_q):
+        p = L - n_q + i
+        for h in range(Hkv * g):
+            ref = _brute(q[i, h], st.K[:p + 1, h // g], st.V[:p + 1, h // g], 0.6)
+            assert np.abs(got[i, h] - ref).max() <= 1e-13
+
+
+def test_prefill_attention_matches_torch_causal_sdpa_fp64():
+    # a prompt's full prefill (n_q = L) is textbook causal attention
+    L, Hkv, g, d = 40, 2, 4, 16
+    st = _random_sequence_tokens(L, Hkv, d, 13)
+    qb = _bf16(np.random.default_rng(14).standard_normal((L, Hkv * g, d)))
+    q = torch.from_numpy(oracle.bf16_bits_to_f64(qb)).permute(1, 0, 2)            # [Hq][L][d]
+    K = torch.from_numpy(st.K).permute(1, 0, 2).repeat_interleave(g, dim=0)       # [Hq][L][d]
+    V = torch.from_numpy(st.V).permute(1, 0, 2).repeat_interleave(g, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(q[None], K[None], V[None], is_causal=True,
+                                                           scale=0.25)[0].permute(1, 0, 2).numpy()
+    assert np.abs(oracle.prefill_attention(st, qb, 0.25) - ref).max() <= 1e-12
+    # a chunk (the last 9 positions) with the mask offset: torch's boolean mask
+    n_q = 9
+    mask = torch.arange(L)[None, :] <= (L - n_q + torch.arange(n_q))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q[None, :, L - n_q:], K[None], V[None], attn_mask=mask,
+                                                           scale=0.25)[0].permute(1, 0, 2).numpy()
+    assert np.abs(oracle.prefill_attention(st, qb[L - n_q:], 0.25) - ref).max() <= 1e-12
+
+
+def test_prefill_attention_last_query_is_decode_and_ignores_later_tokens():
+    w = synth.WORKLOADS["tiny"]
+    L, n_q = w.len_lo, 5
+    k = synth.bf16_bits(synth.kv_tokens(w, 0, 0, 0, L))
+    v = synth.bf16_bits(synth.kv_tokens(w, 1, 0, 0, L))
+    RK, RV = oracle.rotation(synth.random_orthogonal_u(w, 0)), oracle.rotation(synth.random_orthogonal_u(w, 1))
+    c = np.full((w.num_kv_heads, w.head_dim), 2.5, dtype=np.float32)
+    st = oracle.build_sequence(k, v, RK, RV, c, c, w.group_size)
+    qb = synth.bf16_bits(synth.queries(w, 0, batch=n_q))
+    got = oracle.prefill_attention(st, qb, 0.125)
+    # the last query sees the whole pool: decode attention
+    assert np.abs(got[-1] - oracle.attend_sequence(st, qb[-1], 0.125)).max() <= 1e-12
+    # each query equals decode attention over the prefix ending at its position
+    for i in range(n_q):
+        p = L - n_q + i
+        pre = oracle.SeqTokens(p + 1, st.K[:p + 1], st.V[:p + 1], {})
+        assert np.abs(got[i] - oracle.attend_sequence(pre, qb[i], 0.125)).max() <= 1e-12
+    # changing tokens after a query's position leaves it unchanged
+    st2 = oracle.SeqTokens(L, st.K.copy(), st.V.copy(), {})
+    st2.K[L - 2:] += 5.0
+    st2.V[L - 2:] -= 3.0
+    got2 = oracle.prefill_attention(st2, qb, 0.125)
+    assert np.array_equal(got2[: n_q - 2], got[: n_q - 2]) and not np.allclose(got2[-1], got[-1])

@@ -192,6 +192,30 @@ def _rel_err_variant(kind):
     return f
 
 
+def _prefill_variant(kind):
+    def f(st, q_bf16, scale, heads=None):
+        n_q, Hq, d = q_bf16.shape
+        L = st.L
+        g = Hq // st.K.shape[1]
+        q = oracle.bf16_bits_to_f64(q_bf16)
+        pos = (np.arange(n_q) if kind == "first" else L - n_q + np.arange(n_q))
+        if kind == "self":
+            visible = np.arange(L)[None, :] < pos[:, None]
+        elif kind == "late":
+            visible = np.arange(L)[None, :] <= pos[:, None] + 1
+        elif kind == "none":
+            visible = np.ones((n_q, L), dtype=bool)
+        else:
+            visible = np.arange(L)[None, :] <= pos[:, None]
+        out = np.full((n_q, Hq, d), np.nan)
+        for h in (range(Hq) if heads is None else heads):
+            logits = np.where(visible, scale * (q[:, h, :] @ st.K[:, h // g, :].T), -np.inf)
+            w = np.exp(logits - logits.max(axis=1, keepdims=True))
+            out[:, h, :] = (w @ st.V[:, h // g, :]) / w.sum(axis=1, keepdims=True)
+        return out
+    return f
+
+
 PY_MISTAKES = {
     "bit reversal left out": ("bitrev", lambda i, bits: i),
     "Hadamard sign from popcount(i | j)": ("hadamard_unnormalized", _bad_hadamard),
@@ -211,6 +235,10 @@ PY_MISTAKES = {
     "row errors averaged instead of the largest": ("row_rel_err", _rel_err_variant("mean")),
     "row error in Euclidean norms": ("row_rel_err", _rel_err_variant("l2")),
     "row error over the signed maximum of the reference": ("row_rel_err", _rel_err_variant("signed")),
+    "prefill query does not see its own position": ("prefill_attention", _prefill_variant("self")),
+    "prefill query sees one position too many": ("prefill_attention", _prefill_variant("late")),
+    "prefill queries taken at the first positions": ("prefill_attention", _prefill_variant("first")),
+    "prefill without the causal mask": ("prefill_attention", _prefill_variant("none")),
 }
 
 
