@@ -31,7 +31,8 @@ _NAMES = {EHIP: "EHIP", ENOMEM: "ENOMEM", EINVAL: "EINVAL", ERANGE: "ERANGE"}
 EXPORTS = (
     "oscar_pool_bytes", "oscar_pool_required_bytes", "oscar_decode_workspace_bytes", "oscar_pool_create", "oscar_pool_destroy",
     "oscar_prefill", "oscar_append_evict", "oscar_decode_attn", "oscar_decode_step",
-    "oscar_decode_step_static", "oscar_pool_check", "oscar_release_seq",
+    "oscar_decode_step_static", "oscar_prefill_workspace_bytes", "oscar_prefill_attn", "oscar_pool_check",
+    "oscar_release_seq",
     "oscar_seq_length", "oscar_page_table", "oscar_free_pages", "oscar_export_history",
     "oscar_export_state", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
     "oscar_profile_end", "oscar_last_error",
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
             "oscar_decode_attn": [_P, _P, _I32, _P, _P, ctypes.c_float, _P, _SZ, _P],
             "oscar_decode_step": [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _SZ, _P],
             "oscar_decode_step_static": [_P, _P, _I32, _P, _P, _P, _P, ctypes.c_float, _P],
+            "oscar_prefill_workspace_bytes": [_P, _I32, _P],
+            "oscar_prefill_attn": [_P, _I32, _I32, _P, _P, ctypes.c_float, _P, _SZ, _P],
             "oscar_pool_check": [_P, _P],
             "oscar_release_seq": [_P, _I32],
             "oscar_seq_length": [_P, _I32, _P],
@@ -209,6 +212,19 @@ def oscar_decode_step_static(h, seq_ids, k_new, v_new, q, out, softmax_scale: fl
     ids = _ids(seq_ids)
     _check(lib().oscar_decode_step_static(h, _np_ptr(ids), len(ids), _dev_ptr(k_new), _dev_ptr(v_new),
                                           _dev_ptr(q), _dev_ptr(out), float(softmax_scale), _stream(stream)))
+
+
+def oscar_prefill_workspace_bytes(cfg: PoolConfig, n_q: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().oscar_prefill_workspace_bytes(ctypes.byref(cfg), n_q, ctypes.byref(n)))
+    return n.value
+
+
+def oscar_prefill_attn(h, seq: int, q, out, softmax_scale: float, workspace, stream=None):
+    """q: device bf16 [n_q][Hq][d] (the last n_q positions' queries); out fp32, same shape."""
+    _check(lib().oscar_prefill_attn(h, seq, q.shape[0], _dev_ptr(q), _dev_ptr(out), float(softmax_scale),
+                                    _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
 
 
 def oscar_pool_check(h, stream=None, host_only=False):
@@ -373,6 +389,19 @@ class Pool:
         if softmax_scale is None:
             softmax_scale = 1.0 / float(np.sqrt(self.cfg.head_dim))
         oscar_decode_step_static(self.handle, seq_ids, k_new, v_new, q, out, softmax_scale, stream)
+        return out
+
+    def prefill_attn(self, seq, q, out=None, softmax_scale=None, workspace=None, stream=None):
+        """Causal attention of the last q.shape[0] positions of `seq` (oscar_prefill_attn)."""
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if softmax_scale is None:
+            softmax_scale = 1.0 / float(np.sqrt(self.cfg.head_dim))
+        if workspace is None:
+            n = oscar_prefill_workspace_bytes(self.cfg, q.shape[0])
+            workspace = torch.empty(max(n, 4) // 4, dtype=torch.float32, device=q.device)
+        oscar_prefill_attn(self.handle, seq, q, out, softmax_scale, workspace, stream)
         return out
 
     def check(self, stream=None):

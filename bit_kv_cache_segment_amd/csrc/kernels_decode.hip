@@ -153,6 +153,25 @@ __device__ __forceinline__ int karg_u16(const uint16_t *a, int i) {
   return (int)((((const uint32_t *)a)[i >> 1] >> (16 * (i & 1))) & 0xffffu);
 }
 
+// Prefill tiles (b.pf_g > 0): virtual head v of entry e is flat row
+// f = pf_flat0[e] + v: query i = f / g (g = b.pf_g) at position
+// len - n_q + i, query head kv g + f % g.  Rows past the call's queries are
+// not real (position -1: they see nothing, and nothing of theirs is
+// written).
+struct PfRow {
+  int query, head, pos;
+  bool real;
+};
+__device__ __forceinline__ PfRow pf_row(const DecodeBatch &b, int e, int kv, int v) {
+  const int g = b.pf_g, f = b.pf_flat0[e] + v, i = f / g;
+  PfRow r;
+  r.query = i;
+  r.head = kv * g + f % g;
+  r.real = i < b.pf_rows;
+  r.pos = r.real ? b.len[e] - b.pf_rows + i : -1;
+  return r;
+}
+
 // A D x D fp32 rotation table in shared memory: 1 KB chunks of 256 / D
 // rows, each followed by 16 pad floats, so that rows of chunks whose index
 // differs mod 4 start 16 banks apart.
@@ -354,7 +373,7 @@ constexpr int win_groups() {
 // Window tokens of one (sequence, kv head) processed by NW waves: wave wi
 // takes the token groups wi, wi + NW, ... and leaves its (m, l, acc) in
 // sm.M[wi], sm.L[wi], sm.A[wi] (a block merge combines the NW waves).
-template <int D, int G, int GQ, int NW>
+template <int D, int G, int GQ, int NW, bool PREFILL = false>
 __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
                              float qscale, int e, int kv, int wi) {
   constexpr int LPT = D / 8, TPI = 64 / LPT, WG = win_groups<D, G, GQ, NW>();
@@ -363,7 +382,19 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
   const int Hkv = p.Hkv, Hq = p.Hq;
   const int seq = b.seq[e], L = b.len[e];
   const int n_sink = min(L, kSink), n_rec = min(max(L - kSink, 0), kRecent), n_win = n_sink + n_rec;
-  {
+  const int n_hist = max(L - kWindow, 0);
+  int vpos[PREFILL ? GQ : 1]; // prefill: position of each head's query
+  if constexpr (PREFILL) {
+    // this wave's copy of the tile's query rows (zero for rows that are not real)
+    const int Hq_real = Hkv * b.pf_g;
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) vpos[h] = pf_row(b, e, kv, h).pos;
+    for (int idx = lane; idx < GQ * D / 2; idx += 64) {
+      const PfRow r = pf_row(b, e, kv, idx / (D / 2));
+      sm.q2[wi][idx / (D / 2)][idx % (D / 2)] =
+          r.real ? ((const uint32_t *)(q + ((size_t)r.query * Hq_real + r.head) * D))[idx % (D / 2)] : 0u;
+    }
+  } else {
     // this wave's copy of the query rows: no block barrier needed
     const uint32_t *src = (const uint32_t *)(q + ((size_t)karg_u16(b.row, e) * Hq + kv * GQ) * D);
     for (int idx = lane; idx < GQ * D / 2; idx += 64) sm.q2[wi][idx / (D / 2)][idx % (D / 2)] = src[idx];
@@ -401,6 +432,9 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
       if (k0 + i >= nk) break;
       const int u = (wi + NW * (k0 + i)) * TPI + ts;
       const bool ok = u < n_win;
+      // position of window token u (sink slot = position; recent slot j holds
+      // the position 64 + n_hist + ((j - n_hist) mod 256))
+      const int upos = u < n_sink ? u : kSink + n_hist + ((u - n_sink - n_hist) & (kRecent - 1));
       float vf[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -419,7 +453,9 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
           d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qw), d, false);
         }
         d = lanes_sum<LPT>(d);
-        const float sc = ok ? d * qscale : -INFINITY;
+        bool vis = ok;
+        if constexpr (PREFILL) vis = vis && upos <= vpos[h];
+        const float sc = vis ? d * qscale : -INFINITY;
         const bool jump = sc > m_ref[h] + kLazy;
         if (__any(jump)) {
           const float mn = jump ? sc : m_ref[h];
@@ -429,7 +465,7 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
           for (int j = 0; j < 8; ++j) acc[h][j] *= al;
           m_ref[h] = mn;
         }
-        const float pr = ok ? fast_exp2(sc - m_ref[h]) : 0.f;
+        const float pr = vis ? fast_exp2(sc - m_ref[h]) : 0.f;
         l_run[h] += pr;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pr, vf[j], acc[h][j]);
@@ -638,7 +674,7 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_ld
 }
 
 // A block that holds only a pair's window: all its waves take part.
-template <int D, int G, int GQ>
+template <int D, int G, int GQ, bool PREFILL = false>
 __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
                              const uint16_t *q, float qscale, float *ws_win, const AppendIn &in, int e, int kv) {
   constexpr int W = main_waves(D, G, GQ);
@@ -651,7 +687,7 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
     if (w < 2) fused_append_slot<D, GQ, W>(sm, p, b, in, e, kv, w, threadIdx.x & 63);
     wait_count(&sm.app_slot_done, 2, p);
   }
-  window_waves<D, G, GQ, W>(sm, p, b, q, qscale, e, kv, w);
+  window_waves<D, G, GQ, W, PREFILL>(sm, p, b, q, qscale, e, kv, w);
   __syncthreads();
   block_merge_store<D, GQ, W>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2));
 }
@@ -768,7 +804,7 @@ __device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk
 template <int D, int G, int GQ>
 constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
-template <int D, int G, int GQ>
+template <int D, int G, int GQ, bool PREFILL = false>
 __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
                               float *ws_hist, float *ws_win, const uint16_t *q, float qscale, const AppendIn &in,
                               int slot, int e, int kv, int p0, int p1, bool with_window) {
@@ -777,6 +813,10 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
   constexpr int RT = GQ >= 4 ? GQ / 4 : 1; // MFMA row tiles of 4 heads x 4 limb rows
   constexpr int NJ = D / 16;               // PV column tiles of 16 channels
+  // With at most 8 heads, rows GQ .. 2 GQ - 1 of the PV tile are free: they
+  // carry the fp16 remainder of each head's weights (P' = hi + lo, ~22
+  // bits), and the epilogue adds their output rows to the heads' rows.
+  constexpr bool LO = 2 * GQ <= 16;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 15, r = lane >> 4;
   const int Hkv = p.Hkv;
@@ -790,14 +830,26 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // evicts, the pair's last page (the plan keeps it in this split) is taken
   // after the loop, once the append has written it.
   const bool fused_evict = b.fused && with_window && b.len[e] - 1 >= kWindow;
-  const int pf = fused_evict ? np - 1 : full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
+  int pf = fused_evict ? np - 1 : full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
+  if constexpr (PREFILL) {
+    // pages every query of the tile sees whole (the tile's first query has
+    // the smallest position); the later ones go to the masked pass
+    const int fv = prefill_visible_hist(pf_row(b, e, kv, 0).pos, n_hist) / kPage;
+    pf = max(p0, min(pf, fv));
+  }
 
   // ---- prologue: R_K (direct to shared memory; no such load may be
   // outstanding in the page loop, where the compiler would order every
   // shared-memory access after it), the query rows and the first segment's
   // page ids are staged; the block builds the query record.
   stage_table<D>(sm.R, p.RK + (size_t)kv * D * D, w, W, lane);
-  {
+  if constexpr (PREFILL) {
+    const int Hq_real = p.Hkv * b.pf_g;
+    for (int idx = tid; idx < GQ * D; idx += NT) {
+      const PfRow rw = pf_row(b, e, kv, idx / D);
+      sm.u.pre.qT[idx % D][idx / D] = rw.real ? bf16f(q[((size_t)rw.query * Hq_real + rw.head) * D + idx % D]) : 0.f;
+    }
+  } else {
     const uint16_t *qrow = q + ((size_t)karg_u16(b.row, e) * p.Hq + kv * GQ) * D;
     for (int idx = tid; idx < GQ * D; idx += NT) sm.u.pre.qT[idx % D][idx / D] = bf16f(qrow[idx]);
   }
@@ -860,7 +912,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       if (w < 2) fused_append_slot<D, GQ, WW>(sm.win, p, b, in, e, kv, w, lane);
       wait_count(&sm.win.app_slot_done, 2, p);
     }
-    window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
+    window_waves<D, G, GQ, WW, PREFILL>(sm.win, p, b, q, qscale, e, kv, w);
     if (b.fused && w < 2) fused_append_page<D, G, GQ, WW>(sm.win, sm.R, p, b, e, kv, w, lane);
   }
   auto stage = [&](int s0, int sf) __attribute__((always_inline)) {
@@ -873,13 +925,14 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   const uint32_t *rec = sm.rec;
   const float *tail = (const float *)(rec + RT * MI * 256);
   v4i Aq[RT][MI];
-  float kfac[RT], qsum[RT][NG];
+  float kfac[RT], ikfac[RT], qsum[RT][NG];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) Aq[rt][mi] = *(const v4i *)(rec + ((rt * MI + mi) * 64 + lane) * 4);
     const int hs = min(rt * 4 + r, GQ - 1); // head of this lane in the logit layout
     kfac[rt] = tail[32 + hs];
+    ikfac[rt] = 1.f / kfac[rt];
 #pragma unroll
     for (int g = 0; g < NG; ++g) qsum[rt][g] = tail[hs * NG + g] / kfac[rt]; // exact: kfac = 2^-k
   }
@@ -894,6 +947,13 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     pfac[T] = ldexpf(1.f, p.pv_shift - 2 * ee);
   }
 
+  // prefill: position of the query of each row tile's head in this lane
+  // (rows rt * 4 + r); tokens after it are masked on the masked pages
+  int vpos[PREFILL ? RT : 1];
+  if constexpr (PREFILL) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) vpos[rt] = pf_row(b, e, kv, min(rt * 4 + r, GQ - 1)).pos;
+  }
   float m_run[RT], thr[RT], l_run[RT], zs[RT][NG];
   v4f acc[NJ];
 #pragma unroll
@@ -932,6 +992,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
             cacc[rt][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[rt][mi], B, cacc[rt][g], 0, 0, 0);
         }
         const bool tvalid = full || 4 * n + T < ntok;
+        const int tpos = kSink + pi * kPage + 4 * n + T; // position of this lane's token
   #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           float l = 0.f;
@@ -946,7 +1007,9 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
             // applies it), so the products are those of kfac * logit exactly
             l = fmaf(f16lo(sz), dv, fmaf(f16hi(sz), qsum[rt][g], l));
           }
-          lg[rt][T] = (tvalid && (GQ >= 4 || rt * 4 + r < GQ)) ? l : -INFINITY;
+          bool vis = tvalid && (GQ >= 4 || rt * 4 + r < GQ);
+          if constexpr (PREFILL) vis = vis && (full || tpos <= vpos[rt]);
+          lg[rt][T] = vis ? l : -INFINITY;
         }
       }
 
@@ -976,18 +1039,16 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
           const float mnew = jump ? mt : m_run[rt];
           alpha[rt] = jump ? fast_exp2(m_run[rt] - mnew) : 1.f;
           m_run[rt] = mnew;
-          thr[rt] = (mnew + kLazy) / kfac[rt];
+          thr[rt] = (mnew + kLazy) * ikfac[rt]; // exact: kfac is a power of two
         }
       }
       // V scale times the token factor of P' (exact: pfac is a power of
       // two), once per token for all row tiles
       float spf[NG][4];
-      if constexpr (RT > 1) {
   #pragma unroll
-        for (int T = 0; T < 4; ++T)
+      for (int T = 0; T < 4; ++T)
   #pragma unroll
-          for (int g = 0; g < NG; ++g) spf[g][T] = fmaf(f16lo(cur.vp[(T * NG + g) / 4][(T * NG + g) % 4]), pfac[T], 0.f);
-      }
+        for (int g = 0; g < NG; ++g) spf[g][T] = fmaf(f16lo(cur.vp[(T * NG + g) / 4][(T * NG + g) % 4]), pfac[T], 0.f);
   #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int hrow = rt * 4 + r;
@@ -1006,10 +1067,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
           for (int g = 0; g < NG; ++g) {
             const uint32_t sz = cur.vp[(T * NG + g) / 4][(T * NG + g) % 4];
             zadd[g] = ok ? fmaf(pt, f16hi(sz), zadd[g]) : zadd[g];
-            // (an fma with a zero addend: one mixed-precision instruction
-            // that rounds the product once, to fp16)
-            if constexpr (RT > 1) pv[g][T] = ok ? fmaf(pt, spf[g][T], 0.f) : 0.f;
-            else pv[g][T] = ok ? fmaf(f16lo(sz), pt * pfac[T], 0.f) : 0.f;
+            pv[g][T] = ok ? pt * spf[g][T] : 0.f;
           }
         }
         l_run[rt] = fmaf(l_run[rt], alpha[rt], psum);
@@ -1020,13 +1078,21 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
             union {
               _Float16 h[4];
               u32x2 u;
-            } pk;
+            } hi, lo;
   #pragma unroll
-            for (int T = 0; T < 4; ++T) pk.h[T] = (_Float16)pv[g][T];
-            *(u32x2 *)&sm.u.P[w][g][hrow][4 * n] = pk.u;
+            for (int T = 0; T < 4; ++T) {
+              hi.h[T] = (_Float16)pv[g][T];
+              // the remainder, exact in fp32, rounded to fp16
+              if constexpr (LO) lo.h[T] = (_Float16)(pv[g][T] - (float)hi.h[T]);
+            }
+            *(u32x2 *)&sm.u.P[w][g][hrow][4 * n] = hi.u;
+            if constexpr (LO) *(u32x2 *)&sm.u.P[w][g][GQ + hrow][4 * n] = lo.u;
           }
         }
-        if (any_jump && n == 0 && hrow < GQ) sm.alpha[w][hrow] = alpha[rt];
+        if (any_jump && n == 0 && hrow < GQ) {
+          sm.alpha[w][hrow] = alpha[rt];
+          if constexpr (LO) sm.alpha[w][GQ + hrow] = alpha[rt];
+        }
       }
       wave_sync();
 
@@ -1094,7 +1160,15 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       }
     }
   }
-  if (pf < p1 && w == W - 1) {
+  if (PREFILL && w == W - 1) {
+    // prefill: the pages some query of the tile sees only in part (and the
+    // sequence's last page), with per-row position masks
+    for (int pi = pf; pi < p1; ++pi) {
+      PageRegs<D, G> last;
+      load_page<D, G>(last, p.pages + (size_t)ptab[pi] * hstride + hoff, true, p.block_bytes, n, r);
+      page_step(last, pi, false);
+    }
+  } else if (pf < p1 && w == W - 1) {
     int id;
     if (fused_evict) {
       wait_count(&sm.win.app_page_done, 2, p);
@@ -1143,17 +1217,20 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   {
     // heads 4 r + i of this lane's accumulator rows: the block maximum and
     // this wave's (two shared-memory reads, not one per wave)
+    // (rows GQ .. 2 GQ - 1 hold the remainder part of heads 0 .. GQ - 1)
     float mb[4], mw[4];
     if constexpr (GQ % 4 == 0) {
-      const float4 tb = *(const float4 *)&sm.Mb[4 * r];
-      const float4 tw = *(const float4 *)&sm.M[w][4 * r];
+      const int hb = LO ? (4 * r) % GQ : 4 * r;
+      const float4 tb = *(const float4 *)&sm.Mb[hb];
+      const float4 tw = *(const float4 *)&sm.M[w][hb];
       mb[0] = tb.x, mb[1] = tb.y, mb[2] = tb.z, mb[3] = tb.w;
       mw[0] = tw.x, mw[1] = tw.y, mw[2] = tw.z, mw[3] = tw.w;
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        mb[i] = 4 * r + i < GQ ? sm.Mb[4 * r + i] : -INFINITY;
-        mw[i] = 4 * r + i < GQ ? sm.M[w][4 * r + i] : -INFINITY;
+        const int row = 4 * r + i, h = LO && row >= GQ ? row - GQ : row;
+        mb[i] = h < GQ ? sm.Mb[h] : -INFINITY;
+        mw[i] = h < GQ ? sm.M[w][h] : -INFINITY;
       }
     }
     const float unscale = ldexpf(1.f, 24 - p.pv_shift);
@@ -1165,6 +1242,19 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       for (int j = 0; j < NJ; ++j) {
         const int c = 16 * j + n;
         if (h < GQ) sm.u.A[w][h][c] = f * fmaf(acc[j][i], unscale, sm.zsum[w][h][c / G]);
+      }
+    }
+    if constexpr (LO) {
+      wave_sync(); // the head rows of this wave are written
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * r + i;
+        const float f = mw[i] == -INFINITY ? 0.f : exp2f(mw[i] - mb[i]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int c = 16 * j + n;
+          if (row >= GQ && row < 2 * GQ) sm.u.A[w][row - GQ][c] += f * (acc[j][i] * unscale);
+        }
       }
     }
   }
@@ -1199,7 +1289,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
 // read together with the window partial, before the pair's own split count
 // is known; slots at or past it are read (in bounds) but never used.  One
 // thread per (head, channel) output.
-template <int D, int GQ, int NT>
+template <int D, int GQ, int NT, bool PREFILL = false>
 __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, int e, int kv,
                            int tid) {
   constexpr int SB = 4; // splits per batch of loads
@@ -1247,7 +1337,13 @@ __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, c
       fetch(s0);
       fold(s0);
     }
-    out_pair[idx] = a / l;
+    if constexpr (PREFILL) {
+      // the tile's head h is query row r.query, query head r.head
+      const PfRow rw = pf_row(b, e, kv, h);
+      if (rw.real) out[((size_t)rw.query * (Hkv * b.pf_g) + rw.head) * D + c] = a / l;
+    } else {
+      out_pair[idx] = a / l;
+    }
   }
 }
 
@@ -1256,15 +1352,15 @@ __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, c
 template <int D, int GQ>
 constexpr int merge_threads() { return GQ * D < 1024 ? GQ * D : 1024; }
 
-template <int D, int GQ>
+template <int D, int GQ, bool PREFILL = false>
 __global__ __launch_bounds__((merge_threads<D, GQ>())) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
                                                                      const float *__restrict__ ws) {
   // grid (sequence, kv head): the pair is known before any kernel argument
   // arrives, so all of them load in one round
-  merge_pair<D, GQ, merge_threads<D, GQ>()>(p, b, out, ws, blockIdx.x, blockIdx.y, threadIdx.x);
+  merge_pair<D, GQ, merge_threads<D, GQ>(), PREFILL>(p, b, out, ws, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
-template <int D, int G, int GQ>
+template <int D, int G, int GQ, bool PREFILL = false>
 __global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
 void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
                         float *__restrict__ ws, AppendIn in) {
@@ -1276,16 +1372,21 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   int s, e, kv;
   block_split(b, Hkv, blk, s, e, kv);
   const int S = karg_u8(b.nsplit, e);
-  const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
+  int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
+  if constexpr (PREFILL) {
+    // the pages up to the tile's last query (the host plans with this count)
+    const int last = (min(b.pf_flat0[e] + GQ, b.pf_rows * b.pf_g) - 1) / b.pf_g; // the tile's last query
+    np = (prefill_visible_hist(b.len[e] - b.pf_rows + last, max(b.len[e] - kWindow, 0)) + kPage - 1) / kPage;
+  }
   int p0, p1;
   split_range(np, S, s, b.win_units, p0, p1);
   // split partial slot: the pair's splits are consecutive, stride the
   // batch's largest split count (launch order is by split count, descending)
   const int slot = (e * Hkv + kv) * karg_u8(b.nsplit, 0) + s;
   if (p0 < p1)
-    history_block<D, G, GQ>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
+    history_block<D, G, GQ, PREFILL>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
   else if (s == S - 1) {
-    window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, in, e, kv);
+    window_block<D, G, GQ, PREFILL>(sm.w, p, b, q, qscale, ws_win, in, e, kv);
     // this split holds no pages: an empty history partial for the merge
     float *dst = ws_hist + (size_t)slot * GQ * (D + 2);
     for (int idx = threadIdx.x; idx < GQ * (D + 2); idx += 64 * W) dst[idx] = idx % (D + 2) == D ? -INFINITY : 0.f;
@@ -1320,6 +1421,23 @@ hipError_t decode_g(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, f
   return hipErrorInvalidValue;
 }
 
+template <int D, int G, int GQ>
+hipError_t prefill_attn_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
+                             float *ws, hipStream_t s) {
+  const AppendIn none{nullptr, nullptr};
+  hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
+                     p, b, q, scale * kLog2e, ws, none);
+  hipLaunchKernelGGL((decode_merge_kernel<D, GQ, true>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s, p, b,
+                     out, (const float *)ws);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t prefill_attn_g(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
+                          float *ws, hipStream_t s) {
+  return prefill_attn_impl<D, G, kPrefillTile>(p, b, q, out, scale, ws, s);
+}
+
 template <int D, int G>
 int blocks_per_cu_g(const PoolDev &p) {
   int nb = 0;
@@ -1334,13 +1452,36 @@ int blocks_per_cu_g(const PoolDev &p) {
   return e == hipSuccess ? nb : 0;
 }
 
+template <int D, int G>
+int prefill_blocks_per_cu_g(const PoolDev &p) {
+  int nb = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &nb, decode_main_kernel<D, G, kPrefillTile, true>, 64 * main_waves(D, G, kPrefillTile), 0);
+  return e == hipSuccess ? nb : 0;
+}
+
 } // namespace
+
+int prefill_blocks_per_cu(const PoolDev &p) {
+  if (p.d == 128 && p.G == 128) return prefill_blocks_per_cu_g<128, 128>(p);
+  if (p.d == 128 && p.G == 64) return prefill_blocks_per_cu_g<128, 64>(p);
+  if (p.d == 64 && p.G == 64) return prefill_blocks_per_cu_g<64, 64>(p);
+  return 0;
+}
 
 int decode_main_blocks_per_cu(const PoolDev &p) {
   if (p.d == 128 && p.G == 128) return blocks_per_cu_g<128, 128>(p);
   if (p.d == 128 && p.G == 64) return blocks_per_cu_g<128, 64>(p);
   if (p.d == 64 && p.G == 64) return blocks_per_cu_g<64, 64>(p);
   return 0;
+}
+
+hipError_t launch_prefill_attn(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
+                               float *ws, hipStream_t s) {
+  if (p.d == 128 && p.G == 128) return prefill_attn_g<128, 128>(p, b, q, out, scale, ws, s);
+  if (p.d == 128 && p.G == 64) return prefill_attn_g<128, 64>(p, b, q, out, scale, ws, s);
+  if (p.d == 64 && p.G == 64) return prefill_attn_g<64, 64>(p, b, q, out, scale, ws, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,

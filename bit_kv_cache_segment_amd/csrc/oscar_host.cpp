@@ -183,7 +183,8 @@ struct oscar_pool {
   Layout lay;
   PoolDev dev;
   bool host_only;
-  int decode_slots = 768; // resident decode blocks on the device
+  int decode_slots = 768;  // resident decode blocks on the device
+  int prefill_slots = 256; // resident prefill-attention blocks
   std::vector<int32_t> len;
   std::vector<std::vector<int32_t>> table;
   std::vector<int32_t> free_list; // pages [free_head, end) are free, front first
@@ -365,6 +366,12 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
       return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "querying the decode occupancy");
     }
     p->decode_slots = cus * per_cu;
+    const int pf_per_cu = prefill_blocks_per_cu(D);
+    if (pf_per_cu <= 0) {
+      delete p;
+      return hip_fail(hipErrorInvalidValue, "querying the prefill occupancy");
+    }
+    p->prefill_slots = cus * pf_per_cu;
     // set-up of the static decode workspace on this device (its address is
     // looked up here, once per device, not in the step that uses it)
     void *ws = nullptr;
@@ -676,6 +683,65 @@ int oscar_pool_check(oscar_pool *p, void *stream) {
   if (e != hipSuccess) return hip_fail(e, "pool check sync");
   const int rc = check_device_status(p);
   return rc ? rc : ok();
+}
+
+int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, size_t *bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!bytes || n_q < 0) return fail(OSCAR_EINVAL, "bad arguments");
+  const int Hkv = cfg->num_kv_heads, g = cfg->num_q_heads / Hkv, vg = kPrefillTile;
+  const int tiles = (int)std::min<int64_t>(((int64_t)n_q * g + vg - 1) / vg, kMaxBatch);
+  *bytes = decode_ws_floats(Hkv * vg, cfg->head_dim, tiles, Hkv, kMaxSplits, vg) * sizeof(float);
+  return ok();
+}
+
+int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *q, float *out, float softmax_scale,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (p->host_only) return fail(OSCAR_EINVAL, "prefill attention on a host-only pool");
+  const int32_t L = p->len[seq];
+  if (n_q < 1 || n_q > L || (int64_t)n_q * p->cfg.num_q_heads > ((int64_t)1 << 30))
+    return fail(OSCAR_EINVAL, "n_q = %d outside [1, L = %d] (or n_q x Hq above 2^30)", n_q, L);
+  if (!q || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
+  if (!std::isfinite(softmax_scale)) return fail(OSCAR_EINVAL, "softmax_scale is not finite");
+  const int Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim, g = p->cfg.num_q_heads / Hkv;
+  const int vg = kPrefillTile;
+  const int64_t rows = (int64_t)n_q * g;
+  const int tiles = (int)((rows + vg - 1) / vg);
+  const int n_hist = std::max(0, L - kWindow);
+  PoolDev pv = p->dev;
+  pv.Hq = Hkv * vg; // the tiles' heads
+  // Each tile is one "sequence" of the decode plan, planned on the pages up
+  // to its last query (a length whose history is exactly those pages).
+  std::vector<DecodeBatch> batches;
+  size_t need = 0;
+  for (int t0 = 0; t0 < tiles; t0 += kMaxBatch) {
+    DecodeBatch b;
+    b.n = std::min(kMaxBatch, tiles - t0);
+    std::vector<int> plan_len(b.n);
+    std::vector<int32_t> ids(b.n, seq);
+    for (int e = 0; e < b.n; ++e) {
+      const int last = (int)((std::min<int64_t>((int64_t)(t0 + e + 1) * vg, rows) - 1) / g); // last query
+      plan_len[e] = kWindow + prefill_visible_hist(L - n_q + last, n_hist);
+    }
+    plan_splits(b, ids.data(), plan_len, Hkv, p->prefill_slots, window_units(d, p->cfg.group_size));
+    for (int i = 0; i < b.n; ++i) {
+      b.pf_flat0[i] = (t0 + b.row[i]) * vg;
+      b.len[i] = L;
+    }
+    b.pf_g = g;
+    b.pf_rows = n_q;
+    need = std::max(need, decode_ws_floats(pv.Hq, d, b.n, Hkv, b.nsplit[0], vg) * sizeof(float));
+    batches.push_back(b);
+  }
+  if (workspace_bytes < need)
+    return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  for (const DecodeBatch &b : batches) {
+    hipError_t e = launch_prefill_attn(pv, b, q, out, softmax_scale, (float *)workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  return ok();
 }
 
 int oscar_release_seq(oscar_pool *p, int32_t seq) {

@@ -123,8 +123,25 @@ struct DecodeBatch {
   // sequence (len is the length after it).  new_page: the page the append
   // takes for the evicted token, or -1 (launch order).
   int32_t fused;
-  int32_t new_page[kMaxBatch];
+  // Prefill attention (oscar_prefill_attn): pf_g > 0 is the pool's query
+  // heads per kv head and pf_rows the call's query count n_q.  The call's
+  // rows (query i, head hh of the kv head), flat index i g + hh, are cut in
+  // tiles of 8; an entry is a tile (pf_flat0: its first flat row) whose rows
+  // act as the "heads" of one pair, each seeing positions up to its query's
+  // own (query i at position len - n_q + i).
+  int32_t pf_g, pf_rows;
+  union {
+    int32_t new_page[kMaxBatch];
+    int32_t pf_flat0[kMaxBatch];
+  };
 };
+
+// History tokens (from the start of the history) visible to a prefill
+// query at position pos: those at positions 64 .. pos.
+__host__ __device__ inline int prefill_visible_hist(int pos, int n_hist) {
+  const int h = pos + 1 - kSink;
+  return h < 0 ? 0 : (h > n_hist ? n_hist : h);
+}
 
 // the kernels read row[] and nsplit[] through whole dwords
 static_assert(offsetof(DecodeBatch, row) % 4 == 0 && offsetof(DecodeBatch, nsplit) % 4 == 0,
@@ -185,8 +202,17 @@ hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t 
 // History entries [0, n_hist) of a sequence in the canonical layout, device
 // to device (codes 4-byte aligned: d/4 is a multiple of 4).
 hipError_t launch_export(const PoolDev &p, int seq, int n_hist, uint8_t *codes, uint16_t *params, hipStream_t s);
+// Resident prefill-attention blocks per compute unit (pool's real heads).
+int prefill_blocks_per_cu(const PoolDev &p);
 // Resident decode_main blocks per compute unit for this pool's shape.
 int decode_main_blocks_per_cu(const PoolDev &p);
+
+// Prefill attention launch (b.pf_g > 0): decode machinery over query tiles;
+// p_virtual is the pool view with Hq = Hkv x (tile heads).
+hipError_t launch_prefill_attn(const PoolDev &p_virtual, const DecodeBatch &b, const uint16_t *q, float *out,
+                               float scale, float *ws, hipStream_t s);
+// Rows (query, head) of a prefill tile.
+constexpr int kPrefillTile = 8;
 
 // k_new, v_new: the appended tokens of a fused step (b.fused), else null.
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out,

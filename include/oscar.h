@@ -221,6 +221,32 @@ int oscar_decode_step_static(oscar_pool *pool, const int32_t *seq_ids, int32_t n
  * Host-only pools always pass. */
 int oscar_pool_check(oscar_pool *pool, void *stream);
 
+/* Bytes of device workspace oscar_prefill_attn needs for n_q queries.
+ * Host only.  Errors: EINVAL. */
+int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, size_t *bytes);
+
+/* Prefill attention over the three-segment pool ([B]: the step before
+ * decode; the prompt, or one chunk of it, attends over everything before
+ * it).  The sequence holds L tokens; the n_q queries are those of its last
+ * n_q positions, query i at position p = L - n_q + i, and each attends with
+ * softmax (scale `softmax_scale`) to positions 0..p of the pool as it
+ * stands: sink and recent tokens as stored (bf16), history tokens as
+ * decoded (dequantized with their group scale and zero point and mapped
+ * back by R^T), exactly the tokens decode attention would see at length
+ * p + 1.  A chunked prefill appends a chunk (oscar_prefill for an empty
+ * sequence, oscar_append_evict otherwise) and then calls this with the
+ * chunk's queries.
+ *   q:   device bf16 [n_q][Hq][d];   out: device fp32 [n_q][Hq][d];
+ *   workspace: device, >= oscar_prefill_workspace_bytes(cfg, n_q) bytes.
+ * The (query, head) rows of each kv head are cut in tiles of 8, which the
+ * decode kernels treat as the heads of one (sequence, kv head) pair, each
+ * masked past its own query's position.
+ * Errors: EINVAL (bad seq, n_q outside [1, min(L, 65535)], NULL, workspace
+ * too small, host-only pool), EHIP. */
+int oscar_prefill_attn(oscar_pool *pool, int32_t seq, int32_t n_q, const uint16_t *q,
+                       float *out, float softmax_scale, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 /* Return a sequence's pages to the back of the free list (in page-table
  * order) and set its length to 0.  Host only.  Errors: EINVAL. */
 int oscar_release_seq(oscar_pool *pool, int32_t seq);
