@@ -164,6 +164,65 @@ def cpu_baseline(w, lengths, budget_s, max_workers=16):
             "host": {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_main(args):
+    """Prefill-attention measurement: the last n_q positions of one prompt of
+    L tokens (the final chunk of a chunked prefill, its K/V already in the
+    pool) attend causally over the three-segment pool.  Algorithmic flops:
+    4 Hq d per (query, visible token) (QK^T and PV)."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_segment_amd as ok
+    import harness
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    L, n_q = args.prefill_len, args.prefill_chunk
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    RK, RV, cK, cV = harness.tables(w)
+    cfg = harness.config_for(w, [L])
+    pools = []
+    for layer in range(args.layers):
+        p = ok.Pool(cfg, RK, RV, cK, cV, max_batch=1)
+        harness.prefill_all(p, w, [L])
+        pools.append(p)
+    q = synth.queries(w, 0, device="cuda", batch=n_q).view(torch.uint16).contiguous()
+    out = torch.empty((n_q, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    wsb = ok.oscar_prefill_workspace_bytes(cfg, n_q)
+    ws = torch.empty(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+    for s in range(args.warmup):
+        pools[s % args.layers].prefill_attn(0, q, out, workspace=ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(args.steps):
+        pools[s % args.layers].prefill_attn(0, q, out, workspace=ws)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    visible = sum(L - n_q + i + 1 for i in range(n_q))
+    flops = 4.0 * w.num_q_heads * w.head_dim * visible
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "prefill attention tokens/s per layer (chunk over the three-segment pool)",
+        "value": n_q / (ms * 1e-3), "unit": "tokens/s per layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int2 codes + fp16 scale/zero history, bf16 windows, int8/fp16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded; K/V ~ N(0,1) with 4 outlier channels x20)",
+        "config": {"workload": f"{w.name} prefill chunk", "prompt_len": L, "chunk": n_q, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "group_size": w.group_size,
+                   "layer_pools": args.layers, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops": flops},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,11 +242,21 @@ def main():
                          "(each timed launch adds a few microseconds to its step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
+    ap.add_argument("--mode", choices=["decode", "prefill"], default="decode",
+                    help="decode: the serving step (headline); prefill: a prefill chunk's attention")
+    ap.add_argument("--prefill-len", type=int, default=32768, help="prefill mode: prompt length")
+    ap.add_argument("--prefill-chunk", type=int, default=2048, help="prefill mode: queries of the last chunk")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode path runs on a single device and has no "
               "multi-GPU mode; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "prefill":
+        if args.workload == "fused_64x_4k_64k":
+            args.workload = "qwen3_8b_32k"
+        prefill_main(args)
+        return
 
     import numpy as np
 
