@@ -23,6 +23,7 @@ PAGE_TOKENS = 64
 MAX_BATCH_PER_LAUNCH = 256
 POOL_HOST_ONLY = 1
 POOL_DETERMINISTIC = 2
+POOL_BF16_HISTORY = 4
 
 OK, EHIP, ENOMEM, EINVAL, ERANGE = 0, -5, -12, -22, -34
 _NAMES = {EHIP: "EHIP", ENOMEM: "ENOMEM", EINVAL: "EINVAL", ERANGE: "ERANGE"}
@@ -34,7 +35,7 @@ EXPORTS = (
     "oscar_decode_step_static", "oscar_prefill_workspace_bytes", "oscar_prefill_attn", "oscar_pool_check",
     "oscar_release_seq",
     "oscar_seq_length", "oscar_page_table", "oscar_free_pages", "oscar_export_history",
-    "oscar_export_state", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
+    "oscar_export_state", "oscar_export_history_bf16", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
     "oscar_profile_end", "oscar_last_error",
 )
 
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
             "oscar_free_pages": [_P, _P],
             "oscar_export_history": [_P, _I32, _I32, _I32, _P, _P, _P],
             "oscar_export_state": [_P, _I32, _P, _P, _P, _P],
+            "oscar_export_history_bf16": [_P, _I32, _I32, _I32, _P, _P, _P],
             "oscar_export_window": [_P, _I32, _P, _P, _P, _P, _P],
             "oscar_build_rotation": [_I32, _P, _P],
             "oscar_calibrate_clip": [_I32, ctypes.c_int64, _P, _P, ctypes.c_double, _P],
@@ -270,6 +272,14 @@ def oscar_export_state(h, seq: int, max_pages: int, codes_dev, params_dev, strea
     _check(lib().oscar_export_state(h, seq, _np_ptr(table), _dev_ptr(codes_dev), _dev_ptr(params_dev),
                                     _stream(stream)))
     return table[:max_pages]
+
+
+def oscar_export_history_bf16(h, seq: int, first: int, count: int, Hkv: int, d: int, stream=None):
+    """BF16-history pools: (k, v) bf16 bits [count][Hkv][d] of history entries [first, first+count)."""
+    k = np.zeros((count, Hkv, d), dtype=np.uint16)
+    v = np.zeros((count, Hkv, d), dtype=np.uint16)
+    _check(lib().oscar_export_history_bf16(h, seq, first, count, _np_ptr(k), _np_ptr(v), _stream(stream)))
+    return k, v
 
 
 def oscar_export_window(h, seq: int, Hkv: int, d: int, stream=None):

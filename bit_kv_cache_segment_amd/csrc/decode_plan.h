@@ -31,6 +31,8 @@ constexpr int kExtraRounds = 0;
 inline int window_units(int d, int G, bool fused = false) {
   return (int)std::lround((fused ? kStepWindowCost : kWindowCost) * kWindow * 4 * d / block_bytes_for(d, G));
 }
+// the same for a BF16-history pool (window and pages cost alike per byte)
+inline int window_units_bf16(int d) { return (int)std::lround((double)kWindow * 4 * d / bf16_block_bytes(d)); }
 
 // fused: the launch also appends (len is the length after the append); a
 // pair whose append evicts into the history keeps its last page in its last

@@ -1476,6 +1476,31 @@ int decode_main_blocks_per_cu(const PoolDev &p) {
   return 0;
 }
 
+template <int D>
+hipError_t merge_d(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, hipStream_t s,
+                   const KernelTimer &tg) {
+#define OSCAR_MERGE(GQv)                                                                                            \
+  hipExtLaunchKernelGGL((decode_merge_kernel<D, GQv>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQv>()), 0, s,       \
+                        tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, out, ws);                   \
+  return hipGetLastError();
+  switch (p.Hq / p.Hkv) {
+  case 1: { OSCAR_MERGE(1) }
+  case 2: { OSCAR_MERGE(2) }
+  case 4: { OSCAR_MERGE(4) }
+  case 8: { OSCAR_MERGE(8) }
+  case 16: { OSCAR_MERGE(16) }
+  }
+#undef OSCAR_MERGE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, hipStream_t s,
+                               const KernelTimer &tg) {
+  if (p.d == 128) return merge_d<128>(p, b, out, ws, s, tg);
+  if (p.d == 64) return merge_d<64>(p, b, out, ws, s, tg);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill_attn(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                                float *ws, hipStream_t s) {
   if (p.d == 128 && p.G == 128) return prefill_attn_g<128, 128>(p, b, q, out, scale, ws, s);

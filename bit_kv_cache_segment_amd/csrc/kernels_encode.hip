@@ -165,6 +165,19 @@ __global__ __launch_bounds__(D) void prefill_encode_kernel(PoolDev p, int seq, c
   }
 }
 
+// Prefill of a BF16-history pool: the history tokens are copied into their
+// pages.  grid (history pages, Hkv, K|V), block D.
+template <int D>
+__global__ __launch_bounds__(D) void prefill_copy_kernel(PoolDev p, int seq, const uint16_t *__restrict__ k,
+                                                         const uint16_t *__restrict__ v, int n_hist) {
+  const int pg_idx = blockIdx.x, kv = blockIdx.y, kind = blockIdx.z, j = threadIdx.x, Hkv = p.Hkv;
+  const uint16_t *src = kind ? v : k;
+  const int page = p.page_table[(size_t)seq * p.maxp + pg_idx];
+  uint16_t *dst = (uint16_t *)(p.pages + ((size_t)page * Hkv + kv) * p.block_bytes) + (kind ? kPage * D : 0);
+  const int t0 = pg_idx * kPage, nt = min(kPage, n_hist - t0);
+  for (int t = 0; t < nt; ++t) dst[t * D + j] = src[((size_t)(kSink + t0 + t) * Hkv + kv) * D + j];
+}
+
 // Prefill: copy sink and recent positions into the BF16 windows.
 // grid (window positions, Hkv), block D: position index u < n_sink is sink
 // position u; otherwise recent position n_hist + 64 + (u - n_sink).
@@ -211,6 +224,14 @@ __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, con
   // evict the oldest recent token (held in this slot) into history n_hist
   const int n_hist = L - kWindow, pg_idx = n_hist / kPage, t = n_hist % kPage;
   const int page = t == 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + pg_idx];
+  if (p.bf16_hist) {
+    // BF16-history pool: the token is copied as it is
+    uint16_t *dst = (uint16_t *)(p.pages + ((size_t)page * Hkv + kv) * p.block_bytes) + (kind ? kPage * D : 0);
+    dst[t * D + j] = rs[j];
+    rs[j] = xnew; // this thread read element j above; no other thread touches it
+    if (t == 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
+    return;
+  }
   const float xj = bf16f(rs[j]);
   const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
   float rc[D];
@@ -312,7 +333,10 @@ hipError_t prefill_impl(const PoolDev &p, int seq, const uint16_t *k, const uint
                        n_sink, n_hist);
   if (n_hist > 0) {
     const int np = (n_hist + kPage - 1) / kPage;
-    hipLaunchKernelGGL((prefill_encode_kernel<D, G>), dim3(np, p.Hkv, 2), dim3(D), 0, s, p, seq, k, v, n_hist);
+    if (p.bf16_hist)
+      hipLaunchKernelGGL((prefill_copy_kernel<D>), dim3(np, p.Hkv, 2), dim3(D), 0, s, p, seq, k, v, n_hist);
+    else
+      hipLaunchKernelGGL((prefill_encode_kernel<D, G>), dim3(np, p.Hkv, 2), dim3(D), 0, s, p, seq, k, v, n_hist);
   }
   return hipGetLastError();
 }

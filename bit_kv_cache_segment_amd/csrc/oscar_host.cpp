@@ -75,7 +75,7 @@ int validate_config(const oscar_pool_config *c) {
   if ((int64_t)c->max_seqs * c->max_pages_per_seq > (int64_t)1 << 31)
     return fail(OSCAR_EINVAL, "page table of %d x %d entries is too large", c->max_seqs,
                 c->max_pages_per_seq);
-  if (c->flags & ~(OSCAR_POOL_HOST_ONLY | OSCAR_POOL_DETERMINISTIC))
+  if (c->flags & ~(OSCAR_POOL_HOST_ONLY | OSCAR_POOL_DETERMINISTIC | OSCAR_POOL_BF16_HISTORY))
     return fail(OSCAR_EINVAL, "unknown flags 0x%x", c->flags);
   return OSCAR_OK;
 }
@@ -100,7 +100,9 @@ Layout layout_of(const oscar_pool_config &c) {
   L.sinkV = take(S * H * kSink * d * 2);
   L.recentK = take(S * H * kRecent * d * 2);
   L.recentV = take(S * H * kRecent * d * 2);
-  L.pages = take((size_t)c.num_pages * H * block_bytes_for(c.head_dim, c.group_size));
+  L.pages = take((size_t)c.num_pages * H *
+                 ((c.flags & OSCAR_POOL_BF16_HISTORY) ? bf16_block_bytes(c.head_dim)
+                                                      : block_bytes_for(c.head_dim, c.group_size)));
   L.total = off;
   return L;
 }
@@ -302,7 +304,8 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
   D.d = d;
   D.G = cfg->group_size;
   D.maxp = cfg->max_pages_per_seq;
-  D.block_bytes = block_bytes_for(d, cfg->group_size);
+  D.bf16_hist = (cfg->flags & OSCAR_POOL_BF16_HISTORY) ? 1 : 0;
+  D.block_bytes = D.bf16_hist ? bf16_block_bytes(d) : block_bytes_for(d, cfg->group_size);
   D.pv_shift = 0;
   D.deterministic = (cfg->flags & OSCAR_POOL_DETERMINISTIC) ? 1 : 0;
   // Polls of a bounded wait inside a decode block before it gives up (and
@@ -360,7 +363,7 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
     int dev = 0, cus = 0;
     e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int per_cu = decode_main_blocks_per_cu(D);
+    const int per_cu = D.bf16_hist ? bf16_decode_blocks_per_cu(D) : decode_main_blocks_per_cu(D);
     if (e != hipSuccess || cus <= 0 || per_cu <= 0) {
       delete p;
       return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "querying the decode occupancy");
@@ -539,6 +542,7 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   }
   const int Hq = p->cfg.num_q_heads, Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim;
   const int g = Hq / Hkv;
+  const bool bf16 = p->dev.bf16_hist != 0;
   std::vector<DecodeBatch> batches;
   size_t need = 0;
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
@@ -546,7 +550,8 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     b.n = std::min(kMaxBatch, n - i0);
     std::vector<int> len(b.n);
     for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]];
-    plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size));
+    plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
+                bf16 ? window_units_bf16(d) : window_units(d, p->cfg.group_size));
     need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
     batches.push_back(b);
   }
@@ -554,9 +559,17 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
   for (size_t i = 0; i < batches.size(); ++i) {
     KernelTimer tm = p->prof.next(0), tg = p->prof.next(1);
-    hipError_t e = launch_decode(p->dev, batches[i], q + i * (size_t)kMaxBatch * Hq * d,
-                                 out + i * (size_t)kMaxBatch * Hq * d, softmax_scale,
-                                 (float *)workspace, nullptr, nullptr, (hipStream_t)stream, tm, tg);
+    const uint16_t *qi = q + i * (size_t)kMaxBatch * Hq * d;
+    float *oi = out + i * (size_t)kMaxBatch * Hq * d;
+    hipError_t e;
+    if (bf16) {
+      e = launch_decode_bf16(p->dev, batches[i], qi, softmax_scale, (float *)workspace, (hipStream_t)stream, tm);
+      if (e == hipSuccess)
+        e = launch_decode_merge(p->dev, batches[i], oi, (const float *)workspace, (hipStream_t)stream, tg);
+    } else {
+      e = launch_decode(p->dev, batches[i], qi, oi, softmax_scale, (float *)workspace, nullptr, nullptr,
+                        (hipStream_t)stream, tm, tg);
+    }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   return ok();
@@ -588,8 +601,9 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
   // the append is its own launch (same results).
   std::vector<DecodeBatch> batches;
   size_t need = 0;
-  bool fused = true;
-  for (int pass = 0; pass < 2; ++pass) {
+  // (BF16-history pools append in their own launch)
+  bool fused = p->dev.bf16_hist == 0;
+  for (int pass = fused ? 0 : 1; pass < 2; ++pass) {
     batches.clear();
     need = 0;
     for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
@@ -597,7 +611,8 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
       b.n = std::min(kMaxBatch, n - i0);
       std::vector<int> len(b.n);
       for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
-      plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots, window_units(d, p->cfg.group_size, fused), fused);
+      plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
+                  p->dev.bf16_hist ? window_units_bf16(d) : window_units(d, p->cfg.group_size, fused), fused);
       need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
       if (b.hist_blocks > p->decode_slots) fused = false;
       batches.push_back(b);
@@ -700,6 +715,7 @@ int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *
   int rc = check_seq(p, seq);
   if (rc) return rc;
   if (p->host_only) return fail(OSCAR_EINVAL, "prefill attention on a host-only pool");
+  if (p->dev.bf16_hist) return fail(OSCAR_EINVAL, "prefill attention runs on INT2-history pools");
   const int32_t L = p->len[seq];
   if (n_q < 1 || n_q > L || (int64_t)n_q * p->cfg.num_q_heads > ((int64_t)1 << 30))
     return fail(OSCAR_EINVAL, "n_q = %d outside [1, L = %d] (or n_q x Hq above 2^30)", n_q, L);
@@ -785,6 +801,7 @@ int oscar_export_history(oscar_pool *p, int32_t seq, int32_t first, int32_t coun
   int rc = check_seq(p, seq);
   if (rc) return rc;
   if (p->host_only) return fail(OSCAR_EINVAL, "export from a host-only pool");
+  if (p->dev.bf16_hist) return fail(OSCAR_EINVAL, "a BF16-history pool has no codes (oscar_export_history_bf16)");
   int64_t n_hist = std::max(0, p->len[seq] - kWindow);
   if (first < 0 || count < 0 || first + (int64_t)count > n_hist)
     return fail(OSCAR_EINVAL, "history range [%d, %d) outside [0, %lld)", first, first + count,
@@ -834,6 +851,7 @@ int oscar_export_state(oscar_pool *p, int32_t seq, int32_t *page_table_host, voi
   int rc = check_seq(p, seq);
   if (rc) return rc;
   if (p->host_only) return fail(OSCAR_EINVAL, "export from a host-only pool");
+  if (p->dev.bf16_hist) return fail(OSCAR_EINVAL, "a BF16-history pool has no codes (oscar_export_history_bf16)");
   if (!page_table_host) return fail(OSCAR_EINVAL, "page_table_host is NULL");
   const int64_t n_hist = std::max(0, p->len[seq] - kWindow);
   if (n_hist > 0 && (!codes_dev || !params_dev)) return fail(OSCAR_EINVAL, "NULL output buffer");
@@ -846,6 +864,40 @@ int oscar_export_state(oscar_pool *p, int32_t seq, int32_t *page_table_host, voi
   }
   const auto &row = p->table[seq];
   for (int i = 0; i < p->cfg.max_pages_per_seq; ++i) page_table_host[i] = i < (int)row.size() ? row[i] : -1;
+  return ok();
+}
+
+int oscar_export_history_bf16(oscar_pool *p, int32_t seq, int32_t first, int32_t count, uint16_t *k, uint16_t *v,
+                              void *stream) {
+  int rc = check_seq(p, seq);
+  if (rc) return rc;
+  if (p->host_only || !p->dev.bf16_hist) return fail(OSCAR_EINVAL, "not a device pool with a BF16 history");
+  const int64_t n_hist = std::max(0, p->len[seq] - kWindow);
+  if (first < 0 || count < 0 || first + (int64_t)count > n_hist)
+    return fail(OSCAR_EINVAL, "history range [%d, %d) outside [0, %lld)", first, first + count, (long long)n_hist);
+  if (count == 0) return ok();
+  if (!k || !v) return fail(OSCAR_EINVAL, "NULL output");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "export sync");
+  if ((rc = check_device_status(p))) return rc;
+  const int H = p->cfg.num_kv_heads, d = p->cfg.head_dim, bb = p->dev.block_bytes;
+  std::vector<uint16_t> page((size_t)H * bb / 2);
+  int cur = -1;
+  for (int64_t i = first; i < first + count; ++i) {
+    const int pg_idx = (int)(i / kPage), t = (int)(i % kPage);
+    if (pg_idx != cur) {
+      e = hipMemcpy(page.data(), p->dev.pages + (size_t)p->table[seq][pg_idx] * H * bb, (size_t)H * bb,
+                    hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "export copy");
+      cur = pg_idx;
+    }
+    for (int h = 0; h < H; ++h) {
+      const uint16_t *blk = page.data() + (size_t)h * bb / 2;
+      const size_t o = ((size_t)(i - first) * H + h) * d;
+      std::memcpy(k + o, blk + (size_t)t * d, d * 2);
+      std::memcpy(v + o, blk + (size_t)(kPage + t) * d, d * 2);
+    }
+  }
   return ok();
 }
 

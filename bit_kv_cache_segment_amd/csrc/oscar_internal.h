@@ -43,6 +43,9 @@ struct PoolDev {
   // synchronising call.
   int32_t wait_limit;
   uint32_t *status;
+  // 1: the history is kept in BF16 (OSCAR_POOL_BF16_HISTORY): a page block
+  // is K bf16 [64][d] then V bf16 [64][d], tokens copied, not encoded.
+  int32_t bf16_hist;
 };
 
 constexpr uint32_t kStatusWaitGaveUp = 1u;
@@ -77,6 +80,8 @@ constexpr int32_t kDefaultWaitLimit = 1 << 22;
 //      32d + 256 d/G + 4 (t * d/G + g)     (V)
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int block_bytes_for(int d, int G) { return 32 * d + 512 * d / G; }
+// (page, head) block of a BF16-history pool: K and V, 64 tokens x d bf16 each
+__host__ __device__ inline int bf16_block_bytes(int d) { return 4 * kPage * d; }
 __host__ __device__ inline int lane_share_off(int lane, int b) { return (b / 16) * 1024 + lane * 16 + b % 16; }
 __host__ __device__ inline int kcode_dword_off(int d, int t, int r, int m) {
   return lane_share_off(16 * r + t / 4, (t % 4) * (d / 16) + 4 * m);
@@ -202,6 +207,13 @@ hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t 
 // History entries [0, n_hist) of a sequence in the canonical layout, device
 // to device (codes 4-byte aligned: d/4 is a multiple of 4).
 hipError_t launch_export(const PoolDev &p, int seq, int n_hist, uint8_t *codes, uint16_t *params, hipStream_t s);
+// BF16-history pools: resident decode blocks per compute unit, the history
+// launch (partials in the decode workspace layout) and the merge launch.
+int bf16_decode_blocks_per_cu(const PoolDev &p);
+hipError_t launch_decode_bf16(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float scale, float *ws,
+                              hipStream_t s, const KernelTimer &t);
+hipError_t launch_decode_merge(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, hipStream_t s,
+                               const KernelTimer &t);
 // Resident prefill-attention blocks per compute unit (pool's real heads).
 int prefill_blocks_per_cu(const PoolDev &p);
 // Resident decode_main blocks per compute unit for this pool's shape.

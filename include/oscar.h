@@ -73,6 +73,16 @@ extern "C" {
  * within the kernel's rounding (relative differences of order 1e-4). */
 #define OSCAR_POOL_DETERMINISTIC 2u
 
+/* Pool flag: keep the history in BF16 instead of INT2: the oldest recent
+ * token is copied into its page as it is (no rotation, clipping or
+ * quantization), everything else (sink, recent window, pages, allocator,
+ * merge) as in the INT2 pool.  The baseline the 2-bit history is measured
+ * against ([N-results]: ~3x faster decode than BF16 at 100K context,
+ * batch 1).  Decode and append work as for INT2 pools (a step runs the
+ * append in its own launch); prefill attention and the code exports are
+ * INT2 only (EINVAL); oscar_export_history_bf16 exports the history. */
+#define OSCAR_POOL_BF16_HISTORY 4u
+
 typedef struct oscar_pool oscar_pool;  /* opaque, host side */
 
 typedef struct oscar_pool_config {
@@ -83,7 +93,7 @@ typedef struct oscar_pool_config {
     int32_t  group_size;        /* G: 64 or 128 channels per scale/zero, G <= d      */
     int32_t  num_pages;         /* history pages in the pool (>= 0)                  */
     int32_t  max_pages_per_seq; /* page-table width                                  */
-    uint32_t flags;             /* OR of OSCAR_POOL_HOST_ONLY, OSCAR_POOL_DETERMINISTIC */
+    uint32_t flags;             /* OR of OSCAR_POOL_* flags                          */
     uint64_t page_shuffle_seed; /* seeds the free-list order                         */
 } oscar_pool_config;
 
@@ -285,6 +295,12 @@ int oscar_export_history(oscar_pool *pool, int32_t seq, int32_t first, int32_t c
  * Errors: EINVAL (bad seq, host-only pool, NULL or misaligned buffers), EHIP. */
 int oscar_export_state(oscar_pool *pool, int32_t seq, int32_t *page_table_host,
                        void *codes_dev, void *params_dev, void *stream);
+
+/* BF16-history pools: history entries [first, first+count) of a sequence
+ * to host memory, k and v bf16 [count][Hkv][d].  Synchronous.
+ * Errors: EINVAL (range, not a device BF16-history pool), EHIP. */
+int oscar_export_history_bf16(oscar_pool *pool, int32_t seq, int32_t first, int32_t count,
+                              uint16_t *k, uint16_t *v, void *stream);
 
 /* Copy a sequence's BF16 windows to host memory: sink_k/sink_v
  * [64][Hkv][d] (slot = position) and recent_k/recent_v [256][Hkv][d]
