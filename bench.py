@@ -223,6 +223,79 @@ def prefill_main(args):
     print(json.dumps(res), flush=True)
 
 
+def compare_bf16_main(args):
+    """Decode at long context, batch 1: the same tokens in an INT2-history
+    pool and in a BF16-history pool (OSCAR_POOL_BF16_HISTORY), decode
+    attention (oscar_decode_attn) and the serving step (oscar_decode_step)
+    timed on each; pools rotate so the read set exceeds the 256 MB cache."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_segment_amd as ok
+    import harness
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lengths0 = [int(x) for x in synth.lengths(w)]
+    ids = list(range(w.batch))
+    total = args.warmup + args.steps
+    per = -(-total // args.layers)
+    RK, RV, cK, cV = harness.tables(w)
+    qs = [synth.queries(w, s, device="cuda").view(torch.uint16).contiguous() for s in range(total)]
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    res = {}
+    for name, flags in (("int2", 0), ("bf16", ok.POOL_BF16_HISTORY)):
+        cfg = harness.config_for(w, lengths0, extra_tokens=per, flags=flags)
+        pools = []
+        for layer in range(args.layers):
+            p = ok.Pool(cfg, RK, RV, cK, cV, max_batch=w.batch)
+            harness.prefill_all(p, w, lengths0)
+            pools.append(p)
+        toks = [harness.step_tokens(w, [L + a for L in lengths0]) for a in range(per)]
+        torch.cuda.synchronize()
+        timing = {}
+        for kind in ("decode", "step"):
+            def run(s):
+                p = pools[s % args.layers]
+                if kind == "decode":
+                    p.decode(ids, qs[s], out)
+                else:
+                    a = s // args.layers
+                    p.step(ids, toks[a][0], toks[a][1], qs[s], out)
+            for s in range(args.warmup):
+                run(s)
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for s in range(args.warmup, total):
+                run(s)
+            ev1.record()
+            torch.cuda.synchronize()
+            timing[kind] = ev0.elapsed_time(ev1) / args.steps * 1e3  # us
+        res[name] = timing
+        res[name]["pool_bytes_per_layer"] = ok.oscar_pool_bytes(cfg)
+        del pools
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    line = {
+        "metric": "decode latency at long context, batch 1: INT2 history vs BF16 history (same pool, same tokens)",
+        "value": res["bf16"]["decode"] / res["int2"]["decode"], "unit": "x (BF16 time / INT2 time, decode attention)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "data": "synthetic (seeded; K/V ~ N(0,1) with 4 outlier channels x20)",
+        "config": {"workload": w.name, "batch": w.batch, "context": lengths0[0], "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "group_size": w.group_size,
+                   "layer_pools": args.layers},
+        "int2_us": {"decode": res["int2"]["decode"], "step": res["int2"]["step"]},
+        "bf16_us": {"decode": res["bf16"]["decode"], "step": res["bf16"]["step"]},
+        "step_speedup": res["bf16"]["step"] / res["int2"]["step"],
+        "pool_bytes_per_layer": {"int2": res["int2"]["pool_bytes_per_layer"],
+                                 "bf16": res["bf16"]["pool_bytes_per_layer"]},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,8 +315,9 @@ def main():
                          "(each timed launch adds a few microseconds to its step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
-    ap.add_argument("--mode", choices=["decode", "prefill"], default="decode",
-                    help="decode: the serving step (headline); prefill: a prefill chunk's attention")
+    ap.add_argument("--mode", choices=["decode", "prefill", "compare_bf16"], default="decode",
+                    help="decode: the serving step (headline); prefill: a prefill chunk's attention; "
+                         "compare_bf16: INT2 vs BF16 history at long context, batch 1")
     ap.add_argument("--prefill-len", type=int, default=32768, help="prefill mode: prompt length")
     ap.add_argument("--prefill-chunk", type=int, default=2048, help="prefill mode: queries of the last chunk")
     args = ap.parse_args()
@@ -252,6 +326,11 @@ def main():
               "multi-GPU mode; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.mode == "compare_bf16":
+        if args.workload == "fused_64x_4k_64k":
+            args.workload = "qwen3_8b_100k_b1"
+        compare_bf16_main(args)
+        return
     if args.mode == "prefill":
         if args.workload == "fused_64x_4k_64k":
             args.workload = "qwen3_8b_32k"

@@ -143,6 +143,9 @@ WORKLOADS = {
     # fused serving step: batch 64, L uniform in [4096, 65536], 256 steps
     # (the group size is not fixed by the workload description; 128 is used)
     "fused_64x_4k_64k": Workload("fused_64x_4k_64k", 5, 64, 32, 8, 128, 128, 4096, 65536, steps=256),
+    # one sequence of 100,000 tokens, Qwen3-8B-shaped layer (the latency
+    # case: decode at 100K context, batch 1)
+    "qwen3_8b_100k_b1": Workload("qwen3_8b_100k_b1", 6, 1, 32, 8, 128, 128, 100000, 100000),
 }
 
 
