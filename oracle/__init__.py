@@ -327,13 +327,22 @@ def free_list(num_pages: int, seed: int) -> list:
 
 @dataclass
 class PoolModel:
-    """Host bookkeeping of the pool: lengths and page tables.
+    """Host bookkeeping of the pool: lengths, page tables, page references.
 
     Pages are popped from the front of the shuffled free list; a page is
     taken when a history token lands on slot 0 of a new page.  Within one
     append call sequences are served in the order given; a prefill takes its
-    pages in history order.  Releasing a sequence appends its pages, in page
-    table order, to the back of the free list.
+    pages in history order.
+
+    Prefix sharing (the article's compatibility with a radix prefix cache):
+    ``fork`` gives an empty sequence the whole state of another, its history
+    pages shared (each page counts the page tables that hold it).  Only the
+    history's last page is ever written again, when the next evicted token
+    lands in it; a sequence about to write into a page that another sequence
+    also holds first takes a page of its own from the free list (at that
+    point of the call's order) and copies the page into it (copy on write).
+    Releasing a sequence drops its references; pages that nobody holds any
+    more go, in page table order, to the back of the free list.
     """
     num_pages: int
     seed: int
@@ -341,6 +350,7 @@ class PoolModel:
     free: list = field(default_factory=list)
     length: dict = field(default_factory=dict)
     table: dict = field(default_factory=dict)
+    refs: dict = field(default_factory=dict)
 
     def __post_init__(self):
         self.free = free_list(self.num_pages, self.seed)
@@ -348,7 +358,9 @@ class PoolModel:
     def _take(self):
         if not self.free:
             raise MemoryError("pool out of pages")
-        return self.free.pop(0)
+        pg = self.free.pop(0)
+        self.refs[pg] = 1
+        return pg
 
     def prefill(self, seq: int, L: int):
         assert self.length.get(seq, 0) == 0
@@ -365,10 +377,26 @@ class PoolModel:
                 n_hist = L - WINDOW
                 if n_hist % PAGE == 0:
                     self.table.setdefault(s, []).append(self._take())
+                else:                          # writes into its last page
+                    i = n_hist // PAGE
+                    pg = self.table[s][i]
+                    if self.refs[pg] > 1:      # shared: copy on write
+                        self.refs[pg] -= 1
+                        self.table[s][i] = self._take()
             self.length[s] = L + 1
 
+    def fork(self, src: int, dst: int):
+        assert self.length.get(dst, 0) == 0 and not self.table.get(dst)
+        self.table[dst] = list(self.table.get(src, []))
+        for pg in self.table[dst]:
+            self.refs[pg] += 1
+        self.length[dst] = self.length.get(src, 0)
+
     def release(self, seq: int):
-        self.free.extend(self.table.get(seq, []))
+        for pg in self.table.get(seq, []):
+            self.refs[pg] -= 1
+            if self.refs[pg] == 0:
+                self.free.append(pg)
         self.table[seq] = []
         self.length[seq] = 0
 

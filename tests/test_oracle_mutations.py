@@ -266,6 +266,63 @@ def test_planted_page_allocation_mistake_fails_a_pin(monkeypatch):
     assert failed, "no pin catches a page taken one slot late"
 
 
+def _append_no_cow(self, seq_ids):
+    for s_ in seq_ids:
+        L = self.length.get(s_, 0)
+        if L >= oracle.WINDOW and (L - oracle.WINDOW) % oracle.PAGE == 0:
+            self.table.setdefault(s_, []).append(self._take())
+        self.length[s_] = L + 1
+
+
+def _append_cow_before_peers(self, seq_ids):
+    # copy on write taken after every new page of the call, not in call order
+    later = []
+    for s_ in seq_ids:
+        L = self.length.get(s_, 0)
+        if L >= oracle.WINDOW:
+            n_hist = L - oracle.WINDOW
+            if n_hist % oracle.PAGE == 0:
+                self.table.setdefault(s_, []).append(self._take())
+            elif self.refs[self.table[s_][n_hist // oracle.PAGE]] > 1:
+                later.append((s_, n_hist // oracle.PAGE))
+        self.length[s_] = L + 1
+    for s_, i in later:
+        self.refs[self.table[s_][i]] -= 1
+        self.table[s_][i] = self._take()
+
+
+def _release_ignoring_refs(self, seq):
+    self.free.extend(self.table.get(seq, []))
+    self.table[seq] = []
+    self.length[seq] = 0
+
+
+def _fork_without_refs(self, src, dst):
+    self.table[dst] = list(self.table.get(src, []))
+    self.length[dst] = self.length.get(src, 0)
+
+
+POOL_MISTAKES = {
+    "shared page written in place (no copy on write)": ("append", _append_no_cow),
+    "copies on write taken after the call's new pages": ("append", _append_cow_before_peers),
+    "release frees pages other sequences hold": ("release", _release_ignoring_refs),
+    "fork does not count the shared pages": ("fork", _fork_without_refs),
+}
+
+
+@pytest.mark.parametrize("name", list(POOL_MISTAKES))
+def test_planted_prefix_sharing_mistake_fails_a_pin(name, monkeypatch):
+    attr, bad = POOL_MISTAKES[name]
+    monkeypatch.setattr(oracle.PoolModel, attr, bad)
+    failed = []
+    for pin_name, pin in PY_PINS:
+        try:
+            pin()
+        except (AssertionError, KeyError):
+            failed.append(pin_name)
+    assert failed, f"no pin catches: {name}"
+
+
 def test_python_pins_pass_unplanted():
     for pin_name, pin in PY_PINS:
         pin()

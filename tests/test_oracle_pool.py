@@ -96,3 +96,64 @@ def test_synthetic_generator_properties():
     a = synth.kv_tokens(w, 1, 5, 100, 50)
     b = synth.kv_tokens(w, 1, 5, 120, 50)
     assert (a[20:] == b[:30]).all()
+
+
+def test_prefix_sharing_hand_worked():
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "prefix_sharing.txt")
+    F = oracle.free_list(10, 77)
+    m = oracle.PoolModel(10, 77, 8)
+    for ln in open(path):
+        ln = ln.strip()
+        if not ln or ln.startswith("#"):
+            continue
+        if ln.startswith("free "):
+            assert m.free == [F[int(k)] for k in ln.split()[1].split(",")]
+            continue
+        op, want = (x.strip() for x in ln.split("|"))
+        name, *args = op.split()
+        args = [int(a) for a in args]
+        if name == "prefill":
+            m.prefill(args[0], args[1])
+        elif name == "fork":
+            m.fork(args[0], args[1])
+        elif name == "append":
+            m.append(args)
+        elif name == "release":
+            m.release(args[0])
+        for item in want.split():
+            seq, pages = item.split(":")
+            assert m.table[int(seq)] == [F[int(k)] for k in pages.split(",") if k != ""], (op, item)
+    # every page is back exactly once
+    assert sorted(m.free) == list(range(10)) and all(v == 0 for v in m.refs.values())
+
+
+def test_prefix_sharing_invariants_random():
+    # random operations: a page is held by exactly as many tables as its
+    # count says; held pages are never on the free list; nothing is lost
+    rng = np.random.default_rng(3)
+    m = oracle.PoolModel(400, 5, 60)
+    for _ in range(3000):
+        op = rng.integers(0, 10)
+        s = int(rng.integers(0, 8))
+        if op == 0 and m.length.get(s, 0) == 0:
+            L = int(rng.integers(0, 1500))
+            if -(-max(0, L - 320) // 64) <= min(len(m.free), 20):
+                m.prefill(s, L)
+        elif op == 1:
+            d = int(rng.integers(0, 8))
+            if d != s and m.length.get(d, 0) == 0:
+                m.fork(s, d)
+        elif op == 2:
+            m.release(s)
+        else:
+            ids = [int(x) for x in rng.permutation(8)[: rng.integers(1, 9)]]
+            if len(m.free) >= len(ids) and all(len(m.table.get(i, [])) < 59 for i in ids):
+                m.append(ids)
+        held = {}
+        for t in m.table.values():
+            for pg in t:
+                held[pg] = held.get(pg, 0) + 1
+        assert all(m.refs[pg] == c for pg, c in held.items())
+        assert not set(held) & set(m.free)
+        assert len(held) + len(m.free) == 400
