@@ -33,7 +33,7 @@ EXPORTS = (
     "oscar_pool_bytes", "oscar_pool_required_bytes", "oscar_decode_workspace_bytes", "oscar_pool_create", "oscar_pool_destroy",
     "oscar_prefill", "oscar_append_evict", "oscar_decode_attn", "oscar_decode_step",
     "oscar_decode_step_static", "oscar_prefill_workspace_bytes", "oscar_prefill_attn", "oscar_pool_check",
-    "oscar_release_seq",
+    "oscar_release_seq", "oscar_fork_seq",
     "oscar_seq_length", "oscar_page_table", "oscar_free_pages", "oscar_export_history",
     "oscar_export_state", "oscar_export_history_bf16", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
     "oscar_profile_end", "oscar_last_error",
@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "oscar_prefill_attn": [_P, _I32, _I32, _P, _P, ctypes.c_float, _P, _SZ, _P],
             "oscar_pool_check": [_P, _P],
             "oscar_release_seq": [_P, _I32],
+            "oscar_fork_seq": [_P, _I32, _I32, _P],
             "oscar_seq_length": [_P, _I32, _P],
             "oscar_page_table": [_P, _I32, _P, _I32, _P],
             "oscar_free_pages": [_P, _P],
@@ -235,6 +236,10 @@ def oscar_pool_check(h, stream=None, host_only=False):
 
 def oscar_release_seq(h, seq: int):
     _check(lib().oscar_release_seq(h, seq))
+
+
+def oscar_fork_seq(h, src: int, dst: int, stream=None, host_only=False):
+    _check(lib().oscar_fork_seq(h, src, dst, None if host_only else _stream(stream)))
 
 
 def oscar_seq_length(h, seq: int) -> int:
@@ -429,6 +434,10 @@ class Pool:
 
     def release(self, seq):
         oscar_release_seq(self.handle, seq)
+
+    def fork(self, src, dst, stream=None):
+        """Prefix sharing: empty sequence dst takes src's state, history pages shared."""
+        oscar_fork_seq(self.handle, src, dst, stream, host_only=self.host_only)
 
     def export_history(self, seq, first, count, stream=None):
         c = self.cfg

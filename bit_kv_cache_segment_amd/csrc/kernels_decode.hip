@@ -578,7 +578,7 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_ld
   if (L0 >= kWindow) {
     wave_sync(); // this wave's writes of the old token to shared memory
     const int n_hist0 = L0 - kWindow, t = n_hist0 % kPage;
-    const int page = t == 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage];
+    const int page = b.new_page[e] >= 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage];
     const float *clip = (kind ? p.clipV : p.clipK) + (size_t)kv * D;
     float y[CPL];
 #pragma unroll
@@ -668,7 +668,8 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_ld
         if (j % G == 0) *(uint32_t *)(blk + vparam_off(D, G, t, g)) = (uint32_t)s16[c] | ((uint32_t)z16[c] << 16);
       }
     }
-    if (t == 0 && kind == 0 && kv == 0 && lane == 0) p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage] = page;
+    if (b.new_page[e] >= 0 && kind == 0 && kv == 0 && lane == 0)
+      p.page_table[(size_t)seq * p.maxp + n_hist0 / kPage] = page;
   }
   publish(&sm.app_page_done, lane);
 }
@@ -1172,8 +1173,9 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     int id;
     if (fused_evict) {
       wait_count(&sm.win.app_page_done, 2, p);
-      // the evicted token started this page: its id is not in the table yet
-      id = (n_hist - 1) % kPage == 0 ? b.new_page[e] : ptab[pf];
+      // a page the append took (the evicted token started it, or it is the
+      // copy of a shared page): its id may not be in the table yet
+      id = b.new_page[e] >= 0 ? b.new_page[e] : ptab[pf];
     } else {
       id = ptab[pf];
     }

@@ -19,6 +19,8 @@
 // The rotation is d x d per token (~33 MFLOP per step for 64 sequences x 8
 // heads x K,V): it is far too small to pay for MFMA tiles, and MFMA would not
 // reproduce the fixed accumulation order the codes are defined with.
+#include <algorithm>
+
 #include "oscar_internal.h"
 
 namespace oscar {
@@ -223,13 +225,13 @@ __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, con
   }
   // evict the oldest recent token (held in this slot) into history n_hist
   const int n_hist = L - kWindow, pg_idx = n_hist / kPage, t = n_hist % kPage;
-  const int page = t == 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + pg_idx];
+  const int page = b.new_page[e] >= 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + pg_idx];
   if (p.bf16_hist) {
     // BF16-history pool: the token is copied as it is
     uint16_t *dst = (uint16_t *)(p.pages + ((size_t)page * Hkv + kv) * p.block_bytes) + (kind ? kPage * D : 0);
     dst[t * D + j] = rs[j];
     rs[j] = xnew; // this thread read element j above; no other thread touches it
-    if (t == 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
+    if (b.new_page[e] >= 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
     return;
   }
   const float xj = bf16f(rs[j]);
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, con
   const float y = fminf(fmaxf(acc, -c), c);
   uint16_t s16, z16;
   const uint32_t code = quantize_channel<D, G>(y, red, s16, z16);
-  if (t == 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
+  if (b.new_page[e] >= 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
   uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
   if (kind == 0) {
     store_k_code<D>(blk, t, code);
@@ -312,6 +314,37 @@ __global__ void export_state_kernel(PoolDev p, int seq, int n_hist, uint32_t *__
   codes[y] = out;
 }
 
+// ---------------------------------------------------------------------------
+// Prefix sharing.  Copy on write: grid (n, chunks), 256 threads; the blocks
+// of page c.src[i] for every kv head, one contiguous run of Hkv x block_bytes
+// bytes (a multiple of 16), go to page c.dst[i], 16 bytes per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void copy_pages_kernel(PoolDev p, PageCopies c) {
+  const size_t bytes = (size_t)p.Hkv * p.block_bytes, words = bytes / 16;
+  const uint4 *src = (const uint4 *)(p.pages + (size_t)c.src[blockIdx.x] * bytes);
+  uint4 *dst = (uint4 *)(p.pages + (size_t)c.dst[blockIdx.x] * bytes);
+  for (size_t i = (size_t)blockIdx.y * 256 + threadIdx.x; i < words; i += (size_t)gridDim.y * 256) dst[i] = src[i];
+}
+
+// Fork: grid (chunks, 5), 256 threads.  Regions 0..3 are sequence src's
+// sinkK, sinkV, recentK, recentV (Hkv x slots x d bf16 each, a multiple of 16
+// bytes), copied to sequence dst 16 bytes per thread; region 4 is the first
+// np entries of its page-table row.
+__global__ __launch_bounds__(256) void fork_kernel(PoolDev p, int src, int dst, int np) {
+  const int r = blockIdx.y;
+  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x, stride = (size_t)gridDim.x * 256;
+  if (r == 4) {
+    for (size_t i = tid; i < (size_t)np; i += stride)
+      p.page_table[(size_t)dst * p.maxp + i] = p.page_table[(size_t)src * p.maxp + i];
+    return;
+  }
+  const size_t words = (size_t)p.Hkv * (r < 2 ? kSink : kRecent) * p.d * 2 / 16;
+  const uint16_t *base = r == 0 ? p.sinkK : r == 1 ? p.sinkV : r == 2 ? p.recentK : p.recentV;
+  const uint4 *from = (const uint4 *)base + (size_t)src * words;
+  uint4 *to = (uint4 *)base + (size_t)dst * words;
+  for (size_t i = tid; i < words; i += stride) to[i] = from[i];
+}
+
 template <int D, int G>
 hipError_t export_impl(const PoolDev &p, int seq, int n_hist, uint8_t *codes, uint16_t *params, hipStream_t s) {
   const long total = (long)n_hist * p.Hkv * 2 * (D / 16 + D / G);
@@ -364,6 +397,21 @@ hipError_t launch_export(const PoolDev &p, int seq, int n_hist, uint8_t *codes, 
   if (p.d == 128 && p.G == 64) return export_impl<128, 64>(p, seq, n_hist, codes, params, s);
   if (p.d == 64 && p.G == 64) return export_impl<64, 64>(p, seq, n_hist, codes, params, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy_pages(const PoolDev &p, const PageCopies &c, hipStream_t s) {
+  if (c.n <= 0) return hipSuccess;
+  const size_t words = (size_t)p.Hkv * p.block_bytes / 16;
+  const unsigned chunks = (unsigned)std::min<size_t>((words + 255) / 256, 16);
+  hipLaunchKernelGGL(copy_pages_kernel, dim3(c.n, chunks), dim3(256), 0, s, p, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_fork(const PoolDev &p, int src, int dst, int np, hipStream_t s) {
+  const size_t words = (size_t)p.Hkv * kRecent * p.d * 2 / 16; // the largest region
+  const unsigned chunks = (unsigned)std::min<size_t>((words + 255) / 256, 64);
+  hipLaunchKernelGGL(fork_kernel, dim3(chunks, 5), dim3(256), 0, s, p, src, dst, np);
+  return hipGetLastError();
 }
 
 hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *kn, const uint16_t *vn,

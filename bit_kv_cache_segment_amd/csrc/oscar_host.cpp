@@ -19,6 +19,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 using namespace oscar;
@@ -191,6 +192,8 @@ struct oscar_pool {
   std::vector<std::vector<int32_t>> table;
   std::vector<int32_t> free_list; // pages [free_head, end) are free, front first
   size_t free_head = 0;
+  // Page tables holding each page (prefix sharing); 0 for a free page.
+  std::vector<int32_t> refs;
 
   int64_t n_free() const { return (int64_t)free_list.size() - (int64_t)free_head; }
   int32_t pop() { return free_list[free_head++]; }
@@ -283,6 +286,7 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
   p->host_only = host_only;
   p->len.assign(cfg->max_seqs, 0);
   p->table.assign(cfg->max_seqs, {});
+  p->refs.assign(cfg->num_pages, 0);
   // Free list: Fisher-Yates shuffle of [0, num_pages) driven by SplitMix64.
   p->free_list.resize(cfg->num_pages);
   for (int i = 0; i < cfg->num_pages; ++i) p->free_list[i] = i;
@@ -435,14 +439,106 @@ int oscar_prefill(oscar_pool *p, int32_t seq, const uint16_t *k, const uint16_t 
       return hip_fail(e, "prefill");
     }
   }
+  for (int32_t pg : row) p->refs[pg] = 1;
   p->table[seq] = std::move(row);
   p->len[seq] = L;
   return ok();
 }
 
+// Pages an append of one token to each of seq_ids[0..n) needs, in seq_ids
+// order: a fresh page where the evicted token starts one; a page of its own
+// where the token lands in a history page that another sequence also holds
+// (copy on write: it copies that page first), counting the references the
+// call's earlier copies have dropped.  With `a`, the pages are popped from
+// the free list (a->taken[i], or -1) and a->cow[i] names the page copied
+// (or -1); reference counts change only in commit_append.
+struct AppendPages {
+  std::vector<int32_t> taken, cow;
+};
+
+static int64_t append_pages(oscar_pool *p, const int32_t *seq_ids, int32_t n, AppendPages *a) {
+  if (a) {
+    a->taken.assign(n, -1);
+    a->cow.assign(n, -1);
+  }
+  std::unordered_map<int32_t, int32_t> dropped;
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    const int32_t s = seq_ids[i], L = p->len[s];
+    if (L < kWindow) continue;
+    const int32_t n_hist = L - kWindow;
+    int32_t cow = -1;
+    if (n_hist % kPage != 0) {
+      const int32_t pg = p->table[s][n_hist / kPage];
+      if (p->refs[pg] > 1) {
+        int32_t &dr = dropped[pg];
+        if (p->refs[pg] - dr > 1) {
+          ++dr;
+          cow = pg;
+        }
+      }
+      if (cow < 0) continue;
+    }
+    ++need;
+    if (a) {
+      a->taken[i] = p->pop();
+      a->cow[i] = cow;
+    }
+  }
+  return need;
+}
+
+// The host mirror of sequence seq_ids[i]'s append once it is enqueued.
+static void commit_append(oscar_pool *p, int32_t s, int32_t taken, int32_t cow) {
+  if (taken >= 0) {
+    if (cow >= 0) {
+      --p->refs[cow];
+      p->table[s].back() = taken; // the shared page was the history's last
+    } else {
+      p->table[s].push_back(taken);
+    }
+    p->refs[taken] = 1;
+  }
+  p->len[s] += 1;
+}
+
+// Enqueues the copies of the call's copy-on-write pages (before its
+// appends).  A failure leaves nothing to undo: the copies only write pages
+// that are still free.
+static hipError_t launch_cows(oscar_pool *p, const AppendPages &a, hipStream_t stream) {
+  PageCopies c;
+  c.n = 0;
+  for (size_t i = 0; i < a.cow.size(); ++i) {
+    if (a.cow[i] < 0) continue;
+    c.src[c.n] = a.cow[i];
+    c.dst[c.n] = a.taken[i];
+    if (++c.n == kMaxBatch) {
+      hipError_t e = launch_copy_pages(p->dev, c, stream);
+      if (e != hipSuccess) return e;
+      c.n = 0;
+    }
+  }
+  return launch_copy_pages(p->dev, c, stream);
+}
+
+// After a failed launch of batch `done` (earlier batches are in flight):
+// keep the mirror of sequences [0, done * kMaxBatch) and return the pages
+// popped for the rest, which were popped after theirs.
+static void commit_prefix(oscar_pool *p, const int32_t *seq_ids, const AppendPages &a, size_t head0,
+                          size_t done) {
+  size_t kept = 0;
+  const size_t m = std::min(done * (size_t)kMaxBatch, a.taken.size());
+  for (size_t j = 0; j < m; ++j) {
+    if (a.taken[j] >= 0) ++kept;
+    commit_append(p, seq_ids[j], a.taken[j], a.cow[j]);
+  }
+  p->free_head = head0 + kept;
+}
+
 // Checks of an append of one token to each of seq_ids[0..n) (n > 0): ids
-// valid and distinct, lengths below the limit, page-table room and free
-// pages for every eviction that starts a page.  Changes nothing.
+// valid and distinct, lengths below the limit, page-table room, and free
+// pages for every eviction that starts a page or copies a shared one.
+// Changes nothing.
 static int check_append(oscar_pool *p, const int32_t *seq_ids, int32_t n) {
   std::vector<int32_t> sorted(seq_ids, seq_ids + n);
   std::sort(sorted.begin(), sorted.end());
@@ -452,7 +548,6 @@ static int check_append(oscar_pool *p, const int32_t *seq_ids, int32_t n) {
     if (i && sorted[i] == sorted[i - 1])
       return fail(OSCAR_EINVAL, "sequence id %d repeated in one append", sorted[i]);
   }
-  int64_t need = 0;
   for (int i = 0; i < n; ++i) {
     int32_t s = seq_ids[i], L = p->len[s];
     if (L >= (1 << 30)) return fail(OSCAR_ERANGE, "sequence %d is at the length limit", s);
@@ -461,9 +556,9 @@ static int check_append(oscar_pool *p, const int32_t *seq_ids, int32_t n) {
       if (np > p->cfg.max_pages_per_seq)
         return fail(OSCAR_ERANGE, "sequence %d would need %d pages > max_pages_per_seq %d", s, np,
                     p->cfg.max_pages_per_seq);
-      ++need;
     }
   }
+  const int64_t need = append_pages(p, seq_ids, n, nullptr);
   if (need > p->n_free())
     return fail(OSCAR_ENOMEM, "append needs %lld new pages, %lld free", (long long)need,
                 (long long)p->n_free());
@@ -481,48 +576,39 @@ int oscar_append_evict(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
     int rc = check_append(p, seq_ids, n);
     if (rc) return rc;
   }
-  // Build the launches, taking pages in seq_ids order.
-  size_t head0 = p->free_head;
+  // Take the pages in seq_ids order, then build the launches.
+  const size_t head0 = p->free_head;
+  AppendPages a;
+  append_pages(p, seq_ids, n, &a);
   std::vector<AppendBatch> batches;
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
     AppendBatch b;
     b.n = std::min(kMaxBatch, n - i0);
     for (int e = 0; e < b.n; ++e) {
-      int32_t s = seq_ids[i0 + e], L = p->len[s];
-      b.seq[e] = s;
-      b.len[e] = L;
-      b.new_page[e] = (L >= kWindow && (L - kWindow) % kPage == 0) ? p->pop() : -1;
+      b.seq[e] = seq_ids[i0 + e];
+      b.len[e] = p->len[b.seq[e]];
+      b.new_page[e] = a.taken[i0 + e];
     }
     batches.push_back(b);
   }
   if (!p->host_only) {
+    hipError_t e = launch_cows(p, a, (hipStream_t)stream);
+    if (e != hipSuccess) {
+      p->free_head = head0;
+      return hip_fail(e, "copy-on-write launch");
+    }
     for (size_t i = 0; i < batches.size(); ++i) {
       const AppendBatch &b = batches[i];
-      hipError_t e = launch_append(p->dev, b, k_new + (size_t)i * kMaxBatch * p->cfg.num_kv_heads *
-                                                          p->cfg.head_dim,
-                                   v_new + (size_t)i * kMaxBatch * p->cfg.num_kv_heads *
-                                               p->cfg.head_dim,
-                                   (hipStream_t)stream, p->prof.next(2));
+      e = launch_append(p->dev, b, k_new + (size_t)i * kMaxBatch * p->cfg.num_kv_heads * p->cfg.head_dim,
+                        v_new + (size_t)i * kMaxBatch * p->cfg.num_kv_heads * p->cfg.head_dim,
+                        (hipStream_t)stream, p->prof.next(2));
       if (e != hipSuccess) {
-        if (i == 0) p->free_head = head0;  // nothing was enqueued
-        else {
-          // earlier launches are in flight: keep their effect in the mirror
-          for (size_t j = 0; j < i; ++j)
-            for (int q = 0; q < batches[j].n; ++q) {
-              int s = batches[j].seq[q];
-              if (batches[j].new_page[q] >= 0) p->table[s].push_back(batches[j].new_page[q]);
-              p->len[s] += 1;
-            }
-        }
+        commit_prefix(p, seq_ids, a, head0, i); // earlier launches are in flight
         return hip_fail(e, "append launch");
       }
     }
   }
-  for (const AppendBatch &b : batches)
-    for (int e = 0; e < b.n; ++e) {
-      if (b.new_page[e] >= 0) p->table[b.seq[e]].push_back(b.new_page[e]);
-      p->len[b.seq[e]] += 1;
-    }
+  for (int i = 0; i < n; ++i) commit_append(p, seq_ids[i], a.taken[i], a.cow[i]);
   p->compact();
   return ok();
 }
@@ -630,16 +716,21 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
     if (rc) return rc;
     return oscar_decode_attn(p, seq_ids, n, q, out, softmax_scale, workspace, workspace_bytes, stream);
   }
-  // the append's pages, taken in seq_ids order, then placed in launch order
+  // the append's pages, taken in seq_ids order, then placed in launch
+  // order; copies on write first
   const size_t head0 = p->free_head;
-  std::vector<int32_t> taken(n, -1);
-  for (int i = 0; i < n; ++i) {
-    const int32_t L = p->len[seq_ids[i]];
-    if (L >= kWindow && (L - kWindow) % kPage == 0) taken[i] = p->pop();
-  }
+  AppendPages a;
+  append_pages(p, seq_ids, n, &a);
   for (size_t i = 0; i < batches.size(); ++i) {
     DecodeBatch &b = batches[i];
-    for (int e = 0; e < b.n; ++e) b.new_page[e] = taken[i * kMaxBatch + b.row[e]];
+    for (int e = 0; e < b.n; ++e) b.new_page[e] = a.taken[i * kMaxBatch + b.row[e]];
+  }
+  {
+    hipError_t e = launch_cows(p, a, (hipStream_t)stream);
+    if (e != hipSuccess) {
+      p->free_head = head0;
+      return hip_fail(e, "copy-on-write launch");
+    }
   }
   for (size_t i = 0; i < batches.size(); ++i) {
     const size_t r0 = i * (size_t)kMaxBatch;
@@ -648,25 +739,11 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
                                  (float *)workspace, k_new + r0 * Hkv * d, v_new + r0 * Hkv * d,
                                  (hipStream_t)stream, tm, tg);
     if (e != hipSuccess) {
-      if (i == 0) {
-        p->free_head = head0; // nothing was enqueued
-        return hip_fail(e, "decode step launch");
-      }
-      // earlier launches are in flight: keep their effect in the mirror
-      for (size_t j = 0; j < i * (size_t)kMaxBatch; ++j) {
-        if (taken[j] >= 0) p->table[seq_ids[j]].push_back(taken[j]);
-        p->len[seq_ids[j]] += 1;
-      }
-      p->free_head = head0;
-      for (size_t j = 0; j < i * (size_t)kMaxBatch; ++j)
-        if (taken[j] >= 0) ++p->free_head;
+      commit_prefix(p, seq_ids, a, head0, i); // earlier launches are in flight
       return hip_fail(e, "decode step launch");
     }
   }
-  for (int i = 0; i < n; ++i) {
-    if (taken[i] >= 0) p->table[seq_ids[i]].push_back(taken[i]);
-    p->len[seq_ids[i]] += 1;
-  }
+  for (int i = 0; i < n; ++i) commit_append(p, seq_ids[i], a.taken[i], a.cow[i]);
   p->compact();
   return ok();
 }
@@ -763,9 +840,27 @@ int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *
 int oscar_release_seq(oscar_pool *p, int32_t seq) {
   int rc = check_seq(p, seq);
   if (rc) return rc;
-  for (int32_t pg : p->table[seq]) p->free_list.push_back(pg);
+  for (int32_t pg : p->table[seq])
+    if (--p->refs[pg] == 0) p->free_list.push_back(pg);
   p->table[seq].clear();
   p->len[seq] = 0;
+  return ok();
+}
+
+int oscar_fork_seq(oscar_pool *p, int32_t src, int32_t dst, void *stream) {
+  int rc = check_seq(p, src);
+  if (!rc) rc = check_seq(p, dst);
+  if (rc) return rc;
+  if (src == dst) return fail(OSCAR_EINVAL, "fork of sequence %d onto itself", src);
+  if (p->len[dst] != 0 || !p->table[dst].empty()) return fail(OSCAR_EINVAL, "sequence %d is not empty", dst);
+  if (p->len[src] == 0) return ok();
+  if (!p->host_only) {
+    hipError_t e = launch_fork(p->dev, src, dst, (int)p->table[src].size(), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "fork launch");
+  }
+  p->table[dst] = p->table[src];
+  for (int32_t pg : p->table[dst]) ++p->refs[pg];
+  p->len[dst] = p->len[src];
   return ok();
 }
 

@@ -98,11 +98,23 @@ __host__ __device__ inline int vparam_off(int d, int G, int t, int g) {
 }
 
 // By-value metadata of one append launch (<= kMaxBatch sequences).
+// new_page: the page the evicted token goes to when it is not the one the
+// page table holds at its index (a fresh page when the token starts one, or
+// the copy-on-write page of a shared last page), else -1; the launch writes
+// it into the page table.
 struct AppendBatch {
   int32_t n;
   int32_t seq[kMaxBatch];
   int32_t len[kMaxBatch];      // length before the append
-  int32_t new_page[kMaxBatch]; // page taken by this append, or -1
+  int32_t new_page[kMaxBatch];
+};
+
+// Copy-on-write copies of one launch: page src[i] to page dst[i], the
+// blocks of every kv head.
+struct PageCopies {
+  int32_t n;
+  int32_t src[kMaxBatch];
+  int32_t dst[kMaxBatch];
 };
 
 // By-value metadata of one decode launch (<= kMaxBatch sequences).  The
@@ -125,8 +137,8 @@ struct DecodeBatch {
   uint8_t nsplit[kMaxBatch];         // blocks per pair, 1 .. kMaxSplits
   int32_t layer_prefix[kMaxSplits + 1];
   // Fused step (oscar_decode_step): the launch first appends one token per
-  // sequence (len is the length after it).  new_page: the page the append
-  // takes for the evicted token, or -1 (launch order).
+  // sequence (len is the length after it).  new_page: as in AppendBatch
+  // (launch order).
   int32_t fused;
   // Prefill attention (oscar_prefill_attn): pf_g > 0 is the pool's query
   // heads per kv head and pf_rows the call's query count n_q.  The call's
@@ -204,6 +216,11 @@ hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const ui
                           int L, hipStream_t s);
 hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t s, const KernelTimer &t);
+// Copy-on-write page copies (every kv head of each page).
+hipError_t launch_copy_pages(const PoolDev &p, const PageCopies &c, hipStream_t s);
+// Fork: sequence src's window (sink and recent ring, all kv heads) and the
+// first np entries of its page-table row, copied to sequence dst.
+hipError_t launch_fork(const PoolDev &p, int src, int dst, int np, hipStream_t s);
 // History entries [0, n_hist) of a sequence in the canonical layout, device
 // to device (codes 4-byte aligned: d/4 is a multiple of 4).
 hipError_t launch_export(const PoolDev &p, int seq, int n_hist, uint8_t *codes, uint16_t *params, hipStream_t s);

@@ -154,8 +154,12 @@ int oscar_prefill(oscar_pool *pool, int32_t seq, const uint16_t *k,
  * (L >= 320), the oldest recent token (position 64 + n_hist, n_hist = L-320,
  * held in that same slot) is first rotated, clipped, quantized and packed
  * into history index n_hist (page n_hist/64, slot n_hist%64); a new page is
- * taken from the free list when n_hist % 64 == 0, sequences being served in
- * the order of seq_ids.
+ * taken from the free list when n_hist % 64 == 0, and also when slot
+ * n_hist%64 lies in a page that another sequence also holds (after
+ * oscar_fork_seq): then the page is first copied into the new one, which
+ * replaces it in this sequence's table (copy on write).  Sequences are
+ * served in the order of seq_ids, each seeing the references the earlier
+ * ones dropped.
  *   seq_ids: host int32 [n], distinct;  k_new, v_new: device bf16 [n][Hkv][d].
  * Errors: EINVAL (n < 0, bad or repeated id, null), ENOMEM, ERANGE. */
 int oscar_append_evict(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
@@ -257,9 +261,23 @@ int oscar_prefill_attn(oscar_pool *pool, int32_t seq, int32_t n_q, const uint16_
                        float *out, float softmax_scale, void *workspace,
                        size_t workspace_bytes, void *stream);
 
-/* Return a sequence's pages to the back of the free list (in page-table
- * order) and set its length to 0.  Host only.  Errors: EINVAL. */
+/* Drop a sequence's references to its pages and set its length to 0; the
+ * pages no other sequence holds go to the back of the free list, in
+ * page-table order.  Host only.  Errors: EINVAL. */
 int oscar_release_seq(oscar_pool *pool, int32_t seq);
+
+/* Prefix sharing, read from OSCAR's serving integration (the paged pool
+ * works with a radix prefix cache; news article on OSCAR, section "From
+ * offline calibration to online inference").  Give the empty sequence dst
+ * the whole state of sequence src: the same length, a copy of its sink and
+ * recent window, and its history pages, shared (each page counts the
+ * sequences that hold it).  Both sequences then decode and grow on their
+ * own: only a history's last page is ever written again, and oscar_append_evict
+ * / oscar_decode_step copy it first while it is shared.  A fork of an empty
+ * src leaves dst empty.  The copy is enqueued on `stream` after src's
+ * earlier work there; no page is taken.
+ * Errors: EINVAL (bad id, src == dst, dst not empty), EHIP. */
+int oscar_fork_seq(oscar_pool *pool, int32_t src, int32_t dst, void *stream);
 
 /* Current length of a sequence (host mirror).  Errors: EINVAL. */
 int oscar_seq_length(const oscar_pool *pool, int32_t seq, int32_t *L);

@@ -69,6 +69,75 @@ def test_host_bookkeeping_matches_oracle_pool_model():
     assert sum(p.length(s) for s in range(6)) > 0
 
 
+def test_host_bookkeeping_with_forks_matches_oracle_pool_model():
+    # prefix sharing: forks, copies on write and releases of shared pages
+    rng = np.random.default_rng(1)
+    p = _host_pool(num_pages=120, maxp=30, seed=77, max_seqs=8)
+    m = oracle.PoolModel(num_pages=120, seed=77, max_pages_per_seq=30)
+    forks = cows = 0
+    for step in range(1500):
+        op = rng.integers(0, 12)
+        s = int(rng.integers(0, 8))
+        if op == 0:
+            if p.length(s) == 0:
+                L = int(rng.integers(0, 1500))
+                if max(0, -(-(L - 320) // 64)) <= min(p.free_pages(), 30):
+                    p.prefill_len(s, L)
+                    m.prefill(s, L)
+        elif op == 1:
+            p.release(s)
+            m.release(s)
+        elif op <= 3:
+            d = int(rng.integers(0, 8))
+            try:
+                p.fork(s, d)
+            except ok.OscarError as e:
+                assert d == s or p.length(d) != 0, e
+                continue
+            m.fork(s, d)
+            forks += p.length(s) > 320
+        else:
+            live = [q for q in range(8) if p.length(q) > 0]
+            ids = [int(x) for x in rng.permutation(live)[: rng.integers(0, len(live) + 1)]]
+            before = {i: list(p.page_table(i)) for i in ids}
+            try:
+                p.append(ids, None, None)
+            except ok.OscarError:
+                continue
+            m.append(ids)
+            after = {i: list(p.page_table(i)) for i in ids}
+            cows += sum(len(after[i]) == len(before[i]) and after[i] != before[i] for i in ids)
+        for q in range(8):
+            assert p.length(q) == m.length.get(q, 0)
+            assert list(p.page_table(q)) == m.table.get(q, [])
+        assert p.free_pages() == len(m.free)
+    assert forks > 20 and cows > 20, (forks, cows)
+
+
+def test_fork_errors():
+    p = _host_pool()
+    p.prefill_len(0, 400)
+    p.prefill_len(1, 10)
+    before = _state(p, 6)
+    for args, code in [((0, 0), ok.EINVAL), ((0, 1), ok.EINVAL), ((0, 6), ok.EINVAL), ((-1, 2), ok.EINVAL)]:
+        with pytest.raises(ok.OscarError) as ei:
+            p.fork(*args)
+        assert ei.value.code == code and _state(p, 6) == before
+    p.fork(2, 3)                       # an empty source leaves the target empty
+    assert _state(p, 6) == before
+    # ENOMEM: a copy on write needs a free page like a new page does
+    q = _host_pool(num_pages=2, maxp=4)
+    q.prefill_len(0, 330)              # history 10 tokens: one page
+    q.fork(0, 1)
+    q.prefill_len(2, 384)              # the last free page
+    with pytest.raises(ok.OscarError) as ei:
+        q.append([1], None, None)
+    assert ei.value.code == ok.ENOMEM
+    q.release(2)
+    q.append([1, 0], None, None)       # seq 1 copies; seq 0 then writes in place
+    assert q.page_table(0) != q.page_table(1) and q.free_pages() == 0
+
+
 def test_errors_leave_state_unchanged():
     p = _host_pool(num_pages=10, maxp=4)
     p.prefill_len(0, 320 + 3 * 64)          # 3 pages
