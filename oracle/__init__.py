@@ -34,6 +34,10 @@ sanyangsrq.com, cited below as "the article"):
 * prefill attention over the pool: each of the last n_q positions attends
   causally (to itself and every earlier position) over the same decoded
   pool.  ``prefill_attention``.
+* calibration: the query covariance Q^T Q sets U for K, the score-weighted
+  value covariance V^T S^T S V sets U for V (section "OSCAR aims the
+  rotation at attention"); U is their eigenbasis.  ``query_covariance``,
+  ``value_covariance``, ``eigenbasis``, ``calibrate_layer``.
 
 Parity pins live in ``tests/test_oracle_*.py``.  Parity unpinned: the
 relation of the synthetic quantization error to the article's accuracy
@@ -204,6 +208,92 @@ def clip_thresholds(calib_bf16: np.ndarray, R: np.ndarray, pct: float = CLIP_PER
     lib().oracle_rotate_many(_ptr(x), N, d, _ptr(R), _ptr(y))
     a = np.sort(np.abs(y), axis=0)
     return np.array([percentile_linear(a[:, j], pct) for j in range(d)], dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------
+# calibration statistics and the eigenbasis U (offline, per layer and head)
+# ---------------------------------------------------------------------------
+
+def query_covariance(q_bf16: np.ndarray, num_kv_heads: int) -> np.ndarray:
+    """fp64 [Hkv][d][d]: Q^T Q per kv head, summed over the query heads that
+    share it (query head h belongs to kv head h // g).
+
+    The article (section "OSCAR aims the rotation at attention") has the K
+    rotation follow the query covariance, because K's error reaches the
+    logits through Q K^T.  q_bf16: uint16 [n][Hq][d] calibration queries."""
+    q = bf16_bits_to_f64(q_bf16)
+    n, Hq, d = q.shape
+    g = Hq // num_kv_heads
+    C = np.zeros((num_kv_heads, d, d))
+    for h in range(Hq):
+        C[h // g] += q[:, h, :].T @ q[:, h, :]
+    return C
+
+
+def causal_scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S [n][n] fp64: row t is the softmax of scale q_t . k_j over j <= t
+    (zero for j > t): the attention scores of a calibration sequence."""
+    n = q.shape[0]
+    logits = scale * (q @ k.T)
+    logits[np.triu_indices(n, 1)] = -np.inf
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def value_covariance(q_bf16: np.ndarray, k_bf16: np.ndarray, v_bf16: np.ndarray, scale: float) -> np.ndarray:
+    """fp64 [Hkv][d][d]: V^T S^T S V per kv head, summed over its query
+    heads, S the causal attention scores of that query head (same section:
+    V's error is weighted by the scores before it reaches the output).
+    q_bf16 uint16 [n][Hq][d]; k_bf16, v_bf16 uint16 [n][Hkv][d]."""
+    q = bf16_bits_to_f64(q_bf16)
+    k = bf16_bits_to_f64(k_bf16)
+    v = bf16_bits_to_f64(v_bf16)
+    n, Hq, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    C = np.zeros((Hkv, d, d))
+    for h in range(Hq):
+        S = causal_scores(q[:, h, :], k[:, h // g, :], scale)
+        V = v[:, h // g, :]
+        C[h // g] += V.T @ S.T @ S @ V
+    return C
+
+
+def eigenbasis(C: np.ndarray):
+    """(U [d][d], eigenvalues [d]) of a symmetric matrix, fp64: the columns
+    of U are orthonormal eigenvectors, eigenvalues in descending order, and
+    each column's entry of largest magnitude (the first such) is positive.
+    The order and the sign are our reading (the article fixes neither)."""
+    w, V = np.linalg.eigh(np.asarray(C, dtype=np.float64))
+    order = np.argsort(-w, kind="stable")
+    w, V = w[order], V[:, order]
+    for c in range(V.shape[1]):
+        if V[np.argmax(np.abs(V[:, c])), c] < 0:
+            V[:, c] = -V[:, c]
+    return V, w
+
+
+def rotation_grid(U: np.ndarray) -> np.ndarray:
+    """U as ``rotation`` takes it: rounded to fp32, then to the nearest
+    multiple of 2**-40 (so that U . H . Pi is exact in fp64)."""
+    u = np.asarray(U, dtype=np.float32).astype(np.float64)
+    return (np.round(u * 2.0**40) / 2.0**40).astype(np.float32)
+
+
+def calibrate_layer(q_bf16, k_bf16, v_bf16, scale: float, pct: float = CLIP_PERCENTILE):
+    """The offline step of one layer from one calibration sequence: per kv
+    head, U_K from the query covariance and U_V from the score-weighted
+    value covariance, R = U . H . Pi, and clip thresholds of the calibration
+    K and V tokens rotated by R.  Returns (R_K, R_V, clip_K, clip_V), fp32."""
+    Hkv = k_bf16.shape[1]
+    CK = query_covariance(q_bf16, Hkv)
+    CV = value_covariance(q_bf16, k_bf16, v_bf16, scale)
+    out = []
+    for C in (CK, CV):
+        out.append(np.stack([rotation(rotation_grid(eigenbasis(C[h])[0])) for h in range(Hkv)]))
+    clips = [np.stack([clip_thresholds(np.ascontiguousarray(x[:, h, :]), out[i][h], pct) for h in range(Hkv)])
+             for i, x in enumerate((k_bf16, v_bf16))]
+    return out[0], out[1], clips[0], clips[1]
 
 
 # ---------------------------------------------------------------------------

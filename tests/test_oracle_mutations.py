@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import test_oracle_attention
+import test_oracle_calibration
 import test_oracle_codec as pins
 import test_oracle_pool
 import test_oracle_rotation
@@ -114,7 +115,8 @@ def _calls(module):
     return out
 
 
-PY_PINS = _calls(test_oracle_rotation) + _calls(test_oracle_attention) + _calls(test_oracle_pool)
+PY_PINS = (_calls(test_oracle_rotation) + _calls(test_oracle_attention) + _calls(test_oracle_pool)
+           + _calls(test_oracle_calibration))
 
 
 def _bad_hadamard(d):
@@ -216,6 +218,52 @@ def _prefill_variant(kind):
     return f
 
 
+def _scores_no_mask(q, k, scale):
+    logits = scale * (q @ k.T)
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def _value_cov_variant(kind):
+    def f(q_bf16, k_bf16, v_bf16, scale):
+        q, k, v = (oracle.bf16_bits_to_f64(x) for x in (q_bf16, k_bf16, v_bf16))
+        n, Hq, d = q.shape
+        Hkv = k.shape[1]
+        g = Hq // Hkv
+        C = np.zeros((Hkv, d, d))
+        for h in range(Hq):
+            S = oracle.causal_scores(q[:, h, :], k[:, h // g, :], scale)
+            V = v[:, h // g, :]
+            if kind == "S":
+                C[h // g] += V.T @ S @ V
+            elif kind == "mean":
+                C[h // g] += V.T @ S.T @ S @ V / g
+            else:  # keys in place of the values
+                K = k[:, h // g, :]
+                C[h // g] += K.T @ S.T @ S @ K
+        return C
+    return f
+
+
+def _query_cov_mod(q_bf16, num_kv_heads):
+    q = oracle.bf16_bits_to_f64(q_bf16)
+    n, Hq, d = q.shape
+    C = np.zeros((num_kv_heads, d, d))
+    for h in range(Hq):
+        C[h % num_kv_heads] += q[:, h, :].T @ q[:, h, :]
+    return C
+
+
+def _eigen_variant(kind):
+    def f(C):
+        w, V = np.linalg.eigh(np.asarray(C, dtype=np.float64))
+        if kind == "ascending":
+            return V, w
+        order = np.argsort(-w, kind="stable")
+        return V[:, order], w[order]   # no sign convention
+    return f
+
+
 PY_MISTAKES = {
     "bit reversal left out": ("bitrev", lambda i, bits: i),
     "Hadamard sign from popcount(i | j)": ("hadamard_unnormalized", _bad_hadamard),
@@ -239,6 +287,14 @@ PY_MISTAKES = {
     "prefill query sees one position too many": ("prefill_attention", _prefill_variant("late")),
     "prefill queries taken at the first positions": ("prefill_attention", _prefill_variant("first")),
     "prefill without the causal mask": ("prefill_attention", _prefill_variant("none")),
+    "calibration scores without the causal mask": ("causal_scores", _scores_no_mask),
+    "value covariance V^T S V": ("value_covariance", _value_cov_variant("S")),
+    "value covariance averaged over the query heads": ("value_covariance", _value_cov_variant("mean")),
+    "value covariance of the keys": ("value_covariance", _value_cov_variant("K")),
+    "query head h to kv head h mod Hkv": ("query_covariance", _query_cov_mod),
+    "eigenvalues ascending": ("eigenbasis", _eigen_variant("ascending")),
+    "eigenvector signs left as computed": ("eigenbasis", _eigen_variant("nosign")),
+    "U not rounded to the grid": ("rotation_grid", lambda U: np.asarray(U, dtype=np.float32)),
 }
 
 
