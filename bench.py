@@ -223,6 +223,99 @@ def prefill_main(args):
     print(json.dumps(res), flush=True)
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def _cpu_calibration(name, n, heads):
+    """The oracle's covariances (Q^T Q and V^T S^T S V) of `heads` query heads
+    of a calibration sequence of n tokens, timed (inputs generated first)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    w = synth.WORKLOADS[name]
+    g = w.num_q_heads // w.num_kv_heads
+    q, k, v = synth.calibration_activations(w, n)
+    kvh = -(-heads // g)
+    qb = synth.bf16_bits(q[:, :heads].contiguous())
+    kb, vb = (synth.bf16_bits(x[:, :kvh].contiguous()) for x in (k, v))
+    t0 = time.perf_counter()
+    oracle.query_covariance(qb, kvh)
+    oracle.value_covariance(qb, kb, vb, 1 / np.sqrt(w.head_dim))
+    return time.perf_counter() - t0
+
+
+def calibrate_main(args):
+    """Offline calibration statistics of one layer on the GPU: for one
+    calibration sequence of n tokens, the causal attention S V of every
+    query head (calib_attn_kernel) and the Gram matrices Q^T Q and
+    (S V)^T (S V) per kv head on matrix cores (gram_kernel), i.e. one
+    oscar_calib_covariance call.  The attention kernel, which dominates,
+    is timed alone (oscar_calib_attention) for the roofline: 4 d flops per
+    (query head, visible key) against the fp32 vector peak."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_segment_amd as ok
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    n = args.calib_tokens
+    cpu = None
+    if args.cpu_seconds > 0:
+        # bounded sample: the oracle on 8 query heads (2 kv heads), scaled to all
+        heads = min(8, w.num_q_heads)
+        secs = _cpu_calibration(w.name, n, heads)
+        from threadpoolctl import threadpool_info
+        blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        cpu = {"value": n / (secs * w.num_q_heads / heads), "unit": "tokens/s per layer",
+               "cores": max(blas) if blas else 1, "kind": "oracle",
+               "sample": f"oracle covariances of {heads} of {w.num_q_heads} query heads at n = {n}, "
+                         f"{secs:.1f} s, scaled to all heads"}
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = (x.to(dev).view(torch.uint16).contiguous() for x in synth.calibration_activations(w, n))
+    Hkv, d = w.num_kv_heads, w.head_dim
+    scale = 1.0 / np.sqrt(d)
+    ck = torch.zeros((Hkv, d, d), dtype=torch.float32, device=dev)
+    cv = torch.zeros_like(ck)
+    ws = torch.empty(ok.oscar_calib_workspace_bytes(n, w.num_q_heads, d), dtype=torch.uint8, device=dev)
+    o = torch.empty((n, w.num_q_heads, d), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_step = timed(lambda: ok.oscar_calib_covariance(q, k, v, scale, ck, cv, ws))
+    ms_attn = timed(lambda: ok.oscar_calib_attention(q, k, v, scale, o))
+    flops = 4.0 * w.num_q_heads * d * (n * (n + 1) / 2)
+    tflops = flops / (ms_attn * 1e-3) / 1e12
+    res = {
+        "metric": "calibration tokens/s per layer (query and score-weighted value covariances)",
+        "value": n / (ms_step * 1e-3), "unit": "tokens/s per layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 inputs, fp32 attention and Gram accumulation",
+        "data": "synthetic (seeded; queries with a planted covariance, K/V with 4 outlier channels x20)",
+        "config": {"workload": f"{w.name} calibration sequence", "tokens": n, "q_heads": w.num_q_heads,
+                   "kv_heads": Hkv, "head_dim": d, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "calib_attn_kernel", "algorithmic_flops": flops, "ms_per_launch": ms_attn},
+        "cpu_baseline": cpu,
+        "detail": {"ms_attention": ms_attn, "ms_gram_both": ms_step - ms_attn},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def compare_bf16_main(args):
     """Decode at long context, batch 1: the same tokens in an INT2-history
     pool and in a BF16-history pool (OSCAR_POOL_BF16_HISTORY), decode
@@ -315,9 +408,11 @@ def main():
                          "(each timed launch adds a few microseconds to its step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
-    ap.add_argument("--mode", choices=["decode", "prefill", "compare_bf16"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "prefill", "compare_bf16", "calibrate"], default="decode",
                     help="decode: the serving step (headline); prefill: a prefill chunk's attention; "
-                         "compare_bf16: INT2 vs BF16 history at long context, batch 1")
+                         "compare_bf16: INT2 vs BF16 history at long context, batch 1; "
+                         "calibrate: offline covariances of one layer")
+    ap.add_argument("--calib-tokens", type=int, default=4096, help="calibrate mode: calibration sequence length")
     ap.add_argument("--prefill-len", type=int, default=32768, help="prefill mode: prompt length")
     ap.add_argument("--prefill-chunk", type=int, default=2048, help="prefill mode: queries of the last chunk")
     args = ap.parse_args()
@@ -330,6 +425,11 @@ def main():
         if args.workload == "fused_64x_4k_64k":
             args.workload = "qwen3_8b_100k_b1"
         compare_bf16_main(args)
+        return
+    if args.mode == "calibrate":
+        if args.workload == "fused_64x_4k_64k":
+            args.workload = "qwen3_8b_32k"
+        calibrate_main(args)
         return
     if args.mode == "prefill":
         if args.workload == "fused_64x_4k_64k":

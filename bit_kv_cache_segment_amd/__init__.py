@@ -35,7 +35,8 @@ EXPORTS = (
     "oscar_decode_step_static", "oscar_prefill_workspace_bytes", "oscar_prefill_attn", "oscar_pool_check",
     "oscar_release_seq", "oscar_fork_seq",
     "oscar_seq_length", "oscar_page_table", "oscar_free_pages", "oscar_export_history",
-    "oscar_export_state", "oscar_export_history_bf16", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip", "oscar_profile_begin",
+    "oscar_export_state", "oscar_export_history_bf16", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip",
+    "oscar_calib_workspace_bytes", "oscar_calib_attention", "oscar_calib_covariance", "oscar_calib_rotation", "oscar_profile_begin",
     "oscar_profile_end", "oscar_last_error",
 )
 
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
             "oscar_export_window": [_P, _I32, _P, _P, _P, _P, _P],
             "oscar_build_rotation": [_I32, _P, _P],
             "oscar_calibrate_clip": [_I32, ctypes.c_int64, _P, _P, ctypes.c_double, _P],
+            "oscar_calib_workspace_bytes": [_I32, _I32, _I32, _P],
+            "oscar_calib_attention": [_I32, _I32, _I32, _I32, _P, _P, _P, ctypes.c_float, _P, _P],
+            "oscar_calib_covariance": [_I32, _I32, _I32, _I32, _P, _P, _P, ctypes.c_float, _P, _P, _P, _SZ, _P],
+            "oscar_calib_rotation": [_I32, _P, _P, _P, _P],
             "oscar_profile_begin": [_P, _I32, ctypes.c_uint32, _I32],
             "oscar_profile_end": [_P, _P],
         }
@@ -311,6 +316,48 @@ def oscar_calibrate_clip(x_bf16: np.ndarray, R: np.ndarray, pct: float = 99.0) -
     out = np.empty(d, dtype=np.float32)
     _check(lib().oscar_calibrate_clip(d, n, _np_ptr(x), _np_ptr(R), float(pct), _np_ptr(out)))
     return out
+
+
+def oscar_calib_workspace_bytes(n: int, num_q_heads: int, head_dim: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().oscar_calib_workspace_bytes(n, num_q_heads, head_dim, ctypes.byref(b)))
+    return b.value
+
+
+def oscar_calib_attention(q, k, v, softmax_scale: float, out=None, stream=None):
+    """S V per query head (device fp32 [n][Hq][d]) of one calibration sequence:
+    q bf16 [n][Hq][d], k, v bf16 [n][Hkv][d] (device tensors)."""
+    import torch
+    n, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty((n, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().oscar_calib_attention(n, Hq, Hkv, d, _dev_ptr(q), _dev_ptr(k), _dev_ptr(v),
+                                       float(softmax_scale), _dev_ptr(out), _stream(stream)))
+    return out
+
+
+def oscar_calib_covariance(q, k, v, softmax_scale: float, cov_k, cov_v, workspace=None, stream=None):
+    """Adds Q^T Q and (S V)^T (S V) per kv head to cov_k, cov_v (device fp32 [Hkv][d][d])."""
+    import torch
+    n, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if workspace is None:
+        workspace = torch.empty(max(1, oscar_calib_workspace_bytes(n, Hq, d)), dtype=torch.uint8, device=q.device)
+    _check(lib().oscar_calib_covariance(n, Hq, Hkv, d, _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), float(softmax_scale),
+                                        _dev_ptr(cov_k), _dev_ptr(cov_v), _dev_ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def oscar_calib_rotation(cov: np.ndarray):
+    """(R, U [d][d] fp32, eigenvalues [d] fp64, descending) of one head's host covariance."""
+    cov = np.ascontiguousarray(cov, dtype=np.float32)
+    d = cov.shape[-1]
+    R = np.empty((d, d), dtype=np.float32)
+    U = np.empty((d, d), dtype=np.float32)
+    w = np.empty(d, dtype=np.float64)
+    _check(lib().oscar_calib_rotation(d, _np_ptr(cov), _np_ptr(U), _np_ptr(R), _np_ptr(w)))
+    return R, U, w
 
 
 PROFILE_DECODE_MAIN, PROFILE_DECODE_MERGE, PROFILE_APPEND = 1, 2, 4

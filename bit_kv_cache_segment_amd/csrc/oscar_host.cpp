@@ -1118,6 +1118,155 @@ int oscar_build_rotation(int32_t d, const float *U, float *R) {
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// Calibration (news article on OSCAR, section "OSCAR aims the rotation at
+// attention"): covariances on the device, eigenbasis on the host.
+// ---------------------------------------------------------------------------
+static int check_calib_shape(int32_t n, int32_t Hq, int32_t Hkv, int32_t d) {
+  if (n < 0 || n > (1 << 24)) return fail(OSCAR_EINVAL, "n = %d outside [0, 2^24]", n);
+  if (Hkv < 1 || Hkv > 64 || Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 64)
+    return fail(OSCAR_EINVAL, "heads %d / %d: Hq must be a multiple of Hkv (Hkv <= 64, Hq/Hkv <= 64)", Hq, Hkv);
+  if (d != 64 && d != 128) return fail(OSCAR_EINVAL, "head_dim %d must be 64 or 128", d);
+  return OSCAR_OK;
+}
+
+static int check_calib_inputs(const uint16_t *q, const uint16_t *k, const uint16_t *v, float scale) {
+  if (!q || !k || !v) return fail(OSCAR_EINVAL, "NULL q, k or v");
+  if (((uintptr_t)k & 15) || ((uintptr_t)v & 3) || ((uintptr_t)q & 1))
+    return fail(OSCAR_EINVAL, "k must be 16-byte, v 4-byte and q 2-byte aligned");
+  if (!std::isfinite(scale)) return fail(OSCAR_EINVAL, "softmax_scale is not finite");
+  return OSCAR_OK;
+}
+
+int oscar_calib_workspace_bytes(int32_t n, int32_t num_q_heads, int32_t head_dim, size_t *bytes) {
+  if (!bytes || n < 0 || num_q_heads < 1 || head_dim < 1) return fail(OSCAR_EINVAL, "bad arguments");
+  *bytes = (size_t)n * num_q_heads * head_dim * sizeof(float);
+  return ok();
+}
+
+int oscar_calib_attention(int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, const uint16_t *q,
+                          const uint16_t *k, const uint16_t *v, float softmax_scale, float *out, void *stream) {
+  int rc = check_calib_shape(n, num_q_heads, num_kv_heads, head_dim);
+  if (rc) return rc;
+  if (n == 0) return ok();
+  rc = check_calib_inputs(q, k, v, softmax_scale);
+  if (rc) return rc;
+  if (!out || ((uintptr_t)out & 3)) return fail(OSCAR_EINVAL, "out is NULL or not 4-byte aligned");
+  hipError_t e = launch_calib_attn(n, num_q_heads, num_kv_heads, head_dim, q, k, v, softmax_scale, out,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "calibration attention launch");
+  return ok();
+}
+
+int oscar_calib_covariance(int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, const uint16_t *q,
+                           const uint16_t *k, const uint16_t *v, float softmax_scale, float *cov_k, float *cov_v,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_calib_shape(n, num_q_heads, num_kv_heads, head_dim);
+  if (rc) return rc;
+  if (n == 0) return ok();
+  rc = check_calib_inputs(q, k, v, softmax_scale);
+  if (rc) return rc;
+  if (!cov_k || !cov_v || ((uintptr_t)cov_k & 3) || ((uintptr_t)cov_v & 3))
+    return fail(OSCAR_EINVAL, "cov_k or cov_v is NULL or not 4-byte aligned");
+  const size_t need = (size_t)n * num_q_heads * head_dim * sizeof(float);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 3))
+    return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required (or NULL, or not 4-byte aligned)",
+                workspace_bytes, need);
+  float *o = (float *)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_calib_attn(n, num_q_heads, num_kv_heads, head_dim, q, k, v, softmax_scale, o, s);
+  if (e == hipSuccess) e = launch_calib_gram(n, num_q_heads, num_kv_heads, head_dim, q, o, cov_k, cov_v, s);
+  if (e != hipSuccess) return hip_fail(e, "calibration covariance launch");
+  return ok();
+}
+
+} // extern "C"
+
+// Eigen-decomposition of a symmetric d x d matrix (row-major, fp64) by the
+// cyclic Jacobi method (Golub and Van Loan, "Matrix Computations", the
+// symmetric Schur decomposition and cyclic Jacobi): sweeps over every
+// off-diagonal pair (p, q), each zeroed by a plane rotation J with
+// tan = sign(tau) / (|tau| + sqrt(1 + tau^2)), tau = (a_qq - a_pp) / (2 a_pq);
+// A <- J^T A J, V <- V J, until the off-diagonal mass is below 1e-30 of the
+// diagonal's (a relative Frobenius size of 1e-15).  On return diag(A) holds
+// the eigenvalues and the columns of V the eigenvectors.
+static void jacobi_eigen(int d, std::vector<double> &A, std::vector<double> &V) {
+  V.assign((size_t)d * d, 0.0);
+  for (int i = 0; i < d; ++i) V[(size_t)i * d + i] = 1.0;
+  auto a = [&](int i, int j) -> double & { return A[(size_t)i * d + j]; };
+  for (int sweep = 0; sweep < 60; ++sweep) {
+    double off = 0.0, diag = 0.0;
+    for (int i = 0; i < d; ++i) {
+      diag += a(i, i) * a(i, i);
+      for (int j = i + 1; j < d; ++j) off += a(i, j) * a(i, j);
+    }
+    if (off == 0.0 || off <= 1e-30 * diag) break;
+    for (int p = 0; p < d - 1; ++p)
+      for (int q = p + 1; q < d; ++q) {
+        const double apq = a(p, q);
+        if (apq == 0.0) continue;
+        const double tau = (a(q, q) - a(p, p)) / (2.0 * apq);
+        const double t = (tau >= 0.0 ? 1.0 : -1.0) / (std::fabs(tau) + std::sqrt(1.0 + tau * tau));
+        const double c = 1.0 / std::sqrt(1.0 + t * t), s = t * c;
+        for (int k = 0; k < d; ++k) { // columns p, q: A J
+          const double akp = a(k, p), akq = a(k, q);
+          a(k, p) = c * akp - s * akq;
+          a(k, q) = s * akp + c * akq;
+        }
+        for (int k = 0; k < d; ++k) { // rows p, q: J^T (A J)
+          const double apk = a(p, k), aqk = a(q, k);
+          a(p, k) = c * apk - s * aqk;
+          a(q, k) = s * apk + c * aqk;
+        }
+        a(p, q) = a(q, p) = 0.0;
+        for (int k = 0; k < d; ++k) {
+          double &vkp = V[(size_t)k * d + p], &vkq = V[(size_t)k * d + q];
+          const double x = vkp, y = vkq;
+          vkp = c * x - s * y;
+          vkq = s * x + c * y;
+        }
+      }
+  }
+}
+
+extern "C" {
+
+int oscar_calib_rotation(int32_t d, const float *cov, float *U, float *R, double *eigenvalues) {
+  if (d < 1 || d > 1024 || (d & (d - 1))) return fail(OSCAR_EINVAL, "d = %d is not a power of two <= 1024", d);
+  if (!cov || !R) return fail(OSCAR_EINVAL, "NULL cov or R");
+  std::vector<double> A((size_t)d * d), V;
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      const float x = cov[(size_t)i * d + j], y = cov[(size_t)j * d + i];
+      if (!std::isfinite(x)) return fail(OSCAR_EINVAL, "covariance entry (%d, %d) is not finite", i, j);
+      A[(size_t)i * d + j] = 0.5 * ((double)x + (double)y);
+    }
+  jacobi_eigen(d, A, V);
+  // eigenvalues descending (equal ones keep their index order)
+  std::vector<int> order(d);
+  for (int i = 0; i < d; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return A[(size_t)x * d + x] > A[(size_t)y * d + y]; });
+  // columns in that order, each with its first entry of largest magnitude
+  // positive, rounded to fp32 and then to the nearest multiple of 2^-40
+  // (ties to even), the grid on which U . H . Pi is exact in fp64
+  std::vector<float> Ug((size_t)d * d);
+  for (int c = 0; c < d; ++c) {
+    const int src = order[c];
+    int jmax = 0;
+    for (int j = 1; j < d; ++j)
+      if (std::fabs(V[(size_t)j * d + src]) > std::fabs(V[(size_t)jmax * d + src])) jmax = j;
+    const double sign = V[(size_t)jmax * d + src] < 0.0 ? -1.0 : 1.0;
+    for (int j = 0; j < d; ++j) {
+      const float f = (float)(sign * V[(size_t)j * d + src]);
+      Ug[(size_t)j * d + c] = (float)std::ldexp(std::nearbyint(std::ldexp((double)f, 40)), -40);
+    }
+    if (eigenvalues) eigenvalues[c] = A[(size_t)src * d + src];
+  }
+  if (U) std::memcpy(U, Ug.data(), Ug.size() * sizeof(float));
+  return oscar_build_rotation(d, Ug.data(), R);
+}
+
 int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R, double pct, float *clip) {
   if (d < 1 || d > 1024) return fail(OSCAR_EINVAL, "bad d = %d", d);
   if (n < 1 || !x || !R || !clip) return fail(OSCAR_EINVAL, "bad arguments");

@@ -249,6 +249,14 @@ hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t 
                          const KernelTimer &t_main, const KernelTimer &t_merge);
 
 
+// Calibration: O = causal softmax(scale Q K^T) V per query head (fp32
+// [n][Hq][d]); then cov_k[h] += sum of Q^T Q and cov_v[h] += sum of O^T O over
+// kv head h's query heads (either output may be null).
+hipError_t launch_calib_attn(int n, int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             float scale, float *o, hipStream_t s);
+hipError_t launch_calib_gram(int n, int Hq, int Hkv, int d, const uint16_t *q, const float *o, float *cov_k,
+                             float *cov_v, hipStream_t s);
+
 // Workspace (4-byte words) of one decode launch: window partials
 // [n][Hq][d + 2], then split partials [n][Hkv][smax][g][d + 2], smax the
 // launch's largest split count (slot s of a pair holds its split s).

@@ -345,6 +345,47 @@ int oscar_build_rotation(int32_t d, const float *U, float *R);
 int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R,
                          double pct, float *clip);
 
+/* Offline calibration statistics ([A]; the news article's section "OSCAR
+ * aims the rotation at attention": the K rotation follows the query
+ * covariance Q^T Q, the V rotation the score-weighted value covariance
+ * V^T S^T S V, per layer and head, from a few calibration samples).
+ * Inputs are one calibration sequence of n tokens of one layer:
+ *   q: device bf16 [n][Hq][d] (2-byte aligned);  k: device bf16 [n][Hkv][d]
+ *   (16-byte aligned);  v: device bf16 [n][Hkv][d] (4-byte aligned);
+ *   d = 64 or 128; Hq a multiple of Hkv; query head h uses kv head h/(Hq/Hkv).
+ * S is the causal attention of the sequence: row t is the softmax of
+ * softmax_scale q_t . k_j over j <= t.
+ *
+ * oscar_calib_attention: out = S V per query head, device fp32 [n][Hq][d]
+ * (the attention output; V^T S^T S V = out^T out).
+ * oscar_calib_covariance: for each kv head h, ADDS to cov_k[h] the sum over
+ * its query heads of Q^T Q and to cov_v[h] the sum of (S V)^T (S V); cov_k,
+ * cov_v: device fp32 [Hkv][d][d] (the caller zeroes them before the first
+ * sequence; several sequences accumulate).  Products and sums in fp32 (the
+ * Gram matrices on matrix cores).  workspace: device, >=
+ * oscar_calib_workspace_bytes(n, Hq, d) bytes (it receives S V).
+ * n = 0 does nothing.  Errors: EINVAL (shape, alignment, null, workspace too
+ * small, scale not finite), EHIP. */
+int oscar_calib_workspace_bytes(int32_t n, int32_t num_q_heads, int32_t head_dim, size_t *bytes);
+int oscar_calib_attention(int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          const uint16_t *q, const uint16_t *k, const uint16_t *v, float softmax_scale,
+                          float *out, void *stream);
+int oscar_calib_covariance(int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           const uint16_t *q, const uint16_t *k, const uint16_t *v, float softmax_scale,
+                           float *cov_k, float *cov_v, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Offline: the rotation of one head from its covariance ([A]): U is the
+ * eigenbasis of the symmetric host fp32 cov[d][d] (symmetrised as
+ * (C + C^T)/2 in fp64; cyclic Jacobi in fp64): column c is the eigenvector
+ * of the c-th largest eigenvalue, signed so that its first entry of largest
+ * magnitude is positive, rounded to fp32 and then to the nearest multiple
+ * of 2^-40.  R = U . H . Pi as oscar_build_rotation.  Outputs (host): R
+ * [d][d] fp32; U [d][d] fp32 and eigenvalues [d] fp64 (descending), each
+ * optional (NULL).  d a power of two <= 1024.  Errors: EINVAL (d, null,
+ * non-finite entry). */
+int oscar_calib_rotation(int32_t d, const float *cov, float *U, float *R, double *eigenvalues);
+
 /* Kernel timing with HIP events recorded on the launch stream around the
  * kernels selected by `kernels` (OSCAR_PROFILE_* bits) in the pool's decode
  * and append calls.  oscar_profile_begin creates event pairs for up to

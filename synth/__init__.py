@@ -21,7 +21,8 @@ arithmetic plus one table lookup and one fp32 multiply):
   fp32 and round to bf16 (round to nearest even).
 
 Streams: 0 lengths, 1 page shuffle seed, 2 U for K, 3 U for V,
-4 calibration tokens, 5 K tokens, 6 V tokens, 7 queries.
+4 calibration tokens, 5 K tokens, 6 V tokens, 7 queries, 8 calibration
+queries, 9 the orthogonal axes of the calibration queries' covariance.
 A token's value depends only on (seed, K|V, sequence, position, head,
 channel), so a prompt and the tokens appended to it later come from one
 stream and any sampled token can be regenerated without storing the pool.
@@ -37,6 +38,7 @@ import torch
 M32 = 0xFFFFFFFF
 STREAM_LENGTHS, STREAM_SHUFFLE, STREAM_UK, STREAM_UV = 0, 1, 2, 3
 STREAM_CALIB, STREAM_K, STREAM_V, STREAM_Q = 4, 5, 6, 7
+STREAM_CALIB_Q, STREAM_CALIB_B = 8, 9
 OUTLIER_CHANNELS = 4
 OUTLIER_FACTOR = 20.0
 POS_BITS = 20          # positions < 2**20 (1M tokens per sequence)
@@ -203,6 +205,36 @@ def calibration_tokens(w: Workload, kind: int, n: int, device="cpu") -> torch.Te
     vals = normals_f32(key, idx)
     vals = vals * _outlier_mask(outlier_channels(w, kind), d, device)[:, None, :]
     return vals.to(torch.bfloat16)
+
+
+CALIB_Q_DECAY = 16.0   # calibration query axis c has standard deviation 2^(-c / 16)
+
+
+def calibration_activations(w: Workload, n: int):
+    """(q bf16 [n][Hq][d], k, v bf16 [n][Hkv][d]) of one calibration sequence,
+    on the CPU.  K and V are the calibration tokens (the data's distribution,
+    outlier channels included).  Queries have a planted anisotropic
+    covariance: per query head, z diag(sigma) B^T with z standard normal
+    (counter generator, stream 8), sigma_c = 2^(-c/16), and B an orthogonal
+    matrix per kv head (QR of a seeded Gaussian, stream 9), shared by the
+    kv head's query heads; the product is taken in fp64 and rounded to bf16."""
+    Hq, Hkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    g = Hq // Hkv
+    k = calibration_tokens(w, 0, n).permute(1, 0, 2).contiguous()
+    v = calibration_tokens(w, 1, n).permute(1, 0, 2).contiguous()
+    key = stream_key(w.seed(STREAM_CALIB_Q), 0)
+    idx = ((torch.arange(n, dtype=torch.int64)[:, None, None] * Hq + torch.arange(Hq)[None, :, None]) * d
+           + torch.arange(d)[None, None, :])
+    z = normals_f32(key, idx).double()
+    sigma = torch.pow(2.0, -torch.arange(d, dtype=torch.float64) / CALIB_Q_DECAY)
+    rng = np.random.default_rng([w.seed(STREAM_CALIB_B)])
+    q = torch.empty((n, Hq, d), dtype=torch.float64)
+    for kv in range(Hkv):
+        B, r = np.linalg.qr(rng.standard_normal((d, d)))
+        B = torch.from_numpy(B * np.sign(np.diag(r))[None, :])
+        for h in range(kv * g, kv * g + g):
+            q[:, h, :] = (z[:, h, :] * sigma) @ B.T
+    return q.to(torch.bfloat16), k, v
 
 
 def queries(w: Workload, step: int, device="cpu", batch: int | None = None) -> torch.Tensor:
