@@ -101,6 +101,10 @@ def configure(L):
     L.oracle_pack.argtypes = [P, ctypes.c_int, P]
     L.oracle_unpack.argtypes = [P, ctypes.c_int, P]
     L.oracle_encode.argtypes = [P, ctypes.c_long, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+    L.oracle_normalized.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+    L.oracle_quantize_lut.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P]
+    L.oracle_encode_lut.argtypes = [P, ctypes.c_long, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P]
+    L.oracle_normalized_many.argtypes = [P, ctypes.c_long, ctypes.c_int, ctypes.c_int, P, P, P]
     L.oracle_rotate_many.argtypes = [P, ctypes.c_long, ctypes.c_int, P, P]
     return L
 
@@ -314,6 +318,83 @@ def encode(x_bf16: np.ndarray, R: np.ndarray, clip: np.ndarray, G: int):
     return packed, s16, z16
 
 
+# ---------------------------------------------------------------------------
+# Lloyd-Max codebook variant (article, section "Why this matters for
+# long-context agents": the OSCAR code pairs the rotation with a Lloyd-Max
+# codebook).  Reading: the group's fp16 scale s and zero point z stay; the
+# four levels become z + (L_k / 64) s for a codebook L (integers 0..255,
+# non-decreasing, per kv head and K|V) fitted offline by Lloyd's algorithm
+# on the normalised values u = (y - z) / s of calibration tokens; a channel
+# takes the nearest level (ties to the lower).
+# ---------------------------------------------------------------------------
+
+LLOYD_ITERS = 32
+LLOYD_GRID = 2 ** 20   # u is fitted on multiples of 2^-20 (exact integer sums)
+
+
+def normalized_values(x_bf16: np.ndarray, R: np.ndarray, clip: np.ndarray, G: int) -> np.ndarray:
+    """fp32 u [N][d] = (y - z) / s of N bf16 vectors after rotation and clip
+    (the codec's own arithmetic, in C); -1 for groups with s == 0."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    N, d = x.shape
+    u = np.empty((N, d), dtype=np.float32)
+    lib().oracle_normalized_many(_ptr(x), N, d, G, _ptr(np.ascontiguousarray(R, dtype=np.float32)),
+                                 _ptr(np.ascontiguousarray(clip, dtype=np.float32)), _ptr(u))
+    return u
+
+
+def lloyd_max_levels(u: np.ndarray, iters: int = LLOYD_ITERS) -> np.ndarray:
+    """Lloyd's algorithm for a 4-level scalar quantizer of the values u >= 0
+    (negative entries, the s == 0 groups, are left out), fp64 levels.
+
+    The values are taken on the grid of 2^-20 (U = rint(u 2^20), integers,
+    so every cell sum is exact).  Start from the uniform levels 0, 1, 2, 3;
+    each iteration sets the thresholds midway between neighbouring levels,
+    puts a value in cell k when it lies above exactly k thresholds, and moves
+    each level to the mean of its cell (a level whose cell is empty stays)."""
+    u = np.asarray(u, dtype=np.float32).ravel()
+    U = np.rint(u[u >= 0].astype(np.float64) * LLOYD_GRID).astype(np.int64)
+    lev = np.array([0.0, 1.0, 2.0, 3.0])
+    for _ in range(iters):
+        thr = (lev[:-1] + lev[1:]) * (LLOYD_GRID / 2)      # in grid units
+        cell = (U[:, None] > thr[None, :]).sum(axis=1)
+        new = lev.copy()
+        for k in range(4):
+            sel = U[cell == k]
+            if len(sel):
+                new[k] = float(int(sel.sum())) / float(len(sel)) / LLOYD_GRID
+        lev = new
+    return lev
+
+
+def lloyd_max_codebook(u: np.ndarray, iters: int = LLOYD_ITERS) -> np.ndarray:
+    """uint8 [4]: the fitted levels on the stored grid, L_k = rint(64 level_k)
+    (ties to even), clamped to 0..255."""
+    return np.clip(np.rint(lloyd_max_levels(u, iters) * 64.0), 0, 255).astype(np.uint8)
+
+
+def encode_lut(x_bf16: np.ndarray, R: np.ndarray, clip: np.ndarray, G: int, L: np.ndarray):
+    """``encode`` with codebook L (uint8 [4]): nearest-level codes."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    N, d = x.shape
+    packed = np.empty((N, d // 4), dtype=np.uint8)
+    s16 = np.empty((N, d // G), dtype=np.uint16)
+    z16 = np.empty((N, d // G), dtype=np.uint16)
+    lib().oracle_encode_lut(_ptr(x), N, d, G, _ptr(np.ascontiguousarray(R, dtype=np.float32)),
+                            _ptr(np.ascontiguousarray(clip, dtype=np.float32)),
+                            _ptr(np.ascontiguousarray(L, dtype=np.uint8)), _ptr(packed), _ptr(s16), _ptr(z16))
+    return packed, s16, z16
+
+
+def dequantize_lut(packed, s16, z16, G: int, L) -> np.ndarray:
+    """z + s L[code] / 64 in fp64 (exact)."""
+    codes = unpack(packed)
+    lv = np.asarray(L, dtype=np.float64)[codes] / 64.0
+    s = np.repeat(f16_table()[s16], G, axis=-1)
+    z = np.repeat(f16_table()[z16], G, axis=-1)
+    return lv * s + z
+
+
 def quantize(y: np.ndarray, G: int):
     """Quantize already rotated+clipped fp32 vectors y [N][d]: (codes, s16, z16)."""
     y = np.ascontiguousarray(y, dtype=np.float32)
@@ -501,6 +582,12 @@ def decode_history(packed, s16, z16, G: int, R: np.ndarray) -> np.ndarray:
     return rot @ np.asarray(R, dtype=np.float64).T
 
 
+def decode_history_lut(packed, s16, z16, G: int, L, R: np.ndarray) -> np.ndarray:
+    """History tokens of the Lloyd-Max variant back in the original basis:
+    dequant_lut(codes) . R^T (fp64)."""
+    return dequantize_lut(packed, s16, z16, G, L) @ np.asarray(R, dtype=np.float64).T
+
+
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
     """Softmax attention of one query head over T tokens, fp64.
     q [d], K [T][d], V [T][d] -> out [d]."""
@@ -546,10 +633,11 @@ class SeqTokens:
 
 
 def build_sequence(k_bf16: np.ndarray, v_bf16: np.ndarray, R_K, R_V, clip_K, clip_V, G: int,
-                   heads=None) -> SeqTokens:
+                   heads=None, codebook=None) -> SeqTokens:
     """Pool contents of a sequence whose tokens (positions 0..L-1) are
     k_bf16/v_bf16 uint16 [L][Hkv][d]: sink and recent kept as bf16, history
-    positions encoded by the codec and decoded again."""
+    positions encoded by the codec and decoded again.  codebook: None for the
+    affine levels, else (L_K, L_V) uint8 [Hkv][4] (the Lloyd-Max variant)."""
     L, Hkv, d = k_bf16.shape
     heads = range(Hkv) if heads is None else heads
     _, hist, _ = segments(L)
@@ -559,10 +647,14 @@ def build_sequence(k_bf16: np.ndarray, v_bf16: np.ndarray, R_K, R_V, clip_K, cli
     if len(hist):
         h0, h1 = hist.start, hist.stop
         for kv in heads:
-            for name, src, R, c, dst in (("K", k_bf16, R_K, clip_K, K), ("V", v_bf16, R_V, clip_V, V)):
-                pk, s16, z16 = encode(src[h0:h1, kv, :], R[kv], c[kv], G)
+            for i, (name, src, R, c, dst) in enumerate((("K", k_bf16, R_K, clip_K, K), ("V", v_bf16, R_V, clip_V, V))):
+                if codebook is None:
+                    pk, s16, z16 = encode(src[h0:h1, kv, :], R[kv], c[kv], G)
+                    dst[h0:h1, kv, :] = decode_history(pk, s16, z16, G, R[kv])
+                else:
+                    pk, s16, z16 = encode_lut(src[h0:h1, kv, :], R[kv], c[kv], G, codebook[i][kv])
+                    dst[h0:h1, kv, :] = decode_history_lut(pk, s16, z16, G, codebook[i][kv], R[kv])
                 enc[(name, kv)] = (pk, s16, z16)
-                dst[h0:h1, kv, :] = decode_history(pk, s16, z16, G, R[kv])
     return SeqTokens(L, K, V, enc)
 
 

@@ -185,3 +185,79 @@ void oracle_rotate_many(const uint16_t *x, long N, int d, const float *R, float 
     for (long t = 0; t < N; ++t)
         oracle_rotate(x + t * d, R, d, y + t * d);
 }
+
+/* ---- Lloyd-Max codebook variant -----------------------------------------
+ * Reading of the article's section "Why this matters for long-context
+ * agents" (the OSCAR code combines the rotation with a Lloyd-Max codebook):
+ * a group keeps its fp16 scale s and zero point z, but its four levels are
+ * z + (L_k / 64) s for a codebook L_0 <= L_1 <= L_2 <= L_3 of integers in
+ * 0..255 (one per kv head and K|V, fitted offline), instead of z + k s.  A
+ * channel takes the nearest level: with u = (y - z) / s (fp32, correctly
+ * rounded), code = [u > t_0] + [u > t_1] + [u > t_2], t_k = (L_k + L_{k+1})
+ * / 128 (exact in fp32), so a value midway between two levels takes the
+ * lower one; s == 0 gives code 0.
+ */
+
+/* u = (y - z) / s of every channel of y[d]; channels of a group with s == 0
+ * get -1 (they carry no information for a codebook fit). */
+void oracle_normalized(const float *y, int d, int G, float *u)
+{
+    uint8_t codes[512];
+    uint16_t s16[512], z16[512];
+    oracle_quantize(y, d, G, codes, s16, z16); /* the group's s and z */
+    for (int g = 0; g < d / G; ++g) {
+        float s = oracle_f16_to_f32(s16[g]);
+        float z = oracle_f16_to_f32(z16[g]);
+        for (int k = 0; k < G; ++k)
+            u[g * G + k] = s != 0.0f ? (y[g * G + k] - z) / s : -1.0f;
+    }
+}
+
+/* Quantization of y[d] with codebook L[4]: codes 0..3, fp16 s and z. */
+void oracle_quantize_lut(const float *y, int d, int G, const uint8_t *L,
+                         uint8_t *codes, uint16_t *scale16, uint16_t *zero16)
+{
+    float t[3];
+    for (int k = 0; k < 3; ++k)
+        t[k] = (float)(L[k] + L[k + 1]) / 128.0f;
+    oracle_quantize(y, d, G, codes, scale16, zero16); /* the group's s and z */
+    for (int g = 0; g < d / G; ++g) {
+        float s = oracle_f16_to_f32(scale16[g]);
+        float z = oracle_f16_to_f32(zero16[g]);
+        for (int k = 0; k < G; ++k) {
+            int c = 0;
+            if (s != 0.0f) {
+                float u = (y[g * G + k] - z) / s;
+                c = (u > t[0]) + (u > t[1]) + (u > t[2]);
+            }
+            codes[g * G + k] = (uint8_t)c;
+        }
+    }
+}
+
+/* Encode N bf16 vectors with codebook L: rotate, clip, quantize, pack. */
+void oracle_encode_lut(const uint16_t *x, long N, int d, int G, const float *R,
+                       const float *clip, const uint8_t *L, uint8_t *packed,
+                       uint16_t *scale16, uint16_t *zero16)
+{
+    float y[512];
+    uint8_t codes[512];
+    for (long t = 0; t < N; ++t) {
+        oracle_rotate(x + t * d, R, d, y);
+        oracle_clip(y, clip, d);
+        oracle_quantize_lut(y, d, G, L, codes, scale16 + t * (d / G), zero16 + t * (d / G));
+        oracle_pack(codes, d, packed + t * (d / 4));
+    }
+}
+
+/* Normalised values u[N][d] of N bf16 vectors (rotate, clip, then u). */
+void oracle_normalized_many(const uint16_t *x, long N, int d, int G, const float *R,
+                            const float *clip, float *u)
+{
+    float y[512];
+    for (long t = 0; t < N; ++t) {
+        oracle_rotate(x + t * d, R, d, y);
+        oracle_clip(y, clip, d);
+        oracle_normalized(y, d, G, u + t * d);
+    }
+}

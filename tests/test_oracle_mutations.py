@@ -17,6 +17,7 @@ import oracle
 import test_oracle_attention
 import test_oracle_calibration
 import test_oracle_codec as pins
+import test_oracle_lloyd_max
 import test_oracle_pool
 import test_oracle_rotation
 
@@ -61,12 +62,22 @@ MISTAKES = {
     "pack with the first code in the high bits": (
         "codes[4 * b] | (codes[4 * b + 1] << 2) |\n                             (codes[4 * b + 2] << 4) | (codes[4 * b + 3] << 6)",
         "(codes[4 * b] << 6) | (codes[4 * b + 1] << 4) |\n                             (codes[4 * b + 2] << 2) | codes[4 * b + 3]"),
+    "codebook ties to the upper level": (
+        "c = (u > t[0]) + (u > t[1]) + (u > t[2]);",
+        "c = (u >= t[0]) + (u >= t[1]) + (u >= t[2]);"),
+    "codebook thresholds at the upper levels": (
+        "t[k] = (float)(L[k] + L[k + 1]) / 128.0f;",
+        "t[k] = (float)L[k + 1] / 64.0f;"),
+    "normalised value without the zero point": (
+        "u[g * G + k] = s != 0.0f ? (y[g * G + k] - z) / s : -1.0f;",
+        "u[g * G + k] = s != 0.0f ? y[g * G + k] / s : -1.0f;"),
     "unpack from the high bits": (
         "codes[i] = (bytes[i / 4] >> (2 * (i % 4))) & 3;",
         "codes[i] = (bytes[i / 4] >> (2 * (3 - i % 4))) & 3;"),
 }
 
-PINS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
+PINS = ([getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
+        + [getattr(test_oracle_lloyd_max, n) for n in dir(test_oracle_lloyd_max) if n.startswith("test_")])
 
 
 def _planted(tmp_path, old, new):
@@ -116,7 +127,7 @@ def _calls(module):
 
 
 PY_PINS = (_calls(test_oracle_rotation) + _calls(test_oracle_attention) + _calls(test_oracle_pool)
-           + _calls(test_oracle_calibration))
+           + _calls(test_oracle_calibration) + _calls(test_oracle_lloyd_max))
 
 
 def _bad_hadamard(d):
@@ -264,6 +275,32 @@ def _eigen_variant(kind):
     return f
 
 
+def _lloyd_variant(kind):
+    def f(u, iters=oracle.LLOYD_ITERS):
+        u = np.asarray(u, dtype=np.float32).ravel()
+        U = np.rint(u[u >= 0].astype(np.float64) * oracle.LLOYD_GRID).astype(np.int64)
+        lev = np.array([0.5, 1.5, 2.5, 3.5]) if kind == "init" else np.array([0.0, 1.0, 2.0, 3.0])
+        for _ in range(iters):
+            thr = (lev[:-1] + lev[1:]) * (oracle.LLOYD_GRID / 2)
+            cell = ((U[:, None] >= thr[None, :]) if kind == "ge" else (U[:, None] > thr[None, :])).sum(axis=1)
+            new = np.zeros(4) if kind == "empty0" else lev.copy()
+            for k in range(4):
+                sel = U[cell == k]
+                if len(sel):
+                    new[k] = float(int(sel.sum())) / float(len(sel)) / oracle.LLOYD_GRID
+            lev = new
+        return lev
+    return f
+
+
+def _dequant_lut_32(packed, s16, z16, G, L):
+    codes = oracle.unpack(packed)
+    lv = np.asarray(L, dtype=np.float64)[codes] / 32.0
+    s = np.repeat(oracle.f16_table()[s16], G, axis=-1)
+    z = np.repeat(oracle.f16_table()[z16], G, axis=-1)
+    return lv * s + z
+
+
 PY_MISTAKES = {
     "bit reversal left out": ("bitrev", lambda i, bits: i),
     "Hadamard sign from popcount(i | j)": ("hadamard_unnormalized", _bad_hadamard),
@@ -295,6 +332,15 @@ PY_MISTAKES = {
     "eigenvalues ascending": ("eigenbasis", _eigen_variant("ascending")),
     "eigenvector signs left as computed": ("eigenbasis", _eigen_variant("nosign")),
     "U not rounded to the grid": ("rotation_grid", lambda U: np.asarray(U, dtype=np.float32)),
+    "Lloyd cells take values on a threshold upward": ("lloyd_max_levels", _lloyd_variant("ge")),
+    "Lloyd empty cell set to 0": ("lloyd_max_levels", _lloyd_variant("empty0")),
+    "Lloyd started from levels 0.5, 1.5, 2.5, 3.5": ("lloyd_max_levels", _lloyd_variant("init")),
+    "codebook levels rounded down": ("lloyd_max_codebook",
+                                     lambda u, iters=oracle.LLOYD_ITERS: np.clip(np.floor(oracle.lloyd_max_levels(u, iters) * 64), 0, 255).astype(np.uint8)),
+    "codebook levels read as L / 32": ("dequantize_lut", _dequant_lut_32),
+    "Lloyd-Max history decoded by R instead of R^T": (
+        "decode_history_lut",
+        lambda pk, s16, z16, G, L, R: oracle.dequantize_lut(pk, s16, z16, G, L) @ np.asarray(R, dtype=np.float64)),
 }
 
 
