@@ -334,7 +334,7 @@ LLOYD_GRID = 2 ** 20   # u is fitted on multiples of 2^-20 (exact integer sums)
 
 def normalized_values(x_bf16: np.ndarray, R: np.ndarray, clip: np.ndarray, G: int) -> np.ndarray:
     """fp32 u [N][d] = (y - z) / s of N bf16 vectors after rotation and clip
-    (the codec's own arithmetic, in C); -1 for groups with s == 0."""
+    (the codec's own arithmetic, in C); NaN for groups with s == 0."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     N, d = x.shape
     u = np.empty((N, d), dtype=np.float32)
@@ -344,8 +344,8 @@ def normalized_values(x_bf16: np.ndarray, R: np.ndarray, clip: np.ndarray, G: in
 
 
 def lloyd_max_levels(u: np.ndarray, iters: int = LLOYD_ITERS) -> np.ndarray:
-    """Lloyd's algorithm for a 4-level scalar quantizer of the values u >= 0
-    (negative entries, the s == 0 groups, are left out), fp64 levels.
+    """Lloyd's algorithm for a 4-level scalar quantizer of the values u
+    (NaN entries, the s == 0 groups, are left out), fp64 levels.
 
     The values are taken on the grid of 2^-20 (U = rint(u 2^20), integers,
     so every cell sum is exact).  Start from the uniform levels 0, 1, 2, 3;
@@ -353,7 +353,7 @@ def lloyd_max_levels(u: np.ndarray, iters: int = LLOYD_ITERS) -> np.ndarray:
     puts a value in cell k when it lies above exactly k thresholds, and moves
     each level to the mean of its cell (a level whose cell is empty stays)."""
     u = np.asarray(u, dtype=np.float32).ravel()
-    U = np.rint(u[u >= 0].astype(np.float64) * LLOYD_GRID).astype(np.int64)
+    U = np.rint(u[~np.isnan(u)].astype(np.float64) * LLOYD_GRID).astype(np.int64)
     lev = np.array([0.0, 1.0, 2.0, 3.0])
     for _ in range(iters):
         thr = (lev[:-1] + lev[1:]) * (LLOYD_GRID / 2)      # in grid units

@@ -198,8 +198,9 @@ void oracle_rotate_many(const uint16_t *x, long N, int d, const float *R, float 
  * lower one; s == 0 gives code 0.
  */
 
-/* u = (y - z) / s of every channel of y[d]; channels of a group with s == 0
- * get -1 (they carry no information for a codebook fit). */
+/* u = (y - z) / s of every channel of y[d] (slightly negative for a group's
+ * minimum when fp16 rounds z above it); channels of a group with s == 0 get
+ * NaN (they carry no information for a codebook fit). */
 void oracle_normalized(const float *y, int d, int G, float *u)
 {
     uint8_t codes[512];
@@ -209,7 +210,7 @@ void oracle_normalized(const float *y, int d, int G, float *u)
         float s = oracle_f16_to_f32(s16[g]);
         float z = oracle_f16_to_f32(z16[g]);
         for (int k = 0; k < G; ++k)
-            u[g * G + k] = s != 0.0f ? (y[g * G + k] - z) / s : -1.0f;
+            u[g * G + k] = s != 0.0f ? (y[g * G + k] - z) / s : NAN;
     }
 }
 

@@ -105,7 +105,7 @@ def test_fit_hand_worked_tie():
 
 def test_fit_ignores_groups_without_scale():
     u = ((np.arange(300000) + 0.5) / 100000).astype(np.float32)
-    assert list(oracle.lloyd_max_codebook(np.r_[u, np.full(5000, -1.0, np.float32)])) == [24, 72, 120, 168]
+    assert list(oracle.lloyd_max_codebook(np.r_[u, np.full(5000, np.nan, np.float32)])) == [24, 72, 120, 168]
 
 
 def test_uniform_codebook_matches_the_affine_codec_off_ties():

@@ -69,8 +69,8 @@ MISTAKES = {
         "t[k] = (float)(L[k] + L[k + 1]) / 128.0f;",
         "t[k] = (float)L[k + 1] / 64.0f;"),
     "normalised value without the zero point": (
-        "u[g * G + k] = s != 0.0f ? (y[g * G + k] - z) / s : -1.0f;",
-        "u[g * G + k] = s != 0.0f ? y[g * G + k] / s : -1.0f;"),
+        "u[g * G + k] = s != 0.0f ? (y[g * G + k] - z) / s : NAN;",
+        "u[g * G + k] = s != 0.0f ? y[g * G + k] / s : NAN;"),
     "unpack from the high bits": (
         "codes[i] = (bytes[i / 4] >> (2 * (i % 4))) & 3;",
         "codes[i] = (bytes[i / 4] >> (2 * (3 - i % 4))) & 3;"),
@@ -278,7 +278,7 @@ def _eigen_variant(kind):
 def _lloyd_variant(kind):
     def f(u, iters=oracle.LLOYD_ITERS):
         u = np.asarray(u, dtype=np.float32).ravel()
-        U = np.rint(u[u >= 0].astype(np.float64) * oracle.LLOYD_GRID).astype(np.int64)
+        U = np.rint(u[~np.isnan(u)].astype(np.float64) * oracle.LLOYD_GRID).astype(np.int64)
         lev = np.array([0.5, 1.5, 2.5, 3.5]) if kind == "init" else np.array([0.0, 1.0, 2.0, 3.0])
         for _ in range(iters):
             thr = (lev[:-1] + lev[1:]) * (oracle.LLOYD_GRID / 2)
