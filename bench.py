@@ -36,10 +36,10 @@ def algorithmic_decode_bytes(w, lengths):
     return total
 
 
-def traffic_record(kernel_src, workload):
+def traffic_record(kernel_src, workload, kernel="decode_main"):
     """HBM bytes per launch measured with rocprofv3 counters, if the record in
     profiles/ was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_main_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     with open(kernel_src, "rb") as f:
@@ -413,6 +413,8 @@ def main():
                          "compare_bf16: INT2 vs BF16 history at long context, batch 1; "
                          "calibrate: offline covariances of one layer")
     ap.add_argument("--calib-tokens", type=int, default=4096, help="calibrate mode: calibration sequence length")
+    ap.add_argument("--codebook", choices=["affine", "lloyd_max"], default="affine",
+                    help="decode mode: the history levels (lloyd_max: the Lloyd-Max codebook variant)")
     ap.add_argument("--prefill-len", type=int, default=32768, help="prefill mode: prompt length")
     ap.add_argument("--prefill-chunk", type=int, default=2048, help="prefill mode: queries of the last chunk")
     args = ap.parse_args()
@@ -443,8 +445,10 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     lengths0 = [int(x) for x in synth.lengths(w)]
-    # the CPU baseline first, before this process touches the GPU
-    cpu = cpu_baseline(w, lengths0, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    lloyd = args.codebook == "lloyd_max"
+    # the CPU baseline first, before this process touches the GPU (the
+    # oracle's step is the affine codec's; no baseline for the variant)
+    cpu = cpu_baseline(w, lengths0, args.cpu_seconds) if args.cpu_seconds > 0 and not lloyd else None
 
     import torch
 
@@ -456,10 +460,13 @@ def main():
     total_steps = args.warmup + args.steps
     appends_per_layer = -(-total_steps // args.layers)
     RK, RV, cK, cV = harness.tables(w)
-    cfg = harness.config_for(w, lengths0, extra_tokens=appends_per_layer)
+    cfg = harness.config_for(w, lengths0, extra_tokens=appends_per_layer, flags=ok.POOL_LLOYD_MAX if lloyd else 0)
+    codebooks = harness.codebooks(w, RK, RV, cK, cV) if lloyd else None
     pools = []
     for layer in range(args.layers):
         p = ok.Pool(cfg, RK, RV, cK, cV, max_batch=w.batch)
+        if lloyd:
+            p.set_codebook(*codebooks)
         harness.prefill_all(p, w, lengths0)
         pools.append(p)
     ids = list(range(w.batch))
@@ -522,8 +529,9 @@ def main():
             bytes_main.append(algorithmic_decode_bytes(w, [L + a + 1 for L in lengths0]))
     bytes_launch = float(np.mean(bytes_main))
     achieved = bytes_launch / (ms_main * 1e-3) / 1e9
-    traffic = traffic_record(os.path.join(ROOT, "bit_kv_cache_segment_amd", "csrc", "kernels_decode.hip"),
-                             w.name)
+    kname = "decode_lut" if lloyd else "decode_main"
+    traffic = traffic_record(os.path.join(ROOT, "bit_kv_cache_segment_amd", "csrc",
+                                          "kernels_lut.hip" if lloyd else "kernels_decode.hip"), w.name, kname)
     value = w.batch / (ms_step * 1e-3)
     step_bytes = bytes_launch + w.batch * w.num_q_heads * w.head_dim * 4
     res = {
@@ -537,9 +545,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int2 codes + fp16 scale/zero history, bf16 windows, fp32 accumulate",
+        "dtype": ("int2 codes (Lloyd-Max codebook) + fp16 scale/zero history, bf16 windows, fp32 accumulate"
+                  if lloyd else "int2 codes + fp16 scale/zero history, bf16 windows, fp32 accumulate"),
         "data": "synthetic (seeded; K/V ~ N(0,1) with 4 outlier channels x20)",
-        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+        "config": {"workload": w.name, "codebook": args.codebook, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "group_size": w.group_size,
                    "context_min": min(lengths0), "context_max": max(lengths0),
                    "context_mean": float(np.mean(lengths0)),
@@ -547,7 +556,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "decode_main_kernel", "bytes_per_launch": bytes_launch,
+                     "kernel": kname + "_kernel", "bytes_per_launch": bytes_launch,
                      "ms_per_launch": ms_main},
         "cpu_baseline": cpu,
         "detail": {"ms_decode_main": ms_main,

@@ -24,6 +24,7 @@ MAX_BATCH_PER_LAUNCH = 256
 POOL_HOST_ONLY = 1
 POOL_DETERMINISTIC = 2
 POOL_BF16_HISTORY = 4
+POOL_LLOYD_MAX = 8
 
 OK, EHIP, ENOMEM, EINVAL, ERANGE = 0, -5, -12, -22, -34
 _NAMES = {EHIP: "EHIP", ENOMEM: "ENOMEM", EINVAL: "EINVAL", ERANGE: "ERANGE"}
@@ -33,7 +34,7 @@ EXPORTS = (
     "oscar_pool_bytes", "oscar_pool_required_bytes", "oscar_decode_workspace_bytes", "oscar_pool_create", "oscar_pool_destroy",
     "oscar_prefill", "oscar_append_evict", "oscar_decode_attn", "oscar_decode_step",
     "oscar_decode_step_static", "oscar_prefill_workspace_bytes", "oscar_prefill_attn", "oscar_pool_check",
-    "oscar_release_seq", "oscar_fork_seq",
+    "oscar_release_seq", "oscar_fork_seq", "oscar_pool_set_codebook", "oscar_lloyd_max_codebook",
     "oscar_seq_length", "oscar_page_table", "oscar_free_pages", "oscar_export_history",
     "oscar_export_state", "oscar_export_history_bf16", "oscar_export_window", "oscar_build_rotation", "oscar_calibrate_clip",
     "oscar_calib_workspace_bytes", "oscar_calib_attention", "oscar_calib_covariance", "oscar_calib_rotation", "oscar_profile_begin",
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
             "oscar_pool_check": [_P, _P],
             "oscar_release_seq": [_P, _I32],
             "oscar_fork_seq": [_P, _I32, _I32, _P],
+            "oscar_pool_set_codebook": [_P, _P, _P, _P],
+            "oscar_lloyd_max_codebook": [_I32, _I32, ctypes.c_int64, _P, _P, _P, _I32, _P],
             "oscar_seq_length": [_P, _I32, _P],
             "oscar_page_table": [_P, _I32, _P, _I32, _P],
             "oscar_free_pages": [_P, _P],
@@ -318,6 +321,21 @@ def oscar_calibrate_clip(x_bf16: np.ndarray, R: np.ndarray, pct: float = 99.0) -
     return out
 
 
+LLOYD_ITERS = 32
+
+
+def oscar_lloyd_max_codebook(x_bf16: np.ndarray, R: np.ndarray, clip: np.ndarray, G: int,
+                             iters: int = LLOYD_ITERS) -> np.ndarray:
+    """uint8 [4] Lloyd-Max codebook of one head from host bf16 tokens x [n][d] (uint16 bits)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    n, d = x.shape
+    R = np.ascontiguousarray(R, dtype=np.float32)
+    clip = np.ascontiguousarray(clip, dtype=np.float32)
+    out = np.empty(4, dtype=np.uint8)
+    _check(lib().oscar_lloyd_max_codebook(d, G, n, _np_ptr(x), _np_ptr(R), _np_ptr(clip), iters, _np_ptr(out)))
+    return out
+
+
 def oscar_calib_workspace_bytes(n: int, num_q_heads: int, head_dim: int) -> int:
     b = ctypes.c_size_t()
     _check(lib().oscar_calib_workspace_bytes(n, num_q_heads, head_dim, ctypes.byref(b)))
@@ -481,6 +499,13 @@ class Pool:
 
     def release(self, seq):
         oscar_release_seq(self.handle, seq)
+
+    def set_codebook(self, levels_k, levels_v, stream=None):
+        """Lloyd-Max pools: uint8 [Hkv][4] codebooks for K and V."""
+        lk = np.ascontiguousarray(levels_k, dtype=np.uint8)
+        lv = np.ascontiguousarray(levels_v, dtype=np.uint8)
+        _check(lib().oscar_pool_set_codebook(self.handle, _np_ptr(lk), _np_ptr(lv),
+                                             None if self.host_only else _stream(stream)))
 
     def fork(self, src, dst, stream=None):
         """Prefix sharing: empty sequence dst takes src's state, history pages shared."""

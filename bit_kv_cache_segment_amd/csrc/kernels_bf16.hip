@@ -17,113 +17,12 @@
 // the window.  Its partial (window and pages together) goes to the window
 // slot of the workspace, every other split's to its split slot, so the
 // merge kernel of the INT2 path completes the attention unchanged.
-#include "oscar_internal.h"
+#include "bf_common.h"
 
 #include <hip/hip_ext.h>
 
 namespace oscar {
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.f;
-constexpr int kBfWaves = 8;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-// Sum over aligned groups of N lanes (8 or 16).
-template <int N>
-__device__ __forceinline__ float lanes_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  if constexpr (N == 16) v += dpp_f<0x140>(v);
-  return v;
-}
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ int karg_u16(const uint16_t *a, int i) {
-  return (int)((((const uint32_t *)a)[i >> 1] >> (16 * (i & 1))) & 0xffffu);
-}
-__device__ __forceinline__ int karg_u8(const uint8_t *a, int i) {
-  return (int)((((const uint32_t *)a)[i >> 2] >> (8 * (i & 3))) & 0xffu);
-}
-
-template <int D, int GQ>
-struct BfSmem {
-  alignas(16) uint32_t q2[GQ][D / 2]; // the pair's query rows as bf16 pairs
-  float M[kBfWaves][GQ], L[kBfWaves][GQ];
-  float A[kBfWaves][GQ][D];
-  uint32_t claim;
-};
-
-// Running (m, l, acc) of one wave for the GQ heads; this lane's 8 channels.
-template <int GQ>
-struct BfState {
-  float m[GQ], l[GQ], acc[GQ][8];
-};
-
-// Token groups [g0, g1) (step `stride`) of a contiguous block of ntok token
-// rows (K at k, V at v), into the wave's state.  WG groups' loads are
-// issued together, then computed.
-template <int D, int GQ, int WG>
-__device__ __forceinline__ void bf_tokens(BfState<GQ> &st, const uint16_t *k, const uint16_t *v, int ntok, int g0,
-                                          int stride, const uint32_t (*q2)[D / 2], float qscale, int lane) {
-  constexpr int LPT = D / 8, TPI = 64 / LPT;
-  const int ts = lane / LPT, cc = lane % LPT;
-  const int ngroups = (ntok + TPI - 1) / TPI;
-  for (int gb = g0; gb < ngroups; gb += WG * stride) {
-    u32x4 kr[WG], vr[WG];
-#pragma unroll
-    for (int i = 0; i < WG; ++i) {
-      const int u = (gb + i * stride) * TPI + ts;
-      kr[i] = vr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (u < ntok) {
-        kr[i] = __builtin_nontemporal_load((const u32x4 *)(k + (size_t)u * D + 8 * cc));
-        vr[i] = __builtin_nontemporal_load((const u32x4 *)(v + (size_t)u * D + 8 * cc));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < WG; ++i) {
-      const int u = (gb + i * stride) * TPI + ts;
-      const bool ok = u < ntok;
-      float vf[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vf[2 * j] = __uint_as_float(vr[i][j] << 16);
-        vf[2 * j + 1] = __uint_as_float(vr[i][j] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        const u32x4 qv = *(const u32x4 *)&q2[h][4 * cc];
-        float d = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t kw = kr[i][j], qw = qv[j];
-          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qw), d, false);
-        }
-        d = lanes_sum<LPT>(d);
-        const float sc = ok ? d * qscale : -INFINITY;
-        const bool jump = sc > st.m[h] + kLazy;
-        if (__any(jump)) {
-          const float mn = jump ? sc : st.m[h];
-          const float al = jump ? fast_exp2(st.m[h] - mn) : 1.f;
-          st.l[h] *= al;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) st.acc[h][j] *= al;
-          st.m[h] = mn;
-        }
-        const float pr = ok ? fast_exp2(sc - st.m[h]) : 0.f;
-        st.l[h] += pr;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st.acc[h][j] = fmaf(pr, vf[j], st.acc[h][j]);
-      }
-    }
-  }
-}
 
 template <int D, int GQ>
 __global__ __launch_bounds__(64 * kBfWaves) void decode_bf16_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q,
@@ -183,32 +82,7 @@ __global__ __launch_bounds__(64 * kBfWaves) void decode_bf16_kernel(PoolDev p, D
     const uint16_t *kb = (const uint16_t *)(p.pages + ((size_t)ptab[pg] * Hkv + kv) * p.block_bytes);
     bf_tokens<D, GQ, WG>(st, kb, kb + kPage * D, ntok, 0, 1, sm.q2, qscale, lane);
   }
-  // merge the TPI token slots of the wave (lanes cc, cc + LPT, ...)
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    float m = st.m[h];
-#pragma unroll
-    for (int o = LPT; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float f = st.m[h] == -INFINITY ? 0.f : exp2f(st.m[h] - m);
-    float l = st.l[h] * f;
-#pragma unroll
-    for (int o = LPT; o < 64; o <<= 1) l += __shfl_xor(l, o, 64);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float a = st.acc[h][j] * f;
-#pragma unroll
-      for (int o = LPT; o < 64; o <<= 1) a += __shfl_xor(a, o, 64);
-      st.acc[h][j] = a;
-    }
-    if (lane == 0) {
-      sm.M[w][h] = m;
-      sm.L[w][h] = l;
-    }
-    if (ts == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sm.A[w][h][8 * cc + j] = st.acc[h][j];
-    }
-  }
+  wave_state_to_smem<D, GQ>(sm, st, w, lane);
   __syncthreads();
   // the block's partial: window slot for the last split (window and its
   // pages), split slot otherwise; the last split's own slot stays empty
@@ -217,14 +91,8 @@ __global__ __launch_bounds__(64 * kBfWaves) void decode_bf16_kernel(PoolDev p, D
   float *dst = with_window ? ws_win + ((size_t)e * Hq + kv * GQ) * (D + 2) : ws_hist + (size_t)slot * GQ * (D + 2);
   for (int idx = tid; idx < GQ * D; idx += 64 * W) {
     const int h = idx / D, c = idx % D;
-    float m = -INFINITY;
-    for (int ww = 0; ww < W; ++ww) m = fmaxf(m, sm.M[ww][h]);
-    float a = 0.f, l = 0.f;
-    for (int ww = 0; ww < W; ++ww) {
-      const float f = sm.M[ww][h] == -INFINITY ? 0.f : exp2f(sm.M[ww][h] - m);
-      a += f * sm.A[ww][h][c];
-      l += f * sm.L[ww][h];
-    }
+    float a, m, l;
+    block_combine<D, GQ>(sm, h, c, a, m, l);
     dst[(size_t)h * (D + 2) + c] = a;
     if (c == 0) {
       dst[(size_t)h * (D + 2) + D] = m;

@@ -72,7 +72,8 @@ __device__ __forceinline__ uint32_t or16(uint32_t v) {
 // is LDS scratch of 2 * (D/64) floats.  Returns the code and sets the
 // group's fp16 scale/zero bits (uniform over the group).
 template <int D, int G>
-__device__ __forceinline__ uint32_t quantize_channel(float y, float *red, uint16_t &s16, uint16_t &z16) {
+__device__ __forceinline__ uint32_t quantize_channel(float y, float *red, uint16_t &s16, uint16_t &z16,
+                                                     bool lut = false, uint32_t lw = 0) {
   const int j = threadIdx.x, w = j / 64;
   float mn = wave_min(y), mx = wave_max(y);
   if (G > 64) {
@@ -97,6 +98,7 @@ __device__ __forceinline__ uint32_t quantize_channel(float y, float *red, uint16
   s16 = f16_bits(((mx - mn) + 0.0f) / 3.0f);
   z16 = f16_bits(mn + 0.0f);
   const float s = f16_val(s16), z = f16_val(z16);
+  if (lut) return lut_code(y, z, s, lw);
   float q = 0.0f;
   if (s != 0.0f) q = fminf(fmaxf(rintf((y - z) / s), 0.0f), 3.0f);
   return (uint32_t)q;
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(D) void prefill_encode_kernel(PoolDev p, int seq, c
 
   const int page = p.page_table[(size_t)seq * p.maxp + pg_idx];
   uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
+  const uint32_t lw = p.lut ? p.codebook[kind * Hkv + kv] : 0u;
   uint32_t vdw[kPage / 16] = {0, 0, 0, 0};
   for (int t = 0; t < nt; ++t) {
     float acc = 0.0f;
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(D) void prefill_encode_kernel(PoolDev p, int seq, c
     for (int i = 0; i < D; ++i) acc = fmaf(xs[t][i], rc[i], acc);
     const float y = fminf(fmaxf(acc, -c), c);
     uint16_t s16, z16;
-    const uint32_t code = quantize_channel<D, G>(y, red, s16, z16);
+    const uint32_t code = quantize_channel<D, G>(y, red, s16, z16, p.lut != 0, lw);
     if (kind == 0) {
       store_k_code<D>(blk, t, code);
       store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
@@ -250,7 +253,8 @@ __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, con
   for (int i = 0; i < D; ++i) acc = fmaf(xs[i], rc[i], acc);
   const float y = fminf(fmaxf(acc, -c), c);
   uint16_t s16, z16;
-  const uint32_t code = quantize_channel<D, G>(y, red, s16, z16);
+  const uint32_t code =
+      quantize_channel<D, G>(y, red, s16, z16, p.lut != 0, p.lut ? p.codebook[kind * Hkv + kv] : 0u);
   if (b.new_page[e] >= 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
   uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
   if (kind == 0) {

@@ -50,7 +50,7 @@ int hip_fail(hipError_t e, const char *what) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t RK, RV, RVt, clipK, clipV, status, page_table, sinkK, sinkV, recentK, recentV, pages, total;
+  size_t RK, RV, RVt, clipK, clipV, status, codebook, page_table, sinkK, sinkV, recentK, recentV, pages, total;
 };
 
 int validate_config(const oscar_pool_config *c) {
@@ -76,8 +76,10 @@ int validate_config(const oscar_pool_config *c) {
   if ((int64_t)c->max_seqs * c->max_pages_per_seq > (int64_t)1 << 31)
     return fail(OSCAR_EINVAL, "page table of %d x %d entries is too large", c->max_seqs,
                 c->max_pages_per_seq);
-  if (c->flags & ~(OSCAR_POOL_HOST_ONLY | OSCAR_POOL_DETERMINISTIC | OSCAR_POOL_BF16_HISTORY))
+  if (c->flags & ~(OSCAR_POOL_HOST_ONLY | OSCAR_POOL_DETERMINISTIC | OSCAR_POOL_BF16_HISTORY | OSCAR_POOL_LLOYD_MAX))
     return fail(OSCAR_EINVAL, "unknown flags 0x%x", c->flags);
+  if ((c->flags & OSCAR_POOL_BF16_HISTORY) && (c->flags & OSCAR_POOL_LLOYD_MAX))
+    return fail(OSCAR_EINVAL, "a BF16 history has no codebook: OSCAR_POOL_LLOYD_MAX excludes OSCAR_POOL_BF16_HISTORY");
   return OSCAR_OK;
 }
 
@@ -96,6 +98,7 @@ Layout layout_of(const oscar_pool_config &c) {
   L.clipK = take(H * d * 4);
   L.clipV = take(H * d * 4);
   L.status = take(4);
+  L.codebook = take(2 * H * 4);
   L.page_table = take(S * (size_t)c.max_pages_per_seq * 4);
   L.sinkK = take(S * H * kSink * d * 2);
   L.sinkV = take(S * H * kSink * d * 2);
@@ -186,6 +189,8 @@ struct oscar_pool {
   Layout lay;
   PoolDev dev;
   bool host_only;
+  // Lloyd-Max pools: the codebook (uint32 per kv head, K then V), once set
+  std::vector<uint32_t> codebook;
   int decode_slots = 768;  // resident decode blocks on the device
   int prefill_slots = 256; // resident prefill-attention blocks
   std::vector<int32_t> len;
@@ -309,6 +314,7 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
   D.G = cfg->group_size;
   D.maxp = cfg->max_pages_per_seq;
   D.bf16_hist = (cfg->flags & OSCAR_POOL_BF16_HISTORY) ? 1 : 0;
+  D.lut = (cfg->flags & OSCAR_POOL_LLOYD_MAX) ? 1 : 0;
   D.block_bytes = D.bf16_hist ? bf16_block_bytes(d) : block_bytes_for(d, cfg->group_size);
   D.pv_shift = 0;
   D.deterministic = (cfg->flags & OSCAR_POOL_DETERMINISTIC) ? 1 : 0;
@@ -345,6 +351,7 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
     D.recentV = (uint16_t *)(b + lay.recentV);
     D.pages = (uint8_t *)(b + lay.pages);
     D.status = (uint32_t *)(b + lay.status);
+    D.codebook = (const uint32_t *)(b + lay.codebook);
     std::vector<float> rvt((size_t)H * d * d);
     for (int h = 0; h < H; ++h)
       for (int i = 0; i < d; ++i)
@@ -367,7 +374,9 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
     int dev = 0, cus = 0;
     e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int per_cu = D.bf16_hist ? bf16_decode_blocks_per_cu(D) : decode_main_blocks_per_cu(D);
+    const int per_cu = D.bf16_hist ? bf16_decode_blocks_per_cu(D)
+                       : D.lut     ? lut_decode_blocks_per_cu(D)
+                                   : decode_main_blocks_per_cu(D);
     if (e != hipSuccess || cus <= 0 || per_cu <= 0) {
       delete p;
       return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "querying the decode occupancy");
@@ -413,6 +422,8 @@ int oscar_prefill(oscar_pool *p, int32_t seq, const uint16_t *k, const uint16_t 
   if (p->len[seq] != 0 || !p->table[seq].empty())
     return fail(OSCAR_EINVAL, "sequence %d is not empty", seq);
   if (L < 0 || L > (1 << 30)) return fail(OSCAR_EINVAL, "prompt length %d is invalid", L);
+  if (p->dev.lut && p->codebook.empty())
+    return fail(OSCAR_EINVAL, "a Lloyd-Max pool needs its codebook (oscar_pool_set_codebook) first");
   if (L == 0) return ok();
   if (!p->host_only && (!k || !v)) return fail(OSCAR_EINVAL, "NULL k or v");
   int64_t n_hist = std::max(0, L - kWindow);
@@ -540,6 +551,8 @@ static void commit_prefix(oscar_pool *p, const int32_t *seq_ids, const AppendPag
 // pages for every eviction that starts a page or copies a shared one.
 // Changes nothing.
 static int check_append(oscar_pool *p, const int32_t *seq_ids, int32_t n) {
+  if (p->dev.lut && p->codebook.empty())
+    return fail(OSCAR_EINVAL, "a Lloyd-Max pool needs its codebook (oscar_pool_set_codebook) first");
   std::vector<int32_t> sorted(seq_ids, seq_ids + n);
   std::sort(sorted.begin(), sorted.end());
   for (int i = 0; i < n; ++i) {
@@ -628,7 +641,7 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   }
   const int Hq = p->cfg.num_q_heads, Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim;
   const int g = Hq / Hkv;
-  const bool bf16 = p->dev.bf16_hist != 0;
+  const bool bf16 = p->dev.bf16_hist != 0, lut = p->dev.lut != 0;
   std::vector<DecodeBatch> batches;
   size_t need = 0;
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
@@ -637,7 +650,7 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     std::vector<int> len(b.n);
     for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]];
     plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
-                bf16 ? window_units_bf16(d) : window_units(d, p->cfg.group_size));
+                bf16 ? window_units_bf16(d) : lut ? window_units_lut() : window_units(d, p->cfg.group_size));
     need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
     batches.push_back(b);
   }
@@ -648,8 +661,9 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     const uint16_t *qi = q + i * (size_t)kMaxBatch * Hq * d;
     float *oi = out + i * (size_t)kMaxBatch * Hq * d;
     hipError_t e;
-    if (bf16) {
-      e = launch_decode_bf16(p->dev, batches[i], qi, softmax_scale, (float *)workspace, (hipStream_t)stream, tm);
+    if (bf16 || lut) {
+      e = bf16 ? launch_decode_bf16(p->dev, batches[i], qi, softmax_scale, (float *)workspace, (hipStream_t)stream, tm)
+               : launch_decode_lut(p->dev, batches[i], qi, softmax_scale, (float *)workspace, (hipStream_t)stream, tm);
       if (e == hipSuccess)
         e = launch_decode_merge(p->dev, batches[i], oi, (const float *)workspace, (hipStream_t)stream, tg);
     } else {
@@ -687,8 +701,8 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
   // the append is its own launch (same results).
   std::vector<DecodeBatch> batches;
   size_t need = 0;
-  // (BF16-history pools append in their own launch)
-  bool fused = p->dev.bf16_hist == 0;
+  // (BF16-history and Lloyd-Max pools append in their own launch)
+  bool fused = p->dev.bf16_hist == 0 && p->dev.lut == 0;
   for (int pass = fused ? 0 : 1; pass < 2; ++pass) {
     batches.clear();
     need = 0;
@@ -698,7 +712,10 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
       std::vector<int> len(b.n);
       for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
       plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
-                  p->dev.bf16_hist ? window_units_bf16(d) : window_units(d, p->cfg.group_size, fused), fused);
+                  p->dev.bf16_hist ? window_units_bf16(d)
+                  : p->dev.lut     ? window_units_lut()
+                                   : window_units(d, p->cfg.group_size, fused),
+                  fused);
       need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
       if (b.hist_blocks > p->decode_slots) fused = false;
       batches.push_back(b);
@@ -792,7 +809,8 @@ int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *
   int rc = check_seq(p, seq);
   if (rc) return rc;
   if (p->host_only) return fail(OSCAR_EINVAL, "prefill attention on a host-only pool");
-  if (p->dev.bf16_hist) return fail(OSCAR_EINVAL, "prefill attention runs on INT2-history pools");
+  if (p->dev.bf16_hist || p->dev.lut)
+    return fail(OSCAR_EINVAL, "prefill attention runs on INT2-history pools with the affine levels");
   const int32_t L = p->len[seq];
   if (n_q < 1 || n_q > L || (int64_t)n_q * p->cfg.num_q_heads > ((int64_t)1 << 30))
     return fail(OSCAR_EINVAL, "n_q = %d outside [1, L = %d] (or n_q x Hq above 2^30)", n_q, L);
@@ -861,6 +879,31 @@ int oscar_fork_seq(oscar_pool *p, int32_t src, int32_t dst, void *stream) {
   p->table[dst] = p->table[src];
   for (int32_t pg : p->table[dst]) ++p->refs[pg];
   p->len[dst] = p->len[src];
+  return ok();
+}
+
+int oscar_pool_set_codebook(oscar_pool *p, const uint8_t *levels_k, const uint8_t *levels_v, void *stream) {
+  if (!p) return fail(OSCAR_EINVAL, "pool is NULL");
+  if (!p->dev.lut) return fail(OSCAR_EINVAL, "not a Lloyd-Max pool (OSCAR_POOL_LLOYD_MAX)");
+  if (!levels_k || !levels_v) return fail(OSCAR_EINVAL, "NULL codebook");
+  for (int s = 0; s < p->cfg.max_seqs; ++s)
+    if (p->len[s] != 0) return fail(OSCAR_EINVAL, "the codebook is set while every sequence is empty (sequence %d is not)", s);
+  const int H = p->cfg.num_kv_heads;
+  std::vector<uint32_t> cb(2 * H);
+  for (int kind = 0; kind < 2; ++kind)
+    for (int h = 0; h < H; ++h) {
+      const uint8_t *l = (kind ? levels_v : levels_k) + 4 * h;
+      if (l[0] > l[1] || l[1] > l[2] || l[2] > l[3])
+        return fail(OSCAR_EINVAL, "codebook of kv head %d (%s) is not non-decreasing", h, kind ? "V" : "K");
+      cb[kind * H + h] = (uint32_t)l[0] | ((uint32_t)l[1] << 8) | ((uint32_t)l[2] << 16) | ((uint32_t)l[3] << 24);
+    }
+  if (!p->host_only) {
+    hipError_t e = hipMemcpyAsync((void *)p->dev.codebook, cb.data(), cb.size() * 4, hipMemcpyHostToDevice,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "copying the codebook");
+  }
+  p->codebook = std::move(cb);
   return ok();
 }
 
@@ -1265,6 +1308,65 @@ int oscar_calib_rotation(int32_t d, const float *cov, float *U, float *R, double
   }
   if (U) std::memcpy(U, Ug.data(), Ug.size() * sizeof(float));
   return oscar_build_rotation(d, Ug.data(), R);
+}
+
+// Lloyd-Max codebook of one head (offline): the normalised values u = (y - z)
+// / s of n tokens (rotation by the eviction's fp32 FMA chain, clip, the
+// group's fp16 s and z), taken on the grid of 2^-20 as integers; Lloyd's
+// algorithm from the uniform levels 0, 1, 2, 3 (cells split midway between
+// levels, a value on a midpoint in the lower cell, each level moved to its
+// cell's mean, an empty cell's level kept), then L_k = rint(64 level_k).
+int oscar_lloyd_max_codebook(int32_t d, int32_t G, int64_t n, const uint16_t *x, const float *R, const float *clip,
+                             int32_t iters, uint8_t *levels) {
+  if (d < 1 || d > 1024 || G < 1 || d % G) return fail(OSCAR_EINVAL, "bad d = %d or G = %d", d, G);
+  if (n < 1 || !x || !R || !clip || !levels) return fail(OSCAR_EINVAL, "bad arguments");
+  if (iters < 0 || iters > 100000) return fail(OSCAR_EINVAL, "iterations %d outside [0, 100000]", iters);
+  constexpr double kGrid = 1048576.0; // 2^20
+  std::vector<int64_t> U;
+  U.reserve((size_t)n * d);
+  std::vector<float> y(d);
+  for (int64_t t = 0; t < n; ++t) {
+    for (int j = 0; j < d; ++j) {
+      float acc = 0.0f;
+      for (int i = 0; i < d; ++i) {
+        uint32_t u = (uint32_t)x[(size_t)t * d + i] << 16;
+        float xf;
+        std::memcpy(&xf, &u, 4);
+        acc = std::fmaf(xf, R[(size_t)i * d + j], acc);
+      }
+      y[j] = std::fmin(std::fmax(acc, -clip[j]), clip[j]);
+    }
+    for (int g = 0; g < d / G; ++g) {
+      float mn = y[g * G], mx = y[g * G];
+      for (int k = 1; k < G; ++k) {
+        mn = std::fmin(mn, y[g * G + k]);
+        mx = std::fmax(mx, y[g * G + k]);
+      }
+      const float range = (mx - mn) + 0.0f;
+      const float s = (float)(_Float16)(range / 3.0f), z = (float)(_Float16)(mn + 0.0f);
+      if (s == 0.0f) continue;
+      for (int k = 0; k < G; ++k) {
+        const float u = (y[g * G + k] - z) / s;
+        U.push_back((int64_t)std::nearbyint((double)u * kGrid));
+      }
+    }
+  }
+  double lev[4] = {0.0, 1.0, 2.0, 3.0};
+  for (int it = 0; it < iters; ++it) {
+    double thr[3];
+    for (int k = 0; k < 3; ++k) thr[k] = (lev[k] + lev[k + 1]) * (kGrid / 2);
+    int64_t sum[4] = {0, 0, 0, 0}, cnt[4] = {0, 0, 0, 0};
+    for (int64_t v : U) {
+      const double dv = (double)v;
+      const int c = (dv > thr[0]) + (dv > thr[1]) + (dv > thr[2]);
+      sum[c] += v;
+      ++cnt[c];
+    }
+    for (int k = 0; k < 4; ++k)
+      if (cnt[k]) lev[k] = (double)sum[k] / (double)cnt[k] / kGrid;
+  }
+  for (int k = 0; k < 4; ++k) levels[k] = (uint8_t)std::min(255.0, std::max(0.0, std::nearbyint(lev[k] * 64.0)));
+  return ok();
 }
 
 int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R, double pct, float *clip) {

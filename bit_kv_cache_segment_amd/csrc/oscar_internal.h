@@ -46,7 +46,26 @@ struct PoolDev {
   // 1: the history is kept in BF16 (OSCAR_POOL_BF16_HISTORY): a page block
   // is K bf16 [64][d] then V bf16 [64][d], tokens copied, not encoded.
   int32_t bf16_hist;
+  // 1: the Lloyd-Max codebook variant (OSCAR_POOL_LLOYD_MAX): a history value
+  // is z + (L[code] / 64) s; codebook[kind * Hkv + kv] holds L_0..L_3 of kv
+  // head kv, K (kind 0) or V (kind 1), one byte each, L_0 in the low byte.
+  // A channel takes the nearest level: u = (y - z) / s against the
+  // midpoints (L_k + L_{k+1}) / 128, a midpoint itself taking the lower.
+  int32_t lut;
+  const uint32_t *codebook;
 };
+
+// Code of a clipped rotated value y under codebook dword lw (see lut above).
+__host__ __device__ inline uint32_t lut_code(float y, float z, float s, uint32_t lw) {
+  if (s == 0.0f) return 0u;
+  const float u = (y - z) / s;
+  uint32_t c = 0;
+  for (int k = 0; k < 3; ++k) {
+    const float t = (float)(((lw >> (8 * k)) & 255u) + ((lw >> (8 * k + 8)) & 255u)) / 128.0f;
+    c += u > t ? 1u : 0u;
+  }
+  return c;
+}
 
 constexpr uint32_t kStatusWaitGaveUp = 1u;
 constexpr int32_t kDefaultWaitLimit = 1 << 22;
@@ -216,6 +235,11 @@ hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const ui
                           int L, hipStream_t s);
 hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t s, const KernelTimer &t);
+// Lloyd-Max pools: resident decode blocks per compute unit and the history
+// launch (partials in the decode workspace layout; the merge is shared).
+int lut_decode_blocks_per_cu(const PoolDev &p);
+hipError_t launch_decode_lut(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float scale, float *ws,
+                             hipStream_t s, const KernelTimer &t);
 // Copy-on-write page copies (every kv head of each page).
 hipError_t launch_copy_pages(const PoolDev &p, const PageCopies &c, hipStream_t s);
 // Fork: sequence src's window (sink and recent ring, all kv heads) and the

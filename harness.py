@@ -29,6 +29,17 @@ def tables(w: synth.Workload, n_cal: int = N_CALIB):
     return R[0], R[1], clips[0], clips[1]
 
 
+def codebooks(w: synth.Workload, R_K, R_V, clip_K, clip_V, n_cal: int = N_CALIB):
+    """(L_K, L_V) uint8 [Hkv][4]: Lloyd-Max codebooks from the library's
+    offline fit on the calibration tokens."""
+    out = []
+    for kind, (R, clip) in enumerate(((R_K, clip_K), (R_V, clip_V))):
+        cal = synth.bf16_bits(synth.calibration_tokens(w, kind, n_cal))
+        out.append(np.stack([oscar.oscar_lloyd_max_codebook(cal[h], R[h], clip[h], w.group_size)
+                             for h in range(w.num_kv_heads)]))
+    return out[0], out[1]
+
+
 def pages_needed(L: int) -> int:
     return max(0, -(-(L - 320) // 64))
 

@@ -83,6 +83,20 @@ extern "C" {
  * INT2 only (EINVAL); oscar_export_history_bf16 exports the history. */
 #define OSCAR_POOL_BF16_HISTORY 4u
 
+/* Pool flag: the Lloyd-Max codebook variant ([A]; the news article's
+ * section "Why this matters for long-context agents": the OSCAR code pairs
+ * the attention-aware rotation with a Lloyd-Max codebook).  A history group
+ * keeps its fp16 scale s and zero point z; its four levels are
+ * z + (L_k / 64) s for a per-(kv head, K|V) codebook L_0 <= .. <= L_3 of
+ * bytes set by oscar_pool_set_codebook (fitted offline by
+ * oscar_lloyd_max_codebook) instead of z + k s, and a channel takes the
+ * nearest level: u = (y - z) / s (fp32) against the midpoints
+ * t_k = (L_k + L_{k+1}) / 128, a value on a midpoint taking the lower level;
+ * s = 0 gives code 0.  Layout, allocator, exports and merge are the INT2
+ * pool's; a step runs the append in its own launch; prefill attention
+ * refuses such pools.  Excludes OSCAR_POOL_BF16_HISTORY. */
+#define OSCAR_POOL_LLOYD_MAX 8u
+
 typedef struct oscar_pool oscar_pool;  /* opaque, host side */
 
 typedef struct oscar_pool_config {
@@ -279,6 +293,14 @@ int oscar_release_seq(oscar_pool *pool, int32_t seq);
  * Errors: EINVAL (bad id, src == dst, dst not empty), EHIP. */
 int oscar_fork_seq(oscar_pool *pool, int32_t src, int32_t dst, void *stream);
 
+/* Lloyd-Max pools: set the codebook, levels_k and levels_v host uint8
+ * [Hkv][4] (each row non-decreasing), while every sequence is empty; the
+ * pool refuses prefill and appends until it is set.  Synchronous on
+ * `stream`.  Errors: EINVAL (not such a pool, order, a non-empty sequence,
+ * null), EHIP. */
+int oscar_pool_set_codebook(oscar_pool *pool, const uint8_t *levels_k, const uint8_t *levels_v,
+                            void *stream);
+
 /* Current length of a sequence (host mirror).  Errors: EINVAL. */
 int oscar_seq_length(const oscar_pool *pool, int32_t seq, int32_t *L);
 
@@ -344,6 +366,19 @@ int oscar_build_rotation(int32_t d, const float *U, float *R);
  * Errors: EINVAL. */
 int oscar_calibrate_clip(int32_t d, int64_t n, const uint16_t *x, const float *R,
                          double pct, float *clip);
+
+/* Offline: the Lloyd-Max codebook of one head ([A]) from n host bf16
+ * calibration tokens x[n][d], its rotation R[d][d] and clip thresholds
+ * clip[d], group size G: the normalised values u = (y - z) / s of every
+ * channel of a group with s != 0 (rotation, clip, fp16 s and z exactly as
+ * the eviction computes them), taken on the grid of 2^-20; Lloyd's
+ * algorithm for `iters` iterations from the levels 0, 1, 2, 3 (cells split
+ * at the midpoints, a value on a midpoint in the lower cell; each level
+ * moves to its cell's mean, exact integer sums, fp64 division; an empty
+ * cell keeps its level); levels[k] = rint(64 level_k) clamped to 0..255.
+ * Errors: EINVAL. */
+int oscar_lloyd_max_codebook(int32_t d, int32_t G, int64_t n, const uint16_t *x, const float *R,
+                             const float *clip, int32_t iters, uint8_t *levels);
 
 /* Offline calibration statistics ([A]; the news article's section "OSCAR
  * aims the rotation at attention": the K rotation follows the query

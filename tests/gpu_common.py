@@ -24,16 +24,32 @@ def oracle_tables(name_or_w, n_cal=4096):
     return R[0], R[1], clips[0], clips[1]
 
 
-def oracle_sequence(w, b, L, heads=None):
+@functools.lru_cache(maxsize=None)
+def oracle_codebooks(name_or_w, n_cal=4096):
+    """(L_K, L_V) uint8 [Hkv][4]: the oracle's Lloyd-Max fit on the
+    calibration tokens with the oracle's own tables."""
+    w = synth.WORKLOADS[name_or_w] if isinstance(name_or_w, str) else name_or_w
+    RK, RV, cK, cV = oracle_tables(w, n_cal)
+    out = []
+    for kind, (R, c) in enumerate(((RK, cK), (RV, cV))):
+        cal = synth.bf16_bits(synth.calibration_tokens(w, kind, n_cal))
+        out.append(np.stack([oracle.lloyd_max_codebook(oracle.normalized_values(cal[h], R[h], c[h], w.group_size))
+                             for h in range(w.num_kv_heads)]))
+    return out[0], out[1]
+
+
+def oracle_sequence(w, b, L, heads=None, lloyd_max=False):
     """Oracle pool contents of synthetic sequence b at length L (optionally only
-    some kv heads: the others stay raw and must not be used)."""
+    some kv heads: the others stay raw and must not be used); lloyd_max: with
+    the oracle's Lloyd-Max codebooks."""
     RK, RV, cK, cV = oracle_tables(w)
     hs = list(range(w.num_kv_heads)) if heads is None else list(heads)
     k = np.zeros((L, w.num_kv_heads, w.head_dim), dtype=np.uint16)
     v = np.zeros_like(k)
     k[:, hs] = synth.bf16_bits(synth.kv_tokens(w, 0, b, 0, L, heads=hs))
     v[:, hs] = synth.bf16_bits(synth.kv_tokens(w, 1, b, 0, L, heads=hs))
-    return oracle.build_sequence(k, v, RK, RV, cK, cV, w.group_size, heads=hs), k, v
+    cb = oracle_codebooks(w) if lloyd_max else None
+    return oracle.build_sequence(k, v, RK, RV, cK, cV, w.group_size, heads=hs, codebook=cb), k, v
 
 
 def check_history_codes(pool, w, seq, st, heads, first=0, count=None):

@@ -180,7 +180,7 @@ def test_errors_leave_state_unchanged():
 
 @pytest.mark.parametrize("kw", [dict(head_dim=96), dict(group_size=32), dict(num_q_heads=6),
                                 dict(num_q_heads=12, num_kv_heads=4), dict(max_seqs=0),
-                                dict(group_size=128, head_dim=64), dict(num_pages=-1), dict(flags=8)])
+                                dict(group_size=128, head_dim=64), dict(num_pages=-1), dict(flags=16), dict(flags=12)])
 def test_bad_configs_rejected(kw):
     base = dict(max_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=64, group_size=64, num_pages=4,
                 max_pages_per_seq=2)

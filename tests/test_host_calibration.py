@@ -77,3 +77,44 @@ def test_calibration_argument_errors():
     assert L.oscar_calib_covariance(4, 8, 2, 128, P(16), P(16), P(16), 1.0, P(16), P(16), P(16), 100,
                                     None) == ok.EINVAL                                          # workspace
     assert ok.oscar_calib_workspace_bytes(10, 8, 128) == 10 * 8 * 128 * 4
+
+
+def test_lloyd_max_fit_matches_oracle():
+    # the library's offline fit and the oracle's, each from the same tokens,
+    # rotation and thresholds: identical codebooks
+    import harness
+    for name in ("tiny", "qwen3_8b_32k"):
+        w = synth.WORKLOADS[name]
+        RK, RV, cK, cV = harness.tables(w, n_cal=1024)
+        for kind, (R, clip) in enumerate(((RK, cK), (RV, cV))):
+            cal = synth.bf16_bits(synth.calibration_tokens(w, kind, 1024))
+            for h in range(min(2, w.num_kv_heads)):
+                lib_L = ok.oscar_lloyd_max_codebook(cal[h], R[h], clip[h], w.group_size)
+                or_L = oracle.lloyd_max_codebook(oracle.normalized_values(cal[h], R[h], clip[h], w.group_size))
+                assert list(lib_L) == list(or_L), (name, kind, h, lib_L, or_L)
+                assert lib_L[0] < lib_L[1] < lib_L[2] < lib_L[3]
+
+
+def test_lloyd_max_pool_calls_on_host_only_pools():
+    cfg = ok.make_config(4, 8, 2, 64, 64, 50, 10, 1, ok.POOL_HOST_ONLY | ok.POOL_LLOYD_MAX)
+    p = ok.Pool(cfg, None, None, None, None)
+    with pytest.raises(ok.OscarError) as ei:
+        p.prefill_len(0, 400)                 # no codebook yet
+    assert ei.value.code == ok.EINVAL and "codebook" in str(ei.value)
+    bad = np.array([[10, 5, 20, 30]] * 2, np.uint8)
+    good = np.array([[40, 79, 114, 154]] * 2, np.uint8)
+    with pytest.raises(ok.OscarError):
+        p.set_codebook(bad, good)             # not non-decreasing
+    p.set_codebook(good, good)
+    p.prefill_len(0, 400)
+    p.append([0], None, None)
+    with pytest.raises(ok.OscarError):
+        p.set_codebook(good, good)            # a sequence is not empty
+    p.release(0)
+    p.set_codebook(good, good)
+    with pytest.raises(ok.OscarError):        # excludes the BF16 history
+        ok.Pool(ok.make_config(4, 8, 2, 64, 64, 50, 10, 1, ok.POOL_HOST_ONLY | ok.POOL_LLOYD_MAX | 4),
+                None, None, None, None)
+    q = ok.Pool(ok.make_config(4, 8, 2, 64, 64, 50, 10, 1, ok.POOL_HOST_ONLY), None, None, None, None)
+    with pytest.raises(ok.OscarError):        # not a Lloyd-Max pool
+        q.set_codebook(good, good)
