@@ -33,9 +33,6 @@ inline int window_units(int d, int G, bool fused = false) {
 }
 // the same for a BF16-history pool (window and pages cost alike per byte)
 inline int window_units_bf16(int d) { return (int)std::lround((double)kWindow * 4 * d / bf16_block_bytes(d)); }
-// the same for a Lloyd-Max pool: a window token (bf16 dot products) costs
-// about half a history token (codebook lookups for K and V) on the VALU
-inline int window_units_lut() { return (int)std::lround(0.5 * kWindow / kPage); }
 
 // fused: the launch also appends (len is the length after the append); a
 // pair whose append evicts into the history keeps its last page in its last

@@ -40,6 +40,15 @@
 //   a pool constant 2^pv_shift go into the fp16 softmax weight P' of the A
 //   operand, the 2^24 / 2^pv_shift is undone once at the end.  The zero-point
 //   term sum_t p_t z_t is accumulated on the VALU.
+// Lloyd-Max codebook pools (LUT = true; news article on OSCAR, section "Why
+//   this matters for long-context agents": the rotation paired with a
+//   Lloyd-Max codebook): a level is z + (L[code] / 64) s.  The same MFMAs
+//   run on level bytes instead of codes: one byte permute per dword of codes
+//   turns four codes into their levels (the codebook dword is the permute
+//   table).  K bytes carry L - 128 as signed int8 (the zero point absorbs
+//   the + 2 s); the query grid is 2^16 so a group's sum stays below 2^31.
+//   V bytes carry L unsigned into the low byte of each fp16 half (two
+//   sub-normals L * 2^-24 per dword, no 4^e factors).
 #include "oscar_internal.h"
 
 #include <hip/hip_ext.h>
@@ -702,12 +711,14 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
 //     `limb` of rint(qs[h][c] 2^E) * {16, 4, 1, 16}[v], c = 64 mi + 16 r + 4 j + v.
 //   Limbs are balanced signed bytes: X = a0 + 2^8 a1 + 2^16 a2.
 // Record tail: qsum[h][g] (group sums of qs) at 0, kfac[h] = 2^-(E+4) at 32.
+// Codebook pools (LUT): E = 16 - e, no {16, 4, 1, 16} factors, and
+// kfac = 2^-(E+6) (the code bytes carry 64 x the level, less 128).
 // On entry R holds R_K and qT the query rows (after a barrier).  The product
 // is taken by column blocks; then one wave per head finds E and the group
 // sums and writes the head's words.  On exit (after a barrier) rec holds the
 // record.
 // ---------------------------------------------------------------------------
-template <int D, int G, int GQ, int W>
+template <int D, int G, int GQ, int W, bool LUT = false>
 __device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const RTable<D> &R, float qscale, int tid) {
   constexpr int NG = D / G, MI = D / 64, RT = GQ >= 4 ? GQ / 4 : 1;
   static_assert(G == 64 || G == D, "channel groups of 64, or one group per token");
@@ -717,7 +728,8 @@ __device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const RTable<D> 
   float *tail = (float *)(rec + RT * MI * 256);
   // lane -> (k-quad r, limb row lam, register v) of the head's words
   const int r = lane >> 4, lam = (lane >> 2) & 3, v = lane & 3;
-  const int mult = v == 1 ? 4 : (v == 2 ? 1 : 16);
+  // codebook pools: the code bytes carry L - 128 (|.| <= 128), no 4^e factor
+  const int mult = LUT ? 1 : (v == 1 ? 4 : (v == 2 ? 1 : 16));
   for (int h = w; h < 4 * RT; h += W) { // heads >= GQ (when GQ < 4) get zero words
     const bool live = h < GQ;
     float x[MI], mx = 0.f; // lane holds channels lane + 64 k
@@ -742,8 +754,10 @@ __device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const RTable<D> 
     }
     int ex = 0;
     frexpf(mx, &ex);
-    const int E = mx > 0.f ? 18 - ex : 0;
-    if (live && lane == 0) tail[32 + h] = ldexpf(1.f, -(E + 4));
+    // |q_int| <= 2^18 (affine codes: products <= 2^18 * 48) or 2^16 (codebook
+    // bytes: products <= 2^16 * 128), so a group's sum stays below 2^31
+    const int E = mx > 0.f ? (LUT ? 16 : 18) - ex : 0;
+    if (live && lane == 0) tail[32 + h] = ldexpf(1.f, LUT ? -(E + 6) : -(E + 4));
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       uint32_t word = 0;
@@ -805,7 +819,7 @@ __device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk
 template <int D, int G, int GQ>
 constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
-template <int D, int G, int GQ, bool PREFILL = false>
+template <int D, int G, int GQ, bool PREFILL = false, bool LUT = false>
 __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
                               float *ws_hist, float *ws_win, const uint16_t *q, float qscale, const AppendIn &in,
                               int slot, int e, int kv, int p0, int p1, bool with_window) {
@@ -892,7 +906,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // across the window.  Each wave then zeroes its own P' rows (only this
   // wave touches them; rows no head owns stay zero for the whole loop).
   auto finish_prologue = [&]() __attribute__((always_inline)) {
-    query_prep<D, G, GQ, W>(sm.u.pre, sm.rec, sm.R, qscale, tid);
+    query_prep<D, G, GQ, W, LUT>(sm.u.pre, sm.rec, sm.R, qscale, tid);
     u32x4 *P = (u32x4 *)&sm.u.P[w][0][0][0];
     for (int idx = lane; idx < NG * 16 * kPRow / 8; idx += 64) P[idx] = u32x4{0u, 0u, 0u, 0u};
   };
@@ -940,13 +954,18 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
 
   // per-token factor of P': 2^pv_shift * 4^-e(k), k = token within its
   // 16-token block, e = pair index (k >> 1), or (k >> 1) - 5 past the shift
+  // (codebook pools: the V bytes are unshifted, so 2^pv_shift alone)
   float pfac[4];
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     const int k = (4 * n + T) & 15, i = k >> 1;
     const int ee = i <= 4 ? i : i - 5;
-    pfac[T] = ldexpf(1.f, p.pv_shift - 2 * ee);
+    pfac[T] = ldexpf(1.f, LUT ? p.pv_shift : p.pv_shift - 2 * ee);
   }
+  // Codebook pools: the levels as permute tables, K as signed bytes L - 128
+  // (the int8 MFMA operand), V as unsigned bytes L (fp16 sub-normals)
+  const uint32_t lutK = LUT ? p.codebook[kv] ^ 0x80808080u : 0u;
+  const uint32_t lutV = LUT ? p.codebook[Hkv + kv] : 0u;
 
   // prefill: position of the query of each row tile's head in this lane
   // (rows rt * 4 + r); tokens after it are masked on the masked pages
@@ -985,8 +1004,16 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
           const uint32_t wv = cur.kc[(T * MI + mi) / 4][(T * MI + mi) % 4];
-          const v4i B = v4i{(int)(wv & 0x03030303u), (int)(wv & 0x0C0C0C0Cu), (int)(wv & 0x30303030u),
-                            (int)((wv >> 6) & 0x03030303u)};
+          v4i B;
+          if constexpr (LUT)
+            // each byte's code selects its level byte
+            B = v4i{(int)__builtin_amdgcn_perm(lutK, lutK, wv & 0x03030303u),
+                    (int)__builtin_amdgcn_perm(lutK, lutK, (wv >> 2) & 0x03030303u),
+                    (int)__builtin_amdgcn_perm(lutK, lutK, (wv >> 4) & 0x03030303u),
+                    (int)__builtin_amdgcn_perm(lutK, lutK, (wv >> 6) & 0x03030303u)};
+          else
+            B = v4i{(int)(wv & 0x03030303u), (int)(wv & 0x0C0C0C0Cu), (int)(wv & 0x30303030u),
+                    (int)((wv >> 6) & 0x03030303u)};
           const int g = NG == 1 ? 0 : mi;
   #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
@@ -1006,7 +1033,13 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
             const uint32_t sz = cur.kp[(T * NG + g) / 4][(T * NG + g) % 4];
             // the logit in units of kfac (a power of two; the softmax below
             // applies it), so the products are those of kfac * logit exactly
-            l = fmaf(f16lo(sz), dv, fmaf(f16hi(sz), qsum[rt][g], l));
+            if constexpr (LUT) {
+              // level = (L - 128) / 64 + 2: the zero point gains 2 s
+              const float sc = f16lo(sz);
+              l = fmaf(sc, dv, fmaf(fmaf(2.f, sc, f16hi(sz)), qsum[rt][g], l));
+            } else {
+              l = fmaf(f16lo(sz), dv, fmaf(f16hi(sz), qsum[rt][g], l));
+            }
           }
           bool vis = tvalid && (GQ >= 4 || rt * 4 + r < GQ);
           if constexpr (PREFILL) vis = vis && (full || tpos <= vpos[rt]);
@@ -1114,9 +1147,20 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const uint32_t wv = cur.vc[j / 4][j % 4];
-        const uint32_t w2 = wv >> 10;
-        const u32x4 b0 = u32x4{wv & 0x00030003u, wv & 0x000C000Cu, wv & 0x00300030u, wv & 0x00C000C0u};
-        const u32x4 b1 = u32x4{wv & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
+        u32x4 b0, b1;
+        if constexpr (LUT) {
+          // tokens (2i, 2i + 1): codes to selector bytes 0 and 2, zero bytes
+          // (selector 0x0C) above them: two fp16 sub-normals L * 2^-24
+          auto pair = [&](int i) __attribute__((always_inline)) {
+            return __builtin_amdgcn_perm(lutV, lutV, ((wv >> (2 * i)) & 0x00030003u) | 0x0C000C00u);
+          };
+          b0 = u32x4{pair(0), pair(1), pair(2), pair(3)};
+          b1 = u32x4{pair(4), pair(5), pair(6), pair(7)};
+        } else {
+          const uint32_t w2 = wv >> 10;
+          b0 = u32x4{wv & 0x00030003u, wv & 0x000C000Cu, wv & 0x00300030u, wv & 0x00C000C0u};
+          b1 = u32x4{wv & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
+        }
         const int g = (16 * j) / G;
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][0], __builtin_bit_cast(v8h, b0), acc[j], 0, 0, 0);
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[g][1], __builtin_bit_cast(v8h, b1), acc[j], 0, 0, 0);
@@ -1235,7 +1279,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
         mw[i] = h < GQ ? sm.M[w][h] : -INFINITY;
       }
     }
-    const float unscale = ldexpf(1.f, 24 - p.pv_shift);
+    const float unscale = ldexpf(1.f, LUT ? 18 - p.pv_shift : 24 - p.pv_shift); // codebook bytes: 64 x the level
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * r + i;
@@ -1362,7 +1406,7 @@ __global__ __launch_bounds__((merge_threads<D, GQ>())) void decode_merge_kernel(
   merge_pair<D, GQ, merge_threads<D, GQ>(), PREFILL>(p, b, out, ws, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
-template <int D, int G, int GQ, bool PREFILL = false>
+template <int D, int G, int GQ, bool PREFILL = false, bool LUT = false>
 __global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
 void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
                         float *__restrict__ ws, AppendIn in) {
@@ -1386,7 +1430,7 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   // batch's largest split count (launch order is by split count, descending)
   const int slot = (e * Hkv + kv) * karg_u8(b.nsplit, 0) + s;
   if (p0 < p1)
-    history_block<D, G, GQ, PREFILL>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
+    history_block<D, G, GQ, PREFILL, LUT>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
   else if (s == S - 1) {
     window_block<D, G, GQ, PREFILL>(sm.w, p, b, q, qscale, ws_win, in, e, kv);
     // this split holds no pages: an empty history partial for the merge
@@ -1401,8 +1445,13 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
   const int blocks = b.hist_blocks;
   // Timed launches take their start/stop timestamps from the dispatch itself
   // (no extra packets between kernels).
-  hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
-                        tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, in);
+  if (p.lut)
+    hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ, false, true>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0,
+                          s, tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws,
+                          in);
+  else
+    hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
+                          tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, in);
   // A separate launch: merging in the last block of each pair needs
   // device-scope fences, which cost more than this kernel here.
   hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s,
@@ -1444,6 +1493,16 @@ template <int D, int G>
 int blocks_per_cu_g(const PoolDev &p) {
   int nb = 0;
   hipError_t e = hipErrorInvalidValue;
+  if (p.lut) {
+    switch (p.Hq / p.Hkv) {
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 1, false, true>, 64 * main_waves(D, G, 1), 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 2, false, true>, 64 * main_waves(D, G, 2), 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 4, false, true>, 64 * main_waves(D, G, 4), 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 8, false, true>, 64 * main_waves(D, G, 8), 0); break;
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 16, false, true>, 64 * main_waves(D, G, 16), 0); break;
+    }
+    return e == hipSuccess ? nb : 0;
+  }
   switch (p.Hq / p.Hkv) {
   case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 1>, 64 * main_waves(D, G, 1), 0); break;
   case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 2>, 64 * main_waves(D, G, 2), 0); break;

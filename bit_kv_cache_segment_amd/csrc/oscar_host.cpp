@@ -374,9 +374,7 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
     int dev = 0, cus = 0;
     e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int per_cu = D.bf16_hist ? bf16_decode_blocks_per_cu(D)
-                       : D.lut     ? lut_decode_blocks_per_cu(D)
-                                   : decode_main_blocks_per_cu(D);
+    const int per_cu = D.bf16_hist ? bf16_decode_blocks_per_cu(D) : decode_main_blocks_per_cu(D);
     if (e != hipSuccess || cus <= 0 || per_cu <= 0) {
       delete p;
       return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "querying the decode occupancy");
@@ -641,7 +639,7 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
   }
   const int Hq = p->cfg.num_q_heads, Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim;
   const int g = Hq / Hkv;
-  const bool bf16 = p->dev.bf16_hist != 0, lut = p->dev.lut != 0;
+  const bool bf16 = p->dev.bf16_hist != 0;
   std::vector<DecodeBatch> batches;
   size_t need = 0;
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
@@ -650,7 +648,7 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     std::vector<int> len(b.n);
     for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]];
     plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
-                bf16 ? window_units_bf16(d) : lut ? window_units_lut() : window_units(d, p->cfg.group_size));
+                bf16 ? window_units_bf16(d) : window_units(d, p->cfg.group_size));
     need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
     batches.push_back(b);
   }
@@ -661,9 +659,8 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     const uint16_t *qi = q + i * (size_t)kMaxBatch * Hq * d;
     float *oi = out + i * (size_t)kMaxBatch * Hq * d;
     hipError_t e;
-    if (bf16 || lut) {
-      e = bf16 ? launch_decode_bf16(p->dev, batches[i], qi, softmax_scale, (float *)workspace, (hipStream_t)stream, tm)
-               : launch_decode_lut(p->dev, batches[i], qi, softmax_scale, (float *)workspace, (hipStream_t)stream, tm);
+    if (bf16) {
+      e = launch_decode_bf16(p->dev, batches[i], qi, softmax_scale, (float *)workspace, (hipStream_t)stream, tm);
       if (e == hipSuccess)
         e = launch_decode_merge(p->dev, batches[i], oi, (const float *)workspace, (hipStream_t)stream, tg);
     } else {
@@ -701,7 +698,8 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
   // the append is its own launch (same results).
   std::vector<DecodeBatch> batches;
   size_t need = 0;
-  // (BF16-history and Lloyd-Max pools append in their own launch)
+  // (BF16-history and Lloyd-Max pools append in their own launch: the
+  // fused append encodes with the affine levels)
   bool fused = p->dev.bf16_hist == 0 && p->dev.lut == 0;
   for (int pass = fused ? 0 : 1; pass < 2; ++pass) {
     batches.clear();
@@ -712,10 +710,7 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
       std::vector<int> len(b.n);
       for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
       plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
-                  p->dev.bf16_hist ? window_units_bf16(d)
-                  : p->dev.lut     ? window_units_lut()
-                                   : window_units(d, p->cfg.group_size, fused),
-                  fused);
+                  p->dev.bf16_hist ? window_units_bf16(d) : window_units(d, p->cfg.group_size, fused), fused);
       need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
       if (b.hist_blocks > p->decode_slots) fused = false;
       batches.push_back(b);

@@ -235,11 +235,6 @@ hipError_t launch_prefill(const PoolDev &p, int seq, const uint16_t *k, const ui
                           int L, hipStream_t s);
 hipError_t launch_append(const PoolDev &p, const AppendBatch &b, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t s, const KernelTimer &t);
-// Lloyd-Max pools: resident decode blocks per compute unit and the history
-// launch (partials in the decode workspace layout; the merge is shared).
-int lut_decode_blocks_per_cu(const PoolDev &p);
-hipError_t launch_decode_lut(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float scale, float *ws,
-                             hipStream_t s, const KernelTimer &t);
 // Copy-on-write page copies (every kv head of each page).
 hipError_t launch_copy_pages(const PoolDev &p, const PageCopies &c, hipStream_t s);
 // Fork: sequence src's window (sink and recent ring, all kv heads) and the
