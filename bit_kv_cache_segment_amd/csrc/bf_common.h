@@ -1,7 +1,7 @@
-// Device pieces shared by the VALU split-KV decode kernels (the BF16-history
-// baseline and the Lloyd-Max codebook variant): DPP lane sums, kernel-argument
-// readers, and the BF16 token loop used for a pair's window (sink and recent
-// tokens, stored as they are) and for BF16 history pages.
+// Device pieces of the VALU split-KV decode kernel of the BF16-history
+// baseline: DPP lane sums, kernel-argument readers, the BF16 token loop used
+// for a pair's window (sink and recent tokens, stored as they are) and for
+// the history pages, and the block epilogue's wave merge.
 #pragma once
 
 #include "oscar_internal.h"

@@ -654,9 +654,14 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_ld
       s16[c] = f16_bits(((mx[c] - mn[c]) + 0.0f) / 3.0f);
       z16[c] = f16_bits(mn[c] + 0.0f);
       const float sc = f16_val(s16[c]), ze = f16_val(z16[c]);
-      float qv = 0.0f;
-      if (sc != 0.0f) qv = fminf(fmaxf(rintf((y[c] - ze) / sc), 0.0f), 3.0f);
-      code[c] = (uint32_t)qv;
+      if (p.lut) {
+        // codebook pools: the nearest level
+        code[c] = lut_code(y[c], ze, sc, p.codebook[kind * Hkv + kv]);
+      } else {
+        float qv = 0.0f;
+        if (sc != 0.0f) qv = fminf(fmaxf(rintf((y[c] - ze) / sc), 0.0f), 3.0f);
+        code[c] = (uint32_t)qv;
+      }
     }
     uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
 #pragma unroll

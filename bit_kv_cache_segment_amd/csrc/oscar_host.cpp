@@ -698,9 +698,8 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
   // the append is its own launch (same results).
   std::vector<DecodeBatch> batches;
   size_t need = 0;
-  // (BF16-history and Lloyd-Max pools append in their own launch: the
-  // fused append encodes with the affine levels)
-  bool fused = p->dev.bf16_hist == 0 && p->dev.lut == 0;
+  // (BF16-history pools append in their own launch)
+  bool fused = p->dev.bf16_hist == 0;
   for (int pass = fused ? 0 : 1; pass < 2; ++pass) {
     batches.clear();
     need = 0;
