@@ -67,29 +67,37 @@ def _cpu_pair(task):
     import oracle
     import synth
 
-    name, b, kv, L = task
+    name, b, kv, L, lloyd = task
     w = synth.WORKLOADS[name]
     with threadpool_limits(limits=1):
         import torch
         torch.set_num_threads(1)
         RK, RV, cK, cV = _cpu_tables(name)
         g, d, G = w.gqa, w.head_dim, w.group_size
+        if lloyd:  # the Lloyd-Max variant: the oracle's own codebooks
+            LK, LV = _cpu_codebooks(name)
+            enc = lambda x, R, c, Lc: oracle.encode_lut(x, R, c, G, Lc)
+            dec = lambda pk, s16, z16, R, Lc: oracle.decode_history_lut(pk, s16, z16, G, Lc, R)
+        else:
+            LK = LV = [None] * w.num_kv_heads
+            enc = lambda x, R, c, Lc: oracle.encode(x, R, c, G)
+            dec = lambda pk, s16, z16, R, Lc: oracle.decode_history(pk, s16, z16, G, R)
         q = synth.bf16_bits(synth.queries(w, 0))
         k = synth.bf16_bits(synth.kv_tokens(w, 0, b, 0, L + 1, heads=[kv]))[:, 0]
         v = synth.bf16_bits(synth.kv_tokens(w, 1, b, 0, L + 1, heads=[kv]))[:, 0]
         n_hist = max(0, L + 1 - 320)
-        hk = oracle.encode(k[64:64 + n_hist - 1], RK[kv], cK[kv], G) if n_hist > 1 else None
-        hv = oracle.encode(v[64:64 + n_hist - 1], RV[kv], cV[kv], G) if n_hist > 1 else None
+        hk = enc(k[64:64 + n_hist - 1], RK[kv], cK[kv], LK[kv]) if n_hist > 1 else None
+        hv = enc(v[64:64 + n_hist - 1], RV[kv], cV[kv], LV[kv]) if n_hist > 1 else None
         t0 = time.perf_counter()
-        ek = oracle.encode(k[64 + n_hist - 1:64 + n_hist], RK[kv], cK[kv], G)
-        ev = oracle.encode(v[64 + n_hist - 1:64 + n_hist], RV[kv], cV[kv], G)
+        ek = enc(k[64 + n_hist - 1:64 + n_hist], RK[kv], cK[kv], LK[kv])
+        ev = enc(v[64 + n_hist - 1:64 + n_hist], RV[kv], cV[kv], LV[kv])
         cat = (lambda a, e: e if a is None else tuple(np.concatenate([x, y]) for x, y in zip(a, e)))
         pk, sk, zk = cat(hk, ek)
         pv, sv, zv = cat(hv, ev)
         K = oracle.bf16_bits_to_f64(k)
         V = oracle.bf16_bits_to_f64(v)
-        K[64:64 + n_hist] = oracle.decode_history(pk, sk, zk, G, RK[kv])
-        V[64:64 + n_hist] = oracle.decode_history(pv, sv, zv, G, RV[kv])
+        K[64:64 + n_hist] = dec(pk, sk, zk, RK[kv], LK[kv])
+        V[64:64 + n_hist] = dec(pv, sv, zv, RV[kv], LV[kv])
         qf = oracle.bf16_bits_to_f64(q[b])
         for h in range(kv * g, (kv + 1) * g):
             oracle.attention(qf[h], K, V, 1 / math.sqrt(d))
@@ -116,6 +124,27 @@ def _cpu_tables(name):
     return _tables_cache[name]
 
 
+_codebook_cache = {}
+
+
+def _cpu_codebooks(name):
+    """The oracle's Lloyd-Max codebooks (built once per worker)."""
+    if name not in _codebook_cache:
+        import numpy as np
+
+        import oracle
+        import synth
+        w = synth.WORKLOADS[name]
+        RK, RV, cK, cV = _cpu_tables(name)
+        out = []
+        for kind, (R, c) in enumerate(((RK, cK), (RV, cV))):
+            cal = synth.bf16_bits(synth.calibration_tokens(w, kind, 4096))
+            out.append(np.stack([oracle.lloyd_max_codebook(oracle.normalized_values(cal[h], R[h], c[h], w.group_size))
+                                 for h in range(w.num_kv_heads)]))
+        _codebook_cache[name] = tuple(out)
+    return _codebook_cache[name]
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -127,7 +156,7 @@ def _cpu_model():
     return None
 
 
-def cpu_baseline(w, lengths, budget_s, max_workers=16):
+def cpu_baseline(w, lengths, budget_s, max_workers=16, lloyd=False):
     """The CPU oracle on a bounded sample of one step, on the host's cores:
     (sequence, kv head) pairs in worker processes (one thread each), spread
     over the batch, until about budget_s seconds of timed step work are done.
@@ -141,7 +170,7 @@ def cpu_baseline(w, lengths, budget_s, max_workers=16):
     cores = max(1, min(len(os.sched_getaffinity(0)), max_workers))
     rng = np.random.default_rng(7)
     pairs = [(int(i) // w.num_kv_heads, int(i) % w.num_kv_heads) for i in rng.permutation(w.batch * w.num_kv_heads)]
-    tasks = [(w.name, b, kv, int(lengths[b])) for b, kv in pairs]
+    tasks = [(w.name, b, kv, int(lengths[b]), lloyd) for b, kv in pairs]
     done, timed = 0, 0.0
     t0 = time.perf_counter()
     with mp.get_context("spawn").Pool(cores) as pool:
@@ -167,6 +196,24 @@ def cpu_baseline(w, lengths, budget_s, max_workers=16):
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
+def _cpu_prefill(name, L, n_q, n_sample):
+    """The oracle's prefill attention of the g query heads of kv head 0 for
+    the last n_sample of the chunk's n_q queries over that kv head's pool (its
+    history encoded first, untimed); returns the timed seconds."""
+    import oracle
+    import synth
+    w = synth.WORKLOADS[name]
+    g = w.num_q_heads // w.num_kv_heads
+    RK, RV, cK, cV = _cpu_tables(name)
+    k = synth.bf16_bits(synth.kv_tokens(w, 0, 0, 0, L, heads=[0]))
+    v = synth.bf16_bits(synth.kv_tokens(w, 1, 0, 0, L, heads=[0]))
+    st = oracle.build_sequence(k, v, RK[:1], RV[:1], cK[:1], cV[:1], w.group_size)
+    q = synth.bf16_bits(synth.queries(w, 0, batch=n_q))[n_q - n_sample:, :g]
+    t0 = time.perf_counter()
+    oracle.prefill_attention(st, q, 1 / math.sqrt(w.head_dim))
+    return time.perf_counter() - t0
+
+
 def prefill_main(args):
     """Prefill-attention measurement: the last n_q positions of one prompt of
     L tokens (the final chunk of a chunked prefill, its K/V already in the
@@ -181,6 +228,18 @@ def prefill_main(args):
 
     w = synth.WORKLOADS[args.workload]
     L, n_q = args.prefill_len, args.prefill_chunk
+    cpu = None
+    if args.cpu_seconds > 0:
+        n_s = min(1024, n_q)
+        g = w.num_q_heads // w.num_kv_heads
+        secs = _cpu_prefill(w.name, L, n_q, n_s)
+        from threadpoolctl import threadpool_info
+        blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        cpu = {"value": n_q / (secs * (n_q / n_s) * (w.num_q_heads / g)), "unit": "tokens/s per layer",
+               "cores": max(blas) if blas else 1, "kind": "oracle",
+               "sample": f"oracle prefill attention of the {g} query heads of 1 of {w.num_kv_heads} kv heads for "
+                         f"the last {n_s} of {n_q} queries ({secs:.1f} s, history encoding untimed), scaled to "
+                         f"the chunk"}
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     RK, RV, cK, cV = harness.tables(w)
@@ -219,6 +278,7 @@ def prefill_main(args):
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
                      "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 
@@ -329,9 +389,13 @@ def compare_bf16_main(args):
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    lengths0 = [int(x) for x in synth.lengths(w)]
+    # the oracle's INT2 decode step on the same workload, before the GPU is touched
+    cpu = cpu_baseline(w, lengths0, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    if cpu:
+        cpu["unit"] = "tokens/s per layer (INT2 history decode step; the metric is a ratio)"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    lengths0 = [int(x) for x in synth.lengths(w)]
     ids = list(range(w.batch))
     total = args.warmup + args.steps
     per = -(-total // args.layers)
@@ -385,6 +449,7 @@ def compare_bf16_main(args):
         "step_speedup": res["bf16"]["step"] / res["int2"]["step"],
         "pool_bytes_per_layer": {"int2": res["int2"]["pool_bytes_per_layer"],
                                  "bf16": res["bf16"]["pool_bytes_per_layer"]},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -446,9 +511,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     lengths0 = [int(x) for x in synth.lengths(w)]
     lloyd = args.codebook == "lloyd_max"
-    # the CPU baseline first, before this process touches the GPU (the
-    # oracle's step is the affine codec's; no baseline for the variant)
-    cpu = cpu_baseline(w, lengths0, args.cpu_seconds) if args.cpu_seconds > 0 and not lloyd else None
+    # the CPU baseline first, before this process touches the GPU
+    cpu = cpu_baseline(w, lengths0, args.cpu_seconds, lloyd=lloyd) if args.cpu_seconds > 0 else None
 
     import torch
 
@@ -529,9 +593,11 @@ def main():
             bytes_main.append(algorithmic_decode_bytes(w, [L + a + 1 for L in lengths0]))
     bytes_launch = float(np.mean(bytes_main))
     achieved = bytes_launch / (ms_main * 1e-3) / 1e9
-    kname = "decode_lut" if lloyd else "decode_main"
-    traffic = traffic_record(os.path.join(ROOT, "bit_kv_cache_segment_amd", "csrc",
-                                          "kernels_lut.hip" if lloyd else "kernels_decode.hip"), w.name, kname)
+    # (the codebook variant is decode_main_kernel's LUT instantiation: its own
+    # traffic record)
+    kname = "decode_main_lut" if lloyd else "decode_main"
+    traffic = traffic_record(os.path.join(ROOT, "bit_kv_cache_segment_amd", "csrc", "kernels_decode.hip"), w.name,
+                             kname)
     value = w.batch / (ms_step * 1e-3)
     step_bytes = bytes_launch + w.batch * w.num_q_heads * w.head_dim * 4
     res = {
@@ -556,7 +622,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": kname + "_kernel", "bytes_per_launch": bytes_launch,
+                     "kernel": "decode_main_kernel" + ("<LUT>" if lloyd else ""), "bytes_per_launch": bytes_launch,
                      "ms_per_launch": ms_main},
         "cpu_baseline": cpu,
         "detail": {"ms_decode_main": ms_main,
