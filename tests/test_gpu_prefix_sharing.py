@@ -17,7 +17,7 @@ import bit_kv_cache_segment_amd as ok
 import harness
 import oracle
 import synth
-from gpu_common import TOL, check_history_codes, check_windows, oracle_tables
+from gpu_common import TOL, check_history_codes, check_windows, oracle_codebooks, oracle_tables
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,8 @@ SOURCES = [394, 1000, 384, 300]
 
 def _workload(name, flags=0):
     Hq, Hkv, d, G = SHAPES[name]
-    return synth.Workload("fork_" + name, 40 + list(SHAPES).index(name) + 5 * bool(flags), 10, Hq, Hkv, d, G, 0, 0)
+    return synth.Workload("fork_" + name, 40 + list(SHAPES).index(name) + 5 * bool(flags) + 3 * bool(flags & 8), 10,
+                          Hq, Hkv, d, G, 0, 0)
 
 
 def _tokens(w, segs, L):
@@ -57,6 +58,8 @@ class Run:
         n_seqs = 10
         cfg = harness.config_for(w, [1000] * n_seqs, extra_tokens=100, slack_pages=4, flags=flags)
         self.pool = ok.Pool(cfg, RK, RV, cK, cV, max_batch=n_seqs)
+        if flags & ok.POOL_LLOYD_MAX:
+            self.pool.set_codebook(*harness.codebooks(w, RK, RV, cK, cV))
         self.model = oracle.PoolModel(cfg.num_pages, cfg.page_shuffle_seed, cfg.max_pages_per_seq)
         self.segs, self.stream, self.length = {}, {}, {}
         self.n_seqs = n_seqs
@@ -96,7 +99,8 @@ class Run:
         if self.flags & ok.POOL_BF16_HISTORY:
             return oracle.SeqTokens(L, oracle.bf16_bits_to_f64(k), oracle.bf16_bits_to_f64(v), {}), k, v
         RK, RV, cK, cV = oracle_tables(w)
-        return oracle.build_sequence(k, v, RK, RV, cK, cV, w.group_size), k, v
+        cb = oracle_codebooks(w) if self.flags & ok.POOL_LLOYD_MAX else None
+        return oracle.build_sequence(k, v, RK, RV, cK, cV, w.group_size, codebook=cb), k, v
 
     def check_out(self, ids, out, q_bits):
         worst = 0.0
@@ -184,6 +188,12 @@ def test_forks_bf16_history_pool():
     w = _workload("g4_d128_G128", ok.POOL_BF16_HISTORY)
     run = Run(w, ok.POOL_BF16_HISTORY)
     _drive(run, 40, 8)
+
+
+def test_forks_lloyd_max_pool():
+    w = _workload("g8_d128_G64", ok.POOL_LLOYD_MAX)
+    run = Run(w, ok.POOL_LLOYD_MAX)
+    _drive(run, 40, 9)
 
 
 def test_fork_then_release_everything_returns_every_page():
