@@ -87,12 +87,14 @@ def check_rows(out_gpu, st, q_bits, w, rows):
     return err
 
 
-def check_evicted(pool, w, seqs, lengths, count):
+def check_evicted(pool, w, seqs, lengths, count, lloyd_max=False):
     """Every kv head of each sequence in `seqs`: the last `count` history
     entries (the tokens the latest appends evicted) bit-exact against the
-    oracle's encoding of those tokens alone.  lengths[b]: length now.
-    Returns the number of (token, kv head, K|V) encodings compared."""
+    oracle's encoding of those tokens alone (with the oracle's Lloyd-Max
+    codebooks if lloyd_max).  lengths[b]: length now.  Returns the number of
+    (token, kv head, K|V) encodings compared."""
     RK, RV, cK, cV = oracle_tables(w)
+    cb = oracle_codebooks(w) if lloyd_max else None
     checked = 0
     for b in seqs:
         n_hist = max(0, int(lengths[b]) - oracle.WINDOW)
@@ -105,7 +107,10 @@ def check_evicted(pool, w, seqs, lengths, count):
         toks = [synth.bf16_bits(synth.kv_tokens(w, kind, b, pos0, c)) for kind in (0, 1)]
         for h in range(w.num_kv_heads):
             for kvi, (R, clip) in enumerate(((RK, cK), (RV, cV))):
-                pk, s16, z16 = oracle.encode(toks[kvi][:, h], R[h], clip[h], w.group_size)
+                if cb is None:
+                    pk, s16, z16 = oracle.encode(toks[kvi][:, h], R[h], clip[h], w.group_size)
+                else:
+                    pk, s16, z16 = oracle.encode_lut(toks[kvi][:, h], R[h], clip[h], w.group_size, cb[kvi][h])
                 assert np.array_equal(codes[:, h, kvi], pk), (b, h, kvi)
                 assert np.array_equal(params[:, h, kvi, :, 0], s16), (b, h, kvi)
                 assert np.array_equal(params[:, h, kvi, :, 1], z16), (b, h, kvi)

@@ -3,7 +3,8 @@ times) at full workload sizes and on plans no smaller test reaches:
 
 * the 16 x 32K and 32 x 64K layers, several steps through the fused step:
   every page table, every evicted token of every (sequence, kv head) pair
-  bit-exact, sampled attention rows within 2e-3;
+  bit-exact, sampled attention rows within 2e-3 (16 x 32K also with the
+  Lloyd-Max codebook);
 * a mid-size fused step whose pairs are cut into two splits, so a history
   block runs beside the window block that appends and the window block
   reads the evicted token's page after the append has written it;
@@ -28,6 +29,8 @@ def _pool(w, lengths, extra, flags=0, seed=None):
     RK, RV, cK, cV = harness.tables(w)
     cfg = harness.config_for(w, lengths, extra_tokens=extra, flags=flags, seed=seed)
     pool = ok.Pool(cfg, RK, RV, cK, cV, max_batch=len(lengths))
+    if flags & ok.POOL_LLOYD_MAX:
+        pool.set_codebook(*harness.codebooks(w, RK, RV, cK, cV))
     harness.prefill_all(pool, w, lengths)
     m = oracle.PoolModel(cfg.num_pages, cfg.page_shuffle_seed, cfg.max_pages_per_seq)
     for b, L in enumerate(lengths):
@@ -39,11 +42,13 @@ def _rows_of(w, kv):
     return list(range(kv * w.gqa, (kv + 1) * w.gqa))
 
 
-@pytest.mark.parametrize("name,steps", [("qwen3_8b_32k", 3), ("qwen3_32b_64k", 2)])
-def test_fused_step_at_full_size(name, steps):
+@pytest.mark.parametrize("name,steps,lloyd", [("qwen3_8b_32k", 3, False), ("qwen3_32b_64k", 2, False),
+                                              ("qwen3_8b_32k", 3, True)],
+                         ids=["qwen3_8b_32k", "qwen3_32b_64k", "qwen3_8b_32k-lloyd_max"])
+def test_fused_step_at_full_size(name, steps, lloyd):
     w = synth.WORKLOADS[name]
     lengths = [int(x) for x in synth.lengths(w)]
-    pool, m = _pool(w, lengths, extra=steps)
+    pool, m = _pool(w, lengths, extra=steps, flags=ok.POOL_LLOYD_MAX if lloyd else 0)
     ids = list(range(w.batch))
     rng = np.random.default_rng(w.config_id + 700)
     for step in range(1, steps + 1):
@@ -57,17 +62,17 @@ def test_fused_step_at_full_size(name, steps):
         assert torch.isfinite(out).all()
         for b in ids:
             assert list(pool.page_table(b)) == m.table[b]
-        n = check_evicted(pool, w, ids, lengths, 1)
+        n = check_evicted(pool, w, ids, lengths, 1, lloyd_max=lloyd)
         assert n == w.batch * w.num_kv_heads * 2
         qb = synth.bf16_bits(synth.queries(w, step))
         pair = (int(rng.integers(0, w.batch)), int(rng.integers(0, w.num_kv_heads)))
         for b, kv in {pair, (w.batch - 1, w.num_kv_heads - 1)}:
-            st, _, _ = oracle_sequence(w, b, lengths[b], heads=[kv])
+            st, _, _ = oracle_sequence(w, b, lengths[b], heads=[kv], lloyd_max=lloyd)
             err = check_rows(out[b], st, qb[b], w, _rows_of(w, kv))
             print(f"  pair {(b, kv)}: row-relative error {err:.2e}", flush=True)
     # the whole history of the sequences, one kv head each, at the end
     for b, kv in ((0, 0), (w.batch - 1, w.num_kv_heads - 1)):
-        st, k, v = oracle_sequence(w, b, lengths[b], heads=[kv])
+        st, k, v = oracle_sequence(w, b, lengths[b], heads=[kv], lloyd_max=lloyd)
         check_history_codes(pool, w, b, st, [kv])
         check_windows(pool, w, b, lengths[b], k, v, [kv])
 
