@@ -46,7 +46,8 @@
 //   run on level bytes instead of codes: one byte permute per dword of codes
 //   turns four codes into their levels (the codebook dword is the permute
 //   table).  K bytes carry L - 128 as signed int8 (the zero point absorbs
-//   the + 2 s); the query grid is 2^16 so a group's sum stays below 2^31.
+//   the + 2 s); the query grid is 2^17 (2^16 for groups of 128 channels
+//   when a level is 0) so a group's sum stays below 2^31.
 //   V bytes carry L unsigned into the low byte of each fp16 half (two
 //   sub-normals L * 2^-24 per dword, no 4^e factors).
 #include "oscar_internal.h"
@@ -716,15 +717,17 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
 //     `limb` of rint(qs[h][c] 2^E) * {16, 4, 1, 16}[v], c = 64 mi + 16 r + 4 j + v.
 //   Limbs are balanced signed bytes: X = a0 + 2^8 a1 + 2^16 a2.
 // Record tail: qsum[h][g] (group sums of qs) at 0, kfac[h] = 2^-(E+4) at 32.
-// Codebook pools (LUT): E = 16 - e, no {16, 4, 1, 16} factors, and
-// kfac = 2^-(E+6) (the code bytes carry 64 x the level, less 128).
+// Codebook pools (LUT): E = 17 - e (16 - e for groups of 128 channels when
+// a level is 0), no {16, 4, 1, 16} factors, and kfac = 2^-(E+6) (the code
+// bytes carry 64 x the level, less 128).
 // On entry R holds R_K and qT the query rows (after a barrier).  The product
 // is taken by column blocks; then one wave per head finds E and the group
 // sums and writes the head's words.  On exit (after a barrier) rec holds the
 // record.
 // ---------------------------------------------------------------------------
 template <int D, int G, int GQ, int W, bool LUT = false>
-__device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const RTable<D> &R, float qscale, int tid) {
+__device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const RTable<D> &R, float qscale, int tid,
+                           int ebits = 18) {
   constexpr int NG = D / G, MI = D / 64, RT = GQ >= 4 ? GQ / 4 : 1;
   static_assert(G == 64 || G == D, "channel groups of 64, or one group per token");
   const int w = tid >> 6, lane = tid & 63;
@@ -759,9 +762,11 @@ __device__ void query_prep(QueryPrep<D, GQ> &pr, uint32_t *rec, const RTable<D> 
     }
     int ex = 0;
     frexpf(mx, &ex);
-    // |q_int| <= 2^18 (affine codes: products <= 2^18 * 48) or 2^16 (codebook
-    // bytes: products <= 2^16 * 128), so a group's sum stays below 2^31
-    const int E = mx > 0.f ? (LUT ? 16 : 18) - ex : 0;
+    // |q_int| <= 2^ebits: 2^18 (affine codes: products <= 2^18 * 48), or for
+    // codebook bytes (products <= |q_int| |L - 128|) 2^17, or 2^16 for groups
+    // of 128 channels with a level of 0 (|L - 128| = 128): a group's sum
+    // stays below 2^31
+    const int E = mx > 0.f ? ebits - ex : 0;
     if (live && lane == 0) tail[32 + h] = ldexpf(1.f, LUT ? -(E + 6) : -(E + 4));
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -843,6 +848,13 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   const int seq = b.seq[e], n_hist = b.len[e] - kWindow;
   const int np = (n_hist + kPage - 1) / kPage;
 
+  // bits of the query's fixed-point grid (see query_prep)
+  int qbits = 18;
+  if constexpr (LUT) {
+    const uint32_t cb = p.codebook[kv];
+    const bool zero_level = ((cb - 0x01010101u) & ~cb & 0x80808080u) != 0u; // some L_k == 0
+    qbits = (G == 64 || !zero_level) ? 17 : 16;
+  }
   const int32_t *ptab = p.page_table + (size_t)seq * p.maxp;
   const size_t hstride = (size_t)Hkv * p.block_bytes;
   const size_t hoff = (size_t)kv * p.block_bytes;
@@ -911,7 +923,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // across the window.  Each wave then zeroes its own P' rows (only this
   // wave touches them; rows no head owns stay zero for the whole loop).
   auto finish_prologue = [&]() __attribute__((always_inline)) {
-    query_prep<D, G, GQ, W, LUT>(sm.u.pre, sm.rec, sm.R, qscale, tid);
+    query_prep<D, G, GQ, W, LUT>(sm.u.pre, sm.rec, sm.R, qscale, tid, qbits);
     u32x4 *P = (u32x4 *)&sm.u.P[w][0][0][0];
     for (int idx = lane; idx < NG * 16 * kPRow / 8; idx += 64) P[idx] = u32x4{0u, 0u, 0u, 0u};
   };
@@ -1481,8 +1493,12 @@ template <int D, int G, int GQ>
 hipError_t prefill_attn_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
                              float *ws, hipStream_t s) {
   const AppendIn none{nullptr, nullptr};
-  hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
-                     p, b, q, scale * kLog2e, ws, none);
+  if (p.lut)
+    hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)),
+                       0, s, p, b, q, scale * kLog2e, ws, none);
+  else
+    hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)), 0,
+                       s, p, b, q, scale * kLog2e, ws, none);
   hipLaunchKernelGGL((decode_merge_kernel<D, GQ, true>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s, p, b,
                      out, (const float *)ws);
   return hipGetLastError();
@@ -1521,8 +1537,11 @@ int blocks_per_cu_g(const PoolDev &p) {
 template <int D, int G>
 int prefill_blocks_per_cu_g(const PoolDev &p) {
   int nb = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &nb, decode_main_kernel<D, G, kPrefillTile, true>, 64 * main_waves(D, G, kPrefillTile), 0);
+  const hipError_t e =
+      p.lut ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, kPrefillTile, true, true>,
+                                                           64 * main_waves(D, G, kPrefillTile), 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, kPrefillTile, true>,
+                                                           64 * main_waves(D, G, kPrefillTile), 0);
   return e == hipSuccess ? nb : 0;
 }
 

@@ -803,8 +803,7 @@ int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *
   int rc = check_seq(p, seq);
   if (rc) return rc;
   if (p->host_only) return fail(OSCAR_EINVAL, "prefill attention on a host-only pool");
-  if (p->dev.bf16_hist || p->dev.lut)
-    return fail(OSCAR_EINVAL, "prefill attention runs on INT2-history pools with the affine levels");
+  if (p->dev.bf16_hist) return fail(OSCAR_EINVAL, "prefill attention runs on INT2-history pools");
   const int32_t L = p->len[seq];
   if (n_q < 1 || n_q > L || (int64_t)n_q * p->cfg.num_q_heads > ((int64_t)1 << 30))
     return fail(OSCAR_EINVAL, "n_q = %d outside [1, L = %d] (or n_q x Hq above 2^30)", n_q, L);

@@ -92,9 +92,9 @@ extern "C" {
  * oscar_lloyd_max_codebook) instead of z + k s, and a channel takes the
  * nearest level: u = (y - z) / s (fp32) against the midpoints
  * t_k = (L_k + L_{k+1}) / 128, a value on a midpoint taking the lower level;
- * s = 0 gives code 0.  Layout, allocator, exports, decode and step are the
- * INT2 pool's (the decode reads levels instead of codes); prefill attention
- * refuses such pools.  Excludes OSCAR_POOL_BF16_HISTORY. */
+ * s = 0 gives code 0.  Layout, allocator, exports, decode, step and prefill
+ * attention are the INT2 pool's (the kernels read levels instead of codes).
+ * Excludes OSCAR_POOL_BF16_HISTORY. */
 #define OSCAR_POOL_LLOYD_MAX 8u
 
 typedef struct oscar_pool oscar_pool;  /* opaque, host side */

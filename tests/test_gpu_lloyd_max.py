@@ -4,7 +4,7 @@ oracle's nearest-level encoding with the oracle's own codebooks (the
 library's offline fit gives the same codebooks, a CPU test), and decode
 attention within 2e-3 row-relative of the oracle's attention over the pool
 decoded with those levels; over the segment-edge lengths, shuffled appends
-and steps, on four shapes, and with prefix sharing."""
+and steps, on four shapes; prefill attention over such a pool."""
 import math
 
 import numpy as np
@@ -120,13 +120,20 @@ def test_deterministic_pool_is_bitwise_reproducible():
     _check_all(w, a, lengths, 3, [0, 1, 2])
 
 
-def test_prefill_attention_refuses_lloyd_max_pools():
-    w = _workload("g1_d64_G64")
-    pool, cfg, _ = _pool(w, [400], 0)
-    harness.prefill_all(pool, w, [400])
-    q = synth.queries(w, 0, device="cuda", batch=8).view(torch.uint16)
-    out = torch.empty((8, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
-    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
-    with pytest.raises(ok.OscarError) as ei:
-        pool.prefill_attn(0, q, out, workspace=ws)
-    assert ei.value.code == ok.EINVAL
+@pytest.mark.parametrize("shape", ["g4_d128_G128", "g8_d128_G64", "g1_d64_G64"])
+def test_prefill_attention_over_a_lloyd_max_pool(shape):
+    # the last n_q positions of a prompt attend causally over the pool with
+    # the codebook's levels: within 2e-3 of the oracle's prefill attention
+    w = _workload(shape)
+    lengths = [1400, 700]
+    pool, cfg, _ = _pool(w, lengths, 0)
+    harness.prefill_all(pool, w, lengths)
+    for seq, L, n_q in ((0, 1400, 1400), (0, 1400, 300), (1, 700, 5)):
+        q = synth.queries(w, 500 + n_q, batch=n_q)
+        out = pool.prefill_attn(seq, q.to("cuda").view(torch.uint16).contiguous())
+        torch.cuda.synchronize()
+        st, _, _ = oracle_sequence(w, seq, L, lloyd_max=True)
+        ref = oracle.prefill_attention(st, synth.bf16_bits(q), 1 / math.sqrt(w.head_dim))
+        err = oracle.row_rel_err(out.double().cpu().numpy().reshape(-1, w.head_dim), ref.reshape(-1, w.head_dim))
+        print(f"{shape}: seq {seq}, n_q {n_q}: worst row error {err:.2e}")
+        assert err <= TOL, (seq, n_q, err)
