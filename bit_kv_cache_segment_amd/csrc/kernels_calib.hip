@@ -7,12 +7,14 @@
 //
 // Two kernels:
 //   calib_attn_kernel  O = causal softmax(scale Q K^T) V per query head, fp32
-//                      (one wave per query row; the sequence is short and
-//                      this runs once per layer, so plain VALU code);
+//                      (one wave per four query rows, sharing their key and
+//                      value loads; the sequence is short and this runs once
+//                      per layer, so plain VALU code);
 //   gram_kernel        C += X^T X per kv head on v_mfma_f32_16x16x4_f32: one
-//                      wave per 16 x 16 output tile, the contraction running
-//                      over tokens (and the kv head's query heads) four
-//                      tokens per instruction, four interleaved accumulators.
+//                      block per 16 x 16 output tile, its 8 waves splitting
+//                      the tokens, the contraction running over tokens (and
+//                      the kv head's query heads) four tokens per
+//                      instruction, four interleaved accumulators per wave.
 #include <hip/hip_runtime.h>
 
 #include "oscar_internal.h"
@@ -36,68 +38,104 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// grid (ceil(n / 4), Hq), 256 threads: wave w takes query row t = 4 x + w of
-// query head y.  Keys are taken 64 at a time, one per lane: the lane's logit
-// is a full dot product of the query (in shared memory, read as a broadcast)
-// with its key row; the chunk then updates the running max m, sum l and the
-// lane's D/64 output channels (online softmax).  Masked keys (j > t) weigh 0.
+// grid (ceil(n / 16), Hq), 256 threads: wave w takes the QW = 4 query rows
+// t0 .. t0 + 3 (t0 = 16 x + 4 w) of query head y, so every key and value row
+// a lane loads serves four queries.  Keys are taken 64 at a time, one per
+// lane: the lane's four logits are full dot products of the queries (in
+// shared memory, read as broadcasts) with its key row; the chunk then
+// updates each query's running max m, sum l and the lane's D/64 output
+// channels (online softmax).  Keys past a query's position weigh 0.
 template <int D>
 __global__ __launch_bounds__(256) void calib_attn_kernel(int n, int Hq, int Hkv, const uint16_t *__restrict__ q,
                                                          const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v, float scale,
                                                          float *__restrict__ o) {
-  constexpr int CPL = D / 64; // output channels per lane: CPL lane + i
-  __shared__ float qs[4][D];
+  constexpr int CPL = D / 64, QW = 4; // output channels per lane; queries per wave
+  __shared__ float qs[4][QW][D];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + w, h = blockIdx.y, kvh = h / (Hq / Hkv);
-  const bool valid = t < n;
-  for (int c = lane; c < D; c += 64) qs[w][c] = valid ? bf16_to_f32(q[((size_t)t * Hq + h) * D + c]) : 0.f;
+  const int t0 = blockIdx.x * 16 + QW * w, h = blockIdx.y, kvh = h / (Hq / Hkv);
+  for (int idx = lane; idx < QW * D; idx += 64) {
+    const int r = idx / D, c = idx % D, t = t0 + r;
+    qs[w][r][c] = t < n ? bf16_to_f32(q[((size_t)t * Hq + h) * D + c]) : 0.f;
+  }
   __syncthreads();
-  if (!valid) return;
-  float m = -INFINITY, l = 0.f, acc[CPL];
+  if (t0 >= n) return;
+  const int tlast = min(t0 + QW - 1, n - 1); // the wave's last query
+  float m[QW], l[QW], acc[QW][CPL];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-  for (int j0 = 0; j0 <= t; j0 += 64) {
+  for (int r = 0; r < QW; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[r][i] = 0.f;
+  }
+  for (int j0 = 0; j0 <= tlast; j0 += 64) {
     const int j = j0 + lane;
-    float logit = -INFINITY;
-    if (j <= t) {
+    float s[QW];
+#pragma unroll
+    for (int r = 0; r < QW; ++r) s[r] = 0.f;
+    if (j <= tlast) {
       const uint4 *kr = (const uint4 *)(k + ((size_t)j * Hkv + kvh) * D);
-      float s = 0.f;
-#pragma unroll 4
+#pragma unroll 2
       for (int c8 = 0; c8 < D / 8; ++c8) {
         const uint4 u = kr[c8];
         const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s = fmaf(qs[w][8 * c8 + 2 * e], __uint_as_float(wd[e] << 16), s);
-          s = fmaf(qs[w][8 * c8 + 2 * e + 1], __uint_as_float(wd[e] & 0xffff0000u), s);
+          const float k0 = __uint_as_float(wd[e] << 16), k1 = __uint_as_float(wd[e] & 0xffff0000u);
+#pragma unroll
+          for (int r = 0; r < QW; ++r) {
+            s[r] = fmaf(qs[w][r][8 * c8 + 2 * e], k0, s[r]);
+            s[r] = fmaf(qs[w][r][8 * c8 + 2 * e + 1], k1, s[r]);
+          }
         }
       }
-      logit = scale * s;
     }
-    const float m_new = fmaxf(m, wave_max(logit)); // finite: key j0 <= t is visible
-    const float alpha = expf(m - m_new);           // 0 on the first chunk
-    const float p = j <= t ? expf(logit - m_new) : 0.f;
-    l = l * alpha + wave_sum(p);
+    float p[QW];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[i] *= alpha;
-    const int cnt = min(64, t + 1 - j0);
+    for (int r = 0; r < QW; ++r) {
+      const bool vis = j <= t0 + r && t0 + r < n;
+      const float logit = vis ? scale * s[r] : -INFINITY;
+      const float mx = wave_max(logit);
+      const float m_new = fmaxf(m[r], mx);
+      // a query whose every key so far is masked (none yet: j0 > its
+      // position never happens before its first chunk) keeps m = -inf
+      const float alpha = m_new == -INFINITY ? 1.f : expf(m[r] - m_new);
+      p[r] = vis ? expf(logit - m_new) : 0.f;
+      l[r] = l[r] * alpha + wave_sum(p[r]);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[r][i] *= alpha;
+      m[r] = m_new;
+    }
+    const int cnt = min(64, tlast + 1 - j0);
     for (int jj = 0; jj < cnt; ++jj) {
-      const float pj = __shfl(p, jj);
+      float pj[QW];
+#pragma unroll
+      for (int r = 0; r < QW; ++r) pj[r] = __shfl(p[r], jj);
       const uint16_t *vr = v + ((size_t)(j0 + jj) * Hkv + kvh) * D + CPL * lane;
+      float vv[CPL];
       if constexpr (CPL == 2) {
         const uint32_t u = *(const uint32_t *)vr;
-        acc[0] = fmaf(pj, __uint_as_float(u << 16), acc[0]);
-        acc[1] = fmaf(pj, __uint_as_float(u & 0xffff0000u), acc[1]);
+        vv[0] = __uint_as_float(u << 16);
+        vv[1] = __uint_as_float(u & 0xffff0000u);
       } else {
-        acc[0] = fmaf(pj, bf16_to_f32(vr[0]), acc[0]);
+        vv[0] = bf16_to_f32(vr[0]);
       }
-    }
-    m = m_new;
-  }
-  float *orow = o + ((size_t)t * Hq + h) * D + CPL * lane;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) orow[i] = acc[i] / l;
+      for (int r = 0; r < QW; ++r)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) acc[r][i] = fmaf(pj[r], vv[i], acc[r][i]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < QW; ++r) {
+    const int t = t0 + r;
+    if (t < n) {
+      float *orow = o + ((size_t)t * Hq + h) * D + CPL * lane;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) orow[i] = acc[r][i] / l[r];
+    }
+  }
 }
 
 template <typename T>
@@ -111,31 +149,38 @@ __device__ __forceinline__ float load_f<float>(const float *x, size_t i) {
   return x[i];
 }
 
-// grid ((D/16)^2, Hkv), 64 threads.  X is [n][Hin][D] (Hin = Hkv g); output
-// kv head y sums input heads y g .. y g + g - 1.  For tile (ti, tj) the
+// grid ((D/16)^2, Hkv), 64 GW threads.  X is [n][Hin][D] (Hin = Hkv g);
+// output kv head y sums input heads y g .. y g + g - 1.  For tile (ti, tj) the
 // instruction's A operand (16 x 4) is X^T rows ti, its B operand (4 x 16)
 // X rows at tj: lane l loads channel 16 ti + l % 16 (A) and 16 tj + l % 16
 // (B) of token t0 + l / 16; the result's lane l holds rows 4 (l / 16) + r,
-// r < 4, of column l % 16.  C += the tile (accumulated into the caller's
-// matrix; one writer per element).
+// r < 4, of column l % 16.  Wave w of the GW waves takes the w-th share of
+// the tokens (multiples of 16); the waves' sums are added in wave order in
+// shared memory, and C += the total (accumulated into the caller's matrix;
+// one writer per element).
+constexpr int kGramWaves = 8;
 template <int D, typename T>
-__global__ __launch_bounds__(64) void gram_kernel(int n, int Hin, int g, const T *__restrict__ x,
-                                                  float *__restrict__ cov) {
-  constexpr int NT = D / 16;
-  const int ti = blockIdx.x / NT, tj = blockIdx.x % NT, ho = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kGramWaves) void gram_kernel(int n, int Hin, int g, const T *__restrict__ x,
+                                                               float *__restrict__ cov) {
+  constexpr int NT = D / 16, GW = kGramWaves;
+  __shared__ floatx4 part[GW][64];
+  const int ti = blockIdx.x / NT, tj = blockIdx.x % NT, ho = blockIdx.y;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, kq = lane >> 4;
+  const int share = ((n + GW - 1) / GW + 15) / 16 * 16;
+  const int tb = w * share, te = min(n, tb + share);
   floatx4 acc[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int hh = 0; hh < g; ++hh) {
     const T *xh = x + (size_t)(ho * g + hh) * D;
     const size_t ld = (size_t)Hin * D;
-    for (int t0 = 0; t0 < n; t0 += 16) {
+    for (int t0 = tb; t0 < te; t0 += 16) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int t = t0 + 4 * a + kq;
         float va = 0.f, vb = 0.f;
-        if (t < n) {
+        if (t < te) {
           va = load_f(xh, t * ld + 16 * ti + r);
           vb = load_f(xh, t * ld + 16 * tj + r);
         }
@@ -143,18 +188,24 @@ __global__ __launch_bounds__(64) void gram_kernel(int n, int Hin, int g, const T
       }
     }
   }
-  const floatx4 s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  part[w][lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (w == 0) {
+    floatx4 s = part[0][lane];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    float *c = cov + ((size_t)ho * D + 16 * ti + 4 * kq + rr) * D + 16 * tj + r;
-    *c += s[rr];
+    for (int ww = 1; ww < GW; ++ww) s += part[ww][lane];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float *c = cov + ((size_t)ho * D + 16 * ti + 4 * kq + rr) * D + 16 * tj + r;
+      *c += s[rr];
+    }
   }
 }
 
 template <int D>
 hipError_t attn_impl(int n, int Hq, int Hkv, const uint16_t *q, const uint16_t *k, const uint16_t *v, float scale,
                      float *o, hipStream_t s) {
-  hipLaunchKernelGGL(calib_attn_kernel<D>, dim3((n + 3) / 4, Hq), dim3(256), 0, s, n, Hq, Hkv, q, k, v, scale, o);
+  hipLaunchKernelGGL(calib_attn_kernel<D>, dim3((n + 15) / 16, Hq), dim3(256), 0, s, n, Hq, Hkv, q, k, v, scale, o);
   return hipGetLastError();
 }
 
@@ -163,11 +214,11 @@ hipError_t gram_impl(int n, int Hq, int Hkv, const uint16_t *q, const float *o, 
                      hipStream_t s) {
   const int g = Hq / Hkv;
   if (cov_k)
-    hipLaunchKernelGGL((gram_kernel<D, uint16_t>), dim3((D / 16) * (D / 16), Hkv), dim3(64), 0, s, n, Hq, g, q,
-                       cov_k);
+    hipLaunchKernelGGL((gram_kernel<D, uint16_t>), dim3((D / 16) * (D / 16), Hkv), dim3(64 * kGramWaves), 0, s, n, Hq,
+                       g, q, cov_k);
   if (cov_v)
-    hipLaunchKernelGGL((gram_kernel<D, float>), dim3((D / 16) * (D / 16), Hkv), dim3(64), 0, s, n, Hq, g, o,
-                       cov_v);
+    hipLaunchKernelGGL((gram_kernel<D, float>), dim3((D / 16) * (D / 16), Hkv), dim3(64 * kGramWaves), 0, s, n, Hq,
+                       g, o, cov_v);
   return hipGetLastError();
 }
 
