@@ -7,7 +7,7 @@
 //
 // Two kernels:
 //   calib_attn_kernel  O = causal softmax(scale Q K^T) V per query head, fp32
-//                      (one wave per four query rows, sharing their key and
+//                      (one wave per eight query rows, sharing their key and
 //                      value loads; the sequence is short and this runs once
 //                      per layer, so plain VALU code);
 //   gram_kernel        C += X^T X per kv head on v_mfma_f32_16x16x4_f32: one
@@ -26,6 +26,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Order shared-memory traffic of the lanes of one wave (no block barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -38,22 +45,25 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// grid (ceil(n / 16), Hq), 256 threads: wave w takes the QW = 4 query rows
-// t0 .. t0 + 3 (t0 = 16 x + 4 w) of query head y, so every key and value row
-// a lane loads serves four queries.  Keys are taken 64 at a time, one per
-// lane: the lane's four logits are full dot products of the queries (in
+// grid (ceil(n / 32), Hq), 256 threads: wave w takes the QW = 8 query rows
+// t0 .. t0 + 7 (t0 = 32 x + 8 w) of query head y, so every key and value row
+// a lane loads serves eight queries.  Keys are taken 64 at a time, one per
+// lane: the lane's eight logits are full dot products of the queries (in
 // shared memory, read as broadcasts) with its key row; the chunk then
 // updates each query's running max m, sum l and the lane's D/64 output
-// channels (online softmax).  Keys past a query's position weigh 0.
+// channels (online softmax), the chunk's weights passing through shared
+// memory (two broadcast reads per key).  Keys past a query's position
+// weigh 0.
 template <int D>
 __global__ __launch_bounds__(256) void calib_attn_kernel(int n, int Hq, int Hkv, const uint16_t *__restrict__ q,
                                                          const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v, float scale,
                                                          float *__restrict__ o) {
-  constexpr int CPL = D / 64, QW = 4; // output channels per lane; queries per wave
+  constexpr int CPL = D / 64, QW = 8; // output channels per lane; queries per wave
   __shared__ float qs[4][QW][D];
+  __shared__ float4 ps[4][64][QW / 4]; // the chunk's weights, [key][query]
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * 16 + QW * w, h = blockIdx.y, kvh = h / (Hq / Hkv);
+  const int t0 = blockIdx.x * (4 * QW) + QW * w, h = blockIdx.y, kvh = h / (Hq / Hkv);
   for (int idx = lane; idx < QW * D; idx += 64) {
     const int r = idx / D, c = idx % D, t = t0 + r;
     qs[w][r][c] = t < n ? bf16_to_f32(q[((size_t)t * Hq + h) * D + c]) : 0.f;
@@ -108,10 +118,16 @@ __global__ __launch_bounds__(256) void calib_attn_kernel(int n, int Hq, int Hkv,
       m[r] = m_new;
     }
     const int cnt = min(64, tlast + 1 - j0);
+#pragma unroll
+    for (int r4 = 0; r4 < QW / 4; ++r4) ps[w][lane][r4] = float4{p[4 * r4], p[4 * r4 + 1], p[4 * r4 + 2], p[4 * r4 + 3]};
+    wave_sync();
     for (int jj = 0; jj < cnt; ++jj) {
       float pj[QW];
 #pragma unroll
-      for (int r = 0; r < QW; ++r) pj[r] = __shfl(p[r], jj);
+      for (int r4 = 0; r4 < QW / 4; ++r4) {
+        const float4 t4 = ps[w][jj][r4];
+        pj[4 * r4] = t4.x, pj[4 * r4 + 1] = t4.y, pj[4 * r4 + 2] = t4.z, pj[4 * r4 + 3] = t4.w;
+      }
       const uint16_t *vr = v + ((size_t)(j0 + jj) * Hkv + kvh) * D + CPL * lane;
       float vv[CPL];
       if constexpr (CPL == 2) {
@@ -126,6 +142,8 @@ __global__ __launch_bounds__(256) void calib_attn_kernel(int n, int Hq, int Hkv,
 #pragma unroll
         for (int i = 0; i < CPL; ++i) acc[r][i] = fmaf(pj[r], vv[i], acc[r][i]);
     }
+    // the next chunk rewrites the weights only after every lane read them
+    wave_sync();
   }
 #pragma unroll
   for (int r = 0; r < QW; ++r) {
@@ -205,7 +223,7 @@ __global__ __launch_bounds__(64 * kGramWaves) void gram_kernel(int n, int Hin, i
 template <int D>
 hipError_t attn_impl(int n, int Hq, int Hkv, const uint16_t *q, const uint16_t *k, const uint16_t *v, float scale,
                      float *o, hipStream_t s) {
-  hipLaunchKernelGGL(calib_attn_kernel<D>, dim3((n + 15) / 16, Hq), dim3(256), 0, s, n, Hq, Hkv, q, k, v, scale, o);
+  hipLaunchKernelGGL(calib_attn_kernel<D>, dim3((n + 31) / 32, Hq), dim3(256), 0, s, n, Hq, Hkv, q, k, v, scale, o);
   return hipGetLastError();
 }
 
