@@ -49,6 +49,7 @@ inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vecto
   b.total_pages = (int32_t)total;
   b.win_units = wu;
   b.fused = fused ? 1 : 0;
+  b.direct = 0;
   b.pf_g = 0;
   b.pf_rows = 0;
   for (int e = 0; e < kMaxBatch; ++e) b.new_page[e] = -1;
@@ -97,6 +98,14 @@ inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vecto
     b.layer_prefix[l + 1] = b.layer_prefix[l] + cnt * Hkv;
   }
   b.hist_blocks = b.layer_prefix[kMaxSplits];
+}
+
+// INT2 decode launches whose pairs all have one split write the output rows
+// from the decode blocks (no merge launch).
+inline void set_direct(DecodeBatch &b) {
+  int one = 1;
+  for (int e = 0; e < b.n; ++e) one &= b.nsplit[e] == 1;
+  b.direct = one;
 }
 
 } // namespace oscar

@@ -336,9 +336,11 @@ union MainSmem {
 
 // Merge per-wave (M, L, A) of the W waves in shared memory and store one
 // partial per head.
+// (out != nullptr: the pair has no other partial, so the normalised rows
+// acc / l go to out[GQ][D] instead.)
 template <int D, int GQ, int W>
 __device__ void block_merge_store(const float (*M)[GQ], const float (*L)[GQ], const float (*A)[GQ][D],
-                                  float *dst /*[GQ][D+2]*/) {
+                                  float *dst /*[GQ][D+2]*/, float *out = nullptr) {
   const int tid = threadIdx.x;
   for (int idx = tid; idx < GQ * D; idx += W * 64) {
     const int h = idx / D, c = idx % D;
@@ -349,6 +351,10 @@ __device__ void block_merge_store(const float (*M)[GQ], const float (*L)[GQ], co
       const float f = M[ww][h] == -INFINITY ? 0.f : exp2f(M[ww][h] - m);
       a += f * A[ww][h][c];
       l += f * L[ww][h];
+    }
+    if (out) {
+      out[(size_t)h * D + c] = a / l;
+      continue;
     }
     float *o = dst + (size_t)h * (D + 2);
     o[c] = a;
@@ -692,7 +698,8 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_ld
 // A block that holds only a pair's window: all its waves take part.
 template <int D, int G, int GQ, bool PREFILL = false>
 __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
-                             const uint16_t *q, float qscale, float *ws_win, const AppendIn &in, int e, int kv) {
+                             const uint16_t *q, float qscale, float *ws_win, float *out, const AppendIn &in, int e,
+                             int kv) {
   constexpr int W = main_waves(D, G, GQ);
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   if (b.fused) {
@@ -705,7 +712,9 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
   }
   window_waves<D, G, GQ, W, PREFILL>(sm, p, b, q, qscale, e, kv, w);
   __syncthreads();
-  block_merge_store<D, GQ, W>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2));
+  block_merge_store<D, GQ, W>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2),
+                              !PREFILL && b.direct ? out + ((size_t)karg_u16(b.row, e) * p.Hq + kv * GQ) * D
+                                                   : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -831,8 +840,8 @@ constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
 template <int D, int G, int GQ, bool PREFILL = false, bool LUT = false>
 __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
-                              float *ws_hist, float *ws_win, const uint16_t *q, float qscale, const AppendIn &in,
-                              int slot, int e, int kv, int p0, int p1, bool with_window) {
+                              float *ws_hist, float *ws_win, float *out, const uint16_t *q, float qscale,
+                              const AppendIn &in, int slot, int e, int kv, int p0, int p1, bool with_window) {
   constexpr int W = main_waves(D, G, GQ), NT = 64 * W, WW = win_waves(W, GQ);
   constexpr int NG = D / G;                // scale/zero groups per token
   constexpr int MI = D / 64;               // i8 MFMAs per 16-token tile (64 channels each)
@@ -1329,15 +1338,49 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
     for (int ww = 0; ww < W; ++ww) a += sm.u.A[ww][h][j];
     sm.mT[j][h] = a;
   }
+  // A pair whose only split this is (b.direct: every pair of the launch
+  // has one) combines its history and window results here and writes the
+  // normalised rows: no merge launch.  dir[0][h] / dir[1][h]: the factors
+  // of the history and window sums (their maxima against the joint one),
+  // divided by the joint denominator; wf[ww][h]: each window wave's weight.
+  static_assert(2 + WW <= W, "the direct-output factors fit in the rescale rows");
+  const bool direct = !PREFILL && b.direct;
+  float(*dir)[16] = sm.alpha; // free after the page loop
+  float(*wf)[16] = sm.alpha + 2;
   if (tid < GQ) {
     const float m = sm.Mb[tid];
     float l = 0.f;
     for (int ww = 0; ww < W; ++ww)
       if (sm.M[ww][tid] != -INFINITY) l = fmaf(exp2f(sm.M[ww][tid] - m), sm.L[ww][tid], l);
-    dst[(size_t)tid * (D + 2) + D] = m;
-    dst[(size_t)tid * (D + 2) + D + 1] = l;
+    if (direct) {
+      float mw = -INFINITY, lw = 0.f;
+      for (int ww = 0; ww < WW; ++ww) mw = fmaxf(mw, sm.win.M[ww][tid]);
+      for (int ww = 0; ww < WW; ++ww) {
+        const float f = sm.win.M[ww][tid] == -INFINITY ? 0.f : exp2f(sm.win.M[ww][tid] - mw);
+        wf[ww][tid] = f;
+        lw += f * sm.win.L[ww][tid];
+      }
+      const float mm = fmaxf(m, mw); // the window is never empty
+      const float fh = m == -INFINITY ? 0.f : exp2f(m - mm), fw = exp2f(mw - mm);
+      const float il = 1.f / fmaf(fh, l, fw * lw);
+      dir[0][tid] = fh * il;
+      dir[1][tid] = fw * il;
+    } else {
+      dst[(size_t)tid * (D + 2) + D] = m;
+      dst[(size_t)tid * (D + 2) + D + 1] = l;
+    }
   }
   __syncthreads();
+  if (direct) {
+    float *o = out + ((size_t)karg_u16(b.row, e) * p.Hq + kv * GQ) * D;
+    contract_columns<D, GQ, W>(&sm.mT[0][0], sm.R, w, lane, [&](int h, int c, float y) {
+      float aw = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WW; ++ww) aw = fmaf(wf[ww][h], sm.win.A[ww][h][c], aw);
+      o[(size_t)h * D + c] = fmaf(dir[0][h], y, dir[1][h] * aw);
+    });
+    return;
+  }
   contract_columns<D, GQ, W>(&sm.mT[0][0], sm.R, w, lane,
                              [&](int h, int c, float y) { dst[(size_t)h * (D + 2) + c] = y; });
   // the window waves' results were written before the barriers above
@@ -1426,7 +1469,7 @@ __global__ __launch_bounds__((merge_threads<D, GQ>())) void decode_merge_kernel(
 template <int D, int G, int GQ, bool PREFILL = false, bool LUT = false>
 __global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
 void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
-                        float *__restrict__ ws, AppendIn in) {
+                        float *__restrict__ ws, float *__restrict__ out, AppendIn in) {
   constexpr int W = main_waves(D, G, GQ);
   __shared__ MainSmem<D, G, GQ, W> sm;
   float *ws_win = ws;
@@ -1447,9 +1490,11 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   // batch's largest split count (launch order is by split count, descending)
   const int slot = (e * Hkv + kv) * karg_u8(b.nsplit, 0) + s;
   if (p0 < p1)
-    history_block<D, G, GQ, PREFILL, LUT>(sm.h, p, b, ws_hist, ws_win, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
+    history_block<D, G, GQ, PREFILL, LUT>(sm.h, p, b, ws_hist, ws_win, out, q, qscale, in, slot, e, kv, p0, p1,
+                                          s == S - 1);
   else if (s == S - 1) {
-    window_block<D, G, GQ, PREFILL>(sm.w, p, b, q, qscale, ws_win, in, e, kv);
+    window_block<D, G, GQ, PREFILL>(sm.w, p, b, q, qscale, ws_win, out, in, e, kv);
+    if (!PREFILL && b.direct) return;
     // this split holds no pages: an empty history partial for the merge
     float *dst = ws_hist + (size_t)slot * GQ * (D + 2);
     for (int idx = threadIdx.x; idx < GQ * (D + 2); idx += 64 * W) dst[idx] = idx % (D + 2) == D ? -INFINITY : 0.f;
@@ -1465,14 +1510,18 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
   if (p.lut)
     hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ, false, true>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0,
                           s, tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws,
-                          in);
+                          out, in);
   else
     hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0, s,
-                          tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, in);
-  // A separate launch: merging in the last block of each pair needs
-  // device-scope fences, which cost more than this kernel here.
-  hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s,
-                        tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, out, (const float *)ws);
+                          tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws, out,
+                          in);
+  // Pairs split over several blocks are merged by a separate launch:
+  // merging in the last block of each pair needs device-scope fences, which
+  // cost more than this kernel here.  (b.direct: no pair is split, the
+  // blocks wrote the rows.)
+  if (!b.direct)
+    hipExtLaunchKernelGGL((decode_merge_kernel<D, GQ>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s,
+                          tg.on ? tg.ev[0] : nullptr, tg.on ? tg.ev[1] : nullptr, 0, p, b, out, (const float *)ws);
   return hipGetLastError();
 }
 
@@ -1495,10 +1544,10 @@ hipError_t prefill_attn_impl(const PoolDev &p, const DecodeBatch &b, const uint1
   const AppendIn none{nullptr, nullptr};
   if (p.lut)
     hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)),
-                       0, s, p, b, q, scale * kLog2e, ws, none);
+                       0, s, p, b, q, scale * kLog2e, ws, out, none);
   else
     hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)), 0,
-                       s, p, b, q, scale * kLog2e, ws, none);
+                       s, p, b, q, scale * kLog2e, ws, out, none);
   hipLaunchKernelGGL((decode_merge_kernel<D, GQ, true>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s, p, b,
                      out, (const float *)ws);
   return hipGetLastError();

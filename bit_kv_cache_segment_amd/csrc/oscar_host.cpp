@@ -649,13 +649,14 @@ int oscar_decode_attn(oscar_pool *p, const int32_t *seq_ids, int32_t n, const ui
     for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]];
     plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
                 bf16 ? window_units_bf16(d) : window_units(d, p->cfg.group_size));
+    if (!bf16) set_direct(b);
     need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
     batches.push_back(b);
   }
   if (workspace_bytes < need)
     return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
   for (size_t i = 0; i < batches.size(); ++i) {
-    KernelTimer tm = p->prof.next(0), tg = p->prof.next(1);
+    KernelTimer tm = p->prof.next(0), tg = batches[i].direct ? KernelTimer{} : p->prof.next(1);
     const uint16_t *qi = q + i * (size_t)kMaxBatch * Hq * d;
     float *oi = out + i * (size_t)kMaxBatch * Hq * d;
     hipError_t e;
@@ -710,6 +711,7 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
       for (int e = 0; e < b.n; ++e) len[e] = p->len[seq_ids[i0 + e]] + 1;
       plan_splits(b, seq_ids + i0, len, Hkv, p->decode_slots,
                   p->dev.bf16_hist ? window_units_bf16(d) : window_units(d, p->cfg.group_size, fused), fused);
+      if (!p->dev.bf16_hist) set_direct(b);
       need = std::max(need, decode_ws_floats(Hq, d, b.n, Hkv, b.nsplit[0], g) * sizeof(float));
       if (b.hist_blocks > p->decode_slots) fused = false;
       batches.push_back(b);
@@ -745,7 +747,7 @@ static int decode_step(oscar_pool *p, const int32_t *seq_ids, int32_t n, const u
   }
   for (size_t i = 0; i < batches.size(); ++i) {
     const size_t r0 = i * (size_t)kMaxBatch;
-    KernelTimer tm = p->prof.next(0), tg = p->prof.next(1);
+    KernelTimer tm = p->prof.next(0), tg = batches[i].direct ? KernelTimer{} : p->prof.next(1);
     hipError_t e = launch_decode(p->dev, batches[i], q + r0 * Hq * d, out + r0 * Hq * d, softmax_scale,
                                  (float *)workspace, k_new + r0 * Hkv * d, v_new + r0 * Hkv * d,
                                  (hipStream_t)stream, tm, tg);

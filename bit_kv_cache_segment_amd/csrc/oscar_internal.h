@@ -159,6 +159,9 @@ struct DecodeBatch {
   // sequence (len is the length after it).  new_page: as in AppendBatch
   // (launch order).
   int32_t fused;
+  // Every pair of the launch has one split: its block writes the output
+  // rows itself and no merge launch follows (INT2 decode only).
+  int32_t direct;
   // Prefill attention (oscar_prefill_attn): pf_g > 0 is the pool's query
   // heads per kv head and pf_rows the call's query count n_q.  The call's
   // rows (query i, head hh of the kv head), flat index i g + hh, are cut in
