@@ -21,9 +21,10 @@
 //       rotation, clip, quantization and packing after it;
 //     * the block merges its waves and de-rotates the history accumulator
 //       by R_V^T; it writes one partial (m, l, acc) per query head for the
-//       history and, if it holds it, one for the window.
-//   decode_merge_kernel, one block per (sequence, kv head): merge the
-//     partials, normalise, write fp32.
+//       history and, if it holds it, one for the window; when no pair of the
+//       launch is split it combines the two itself and writes the rows.
+//   decode_merge_kernel, one block per (sequence, kv head), when some pair
+//     is split: merge the partials, normalise, write fp32.
 // Softmax runs in base 2: logits are pre-multiplied by scale * log2(e).
 //
 // History pages (per wave):

@@ -50,6 +50,14 @@ int main(int argc, char **argv) {
     }
     for (int e = 0; e < b.n; ++e)
       if (seen_row[e] != 1) return fail("row not a permutation", it);
+    // direct output (no merge launch) exactly when no pair is split
+    if (b.direct != 0) return fail("a plan starts without direct output", it);
+    set_direct(b);
+    {
+      bool one = true;
+      for (int e = 0; e < b.n; ++e) one = one && b.nsplit[e] == 1;
+      if ((b.direct != 0) != one) return fail("direct output with a split pair, or not without one", it);
+    }
     if (b.hist_blocks != b.layer_prefix[kMaxSplits]) return fail("block count", it);
     std::vector<std::vector<int>> pages(b.n * Hkv), windows(b.n * Hkv, std::vector<int>(1, 0));
     for (int e = 0; e < b.n; ++e)

@@ -2,7 +2,8 @@
 math that the decode and merge kernels share (csrc/decode_plan.h,
 csrc/oscar_internal.h) are compiled for the host and run on random batches
 (every page and window covered exactly once, indices inside each pair, the
-launch order a permutation of the batch).  No GPU needed."""
+launch order a permutation of the batch, blocks writing the output rows
+themselves exactly when no pair is split).  No GPU needed."""
 import os
 import shutil
 import subprocess
