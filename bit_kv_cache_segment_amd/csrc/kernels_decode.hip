@@ -993,6 +993,11 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // (the int8 MFMA operand), V as unsigned bytes L (fp16 sub-normals)
   const uint32_t lutK = LUT ? p.codebook[kv] ^ 0x80808080u : 0u;
   const uint32_t lutV = LUT ? p.codebook[Hkv + kv] : 0u;
+  // V level pairs: selector bytes 1 and 3 pick zero.  Held in a register
+  // (mbcnt of an empty mask is 0, which the compiler does not fold), so that
+  // mask and OR form one v_and_or_b32: one instruction cannot take two
+  // literals here.
+  const uint32_t vsel_zero = 0x0C000C00u | __builtin_amdgcn_mbcnt_lo(0u, 0u);
 
   // prefill: position of the query of each row tile's head in this lane
   // (rows rt * 4 + r); tokens after it are masked on the masked pages
@@ -1179,7 +1184,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
           // tokens (2i, 2i + 1): codes to selector bytes 0 and 2, zero bytes
           // (selector 0x0C) above them: two fp16 sub-normals L * 2^-24
           auto pair = [&](int i) __attribute__((always_inline)) {
-            return __builtin_amdgcn_perm(lutV, lutV, ((wv >> (2 * i)) & 0x00030003u) | 0x0C000C00u);
+            return __builtin_amdgcn_perm(lutV, lutV, ((wv >> (2 * i)) & 0x00030003u) | vsel_zero);
           };
           b0 = u32x4{pair(0), pair(1), pair(2), pair(3)};
           b1 = u32x4{pair(4), pair(5), pair(6), pair(7)};
