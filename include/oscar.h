@@ -185,7 +185,9 @@ int oscar_append_evict(oscar_pool *pool, const int32_t *seq_ids, int32_t n,
  * as stored (bf16), history tokens as decoded, i.e. dequantized with their
  * group scale and zero point and mapped back by R_V^T / R_K^T.  Internally
  * the history is attended in the rotated basis (q . R_K, then acc . R_V^T),
- * split over pages, and merged with the window by an online softmax.
+ * split over pages, and merged with the window by an online softmax (by a
+ * merge kernel when some pair of a launch is split over several blocks, else
+ * inside each pair's block).
  *   seq_ids: host int32 [n] (every sequence non-empty);
  *   q:       device bf16 [n][Hq][d];   out: device fp32 [n][Hq][d];
  *   workspace: device, >= oscar_decode_workspace_bytes(cfg, n) bytes.
@@ -436,7 +438,8 @@ int oscar_calib_rotation(int32_t d, const float *cov, float *U, float *R, double
  * Errors: EINVAL, EHIP. */
 typedef struct oscar_profile {
     int32_t n_decode_main;   float ms_decode_main;   /* query prep, INT2 history, BF16 window */
-    int32_t n_decode_merge;  float ms_decode_merge;  /* merge of the partials                 */
+    int32_t n_decode_merge;  float ms_decode_merge;  /* merge of the partials (launches with a
+                                                         split pair; none otherwise)         */
     int32_t n_append;        float ms_append;        /* append / eviction                     */
 } oscar_profile;
 
