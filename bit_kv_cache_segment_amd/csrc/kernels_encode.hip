@@ -206,69 +206,80 @@ __global__ void prefill_window_kernel(PoolDev p, int seq, const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Append: grid (n, Hkv, K|V), block D: one sequence per block.  The loads a
-// token needs (its page id, the evicted element, column j of R) are issued
-// together before any of them is used.
+// Append: grid (ceil(n / spb), Hkv, K|V), block D: spb consecutive
+// sequences per block, one after the other, so that column j of R (the
+// loads of a thread) is read once per block rather than once per sequence.
+// Per sequence, the loads a token needs (its page id, the evicted element)
+// are issued together before they are used.
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(D) void append_kernel(PoolDev p, AppendBatch b, const uint16_t *__restrict__ k_new,
-                                                   const uint16_t *__restrict__ v_new) {
-  const int e = blockIdx.x, kv = blockIdx.y, kind = blockIdx.z, j = threadIdx.x, Hkv = p.Hkv;
-  const int seq = b.seq[e], L = b.len[e]; // length before the append
-  const uint16_t xnew = (kind ? v_new : k_new)[((size_t)e * Hkv + kv) * D + j];
-  if (L < kSink) {
-    (kind ? p.sinkV : p.sinkK)[(((size_t)seq * Hkv + kv) * kSink + L) * D + j] = xnew;
-    return;
-  }
-  const int slot = (L - kSink) % kRecent;
-  uint16_t *rs = (kind ? p.recentV : p.recentK) + (((size_t)seq * Hkv + kv) * kRecent + slot) * D;
-  if (L < kWindow) {
-    rs[j] = xnew;
-    return;
-  }
-  // evict the oldest recent token (held in this slot) into history n_hist
-  const int n_hist = L - kWindow, pg_idx = n_hist / kPage, t = n_hist % kPage;
-  const int page = b.new_page[e] >= 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + pg_idx];
-  if (p.bf16_hist) {
-    // BF16-history pool: the token is copied as it is
-    uint16_t *dst = (uint16_t *)(p.pages + ((size_t)page * Hkv + kv) * p.block_bytes) + (kind ? kPage * D : 0);
-    dst[t * D + j] = rs[j];
-    rs[j] = xnew; // this thread read element j above; no other thread touches it
-    if (b.new_page[e] >= 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
-    return;
-  }
-  const float xj = bf16f(rs[j]);
-  const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
-  float rc[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) rc[i] = R[i * D + j];
-  const float c = (kind ? p.clipV : p.clipK)[kv * D + j];
+                                                   const uint16_t *__restrict__ v_new, int spb) {
+  const int kv = blockIdx.y, kind = blockIdx.z, j = threadIdx.x, Hkv = p.Hkv;
+  const int e0 = blockIdx.x * spb, e1 = min(b.n, e0 + spb);
   __shared__ float xs[D];
   __shared__ float red[2 * (D / 64)];
-  xs[j] = xj;
-  rs[j] = xnew; // this thread read element j above; no other thread touches it
-  __syncthreads();
-  float acc = 0.0f;
+  // column j of R, loaded once for the block's sequences (a block whose
+  // sequences do not evict, or a BF16-history pool, leaves it unused)
+  float rc[D];
+  {
+    const float *R = (kind ? p.RV : p.RK) + (size_t)kv * D * D;
 #pragma unroll
-  for (int i = 0; i < D; ++i) acc = fmaf(xs[i], rc[i], acc);
-  const float y = fminf(fmaxf(acc, -c), c);
-  uint16_t s16, z16;
-  const uint32_t code =
-      quantize_channel<D, G>(y, red, s16, z16, p.lut != 0, p.lut ? p.codebook[kind * Hkv + kv] : 0u);
-  if (b.new_page[e] >= 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
-  uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
-  if (kind == 0) {
-    store_k_code<D>(blk, t, code);
-    store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
-  } else {
-    // a byte holds four tokens of channel j (those with equal k & 1 and
-    // k >> 3, k = t % 16); the first of them, k & 6 == 0, starts the byte
-    const int k = t % 16;
-    uint8_t *byte = blk + vcode_dword_off(D, t / 16, j) + vbit(k) / 8;
-    const int sh = vbit(k) % 8;
-    const uint32_t old = (k & 6) == 0 ? 0u : *byte;
-    *byte = (uint8_t)((old & ~(3u << sh)) | (code << sh));
-    store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
+    for (int i = 0; i < D; ++i) rc[i] = R[i * D + j];
+  }
+  for (int e = e0; e < e1; ++e) {
+    const int seq = b.seq[e], L = b.len[e]; // length before the append
+    const uint16_t xnew = (kind ? v_new : k_new)[((size_t)e * Hkv + kv) * D + j];
+    if (L < kSink) {
+      (kind ? p.sinkV : p.sinkK)[(((size_t)seq * Hkv + kv) * kSink + L) * D + j] = xnew;
+      continue;
+    }
+    const int slot = (L - kSink) % kRecent;
+    uint16_t *rs = (kind ? p.recentV : p.recentK) + (((size_t)seq * Hkv + kv) * kRecent + slot) * D;
+    if (L < kWindow) {
+      rs[j] = xnew;
+      continue;
+    }
+    // evict the oldest recent token (held in this slot) into history n_hist
+    const int n_hist = L - kWindow, pg_idx = n_hist / kPage, t = n_hist % kPage;
+    const int page = b.new_page[e] >= 0 ? b.new_page[e] : p.page_table[(size_t)seq * p.maxp + pg_idx];
+    if (p.bf16_hist) {
+      // BF16-history pool: the token is copied as it is
+      uint16_t *dst = (uint16_t *)(p.pages + ((size_t)page * Hkv + kv) * p.block_bytes) + (kind ? kPage * D : 0);
+      dst[t * D + j] = rs[j];
+      rs[j] = xnew; // this thread read element j above; no other thread touches it
+      if (b.new_page[e] >= 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
+      continue;
+    }
+    const float xj = bf16f(rs[j]);
+    const float c = (kind ? p.clipV : p.clipK)[kv * D + j];
+    // (the branches above are block-uniform; the previous sequence's reads
+    // of xs and red ended before the barriers of its quantization)
+    xs[j] = xj;
+    rs[j] = xnew; // this thread read element j above; no other thread touches it
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc = fmaf(xs[i], rc[i], acc);
+    const float y = fminf(fmaxf(acc, -c), c);
+    uint16_t s16, z16;
+    const uint32_t code =
+        quantize_channel<D, G>(y, red, s16, z16, p.lut != 0, p.lut ? p.codebook[kind * Hkv + kv] : 0u);
+    if (b.new_page[e] >= 0 && kv == 0 && kind == 0 && j == 0) p.page_table[(size_t)seq * p.maxp + pg_idx] = page;
+    uint8_t *blk = p.pages + ((size_t)page * Hkv + kv) * p.block_bytes;
+    if (kind == 0) {
+      store_k_code<D>(blk, t, code);
+      store_params<D, G>(blk, kparam_off(D, G, t, j / G), s16, z16);
+    } else {
+      // a byte holds four tokens of channel j (those with equal k & 1 and
+      // k >> 3, k = t % 16); the first of them, k & 6 == 0, starts the byte
+      const int k = t % 16;
+      uint8_t *byte = blk + vcode_dword_off(D, t / 16, j) + vbit(k) / 8;
+      const int sh = vbit(k) % 8;
+      const uint32_t old = (k & 6) == 0 ? 0u : *byte;
+      *byte = (uint8_t)((old & ~(3u << sh)) | (code << sh));
+      store_params<D, G>(blk, vparam_off(D, G, t, j / G), s16, z16);
+    }
   }
 }
 
@@ -381,8 +392,10 @@ hipError_t prefill_impl(const PoolDev &p, int seq, const uint16_t *k, const uint
 template <int D, int G>
 hipError_t append_impl(const PoolDev &p, const AppendBatch &b, const uint16_t *kn, const uint16_t *vn,
                        hipStream_t s, const KernelTimer &t) {
+  // sequences per block: about 512 blocks (two per compute unit), at most 8
+  const int spb = std::max(1, std::min(8, b.n * p.Hkv * 2 / 512));
   if (t.on) (void)hipEventRecord(t.ev[0], s);
-  hipLaunchKernelGGL((append_kernel<D, G>), dim3(b.n, p.Hkv, 2), dim3(D), 0, s, p, b, kn, vn);
+  hipLaunchKernelGGL((append_kernel<D, G>), dim3((b.n + spb - 1) / spb, p.Hkv, 2), dim3(D), 0, s, p, b, kn, vn, spb);
   if (t.on) (void)hipEventRecord(t.ev[1], s);
   return hipGetLastError();
 }
