@@ -270,7 +270,7 @@ def prefill_main(args):
         "metric": "prefill attention tokens/s per layer (chunk over the three-segment pool)",
         "value": n_q / (ms * 1e-3), "unit": "tokens/s per layer", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int2 codes + fp16 scale/zero history, bf16 windows, int8/fp16 MFMA, fp32 accumulate",
+        "vs_baseline": None, "dtype": "int2 codes + fp16 scale/zero history, bf16 windows, fp16 (hi + lo) / bf16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded; K/V ~ N(0,1) with 4 outlier channels x20)",
         "config": {"workload": f"{w.name} prefill chunk", "prompt_len": L, "chunk": n_q, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "group_size": w.group_size,

@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liboscar.so")
-SOURCES = ["oscar_host.cpp", "kernels_encode.hip", "kernels_decode.hip", "kernels_bf16.hip", "kernels_calib.hip"]
+SOURCES = ["oscar_host.cpp", "kernels_encode.hip", "kernels_decode.hip", "kernels_bf16.hip", "kernels_calib.hip",
+           "kernels_prefill.hip"]
 ARCH = os.environ.get("OSCAR_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 instructions are disabled for all device code.

@@ -1,0 +1,696 @@
+// Prefill attention on matrix cores: many query rows of one kv head attend
+// over the three-segment pool.
+//
+// Method: news article on OSCAR (sanyangsrq.com), section "From offline
+// calibration to online inference": the INT2 history is unpacked,
+// dequantized with each token's scale and zero point and attended in the
+// rotated basis; the BF16 sink and recent tokens are attended in the basis
+// of the raw keys; an online softmax merges both.  The query rows of a call
+// are (query i, head of the kv head) pairs, flat index i g + hh (g query
+// heads per kv head); query i sits at position L - n_q + i and sees the
+// positions up to its own.
+//
+// Launches (one stream), for pools with d = 128 and one scale group per
+// token (G = 128), affine levels:
+//   prefill_qprep_kernel, one block per (tile of 128 rows, kv head): the
+//     rows' queries are rotated by R_K (v_mfma_f32_32x32x2f32), scaled by
+//     scale * log2(e) and 2^E (E per tile: |a| 2^E < 2^14) and split into
+//     fp16 hi + lo (~22 bits), laid out as the B operand of
+//     v_mfma_f32_32x32x16_f16 with the per-channel factors 4^-e that the K
+//     code operand's sub-normal pairs need; the row sums of a (the zero
+//     point term) go beside them.
+//   prefill_hist_kernel, one block per (tile, kv head, split of the tile's
+//     visible history pages), 4 waves of 32 rows, two blocks per compute
+//     unit: the block stages each page once in shared memory as MFMA
+//     operands (K and V codes as fp16 sub-normal pairs code 4^e 2^-24,
+//     per-token scale/zero terms in fp32); each wave computes
+//       S^T = K_codes . (Q_hi + Q_lo)^T        (fp16 MFMA, fp32 accumulate)
+//       logit = s_K 2^(24-E) S + z_K sum(a)   (log2 units, exact fp32 terms)
+//     runs a lazy online softmax (integer reference m, moved only when a
+//     logit exceeds it by more than 8) and accumulates
+//       O += P' V_codes,  P' = p s_V 2^pv_shift 4^-e  (fp16 hi + lo)
+//     on v_mfma_f32_32x32x16_f16, plus sum p z_V on the VALU.  The token
+//     order inside a 32-token tile is chosen so that the S^T accumulators
+//     of a lane are the P' operand of the same lane (no data movement).
+//     It writes the split's (m, l, O) in the rotated basis.
+//   prefill_finish_kernel, one block per (tile, kv head): merges the
+//     splits, de-rotates by R_V^T (v_mfma_f32_32x32x2f32), continues the
+//     online softmax over the sink and recent tokens with the raw queries
+//     (v_mfma_f32_32x32x16_bf16 for both products, P in bf16 hi + lo) and
+//     writes the normalised rows.
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;          // head dimension of this path
+constexpr int kRows = 128;       // flat rows per tile (4 waves x 32)
+constexpr int kWaves = 4;
+constexpr int kQBits = 14;       // |a| 2^E < 2^kQBits: fp16 hi/lo parts stay finite
+constexpr float kLazyPf = 8.f;   // log2 headroom of the lazy softmax reference
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Token (0..31) of a 32-token tile held in row m of an S^T accumulator: the
+// lanes of half h of the wave then hold tokens 16 h .. 16 h + 15, register v
+// holding token 16 h + v.
+__host__ __device__ inline int tile_token(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+// Row of the S^T accumulator (and A-operand lane) that holds token u.
+__host__ __device__ inline int token_row(int u) { return 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3); }
+
+// Tile geometry shared by the three kernels.
+struct TileInfo {
+  int f0, nrows;     // first flat row, real rows in the tile
+  int pos0, pos1;    // positions of its first and last query
+};
+__device__ __forceinline__ TileInfo tile_info(const PrefillArgs &a, int T) {
+  TileInfo t;
+  t.f0 = T * kRows;
+  const int rows = a.n_q * a.g;
+  t.nrows = min(kRows, rows - t.f0);
+  t.pos0 = a.L - a.n_q + t.f0 / a.g;
+  t.pos1 = a.L - a.n_q + (t.f0 + t.nrows - 1) / a.g;
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Query preparation.
+// ---------------------------------------------------------------------------
+struct QprepSmem {
+  float a[kWaves][32][kD + 1]; // rotated, scaled rows of each wave
+  uint32_t amax;               // tile maximum of |a| (bits of a non-negative float)
+};
+
+__global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillArgs a, const uint16_t *q,
+                                                            u32x4 *qrec, float *qaux) {
+  __shared__ QprepSmem sm;
+  const int T = blockIdx.x, kv = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const TileInfo ti = tile_info(a, T);
+  if (tid == 0) sm.amax = 0u;
+  // A operand of the rotation: row n of the wave, channels j = st + 64 h
+  const int fr = 32 * w + n; // row in the tile
+  const bool real = fr < ti.nrows;
+  const int f = ti.f0 + fr;
+  u32x4 qv[8];
+  if (real) {
+    const int i = f / a.g, head = kv * a.g + f % a.g;
+    const u32x4 *src = (const u32x4 *)(q + ((size_t)i * p.Hq + head) * kD + 64 * h);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[k] = src[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[k] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // x_rot[c] = sum_j x[j] R_K[j][c]: B operand R_K[st + 64 h][32 ct + n]
+  const float *R = p.RK + (size_t)kv * kD * kD;
+  v16f acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = v16f{};
+#pragma unroll 4
+  for (int st = 0; st < 64; ++st) {
+    const uint32_t wd = qv[st / 8][(st / 2) % 4];
+    const float x = bf16f((uint16_t)((st & 1) ? (wd >> 16) : (wd & 0xffffu)));
+    const float *rr = R + (size_t)(st + 64 * h) * kD + n;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, rr[32 * ct], acc[ct], 0, 0, 0);
+  }
+  // scale, tile maximum, transpose through shared memory
+  float mx = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float y = acc[ct][v] * a.qscale;
+      mx = fmaxf(mx, fabsf(y));
+      sm.a[w][8 * (v / 4) + 4 * h + v % 4][32 * ct + n] = y;
+    }
+  __syncthreads();
+  atomicMax(&sm.amax, __float_as_uint(mx)); // non-negative floats order as their bits
+  __syncthreads();
+  const float amax = __uint_as_float(sm.amax);
+  int ex = 0;
+  frexpf(amax, &ex);
+  const int E = amax > 0.f ? kQBits - ex : 0; // amax 2^E < 2^kQBits
+  // B operand of the QK^T MFMA for lane (row n, half h), k-step ks (the
+  // 16 channels 16 ks ..): element e = 2 j + x holds channel
+  // 16 ks + 8 x + 4 h + j times 4^-e(4 h + j), e(p) = p <= 4 ? p : p - 5, as
+  // fp16 hi and lo parts (the K operand holds code 4^e(p) 2^-24 there)
+  u32x4 *dst = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (8 * 2 * 64);
+  float part = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    v8h hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = e >> 1, pr = 4 * h + j, ef = pr <= 4 ? pr : pr - 5;
+      const float y = sm.a[w][n][16 * ks + 8 * (e & 1) + pr];
+      part += y;
+      const float ys = ldexpf(y, E - 2 * ef);
+      const _Float16 yh = (_Float16)ys;
+      hi[e] = yh;
+      lo[e] = (_Float16)(ys - (float)yh);
+    }
+    dst[(ks * 2 + 0) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
+    dst[(ks * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
+  }
+  // row sum of a over all channels (the two halves hold 64 each)
+  const float qsum = part + __shfl_xor(part, 32, 64);
+  float *aux = qaux + ((size_t)kv * a.NT + T) * (kRows + 1);
+  if (h == 0) aux[32 * w + n] = qsum;
+  if (tid == 0) aux[kRows] = ldexpf(1.f, 24 - E);
+}
+
+// ---------------------------------------------------------------------------
+// History pages.
+// ---------------------------------------------------------------------------
+// One page (64 tokens of one kv head) as MFMA operands.  The lane slot of
+// an operand is XOR-swizzled in bits 1-3 (a constant within each group of 16
+// lanes, so a wave's reads stay conflict-free): the staging writes of a wave,
+// which would otherwise put four lanes on each bank, spread over all banks.
+// K: lane ^ (2 ((lane >> 4) & 1) + 4 ((k-step >> 2) & 1));
+// V: lane ^ (4 (channel tile & 1) + 8 ((lane >> 4) & 1)).
+struct PageSlot {
+  u32x4 K[2][8][64];    // [tile][k-step][lane]: 8 fp16 K code values (A operand)
+  u32x4 V[4][2][2][64]; // [channel tile][tile][k-step][lane]: 8 fp16 V code values (B operand)
+  float par[4][64];     // per token: s_K 2^(24-E), z_K, s_V 2^pv_shift 4^-e, z_V
+};
+struct HistSmemPf {
+  PageSlot slot[2];
+  float row[kWaves][32]; // per-wave row broadcast (rescale factors, zero sums)
+};
+
+// Raw words of one page a thread stages: K and V code dwords tid and
+// tid + 256, and (threads < 128) one parameter dword.
+struct PageRaw {
+  uint32_t k0, k1, v0, v1, par;
+};
+
+__device__ __forceinline__ void load_raw(PageRaw &r, const uint8_t *blk, int tid) {
+  const uint32_t *w = (const uint32_t *)blk;
+  r.k0 = __builtin_nontemporal_load(w + tid);
+  r.k1 = __builtin_nontemporal_load(w + tid + 256);
+  r.v0 = __builtin_nontemporal_load(w + 512 + tid);
+  r.v1 = __builtin_nontemporal_load(w + 512 + tid + 256);
+  // K params at byte 32 d + 4 t, V params 256 bytes later (G = d)
+  r.par = tid < 128 ? __builtin_nontemporal_load(w + 1024 + tid) : 0u;
+}
+
+// K code dword i of the pool layout -> (token t, 16-channel group gi): its
+// channel pairs (p, p + 8) become fp16 sub-normal pairs code 4^e(p) 2^-24,
+// pairs 0..3 in the lanes of half 0 and 4..7 in half 1 of k-step gi.
+__device__ __forceinline__ void stage_k(PageSlot &s, int i, uint32_t wd) {
+  const int off = 4 * i;
+  const int ls = (off & 1023) >> 4;                 // lane of the share
+  const int b = 16 * (off >> 10) + (off & 15);      // byte of the lane's share
+  const int t = 4 * (ls & 15) + b / (kD / 16);      // token
+  const int gi = 4 * ((b % (kD / 16)) / 4) + (ls >> 4); // channels 16 gi .. 16 gi + 15
+  const uint32_t w2 = wd >> 10;
+  const int row = token_row(t & 31);
+  const int kz = 2 * ((row >> 4) & 1) + 4 * ((gi >> 2) & 1);
+  s.K[t >> 5][gi][row ^ kz] = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
+  s.K[t >> 5][gi][(row + 32) ^ kz] = u32x4{wd & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
+}
+
+// V code dword i -> (channel c, 16-token block r); tokens 8 ks .. 8 ks + 7
+// of the block become k-step ks of the B operand (token pairs as fp16
+// sub-normals code 4^e 2^-24, e from the pair index).
+__device__ __forceinline__ void stage_v(PageSlot &s, int i, uint32_t wd) {
+  const int off = 4 * i;
+  const int ls = (off & 1023) >> 4;
+  const int b = 16 * (off >> 10) + (off & 15);
+  const int r = ls >> 4, c = 16 * (b / 4) + (ls & 15);
+  const int lane0 = (c & 31) + 32 * (r & 1);
+  const int lane = lane0 ^ (4 * ((c >> 5) & 1) + 8 * ((lane0 >> 4) & 1));
+  const uint32_t w2 = wd >> 10;
+  s.V[c >> 5][r >> 1][0][lane] = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
+  s.V[c >> 5][r >> 1][1][lane] = u32x4{wd & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
+}
+
+__device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu)); }
+__device__ __forceinline__ float f16hi(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16)); }
+
+__device__ __forceinline__ void stage_page(PageSlot &s, const PageRaw &r, int tid, int ntok, float kscale,
+                                           float vscale) {
+  stage_k(s, tid, r.k0);
+  stage_k(s, tid + 256, r.k1);
+  stage_v(s, tid, r.v0);
+  stage_v(s, tid + 256, r.v1);
+  if (tid < 64) {
+    // tokens past the history hold no data: their terms are zero
+    const bool ok = tid < ntok;
+    s.par[0][tid] = ok ? f16lo(r.par) * kscale : 0.f;
+    s.par[1][tid] = ok ? f16hi(r.par) : 0.f;
+  } else if (tid < 128) {
+    const int t = tid - 64, pr = (t & 15) >> 1, e = pr <= 4 ? pr : pr - 5;
+    const bool ok = t < ntok;
+    s.par[2][t] = ok ? f16lo(r.par) * ldexpf(vscale, -2 * e) : 0.f;
+    s.par[3][t] = ok ? f16hi(r.par) : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, PrefillArgs a, const u32x4 *qrec,
+                                                              const float *qaux, float *part_o, float *part_ml) {
+  __shared__ HistSmemPf sm;
+  const int kv = blockIdx.y;
+  const int T = a.NT - 1 - (int)blockIdx.x / a.S, s = (int)blockIdx.x % a.S; // later tiles (more pages) first
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const TileInfo ti = tile_info(a, T);
+  const int n_hist = a.n_hist;
+  const int vis_last = prefill_visible_hist(ti.pos1, n_hist);
+  const int pe = (vis_last + kPage - 1) / kPage;               // pages some row sees
+  const int fv = prefill_visible_hist(ti.pos0, n_hist) / kPage; // pages every row sees whole
+  const int p0 = (int)((long)s * pe / a.S), p1 = (int)((long)(s + 1) * pe / a.S);
+
+  // this lane's row (S^T column n)
+  const int fr = 32 * w + n;
+  const bool real = fr < ti.nrows;
+  const int vis = real ? prefill_visible_hist(a.L - a.n_q + (ti.f0 + fr) / a.g, n_hist) : 0;
+  const float *aux = qaux + ((size_t)kv * a.NT + T) * (kRows + 1);
+  const float qsum = aux[fr];
+  const float kscale = aux[kRows]; // 2^(24 - E)
+  const float vscale = ldexpf(1.f, p.pv_shift);
+  v8h Qh[8], Ql[8];
+  {
+    const u32x4 *src = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (8 * 2 * 64);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      Qh[ks] = __builtin_bit_cast(v8h, src[(ks * 2 + 0) * 64 + lane]);
+      Ql[ks] = __builtin_bit_cast(v8h, src[(ks * 2 + 1) * 64 + lane]);
+    }
+  }
+  float m = -INFINITY, negm = INFINITY, lsum = 0.f, zsum = 0.f;
+  v16f O[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) O[ct] = v16f{};
+
+  const int32_t *ptab = p.page_table + (size_t)a.seq * p.maxp;
+  const size_t hstride = (size_t)p.Hkv * p.block_bytes, hoff = (size_t)kv * p.block_bytes;
+  auto page_ptr = [&](int pi) { return p.pages + (size_t)ptab[pi] * hstride + hoff; };
+  auto ntok_of = [&](int pi) { return min(kPage, n_hist - pi * kPage); };
+
+  PageRaw ra, rb;
+  if (p0 < p1) {
+    load_raw(ra, page_ptr(p0), tid);
+    if (p0 + 1 < p1) load_raw(rb, page_ptr(p0 + 1), tid);
+    stage_page(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale);
+  }
+  __syncthreads();
+
+  // One page: nxt holds the raw words of page pi + 1 (loaded one step
+  // earlier), fut receives the loads of page pi + 2.  The page's operands
+  // are in slot (pi - p0) & 1; page pi + 1 is staged into the other slot
+  // after the compute, and one barrier ends the step.
+  auto step = [&](int pi, const PageRaw &nxt, PageRaw &fut) __attribute__((always_inline)) {
+    const int sl = (pi - p0) & 1;
+    if (pi + 2 < p1) load_raw(fut, page_ptr(pi + 2), tid);
+    const PageSlot &S = sm.slot[sl];
+    const bool masked = pi >= fv;
+    const int tbase = pi * kPage;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      // ---- S^T = K codes . (Q_hi + Q_lo)^T
+      v16f acc = v16f{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const v8h A = __builtin_bit_cast(v8h, S.K[tt][ks][lane ^ (2 * ((lane >> 4) & 1) + 4 * ((ks >> 2) & 1))]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Qh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Ql[ks], acc, 0, 0, 0);
+      }
+      // ---- logits (log2 units) of tokens 16 h + v of the tile
+      float x[16];
+      const int tok0 = 32 * tt + 16 * h; // token (in the page) of register 0
+      float mxl = -INFINITY;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const v4f sk = *(const v4f *)&S.par[0][tok0 + 4 * J];
+        const v4f zk = *(const v4f *)&S.par[1][tok0 + 4 * J];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * J + i;
+          float xv = fmaf(sk[i], acc[v], fmaf(zk[i], qsum, negm));
+          if (masked) xv = tbase + tok0 + v < vis ? xv : -INFINITY;
+          x[v] = xv;
+          mxl = fmaxf(mxl, xv);
+        }
+      }
+      // ---- lazy reference: moves (to an integer) only when a logit
+      // exceeds it by more than kLazyPf; rows are lanes n and n + 32
+      if (__any(mxl > kLazyPf)) {
+        float lg = -INFINITY;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const v4f sk = *(const v4f *)&S.par[0][tok0 + 4 * J];
+          const v4f zk = *(const v4f *)&S.par[1][tok0 + 4 * J];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = 4 * J + i;
+            const float lv = fmaf(sk[i], acc[v], zk[i] * qsum);
+            const bool ok = !masked || tbase + tok0 + v < vis;
+            lg = ok ? fmaxf(lg, lv) : lg;
+          }
+        }
+        lg = fmaxf(lg, __shfl_xor(lg, 32, 64));
+        const bool jump = lg > m + kLazyPf;
+        const float mn = jump ? ceilf(lg) : m;
+        const float alpha = jump ? exp2f(m - mn) : 1.f; // m = -inf: 0
+        m = mn;
+        negm = -mn;
+        lsum *= alpha;
+        zsum *= alpha;
+        if (n == lane) sm.row[w][n] = alpha; // lanes 0..31 (both halves agree)
+        wave_sync();
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const v4f al = *(const v4f *)&sm.row[w][8 * J + 4 * h];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= al[i];
+        }
+        wave_sync();
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const v4f sk = *(const v4f *)&S.par[0][tok0 + 4 * J];
+          const v4f zk = *(const v4f *)&S.par[1][tok0 + 4 * J];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = 4 * J + i;
+            const float xv = fmaf(sk[i], acc[v], fmaf(zk[i], qsum, negm));
+            x[v] = (!masked || tbase + tok0 + v < vis) ? xv : -INFINITY;
+          }
+        }
+      }
+      // ---- weights, sums, P' (fp16 hi + lo) and PV
+      float pp[16];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const v4f sp = *(const v4f *)&S.par[2][tok0 + 4 * J];
+        const v4f zv = *(const v4f *)&S.par[3][tok0 + 4 * J];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * J + i;
+          const float pv = __builtin_amdgcn_exp2f(x[v]);
+          lsum += pv;
+          zsum = fmaf(pv, zv[i], zsum);
+          pp[v] = pv * sp[i];
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v8h hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = pp[8 * ks + e];
+          const _Float16 yh = (_Float16)y;
+          hi[e] = yh;
+          lo[e] = (_Float16)(y - (float)yh);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const v8h B = __builtin_bit_cast(v8h, S.V[ct][tt][ks][lane ^ (4 * (ct & 1) + 8 * ((lane >> 4) & 1))]);
+          O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, B, O[ct], 0, 0, 0);
+          O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, B, O[ct], 0, 0, 0);
+        }
+      }
+    }
+    if (pi + 1 < p1) stage_page(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale);
+    __syncthreads();
+  };
+  for (int pi = p0; pi < p1; pi += 2) {
+    step(pi, rb, ra);
+    if (pi + 1 < p1) step(pi + 1, ra, rb);
+  }
+
+  // ---- epilogue: (m, l) per row; O in the rotated basis, true units:
+  // O 2^(24 - pv_shift) + sum_t p_t z_V(t)
+  const float lrow = lsum + __shfl_xor(lsum, 32, 64);
+  const float zrow = zsum + __shfl_xor(zsum, 32, 64);
+  if (lane < 32) sm.row[w][n] = zrow;
+  wave_sync();
+  const size_t base = (((size_t)kv * a.NT + T) * a.S + s) * kRows + 32 * w;
+  const float k24 = ldexpf(1.f, 24 - p.pv_shift);
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    const v4f zr = *(const v4f *)&sm.row[w][8 * J + 4 * h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 8 * J + 4 * h + i;
+      float *dst = part_o + (base + rr) * kD + n;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) dst[32 * ct] = fmaf(O[ct][4 * J + i], k24, zr[i]);
+    }
+  }
+  if (lane < 32) {
+    part_ml[(base + n) * 2] = m;
+    part_ml[(base + n) * 2 + 1] = lrow;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge, de-rotation and the BF16 window.
+// ---------------------------------------------------------------------------
+struct FinishSmem {
+  u32x4 V[2][4][2][64]; // [buffer][channel tile][k-step][lane]: 8 bf16 window V values
+  float row[kWaves][32];
+};
+
+__global__ __launch_bounds__(256) void prefill_finish_kernel(PoolDev p, PrefillArgs a, const uint16_t *q,
+                                                             const float *part_o, const float *part_ml, float *out) {
+  __shared__ FinishSmem sm;
+  const int T = blockIdx.x, kv = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const TileInfo ti = tile_info(a, T);
+  const int fr = 32 * w + n;
+  const bool real = fr < ti.nrows;
+  const int f = ti.f0 + fr;
+  const int qi = real ? f / a.g : 0, head = kv * a.g + (real ? f % a.g : 0);
+  const int rowpos = real ? a.L - a.n_q + qi : -1;
+
+  // ---- merge the splits of this lane's row: reference, weights, l
+  const size_t base = ((size_t)kv * a.NT + T) * a.S * kRows + fr;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, part_ml[(base + (size_t)s * kRows) * 2]);
+  float L = 0.f;
+  // A operand of the de-rotation: O_rot[row][j], j = st + 64 h; the lane
+  // keeps its 64 merged values
+  float orot[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) orot[j] = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const float ms = part_ml[(base + (size_t)s * kRows) * 2];
+    const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    L = fmaf(ws, part_ml[(base + (size_t)s * kRows) * 2 + 1], L);
+    if (ws != 0.f) {
+      const v4f *src = (const v4f *)(part_o + (base + (size_t)s * kRows) * kD + 64 * h);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const v4f v4 = src[k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orot[4 * k + i] = fmaf(ws, v4[i], orot[4 * k + i]);
+      }
+    }
+  }
+  // ---- de-rotation: out[c] = sum_j O_rot[j] R_V^T[j][c]
+  const float *RVt = p.RVt + (size_t)kv * kD * kD;
+  v16f O[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) O[ct] = v16f{};
+#pragma unroll
+  for (int st = 0; st < 64; ++st) {
+    const float *rr = RVt + (size_t)(st + 64 * h) * kD + n;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) O[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(orot[st], rr[32 * ct], O[ct], 0, 0, 0);
+  }
+
+  // ---- window: sink and recent tokens, raw queries, bf16 MFMAs
+  const int seq = a.seq;
+  const int n_sink = min(a.L, kSink), n_rec = min(max(a.L - kSink, 0), kRecent), n_win = n_sink + n_rec;
+  const int n_hist = a.n_hist;
+  const uint16_t *sinkK = p.sinkK + ((size_t)seq * p.Hkv + kv) * kSink * kD;
+  const uint16_t *sinkV = p.sinkV + ((size_t)seq * p.Hkv + kv) * kSink * kD;
+  const uint16_t *recK = p.recentK + ((size_t)seq * p.Hkv + kv) * kRecent * kD;
+  const uint16_t *recV = p.recentV + ((size_t)seq * p.Hkv + kv) * kRecent * kD;
+  auto krow = [&](int u) { return u < n_sink ? sinkK + (size_t)u * kD : recK + (size_t)(u - n_sink) * kD; };
+  auto vrow = [&](int u) { return u < n_sink ? sinkV + (size_t)u * kD : recV + (size_t)(u - n_sink) * kD; };
+  // position of window token u (recent slot j holds 64 + n_hist + ((j - n_hist) mod 256))
+  auto upos = [&](int u) { return u < n_sink ? u : kSink + n_hist + ((u - n_sink - n_hist) & (kRecent - 1)); };
+  // B operand: raw query row n, channels 16 ks + 8 h .. + 7
+  v8bf Qw[8];
+  {
+    const u32x4 *src = (const u32x4 *)(q + ((size_t)qi * p.Hq + head) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      Qw[ks] = __builtin_bit_cast(v8bf, real ? src[2 * ks + h] : u32x4{0u, 0u, 0u, 0u});
+  }
+  // online state continues from the merged history (reference M); the
+  // row's l is the sum over its two lanes, so the history's L enters once
+  float m = M, negm = -M, lsum = h == 0 ? L : 0.f;
+  const int nchunk = (n_win + 31) / 32;
+  // stage chunk c's V rows into buffer c & 1 (transposed to the B operand)
+  auto stage = [&](int c) {
+    const int tk = tid >> 3, cb = tid & 7; // token of the chunk, 16-channel block
+    const int u = 32 * c + tk;
+    u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = v0;
+    if (u < n_win) {
+      const u32x4 *src = (const u32x4 *)(vrow(u) + 16 * cb);
+      v0 = src[0];
+      v1 = src[1];
+    }
+    const int hh = tk >> 4, ks = (tk & 15) >> 3, e = tk & 7;
+    uint16_t *V = (uint16_t *)&sm.V[c & 1][0][0][0];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t wd = k < 8 ? v0[k / 2] : v1[(k - 8) / 2];
+      const uint16_t val = (uint16_t)((k & 1) ? (wd >> 16) : (wd & 0xffffu));
+      const int c2 = 16 * cb + k;
+      V[(((c2 >> 5) * 2 + ks) * 64 + (c2 & 31) + 32 * hh) * 8 + e] = val;
+    }
+  };
+  if (nchunk > 0) stage(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    if (c + 1 < nchunk) stage(c + 1);
+    // S^T = K_win . q^T: A operand token tile_token(n) of the chunk
+    v16f S = v16f{};
+    {
+      const int u = 32 * c + tile_token(n);
+      const bool ok = u < n_win;
+      const u32x4 *src = (const u32x4 *)(ok ? krow(u) : sinkK);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const v8bf A = __builtin_bit_cast(v8bf, ok ? src[2 * ks + h] : u32x4{0u, 0u, 0u, 0u});
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Qw[ks], S, 0, 0, 0);
+      }
+    }
+    float x[16], mxl = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int u = 32 * c + 16 * h + v;
+      const bool ok = u < n_win && upos(u) <= rowpos;
+      x[v] = ok ? fmaf(S[v], a.qscale, negm) : -INFINITY;
+      mxl = fmaxf(mxl, x[v]);
+    }
+    if (__any(mxl > kLazyPf)) {
+      float lg = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int u = 32 * c + 16 * h + v;
+        const bool ok = u < n_win && upos(u) <= rowpos;
+        lg = ok ? fmaxf(lg, S[v] * a.qscale) : lg;
+      }
+      lg = fmaxf(lg, __shfl_xor(lg, 32, 64));
+      const bool jump = lg > m + kLazyPf;
+      const float mn = jump ? ceilf(lg) : m;
+      const float alpha = jump ? exp2f(m - mn) : 1.f;
+      m = mn;
+      negm = -mn;
+      lsum *= alpha;
+      if (n == lane) sm.row[w][n] = alpha;
+      wave_sync();
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const v4f al = *(const v4f *)&sm.row[w][8 * J + 4 * h];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= al[i];
+      }
+      wave_sync();
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int u = 32 * c + 16 * h + v;
+        const bool ok = u < n_win && upos(u) <= rowpos;
+        x[v] = ok ? fmaf(S[v], a.qscale, negm) : -INFINITY;
+      }
+    }
+    float pp[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      pp[v] = __builtin_amdgcn_exp2f(x[v]);
+      lsum += pp[v];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v8bf hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = pp[8 * ks + e];
+        const __bf16 yh = (__bf16)y;
+        hi[e] = yh;
+        lo[e] = (__bf16)(y - (float)yh);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const v8bf B = __builtin_bit_cast(v8bf, sm.V[c & 1][ct][ks][lane]);
+        O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, B, O[ct], 0, 0, 0);
+        O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, B, O[ct], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // ---- normalise and store: register (J, i) holds row 8 J + 4 h + i,
+  // channel 32 ct + n; the history part was weighted relative to M, the
+  // window relative to m >= M (rescales by alpha applied to both)
+  const float lrow = lsum + __shfl_xor(lsum, 32, 64);
+  if (lane < 32) sm.row[w][n] = lrow > 0.f ? 1.f / lrow : 0.f;
+  wave_sync();
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    const v4f il = *(const v4f *)&sm.row[w][8 * J + 4 * h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 8 * J + 4 * h + i;
+      const int fo = ti.f0 + 32 * w + rr;
+      if (32 * w + rr < ti.nrows) {
+        float *dst = out + ((size_t)(fo / a.g) * p.Hq + kv * a.g + fo % a.g) * kD + n;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) dst[32 * ct] = O[ct][4 * J + i] * il[i];
+      }
+    }
+  }
+}
+
+} // namespace
+
+size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S) {
+  const size_t qrec = (size_t)Hkv * NT * kWaves * 8 * 2 * 64 * 16;
+  const size_t qaux = (size_t)Hkv * NT * (kRows + 1) * 4;
+  const size_t po = (size_t)Hkv * NT * S * kRows * kD * 4;
+  const size_t pml = (size_t)Hkv * NT * S * kRows * 2 * 4;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  return al(qrec) + al(qaux) + al(po) + al(pml);
+}
+
+bool prefill_mfma_supported(const PoolDev &p) { return p.d == kD && p.G == kD && !p.lut && !p.bf16_hist; }
+
+hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, void *ws,
+                               hipStream_t s) {
+  if (!prefill_mfma_supported(p) || a.NT < 1 || a.S < 1) return hipErrorInvalidValue;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  uint8_t *base = (uint8_t *)ws;
+  u32x4 *qrec = (u32x4 *)base;
+  base += al((size_t)p.Hkv * a.NT * kWaves * 8 * 2 * 64 * 16);
+  float *qaux = (float *)base;
+  base += al((size_t)p.Hkv * a.NT * (kRows + 1) * 4);
+  float *po = (float *)base;
+  base += al((size_t)p.Hkv * a.NT * a.S * kRows * kD * 4);
+  float *pml = (float *)base;
+  hipLaunchKernelGGL(prefill_qprep_kernel, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
+  hipLaunchKernelGGL(prefill_hist_kernel, dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po, pml);
+  hipLaunchKernelGGL(prefill_finish_kernel, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, po, pml, out);
+  return hipGetLastError();
+}
+
+} // namespace oscar

@@ -790,13 +790,27 @@ int oscar_pool_check(oscar_pool *p, void *stream) {
   return rc ? rc : ok();
 }
 
+// Pools whose prefill attention runs on the matrix-core path (the same test
+// as prefill_mfma_supported, from the configuration).
+static bool prefill_mfma_config(const oscar_pool_config *c) {
+  return c->head_dim == 128 && c->group_size == 128 && !(c->flags & OSCAR_POOL_LLOYD_MAX) &&
+         !(c->flags & OSCAR_POOL_BF16_HISTORY);
+}
+
 int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, size_t *bytes) {
   int rc = validate_config(cfg);
   if (rc) return rc;
   if (!bytes || n_q < 0) return fail(OSCAR_EINVAL, "bad arguments");
   const int Hkv = cfg->num_kv_heads, g = cfg->num_q_heads / Hkv, vg = kPrefillTile;
-  const int tiles = (int)std::min<int64_t>(((int64_t)n_q * g + vg - 1) / vg, kMaxBatch);
-  *bytes = decode_ws_floats(Hkv * vg, cfg->head_dim, tiles, Hkv, kMaxSplits, vg) * sizeof(float);
+  size_t need;
+  if (prefill_mfma_config(cfg)) {
+    const int NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
+    need = prefill_mfma_ws_bytes(Hkv, NT, prefill_mfma_splits(NT, Hkv));
+  } else {
+    const int tiles = (int)std::min<int64_t>(((int64_t)n_q * g + vg - 1) / vg, kMaxBatch);
+    need = decode_ws_floats(Hkv * vg, cfg->head_dim, tiles, Hkv, kMaxSplits, vg) * sizeof(float);
+  }
+  *bytes = need;
   return ok();
 }
 
@@ -812,6 +826,24 @@ int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *
   if (!q || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
   if (!std::isfinite(softmax_scale)) return fail(OSCAR_EINVAL, "softmax_scale is not finite");
   const int Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim, g = p->cfg.num_q_heads / Hkv;
+  if (prefill_mfma_supported(p->dev)) {
+    // matrix-core path: tiles of kPfTileRows rows, S splits each
+    PrefillArgs a;
+    a.seq = seq;
+    a.L = L;
+    a.n_q = n_q;
+    a.g = g;
+    a.n_hist = std::max(0, L - kWindow);
+    a.NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
+    a.S = prefill_mfma_splits(a.NT, Hkv);
+    a.qscale = softmax_scale * 1.4426950408889634f;
+    const size_t need = prefill_mfma_ws_bytes(Hkv, a.NT, a.S);
+    if (workspace_bytes < need)
+      return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+    hipError_t e = launch_prefill_mfma(p->dev, a, q, out, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+    return ok();
+  }
   const int vg = kPrefillTile;
   const int64_t rows = (int64_t)n_q * g;
   const int tiles = (int)((rows + vg - 1) / vg);

@@ -265,6 +265,27 @@ hipError_t launch_prefill_attn(const PoolDev &p_virtual, const DecodeBatch &b, c
 // Rows (query, head) of a prefill tile.
 constexpr int kPrefillTile = 8;
 
+// Prefill attention on matrix cores (pools with d = 128, one scale group per
+// token, affine levels): the call's flat rows (query i, head hh of the kv
+// head; index i g + hh) are cut in tiles of kPfTileRows, and each tile's
+// visible history pages in S splits.
+constexpr int kPfTileRows = 128;
+struct PrefillArgs {
+  int32_t seq, L, n_q, g, n_hist;
+  int32_t NT, S;   // tiles per kv head, splits per tile
+  float qscale;    // softmax scale * log2(e)
+};
+// Splits per tile: about 512 blocks per launch (two per compute unit), at
+// most 16 splits.
+inline int prefill_mfma_splits(int NT, int Hkv) {
+  const int blocks = NT * Hkv, want = (512 + blocks - 1) / blocks;
+  return want < 1 ? 1 : (want > 16 ? 16 : want);
+}
+bool prefill_mfma_supported(const PoolDev &p);
+size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S);
+hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, void *ws,
+                               hipStream_t s);
+
 // k_new, v_new: the appended tokens of a fused step (b.fused), else null.
 hipError_t launch_decode(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out,
                          float scale, float *ws, const uint16_t *k_new, const uint16_t *v_new, hipStream_t s,

@@ -24,7 +24,7 @@ $CLANG $SAN -shared-libsan -fno-fast-math -ffp-contract=off -mfma -fPIC -shared 
 HFLAGS="-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -Xarch_host -fno-sanitize-recover=undefined"
 DEV="-O1 -g -std=c++17 -fPIC --offload-arch=gfx950 -Xclang -target-feature -Xclang -packed-fp32-ops -I $WORK/include"
 mkdir -p "$WORK/_san"
-for src in oscar_host.cpp kernels_encode.hip kernels_decode.hip kernels_bf16.hip kernels_calib.hip; do
+for src in oscar_host.cpp kernels_encode.hip kernels_decode.hip kernels_bf16.hip kernels_calib.hip kernels_prefill.hip; do
   $HIPCC -x hip $DEV $HFLAGS -shared-libsan -c "$WORK/bit_kv_cache_segment_amd/csrc/$src" -o "$WORK/_san/$src.o" 2>&1 \
     | grep -v "packed-fp32-ops" || true
 done

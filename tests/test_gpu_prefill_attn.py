@@ -4,8 +4,9 @@ decoded pool: every query row within 2e-3 (row-relative).  Cases: a whole
 prompt (queries in the sink, the history and the recent window), a chunk
 longer than the recent window appended to a prefilled sequence (its first
 queries' own positions are already in the INT2 history), small chunks,
-n_q = 1 against decode attention, and a long context whose tiles are cut
-into several splits."""
+n_q = 1 against decode attention, a long context whose tiles are cut
+into several splits, and the benchmark's full-size chunk (two query heads
+checked, every query)."""
 import math
 
 import numpy as np
@@ -102,6 +103,29 @@ def test_long_context_chunk_with_split_plans(shape):
     pool = ok.Pool(cfg, RK, RV, cK, cV, max_batch=1)
     harness.prefill_all(pool, w, [L])
     _check(pool, w, 0, L, n_q, 5)
+
+
+def test_bench_chunk_full_size_sampled_heads():
+    # the prefill benchmark's launch: the last 2048 queries of a 32,768-token
+    # prompt, 32 query / 8 kv heads (d 128, G 128); query heads 0 and 31 (kv
+    # heads 0 and 7) of every query against the oracle
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    L, n_q = 32768, 2048
+    RK, RV, cK, cV = harness.tables(w)
+    cfg = harness.config_for(w, [L])
+    pool = ok.Pool(cfg, RK, RV, cK, cV, max_batch=1)
+    harness.prefill_all(pool, w, [L])
+    q = synth.queries(w, 0, batch=n_q)
+    got = pool.prefill_attn(0, q.to("cuda").view(torch.uint16).contiguous())
+    torch.cuda.synchronize()
+    g = w.num_q_heads // w.num_kv_heads
+    heads = [0, w.num_q_heads - 1]
+    st, _, _ = oracle_sequence(w, 0, L, heads=sorted({h // g for h in heads}))
+    ref = oracle.prefill_attention(st, synth.bf16_bits(q), 1 / math.sqrt(w.head_dim), heads=heads)
+    out = got.double().cpu().numpy()
+    for h in heads:
+        err = oracle.row_rel_err(out[:, h], ref[:, h])
+        assert err <= TOL, (h, err)
 
 
 def test_prefill_attn_rejects_bad_arguments():
