@@ -84,10 +84,36 @@ __device__ __forceinline__ TileInfo tile_info(const PrefillArgs &a, int T) {
   return t;
 }
 
+
+// A d x d fp32 rotation R (row j, column c) as the B operands of
+// v_mfma_f32_32x32x16_f16 contractions x . R over j, in shared memory:
+// k-step kk, lane (column 32 ct + l % 32, half h = l / 32) holds rows
+// 64 h + 8 kk + e, e = 0..7, split into fp16 hi and lo parts (~22 bits).
+struct RotB {
+  u32x4 b[8][4][2][64]; // [k-step][column tile][hi, lo][lane]  (64 KB)
+};
+__device__ __forceinline__ void stage_rot(RotB &rb, const float *R, int tid) {
+  const int lane = tid & 63, ct = tid >> 6, n = lane & 31, h = lane >> 5;
+#pragma unroll 2
+  for (int kk = 0; kk < 8; ++kk) {
+    v8h hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = R[(size_t)(64 * h + 8 * kk + e) * kD + 32 * ct + n];
+      const _Float16 yh = (_Float16)y;
+      hi[e] = yh;
+      lo[e] = (_Float16)(y - (float)yh);
+    }
+    rb.b[kk][ct][0][lane] = __builtin_bit_cast(u32x4, hi);
+    rb.b[kk][ct][1][lane] = __builtin_bit_cast(u32x4, lo);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Query preparation.
 // ---------------------------------------------------------------------------
 struct QprepSmem {
+  RotB rot;                    // R_K as B operands
   float a[kWaves][32][kD + 1]; // rotated, scaled rows of each wave
   uint32_t amax;               // tile maximum of |a| (bits of a non-negative float)
 };
@@ -113,18 +139,26 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
 #pragma unroll
     for (int k = 0; k < 8; ++k) qv[k] = u32x4{0u, 0u, 0u, 0u};
   }
-  // x_rot[c] = sum_j x[j] R_K[j][c]: B operand R_K[st + 64 h][32 ct + n]
-  const float *R = p.RK + (size_t)kv * kD * kD;
+  // x_rot[c] = sum_j x[j] R_K[j][c]: the query row (bf16, exact in fp16)
+  // times R_K's hi and lo parts; k-step kk holds channels 64 h + 8 kk + e
+  stage_rot(sm.rot, p.RK + (size_t)kv * kD * kD, tid);
+  __syncthreads();
   v16f acc[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) acc[ct] = v16f{};
-#pragma unroll 4
-  for (int st = 0; st < 64; ++st) {
-    const uint32_t wd = qv[st / 8][(st / 2) % 4];
-    const float x = bf16f((uint16_t)((st & 1) ? (wd >> 16) : (wd & 0xffffu)));
-    const float *rr = R + (size_t)(st + 64 * h) * kD + n;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, rr[32 * ct], acc[ct], 0, 0, 0);
+  for (int kk = 0; kk < 8; ++kk) {
+    v8h A;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wd = qv[kk][e / 2];
+      A[e] = (_Float16)bf16f((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu)));
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(v8h, sm.rot.b[kk][ct][0][lane]), acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(v8h, sm.rot.b[kk][ct][1][lane]), acc[ct], 0, 0, 0);
+    }
   }
   // scale, tile maximum, transpose through shared memory
   float mx = 0.f;
@@ -320,6 +354,15 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
     const int tbase = pi * kPage;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      const int tok0 = 32 * tt + 16 * h; // token (in the page) of register 0
+      // the logits' per-token terms, read before the QK^T chain so that
+      // their shared-memory latency overlaps it
+      v4f skp[4], zkp[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        skp[J] = *(const v4f *)&S.par[0][tok0 + 4 * J];
+        zkp[J] = *(const v4f *)&S.par[1][tok0 + 4 * J];
+      }
       // ---- S^T = K codes . (Q_hi + Q_lo)^T
       v16f acc = v16f{};
 #pragma unroll
@@ -330,12 +373,11 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
       }
       // ---- logits (log2 units) of tokens 16 h + v of the tile
       float x[16];
-      const int tok0 = 32 * tt + 16 * h; // token (in the page) of register 0
       float mxl = -INFINITY;
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        const v4f sk = *(const v4f *)&S.par[0][tok0 + 4 * J];
-        const v4f zk = *(const v4f *)&S.par[1][tok0 + 4 * J];
+        const v4f sk = skp[J];
+        const v4f zk = zkp[J];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v = 4 * J + i;
@@ -462,6 +504,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
 // Merge, de-rotation and the BF16 window.
 // ---------------------------------------------------------------------------
 struct FinishSmem {
+  RotB rot;             // R_V^T as B operands
   u32x4 V[2][4][2][64]; // [buffer][channel tile][k-step][lane]: 8 bf16 window V values
   float row[kWaves][32];
 };
@@ -478,6 +521,7 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PoolDev p, PrefillA
   const int qi = real ? f / a.g : 0, head = kv * a.g + (real ? f % a.g : 0);
   const int rowpos = real ? a.L - a.n_q + qi : -1;
 
+  stage_rot(sm.rot, p.RVt + (size_t)kv * kD * kD, tid);
   // ---- merge the splits of this lane's row: reference, weights, l
   const size_t base = ((size_t)kv * a.NT + T) * a.S * kRows + fr;
   float M = -INFINITY;
@@ -502,17 +546,48 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PoolDev p, PrefillA
       }
     }
   }
-  // ---- de-rotation: out[c] = sum_j O_rot[j] R_V^T[j][c]
-  const float *RVt = p.RVt + (size_t)kv * kD * kD;
+  __syncthreads(); // R_V^T staged
+  // ---- de-rotation: out[c] = sum_j O_rot[j] R_V^T[j][c].  The row is
+  // scaled by 2^-e (|O_rot| / L stays below the largest V value, so the
+  // scaled row fits fp16), split into fp16 hi + lo, and multiplied by R_V^T's
+  // hi and lo parts (three products; lo x lo is below fp32 rounding); the
+  // result is scaled back by 2^e, both exactly.
+  int ex = 0;
+  frexpf(L, &ex);
+  const float sdown = L > 0.f ? ldexpf(1.f, -ex) : 0.f;
+  if (lane < 32) sm.row[w][n] = L > 0.f ? ldexpf(1.f, ex) : 0.f;
   v16f O[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) O[ct] = v16f{};
 #pragma unroll
-  for (int st = 0; st < 64; ++st) {
-    const float *rr = RVt + (size_t)(st + 64 * h) * kD + n;
+  for (int kk = 0; kk < 8; ++kk) {
+    v8h Ah, Al;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) O[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(orot[st], rr[32 * ct], O[ct], 0, 0, 0);
+    for (int e = 0; e < 8; ++e) {
+      const float y = orot[8 * kk + e] * sdown;
+      const _Float16 yh = (_Float16)y;
+      Ah[e] = yh;
+      Al[e] = (_Float16)(y - (float)yh);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const v8h Bh = __builtin_bit_cast(v8h, sm.rot.b[kk][ct][0][lane]);
+      const v8h Bl = __builtin_bit_cast(v8h, sm.rot.b[kk][ct][1][lane]);
+      O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, Bh, O[ct], 0, 0, 0);
+      O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, Bl, O[ct], 0, 0, 0);
+      O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, Bh, O[ct], 0, 0, 0);
+    }
   }
+  wave_sync();
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    const v4f up = *(const v4f *)&sm.row[w][8 * J + 4 * h];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= up[i];
+  }
+  wave_sync();
 
   // ---- window: sink and recent tokens, raw queries, bf16 MFMAs
   const int seq = a.seq;
