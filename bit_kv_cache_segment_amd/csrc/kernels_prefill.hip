@@ -504,12 +504,14 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
 // Merge, de-rotation and the BF16 window.
 // ---------------------------------------------------------------------------
 struct FinishSmem {
-  RotB rot;             // R_V^T as B operands
-  u32x4 V[2][4][2][64]; // [buffer][channel tile][k-step][lane]: 8 bf16 window V values
+  union {
+    RotB rot;             // R_V^T as B operands (de-rotation)
+    u32x4 V[2][4][2][64]; // then: [buffer][channel tile][k-step][lane], 8 bf16 window V values
+  };
   float row[kWaves][32];
 };
 
-__global__ __launch_bounds__(256) void prefill_finish_kernel(PoolDev p, PrefillArgs a, const uint16_t *q,
+__global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, PrefillArgs a, const uint16_t *q,
                                                              const float *part_o, const float *part_ml, float *out) {
   __shared__ FinishSmem sm;
   const int T = blockIdx.x, kv = blockIdx.y;
@@ -613,42 +615,53 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PoolDev p, PrefillA
   // row's l is the sum over its two lanes, so the history's L enters once
   float m = M, negm = -M, lsum = h == 0 ? L : 0.f;
   const int nchunk = (n_win + 31) / 32;
-  // stage chunk c's V rows into buffer c & 1 (transposed to the B operand)
-  auto stage = [&](int c) {
-    const int tk = tid >> 3, cb = tid & 7; // token of the chunk, 16-channel block
-    const int u = 32 * c + tk;
-    u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = v0;
+  // Chunk c's words are loaded one chunk ahead: the A-operand words of its
+  // keys (token tile_token(n) of the chunk, channels 16 ks + 8 h ..) into
+  // registers, its V rows (token tid / 8, channels 16 (tid % 8) ..) into
+  // registers and then, transposed to the B operand, into buffer c & 1.
+  auto kload = [&](int c, u32x4 (&kr)[8]) __attribute__((always_inline)) {
+    const int u = 32 * c + tile_token(n);
+    const bool ok = u < n_win;
+    const u32x4 *src = (const u32x4 *)(ok ? krow(u) : sinkK);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kr[ks] = ok ? src[2 * ks + h] : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto vload = [&](int c, u32x4 (&vr)[2]) __attribute__((always_inline)) {
+    const int u = 32 * c + (tid >> 3);
+    vr[0] = vr[1] = u32x4{0u, 0u, 0u, 0u};
     if (u < n_win) {
-      const u32x4 *src = (const u32x4 *)(vrow(u) + 16 * cb);
-      v0 = src[0];
-      v1 = src[1];
+      const u32x4 *src = (const u32x4 *)(vrow(u) + 16 * (tid & 7));
+      vr[0] = src[0];
+      vr[1] = src[1];
     }
+  };
+  auto vstore = [&](int c, const u32x4 (&vr)[2]) __attribute__((always_inline)) {
+    const int tk = tid >> 3, cb = tid & 7; // token of the chunk, 16-channel block
     const int hh = tk >> 4, ks = (tk & 15) >> 3, e = tk & 7;
     uint16_t *V = (uint16_t *)&sm.V[c & 1][0][0][0];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const uint32_t wd = k < 8 ? v0[k / 2] : v1[(k - 8) / 2];
+      const uint32_t wd = k < 8 ? vr[0][k / 2] : vr[1][(k - 8) / 2];
       const uint16_t val = (uint16_t)((k & 1) ? (wd >> 16) : (wd & 0xffffu));
       const int c2 = 16 * cb + k;
       V[(((c2 >> 5) * 2 + ks) * 64 + (c2 & 31) + 32 * hh) * 8 + e] = val;
     }
   };
-  if (nchunk > 0) stage(0);
+  u32x4 kc[8], kn[8], vr[2];
+  __syncthreads(); // every wave is done with R_V^T: the window buffers overlay it
+  if (nchunk > 0) {
+    vload(0, vr);
+    vstore(0, vr);
+    kload(0, kc);
+    if (nchunk > 1) vload(1, vr);
+  }
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
-    if (c + 1 < nchunk) stage(c + 1);
+    if (c + 1 < nchunk) kload(c + 1, kn);
     // S^T = K_win . q^T: A operand token tile_token(n) of the chunk
     v16f S = v16f{};
-    {
-      const int u = 32 * c + tile_token(n);
-      const bool ok = u < n_win;
-      const u32x4 *src = (const u32x4 *)(ok ? krow(u) : sinkK);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const v8bf A = __builtin_bit_cast(v8bf, ok ? src[2 * ks + h] : u32x4{0u, 0u, 0u, 0u});
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Qw[ks], S, 0, 0, 0);
-      }
-    }
+    for (int ks = 0; ks < 8; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kc[ks]), Qw[ks], S, 0, 0, 0);
     float x[16], mxl = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -713,7 +726,11 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PoolDev p, PrefillA
         O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, B, O[ct], 0, 0, 0);
       }
     }
+    if (c + 1 < nchunk) vstore(c + 1, vr);
+    if (c + 2 < nchunk) vload(c + 2, vr);
     __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kc[ks] = kn[ks];
   }
   // ---- normalise and store: register (J, i) holds row 8 J + 4 h + i,
   // channel 32 ct + n; the history part was weighted relative to M, the
