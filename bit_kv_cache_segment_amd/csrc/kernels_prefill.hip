@@ -11,7 +11,9 @@
 // positions up to its own.
 //
 // Launches (one stream), for pools with d = 128 and one scale group per
-// token (G = 128), affine levels:
+// token (G = 128), affine or codebook levels (a codebook pool's level is
+// z + (L[code] / 64) s: its staged codes are the level bytes L, from one byte
+// permute per pair, and both scales carry the 1/64):
 //   prefill_qprep_kernel, one block per (tile of 128 rows, kv head): the
 //     rows' queries are rotated by R_K (v_mfma_f32_32x32x2f32), scaled by
 //     scale * log2(e) and 2^E (E per tile: |a| 2^E < 2^14) and split into
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
     v8h hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int j = e >> 1, pr = 4 * h + j, ef = pr <= 4 ? pr : pr - 5;
+      const int j = e >> 1, pr = 4 * h + j, ef = p.lut ? 0 : (pr <= 4 ? pr : pr - 5);
       const float y = sm.a[w][n][16 * ks + 8 * (e & 1) + pr];
       part += y;
       const float ys = ldexpf(y, E - 2 * ef);
@@ -244,7 +246,12 @@ __device__ __forceinline__ void load_raw(PageRaw &r, const uint8_t *blk, int tid
 // K code dword i of the pool layout -> (token t, 16-channel group gi): its
 // channel pairs (p, p + 8) become fp16 sub-normal pairs code 4^e(p) 2^-24,
 // pairs 0..3 in the lanes of half 0 and 4..7 in half 1 of k-step gi.
-__device__ __forceinline__ void stage_k(PageSlot &s, int i, uint32_t wd) {
+// Codebook pools (lut != 0): each pair holds the two codes' level bytes L
+// (one byte permute per pair), sub-normals L 2^-24 with no 4^e factor.
+__device__ __forceinline__ uint32_t lut_pair(uint32_t wd, int sh, uint32_t lut) {
+  return __builtin_amdgcn_perm(lut, lut, ((wd >> sh) & 0x00030003u) | 0x0C000C00u);
+}
+__device__ __forceinline__ void stage_k(PageSlot &s, int i, uint32_t wd, bool lut, uint32_t lk) {
   const int off = 4 * i;
   const int ls = (off & 1023) >> 4;                 // lane of the share
   const int b = 16 * (off >> 10) + (off & 15);      // byte of the lane's share
@@ -253,6 +260,12 @@ __device__ __forceinline__ void stage_k(PageSlot &s, int i, uint32_t wd) {
   const uint32_t w2 = wd >> 10;
   const int row = token_row(t & 31);
   const int kz = 2 * ((row >> 4) & 1) + 4 * ((gi >> 2) & 1);
+  if (lut) {
+    s.K[t >> 5][gi][row ^ kz] = u32x4{lut_pair(wd, 0, lk), lut_pair(wd, 2, lk), lut_pair(wd, 4, lk), lut_pair(wd, 6, lk)};
+    s.K[t >> 5][gi][(row + 32) ^ kz] =
+        u32x4{lut_pair(wd, 8, lk), lut_pair(wd, 10, lk), lut_pair(wd, 12, lk), lut_pair(wd, 14, lk)};
+    return;
+  }
   s.K[t >> 5][gi][row ^ kz] = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
   s.K[t >> 5][gi][(row + 32) ^ kz] = u32x4{wd & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
 }
@@ -260,7 +273,7 @@ __device__ __forceinline__ void stage_k(PageSlot &s, int i, uint32_t wd) {
 // V code dword i -> (channel c, 16-token block r); tokens 8 ks .. 8 ks + 7
 // of the block become k-step ks of the B operand (token pairs as fp16
 // sub-normals code 4^e 2^-24, e from the pair index).
-__device__ __forceinline__ void stage_v(PageSlot &s, int i, uint32_t wd) {
+__device__ __forceinline__ void stage_v(PageSlot &s, int i, uint32_t wd, bool lut, uint32_t lv) {
   const int off = 4 * i;
   const int ls = (off & 1023) >> 4;
   const int b = 16 * (off >> 10) + (off & 15);
@@ -268,6 +281,12 @@ __device__ __forceinline__ void stage_v(PageSlot &s, int i, uint32_t wd) {
   const int lane0 = (c & 31) + 32 * (r & 1);
   const int lane = lane0 ^ (4 * ((c >> 5) & 1) + 8 * ((lane0 >> 4) & 1));
   const uint32_t w2 = wd >> 10;
+  if (lut) {
+    s.V[c >> 5][r >> 1][0][lane] = u32x4{lut_pair(wd, 0, lv), lut_pair(wd, 2, lv), lut_pair(wd, 4, lv), lut_pair(wd, 6, lv)};
+    s.V[c >> 5][r >> 1][1][lane] =
+        u32x4{lut_pair(wd, 8, lv), lut_pair(wd, 10, lv), lut_pair(wd, 12, lv), lut_pair(wd, 14, lv)};
+    return;
+  }
   s.V[c >> 5][r >> 1][0][lane] = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
   s.V[c >> 5][r >> 1][1][lane] = u32x4{wd & 0x03000300u, w2 & 0x00030003u, w2 & 0x000C000Cu, w2 & 0x00300030u};
 }
@@ -275,19 +294,20 @@ __device__ __forceinline__ void stage_v(PageSlot &s, int i, uint32_t wd) {
 __device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu)); }
 __device__ __forceinline__ float f16hi(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16)); }
 
+// Codebook pools: a level is z + (L / 64) s, so both scales carry 1/64.
 __device__ __forceinline__ void stage_page(PageSlot &s, const PageRaw &r, int tid, int ntok, float kscale,
-                                           float vscale) {
-  stage_k(s, tid, r.k0);
-  stage_k(s, tid + 256, r.k1);
-  stage_v(s, tid, r.v0);
-  stage_v(s, tid + 256, r.v1);
+                                           float vscale, bool lut, uint32_t lk, uint32_t lv) {
+  stage_k(s, tid, r.k0, lut, lk);
+  stage_k(s, tid + 256, r.k1, lut, lk);
+  stage_v(s, tid, r.v0, lut, lv);
+  stage_v(s, tid + 256, r.v1, lut, lv);
   if (tid < 64) {
     // tokens past the history hold no data: their terms are zero
     const bool ok = tid < ntok;
-    s.par[0][tid] = ok ? f16lo(r.par) * kscale : 0.f;
+    s.par[0][tid] = ok ? f16lo(r.par) * (lut ? kscale * 0.015625f : kscale) : 0.f;
     s.par[1][tid] = ok ? f16hi(r.par) : 0.f;
   } else if (tid < 128) {
-    const int t = tid - 64, pr = (t & 15) >> 1, e = pr <= 4 ? pr : pr - 5;
+    const int t = tid - 64, pr = (t & 15) >> 1, e = lut ? 3 : (pr <= 4 ? pr : pr - 5); // 4^-3 = 1/64
     const bool ok = t < ntok;
     s.par[2][t] = ok ? f16lo(r.par) * ldexpf(vscale, -2 * e) : 0.f;
     s.par[3][t] = ok ? f16hi(r.par) : 0.f;
@@ -315,6 +335,8 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   const float qsum = aux[fr];
   const float kscale = aux[kRows]; // 2^(24 - E)
   const float vscale = ldexpf(1.f, p.pv_shift);
+  const bool lut = p.lut != 0;
+  const uint32_t lutK = lut ? p.codebook[kv] : 0u, lutV = lut ? p.codebook[p.Hkv + kv] : 0u;
   v8h Qh[8], Ql[8];
   {
     const u32x4 *src = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (8 * 2 * 64);
@@ -338,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   if (p0 < p1) {
     load_raw(ra, page_ptr(p0), tid);
     if (p0 + 1 < p1) load_raw(rb, page_ptr(p0 + 1), tid);
-    stage_page(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale);
+    stage_page(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale, lut, lutK, lutV);
   }
   __syncthreads();
 
@@ -467,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
         }
       }
     }
-    if (pi + 1 < p1) stage_page(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale);
+    if (pi + 1 < p1) stage_page(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale, lut, lutK, lutV);
     __syncthreads();
   };
   for (int pi = p0; pi < p1; pi += 2) {
@@ -765,7 +787,7 @@ size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S) {
   return al(qrec) + al(qaux) + al(po) + al(pml);
 }
 
-bool prefill_mfma_supported(const PoolDev &p) { return p.d == kD && p.G == kD && !p.lut && !p.bf16_hist; }
+bool prefill_mfma_supported(const PoolDev &p) { return p.d == kD && p.G == kD && !p.bf16_hist; }
 
 hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, void *ws,
                                hipStream_t s) {
