@@ -15,7 +15,8 @@
 // z + (L[code] / 64) s: its staged codes are the level bytes L, from one byte
 // permute per pair, and both scales carry the 1/64):
 //   prefill_qprep_kernel, one block per (tile of 128 rows, kv head): the
-//     rows' queries are rotated by R_K (v_mfma_f32_32x32x2f32), scaled by
+//     rows' queries are rotated by R_K (fp16 MFMAs: the bf16 query is exact
+//     in fp16, R_K is staged as hi + lo parts), scaled by
 //     scale * log2(e) and 2^E (E per tile: |a| 2^E < 2^14) and split into
 //     fp16 hi + lo (~22 bits), laid out as the B operand of
 //     v_mfma_f32_32x32x16_f16 with the per-channel factors 4^-e that the K
@@ -36,7 +37,8 @@
 //     of a lane are the P' operand of the same lane (no data movement).
 //     It writes the split's (m, l, O) in the rotated basis.
 //   prefill_finish_kernel, one block per (tile, kv head): merges the
-//     splits, de-rotates by R_V^T (v_mfma_f32_32x32x2f32), continues the
+//     splits, de-rotates by R_V^T (fp16 MFMAs, the row and R_V^T each split
+//     hi + lo, three products), continues the
 //     online softmax over the sink and recent tokens with the raw queries
 //     (v_mfma_f32_32x32x16_bf16 for both products, P in bf16 hi + lo) and
 //     writes the normalised rows.
@@ -86,7 +88,6 @@ __device__ __forceinline__ TileInfo tile_info(const PrefillArgs &a, int T) {
   return t;
 }
 
-
 // A d x d fp32 rotation R (row j, column c) as the B operands of
 // v_mfma_f32_32x32x16_f16 contractions x . R over j, in shared memory:
 // k-step kk, lane (column 32 ct + l % 32, half h = l / 32) holds rows
@@ -117,6 +118,7 @@ __device__ __forceinline__ void stage_rot(RotB &rb, const float *R, int tid) {
 struct QprepSmem {
   RotB rot;                    // R_K as B operands
   float a[kWaves][32][kD + 1]; // rotated, scaled rows of each wave
+  float up[kWaves][32];        // per row: the power of two its query was scaled down by
   uint32_t amax;               // tile maximum of |a| (bits of a non-negative float)
 };
 
@@ -127,7 +129,8 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const TileInfo ti = tile_info(a, T);
   if (tid == 0) sm.amax = 0u;
-  // A operand of the rotation: row n of the wave, channels j = st + 64 h
+  // A operand of the rotation: row n of the wave; its half h holds channels
+  // 64 h .. 64 h + 63 (8 per k-step)
   const int fr = 32 * w + n; // row in the tile
   const bool real = fr < ti.nrows;
   const int f = ti.f0 + fr;
@@ -145,6 +148,20 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
   // times R_K's hi and lo parts; k-step kk holds channels 64 h + 8 kk + e
   stage_rot(sm.rot, p.RK + (size_t)kv * kD * kD, tid);
   __syncthreads();
+  // a row whose largest element reaches 2^14 is scaled down by an exact
+  // power of two first (fp16 ends at 65504) and scaled back after
+  float qm = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      qm = fmaxf(qm, fmaxf(fabsf(bf16f((uint16_t)(qv[k][i] & 0xffffu))), fabsf(bf16f((uint16_t)(qv[k][i] >> 16)))));
+  qm = fmaxf(qm, __shfl_xor(qm, 32, 64));
+  int qe = 0;
+  frexpf(qm, &qe);
+  const int down = qe > 14 ? qe - 14 : 0;
+  if (h == 0) sm.up[w][n] = ldexpf(1.f, down);
+  wave_sync();
   v16f acc[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) acc[ct] = v16f{};
@@ -154,7 +171,7 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t wd = qv[kk][e / 2];
-      A[e] = (_Float16)bf16f((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu)));
+      A[e] = (_Float16)ldexpf(bf16f((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu))), -down);
     }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float y = acc[ct][v] * a.qscale;
+      const float y = acc[ct][v] * sm.up[w][8 * (v / 4) + 4 * h + v % 4] * a.qscale;
       mx = fmaxf(mx, fabsf(y));
       sm.a[w][8 * (v / 4) + 4 * h + v % 4][32 * ct + n] = y;
     }

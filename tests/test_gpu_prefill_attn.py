@@ -128,6 +128,27 @@ def test_bench_chunk_full_size_sampled_heads():
         assert err <= TOL, (h, err)
 
 
+def test_query_elements_beyond_fp16_range():
+    # queries times 2^17 (elements up to ~10^6, past fp16's 65504): the
+    # matrix-core path scales such rows by an exact power of two before its
+    # fp16 rotation and back after it
+    w = _workload("g4_d128_G128", 1)
+    L, n_q = 700, 40
+    RK, RV, cK, cV = harness.tables(w)
+    cfg = harness.config_for(w, [L], extra_tokens=0)
+    pool = ok.Pool(cfg, RK, RV, cK, cV, max_batch=1)
+    harness.prefill_all(pool, w, [L])
+    q = _queries(w, 0, n_q, 11) * 2.0 ** 17
+    got = pool.prefill_attn(0, q.to("cuda").view(torch.uint16).contiguous())
+    torch.cuda.synchronize()
+    st, _, _ = oracle_sequence(w, 0, L)
+    ref = oracle.prefill_attention(st, synth.bf16_bits(q), 1 / math.sqrt(w.head_dim))
+    g = got.double().cpu().numpy()
+    assert np.isfinite(g).all()
+    err = oracle.row_rel_err(g.reshape(-1, w.head_dim), ref.reshape(-1, w.head_dim))
+    assert err <= TOL, err
+
+
 def test_prefill_attn_rejects_bad_arguments():
     w = _workload("g4_d128_G128", 2)
     RK, RV, cK, cV = harness.tables(w)
