@@ -10,8 +10,10 @@
 // heads per kv head); query i sits at position L - n_q + i and sees the
 // positions up to its own.
 //
-// Launches (one stream), for pools with d = 128 and one scale group per
-// token (G = 128), affine or codebook levels (a codebook pool's level is
+// Launches (one stream), for pools with d = 128, one or two scale groups
+// per token (G = 128 or 64: with two, the logit sums one QK^T chain per
+// group and P' is formed per group for its channel tiles), affine or
+// codebook levels (a codebook pool's level is
 // z + (L[code] / 64) s: its staged codes are the level bytes L, from one byte
 // permute per pair, and both scales carry the 1/64):
 //   prefill_qprep_kernel, one block per (tile of 128 rows, kv head): the
@@ -58,6 +60,9 @@ constexpr int kRows = 128;       // flat rows per tile (4 waves x 32)
 constexpr int kWaves = 4;
 constexpr int kQBits = 14;       // |a| 2^E < 2^kQBits: fp16 hi/lo parts stay finite
 constexpr float kLazyPf = 8.f;   // log2 headroom of the lazy softmax reference
+// Per tile, beside the query records: the rows' sums of a for each of up to
+// two channel groups (G = 128: one; G = 64: two), then 2^(24 - E).
+constexpr int kAux = 2 * kRows + 1;
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -122,6 +127,7 @@ struct QprepSmem {
   uint32_t amax;               // tile maximum of |a| (bits of a non-negative float)
 };
 
+template <int NG>
 __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillArgs a, const uint16_t *q,
                                                             u32x4 *qrec, float *qaux) {
   __shared__ QprepSmem sm;
@@ -201,7 +207,9 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
   // 16 ks + 8 x + 4 h + j times 4^-e(4 h + j), e(p) = p <= 4 ? p : p - 5, as
   // fp16 hi and lo parts (the K operand holds code 4^e(p) 2^-24 there)
   u32x4 *dst = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (8 * 2 * 64);
-  float part = 0.f;
+  float part[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) part[g] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     v8h hi, lo;
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
     for (int e = 0; e < 8; ++e) {
       const int j = e >> 1, pr = 4 * h + j, ef = p.lut ? 0 : (pr <= 4 ? pr : pr - 5);
       const float y = sm.a[w][n][16 * ks + 8 * (e & 1) + pr];
-      part += y;
+      part[NG == 2 ? ks / 4 : 0] += y; // k-steps 0..3 hold channels 0..63
       const float ys = ldexpf(y, E - 2 * ef);
       const _Float16 yh = (_Float16)ys;
       hi[e] = yh;
@@ -218,11 +226,14 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
     dst[(ks * 2 + 0) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
     dst[(ks * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
   }
-  // row sum of a over all channels (the two halves hold 64 each)
-  const float qsum = part + __shfl_xor(part, 32, 64);
-  float *aux = qaux + ((size_t)kv * a.NT + T) * (kRows + 1);
-  if (h == 0) aux[32 * w + n] = qsum;
-  if (tid == 0) aux[kRows] = ldexpf(1.f, 24 - E);
+  // row sums of a over each channel group (the two halves hold 32 of each)
+  float *aux = qaux + ((size_t)kv * a.NT + T) * kAux;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const float qsum = part[g] + __shfl_xor(part[g], 32, 64);
+    if (h == 0) aux[g * kRows + 32 * w + n] = qsum;
+  }
+  if (tid == 0) aux[2 * kRows] = ldexpf(1.f, 24 - E);
 }
 
 // ---------------------------------------------------------------------------
@@ -237,11 +248,12 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
 struct PageSlot {
   u32x4 K[2][8][64];    // [tile][k-step][lane]: 8 fp16 K code values (A operand)
   u32x4 V[4][2][2][64]; // [channel tile][tile][k-step][lane]: 8 fp16 V code values (B operand)
-  float par[4][64];     // per token: s_K 2^(24-E), z_K, s_V 2^pv_shift 4^-e, z_V
+  float par[8][64];     // per token, channel group g: [2g] s_K 2^(24-E), [2g+1] z_K,
+                        // [4+2g] s_V 2^pv_shift 4^-e, [5+2g] z_V
 };
 struct HistSmemPf {
   PageSlot slot[2];
-  float row[kWaves][32]; // per-wave row broadcast (rescale factors, zero sums)
+  float row[kWaves][2][32]; // per-wave row broadcast (rescale factors, zero sums)
 };
 
 // Raw words of one page a thread stages: K and V code dwords tid and
@@ -250,14 +262,15 @@ struct PageRaw {
   uint32_t k0, k1, v0, v1, par;
 };
 
-__device__ __forceinline__ void load_raw(PageRaw &r, const uint8_t *blk, int tid) {
+// npar = 128 NG: the K then V (scale, zero) dwords of the page, token-major
+__device__ __forceinline__ void load_raw(PageRaw &r, const uint8_t *blk, int tid, int npar) {
   const uint32_t *w = (const uint32_t *)blk;
   r.k0 = __builtin_nontemporal_load(w + tid);
   r.k1 = __builtin_nontemporal_load(w + tid + 256);
   r.v0 = __builtin_nontemporal_load(w + 512 + tid);
   r.v1 = __builtin_nontemporal_load(w + 512 + tid + 256);
-  // K params at byte 32 d + 4 t, V params 256 bytes later (G = d)
-  r.par = tid < 128 ? __builtin_nontemporal_load(w + 1024 + tid) : 0u;
+  // K params at byte 32 d + 4 (NG t + g), V params 256 NG bytes later
+  r.par = tid < npar ? __builtin_nontemporal_load(w + 1024 + tid) : 0u;
 }
 
 // K code dword i of the pool layout -> (token t, 16-channel group gi): its
@@ -312,25 +325,29 @@ __device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit
 __device__ __forceinline__ float f16hi(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16)); }
 
 // Codebook pools: a level is z + (L / 64) s, so both scales carry 1/64.
+template <int NG>
 __device__ __forceinline__ void stage_page(PageSlot &s, const PageRaw &r, int tid, int ntok, float kscale,
                                            float vscale, bool lut, uint32_t lk, uint32_t lv) {
   stage_k(s, tid, r.k0, lut, lk);
   stage_k(s, tid + 256, r.k1, lut, lk);
   stage_v(s, tid, r.v0, lut, lv);
   stage_v(s, tid + 256, r.v1, lut, lv);
-  if (tid < 64) {
+  if (tid < 64 * NG) {
     // tokens past the history hold no data: their terms are zero
-    const bool ok = tid < ntok;
-    s.par[0][tid] = ok ? f16lo(r.par) * (lut ? kscale * 0.015625f : kscale) : 0.f;
-    s.par[1][tid] = ok ? f16hi(r.par) : 0.f;
-  } else if (tid < 128) {
-    const int t = tid - 64, pr = (t & 15) >> 1, e = lut ? 3 : (pr <= 4 ? pr : pr - 5); // 4^-3 = 1/64
+    const int t = tid / NG, g = tid % NG;
     const bool ok = t < ntok;
-    s.par[2][t] = ok ? f16lo(r.par) * ldexpf(vscale, -2 * e) : 0.f;
-    s.par[3][t] = ok ? f16hi(r.par) : 0.f;
+    s.par[2 * g][t] = ok ? f16lo(r.par) * (lut ? kscale * 0.015625f : kscale) : 0.f;
+    s.par[2 * g + 1][t] = ok ? f16hi(r.par) : 0.f;
+  } else if (tid < 128 * NG) {
+    const int t = (tid - 64 * NG) / NG, g = (tid - 64 * NG) % NG;
+    const int pr = (t & 15) >> 1, e = lut ? 3 : (pr <= 4 ? pr : pr - 5); // 4^-3 = 1/64
+    const bool ok = t < ntok;
+    s.par[4 + 2 * g][t] = ok ? f16lo(r.par) * ldexpf(vscale, -2 * e) : 0.f;
+    s.par[5 + 2 * g][t] = ok ? f16hi(r.par) : 0.f;
   }
 }
 
+template <int NG>
 __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, PrefillArgs a, const u32x4 *qrec,
                                                               const float *qaux, float *part_o, float *part_ml) {
   __shared__ HistSmemPf sm;
@@ -348,9 +365,9 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   const int fr = 32 * w + n;
   const bool real = fr < ti.nrows;
   const int vis = real ? prefill_visible_hist(a.L - a.n_q + (ti.f0 + fr) / a.g, n_hist) : 0;
-  const float *aux = qaux + ((size_t)kv * a.NT + T) * (kRows + 1);
-  const float qsum = aux[fr];
-  const float kscale = aux[kRows]; // 2^(24 - E)
+  const float *aux = qaux + ((size_t)kv * a.NT + T) * kAux;
+  const float qsum = aux[fr], qsum1 = NG == 2 ? aux[kRows + fr] : 0.f; // per channel group
+  const float kscale = aux[2 * kRows]; // 2^(24 - E)
   const float vscale = ldexpf(1.f, p.pv_shift);
   const bool lut = p.lut != 0;
   const uint32_t lutK = lut ? p.codebook[kv] : 0u, lutV = lut ? p.codebook[p.Hkv + kv] : 0u;
@@ -363,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
       Ql[ks] = __builtin_bit_cast(v8h, src[(ks * 2 + 1) * 64 + lane]);
     }
   }
-  float m = -INFINITY, negm = INFINITY, lsum = 0.f, zsum = 0.f;
+  float m = -INFINITY, negm = INFINITY, lsum = 0.f, zsum = 0.f, zsum1 = 0.f;
   v16f O[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) O[ct] = v16f{};
@@ -375,9 +392,9 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
 
   PageRaw ra, rb;
   if (p0 < p1) {
-    load_raw(ra, page_ptr(p0), tid);
-    if (p0 + 1 < p1) load_raw(rb, page_ptr(p0 + 1), tid);
-    stage_page(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale, lut, lutK, lutV);
+    load_raw(ra, page_ptr(p0), tid, 128 * NG);
+    if (p0 + 1 < p1) load_raw(rb, page_ptr(p0 + 1), tid, 128 * NG);
+    stage_page<NG>(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale, lut, lutK, lutV);
   }
   __syncthreads();
 
@@ -387,12 +404,114 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   // after the compute, and one barrier ends the step.
   auto step = [&](int pi, const PageRaw &nxt, PageRaw &fut) __attribute__((always_inline)) {
     const int sl = (pi - p0) & 1;
-    if (pi + 2 < p1) load_raw(fut, page_ptr(pi + 2), tid);
+    if (pi + 2 < p1) load_raw(fut, page_ptr(pi + 2), tid, 128 * NG);
     const PageSlot &S = sm.slot[sl];
     const bool masked = pi >= fv;
     const int tbase = pi * kPage;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      if constexpr (NG == 2) {
+        // two scale groups per token (channels 0..63, 64..127): the logit
+        // sums one QK^T chain per group, each with its scale and zero term;
+        // it is kept without the reference (lg), which the weights subtract
+        const int tok0 = 32 * tt + 16 * h; // token (in the page) of register 0
+        float lg[16];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          v16f acc = v16f{};
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int ks = 4 * g + k4;
+            const v8h A = __builtin_bit_cast(v8h, S.K[tt][ks][lane ^ (2 * ((lane >> 4) & 1) + 4 * ((ks >> 2) & 1))]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Qh[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Ql[ks], acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            const v4f sk = *(const v4f *)&S.par[2 * g][tok0 + 4 * J];
+            const v4f zk = *(const v4f *)&S.par[2 * g + 1][tok0 + 4 * J];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int v = 4 * J + i;
+              lg[v] = g == 0 ? fmaf(sk[i], acc[v], zk[i] * qsum) : fmaf(sk[i], acc[v], fmaf(zk[i], qsum1, lg[v]));
+            }
+          }
+        }
+        float mxl = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if (masked) lg[v] = tbase + tok0 + v < vis ? lg[v] : -INFINITY;
+          mxl = fmaxf(mxl, lg[v]);
+        }
+        // lazy reference (as for one group): rows are lanes n and n + 32
+        if (__any(mxl > m + kLazyPf)) {
+          const float rm = fmaxf(mxl, __shfl_xor(mxl, 32, 64));
+          const bool jump = rm > m + kLazyPf;
+          const float mn = jump ? ceilf(rm) : m;
+          const float alpha = jump ? exp2f(m - mn) : 1.f; // m = -inf: 0
+          m = mn;
+          lsum *= alpha;
+          zsum *= alpha;
+          zsum1 *= alpha;
+          if (n == lane) sm.row[w][0][n] = alpha;
+          wave_sync();
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            const v4f al = *(const v4f *)&sm.row[w][0][8 * J + 4 * h];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= al[i];
+          }
+          wave_sync();
+        }
+        // a row that has seen no token yet has only masked (-inf) logits
+        const float nm = m == -INFINITY ? 0.f : -m;
+        float pw[16];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const v4f zv0 = *(const v4f *)&S.par[5][tok0 + 4 * J];
+          const v4f zv1 = *(const v4f *)&S.par[7][tok0 + 4 * J];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = 4 * J + i;
+            const float pv = __builtin_amdgcn_exp2f(lg[v] + nm);
+            lsum += pv;
+            zsum = fmaf(pv, zv0[i], zsum);
+            zsum1 = fmaf(pv, zv1[i], zsum1);
+            pw[v] = pv;
+          }
+        }
+        // P' of group g (its V scale) for the channel tiles 2 g, 2 g + 1
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float pp[16];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            const v4f sp = *(const v4f *)&S.par[4 + 2 * g][tok0 + 4 * J];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pp[4 * J + i] = pw[4 * J + i] * sp[i];
+          }
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            v8h hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float y = pp[8 * ks + e];
+              const _Float16 yh = (_Float16)y;
+              hi[e] = yh;
+              lo[e] = (_Float16)(y - (float)yh);
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              const int ct = 2 * g + c2;
+              const v8h B = __builtin_bit_cast(v8h, S.V[ct][tt][ks][lane ^ (4 * (ct & 1) + 8 * ((lane >> 4) & 1))]);
+              O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, B, O[ct], 0, 0, 0);
+              O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, B, O[ct], 0, 0, 0);
+            }
+          }
+        }
+      } else {
       const int tok0 = 32 * tt + 16 * h; // token (in the page) of register 0
       // the logits' per-token terms, read before the QK^T chain so that
       // their shared-memory latency overlaps it
@@ -450,11 +569,11 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
         negm = -mn;
         lsum *= alpha;
         zsum *= alpha;
-        if (n == lane) sm.row[w][n] = alpha; // lanes 0..31 (both halves agree)
+        if (n == lane) sm.row[w][0][n] = alpha; // lanes 0..31 (both halves agree)
         wave_sync();
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-          const v4f al = *(const v4f *)&sm.row[w][8 * J + 4 * h];
+          const v4f al = *(const v4f *)&sm.row[w][0][8 * J + 4 * h];
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -477,8 +596,8 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
       float pp[16];
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        const v4f sp = *(const v4f *)&S.par[2][tok0 + 4 * J];
-        const v4f zv = *(const v4f *)&S.par[3][tok0 + 4 * J];
+        const v4f sp = *(const v4f *)&S.par[4][tok0 + 4 * J];
+        const v4f zv = *(const v4f *)&S.par[5][tok0 + 4 * J];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v = 4 * J + i;
@@ -505,8 +624,9 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
           O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, B, O[ct], 0, 0, 0);
         }
       }
+      }
     }
-    if (pi + 1 < p1) stage_page(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale, lut, lutK, lutV);
+    if (pi + 1 < p1) stage_page<NG>(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale, lut, lutK, lutV);
     __syncthreads();
   };
   for (int pi = p0; pi < p1; pi += 2) {
@@ -518,19 +638,25 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   // O 2^(24 - pv_shift) + sum_t p_t z_V(t)
   const float lrow = lsum + __shfl_xor(lsum, 32, 64);
   const float zrow = zsum + __shfl_xor(zsum, 32, 64);
-  if (lane < 32) sm.row[w][n] = zrow;
+  const float zrow1 = zsum1 + __shfl_xor(zsum1, 32, 64);
+  if (lane < 32) {
+    sm.row[w][0][n] = zrow;
+    sm.row[w][1][n] = zrow1;
+  }
   wave_sync();
   const size_t base = (((size_t)kv * a.NT + T) * a.S + s) * kRows + 32 * w;
   const float k24 = ldexpf(1.f, 24 - p.pv_shift);
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
-    const v4f zr = *(const v4f *)&sm.row[w][8 * J + 4 * h];
+    const v4f zr = *(const v4f *)&sm.row[w][0][8 * J + 4 * h];
+    const v4f zr1 = *(const v4f *)&sm.row[w][1][8 * J + 4 * h];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 8 * J + 4 * h + i;
       float *dst = part_o + (base + rr) * kD + n;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) dst[32 * ct] = fmaf(O[ct][4 * J + i], k24, zr[i]);
+      for (int ct = 0; ct < 4; ++ct)
+        dst[32 * ct] = fmaf(O[ct][4 * J + i], k24, (NG == 2 && ct >= 2) ? zr1[i] : zr[i]);
     }
   }
   if (lane < 32) {
@@ -797,14 +923,14 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
 
 size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S) {
   const size_t qrec = (size_t)Hkv * NT * kWaves * 8 * 2 * 64 * 16;
-  const size_t qaux = (size_t)Hkv * NT * (kRows + 1) * 4;
+  const size_t qaux = (size_t)Hkv * NT * kAux * 4;
   const size_t po = (size_t)Hkv * NT * S * kRows * kD * 4;
   const size_t pml = (size_t)Hkv * NT * S * kRows * 2 * 4;
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   return al(qrec) + al(qaux) + al(po) + al(pml);
 }
 
-bool prefill_mfma_supported(const PoolDev &p) { return p.d == kD && p.G == kD && !p.bf16_hist; }
+bool prefill_mfma_supported(const PoolDev &p) { return p.d == kD && (p.G == kD || p.G == 64) && !p.bf16_hist; }
 
 hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, void *ws,
                                hipStream_t s) {
@@ -814,12 +940,17 @@ hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uin
   u32x4 *qrec = (u32x4 *)base;
   base += al((size_t)p.Hkv * a.NT * kWaves * 8 * 2 * 64 * 16);
   float *qaux = (float *)base;
-  base += al((size_t)p.Hkv * a.NT * (kRows + 1) * 4);
+  base += al((size_t)p.Hkv * a.NT * kAux * 4);
   float *po = (float *)base;
   base += al((size_t)p.Hkv * a.NT * a.S * kRows * kD * 4);
   float *pml = (float *)base;
-  hipLaunchKernelGGL(prefill_qprep_kernel, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
-  hipLaunchKernelGGL(prefill_hist_kernel, dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po, pml);
+  if (p.G == kD) {
+    hipLaunchKernelGGL(prefill_qprep_kernel<1>, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
+    hipLaunchKernelGGL(prefill_hist_kernel<1>, dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po, pml);
+  } else {
+    hipLaunchKernelGGL(prefill_qprep_kernel<2>, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
+    hipLaunchKernelGGL(prefill_hist_kernel<2>, dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po, pml);
+  }
   hipLaunchKernelGGL(prefill_finish_kernel, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, po, pml, out);
   return hipGetLastError();
 }

@@ -793,7 +793,7 @@ int oscar_pool_check(oscar_pool *p, void *stream) {
 // Pools whose prefill attention runs on the matrix-core path (the same test
 // as prefill_mfma_supported, from the configuration).
 static bool prefill_mfma_config(const oscar_pool_config *c) {
-  return c->head_dim == 128 && c->group_size == 128 && !(c->flags & OSCAR_POOL_BF16_HISTORY);
+  return c->head_dim == 128 && !(c->flags & OSCAR_POOL_BF16_HISTORY);
 }
 
 int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, size_t *bytes) {

@@ -269,7 +269,7 @@ int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, siz
  *   q:   device bf16 [n_q][Hq][d];   out: device fp32 [n_q][Hq][d];
  *   workspace: device, >= oscar_prefill_workspace_bytes(cfg, n_q) bytes.
  * The (query, head) rows of each kv head are cut in tiles: 128 rows on the
- * matrix-core path (pools with head_dim 128 and group_size 128, affine or
+ * matrix-core path (pools with head_dim 128, any group size, affine or
  * Lloyd-Max levels: query preparation, history and finish launches), else
  * 8 rows,
  * which the decode kernels treat as the heads of one (sequence, kv head)
