@@ -6,7 +6,7 @@ oracle's pool built from that stream within 2e-3 row-relative error, and
 codes, scale/zero, windows and page tables (against the oracle's pool model
 with forks) must be bit-exact, through fused steps and separate
 append + decode calls, chained forks, and releases of sources whose pages
-forks still hold."""
+forks still hold; and prefill attention over forked sequences."""
 import math
 
 import numpy as np
@@ -176,11 +176,27 @@ def _drive(run, steps, seed):
     return worst
 
 
+def _check_prefill(run, seqs, n_q):
+    """Prefill attention of the last n_q positions of forked sequences (their
+    history partly in pages they share, partly in copied pages) against the
+    oracle's causal attention over the composite token stream."""
+    w = run.w
+    for s in seqs:
+        q = synth.queries(w, 500 + s, batch=n_q)
+        got = run.pool.prefill_attn(s, q.to("cuda").view(torch.uint16).contiguous())
+        torch.cuda.synchronize()
+        st, _, _ = run.oracle_seq(s)
+        ref = oracle.prefill_attention(st, synth.bf16_bits(q), 1 / math.sqrt(w.head_dim))
+        err = oracle.row_rel_err(got.double().cpu().numpy().reshape(-1, w.head_dim), ref.reshape(-1, w.head_dim))
+        assert err <= TOL, (s, err)
+
+
 @pytest.mark.parametrize("shape", list(SHAPES))
 def test_forks_match_oracle(shape):
     w = _workload(shape)
     run = Run(w, 0)
     worst = _drive(run, 60, 7)
+    _check_prefill(run, [5, 8], 300)
     print(f"{shape}: worst row error {worst:.2e}")
 
 
@@ -194,6 +210,7 @@ def test_forks_lloyd_max_pool():
     w = _workload("g8_d128_G64", ok.POOL_LLOYD_MAX)
     run = Run(w, ok.POOL_LLOYD_MAX)
     _drive(run, 40, 9)
+    _check_prefill(run, [5, 8], 300)
 
 
 def test_fork_then_release_everything_returns_every_page():
