@@ -55,7 +55,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;          // head dimension of this path
 constexpr int kRows = 128;       // flat rows per tile (4 waves x 32)
 constexpr int kWaves = 4;
 constexpr int kQBits = 14;       // |a| 2^E < 2^kQBits: fp16 hi/lo parts stay finite
@@ -96,18 +95,21 @@ __device__ __forceinline__ TileInfo tile_info(const PrefillArgs &a, int T) {
 // A d x d fp32 rotation R (row j, column c) as the B operands of
 // v_mfma_f32_32x32x16_f16 contractions x . R over j, in shared memory:
 // k-step kk, lane (column 32 ct + l % 32, half h = l / 32) holds rows
-// 64 h + 8 kk + e, e = 0..7, split into fp16 hi and lo parts (~22 bits).
+// (d / 2) h + 8 kk + e, e = 0..7, split into fp16 hi and lo parts (~22 bits).
+template <int D>
 struct RotB {
-  u32x4 b[8][4][2][64]; // [k-step][column tile][hi, lo][lane]  (64 KB)
+  u32x4 b[D / 16][D / 32][2][64]; // [k-step][column tile][hi, lo][lane]  (D^2 4 bytes)
 };
-__device__ __forceinline__ void stage_rot(RotB &rb, const float *R, int tid) {
+template <int D>
+__device__ __forceinline__ void stage_rot(RotB<D> &rb, const float *R, int tid) {
   const int lane = tid & 63, ct = tid >> 6, n = lane & 31, h = lane >> 5;
+  if (ct >= D / 32) return;
 #pragma unroll 2
-  for (int kk = 0; kk < 8; ++kk) {
+  for (int kk = 0; kk < D / 16; ++kk) {
     v8h hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float y = R[(size_t)(64 * h + 8 * kk + e) * kD + 32 * ct + n];
+      const float y = R[(size_t)(D / 2 * h + 8 * kk + e) * D + 32 * ct + n];
       const _Float16 yh = (_Float16)y;
       hi[e] = yh;
       lo[e] = (_Float16)(y - (float)yh);
@@ -120,45 +122,47 @@ __device__ __forceinline__ void stage_rot(RotB &rb, const float *R, int tid) {
 // ---------------------------------------------------------------------------
 // Query preparation.
 // ---------------------------------------------------------------------------
+template <int D>
 struct QprepSmem {
-  RotB rot;                    // R_K as B operands
-  float a[kWaves][32][kD + 1]; // rotated, scaled rows of each wave
+  RotB<D> rot;                 // R_K as B operands
+  float a[kWaves][32][D + 1];  // rotated, scaled rows of each wave
   float up[kWaves][32];        // per row: the power of two its query was scaled down by
   uint32_t amax;               // tile maximum of |a| (bits of a non-negative float)
 };
 
-template <int NG>
+template <int D, int NG>
 __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillArgs a, const uint16_t *q,
                                                             u32x4 *qrec, float *qaux) {
-  __shared__ QprepSmem sm;
+  constexpr int KS = D / 16, CT = D / 32; // k-steps of 16 channels, tiles of 32 columns
+  __shared__ QprepSmem<D> sm;
   const int T = blockIdx.x, kv = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const TileInfo ti = tile_info(a, T);
   if (tid == 0) sm.amax = 0u;
   // A operand of the rotation: row n of the wave; its half h holds channels
-  // 64 h .. 64 h + 63 (8 per k-step)
+  // (d / 2) h .. (d / 2) h + d / 2 - 1 (8 per k-step)
   const int fr = 32 * w + n; // row in the tile
   const bool real = fr < ti.nrows;
   const int f = ti.f0 + fr;
-  u32x4 qv[8];
+  u32x4 qv[KS];
   if (real) {
     const int i = f / a.g, head = kv * a.g + f % a.g;
-    const u32x4 *src = (const u32x4 *)(q + ((size_t)i * p.Hq + head) * kD + 64 * h);
+    const u32x4 *src = (const u32x4 *)(q + ((size_t)i * p.Hq + head) * D + D / 2 * h);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qv[k] = src[k];
+    for (int k = 0; k < KS; ++k) qv[k] = src[k];
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qv[k] = u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < KS; ++k) qv[k] = u32x4{0u, 0u, 0u, 0u};
   }
   // x_rot[c] = sum_j x[j] R_K[j][c]: the query row (bf16, exact in fp16)
-  // times R_K's hi and lo parts; k-step kk holds channels 64 h + 8 kk + e
-  stage_rot(sm.rot, p.RK + (size_t)kv * kD * kD, tid);
+  // times R_K's hi and lo parts; k-step kk holds channels (d / 2) h + 8 kk + e
+  stage_rot<D>(sm.rot, p.RK + (size_t)kv * D * D, tid);
   __syncthreads();
   // a row whose largest element reaches 2^14 is scaled down by an exact
   // power of two first (fp16 ends at 65504) and scaled back after
   float qm = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
+  for (int k = 0; k < KS; ++k)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       qm = fmaxf(qm, fmaxf(fabsf(bf16f((uint16_t)(qv[k][i] & 0xffffu))), fabsf(bf16f((uint16_t)(qv[k][i] >> 16)))));
@@ -168,11 +172,11 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
   const int down = qe > 14 ? qe - 14 : 0;
   if (h == 0) sm.up[w][n] = ldexpf(1.f, down);
   wave_sync();
-  v16f acc[4];
+  v16f acc[CT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = v16f{};
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = v16f{};
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
+  for (int kk = 0; kk < KS; ++kk) {
     v8h A;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
       A[e] = (_Float16)ldexpf(bf16f((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu))), -down);
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(v8h, sm.rot.b[kk][ct][0][lane]), acc[ct], 0, 0, 0);
       acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(v8h, sm.rot.b[kk][ct][1][lane]), acc[ct], 0, 0, 0);
     }
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
   // scale, tile maximum, transpose through shared memory
   float mx = 0.f;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float y = acc[ct][v] * sm.up[w][8 * (v / 4) + 4 * h + v % 4] * a.qscale;
@@ -206,18 +210,18 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
   // 16 channels 16 ks ..): element e = 2 j + x holds channel
   // 16 ks + 8 x + 4 h + j times 4^-e(4 h + j), e(p) = p <= 4 ? p : p - 5, as
   // fp16 hi and lo parts (the K operand holds code 4^e(p) 2^-24 there)
-  u32x4 *dst = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (8 * 2 * 64);
+  u32x4 *dst = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (KS * 2 * 64);
   float part[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) part[g] = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     v8h hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = e >> 1, pr = 4 * h + j, ef = p.lut ? 0 : (pr <= 4 ? pr : pr - 5);
       const float y = sm.a[w][n][16 * ks + 8 * (e & 1) + pr];
-      part[NG == 2 ? ks / 4 : 0] += y; // k-steps 0..3 hold channels 0..63
+      part[NG == 2 ? ks / (KS / 2) : 0] += y; // k-steps 0 .. KS / 2 - 1 hold the first group
       const float ys = ldexpf(y, E - 2 * ef);
       const _Float16 yh = (_Float16)ys;
       hi[e] = yh;
@@ -245,32 +249,37 @@ __global__ __launch_bounds__(256) void prefill_qprep_kernel(PoolDev p, PrefillAr
 // which would otherwise put four lanes on each bank, spread over all banks.
 // K: lane ^ (2 ((lane >> 4) & 1) + 4 ((k-step >> 2) & 1));
 // V: lane ^ (4 (channel tile & 1) + 8 ((lane >> 4) & 1)).
+template <int D>
 struct PageSlot {
-  u32x4 K[2][8][64];    // [tile][k-step][lane]: 8 fp16 K code values (A operand)
-  u32x4 V[4][2][2][64]; // [channel tile][tile][k-step][lane]: 8 fp16 V code values (B operand)
-  float par[8][64];     // per token, channel group g: [2g] s_K 2^(24-E), [2g+1] z_K,
-                        // [4+2g] s_V 2^pv_shift 4^-e, [5+2g] z_V
+  u32x4 K[2][D / 16][64];        // [tile][k-step][lane]: 8 fp16 K code values (A operand)
+  u32x4 V[D / 32][2][2][64];     // [channel tile][tile][k-step][lane]: 8 fp16 V code values (B operand)
+  float par[8][64];              // per token, channel group g: [2g] s_K 2^(24-E), [2g+1] z_K,
+                                 // [4+2g] s_V 2^pv_shift 4^-e, [5+2g] z_V
 };
+template <int D>
 struct HistSmemPf {
-  PageSlot slot[2];
+  PageSlot<D> slot[2];
   float row[kWaves][2][32]; // per-wave row broadcast (rescale factors, zero sums)
 };
 
-// Raw words of one page a thread stages: K and V code dwords tid and
-// tid + 256, and (threads < 128) one parameter dword.
+// Raw words of one page a thread stages: K and V code dwords tid + 256 j
+// (4 d of each in a page block), and one parameter dword.
+template <int D>
 struct PageRaw {
-  uint32_t k0, k1, v0, v1, par;
+  uint32_t k[D / 64], v[D / 64], par;
 };
 
 // npar = 128 NG: the K then V (scale, zero) dwords of the page, token-major
-__device__ __forceinline__ void load_raw(PageRaw &r, const uint8_t *blk, int tid, int npar) {
+template <int D>
+__device__ __forceinline__ void load_raw(PageRaw<D> &r, const uint8_t *blk, int tid, int npar) {
   const uint32_t *w = (const uint32_t *)blk;
-  r.k0 = __builtin_nontemporal_load(w + tid);
-  r.k1 = __builtin_nontemporal_load(w + tid + 256);
-  r.v0 = __builtin_nontemporal_load(w + 512 + tid);
-  r.v1 = __builtin_nontemporal_load(w + 512 + tid + 256);
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    r.k[j] = __builtin_nontemporal_load(w + tid + 256 * j);
+    r.v[j] = __builtin_nontemporal_load(w + 4 * D + tid + 256 * j);
+  }
   // K params at byte 32 d + 4 (NG t + g), V params 256 NG bytes later
-  r.par = tid < npar ? __builtin_nontemporal_load(w + 1024 + tid) : 0u;
+  r.par = tid < npar ? __builtin_nontemporal_load(w + 8 * D + tid) : 0u;
 }
 
 // K code dword i of the pool layout -> (token t, 16-channel group gi): its
@@ -281,12 +290,13 @@ __device__ __forceinline__ void load_raw(PageRaw &r, const uint8_t *blk, int tid
 __device__ __forceinline__ uint32_t lut_pair(uint32_t wd, int sh, uint32_t lut) {
   return __builtin_amdgcn_perm(lut, lut, ((wd >> sh) & 0x00030003u) | 0x0C000C00u);
 }
-__device__ __forceinline__ void stage_k(PageSlot &s, int i, uint32_t wd, bool lut, uint32_t lk) {
+template <int D>
+__device__ __forceinline__ void stage_k(PageSlot<D> &s, int i, uint32_t wd, bool lut, uint32_t lk) {
   const int off = 4 * i;
   const int ls = (off & 1023) >> 4;                 // lane of the share
   const int b = 16 * (off >> 10) + (off & 15);      // byte of the lane's share
-  const int t = 4 * (ls & 15) + b / (kD / 16);      // token
-  const int gi = 4 * ((b % (kD / 16)) / 4) + (ls >> 4); // channels 16 gi .. 16 gi + 15
+  const int t = 4 * (ls & 15) + b / (D / 16);       // token
+  const int gi = 4 * ((b % (D / 16)) / 4) + (ls >> 4); // channels 16 gi .. 16 gi + 15
   const uint32_t w2 = wd >> 10;
   const int row = token_row(t & 31);
   const int kz = 2 * ((row >> 4) & 1) + 4 * ((gi >> 2) & 1);
@@ -303,7 +313,8 @@ __device__ __forceinline__ void stage_k(PageSlot &s, int i, uint32_t wd, bool lu
 // V code dword i -> (channel c, 16-token block r); tokens 8 ks .. 8 ks + 7
 // of the block become k-step ks of the B operand (token pairs as fp16
 // sub-normals code 4^e 2^-24, e from the pair index).
-__device__ __forceinline__ void stage_v(PageSlot &s, int i, uint32_t wd, bool lut, uint32_t lv) {
+template <int D>
+__device__ __forceinline__ void stage_v(PageSlot<D> &s, int i, uint32_t wd, bool lut, uint32_t lv) {
   const int off = 4 * i;
   const int ls = (off & 1023) >> 4;
   const int b = 16 * (off >> 10) + (off & 15);
@@ -325,13 +336,14 @@ __device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit
 __device__ __forceinline__ float f16hi(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16)); }
 
 // Codebook pools: a level is z + (L / 64) s, so both scales carry 1/64.
-template <int NG>
-__device__ __forceinline__ void stage_page(PageSlot &s, const PageRaw &r, int tid, int ntok, float kscale,
+template <int D, int NG>
+__device__ __forceinline__ void stage_page(PageSlot<D> &s, const PageRaw<D> &r, int tid, int ntok, float kscale,
                                            float vscale, bool lut, uint32_t lk, uint32_t lv) {
-  stage_k(s, tid, r.k0, lut, lk);
-  stage_k(s, tid + 256, r.k1, lut, lk);
-  stage_v(s, tid, r.v0, lut, lv);
-  stage_v(s, tid + 256, r.v1, lut, lv);
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    stage_k<D>(s, tid + 256 * j, r.k[j], lut, lk);
+    stage_v<D>(s, tid + 256 * j, r.v[j], lut, lv);
+  }
   if (tid < 64 * NG) {
     // tokens past the history hold no data: their terms are zero
     const int t = tid / NG, g = tid % NG;
@@ -347,10 +359,11 @@ __device__ __forceinline__ void stage_page(PageSlot &s, const PageRaw &r, int ti
   }
 }
 
-template <int NG>
+template <int D, int NG>
 __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, PrefillArgs a, const u32x4 *qrec,
                                                               const float *qaux, float *part_o, float *part_ml) {
-  __shared__ HistSmemPf sm;
+  constexpr int KS = D / 16, CT = D / 32; // k-steps of 16 channels, tiles of 32 channels
+  __shared__ HistSmemPf<D> sm;
   const int kv = blockIdx.y;
   const int T = a.NT - 1 - (int)blockIdx.x / a.S, s = (int)blockIdx.x % a.S; // later tiles (more pages) first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
@@ -371,30 +384,30 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   const float vscale = ldexpf(1.f, p.pv_shift);
   const bool lut = p.lut != 0;
   const uint32_t lutK = lut ? p.codebook[kv] : 0u, lutV = lut ? p.codebook[p.Hkv + kv] : 0u;
-  v8h Qh[8], Ql[8];
+  v8h Qh[KS], Ql[KS];
   {
-    const u32x4 *src = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (8 * 2 * 64);
+    const u32x4 *src = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (KS * 2 * 64);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       Qh[ks] = __builtin_bit_cast(v8h, src[(ks * 2 + 0) * 64 + lane]);
       Ql[ks] = __builtin_bit_cast(v8h, src[(ks * 2 + 1) * 64 + lane]);
     }
   }
   float m = -INFINITY, negm = INFINITY, lsum = 0.f, zsum = 0.f, zsum1 = 0.f;
-  v16f O[4];
+  v16f O[CT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) O[ct] = v16f{};
+  for (int ct = 0; ct < CT; ++ct) O[ct] = v16f{};
 
   const int32_t *ptab = p.page_table + (size_t)a.seq * p.maxp;
   const size_t hstride = (size_t)p.Hkv * p.block_bytes, hoff = (size_t)kv * p.block_bytes;
   auto page_ptr = [&](int pi) { return p.pages + (size_t)ptab[pi] * hstride + hoff; };
   auto ntok_of = [&](int pi) { return min(kPage, n_hist - pi * kPage); };
 
-  PageRaw ra, rb;
+  PageRaw<D> ra, rb;
   if (p0 < p1) {
-    load_raw(ra, page_ptr(p0), tid, 128 * NG);
-    if (p0 + 1 < p1) load_raw(rb, page_ptr(p0 + 1), tid, 128 * NG);
-    stage_page<NG>(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale, lut, lutK, lutV);
+    load_raw<D>(ra, page_ptr(p0), tid, 128 * NG);
+    if (p0 + 1 < p1) load_raw<D>(rb, page_ptr(p0 + 1), tid, 128 * NG);
+    stage_page<D, NG>(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale, lut, lutK, lutV);
   }
   __syncthreads();
 
@@ -402,10 +415,10 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   // earlier), fut receives the loads of page pi + 2.  The page's operands
   // are in slot (pi - p0) & 1; page pi + 1 is staged into the other slot
   // after the compute, and one barrier ends the step.
-  auto step = [&](int pi, const PageRaw &nxt, PageRaw &fut) __attribute__((always_inline)) {
+  auto step = [&](int pi, const PageRaw<D> &nxt, PageRaw<D> &fut) __attribute__((always_inline)) {
     const int sl = (pi - p0) & 1;
-    if (pi + 2 < p1) load_raw(fut, page_ptr(pi + 2), tid, 128 * NG);
-    const PageSlot &S = sm.slot[sl];
+    if (pi + 2 < p1) load_raw<D>(fut, page_ptr(pi + 2), tid, 128 * NG);
+    const PageSlot<D> &S = sm.slot[sl];
     const bool masked = pi >= fv;
     const int tbase = pi * kPage;
 #pragma unroll
@@ -420,8 +433,8 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
         for (int g = 0; g < 2; ++g) {
           v16f acc = v16f{};
 #pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            const int ks = 4 * g + k4;
+          for (int k4 = 0; k4 < KS / 2; ++k4) {
+            const int ks = KS / 2 * g + k4;
             const v8h A = __builtin_bit_cast(v8h, S.K[tt][ks][lane ^ (2 * ((lane >> 4) & 1) + 4 * ((ks >> 2) & 1))]);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Qh[ks], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Ql[ks], acc, 0, 0, 0);
@@ -459,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
           for (int J = 0; J < 4; ++J) {
             const v4f al = *(const v4f *)&sm.row[w][0][8 * J + 4 * h];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
               for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= al[i];
           }
@@ -503,8 +516,8 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
               lo[e] = (_Float16)(y - (float)yh);
             }
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-              const int ct = 2 * g + c2;
+            for (int c2 = 0; c2 < CT / 2; ++c2) {
+              const int ct = CT / 2 * g + c2;
               const v8h B = __builtin_bit_cast(v8h, S.V[ct][tt][ks][lane ^ (4 * (ct & 1) + 8 * ((lane >> 4) & 1))]);
               O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, B, O[ct], 0, 0, 0);
               O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, B, O[ct], 0, 0, 0);
@@ -524,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
       // ---- S^T = K codes . (Q_hi + Q_lo)^T
       v16f acc = v16f{};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         const v8h A = __builtin_bit_cast(v8h, S.K[tt][ks][lane ^ (2 * ((lane >> 4) & 1) + 4 * ((ks >> 2) & 1))]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Qh[ks], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Ql[ks], acc, 0, 0, 0);
@@ -575,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
         for (int J = 0; J < 4; ++J) {
           const v4f al = *(const v4f *)&sm.row[w][0][8 * J + 4 * h];
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+          for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= al[i];
         }
@@ -618,7 +631,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
           lo[e] = (_Float16)(y - (float)yh);
         }
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int ct = 0; ct < CT; ++ct) {
           const v8h B = __builtin_bit_cast(v8h, S.V[ct][tt][ks][lane ^ (4 * (ct & 1) + 8 * ((lane >> 4) & 1))]);
           O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, B, O[ct], 0, 0, 0);
           O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, B, O[ct], 0, 0, 0);
@@ -626,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
       }
       }
     }
-    if (pi + 1 < p1) stage_page<NG>(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale, lut, lutK, lutV);
+    if (pi + 1 < p1) stage_page<D, NG>(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale, lut, lutK, lutV);
     __syncthreads();
   };
   for (int pi = p0; pi < p1; pi += 2) {
@@ -653,10 +666,10 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 8 * J + 4 * h + i;
-      float *dst = part_o + (base + rr) * kD + n;
+      float *dst = part_o + (base + rr) * D + n;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        dst[32 * ct] = fmaf(O[ct][4 * J + i], k24, (NG == 2 && ct >= 2) ? zr1[i] : zr[i]);
+      for (int ct = 0; ct < CT; ++ct)
+        dst[32 * ct] = fmaf(O[ct][4 * J + i], k24, (NG == 2 && ct >= CT / 2) ? zr1[i] : zr[i]);
     }
   }
   if (lane < 32) {
@@ -668,17 +681,21 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
 // ---------------------------------------------------------------------------
 // Merge, de-rotation and the BF16 window.
 // ---------------------------------------------------------------------------
+template <int D>
 struct FinishSmem {
   union {
-    RotB rot;             // R_V^T as B operands (de-rotation)
-    u32x4 V[2][4][2][64]; // then: [buffer][channel tile][k-step][lane], 8 bf16 window V values
+    RotB<D> rot;               // R_V^T as B operands (de-rotation)
+    u32x4 V[2][D / 32][2][64]; // then: [buffer][channel tile][k-step][lane], 8 bf16 window V values
   };
   float row[kWaves][32];
 };
 
+template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, PrefillArgs a, const uint16_t *q,
                                                              const float *part_o, const float *part_ml, float *out) {
-  __shared__ FinishSmem sm;
+  constexpr int KS = D / 16, CT = D / 32;
+  constexpr int VW = D / 64; // 16-byte words of a window V row each thread loads (channels D/8 (tid % 8) ..)
+  __shared__ FinishSmem<D> sm;
   const int T = blockIdx.x, kv = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const TileInfo ti = tile_info(a, T);
@@ -688,25 +705,25 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
   const int qi = real ? f / a.g : 0, head = kv * a.g + (real ? f % a.g : 0);
   const int rowpos = real ? a.L - a.n_q + qi : -1;
 
-  stage_rot(sm.rot, p.RVt + (size_t)kv * kD * kD, tid);
+  stage_rot<D>(sm.rot, p.RVt + (size_t)kv * D * D, tid);
   // ---- merge the splits of this lane's row: reference, weights, l
   const size_t base = ((size_t)kv * a.NT + T) * a.S * kRows + fr;
   float M = -INFINITY;
   for (int s = 0; s < a.S; ++s) M = fmaxf(M, part_ml[(base + (size_t)s * kRows) * 2]);
   float L = 0.f;
-  // A operand of the de-rotation: O_rot[row][j], j = st + 64 h; the lane
-  // keeps its 64 merged values
-  float orot[64];
+  // A operand of the de-rotation: O_rot[row][j], j = st + (D / 2) h; the
+  // lane keeps its D / 2 merged values
+  float orot[D / 2];
 #pragma unroll
-  for (int j = 0; j < 64; ++j) orot[j] = 0.f;
+  for (int j = 0; j < D / 2; ++j) orot[j] = 0.f;
   for (int s = 0; s < a.S; ++s) {
     const float ms = part_ml[(base + (size_t)s * kRows) * 2];
     const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
     L = fmaf(ws, part_ml[(base + (size_t)s * kRows) * 2 + 1], L);
     if (ws != 0.f) {
-      const v4f *src = (const v4f *)(part_o + (base + (size_t)s * kRows) * kD + 64 * h);
+      const v4f *src = (const v4f *)(part_o + (base + (size_t)s * kRows) * D + D / 2 * h);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < D / 8; ++k) {
         const v4f v4 = src[k];
 #pragma unroll
         for (int i = 0; i < 4; ++i) orot[4 * k + i] = fmaf(ws, v4[i], orot[4 * k + i]);
@@ -723,11 +740,11 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
   frexpf(L, &ex);
   const float sdown = L > 0.f ? ldexpf(1.f, -ex) : 0.f;
   if (lane < 32) sm.row[w][n] = L > 0.f ? ldexpf(1.f, ex) : 0.f;
-  v16f O[4];
+  v16f O[CT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) O[ct] = v16f{};
+  for (int ct = 0; ct < CT; ++ct) O[ct] = v16f{};
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
+  for (int kk = 0; kk < KS; ++kk) {
     v8h Ah, Al;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -737,7 +754,7 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
       Al[e] = (_Float16)(y - (float)yh);
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       const v8h Bh = __builtin_bit_cast(v8h, sm.rot.b[kk][ct][0][lane]);
       const v8h Bl = __builtin_bit_cast(v8h, sm.rot.b[kk][ct][1][lane]);
       O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, Bh, O[ct], 0, 0, 0);
@@ -750,7 +767,7 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
   for (int J = 0; J < 4; ++J) {
     const v4f up = *(const v4f *)&sm.row[w][8 * J + 4 * h];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= up[i];
   }
@@ -760,20 +777,20 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
   const int seq = a.seq;
   const int n_sink = min(a.L, kSink), n_rec = min(max(a.L - kSink, 0), kRecent), n_win = n_sink + n_rec;
   const int n_hist = a.n_hist;
-  const uint16_t *sinkK = p.sinkK + ((size_t)seq * p.Hkv + kv) * kSink * kD;
-  const uint16_t *sinkV = p.sinkV + ((size_t)seq * p.Hkv + kv) * kSink * kD;
-  const uint16_t *recK = p.recentK + ((size_t)seq * p.Hkv + kv) * kRecent * kD;
-  const uint16_t *recV = p.recentV + ((size_t)seq * p.Hkv + kv) * kRecent * kD;
-  auto krow = [&](int u) { return u < n_sink ? sinkK + (size_t)u * kD : recK + (size_t)(u - n_sink) * kD; };
-  auto vrow = [&](int u) { return u < n_sink ? sinkV + (size_t)u * kD : recV + (size_t)(u - n_sink) * kD; };
+  const uint16_t *sinkK = p.sinkK + ((size_t)seq * p.Hkv + kv) * kSink * D;
+  const uint16_t *sinkV = p.sinkV + ((size_t)seq * p.Hkv + kv) * kSink * D;
+  const uint16_t *recK = p.recentK + ((size_t)seq * p.Hkv + kv) * kRecent * D;
+  const uint16_t *recV = p.recentV + ((size_t)seq * p.Hkv + kv) * kRecent * D;
+  auto krow = [&](int u) { return u < n_sink ? sinkK + (size_t)u * D : recK + (size_t)(u - n_sink) * D; };
+  auto vrow = [&](int u) { return u < n_sink ? sinkV + (size_t)u * D : recV + (size_t)(u - n_sink) * D; };
   // position of window token u (recent slot j holds 64 + n_hist + ((j - n_hist) mod 256))
   auto upos = [&](int u) { return u < n_sink ? u : kSink + n_hist + ((u - n_sink - n_hist) & (kRecent - 1)); };
   // B operand: raw query row n, channels 16 ks + 8 h .. + 7
-  v8bf Qw[8];
+  v8bf Qw[KS];
   {
-    const u32x4 *src = (const u32x4 *)(q + ((size_t)qi * p.Hq + head) * kD);
+    const u32x4 *src = (const u32x4 *)(q + ((size_t)qi * p.Hq + head) * D);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
       Qw[ks] = __builtin_bit_cast(v8bf, real ? src[2 * ks + h] : u32x4{0u, 0u, 0u, 0u});
   }
   // online state continues from the merged history (reference M); the
@@ -782,37 +799,38 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
   const int nchunk = (n_win + 31) / 32;
   // Chunk c's words are loaded one chunk ahead: the A-operand words of its
   // keys (token tile_token(n) of the chunk, channels 16 ks + 8 h ..) into
-  // registers, its V rows (token tid / 8, channels 16 (tid % 8) ..) into
+  // registers, its V rows (token tid / 8, channels D/8 (tid % 8) ..) into
   // registers and then, transposed to the B operand, into buffer c & 1.
-  auto kload = [&](int c, u32x4 (&kr)[8]) __attribute__((always_inline)) {
+  auto kload = [&](int c, u32x4 (&kr)[KS]) __attribute__((always_inline)) {
     const int u = 32 * c + tile_token(n);
     const bool ok = u < n_win;
     const u32x4 *src = (const u32x4 *)(ok ? krow(u) : sinkK);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kr[ks] = ok ? src[2 * ks + h] : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = ok ? src[2 * ks + h] : u32x4{0u, 0u, 0u, 0u};
   };
-  auto vload = [&](int c, u32x4 (&vr)[2]) __attribute__((always_inline)) {
+  auto vload = [&](int c, u32x4 (&vr)[VW]) __attribute__((always_inline)) {
     const int u = 32 * c + (tid >> 3);
-    vr[0] = vr[1] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < VW; ++j) vr[j] = u32x4{0u, 0u, 0u, 0u};
     if (u < n_win) {
-      const u32x4 *src = (const u32x4 *)(vrow(u) + 16 * (tid & 7));
-      vr[0] = src[0];
-      vr[1] = src[1];
+      const u32x4 *src = (const u32x4 *)(vrow(u) + D / 8 * (tid & 7));
+#pragma unroll
+      for (int j = 0; j < VW; ++j) vr[j] = src[j];
     }
   };
-  auto vstore = [&](int c, const u32x4 (&vr)[2]) __attribute__((always_inline)) {
-    const int tk = tid >> 3, cb = tid & 7; // token of the chunk, 16-channel block
+  auto vstore = [&](int c, const u32x4 (&vr)[VW]) __attribute__((always_inline)) {
+    const int tk = tid >> 3, cb = tid & 7; // token of the chunk, block of D/8 channels
     const int hh = tk >> 4, ks = (tk & 15) >> 3, e = tk & 7;
     uint16_t *V = (uint16_t *)&sm.V[c & 1][0][0][0];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t wd = k < 8 ? vr[0][k / 2] : vr[1][(k - 8) / 2];
+    for (int k = 0; k < D / 8; ++k) {
+      const uint32_t wd = vr[k / 8][(k % 8) / 2];
       const uint16_t val = (uint16_t)((k & 1) ? (wd >> 16) : (wd & 0xffffu));
-      const int c2 = 16 * cb + k;
+      const int c2 = D / 8 * cb + k;
       V[(((c2 >> 5) * 2 + ks) * 64 + (c2 & 31) + 32 * hh) * 8 + e] = val;
     }
   };
-  u32x4 kc[8], kn[8], vr[2];
+  u32x4 kc[KS], kn[KS], vr[VW];
   __syncthreads(); // every wave is done with R_V^T: the window buffers overlay it
   if (nchunk > 0) {
     vload(0, vr);
@@ -826,7 +844,7 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
     // S^T = K_win . q^T: A operand token tile_token(n) of the chunk
     v16f S = v16f{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kc[ks]), Qw[ks], S, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kc[ks]), Qw[ks], S, 0, 0, 0);
     float x[16], mxl = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -856,7 +874,7 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
       for (int J = 0; J < 4; ++J) {
         const v4f al = *(const v4f *)&sm.row[w][8 * J + 4 * h];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i) O[ct][4 * J + i] *= al[i];
       }
@@ -885,7 +903,7 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
         lo[e] = (__bf16)(y - (float)yh);
       }
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         const v8bf B = __builtin_bit_cast(v8bf, sm.V[c & 1][ct][ks][lane]);
         O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, B, O[ct], 0, 0, 0);
         O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, B, O[ct], 0, 0, 0);
@@ -895,7 +913,7 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
     if (c + 2 < nchunk) vload(c + 2, vr);
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kc[ks] = kn[ks];
+    for (int ks = 0; ks < KS; ++ks) kc[ks] = kn[ks];
   }
   // ---- normalise and store: register (J, i) holds row 8 J + 4 h + i,
   // channel 32 ct + n; the history part was weighted relative to M, the
@@ -911,9 +929,9 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
       const int rr = 8 * J + 4 * h + i;
       const int fo = ti.f0 + 32 * w + rr;
       if (32 * w + rr < ti.nrows) {
-        float *dst = out + ((size_t)(fo / a.g) * p.Hq + kv * a.g + fo % a.g) * kD + n;
+        float *dst = out + ((size_t)(fo / a.g) * p.Hq + kv * a.g + fo % a.g) * D + n;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) dst[32 * ct] = O[ct][4 * J + i] * il[i];
+        for (int ct = 0; ct < CT; ++ct) dst[32 * ct] = O[ct][4 * J + i] * il[i];
       }
     }
   }
@@ -921,16 +939,27 @@ __global__ __launch_bounds__(256, 2) void prefill_finish_kernel(PoolDev p, Prefi
 
 } // namespace
 
-size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S) {
-  const size_t qrec = (size_t)Hkv * NT * kWaves * 8 * 2 * 64 * 16;
+size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S, int d) {
+  const size_t qrec = (size_t)Hkv * NT * kWaves * (d / 16) * 2 * 64 * 16;
   const size_t qaux = (size_t)Hkv * NT * kAux * 4;
-  const size_t po = (size_t)Hkv * NT * S * kRows * kD * 4;
+  const size_t po = (size_t)Hkv * NT * S * kRows * d * 4;
   const size_t pml = (size_t)Hkv * NT * S * kRows * 2 * 4;
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   return al(qrec) + al(qaux) + al(po) + al(pml);
 }
 
-bool prefill_mfma_supported(const PoolDev &p) { return p.d == kD && (p.G == kD || p.G == 64) && !p.bf16_hist; }
+bool prefill_mfma_supported(const PoolDev &p) {
+  return (p.d == 128 || p.d == 64) && (p.G == p.d || (p.d == 128 && p.G == 64)) && !p.bf16_hist;
+}
+
+template <int D, int NG>
+static void launch_all(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, u32x4 *qrec,
+                       float *qaux, float *po, float *pml, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_qprep_kernel<D, NG>), dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
+  hipLaunchKernelGGL((prefill_hist_kernel<D, NG>), dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po,
+                     pml);
+  hipLaunchKernelGGL((prefill_finish_kernel<D>), dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, po, pml, out);
+}
 
 hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, void *ws,
                                hipStream_t s) {
@@ -938,20 +967,18 @@ hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uin
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   uint8_t *base = (uint8_t *)ws;
   u32x4 *qrec = (u32x4 *)base;
-  base += al((size_t)p.Hkv * a.NT * kWaves * 8 * 2 * 64 * 16);
+  base += al((size_t)p.Hkv * a.NT * kWaves * (p.d / 16) * 2 * 64 * 16);
   float *qaux = (float *)base;
   base += al((size_t)p.Hkv * a.NT * kAux * 4);
   float *po = (float *)base;
-  base += al((size_t)p.Hkv * a.NT * a.S * kRows * kD * 4);
+  base += al((size_t)p.Hkv * a.NT * a.S * kRows * p.d * 4);
   float *pml = (float *)base;
-  if (p.G == kD) {
-    hipLaunchKernelGGL(prefill_qprep_kernel<1>, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
-    hipLaunchKernelGGL(prefill_hist_kernel<1>, dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po, pml);
-  } else {
-    hipLaunchKernelGGL(prefill_qprep_kernel<2>, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
-    hipLaunchKernelGGL(prefill_hist_kernel<2>, dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po, pml);
-  }
-  hipLaunchKernelGGL(prefill_finish_kernel, dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, po, pml, out);
+  if (p.d == 64)
+    launch_all<64, 1>(p, a, q, out, qrec, qaux, po, pml, s);
+  else if (p.G == 128)
+    launch_all<128, 1>(p, a, q, out, qrec, qaux, po, pml, s);
+  else
+    launch_all<128, 2>(p, a, q, out, qrec, qaux, po, pml, s);
   return hipGetLastError();
 }
 

@@ -791,10 +791,9 @@ int oscar_pool_check(oscar_pool *p, void *stream) {
 }
 
 // Pools whose prefill attention runs on the matrix-core path (the same test
-// as prefill_mfma_supported, from the configuration).
-static bool prefill_mfma_config(const oscar_pool_config *c) {
-  return c->head_dim == 128 && !(c->flags & OSCAR_POOL_BF16_HISTORY);
-}
+// as prefill_mfma_supported, from the configuration): every INT2 history
+// (d 64 or 128, G 64 or 128 with G <= d).
+static bool prefill_mfma_config(const oscar_pool_config *c) { return !(c->flags & OSCAR_POOL_BF16_HISTORY); }
 
 int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, size_t *bytes) {
   int rc = validate_config(cfg);
@@ -804,7 +803,7 @@ int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, siz
   size_t need;
   if (prefill_mfma_config(cfg)) {
     const int NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
-    need = prefill_mfma_ws_bytes(Hkv, NT, prefill_mfma_splits(NT, Hkv));
+    need = prefill_mfma_ws_bytes(Hkv, NT, prefill_mfma_splits(NT, Hkv), cfg->head_dim);
   } else {
     const int tiles = (int)std::min<int64_t>(((int64_t)n_q * g + vg - 1) / vg, kMaxBatch);
     need = decode_ws_floats(Hkv * vg, cfg->head_dim, tiles, Hkv, kMaxSplits, vg) * sizeof(float);
@@ -836,7 +835,7 @@ int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *
     a.NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
     a.S = prefill_mfma_splits(a.NT, Hkv);
     a.qscale = softmax_scale * 1.4426950408889634f;
-    const size_t need = prefill_mfma_ws_bytes(Hkv, a.NT, a.S);
+    const size_t need = prefill_mfma_ws_bytes(Hkv, a.NT, a.S, p->dev.d);
     if (workspace_bytes < need)
       return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
     hipError_t e = launch_prefill_mfma(p->dev, a, q, out, workspace, (hipStream_t)stream);

@@ -265,8 +265,8 @@ hipError_t launch_prefill_attn(const PoolDev &p_virtual, const DecodeBatch &b, c
 // Rows (query, head) of a prefill tile.
 constexpr int kPrefillTile = 8;
 
-// Prefill attention on matrix cores (pools with d = 128, one scale group per
-// token, affine levels): the call's flat rows (query i, head hh of the kv
+// Prefill attention on matrix cores (INT2-history pools, d 64 or 128, one or
+// two scale groups per head row, affine or codebook levels): the call's flat rows (query i, head hh of the kv
 // head; index i g + hh) are cut in tiles of kPfTileRows, and each tile's
 // visible history pages in S splits.
 constexpr int kPfTileRows = 128;
@@ -282,7 +282,7 @@ inline int prefill_mfma_splits(int NT, int Hkv) {
   return want < 1 ? 1 : (want > 16 ? 16 : want);
 }
 bool prefill_mfma_supported(const PoolDev &p);
-size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S);
+size_t prefill_mfma_ws_bytes(int Hkv, int NT, int S, int d);
 hipError_t launch_prefill_mfma(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, void *ws,
                                hipStream_t s);
 

@@ -91,11 +91,11 @@ def test_single_query_equals_decode():
     assert ra <= TOL
 
 
-@pytest.mark.parametrize("shape", ["g4_d128_G128", "g16_d128_G128"])
+@pytest.mark.parametrize("shape", ["g4_d128_G128", "g16_d128_G128", "g8_d128_G64", "g2_d64_G64"])
 def test_long_context_chunk_with_split_plans(shape):
-    # 64 queries over 20,000 tokens: 32 (g 4) or 64 (g 16) tiles x 2 kv
-    # heads, far fewer pairs than block slots, so each tile's pages are cut
-    # into several splits and merged
+    # 64 queries over 20,000 tokens: 1 to 8 tiles of 128 rows x 2 kv heads,
+    # far fewer blocks than block slots, so each tile's pages are cut into
+    # several splits and merged
     w = _workload(shape, 1)
     L, n_q = 20000, 64
     RK, RV, cK, cV = harness.tables(w)
