@@ -50,8 +50,6 @@ inline void plan_splits(DecodeBatch &b, const int32_t *seq_ids, const std::vecto
   b.win_units = wu;
   b.fused = fused ? 1 : 0;
   b.direct = 0;
-  b.pf_g = 0;
-  b.pf_rows = 0;
   for (int e = 0; e < kMaxBatch; ++e) b.new_page[e] = -1;
   auto splits = [&](int e, int64_t P) {
     if (np[e] == 0) return 1; // window only

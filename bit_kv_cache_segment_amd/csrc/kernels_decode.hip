@@ -164,25 +164,6 @@ __device__ __forceinline__ int karg_u16(const uint16_t *a, int i) {
   return (int)((((const uint32_t *)a)[i >> 1] >> (16 * (i & 1))) & 0xffffu);
 }
 
-// Prefill tiles (b.pf_g > 0): virtual head v of entry e is flat row
-// f = pf_flat0[e] + v: query i = f / g (g = b.pf_g) at position
-// len - n_q + i, query head kv g + f % g.  Rows past the call's queries are
-// not real (position -1: they see nothing, and nothing of theirs is
-// written).
-struct PfRow {
-  int query, head, pos;
-  bool real;
-};
-__device__ __forceinline__ PfRow pf_row(const DecodeBatch &b, int e, int kv, int v) {
-  const int g = b.pf_g, f = b.pf_flat0[e] + v, i = f / g;
-  PfRow r;
-  r.query = i;
-  r.head = kv * g + f % g;
-  r.real = i < b.pf_rows;
-  r.pos = r.real ? b.len[e] - b.pf_rows + i : -1;
-  return r;
-}
-
 // A D x D fp32 rotation table in shared memory: 1 KB chunks of 256 / D
 // rows, each followed by 16 pad floats, so that rows of chunks whose index
 // differs mod 4 start 16 banks apart.
@@ -390,7 +371,7 @@ constexpr int win_groups() {
 // Window tokens of one (sequence, kv head) processed by NW waves: wave wi
 // takes the token groups wi, wi + NW, ... and leaves its (m, l, acc) in
 // sm.M[wi], sm.L[wi], sm.A[wi] (a block merge combines the NW waves).
-template <int D, int G, int GQ, int NW, bool PREFILL = false>
+template <int D, int G, int GQ, int NW>
 __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const DecodeBatch &b, const uint16_t *q,
                              float qscale, int e, int kv, int wi) {
   constexpr int LPT = D / 8, TPI = 64 / LPT, WG = win_groups<D, G, GQ, NW>();
@@ -400,18 +381,7 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
   const int seq = b.seq[e], L = b.len[e];
   const int n_sink = min(L, kSink), n_rec = min(max(L - kSink, 0), kRecent), n_win = n_sink + n_rec;
   const int n_hist = max(L - kWindow, 0);
-  int vpos[PREFILL ? GQ : 1]; // prefill: position of each head's query
-  if constexpr (PREFILL) {
-    // this wave's copy of the tile's query rows (zero for rows that are not real)
-    const int Hq_real = Hkv * b.pf_g;
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) vpos[h] = pf_row(b, e, kv, h).pos;
-    for (int idx = lane; idx < GQ * D / 2; idx += 64) {
-      const PfRow r = pf_row(b, e, kv, idx / (D / 2));
-      sm.q2[wi][idx / (D / 2)][idx % (D / 2)] =
-          r.real ? ((const uint32_t *)(q + ((size_t)r.query * Hq_real + r.head) * D))[idx % (D / 2)] : 0u;
-    }
-  } else {
+  {
     // this wave's copy of the query rows: no block barrier needed
     const uint32_t *src = (const uint32_t *)(q + ((size_t)karg_u16(b.row, e) * Hq + kv * GQ) * D);
     for (int idx = lane; idx < GQ * D / 2; idx += 64) sm.q2[wi][idx / (D / 2)][idx % (D / 2)] = src[idx];
@@ -449,9 +419,6 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
       if (k0 + i >= nk) break;
       const int u = (wi + NW * (k0 + i)) * TPI + ts;
       const bool ok = u < n_win;
-      // position of window token u (sink slot = position; recent slot j holds
-      // the position 64 + n_hist + ((j - n_hist) mod 256))
-      const int upos = u < n_sink ? u : kSink + n_hist + ((u - n_sink - n_hist) & (kRecent - 1));
       float vf[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -470,9 +437,7 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
           d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qw), d, false);
         }
         d = lanes_sum<LPT>(d);
-        bool vis = ok;
-        if constexpr (PREFILL) vis = vis && upos <= vpos[h];
-        const float sc = vis ? d * qscale : -INFINITY;
+        const float sc = ok ? d * qscale : -INFINITY;
         const bool jump = sc > m_ref[h] + kLazy;
         if (__any(jump)) {
           const float mn = jump ? sc : m_ref[h];
@@ -482,7 +447,7 @@ __device__ void window_waves(WinSmem<D, GQ, NW> &sm, const PoolDev &p, const Dec
           for (int j = 0; j < 8; ++j) acc[h][j] *= al;
           m_ref[h] = mn;
         }
-        const float pr = vis ? fast_exp2(sc - m_ref[h]) : 0.f;
+        const float pr = ok ? fast_exp2(sc - m_ref[h]) : 0.f;
         l_run[h] += pr;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pr, vf[j], acc[h][j]);
@@ -697,7 +662,7 @@ __device__ void fused_append_page(WinSmem<D, GQ, NW> &sm, const RTable<D> &RK_ld
 }
 
 // A block that holds only a pair's window: all its waves take part.
-template <int D, int G, int GQ, bool PREFILL = false>
+template <int D, int G, int GQ>
 __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
                              const uint16_t *q, float qscale, float *ws_win, float *out, const AppendIn &in, int e,
                              int kv) {
@@ -711,11 +676,10 @@ __device__ void window_block(WinSmem<D, GQ, main_waves(D, G, GQ)> &sm, const Poo
     if (w < 2) fused_append_slot<D, GQ, W>(sm, p, b, in, e, kv, w, threadIdx.x & 63);
     wait_count(&sm.app_slot_done, 2, p);
   }
-  window_waves<D, G, GQ, W, PREFILL>(sm, p, b, q, qscale, e, kv, w);
+  window_waves<D, G, GQ, W>(sm, p, b, q, qscale, e, kv, w);
   __syncthreads();
   block_merge_store<D, GQ, W>(sm.M, sm.L, sm.A, ws_win + ((size_t)e * p.Hq + kv * GQ) * (D + 2),
-                              !PREFILL && b.direct ? out + ((size_t)karg_u16(b.row, e) * p.Hq + kv * GQ) * D
-                                                   : nullptr);
+                              b.direct ? out + ((size_t)karg_u16(b.row, e) * p.Hq + kv * GQ) * D : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -839,7 +803,7 @@ __device__ __forceinline__ void load_page(PageRegs<D, G> &pr, const uint8_t *blk
 template <int D, int G, int GQ>
 constexpr int kPrefetch = (D == 64 || (G == D && GQ <= 4)) ? 2 : 1;
 
-template <int D, int G, int GQ, bool PREFILL = false, bool LUT = false>
+template <int D, int G, int GQ, bool LUT = false>
 __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, const PoolDev &p, const DecodeBatch &b,
                               float *ws_hist, float *ws_win, float *out, const uint16_t *q, float qscale,
                               const AppendIn &in, int slot, int e, int kv, int p0, int p1, bool with_window) {
@@ -872,26 +836,14 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // evicts, the pair's last page (the plan keeps it in this split) is taken
   // after the loop, once the append has written it.
   const bool fused_evict = b.fused && with_window && b.len[e] - 1 >= kWindow;
-  int pf = fused_evict ? np - 1 : full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
-  if constexpr (PREFILL) {
-    // pages every query of the tile sees whole (the tile's first query has
-    // the smallest position); the later ones go to the masked pass
-    const int fv = prefill_visible_hist(pf_row(b, e, kv, 0).pos, n_hist) / kPage;
-    pf = max(p0, min(pf, fv));
-  }
+  const int pf = fused_evict ? np - 1 : full_pages_end(n_hist, p0, p1); // p0 <= pf <= p1
 
   // ---- prologue: R_K (direct to shared memory; no such load may be
   // outstanding in the page loop, where the compiler would order every
   // shared-memory access after it), the query rows and the first segment's
   // page ids are staged; the block builds the query record.
   stage_table<D>(sm.R, p.RK + (size_t)kv * D * D, w, W, lane);
-  if constexpr (PREFILL) {
-    const int Hq_real = p.Hkv * b.pf_g;
-    for (int idx = tid; idx < GQ * D; idx += NT) {
-      const PfRow rw = pf_row(b, e, kv, idx / D);
-      sm.u.pre.qT[idx % D][idx / D] = rw.real ? bf16f(q[((size_t)rw.query * Hq_real + rw.head) * D + idx % D]) : 0.f;
-    }
-  } else {
+  {
     const uint16_t *qrow = q + ((size_t)karg_u16(b.row, e) * p.Hq + kv * GQ) * D;
     for (int idx = tid; idx < GQ * D; idx += NT) sm.u.pre.qT[idx % D][idx / D] = bf16f(qrow[idx]);
   }
@@ -954,7 +906,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       if (w < 2) fused_append_slot<D, GQ, WW>(sm.win, p, b, in, e, kv, w, lane);
       wait_count(&sm.win.app_slot_done, 2, p);
     }
-    window_waves<D, G, GQ, WW, PREFILL>(sm.win, p, b, q, qscale, e, kv, w);
+    window_waves<D, G, GQ, WW>(sm.win, p, b, q, qscale, e, kv, w);
     if (b.fused && w < 2) fused_append_page<D, G, GQ, WW>(sm.win, sm.R, p, b, e, kv, w, lane);
   }
   auto stage = [&](int s0, int sf) __attribute__((always_inline)) {
@@ -999,13 +951,6 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // literals here.
   const uint32_t vsel_zero = 0x0C000C00u | __builtin_amdgcn_mbcnt_lo(0u, 0u);
 
-  // prefill: position of the query of each row tile's head in this lane
-  // (rows rt * 4 + r); tokens after it are masked on the masked pages
-  int vpos[PREFILL ? RT : 1];
-  if constexpr (PREFILL) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) vpos[rt] = pf_row(b, e, kv, min(rt * 4 + r, GQ - 1)).pos;
-  }
   float m_run[RT], thr[RT], l_run[RT], zs[RT][NG];
   v4f acc[NJ];
 #pragma unroll
@@ -1052,7 +997,6 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
             cacc[rt][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[rt][mi], B, cacc[rt][g], 0, 0, 0);
         }
         const bool tvalid = full || 4 * n + T < ntok;
-        const int tpos = kSink + pi * kPage + 4 * n + T; // position of this lane's token
   #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           float l = 0.f;
@@ -1073,8 +1017,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
               l = fmaf(f16lo(sz), dv, fmaf(f16hi(sz), qsum[rt][g], l));
             }
           }
-          bool vis = tvalid && (GQ >= 4 || rt * 4 + r < GQ);
-          if constexpr (PREFILL) vis = vis && (full || tpos <= vpos[rt]);
+          const bool vis = tvalid && (GQ >= 4 || rt * 4 + r < GQ);
           lg[rt][T] = vis ? l : -INFINITY;
         }
       }
@@ -1237,15 +1180,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
       }
     }
   }
-  if (PREFILL && w == W - 1) {
-    // prefill: the pages some query of the tile sees only in part (and the
-    // sequence's last page), with per-row position masks
-    for (int pi = pf; pi < p1; ++pi) {
-      PageRegs<D, G> last;
-      load_page<D, G>(last, p.pages + (size_t)ptab[pi] * hstride + hoff, true, p.block_bytes, n, r);
-      page_step(last, pi, false);
-    }
-  } else if (pf < p1 && w == W - 1) {
+  if (pf < p1 && w == W - 1) {
     int id;
     if (fused_evict) {
       wait_count(&sm.win.app_page_done, 2, p);
@@ -1350,7 +1285,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // of the history and window sums (their maxima against the joint one),
   // divided by the joint denominator; wf[ww][h]: each window wave's weight.
   static_assert(2 + WW <= W, "the direct-output factors fit in the rescale rows");
-  const bool direct = !PREFILL && b.direct;
+  const bool direct = b.direct;
   float(*dir)[16] = sm.alpha; // free after the page loop
   float(*wf)[16] = sm.alpha + 2;
   if (tid < GQ) {
@@ -1401,7 +1336,7 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
 // read together with the window partial, before the pair's own split count
 // is known; slots at or past it are read (in bounds) but never used.  One
 // thread per (head, channel) output.
-template <int D, int GQ, int NT, bool PREFILL = false>
+template <int D, int GQ, int NT>
 __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, int e, int kv,
                            int tid) {
   constexpr int SB = 4; // splits per batch of loads
@@ -1449,13 +1384,7 @@ __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, c
       fetch(s0);
       fold(s0);
     }
-    if constexpr (PREFILL) {
-      // the tile's head h is query row r.query, query head r.head
-      const PfRow rw = pf_row(b, e, kv, h);
-      if (rw.real) out[((size_t)rw.query * (Hkv * b.pf_g) + rw.head) * D + c] = a / l;
-    } else {
-      out_pair[idx] = a / l;
-    }
+    out_pair[idx] = a / l;
   }
 }
 
@@ -1464,15 +1393,15 @@ __device__ void merge_pair(const PoolDev &p, const DecodeBatch &b, float *out, c
 template <int D, int GQ>
 constexpr int merge_threads() { return GQ * D < 1024 ? GQ * D : 1024; }
 
-template <int D, int GQ, bool PREFILL = false>
+template <int D, int GQ>
 __global__ __launch_bounds__((merge_threads<D, GQ>())) void decode_merge_kernel(PoolDev p, DecodeBatch b, float *__restrict__ out,
                                                                      const float *__restrict__ ws) {
   // grid (sequence, kv head): the pair is known before any kernel argument
   // arrives, so all of them load in one round
-  merge_pair<D, GQ, merge_threads<D, GQ>(), PREFILL>(p, b, out, ws, blockIdx.x, blockIdx.y, threadIdx.x);
+  merge_pair<D, GQ, merge_threads<D, GQ>()>(p, b, out, ws, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
-template <int D, int G, int GQ, bool PREFILL = false, bool LUT = false>
+template <int D, int G, int GQ, bool LUT = false>
 __global__ __launch_bounds__(64 * main_waves(D, G, GQ)) __attribute__((amdgpu_waves_per_eu(main_occupancy(D, G, GQ))))
 void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q, float qscale,
                         float *__restrict__ ws, float *__restrict__ out, AppendIn in) {
@@ -1484,23 +1413,17 @@ void decode_main_kernel(PoolDev p, DecodeBatch b, const uint16_t *__restrict__ q
   int s, e, kv;
   block_split(b, Hkv, blk, s, e, kv);
   const int S = karg_u8(b.nsplit, e);
-  int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
-  if constexpr (PREFILL) {
-    // the pages up to the tile's last query (the host plans with this count)
-    const int last = (min(b.pf_flat0[e] + GQ, b.pf_rows * b.pf_g) - 1) / b.pf_g; // the tile's last query
-    np = (prefill_visible_hist(b.len[e] - b.pf_rows + last, max(b.len[e] - kWindow, 0)) + kPage - 1) / kPage;
-  }
+  const int np = (max(b.len[e] - kWindow, 0) + kPage - 1) / kPage;
   int p0, p1;
   split_range(np, S, s, b.win_units, p0, p1);
   // split partial slot: the pair's splits are consecutive, stride the
   // batch's largest split count (launch order is by split count, descending)
   const int slot = (e * Hkv + kv) * karg_u8(b.nsplit, 0) + s;
   if (p0 < p1)
-    history_block<D, G, GQ, PREFILL, LUT>(sm.h, p, b, ws_hist, ws_win, out, q, qscale, in, slot, e, kv, p0, p1,
-                                          s == S - 1);
+    history_block<D, G, GQ, LUT>(sm.h, p, b, ws_hist, ws_win, out, q, qscale, in, slot, e, kv, p0, p1, s == S - 1);
   else if (s == S - 1) {
-    window_block<D, G, GQ, PREFILL>(sm.w, p, b, q, qscale, ws_win, out, in, e, kv);
-    if (!PREFILL && b.direct) return;
+    window_block<D, G, GQ>(sm.w, p, b, q, qscale, ws_win, out, in, e, kv);
+    if (b.direct) return;
     // this split holds no pages: an empty history partial for the merge
     float *dst = ws_hist + (size_t)slot * GQ * (D + 2);
     for (int idx = threadIdx.x; idx < GQ * (D + 2); idx += 64 * W) dst[idx] = idx % (D + 2) == D ? -INFINITY : 0.f;
@@ -1514,7 +1437,7 @@ hipError_t decode_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q
   // Timed launches take their start/stop timestamps from the dispatch itself
   // (no extra packets between kernels).
   if (p.lut)
-    hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ, false, true>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0,
+    hipExtLaunchKernelGGL((decode_main_kernel<D, G, GQ, true>), dim3(blocks), dim3(64 * main_waves(D, G, GQ)), 0,
                           s, tm.on ? tm.ev[0] : nullptr, tm.on ? tm.ev[1] : nullptr, 0, p, b, q, scale * kLog2e, ws,
                           out, in);
   else
@@ -1544,38 +1467,17 @@ hipError_t decode_g(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, f
   return hipErrorInvalidValue;
 }
 
-template <int D, int G, int GQ>
-hipError_t prefill_attn_impl(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
-                             float *ws, hipStream_t s) {
-  const AppendIn none{nullptr, nullptr};
-  if (p.lut)
-    hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)),
-                       0, s, p, b, q, scale * kLog2e, ws, out, none);
-  else
-    hipLaunchKernelGGL((decode_main_kernel<D, G, GQ, true>), dim3(b.hist_blocks), dim3(64 * main_waves(D, G, GQ)), 0,
-                       s, p, b, q, scale * kLog2e, ws, out, none);
-  hipLaunchKernelGGL((decode_merge_kernel<D, GQ, true>), dim3(b.n, p.Hkv), dim3(merge_threads<D, GQ>()), 0, s, p, b,
-                     out, (const float *)ws);
-  return hipGetLastError();
-}
-
-template <int D, int G>
-hipError_t prefill_attn_g(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
-                          float *ws, hipStream_t s) {
-  return prefill_attn_impl<D, G, kPrefillTile>(p, b, q, out, scale, ws, s);
-}
-
 template <int D, int G>
 int blocks_per_cu_g(const PoolDev &p) {
   int nb = 0;
   hipError_t e = hipErrorInvalidValue;
   if (p.lut) {
     switch (p.Hq / p.Hkv) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 1, false, true>, 64 * main_waves(D, G, 1), 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 2, false, true>, 64 * main_waves(D, G, 2), 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 4, false, true>, 64 * main_waves(D, G, 4), 0); break;
-    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 8, false, true>, 64 * main_waves(D, G, 8), 0); break;
-    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 16, false, true>, 64 * main_waves(D, G, 16), 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 1, true>, 64 * main_waves(D, G, 1), 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 2, true>, 64 * main_waves(D, G, 2), 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 4, true>, 64 * main_waves(D, G, 4), 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 8, true>, 64 * main_waves(D, G, 8), 0); break;
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, 16, true>, 64 * main_waves(D, G, 16), 0); break;
     }
     return e == hipSuccess ? nb : 0;
   }
@@ -1589,25 +1491,7 @@ int blocks_per_cu_g(const PoolDev &p) {
   return e == hipSuccess ? nb : 0;
 }
 
-template <int D, int G>
-int prefill_blocks_per_cu_g(const PoolDev &p) {
-  int nb = 0;
-  const hipError_t e =
-      p.lut ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, kPrefillTile, true, true>,
-                                                           64 * main_waves(D, G, kPrefillTile), 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_main_kernel<D, G, kPrefillTile, true>,
-                                                           64 * main_waves(D, G, kPrefillTile), 0);
-  return e == hipSuccess ? nb : 0;
-}
-
 } // namespace
-
-int prefill_blocks_per_cu(const PoolDev &p) {
-  if (p.d == 128 && p.G == 128) return prefill_blocks_per_cu_g<128, 128>(p);
-  if (p.d == 128 && p.G == 64) return prefill_blocks_per_cu_g<128, 64>(p);
-  if (p.d == 64 && p.G == 64) return prefill_blocks_per_cu_g<64, 64>(p);
-  return 0;
-}
 
 int decode_main_blocks_per_cu(const PoolDev &p) {
   if (p.d == 128 && p.G == 128) return blocks_per_cu_g<128, 128>(p);
@@ -1638,14 +1522,6 @@ hipError_t launch_decode_merge(const PoolDev &p, const DecodeBatch &b, float *ou
                                const KernelTimer &tg) {
   if (p.d == 128) return merge_d<128>(p, b, out, ws, s, tg);
   if (p.d == 64) return merge_d<64>(p, b, out, ws, s, tg);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_prefill_attn(const PoolDev &p, const DecodeBatch &b, const uint16_t *q, float *out, float scale,
-                               float *ws, hipStream_t s) {
-  if (p.d == 128 && p.G == 128) return prefill_attn_g<128, 128>(p, b, q, out, scale, ws, s);
-  if (p.d == 128 && p.G == 64) return prefill_attn_g<128, 64>(p, b, q, out, scale, ws, s);
-  if (p.d == 64 && p.G == 64) return prefill_attn_g<64, 64>(p, b, q, out, scale, ws, s);
   return hipErrorInvalidValue;
 }
 

@@ -191,8 +191,7 @@ struct oscar_pool {
   bool host_only;
   // Lloyd-Max pools: the codebook (uint32 per kv head, K then V), once set
   std::vector<uint32_t> codebook;
-  int decode_slots = 768;  // resident decode blocks on the device
-  int prefill_slots = 256; // resident prefill-attention blocks
+  int decode_slots = 768; // resident decode blocks on the device
   std::vector<int32_t> len;
   std::vector<std::vector<int32_t>> table;
   std::vector<int32_t> free_list; // pages [free_head, end) are free, front first
@@ -380,12 +379,6 @@ int oscar_pool_create(const oscar_pool_config *cfg, void *device_buf, size_t byt
       return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "querying the decode occupancy");
     }
     p->decode_slots = cus * per_cu;
-    const int pf_per_cu = prefill_blocks_per_cu(D);
-    if (pf_per_cu <= 0) {
-      delete p;
-      return hip_fail(hipErrorInvalidValue, "querying the prefill occupancy");
-    }
-    p->prefill_slots = cus * pf_per_cu;
     // set-up of the static decode workspace on this device (its address is
     // looked up here, once per device, not in the step that uses it)
     void *ws = nullptr;
@@ -790,25 +783,15 @@ int oscar_pool_check(oscar_pool *p, void *stream) {
   return rc ? rc : ok();
 }
 
-// Pools whose prefill attention runs on the matrix-core path (the same test
-// as prefill_mfma_supported, from the configuration): every INT2 history
-// (d 64 or 128, G 64 or 128 with G <= d).
-static bool prefill_mfma_config(const oscar_pool_config *c) { return !(c->flags & OSCAR_POOL_BF16_HISTORY); }
-
+// The workspace of the matrix-core launches (prefill_mfma_ws_bytes): it
+// depends on the configuration and n_q only.
 int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, size_t *bytes) {
   int rc = validate_config(cfg);
   if (rc) return rc;
   if (!bytes || n_q < 0) return fail(OSCAR_EINVAL, "bad arguments");
-  const int Hkv = cfg->num_kv_heads, g = cfg->num_q_heads / Hkv, vg = kPrefillTile;
-  size_t need;
-  if (prefill_mfma_config(cfg)) {
-    const int NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
-    need = prefill_mfma_ws_bytes(Hkv, NT, prefill_mfma_splits(NT, Hkv), cfg->head_dim);
-  } else {
-    const int tiles = (int)std::min<int64_t>(((int64_t)n_q * g + vg - 1) / vg, kMaxBatch);
-    need = decode_ws_floats(Hkv * vg, cfg->head_dim, tiles, Hkv, kMaxSplits, vg) * sizeof(float);
-  }
-  *bytes = need;
+  const int Hkv = cfg->num_kv_heads, g = cfg->num_q_heads / Hkv;
+  const int NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
+  *bytes = prefill_mfma_ws_bytes(Hkv, NT, prefill_mfma_splits(NT, Hkv), cfg->head_dim);
   return ok();
 }
 
@@ -824,59 +807,22 @@ int oscar_prefill_attn(oscar_pool *p, int32_t seq, int32_t n_q, const uint16_t *
   if (!q || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
   if (!std::isfinite(softmax_scale)) return fail(OSCAR_EINVAL, "softmax_scale is not finite");
   const int Hkv = p->cfg.num_kv_heads, d = p->cfg.head_dim, g = p->cfg.num_q_heads / Hkv;
-  if (prefill_mfma_supported(p->dev)) {
-    // matrix-core path: tiles of kPfTileRows rows, S splits each
-    PrefillArgs a;
-    a.seq = seq;
-    a.L = L;
-    a.n_q = n_q;
-    a.g = g;
-    a.n_hist = std::max(0, L - kWindow);
-    a.NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
-    a.S = prefill_mfma_splits(a.NT, Hkv);
-    a.qscale = softmax_scale * 1.4426950408889634f;
-    const size_t need = prefill_mfma_ws_bytes(Hkv, a.NT, a.S, p->dev.d);
-    if (workspace_bytes < need)
-      return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
-    hipError_t e = launch_prefill_mfma(p->dev, a, q, out, workspace, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
-    return ok();
-  }
-  const int vg = kPrefillTile;
-  const int64_t rows = (int64_t)n_q * g;
-  const int tiles = (int)((rows + vg - 1) / vg);
-  const int n_hist = std::max(0, L - kWindow);
-  PoolDev pv = p->dev;
-  pv.Hq = Hkv * vg; // the tiles' heads
-  // Each tile is one "sequence" of the decode plan, planned on the pages up
-  // to its last query (a length whose history is exactly those pages).
-  std::vector<DecodeBatch> batches;
-  size_t need = 0;
-  for (int t0 = 0; t0 < tiles; t0 += kMaxBatch) {
-    DecodeBatch b;
-    b.n = std::min(kMaxBatch, tiles - t0);
-    std::vector<int> plan_len(b.n);
-    std::vector<int32_t> ids(b.n, seq);
-    for (int e = 0; e < b.n; ++e) {
-      const int last = (int)((std::min<int64_t>((int64_t)(t0 + e + 1) * vg, rows) - 1) / g); // last query
-      plan_len[e] = kWindow + prefill_visible_hist(L - n_q + last, n_hist);
-    }
-    plan_splits(b, ids.data(), plan_len, Hkv, p->prefill_slots, window_units(d, p->cfg.group_size));
-    for (int i = 0; i < b.n; ++i) {
-      b.pf_flat0[i] = (t0 + b.row[i]) * vg;
-      b.len[i] = L;
-    }
-    b.pf_g = g;
-    b.pf_rows = n_q;
-    need = std::max(need, decode_ws_floats(pv.Hq, d, b.n, Hkv, b.nsplit[0], vg) * sizeof(float));
-    batches.push_back(b);
-  }
+  if (!prefill_mfma_supported(p->dev)) return fail(OSCAR_EINVAL, "no prefill kernel for d = %d, G = %d", d, p->cfg.group_size);
+  // tiles of kPfTileRows (query, head) rows per kv head, S splits each
+  PrefillArgs a;
+  a.seq = seq;
+  a.L = L;
+  a.n_q = n_q;
+  a.g = g;
+  a.n_hist = std::max(0, L - kWindow);
+  a.NT = (int)(((int64_t)n_q * g + kPfTileRows - 1) / kPfTileRows);
+  a.S = prefill_mfma_splits(a.NT, Hkv);
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  const size_t need = prefill_mfma_ws_bytes(Hkv, a.NT, a.S, d);
   if (workspace_bytes < need)
     return fail(OSCAR_EINVAL, "workspace of %zu bytes < %zu required", workspace_bytes, need);
-  for (const DecodeBatch &b : batches) {
-    hipError_t e = launch_prefill_attn(pv, b, q, out, softmax_scale, (float *)workspace, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
-  }
+  hipError_t e = launch_prefill_mfma(p->dev, a, q, out, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   return ok();
 }
 

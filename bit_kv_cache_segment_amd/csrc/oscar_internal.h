@@ -162,17 +162,7 @@ struct DecodeBatch {
   // Every pair of the launch has one split: its block writes the output
   // rows itself and no merge launch follows (INT2 decode only).
   int32_t direct;
-  // Prefill attention (oscar_prefill_attn): pf_g > 0 is the pool's query
-  // heads per kv head and pf_rows the call's query count n_q.  The call's
-  // rows (query i, head hh of the kv head), flat index i g + hh, are cut in
-  // tiles of 8; an entry is a tile (pf_flat0: its first flat row) whose rows
-  // act as the "heads" of one pair, each seeing positions up to its query's
-  // own (query i at position len - n_q + i).
-  int32_t pf_g, pf_rows;
-  union {
-    int32_t new_page[kMaxBatch];
-    int32_t pf_flat0[kMaxBatch];
-  };
+  int32_t new_page[kMaxBatch];
 };
 
 // History tokens (from the start of the history) visible to a prefill
@@ -253,17 +243,8 @@ hipError_t launch_decode_bf16(const PoolDev &p, const DecodeBatch &b, const uint
                               hipStream_t s, const KernelTimer &t);
 hipError_t launch_decode_merge(const PoolDev &p, const DecodeBatch &b, float *out, const float *ws, hipStream_t s,
                                const KernelTimer &t);
-// Resident prefill-attention blocks per compute unit (pool's real heads).
-int prefill_blocks_per_cu(const PoolDev &p);
 // Resident decode_main blocks per compute unit for this pool's shape.
 int decode_main_blocks_per_cu(const PoolDev &p);
-
-// Prefill attention launch (b.pf_g > 0): decode machinery over query tiles;
-// p_virtual is the pool view with Hq = Hkv x (tile heads).
-hipError_t launch_prefill_attn(const PoolDev &p_virtual, const DecodeBatch &b, const uint16_t *q, float *out,
-                               float scale, float *ws, hipStream_t s);
-// Rows (query, head) of a prefill tile.
-constexpr int kPrefillTile = 8;
 
 // Prefill attention on matrix cores (INT2-history pools, d 64 or 128, one or
 // two scale groups per head row, affine or codebook levels): the call's flat rows (query i, head hh of the kv

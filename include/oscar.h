@@ -268,12 +268,10 @@ int oscar_prefill_workspace_bytes(const oscar_pool_config *cfg, int32_t n_q, siz
  * chunk's queries.
  *   q:   device bf16 [n_q][Hq][d];   out: device fp32 [n_q][Hq][d];
  *   workspace: device, >= oscar_prefill_workspace_bytes(cfg, n_q) bytes.
- * The (query, head) rows of each kv head are cut in tiles: 128 rows on the
- * matrix-core path (pools with head_dim 128, any group size, affine or
- * Lloyd-Max levels: query preparation, history and finish launches), else
- * 8 rows,
- * which the decode kernels treat as the heads of one (sequence, kv head)
- * pair; each row is masked past its own query's position.
+ * The (query, head) rows of each kv head are cut in tiles of 128 rows
+ * (every INT2 pool shape, affine or Lloyd-Max levels: query preparation,
+ * history and finish launches on the matrix cores); each row is masked
+ * past its own query's position.
  * Errors: EINVAL (bad seq, n_q outside [1, min(L, 65535)], NULL, workspace
  * too small, host-only pool), EHIP. */
 int oscar_prefill_attn(oscar_pool *pool, int32_t seq, int32_t n_q, const uint16_t *q,
