@@ -57,6 +57,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 128;       // flat rows per tile (4 waves x 32)
 constexpr int kWaves = 4;
+constexpr int kPfTilesPerBlock = 2; // tiles whose rows share each staged history page
 constexpr int kQBits = 14;       // |a| 2^E < 2^kQBits: fp16 hi/lo parts stay finite
 constexpr float kLazyPf = 8.f;   // log2 headroom of the lazy softmax reference
 // Per tile, beside the query records: the rows' sums of a for each of up to
@@ -253,30 +254,33 @@ template <int D>
 struct PageSlot {
   u32x4 K[2][D / 16][64];        // [tile][k-step][lane]: 8 fp16 K code values (A operand)
   u32x4 V[D / 32][2][2][64];     // [channel tile][tile][k-step][lane]: 8 fp16 V code values (B operand)
-  float par[8][64];              // per token, channel group g: [2g] s_K 2^(24-E), [2g+1] z_K,
-                                 // [4+2g] s_V 2^pv_shift 4^-e, [5+2g] z_V
+  float par[8 + 2 * kPfTilesPerBlock][64]; // per token, channel group g: [2g+1] z_K, [4+2g] s_V 2^pv_shift
+                                           // 4^-e, [5+2g] z_V; [8+2w+g] s_K 2^(24-E) for tile w of the block
 };
-template <int D>
+template <int D, int NW>
 struct HistSmemPf {
   PageSlot<D> slot[2];
-  float row[kWaves][2][32]; // per-wave row broadcast (rescale factors, zero sums)
+  float row[NW][2][32]; // per-wave row broadcast (rescale factors, zero sums)
 };
 
-// Raw words of one page a thread stages: K and V code dwords tid + 256 j
-// (4 d of each in a page block), and one parameter dword.
-template <int D>
+// Raw words of one page a thread of NTH stages: K and V code dwords
+// tid + NTH j (4 d of each in a page block), and one parameter dword.
+template <int D, int NTH>
 struct PageRaw {
-  uint32_t k[D / 64], v[D / 64], par;
+  static constexpr int KW = (4 * D + NTH - 1) / NTH;
+  uint32_t k[KW], v[KW], par;
 };
 
 // npar = 128 NG: the K then V (scale, zero) dwords of the page, token-major
-template <int D>
-__device__ __forceinline__ void load_raw(PageRaw<D> &r, const uint8_t *blk, int tid, int npar) {
+template <int D, int NTH>
+__device__ __forceinline__ void load_raw(PageRaw<D, NTH> &r, const uint8_t *blk, int tid, int npar) {
   const uint32_t *w = (const uint32_t *)blk;
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    r.k[j] = __builtin_nontemporal_load(w + tid + 256 * j);
-    r.v[j] = __builtin_nontemporal_load(w + 4 * D + tid + 256 * j);
+  for (int j = 0; j < PageRaw<D, NTH>::KW; ++j) {
+    const int i = tid + NTH * j;
+    const bool in = (4 * D) % NTH == 0 || i < 4 * D;
+    r.k[j] = in ? __builtin_nontemporal_load(w + i) : 0u;
+    r.v[j] = in ? __builtin_nontemporal_load(w + 4 * D + i) : 0u;
   }
   // K params at byte 32 d + 4 (NG t + g), V params 256 NG bytes later
   r.par = tid < npar ? __builtin_nontemporal_load(w + 8 * D + tid) : 0u;
@@ -336,19 +340,25 @@ __device__ __forceinline__ float f16lo(uint32_t b) { return (float)__builtin_bit
 __device__ __forceinline__ float f16hi(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16)); }
 
 // Codebook pools: a level is z + (L / 64) s, so both scales carry 1/64.
-template <int D, int NG>
-__device__ __forceinline__ void stage_page(PageSlot<D> &s, const PageRaw<D> &r, int tid, int ntok, float kscale,
-                                           float vscale, bool lut, uint32_t lk, uint32_t lv) {
+template <int D, int NG, int NTH>
+__device__ __forceinline__ void stage_page(PageSlot<D> &s, const PageRaw<D, NTH> &r, int tid, int ntok,
+                                           const float (&kscale)[kPfTilesPerBlock], float vscale, bool lut, uint32_t lk,
+                                           uint32_t lv) {
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    stage_k<D>(s, tid + 256 * j, r.k[j], lut, lk);
-    stage_v<D>(s, tid + 256 * j, r.v[j], lut, lv);
+  for (int j = 0; j < PageRaw<D, NTH>::KW; ++j) {
+    const int i = tid + NTH * j;
+    if ((4 * D) % NTH == 0 || i < 4 * D) {
+      stage_k<D>(s, i, r.k[j], lut, lk);
+      stage_v<D>(s, i, r.v[j], lut, lv);
+    }
   }
   if (tid < 64 * NG) {
     // tokens past the history hold no data: their terms are zero
     const int t = tid / NG, g = tid % NG;
     const bool ok = t < ntok;
-    s.par[2 * g][t] = ok ? f16lo(r.par) * (lut ? kscale * 0.015625f : kscale) : 0.f;
+    const float sk = lut ? f16lo(r.par) * 0.015625f : f16lo(r.par);
+#pragma unroll
+    for (int wt = 0; wt < kPfTilesPerBlock; ++wt) s.par[8 + 2 * wt + g][t] = ok ? sk * kscale[wt] : 0.f;
     s.par[2 * g + 1][t] = ok ? f16hi(r.par) : 0.f;
   } else if (tid < 128 * NG) {
     const int t = (tid - 64 * NG) / NG, g = (tid - 64 * NG) % NG;
@@ -359,34 +369,48 @@ __device__ __forceinline__ void stage_page(PageSlot<D> &s, const PageRaw<D> &r, 
   }
 }
 
-template <int D, int NG>
-__global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, PrefillArgs a, const u32x4 *qrec,
-                                                              const float *qaux, float *part_o, float *part_ml) {
+// TW consecutive tiles per block (4 TW waves; a missing last tile's waves
+// only stage): every staged page serves 128 TW rows.
+template <int D, int NG, int TW>
+__global__ __launch_bounds__(256 * TW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_hist_kernel(
+    PoolDev p, PrefillArgs a, const u32x4 *qrec, const float *qaux, float *part_o, float *part_ml) {
   constexpr int KS = D / 16, CT = D / 32; // k-steps of 16 channels, tiles of 32 channels
-  __shared__ HistSmemPf<D> sm;
+  constexpr int NTH = 256 * TW;
+  static_assert(TW == kPfTilesPerBlock, "the staged K scales are laid out for kPfTilesPerBlock tiles");
+  __shared__ HistSmemPf<D, kWaves * TW> sm;
   const int kv = blockIdx.y;
-  const int T = a.NT - 1 - (int)blockIdx.x / a.S, s = (int)blockIdx.x % a.S; // later tiles (more pages) first
+  const int NTP = (a.NT + TW - 1) / TW;
+  const int TP = NTP - 1 - (int)blockIdx.x / a.S, s = (int)blockIdx.x % a.S; // later tiles (more pages) first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
-  const TileInfo ti = tile_info(a, T);
+  const int wl = w % kWaves;                 // wave in its tile
+  const int T = TW * TP + w / kWaves;        // this wave's tile
+  const bool have = T < a.NT;
+  const int T0 = TW * TP, T1 = min(TW * TP + TW - 1, a.NT - 1); // the block's first and last tiles
+  const TileInfo ti = tile_info(a, have ? T : T0);
   const int n_hist = a.n_hist;
-  const int vis_last = prefill_visible_hist(ti.pos1, n_hist);
-  const int pe = (vis_last + kPage - 1) / kPage;               // pages some row sees
-  const int fv = prefill_visible_hist(ti.pos0, n_hist) / kPage; // pages every row sees whole
+  const int vis_last = prefill_visible_hist(tile_info(a, T1).pos1, n_hist);
+  const int pe = (vis_last + kPage - 1) / kPage;                            // pages some row sees
+  const int fv = prefill_visible_hist(tile_info(a, T0).pos0, n_hist) / kPage; // pages every row sees whole
   const int p0 = (int)((long)s * pe / a.S), p1 = (int)((long)(s + 1) * pe / a.S);
 
   // this lane's row (S^T column n)
-  const int fr = 32 * w + n;
-  const bool real = fr < ti.nrows;
+  const int fr = 32 * wl + n;
+  const bool real = have && fr < ti.nrows;
   const int vis = real ? prefill_visible_hist(a.L - a.n_q + (ti.f0 + fr) / a.g, n_hist) : 0;
-  const float *aux = qaux + ((size_t)kv * a.NT + T) * kAux;
+  const float *aux = qaux + ((size_t)kv * a.NT + (have ? T : T0)) * kAux;
   const float qsum = aux[fr], qsum1 = NG == 2 ? aux[kRows + fr] : 0.f; // per channel group
-  const float kscale = aux[2 * kRows]; // 2^(24 - E)
+  // 2^(24 - E) of each tile of the block (E per tile; a missing tile repeats the last)
+  float kscale[kPfTilesPerBlock];
+#pragma unroll
+  for (int wt = 0; wt < kPfTilesPerBlock; ++wt)
+    kscale[wt] = qaux[((size_t)kv * a.NT + min(T0 + wt, T1)) * kAux + 2 * kRows];
+  const int skr = 8 + 2 * (w / kWaves); // this wave's row of K scales in the staged parameters
   const float vscale = ldexpf(1.f, p.pv_shift);
   const bool lut = p.lut != 0;
   const uint32_t lutK = lut ? p.codebook[kv] : 0u, lutV = lut ? p.codebook[p.Hkv + kv] : 0u;
   v8h Qh[KS], Ql[KS];
   {
-    const u32x4 *src = qrec + (((size_t)kv * a.NT + T) * kWaves + w) * (KS * 2 * 64);
+    const u32x4 *src = qrec + (((size_t)kv * a.NT + (have ? T : T0)) * kWaves + wl) * (KS * 2 * 64);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Qh[ks] = __builtin_bit_cast(v8h, src[(ks * 2 + 0) * 64 + lane]);
@@ -403,11 +427,11 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   auto page_ptr = [&](int pi) { return p.pages + (size_t)ptab[pi] * hstride + hoff; };
   auto ntok_of = [&](int pi) { return min(kPage, n_hist - pi * kPage); };
 
-  PageRaw<D> ra, rb;
+  PageRaw<D, NTH> ra, rb;
   if (p0 < p1) {
-    load_raw<D>(ra, page_ptr(p0), tid, 128 * NG);
-    if (p0 + 1 < p1) load_raw<D>(rb, page_ptr(p0 + 1), tid, 128 * NG);
-    stage_page<D, NG>(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale, lut, lutK, lutV);
+    load_raw<D, NTH>(ra, page_ptr(p0), tid, 128 * NG);
+    if (p0 + 1 < p1) load_raw<D, NTH>(rb, page_ptr(p0 + 1), tid, 128 * NG);
+    stage_page<D, NG, NTH>(sm.slot[0], ra, tid, ntok_of(p0), kscale, vscale, lut, lutK, lutV);
   }
   __syncthreads();
 
@@ -415,14 +439,15 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
   // earlier), fut receives the loads of page pi + 2.  The page's operands
   // are in slot (pi - p0) & 1; page pi + 1 is staged into the other slot
   // after the compute, and one barrier ends the step.
-  auto step = [&](int pi, const PageRaw<D> &nxt, PageRaw<D> &fut) __attribute__((always_inline)) {
+  auto step = [&](int pi, const PageRaw<D, NTH> &nxt, PageRaw<D, NTH> &fut) __attribute__((always_inline)) {
     const int sl = (pi - p0) & 1;
-    if (pi + 2 < p1) load_raw<D>(fut, page_ptr(pi + 2), tid, 128 * NG);
+    if (pi + 2 < p1) load_raw<D, NTH>(fut, page_ptr(pi + 2), tid, 128 * NG);
     const PageSlot<D> &S = sm.slot[sl];
     const bool masked = pi >= fv;
     const int tbase = pi * kPage;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      if (!have) break; // a missing tile's waves only stage
       if constexpr (NG == 2) {
         // two scale groups per token (channels 0..63, 64..127): the logit
         // sums one QK^T chain per group, each with its scale and zero term;
@@ -441,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
           }
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
-            const v4f sk = *(const v4f *)&S.par[2 * g][tok0 + 4 * J];
+            const v4f sk = *(const v4f *)&S.par[skr + g][tok0 + 4 * J];
             const v4f zk = *(const v4f *)&S.par[2 * g + 1][tok0 + 4 * J];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -531,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
       v4f skp[4], zkp[4];
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        skp[J] = *(const v4f *)&S.par[0][tok0 + 4 * J];
+        skp[J] = *(const v4f *)&S.par[skr][tok0 + 4 * J];
         zkp[J] = *(const v4f *)&S.par[1][tok0 + 4 * J];
       }
       // ---- S^T = K codes . (Q_hi + Q_lo)^T
@@ -564,7 +589,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
         float lg = -INFINITY;
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-          const v4f sk = *(const v4f *)&S.par[0][tok0 + 4 * J];
+          const v4f sk = *(const v4f *)&S.par[skr][tok0 + 4 * J];
           const v4f zk = *(const v4f *)&S.par[1][tok0 + 4 * J];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -595,7 +620,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
         wave_sync();
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-          const v4f sk = *(const v4f *)&S.par[0][tok0 + 4 * J];
+          const v4f sk = *(const v4f *)&S.par[skr][tok0 + 4 * J];
           const v4f zk = *(const v4f *)&S.par[1][tok0 + 4 * J];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -639,7 +664,7 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
       }
       }
     }
-    if (pi + 1 < p1) stage_page<D, NG>(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale, lut, lutK, lutV);
+    if (pi + 1 < p1) stage_page<D, NG, NTH>(sm.slot[sl ^ 1], nxt, tid, ntok_of(pi + 1), kscale, vscale, lut, lutK, lutV);
     __syncthreads();
   };
   for (int pi = p0; pi < p1; pi += 2) {
@@ -657,7 +682,8 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(PoolDev p, Prefill
     sm.row[w][1][n] = zrow1;
   }
   wave_sync();
-  const size_t base = (((size_t)kv * a.NT + T) * a.S + s) * kRows + 32 * w;
+  if (!have) return;
+  const size_t base = (((size_t)kv * a.NT + T) * a.S + s) * kRows + 32 * wl;
   const float k24 = ldexpf(1.f, 24 - p.pv_shift);
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
@@ -955,9 +981,10 @@ bool prefill_mfma_supported(const PoolDev &p) {
 template <int D, int NG>
 static void launch_all(const PoolDev &p, const PrefillArgs &a, const uint16_t *q, float *out, u32x4 *qrec,
                        float *qaux, float *po, float *pml, hipStream_t s) {
+  constexpr int TW = kPfTilesPerBlock;
   hipLaunchKernelGGL((prefill_qprep_kernel<D, NG>), dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, qrec, qaux);
-  hipLaunchKernelGGL((prefill_hist_kernel<D, NG>), dim3(a.NT * a.S, p.Hkv), dim3(256), 0, s, p, a, qrec, qaux, po,
-                     pml);
+  hipLaunchKernelGGL((prefill_hist_kernel<D, NG, TW>), dim3((a.NT + TW - 1) / TW * a.S, p.Hkv), dim3(256 * TW), 0, s,
+                     p, a, qrec, qaux, po, pml);
   hipLaunchKernelGGL((prefill_finish_kernel<D>), dim3(a.NT, p.Hkv), dim3(256), 0, s, p, a, q, po, pml, out);
 }
 
