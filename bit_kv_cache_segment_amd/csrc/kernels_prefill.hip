@@ -10,9 +10,10 @@
 // heads per kv head); query i sits at position L - n_q + i and sees the
 // positions up to its own.
 //
-// Launches (one stream), for pools with d = 128, one or two scale groups
-// per token (G = 128 or 64: with two, the logit sums one QK^T chain per
-// group and P' is formed per group for its channel tiles), affine or
+// Launches (one stream), templated on the head dimension D (64 or 128) and
+// the scale groups per head row (one, or two for d = 128 and G = 64: then
+// the logit sums one QK^T chain per group and P' is formed per group for
+// its channel tiles), affine or
 // codebook levels (a codebook pool's level is
 // z + (L[code] / 64) s: its staged codes are the level bytes L, from one byte
 // permute per pair, and both scales carry the 1/64):
@@ -24,11 +25,12 @@
 //     v_mfma_f32_32x32x16_f16 with the per-channel factors 4^-e that the K
 //     code operand's sub-normal pairs need; the row sums of a (the zero
 //     point term) go beside them.
-//   prefill_hist_kernel, one block per (tile, kv head, split of the tile's
-//     visible history pages), 4 waves of 32 rows, two blocks per compute
-//     unit: the block stages each page once in shared memory as MFMA
-//     operands (K and V codes as fp16 sub-normal pairs code 4^e 2^-24,
-//     per-token scale/zero terms in fp32); each wave computes
+//   prefill_hist_kernel, one block per (two consecutive tiles, kv head,
+//     split of their visible history pages), 8 waves of 32 rows, one block
+//     per compute unit: the block stages each page once in shared memory
+//     as MFMA operands (K and V codes as fp16 sub-normal pairs code 4^e
+//     2^-24, per-token scale/zero terms in fp32, the K scale once per tile
+//     since E is per tile), for 256 rows; each wave computes
 //       S^T = K_codes . (Q_hi + Q_lo)^T        (fp16 MFMA, fp32 accumulate)
 //       logit = s_K 2^(24-E) S + z_K sum(a)   (log2 units, exact fp32 terms)
 //     runs a lazy online softmax (integer reference m, moved only when a
