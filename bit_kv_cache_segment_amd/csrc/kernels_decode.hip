@@ -945,11 +945,6 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
   // (the int8 MFMA operand), V as unsigned bytes L (fp16 sub-normals)
   const uint32_t lutK = LUT ? p.codebook[kv] ^ 0x80808080u : 0u;
   const uint32_t lutV = LUT ? p.codebook[Hkv + kv] : 0u;
-  // V level pairs: selector bytes 1 and 3 pick zero.  Held in a register
-  // (mbcnt of an empty mask is 0, which the compiler does not fold), so that
-  // mask and OR form one v_and_or_b32: one instruction cannot take two
-  // literals here.
-  const uint32_t vsel_zero = 0x0C000C00u | __builtin_amdgcn_mbcnt_lo(0u, 0u);
 
   float m_run[RT], thr[RT], l_run[RT], zs[RT][NG];
   v4f acc[NJ];
@@ -1124,13 +1119,20 @@ __device__ void history_block(HistSmem<D, G, GQ, main_waves(D, G, GQ)> &sm, cons
         const uint32_t wv = cur.vc[j / 4][j % 4];
         u32x4 b0, b1;
         if constexpr (LUT) {
-          // tokens (2i, 2i + 1): codes to selector bytes 0 and 2, zero bytes
-          // (selector 0x0C) above them: two fp16 sub-normals L * 2^-24
-          auto pair = [&](int i) __attribute__((always_inline)) {
-            return __builtin_amdgcn_perm(lutV, lutV, ((wv >> (2 * i)) & 0x00030003u) | vsel_zero);
-          };
-          b0 = u32x4{pair(0), pair(1), pair(2), pair(3)};
-          b1 = u32x4{pair(4), pair(5), pair(6), pair(7)};
+          // token k's code sits at bit 16 (k & 1) + 2 (k >> 1): one permute
+          // per four codes gives x_i, the level bytes of tokens 2i, 8 + 2i,
+          // 2i + 1, 9 + 2i; a mask (tokens 2i, 2i + 1) and a second permute
+          // (tokens 8 + 2i, 9 + 2i) put each pair in bytes 0 and 2 with zero
+          // bytes above: two fp16 sub-normals L * 2^-24
+          uint32_t lo4[4], hi4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t x = __builtin_amdgcn_perm(lutV, lutV, (wv >> (2 * i)) & 0x03030303u);
+            lo4[i] = x & 0x00FF00FFu;
+            hi4[i] = __builtin_amdgcn_perm(x, x, 0x0C030C01u);
+          }
+          b0 = u32x4{lo4[0], lo4[1], lo4[2], lo4[3]};
+          b1 = u32x4{hi4[0], hi4[1], hi4[2], hi4[3]};
         } else {
           const uint32_t w2 = wv >> 10;
           b0 = u32x4{wv & 0x00030003u, wv & 0x000C000Cu, wv & 0x00300030u, wv & 0x00C000C0u};
