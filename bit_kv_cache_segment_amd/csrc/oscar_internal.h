@@ -256,10 +256,11 @@ struct PrefillArgs {
   int32_t NT, S;   // tiles per kv head, splits per tile
   float qscale;    // softmax scale * log2(e)
 };
-// Splits per tile: about 512 blocks per launch (two per compute unit), at
-// most 16 splits.
+// Splits per tile: about 512 (tile, split) pairs per launch, at most 16
+// splits; the history kernel takes two tiles per block, so about 256 blocks
+// (one per compute unit).
 inline int prefill_mfma_splits(int NT, int Hkv) {
-  const int blocks = NT * Hkv, want = (512 + blocks - 1) / blocks;
+  const int tiles = NT * Hkv, want = (512 + tiles - 1) / tiles;
   return want < 1 ? 1 : (want > 16 ? 16 : want);
 }
 bool prefill_mfma_supported(const PoolDev &p);
