@@ -16,7 +16,7 @@
 // its channel tiles), affine or
 // codebook levels (a codebook pool's level is
 // z + (L[code] / 64) s: its staged codes are the level bytes L, from one byte
-// permute per pair, and both scales carry the 1/64):
+// permute per four codes, and both scales carry the 1/64):
 //   prefill_qprep_kernel, one block per (tile of 128 rows, kv head): the
 //     rows' queries are rotated by R_K (fp16 MFMAs: the bf16 query is exact
 //     in fp16, R_K is staged as hi + lo parts), scaled by
@@ -291,10 +291,18 @@ __device__ __forceinline__ void load_raw(PageRaw<D, NTH> &r, const uint8_t *blk,
 // K code dword i of the pool layout -> (token t, 16-channel group gi): its
 // channel pairs (p, p + 8) become fp16 sub-normal pairs code 4^e(p) 2^-24,
 // pairs 0..3 in the lanes of half 0 and 4..7 in half 1 of k-step gi.
-// Codebook pools (lut != 0): each pair holds the two codes' level bytes L
-// (one byte permute per pair), sub-normals L 2^-24 with no 4^e factor.
-__device__ __forceinline__ uint32_t lut_pair(uint32_t wd, int sh, uint32_t lut) {
-  return __builtin_amdgcn_perm(lut, lut, ((wd >> sh) & 0x00030003u) | 0x0C000C00u);
+// Codebook pools (lut != 0): each pair holds the two codes' level bytes L,
+// sub-normals L 2^-24 with no 4^e factor.  One byte permute per four codes
+// (the codes at bits 2i, 8 + 2i, 16 + 2i, 24 + 2i) gives their level bytes;
+// a mask keeps the pair at bits (2i, 16 + 2i) (lo[i]) and a second permute
+// moves the pair at bits (8 + 2i, 24 + 2i) into place (hi[i]).
+__device__ __forceinline__ void lut_pairs(uint32_t wd, uint32_t lut, u32x4 &lo, u32x4 &hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = __builtin_amdgcn_perm(lut, lut, (wd >> (2 * i)) & 0x03030303u);
+    lo[i] = x & 0x00FF00FFu;
+    hi[i] = __builtin_amdgcn_perm(x, x, 0x0C030C01u);
+  }
 }
 template <int D>
 __device__ __forceinline__ void stage_k(PageSlot<D> &s, int i, uint32_t wd, bool lut, uint32_t lk) {
@@ -307,9 +315,10 @@ __device__ __forceinline__ void stage_k(PageSlot<D> &s, int i, uint32_t wd, bool
   const int row = token_row(t & 31);
   const int kz = 2 * ((row >> 4) & 1) + 4 * ((gi >> 2) & 1);
   if (lut) {
-    s.K[t >> 5][gi][row ^ kz] = u32x4{lut_pair(wd, 0, lk), lut_pair(wd, 2, lk), lut_pair(wd, 4, lk), lut_pair(wd, 6, lk)};
-    s.K[t >> 5][gi][(row + 32) ^ kz] =
-        u32x4{lut_pair(wd, 8, lk), lut_pair(wd, 10, lk), lut_pair(wd, 12, lk), lut_pair(wd, 14, lk)};
+    u32x4 lo, hi;
+    lut_pairs(wd, lk, lo, hi);
+    s.K[t >> 5][gi][row ^ kz] = lo;
+    s.K[t >> 5][gi][(row + 32) ^ kz] = hi;
     return;
   }
   s.K[t >> 5][gi][row ^ kz] = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
@@ -329,9 +338,10 @@ __device__ __forceinline__ void stage_v(PageSlot<D> &s, int i, uint32_t wd, bool
   const int lane = lane0 ^ (4 * ((c >> 5) & 1) + 8 * ((lane0 >> 4) & 1));
   const uint32_t w2 = wd >> 10;
   if (lut) {
-    s.V[c >> 5][r >> 1][0][lane] = u32x4{lut_pair(wd, 0, lv), lut_pair(wd, 2, lv), lut_pair(wd, 4, lv), lut_pair(wd, 6, lv)};
-    s.V[c >> 5][r >> 1][1][lane] =
-        u32x4{lut_pair(wd, 8, lv), lut_pair(wd, 10, lv), lut_pair(wd, 12, lv), lut_pair(wd, 14, lv)};
+    u32x4 lo, hi;
+    lut_pairs(wd, lv, lo, hi);
+    s.V[c >> 5][r >> 1][0][lane] = lo;
+    s.V[c >> 5][r >> 1][1][lane] = hi;
     return;
   }
   s.V[c >> 5][r >> 1][0][lane] = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
