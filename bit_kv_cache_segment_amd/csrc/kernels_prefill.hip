@@ -468,6 +468,14 @@ __global__ __launch_bounds__(256 * TW) __attribute__((amdgpu_waves_per_eu(2, 2))
         float lg[16];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
+          // the group's per-token logit terms, read before its QK^T chain
+          // so that their shared-memory latency overlaps it
+          v4f skp[4], zkp[4];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            skp[J] = *(const v4f *)&S.par[skr + g][tok0 + 4 * J];
+            zkp[J] = *(const v4f *)&S.par[2 * g + 1][tok0 + 4 * J];
+          }
           v16f acc = v16f{};
 #pragma unroll
           for (int k4 = 0; k4 < KS / 2; ++k4) {
@@ -478,8 +486,8 @@ __global__ __launch_bounds__(256 * TW) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
-            const v4f sk = *(const v4f *)&S.par[skr + g][tok0 + 4 * J];
-            const v4f zk = *(const v4f *)&S.par[2 * g + 1][tok0 + 4 * J];
+            const v4f sk = skp[J];
+            const v4f zk = zkp[J];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int v = 4 * J + i;
